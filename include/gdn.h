@@ -1,0 +1,141 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta-rule token mixer.
+ *
+ * The mixer is the Gated DeltaNet layer that InfiniteVL interleaves with
+ * sliding-window attention (explainer page "InfiniteVL: Synergizing Linear and
+ * Sparse Attention for Highly-Efficient, Unlimited-Input Vision-Language
+ * Models", sections "The Concept: Gated DeltaNet" and "Step 2: Process tokens
+ * with Hybrid Blocks").  Per (batch b, head h) it keeps a fixed-size memory and,
+ * for every token t, applies the gated delta rule
+ *
+ *     S_t = a_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T ,
+ *     o_t = S_t q_t ,            a_t = exp(g_t) ,
+ *
+ * S_t being d_v x d_k.  The state is stored transposed, key-major:
+ *     state[b][h][i][j] = S[j][i]      (i < d_k over keys, j < d_v over values).
+ * No query scaling is applied (scale q beforehand if wanted); the readout uses
+ * the state after the token's own update.
+ *
+ * Common conventions of every entry point
+ *   - All pointers are DEVICE pointers on the current HIP device, except
+ *     `stream`, a hipStream_t passed as void* (NULL = the null stream).
+ *   - Row-major, contiguous layouts:
+ *       q, k  [B][T][H][d_k]     v, o  [B][T][H][d_v]     g, beta  [B][T][H]
+ *     (decode: T is absent, i.e. [B][H][d] and [B][H]).  q/k/v are bf16
+ *     (dtype GDN_BF16, raw bfloat16 bits) or fp32 (GDN_F32); g, beta, state
+ *     and o are always fp32.  g is the log of the decay a (g <= 0), beta the
+ *     write strength (0 <= beta <= 1).  Values outside that domain are not
+ *     rejected; the result is then unspecified (bf16-input paths hold operands
+ *     in fp16 inside the matrix cores and assume unit-norm-scale keys).
+ *   - Supported sizes: d_k == d_v in {64, 128}; B, H >= 1; T >= 1 (any T).
+ *   - Every pointer must be 16-byte aligned.
+ *   - Outputs (o, state_out / state) must not overlap any input; the only
+ *     allowed overlap is state_out == state_in exactly (in-place update).
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronises; work is enqueued on `stream` and completes asynchronously.
+ *     Calls are graph-capturable (fixed pointers, no allocation).
+ *   - All checks run on the host before anything is enqueued: on any error
+ *     nothing is launched and no output byte changes.  A launch failure
+ *     reported by the runtime returns GDN_ERR_LAUNCH.  Device faults surface
+ *     at the caller's next synchronisation.  No exception crosses the ABI and
+ *     nothing calls exit/abort.  The library keeps no global state; calls on
+ *     different streams may run concurrently.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,         /* a required pointer is NULL                      */
+    GDN_ERR_SHAPE = 2,        /* a size is < 1, or d_k != d_v                    */
+    GDN_ERR_DTYPE = 3,        /* dtype is not GDN_BF16 / GDN_F32                  */
+    GDN_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned                */
+    GDN_ERR_ALIAS = 5,        /* an output overlaps an input (other than in place) */
+    GDN_ERR_UNSUPPORTED = 6,  /* d not in {64, 128}, or sizes beyond 2^31 elements */
+    GDN_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than required          */
+    GDN_ERR_LAUNCH = 8        /* the HIP runtime rejected a launch                */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+
+/* GDN_ABI_VERSION of the built library. */
+int gdn_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *gdn_status_str(int status);
+
+/*
+ * Bytes of device workspace gdn_prefill / gdn_stream_chunk need for these sizes
+ * (0 is a valid answer).  Pure host arithmetic; returns 0 for invalid sizes.
+ */
+size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype);
+
+/*
+ * gdn_prefill -- the whole recurrence over T tokens (chunkwise-parallel form).
+ *
+ * Operation: for every (b, h), starting from state_in (or zeros if state_in is
+ * NULL), run the gated delta rule over t = 0..T-1, writing o[b][t][h][:] and
+ * the final state to state_out.  The chunked evaluation (64-token chunks:
+ * per-chunk triangular solve into WY-type factors, state carried between
+ * chunks) gives the same result up to rounding.  This is the layer's prefill
+ * over a whole prompt or video segment (explainer page, "Efficiency and
+ * Streaming"; README "hustvl/InfiniteVL", "Accelerated Streaming Inference").
+ *
+ * q, k, v, g, beta  inputs, layouts above; dtype selects bf16 / fp32 q,k,v.
+ * state_in          [B][H][d_k][d_v] fp32 or NULL (zero initial state).
+ * state_out         [B][H][d_k][d_v] fp32; may equal state_in (in place).
+ * o                 [B][T][H][d_v] fp32.
+ * workspace         device scratch of at least gdn_prefill_workspace_bytes()
+ *                   bytes (may be NULL when that is 0).  Its contents on entry
+ *                   are ignored; it must not overlap any other argument and
+ *                   must not be shared by calls that can run concurrently.
+ */
+int gdn_prefill(const void *q, const void *k, const void *v, int dtype,
+                const float *g, const float *beta,
+                const float *state_in, float *state_out, float *o,
+                int B, int T, int H, int dk, int dv,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_stream_chunk -- one call of a stream: the next T tokens of B sequences
+ * whose memory persists across calls in `state` (README "hustvl/InfiniteVL",
+ * "Accelerated Streaming Inference": the linear memory state is updated on the
+ * fly, frame after frame, at constant memory).
+ *
+ * Identical to gdn_prefill(q, k, v, dtype, g, beta, state, state, o, ...):
+ * `state` [B][H][d_k][d_v] fp32 is required (not NULL) and is updated in place.
+ * Any T >= 1; successive calls with the same state equal one gdn_prefill over
+ * the concatenated tokens, up to rounding.
+ */
+int gdn_stream_chunk(const void *q, const void *k, const void *v, int dtype,
+                     const float *g, const float *beta, float *state, float *o,
+                     int B, int T, int H, int dk, int dv,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_decode_step -- one new token for each of B independent sequences
+ * (README "hustvl/InfiniteVL", "Accelerated Decode": token generation with the
+ * constant-size state).
+ *
+ * q, k [B][H][d_k], v [B][H][d_v] (bf16 or fp32), g, beta [B][H] fp32;
+ * state [B][H][d_k][d_v] fp32, updated in place; o [B][H][d_v] fp32.
+ * Equivalent to gdn_prefill with T = 1 and the state in place.  Needs no
+ * workspace.  Each head's state is read once and written once.
+ */
+int gdn_decode_step(const void *q, const void *k, const void *v, int dtype,
+                    const float *g, const float *beta, float *state, float *o,
+                    int B, int H, int dk, int dv, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

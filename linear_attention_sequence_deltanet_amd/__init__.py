@@ -1,0 +1,167 @@
+"""Gated delta-rule token mixer on MI355X (gfx950): thin Python binding.
+
+Every step of the computation runs in ``libgdn.so`` (hand-written HIP kernels
+behind the C ABI of ``include/gdn.h``).  This module only marshals arguments:
+it checks that tensors live on the GPU, allocates outputs with torch when the
+caller passes none, and forwards raw pointers plus torch's current stream.
+There is no CPU fallback: without the built library, importing fails.
+
+Entry points (same names as the C ABI):
+    prefill(q, k, v, g, beta, state_in=None)      -> (o, state_out)
+    stream_chunk(q, k, v, g, beta, state)         -> o        (state in place)
+    decode_step(q, k, v, g, beta, state)          -> o        (state in place)
+    prefill_workspace_bytes(B, T, H, dk, dv, dtype)
+
+Shapes: q, k [B, T, H, dk]; v [B, T, H, dv]; g (log-decay), beta [B, T, H];
+state [B, H, dk, dv] fp32 with state[b, h, i, j] = S[j, i]; o fp32.  Decode drops
+the T axis.  q/k/v are torch.bfloat16 or torch.float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["prefill", "stream_chunk", "decode_step", "prefill_workspace_bytes", "GdnError",
+           "library_path", "GDN_BF16", "GDN_F32"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_BF16 = 0
+GDN_F32 = 1
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, _lib.gdn_status_str(status).decode(), status))
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libgdn.so is not built (%s); run __graft_entry__.build() or "
+                          "python linear_attention_sequence_deltanet_amd/build.py" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.gdn_abi_version.restype = i
+    lib.gdn_abi_version.argtypes = []
+    lib.gdn_status_str.restype = ctypes.c_char_p
+    lib.gdn_status_str.argtypes = [i]
+    lib.gdn_prefill_workspace_bytes.restype = sz
+    lib.gdn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.gdn_prefill.restype = i
+    lib.gdn_prefill.argtypes = [vp, vp, vp, i, fp, fp, fp, fp, fp, i, i, i, i, i, vp, sz, vp]
+    lib.gdn_stream_chunk.restype = i
+    lib.gdn_stream_chunk.argtypes = [vp, vp, vp, i, fp, fp, fp, fp, i, i, i, i, i, vp, sz, vp]
+    lib.gdn_decode_step.restype = i
+    lib.gdn_decode_step.argtypes = [vp, vp, vp, i, fp, fp, fp, fp, i, i, i, i, vp]
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def abi_version() -> int:
+    return int(_lib.gdn_abi_version())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU (got %s)" % t.device)
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def prefill_workspace_bytes(B, T, H, dk, dv, dtype=GDN_BF16) -> int:
+    if not isinstance(dtype, int):
+        dtype = _dtype_code(_torch().empty(0, dtype=dtype))
+    return int(_lib.gdn_prefill_workspace_bytes(B, T, H, dk, dv, dtype))
+
+
+def _workspace(workspace, B, T, H, dk, dv, code, device):
+    need = int(_lib.gdn_prefill_workspace_bytes(B, T, H, dk, dv, code))
+    if workspace is None and need > 0:
+        torch = _torch()
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, nbytes
+
+
+def prefill(q, k, v, g, beta, state_in=None, *, state_out=None, o=None, workspace=None,
+            stream=None):
+    """Run the recurrence over all T tokens; returns (o, state_out)."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    if state_out is None:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    workspace, nbytes = _workspace(workspace, B, T, H, dk, dv, code, q.device)
+    st = _lib.gdn_prefill(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), _ptr(state_in),
+                          _ptr(state_out), _ptr(o), B, T, H, dk, dv, _ptr(workspace), nbytes,
+                          _stream(stream, q.device))
+    if st != 0:
+        raise GdnError(st, "gdn_prefill")
+    return o, state_out
+
+
+def stream_chunk(q, k, v, g, beta, state, *, o=None, workspace=None, stream=None):
+    """Next T tokens of a stream; `state` is updated in place. Returns o."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    workspace, nbytes = _workspace(workspace, B, T, H, dk, dv, code, q.device)
+    st = _lib.gdn_stream_chunk(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), _ptr(state),
+                               _ptr(o), B, T, H, dk, dv, _ptr(workspace), nbytes,
+                               _stream(stream, q.device))
+    if st != 0:
+        raise GdnError(st, "gdn_stream_chunk")
+    return o
+
+
+def decode_step(q, k, v, g, beta, state, *, o=None, stream=None):
+    """One token per sequence: q, k [B, H, dk], v [B, H, dv], g, beta [B, H];
+    `state` [B, H, dk, dv] is updated in place. Returns o [B, H, dv]."""
+    torch = _torch()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    st = _lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), _ptr(state),
+                              _ptr(o), B, H, dk, dv, _stream(stream, q.device))
+    if st != 0:
+        raise GdnError(st, "gdn_decode_step")
+    return o

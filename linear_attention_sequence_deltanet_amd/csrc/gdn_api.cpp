@@ -1,0 +1,142 @@
+// gdn_api.cpp -- the C ABI declared in include/gdn.h: host-side validation,
+// then launches on the caller's stream.  No allocation, no synchronisation,
+// no exceptions across the boundary.
+#include "gdn.h"
+
+#include <stdint.h>
+
+#include "gdn_launch.h"
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+inline Range span(const void* p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + bytes};
+}
+
+inline bool overlap(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks shared by every entry point. T = 1 for decode.
+int check_sizes(int B, int T, int H, int dk, int dv, int dtype) {
+    if (dtype != GDN_BF16 && dtype != GDN_F32) return GDN_ERR_DTYPE;
+    if (B < 1 || T < 1 || H < 1 || dk < 1 || dv < 1) return GDN_ERR_SHAPE;
+    if (dk != dv) return GDN_ERR_SHAPE;
+    if (dk != 64 && dk != 128) return GDN_ERR_UNSUPPORTED;
+    // element counts of the largest tensors must fit the kernels' 64-bit
+    // indexing and the grid limits: B*H heads, B*T*H tokens.
+    const long long tokens = (long long)B * T * H;
+    if ((long long)B * H > (1LL << 31) - 1 || tokens * dk > (1LL << 50)) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+int check_io(const void* q, const void* k, const void* v, int dtype, const float* g,
+             const float* beta, const float* state_in, const float* state_out, const float* o,
+             int B, int T, int H, int dk, int dv, const void* ws, size_t ws_bytes) {
+    if (!q || !k || !v || !g || !beta || !state_out || !o) return GDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, g, beta, state_in, state_out, o, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+
+    const size_t el = dtype == GDN_BF16 ? 2 : 4;
+    const size_t tok = (size_t)B * T * H;
+    const Range rq = span(q, tok * dk * el), rk = span(k, tok * dk * el),
+                rv = span(v, tok * dv * el), rg = span(g, tok * 4), rb = span(beta, tok * 4);
+    const size_t sbytes = (size_t)B * H * dk * dv * 4;
+    const Range rsi = state_in ? span(state_in, sbytes) : Range{0, 0};
+    const Range rso = span(state_out, sbytes), ro = span(o, tok * dv * 4);
+    const Range rws = ws ? span(ws, ws_bytes) : Range{0, 0};
+
+    const Range inputs[] = {rq, rk, rv, rg, rb};
+    for (const Range& in : inputs) {
+        if (overlap(in, rso) || overlap(in, ro) || overlap(in, rws)) return GDN_ERR_ALIAS;
+    }
+    if (overlap(ro, rso) || overlap(ro, rws) || overlap(rso, rws)) return GDN_ERR_ALIAS;
+    if (state_in) {
+        if (overlap(rsi, ro) || overlap(rsi, rws)) return GDN_ERR_ALIAS;
+        if (overlap(rsi, rso) && state_in != state_out) return GDN_ERR_ALIAS;
+    }
+    return GDN_OK;
+}
+
+inline int launch_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
+
+int run_prefill(const void* q, const void* k, const void* v, int dtype, const float* g,
+                const float* beta, const float* state_in, float* state_out, float* o, int B,
+                int T, int H, int dk, void* ws, size_t ws_bytes, hipStream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    return launch_status(gdn::launch_recurrent(q, k, v, dtype == GDN_BF16, g, beta, state_in,
+                                               state_out, o, B, T, H, dk, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_str(int status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "invalid sizes (B, T, H, d must be >= 1 and d_k == d_v)";
+        case GDN_ERR_DTYPE: return "dtype must be GDN_BF16 or GDN_F32";
+        case GDN_ERR_ALIGN: return "every pointer must be 16-byte aligned";
+        case GDN_ERR_ALIAS: return "an output overlaps an input (only state_out == state_in is allowed)";
+        case GDN_ERR_UNSUPPORTED: return "unsupported sizes (d must be 64 or 128)";
+        case GDN_ERR_WORKSPACE: return "workspace missing or smaller than gdn_prefill_workspace_bytes()";
+        case GDN_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+        default: return "unknown status";
+    }
+}
+
+size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype) {
+    if (check_sizes(B, T, H, dk, dv, dtype) != GDN_OK) return 0;
+    return 0;
+}
+
+int gdn_prefill(const void* q, const void* k, const void* v, int dtype, const float* g,
+                const float* beta, const float* state_in, float* state_out, float* o, int B,
+                int T, int H, int dk, int dv, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    int s = check_sizes(B, T, H, dk, dv, dtype);
+    if (s != GDN_OK) return s;
+    const size_t need = gdn_prefill_workspace_bytes(B, T, H, dk, dv, dtype);
+    s = check_io(q, k, v, dtype, g, beta, state_in, state_out, o, B, T, H, dk, dv, workspace,
+                 workspace ? workspace_bytes : 0);
+    if (s != GDN_OK) return s;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
+    return run_prefill(q, k, v, dtype, g, beta, state_in, state_out, o, B, T, H, dk, workspace,
+                       workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int gdn_stream_chunk(const void* q, const void* k, const void* v, int dtype, const float* g,
+                     const float* beta, float* state, float* o, int B, int T, int H, int dk,
+                     int dv, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!state) return GDN_ERR_NULL;
+    return gdn_prefill(q, k, v, dtype, g, beta, state, state, o, B, T, H, dk, dv, workspace,
+                       workspace_bytes, stream);
+}
+
+int gdn_decode_step(const void* q, const void* k, const void* v, int dtype, const float* g,
+                    const float* beta, float* state, float* o, int B, int H, int dk, int dv,
+                    void* stream) {
+    int s = check_sizes(B, 1, H, dk, dv, dtype);
+    if (s != GDN_OK) return s;
+    if (!state) return GDN_ERR_NULL;
+    s = check_io(q, k, v, dtype, g, beta, state, state, o, B, 1, H, dk, dv, nullptr, 0);
+    if (s != GDN_OK) return s;
+    return launch_status(gdn::launch_recurrent(q, k, v, dtype == GDN_BF16, g, beta, state, state,
+                                               o, B, 1, H, dk, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -33,7 +33,7 @@ def build(force: bool = False) -> str:
     """Compile the C oracle with gcc (fp64, OpenMP, no fast-math)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+        subprocess.check_call(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c99",
                                "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB

@@ -65,20 +65,21 @@ int gdn_oracle_recurrence(const double *q, const double *k, const double *v,
 #endif
     for (long bh = 0; bh < B * H; ++bh) {
         const long b = bh / H, h = bh % H;
-        /* S in the orientation of the definition: S[j*dk + i], d_v rows, d_k columns. */
-        double *S = (double *)malloc(sizeof(double) * (size_t)(dk * dv));
+        /* St holds S transposed, St[i*dv + j] = S[j][i] (the stored layout), so
+         * that every loop below runs over the value index j innermost; each
+         * sum over the key index i is still accumulated in increasing i. */
+        double *St = (double *)malloc(sizeof(double) * (size_t)(dk * dv));
         double *u = (double *)malloc(sizeof(double) * (size_t)dv);
-        if (!S || !u) {
-            free(S); free(u);
+        if (!St || !u) {
+            free(St); free(u);
 #ifdef _OPENMP
 #pragma omp atomic write
 #endif
             failed = 1;
             continue;
         }
-        for (long i = 0; i < dk; ++i)
-            for (long j = 0; j < dv; ++j)
-                S[j * dk + i] = state_in ? state_in[(bh * dk + i) * dv + j] : 0.0;
+        for (long e = 0; e < dk * dv; ++e)
+            St[e] = state_in ? state_in[bh * dk * dv + e] : 0.0;
 
         for (long t = 0; t < T; ++t) {
             const long tok = (b * T + t) * H + h;
@@ -89,30 +90,24 @@ int gdn_oracle_recurrence(const double *q, const double *k, const double *v,
             const double bt = beta[tok];
 
             /* step 3: S (I - b k k^T) = S - b (S k) k^T ; u = S k */
-            for (long j = 0; j < dv; ++j) {
-                double s = 0.0;
-                for (long i = 0; i < dk; ++i) s += S[j * dk + i] * kt[i];
-                u[j] = s;
-            }
+            for (long j = 0; j < dv; ++j) u[j] = 0.0;
+            for (long i = 0; i < dk; ++i)
+                for (long j = 0; j < dv; ++j) u[j] += St[i * dv + j] * kt[i];
             /* steps 2-4: S <- a (S - b u k^T) + b v k^T */
-            for (long j = 0; j < dv; ++j)
-                for (long i = 0; i < dk; ++i)
-                    S[j * dk + i] = a * (S[j * dk + i] - bt * u[j] * kt[i]) + bt * vt[j] * kt[i];
+            for (long i = 0; i < dk; ++i)
+                for (long j = 0; j < dv; ++j)
+                    St[i * dv + j] = a * (St[i * dv + j] - bt * u[j] * kt[i]) + bt * vt[j] * kt[i];
 
             /* step 5: o_t = S_t q_t (readout after the update) */
             if (o) {
                 double *ot = o + tok * dv;
-                for (long j = 0; j < dv; ++j) {
-                    double s = 0.0;
-                    for (long i = 0; i < dk; ++i) s += S[j * dk + i] * qt[i];
-                    ot[j] = s;
-                }
+                for (long j = 0; j < dv; ++j) ot[j] = 0.0;
+                for (long i = 0; i < dk; ++i)
+                    for (long j = 0; j < dv; ++j) ot[j] += St[i * dv + j] * qt[i];
             }
         }
-        for (long i = 0; i < dk; ++i)
-            for (long j = 0; j < dv; ++j)
-                state_out[(bh * dk + i) * dv + j] = S[j * dk + i];
-        free(S);
+        for (long e = 0; e < dk * dv; ++e) state_out[bh * dk * dv + e] = St[e];
+        free(St);
         free(u);
     }
     return failed ? -2 : 0;

@@ -1,0 +1,138 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch.
+
+The pointers used here are fake addresses: each call below fails validation,
+and validation runs entirely on the host, so nothing is dereferenced or
+launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+LIB = os.path.join(ROOT, "linear_attention_sequence_deltanet_amd", "libgdn.so")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, UNSUP, WS, LAUNCH = range(9)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from linear_attention_sequence_deltanet_amd import build
+        build.build()
+    import linear_attention_sequence_deltanet_amd as gdn
+    return gdn._lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("gdn_prefill", "gdn_decode_step", "gdn_stream_chunk"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define\s+GDN_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert lib.gdn_abi_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert lib.gdn_status_str(s) and lib.gdn_status_str(s) != b"unknown status"
+    assert lib.gdn_status_str(1234) == b"unknown status"
+
+
+def test_workspace_bytes_invalid_sizes_is_zero(lib):
+    assert lib.gdn_prefill_workspace_bytes(0, 10, 2, 128, 128, 0) == 0
+    assert lib.gdn_prefill_workspace_bytes(1, 10, 2, 96, 96, 0) == 0
+    assert lib.gdn_prefill_workspace_bytes(1, 10, 2, 128, 128, 7) == 0
+
+
+# fake, 16-byte aligned, well separated device addresses
+BASE = 1 << 40
+GB = 1 << 30
+P = {n: BASE + i * GB for i, n in enumerate(["q", "k", "v", "g", "beta", "sin", "sout", "o", "ws"])}
+
+
+def _prefill(lib, B=1, T=100, H=2, d=128, dtype=0, **over):
+    a = dict(P)
+    a.update(over)
+    return lib.gdn_prefill(a["q"], a["k"], a["v"], dtype, a["g"], a["beta"], a["sin"], a["sout"],
+                           a["o"], B, T, H, d, d, a["ws"], GB, None)
+
+
+def test_prefill_null_pointers(lib):
+    for name in ("q", "k", "v", "g", "beta", "sout", "o"):
+        assert _prefill(lib, **{name: None}) == NULL, name
+
+
+def test_prefill_bad_dtype_and_shapes(lib):
+    assert _prefill(lib, dtype=5) == DTYPE
+    assert _prefill(lib, B=0) == SHAPE
+    assert _prefill(lib, T=0) == SHAPE
+    assert _prefill(lib, H=-1) == SHAPE
+    assert lib.gdn_prefill(P["q"], P["k"], P["v"], 0, P["g"], P["beta"], P["sin"], P["sout"],
+                           P["o"], 1, 10, 2, 128, 64, P["ws"], GB, None) == SHAPE
+    assert _prefill(lib, d=96) == UNSUP
+    assert _prefill(lib, d=256) == UNSUP
+
+
+def test_prefill_misaligned(lib):
+    for name in ("q", "k", "v", "g", "beta", "sin", "sout", "o"):
+        assert _prefill(lib, **{name: P[name] + 4}) == ALIGN, name
+
+
+def test_prefill_aliasing(lib):
+    assert _prefill(lib, o=P["q"] + 256) == ALIAS            # output inside an input
+    assert _prefill(lib, sout=P["v"]) == ALIAS
+    assert _prefill(lib, sout=P["o"] + 1024) == ALIAS        # two outputs overlap
+    assert _prefill(lib, sout=P["sin"] + 16) == ALIAS        # partial in-place overlap
+    assert _prefill(lib, ws=P["o"]) == ALIAS
+
+
+def test_prefill_workspace_too_small(lib):
+    need = lib.gdn_prefill_workspace_bytes(1, 100, 2, 128, 128, 0)
+    if need == 0:
+        pytest.skip("no workspace needed for these sizes")
+    r = lib.gdn_prefill(P["q"], P["k"], P["v"], 0, P["g"], P["beta"], P["sin"], P["sout"],
+                        P["o"], 1, 100, 2, 128, 128, P["ws"], need - 1, None)
+    assert r == WS
+    r = lib.gdn_prefill(P["q"], P["k"], P["v"], 0, P["g"], P["beta"], P["sin"], P["sout"],
+                        P["o"], 1, 100, 2, 128, 128, None, 0, None)
+    assert r == WS
+
+
+def test_stream_chunk_requires_state(lib):
+    r = lib.gdn_stream_chunk(P["q"], P["k"], P["v"], 0, P["g"], P["beta"], None, P["o"],
+                             1, 272, 16, 128, 128, P["ws"], GB, None)
+    assert r == NULL
+
+
+def test_decode_errors(lib):
+    def dec(**over):
+        a = dict(P)
+        a.update(over)
+        return lib.gdn_decode_step(a["q"], a["k"], a["v"], a.get("dtype", 0), a["g"], a["beta"],
+                                   a["sout"], a["o"], a.get("B", 64), 16, a.get("d", 128),
+                                   a.get("d", 128), None)
+    assert dec(sout=None) == NULL
+    assert dec(q=None) == NULL
+    assert dec(dtype=9) == DTYPE
+    assert dec(B=0) == SHAPE
+    assert dec(d=32) == UNSUP
+    assert dec(o=P["sout"] + 64) == ALIAS
+    assert dec(k=P["k"] + 2) == ALIGN
