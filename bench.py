@@ -1,0 +1,183 @@
+"""Benchmark of the gated delta-rule mixer on one MI355X.
+
+A step is one whole-path call over one batch of synthetic inputs already in HBM:
+  * value: gdn_prefill over the 8192-token prompt, B=1, H=16, d_k=d_v=128, bf16
+    q/k/v, fp32 gates/state/output, zero initial state (tokens/s);
+  * decode: gdn_decode_step for 64 sequences x 16 heads, d=128, fp32 state updated
+    in place, 1000 consecutive steps with fresh inputs (tokens/s, reported beside).
+Timing uses HIP events on the stream the library launches on (torch's current
+stream).  The fp64 oracle is timed on the host cores as a reported CPU baseline.
+Prints ONE JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFS = 2516.6     # MI355X dense fp16/bf16 matrix, TFLOP/s
+
+# Algorithmic work per token x head of the prefill at d = 128, chunk 64:
+#   bytes: q, k, v bf16 (3 x 256) + g, beta fp32 (8) + o fp32 (512)
+#   flops: 6 d_k d_v + C (3 d_k + 2 d_v)
+PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 256 + 8 + 512
+PREFILL_FLOPS_PER_TOKEN_HEAD = 6 * 128 * 128 + 64 * (3 * 128 + 2 * 128)
+# Decode per head x step: state read + write (2 x 64 KiB) + q,k,v bf16 (768) +
+# g, beta (8) + o fp32 (512)
+DECODE_BYTES_PER_HEAD = 2 * 128 * 128 * 4 + 3 * 256 + 8 + 512
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--decode-steps", type=int, default=1000)
+    p.add_argument("--decode-reps", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def stage_bf16(arr, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def time_prefill(gdn, args, dev):
+    import torch
+    import gdn_inputs
+    d = gdn_inputs.sequence_inputs("prefill8k")
+    B, T, H, dk = d["q"].shape
+    q, k, v = (stage_bf16(d[x], dev) for x in ("q", "k", "v"))
+    g = torch.from_numpy(d["g"]).to(dev)
+    beta = torch.from_numpy(d["beta"]).to(dev)
+    o = torch.empty((B, T, H, dk), dtype=torch.float32, device=dev)
+    st = torch.empty((B, H, dk, dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, gdn.prefill_workspace_bytes(B, T, H, dk, dk)), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        gdn.prefill(q, k, v, g, beta, None, state_out=st, o=o, workspace=ws)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        gdn.prefill(q, k, v, g, beta, None, state_out=st, o=o, workspace=ws)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    return d, ms, (B, T, H, dk)
+
+
+def time_decode(gdn, args, dev):
+    import torch
+    import gdn_inputs
+    d = gdn_inputs.decode_inputs("decode64", steps=args.decode_steps)
+    N, B, H, dk = d["q"].shape
+    q, k, v = (stage_bf16(d[x], dev) for x in ("q", "k", "v"))
+    g = torch.from_numpy(d["g"]).to(dev)
+    beta = torch.from_numpy(d["beta"]).to(dev)
+    s0 = torch.from_numpy(d["state0"]).to(dev)
+    state = s0.clone()
+    o = torch.empty((N, B, H, dk), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for n in range(min(N, 50)):  # warm-up
+        gdn.decode_step(q[n], k[n], v[n], g[n], beta[n], state, o=o[n])
+    times = []
+    for _ in range(args.decode_reps):
+        state.copy_(s0)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for n in range(N):
+            gdn.decode_step(q[n], k[n], v[n], g[n], beta[n], state, o=o[n])
+        end.record(stream)
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end) / N)
+    ms = float(np.median(times))
+    return ms, (N, B, H, dk)
+
+
+def cpu_baseline(d, seconds):
+    """Time the fp64 oracle on the host over (repeats of) the prefill workload."""
+    import gdn_inputs
+    import oracle
+    threads = oracle.default_threads()
+    f = lambda x: gdn_inputs.to_f64(x, d["dtype"])
+    B, T, H, dk = d["q"].shape
+    # bounded sample: a prefix of the prompt, grown until the run lasts ~seconds
+    Ts = 512
+    while True:
+        t0 = time.time()
+        oracle.recurrence(f(d["q"][:, :Ts]), f(d["k"][:, :Ts]), f(d["v"][:, :Ts]),
+                          d["g"][:, :Ts], d["beta"][:, :Ts], None, threads=threads)
+        dt = time.time() - t0
+        if dt >= seconds or Ts >= T:
+            break
+        Ts = min(T, max(Ts * 2, int(Ts * seconds / max(dt, 1e-3) * 1.1)))
+    return {"value": B * Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 token-serial oracle, first %d of %d tokens of the prefill8k "
+                      "workload (B=1, H=16, d=128), %.1f s wall" % (Ts, T, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not os.path.exists(os.path.join(ROOT, "linear_attention_sequence_deltanet_amd", "libgdn.so")):
+        import __graft_entry__
+        __graft_entry__.build()
+    import linear_attention_sequence_deltanet_amd as gdn
+    dev = torch.device("cuda:0")
+
+    d, ms, (B, T, H, dk) = time_prefill(gdn, args, dev)
+    tok_s = B * T / (ms / 1e3)
+    bytes_call = PREFILL_BYTES_PER_TOKEN_HEAD * B * T * H
+    flops_call = PREFILL_FLOPS_PER_TOKEN_HEAD * B * T * H
+    gbs = bytes_call / (ms / 1e3) / 1e9
+    tfs = flops_call / (ms / 1e3) / 1e12
+    line = {
+        "metric": "Gated DeltaNet prefill tokens/s at H=16, d=128 (decode tokens/s beside)",
+        "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill8k: B=1, H=16, T=8192, d_k=d_v=128, bf16 q/k/v, "
+                               "fp32 g/beta/state/o, chunk 64, zero initial state",
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": dk},
+        "roofline": {"kernel": "gdn_prefill (whole call)", "bound": "hbm", "achieved": gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None,
+                     "mfma_tflops": tfs, "mfma_frac": tfs / MFMA_F16_PEAK_TFS,
+                     "bytes_per_call": bytes_call, "flops_per_call": flops_call},
+    }
+    if not args.no_decode:
+        dms, (N, DB, DH, ddk) = time_decode(gdn, args, dev)
+        dbytes = DECODE_BYTES_PER_HEAD * DB * DH
+        dgbs = dbytes / (dms / 1e3) / 1e9
+        line["decode"] = {
+            "workload": "decode64: B=64 sequences, H=16, d=128, %d steps, state in place" % N,
+            "value": DB / (dms / 1e3), "unit": "tokens/s", "us_per_step": dms * 1e3,
+            "roofline": {"kernel": "gdn_decode_step", "bound": "hbm", "achieved": dgbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
+                         "traffic": None, "bytes_per_call": dbytes},
+        }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

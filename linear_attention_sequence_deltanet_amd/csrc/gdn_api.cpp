@@ -33,8 +33,10 @@ int check_sizes(int B, int T, int H, int dk, int dv, int dtype) {
     if (dk != 64 && dk != 128) return GDN_ERR_UNSUPPORTED;
     // element counts of the largest tensors must fit the kernels' 64-bit
     // indexing and the grid limits: B*H heads, B*T*H tokens.
+    // (prefill grids are (chunks, H, B): H and B must fit a grid dimension).
     const long long tokens = (long long)B * T * H;
     if ((long long)B * H > (1LL << 31) - 1 || tokens * dk > (1LL << 50)) return GDN_ERR_UNSUPPORTED;
+    if (T > 1 && (B > 65535 || H > 65535)) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
 
@@ -72,10 +74,9 @@ inline int launch_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E
 int run_prefill(const void* q, const void* k, const void* v, int dtype, const float* g,
                 const float* beta, const float* state_in, float* state_out, float* o, int B,
                 int T, int H, int dk, void* ws, size_t ws_bytes, hipStream_t stream) {
-    (void)ws;
     (void)ws_bytes;
-    return launch_status(gdn::launch_recurrent(q, k, v, dtype == GDN_BF16, g, beta, state_in,
-                                               state_out, o, B, T, H, dk, stream));
+    return launch_status(gdn::launch_chunked(q, k, v, dtype == GDN_BF16, g, beta, state_in,
+                                             state_out, o, B, T, H, dk, ws, stream));
 }
 
 }  // namespace
@@ -101,7 +102,7 @@ const char* gdn_status_str(int status) {
 
 size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype) {
     if (check_sizes(B, T, H, dk, dv, dtype) != GDN_OK) return 0;
-    return 0;
+    return gdn::chunked_workspace_bytes(B, T, H, dk, dtype == GDN_BF16);
 }
 
 int gdn_prefill(const void* q, const void* k, const void* v, int dtype, const float* g,
