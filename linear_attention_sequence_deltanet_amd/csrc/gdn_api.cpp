@@ -33,10 +33,8 @@ int check_sizes(int B, int T, int H, int dk, int dv, int dtype) {
     if (dk != 64 && dk != 128) return GDN_ERR_UNSUPPORTED;
     // element counts of the largest tensors must fit the kernels' 64-bit
     // indexing and the grid limits: B*H heads, B*T*H tokens.
-    // (prefill grids are (chunks, H, B): H and B must fit a grid dimension).
     const long long tokens = (long long)B * T * H;
     if ((long long)B * H > (1LL << 31) - 1 || tokens * dk > (1LL << 50)) return GDN_ERR_UNSUPPORTED;
-    if (T > 1 && (B > 65535 || H > 65535)) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }
 
@@ -111,6 +109,7 @@ int gdn_prefill(const void* q, const void* k, const void* v, int dtype, const fl
                 void* stream) {
     int s = check_sizes(B, T, H, dk, dv, dtype);
     if (s != GDN_OK) return s;
+    if (B > 65535 || H > 65535) return GDN_ERR_UNSUPPORTED;  // grid (chunks, H, B)
     const size_t need = gdn_prefill_workspace_bytes(B, T, H, dk, dv, dtype);
     s = check_io(q, k, v, dtype, g, beta, state_in, state_out, o, B, T, H, dk, dv, workspace,
                  workspace ? workspace_bytes : 0);
