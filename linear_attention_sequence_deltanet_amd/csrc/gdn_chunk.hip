@@ -21,11 +21,13 @@
 //   chunk_prep  (one workgroup per chunk x head, fully parallel): gam, the Gram
 //               products K K^T and Q K^T, the triangular solve by 16-row
 //               blocks (diagonal blocks by forward substitution in fp32,
-//               off-diagonal corrections on matrix cores), and writes
-//               -W, U, P, gam to the workspace.
+//               off-diagonal corrections on matrix cores), and writes -W, U,
+//               P, K^T and gam to the workspace in the exact register-fragment
+//               order the scan consumes them (16-byte coalesced per lane).
 //   chunk_scan  (one workgroup per head x 16-column slice of the state,
 //               sequential over chunks): Delta, O and the state update, with
-//               the fp32 state tile held in registers across chunks.
+//               the fp32 state tile held in registers across chunks and the
+//               next chunk's operands prefetched into registers.
 // bf16 inputs run the products on fp16 operands (bf16 values are exact in
 // fp16 at these magnitudes) with fp32 accumulation; the dominant terms
 // (b V, b Gam K in the solve, the state itself) stay fp32.  fp32 inputs run the
@@ -72,32 +74,46 @@ __device__ __forceinline__ typename Mfma<OT>::frag8 load8_in(const float* p) {
     return r;
 }
 
-// Workspace layout per (b, h, chunk), chunk-major: -W [CH][D] OT, U [CH][D] f32,
-// P [CH][CH] OT, gam [CH] f32.
-template <typename OT, int D>
-struct WsLayout {
-    static constexpr size_t w_elems = (size_t)CH * D;
-    static constexpr size_t u_elems = (size_t)CH * D;
-    static constexpr size_t p_elems = (size_t)CH * CH;
-    static constexpr size_t bytes_per_chunk =
-        w_elems * sizeof(OT) + u_elems * 4 + p_elems * sizeof(OT) + CH * 4;
-};
+template <typename OT>
+__device__ __forceinline__ typename Mfma<OT>::frag8 zero8() {
+    typename Mfma<OT>::frag8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = OT(0);
+    return r;
+}
 
+// Workspace per (b, h, chunk), chunk-major, every block in lane order:
+//   Wf  [4 row blocks][D/32 k-steps][64 lanes][8]  OT   -W  (A operand of W H0)
+//   Pf  [4 row blocks][2 k-steps][64 lanes][8]     OT   P   (A operand of P Delta)
+//   KTf [D/16 key tiles][2 k-steps][64 lanes][8]   OT   K^T (A operand of K^T e Delta)
+//   Uf  [4 row blocks][D/16 col tiles][64 lanes][4] f32 U  (C layout)
+//   gam [64]                                       f32
+// A-operand fragment (tile row block m, k-step kk) of lane (g, c) holds
+// X[16 m + c][32 kk + 8 g + j], j = 0..7; the C layout holds X[16 m + 4 g + e][16 n + c].
 template <typename OT, int D>
-struct WsPtrs {
-    OT* wn;
-    float* u;
+struct Ws {
+    static constexpr size_t wf = (size_t)4 * (D / 32) * 64 * 8;
+    static constexpr size_t pf = (size_t)4 * 2 * 64 * 8;
+    static constexpr size_t ktf = (size_t)(D / 16) * 2 * 64 * 8;
+    static constexpr size_t uf = (size_t)4 * (D / 16) * 64 * 4;
+    static constexpr size_t bytes_per_chunk = (wf + pf + ktf) * sizeof(OT) + (uf + CH) * 4;
+
+    OT* w;
     OT* p;
+    OT* kt;
+    float* u;
     float* gam;
-    __host__ __device__ WsPtrs(void* ws, long nchunks_total) {
-        char* base = static_cast<char*>(ws);
-        wn = reinterpret_cast<OT*>(base);
-        base += WsLayout<OT, D>::w_elems * sizeof(OT) * nchunks_total;
-        u = reinterpret_cast<float*>(base);
-        base += WsLayout<OT, D>::u_elems * 4 * nchunks_total;
-        p = reinterpret_cast<OT*>(base);
-        base += WsLayout<OT, D>::p_elems * sizeof(OT) * nchunks_total;
-        gam = reinterpret_cast<float*>(base);
+    __device__ Ws(void* base, long nchunks_total) {
+        char* b = static_cast<char*>(base);
+        w = reinterpret_cast<OT*>(b);
+        b += wf * sizeof(OT) * nchunks_total;
+        p = reinterpret_cast<OT*>(b);
+        b += pf * sizeof(OT) * nchunks_total;
+        kt = reinterpret_cast<OT*>(b);
+        b += ktf * sizeof(OT) * nchunks_total;
+        u = reinterpret_cast<float*>(b);
+        b += uf * 4 * nchunks_total;
+        gam = reinterpret_cast<float*>(b);
     }
 };
 
@@ -113,16 +129,18 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
                                                   int T, int H, int NC, long nchunks_total) {
     using OT = typename OpType<In>::type;
     using M = Mfma<OT>;
-    constexpr int LD = D + 8;        // padded row stride (elements) of q/k/v tiles
-    constexpr int LA = CH + 8;       // padded row stride of the A matrix
-    constexpr int NT = 2 * D / 16;   // 16-column tiles of [W | U]
-    constexpr int NTW = NT / 4;      // tiles per wave
+    using F8 = typename M::frag8;
+    using F4 = typename M::frag4;
+    constexpr int LD = D + 8;       // padded row stride (elements) of k/v tiles
+    constexpr int LA = CH + 8;      // padded row stride of 64 x 64 tiles
+    constexpr int NTD = D / 16;     // 16-column tiles of W (and of U)
+    constexpr int NTW = NTD / 4;    // tiles of each part per wave
 
     __shared__ __align__(16) OT sK[CH * LD];
-    __shared__ __align__(16) OT sQ[CH * LD];
-    __shared__ __align__(16) OT sV[CH * LD];
-    __shared__ __align__(16) OT sA[CH * LA];      // -A off-diagonal blocks, (T_bb - I) diagonal
-    __shared__ float sAd[4][16][17];             // diagonal blocks of A, fp32
+    __shared__ __align__(16) OT sV[CH * LD];   // V, later the staging of -W
+    __shared__ __align__(16) OT sA[CH * LA];   // -A off-diagonal blocks, (T_bb - I) diagonal
+    __shared__ __align__(16) OT sP[CH * LA];   // P staging
+    __shared__ float sAd[4][16][17];           // diagonal blocks of A, fp32
     __shared__ float sgam[CH], sbeta[CH];
 
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -131,7 +149,7 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
     const long t0 = (long)c * CH;
     const int n = (int)min((long)CH, (long)T - t0);
     const long ch = ((long)b * H + h) * NC + c;
-    WsPtrs<OT, D> W(ws, nchunks_total);
+    Ws<OT, D> W(ws, nchunks_total);
 
     // gates: gam = inclusive cumsum of g within the chunk (padded rows: g = b = 0)
     if (wave == 0) {
@@ -148,36 +166,39 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
         W.gam[ch * CH + lane] = gv;
     }
 
-    // q, k, v rows of the chunk into LDS as OT (zero rows past the end)
+    // k, v rows of the chunk into LDS as OT (zero rows past the end)
     for (int idx = tid; idx < CH * D / 8; idx += 256) {
         const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-        typename M::frag8 fq, fk, fv;
+        F8 fk = zero8<OT>(), fv = zero8<OT>();
         if (r < n) {
             const long off = (((long)b * T + t0 + r) * H + h) * D + c8;
-            fq = load8_in<OT>(q + off);
             fk = load8_in<OT>(k + off);
             fv = load8_in<OT>(v + off);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) fq[e] = fk[e] = fv[e] = OT(0);
         }
-        *reinterpret_cast<typename M::frag8*>(&sQ[r * LD + c8]) = fq;
-        *reinterpret_cast<typename M::frag8*>(&sK[r * LD + c8]) = fk;
-        *reinterpret_cast<typename M::frag8*>(&sV[r * LD + c8]) = fv;
+        *reinterpret_cast<F8*>(&sK[r * LD + c8]) = fk;
+        *reinterpret_cast<F8*>(&sV[r * LD + c8]) = fv;
+    }
+    // Q operand rows of this wave's Q K^T block straight from global memory
+    const int mq = 3 - wave;
+    F8 fq[D / 32];
+    {
+        const int r = 16 * mq + lc;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+            fq[kk] = r < n ? load8_in<OT>(q + ((((long)b * T + t0 + r) * H + h) * D + 32 * kk + 8 * lg))
+                           : zero8<OT>();
     }
     __syncthreads();
 
     // Gram tiles: wave w does K K^T for row block w and Q K^T for row block 3 - w.
     {
-        const int mk = wave, mq = 3 - wave;
+        const int mk = wave;
         for (int ni = 0; ni <= mk; ++ni) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                const auto fa = ld8<OT>(&sK[(16 * mk + lc) * LD + 32 * kk + 8 * lg]);
-                const auto fb = ld8<OT>(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]);
-                acc = M::k32(fa, fb, acc);
-            }
+            for (int kk = 0; kk < D / 32; ++kk)
+                acc = M::k32(ld8<OT>(&sK[(16 * mk + lc) * LD + 32 * kk + 8 * lg]),
+                             ld8<OT>(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]), acc);
             const int i = 16 * ni + lc;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -189,23 +210,19 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
                     sA[r * LA + i] = static_cast<OT>(-a);
             }
         }
-        OT* P = W.p + ch * WsLayout<OT, D>::p_elems;
         for (int ni = 0; ni < 4; ++ni) {
             f32x4 acc = zero4();
             if (ni <= mq) {
 #pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk) {
-                    const auto fa = ld8<OT>(&sQ[(16 * mq + lc) * LD + 32 * kk + 8 * lg]);
-                    const auto fb = ld8<OT>(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]);
-                    acc = M::k32(fa, fb, acc);
-                }
+                for (int kk = 0; kk < D / 32; ++kk)
+                    acc = M::k32(fq[kk], ld8<OT>(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]), acc);
             }
             const int i = 16 * ni + lc;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * mq + 4 * lg + e;
                 const float pv = i <= r ? __expf(sgam[r] - sgam[i]) * acc[e] : 0.f;
-                P[r * CH + i] = static_cast<OT>(pv);
+                sP[r * LA + i] = static_cast<OT>(pv);
             }
         }
     }
@@ -227,188 +244,251 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
         for (int r = 0; r < 16; ++r)
             sA[(16 * wave + r) * LA + 16 * wave + cc] = static_cast<OT>(r == cc ? 0.f : x[r]);
     }
-    __syncthreads();
-
-    // Blocked forward substitution for X = [W | U], 16-row blocks b:
-    //   Y_b = B_b - sum_{j<b} A_bj X_j ,   X_b = Y_b + N_bb Y_b .
-    // The right-hand side B_b enters in fp32; only corrections use OT operands.
-    OT* Wn = W.wn + ch * WsLayout<OT, D>::w_elems;
-    float* U = W.u + ch * WsLayout<OT, D>::u_elems;
+    // P fragments (row block = wave) and K^T fragments (key tiles of this wave) out
+    {
+        OT* Pf = W.p + ch * Ws<OT, D>::pf;
 #pragma unroll
-    for (int tt = 0; tt < NTW; ++tt) {
-        const int nt = wave * NTW + tt;
-        const bool is_w = nt < D / 16;
-        const int col = (nt % (D / 16)) * 16 + lc;
-        typename M::frag4 xh[4];
+        for (int kk = 0; kk < 2; ++kk)
+            *reinterpret_cast<F8*>(Pf + ((wave * 2 + kk) * 64 + lane) * 8) =
+                ld8<OT>(&sP[(16 * wave + lc) * LA + 32 * kk + 8 * lg]);
+        OT* KTf = W.kt + ch * Ws<OT, D>::ktf;
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            f32x4 acc;
+        for (int m = 0; m < NTD / 4; ++m) {
+            const int mt = wave * (NTD / 4) + m;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * bb + 4 * lg + e;
-                acc[e] = is_w ? sbeta[r] * __expf(sgam[r]) * static_cast<float>(sK[r * LD + col])
-                              : sbeta[r] * static_cast<float>(sV[r * LD + col]);
-            }
+            for (int kk = 0; kk < 2; ++kk) {
+                F8 f;
 #pragma unroll
-            for (int j = 0; j < bb; ++j)
-                acc = M::k16(ld4<OT>(&sA[(16 * bb + lc) * LA + 16 * j + 4 * lg]), xh[j], acc);
-            const auto yh = cvt4<OT>(acc);
-            acc = M::k16(ld4<OT>(&sA[(16 * bb + lc) * LA + 16 * bb + 4 * lg]), yh, acc);
-            xh[bb] = cvt4<OT>(acc);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * bb + 4 * lg + e;
-                if (is_w)
-                    Wn[r * D + col] = static_cast<OT>(-acc[e]);
-                else
-                    U[r * D + col] = acc[e];
+                for (int j = 0; j < 8; ++j) f[j] = sK[(32 * kk + 8 * lg + j) * LD + 16 * mt + lc];
+                *reinterpret_cast<F8*>(KTf + ((mt * 2 + kk) * 64 + lane) * 8) = f;
             }
         }
     }
+    __syncthreads();
+
+    // Blocked forward substitution for X = [W | U], 16-row blocks bb:
+    //   Y_b = B_b - sum_{j<b} A_bj X_j ,   X_b = Y_b + N_bb Y_b .
+    // The right-hand side B_b enters in fp32; only corrections use OT operands.
+    // U first (its right-hand side is V), then -W into the V buffer.
+    float* Uf = W.u + ch * Ws<OT, D>::uf;
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+        const bool is_w = part == 1;
+#pragma unroll
+        for (int tt = 0; tt < NTW; ++tt) {
+            const int nt = wave * NTW + tt;
+            const int col = 16 * nt + lc;
+            F4 xh[4];
+            f32x4 res[4];
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                f32x4 acc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * bb + 4 * lg + e;
+                    acc[e] = is_w ? sbeta[r] * __expf(sgam[r]) * static_cast<float>(sK[r * LD + col])
+                                  : sbeta[r] * static_cast<float>(sV[r * LD + col]);
+                }
+#pragma unroll
+                for (int j = 0; j < bb; ++j)
+                    acc = M::k16(ld4<OT>(&sA[(16 * bb + lc) * LA + 16 * j + 4 * lg]), xh[j], acc);
+                const F4 yh = cvt4<OT>(acc);
+                acc = M::k16(ld4<OT>(&sA[(16 * bb + lc) * LA + 16 * bb + 4 * lg]), yh, acc);
+                xh[bb] = cvt4<OT>(acc);
+                res[bb] = acc;
+            }
+            if (!is_w) {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+                    *reinterpret_cast<f32x4*>(Uf + ((bb * NTD + nt) * 64 + lane) * 4) = res[bb];
+            } else {
+                __syncthreads();  // (first W tile only matters) every wave is done reading V
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sV[(16 * bb + 4 * lg + e) * LD + col] = static_cast<OT>(-res[bb][e]);
+            }
+        }
+    }
+    __syncthreads();
+    OT* Wf = W.w + ch * Ws<OT, D>::wf;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+        *reinterpret_cast<F8*>(Wf + ((wave * (D / 32) + kk) * 64 + lane) * 8) =
+            ld8<OT>(&sV[(16 * wave + lc) * LD + 32 * kk + 8 * lg]);
 }
 
 // ---------------------------------------------------------------------------
-// chunk_scan: grid (D / 16, H, B), 256 threads; sequential over the chunks.
-// Wave w owns state rows (keys) [D/4 * w, D/4 * (w+1)) of a 16-column slice.
+// chunk_scan: 1-D grid of B*H*(D/16) workgroups, 256 threads; sequential over
+// the chunks.  All 16-column slices of one head run on the same XCD (blocks
+// are dealt to XCDs round-robin), so they share its L2 for the chunk operands.
+// Wave w owns token rows [16w, 16w+16) of Delta and O, and key tiles
+// [w*D/64, (w+1)*D/64) of the state slice.
 // ---------------------------------------------------------------------------
+template <typename OT, int D>
+struct ScanFrags {
+    typename Mfma<OT>::frag8 w[D / 32];   // -W rows of this wave
+    typename Mfma<OT>::frag8 q[D / 32];   // Q rows of this wave
+    typename Mfma<OT>::frag8 p[2];        // P rows of this wave
+    typename Mfma<OT>::frag8 kt[D / 64][2];
+    f32x4 u;                               // U (C layout)
+    f32x4 gam;                             // gam of rows 16w + 4g + e
+    float gamC;
+};
+
 template <typename In, int D>
-__global__ __launch_bounds__(256) void chunk_scan(const In* __restrict__ q,
-                                                  const In* __restrict__ k,
-                                                  const void* ws, const float* state_in,
-                                                  float* state_out, float* __restrict__ o,
-                                                  int T, int H, int NC, long nchunks_total) {
+__device__ __forceinline__ void scan_load(ScanFrags<typename OpType<In>::type, D>& f,
+                                          const In* __restrict__ q,
+                                          const Ws<typename OpType<In>::type, D>& W, long bh,
+                                          int c, int NC, int T, int H, int b, int h, int slice,
+                                          int wave, int lane) {
+    using OT = typename OpType<In>::type;
+    using F8 = typename Mfma<OT>::frag8;
+    const int lg = lane >> 4, lc = lane & 15;
+    const long ch = bh * NC + c;
+    const long t0 = (long)c * CH;
+    const OT* Wf = W.w + ch * Ws<OT, D>::wf;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+        f.w[kk] = *reinterpret_cast<const F8*>(Wf + ((wave * (D / 32) + kk) * 64 + lane) * 8);
+    const OT* Pf = W.p + ch * Ws<OT, D>::pf;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+        f.p[kk] = *reinterpret_cast<const F8*>(Pf + ((wave * 2 + kk) * 64 + lane) * 8);
+    const OT* KTf = W.kt + ch * Ws<OT, D>::ktf;
+#pragma unroll
+    for (int m = 0; m < D / 64; ++m)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            f.kt[m][kk] = *reinterpret_cast<const F8*>(
+                KTf + (((wave * (D / 64) + m) * 2 + kk) * 64 + lane) * 8);
+    f.u = *reinterpret_cast<const f32x4*>(W.u + ch * Ws<OT, D>::uf +
+                                          ((wave * (D / 16) + slice) * 64 + lane) * 4);
+    f.gam = *reinterpret_cast<const f32x4*>(W.gam + ch * CH + 16 * wave + 4 * lg);
+    f.gamC = W.gam[ch * CH + CH - 1];
+    const long r = t0 + 16 * wave + lc;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+        f.q[kk] = r < T ? load8_in<OT>(q + ((((long)b * T + r) * H + h) * D + 32 * kk + 8 * lg))
+                        : zero8<OT>();
+}
+
+template <typename In, int D>
+__global__ __launch_bounds__(256) void chunk_scan(const In* __restrict__ q, const void* ws,
+                                                  const float* state_in, float* state_out,
+                                                  float* __restrict__ o, int T, int H, int B,
+                                                  int NC, long nchunks_total) {
     using OT = typename OpType<In>::type;
     using M = Mfma<OT>;
-    constexpr int DV = 16;            // state columns per workgroup
-    constexpr int MT = D / 16 / 4;    // key tiles per wave
-    constexpr int LS = D + 8;         // row stride of the f16 state copy (per value column)
+    constexpr int NS = D / 16;        // 16-column slices per head
+    constexpr int MT = D / 64;        // key tiles per wave
+    constexpr int LS = D + 8;         // row stride of the OT state copy (per value column)
     constexpr int LT = CH + 8;        // row stride of token-contiguous tiles
 
-    __shared__ __align__(16) OT sS[DV * LS];   // state slice, S orientation [dv][dk]
-    __shared__ __align__(16) OT sKT[D * LT];   // K^T [dk][t]
-    __shared__ __align__(16) OT sDT[DV * LT];  // Delta^T [dv][t]
-    __shared__ __align__(16) OT sET[DV * LT];  // (e Delta)^T [dv][t]
-    __shared__ float sgam[CH];
+    __shared__ __align__(16) OT sS[16 * LS];   // state slice, S orientation [dv][dk]
+    __shared__ __align__(16) OT sDT[16 * LT];  // Delta^T [dv][t]
+    __shared__ __align__(16) OT sET[16 * LT];  // (e Delta)^T [dv][t]
 
-    const int slice = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // XCD-aware placement: block L runs on XCD L % 8; keep a head's slices together.
+    const int L = blockIdx.x, G = B * H;
+    int head, slice;
+    if (G % 8 == 0) {
+        head = (L % 8) + 8 * ((L / 8) / NS);
+        slice = (L / 8) % NS;
+    } else {
+        head = L / NS;
+        slice = L % NS;
+    }
+    const int b = head / H, h = head % H;
+    const long bh = head;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lg = lane >> 4, lc = lane & 15;
-    const int col0 = slice * DV;
-    const long bh = (long)b * H + h;
-    WsPtrs<OT, D> Wp(const_cast<void*>(ws), nchunks_total);
+    const int col0 = slice * 16;
+    Ws<OT, D> W(const_cast<void*>(ws), nchunks_total);
 
-    // fp32 state slice in C layout: rows (keys) 16*(wave*MT + m) + 4*lg + e, column col0 + lc
+    // fp32 state slice in C layout: keys 16*(wave*MT + m) + 4*lg + e, column col0 + lc
     f32x4 hs[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int key = 16 * (wave * MT + m) + 4 * lg + e;
             hs[m][e] = state_in ? state_in[(bh * D + key) * D + col0 + lc] : 0.f;
         }
-    }
 
-    for (int c = 0; c < NC; ++c) {
+    auto step = [&](const ScanFrags<OT, D>& f, int c) {
         const long t0 = (long)c * CH;
-        const int n = (int)min((long)CH, (long)T - t0);
-        const long ch = bh * NC + c;
-
-        // f16/f32 copy of the state slice for the B operand of W H and Q H
+        // B operand copy of the state slice
 #pragma unroll
         for (int m = 0; m < MT; ++m)
             st4<OT>(&sS[lc * LS + 16 * (wave * MT + m) + 4 * lg], cvt4<OT>(hs[m]));
-        if (tid < CH) sgam[tid] = Wp.gam[ch * CH + tid];
-        // K^T of the chunk (zero columns past the end)
-        for (int idx = tid; idx < CH * D / 8; idx += 256) {
-            const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-            typename M::frag8 fk;
-            if (r < n) {
-                fk = load8_in<OT>(k + ((((long)b * T + t0 + r) * H + h) * D + c8));
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) fk[e] = OT(0);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sKT[(c8 + e) * LT + r] = fk[e];
-        }
         __syncthreads();
-
-        const float gamC = sgam[CH - 1];
-        // Delta = U - W H0 and Q H0 for token rows 16*wave + (4*lg + e)
-        const OT* Wn = Wp.wn + ch * WsLayout<OT, D>::w_elems;
-        const float* U = Wp.u + ch * WsLayout<OT, D>::u_elems;
-        const int rA = 16 * wave + lc;  // operand row of this lane
-        f32x4 dl, qh = zero4();
+        // Delta = U - W H0 and Q H0, rows 16*wave + 4*lg + e; two accumulation chains each
+        f32x4 d0 = f.u, d1 = zero4(), q0 = zero4(), q1 = zero4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dl[e] = U[(16 * wave + 4 * lg + e) * D + col0 + lc];
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-            const auto fs = ld8<OT>(&sS[lc * LS + 32 * kk + 8 * lg]);
-            dl = M::k32(ld8<OT>(Wn + rA * D + 32 * kk + 8 * lg), fs, dl);
-            typename M::frag8 fq;
-            if (rA < n) {
-                fq = load8_in<OT>(q + ((((long)b * T + t0 + rA) * H + h) * D + 32 * kk + 8 * lg));
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) fq[e] = OT(0);
-            }
-            qh = M::k32(fq, fs, qh);
+        for (int kk = 0; kk < D / 32; kk += 2) {
+            const auto s0 = ld8<OT>(&sS[lc * LS + 32 * kk + 8 * lg]);
+            const auto s1 = ld8<OT>(&sS[lc * LS + 32 * (kk + 1) + 8 * lg]);
+            d0 = M::k32(f.w[kk], s0, d0);
+            q0 = M::k32(f.q[kk], s0, q0);
+            d1 = M::k32(f.w[kk + 1], s1, d1);
+            q1 = M::k32(f.q[kk + 1], s1, q1);
         }
-        f32x4 edl;
+        const f32x4 dl = d0 + d1;
+        f32x4 oq = q0 + q1, edl;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int r = 16 * wave + 4 * lg + e;
-            edl[e] = __expf(gamC - sgam[r]) * dl[e];
-            qh[e] *= __expf(sgam[r]);
+            edl[e] = __expf(f.gamC - f.gam[e]) * dl[e];
+            oq[e] *= __expf(f.gam[e]);
         }
         st4<OT>(&sDT[lc * LT + 16 * wave + 4 * lg], cvt4<OT>(dl));
         st4<OT>(&sET[lc * LT + 16 * wave + 4 * lg], cvt4<OT>(edl));
         __syncthreads();
-
-        // O = diag(Gam) Q H0 + P Delta  (P is lower triangular: K-blocks up to the diagonal)
-        const OT* P = Wp.p + ch * WsLayout<OT, D>::p_elems;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            if (32 * kk <= 16 * wave + 15)
-                qh = M::k32(ld8<OT>(P + rA * CH + 32 * kk + 8 * lg),
-                            ld8<OT>(&sDT[lc * LT + 32 * kk + 8 * lg]), qh);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 16 * wave + 4 * lg + e;
-            if (r < n) o[(((long)b * T + t0 + r) * H + h) * D + col0 + lc] = qh[e];
-        }
-
         // H = Gam_C H0 + K^T (e Delta)
-        const float GC = __expf(gamC);
+        const float GC = __expf(f.gamC);
+        const auto e0 = ld8<OT>(&sET[lc * LT + 8 * lg]);
+        const auto e1 = ld8<OT>(&sET[lc * LT + 32 + 8 * lg]);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             f32x4 acc = hs[m] * GC;
-            const int key = 16 * (wave * MT + m) + lc;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                acc = M::k32(ld8<OT>(&sKT[key * LT + 32 * kk + 8 * lg]),
-                             ld8<OT>(&sET[lc * LT + 32 * kk + 8 * lg]), acc);
-            hs[m] = acc;
+            acc = M::k32(f.kt[m][0], e0, acc);
+            hs[m] = M::k32(f.kt[m][1], e1, acc);
         }
-        __syncthreads();
+        // O = diag(Gam) Q H0 + P Delta (P is lower triangular)
+        oq = M::k32(f.p[0], ld8<OT>(&sDT[lc * LT + 8 * lg]), oq);
+        if (wave >= 2) oq = M::k32(f.p[1], ld8<OT>(&sDT[lc * LT + 32 + 8 * lg]), oq);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const long r = t0 + 16 * wave + 4 * lg + e;
+            if (r < T) o[(((long)b * T + r) * H + h) * D + col0 + lc] = oq[e];
+        }
+    };
+
+    ScanFrags<OT, D> fa, fb;
+    scan_load<In, D>(fa, q, W, bh, 0, NC, T, H, b, h, slice, wave, lane);
+    for (int c = 0; c < NC; c += 2) {
+        if (c + 1 < NC) scan_load<In, D>(fb, q, W, bh, c + 1, NC, T, H, b, h, slice, wave, lane);
+        step(fa, c);
+        if (c + 1 >= NC) break;
+        if (c + 2 < NC) scan_load<In, D>(fa, q, W, bh, c + 2, NC, T, H, b, h, slice, wave, lane);
+        step(fb, c + 1);
     }
 
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int key = 16 * (wave * MT + m) + 4 * lg + e;
             state_out[(bh * D + key) * D + col0 + lc] = hs[m][e];
         }
-    }
 }
 
 template <typename In, int D>
 static size_t ws_bytes_t(int B, int T, int H) {
     using OT = typename OpType<In>::type;
     const long nc = (T + CH - 1) / CH;
-    return WsLayout<OT, D>::bytes_per_chunk * (size_t)B * H * nc;
+    return Ws<OT, D>::bytes_per_chunk * (size_t)B * H * nc;
 }
 
 size_t chunked_workspace_bytes(int B, int T, int H, int D, int dtype_bf16) {
@@ -427,9 +507,9 @@ static hipError_t launch_chunked_t(const void* q, const void* k, const void* v, 
                        static_cast<const In*>(v), g, beta, ws, T, H, NC, total);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_scan<In, D>), dim3(D / 16, H, B), dim3(256), 0, stream,
-                       static_cast<const In*>(q), static_cast<const In*>(k),
-                       static_cast<const void*>(ws), state_in, state_out, o, T, H, NC, total);
+    hipLaunchKernelGGL((chunk_scan<In, D>), dim3((unsigned)(B * H * (D / 16))), dim3(256), 0,
+                       stream, static_cast<const In*>(q), static_cast<const void*>(ws), state_in,
+                       state_out, o, T, H, B, NC, total);
     return hipGetLastError();
 }
 
