@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
             fq[kk] = r < n ? load8_in<OT>(q + ((((long)b * T + t0 + r) * H + h) * D + 32 * kk + 8 * lg))
                            : zero8<OT>();
     }
-    __syncthreads();
+    lds_sync();
 
     // Gram tiles: wave w does K K^T for row block w and Q K^T for row block 3 - w.
     {
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
             }
         }
     }
-    __syncthreads();
+    lds_sync();
 
     // Diagonal blocks: (I + A_bb)^{-1} by forward substitution in fp32, one
     // column per lane; stored as N_bb = (I + A_bb)^{-1} - I.
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
             }
         }
     }
-    __syncthreads();
+    lds_sync();
 
     // Blocked forward substitution for X = [W | U], 16-row blocks bb:
     //   Y_b = B_b - sum_{j<b} A_bj X_j ,   X_b = Y_b + N_bb Y_b .
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
                 for (int bb = 0; bb < 4; ++bb)
                     *reinterpret_cast<f32x4*>(Uf + ((bb * NTD + nt) * 64 + lane) * 4) = res[bb];
             } else {
-                __syncthreads();  // (first W tile only matters) every wave is done reading V
+                lds_sync();  // (first W tile only matters) every wave is done reading V
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
             }
         }
     }
-    __syncthreads();
+    lds_sync();
     OT* Wf = W.w + ch * Ws<OT, D>::wf;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(256) void chunk_scan(const In* __restrict__ q, cons
 #pragma unroll
         for (int m = 0; m < MT; ++m)
             st4<OT>(&sS[lc * LS + 16 * (wave * MT + m) + 4 * lg], cvt4<OT>(hs[m]));
-        __syncthreads();
+        lds_sync();
         // Delta = U - W H0 and Q H0, rows 16*wave + 4*lg + e; two accumulation chains each
         f32x4 d0 = f.u, d1 = zero4(), q0 = zero4(), q1 = zero4();
 #pragma unroll
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(256) void chunk_scan(const In* __restrict__ q, cons
         }
         st4<OT>(&sDT[lc * LT + 16 * wave + 4 * lg], cvt4<OT>(dl));
         st4<OT>(&sET[lc * LT + 16 * wave + 4 * lg], cvt4<OT>(edl));
-        __syncthreads();
+        lds_sync();
         // H = Gam_C H0 + K^T (e Delta)
         const float GC = __expf(f.gamC);
         const auto e0 = ld8<OT>(&sET[lc * LT + 8 * lg]);

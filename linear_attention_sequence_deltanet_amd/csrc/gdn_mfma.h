@@ -75,4 +75,13 @@ __device__ __forceinline__ typename Mfma<OT>::frag4 cvt4(f32x4 x) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations,
+// then meets the other waves.  Unlike __syncthreads() it does not wait for
+// outstanding global loads or stores, so register prefetches and output
+// stores stay in flight across it.  Global memory is never exchanged between
+// waves through these barriers.
+__device__ __forceinline__ void lds_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace gdn
