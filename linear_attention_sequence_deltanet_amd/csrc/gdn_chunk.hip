@@ -74,6 +74,42 @@ __device__ __forceinline__ typename Mfma<OT>::frag8 load8_in(const float* p) {
     return r;
 }
 
+// Raw (unconverted) eight-element input fragment: loads stay in flight until
+// the fragment is converted at its first use.
+template <typename In>
+struct Raw8;
+template <>
+struct Raw8<bf16_t> {
+    uint4 w;
+    __device__ __forceinline__ void load(const bf16_t* p) { w = *reinterpret_cast<const uint4*>(p); }
+    template <typename OT>
+    __device__ __forceinline__ typename Mfma<OT>::frag8 get() const {
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+        typename Mfma<OT>::frag8 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            r[2 * i] = static_cast<OT>(__uint_as_float(u[i] << 16));
+            r[2 * i + 1] = static_cast<OT>(__uint_as_float(u[i] & 0xffff0000u));
+        }
+        return r;
+    }
+};
+template <>
+struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const float4*>(p);
+        b = *reinterpret_cast<const float4*>(p + 4);
+    }
+    template <typename OT>
+    __device__ __forceinline__ typename Mfma<OT>::frag8 get() const {
+        typename Mfma<OT>::frag8 r;
+        r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+        r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+        return r;
+    }
+};
+
 template <typename OT>
 __device__ __forceinline__ typename Mfma<OT>::frag8 zero8() {
     typename Mfma<OT>::frag8 r;
@@ -326,10 +362,10 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
 // Wave w owns token rows [16w, 16w+16) of Delta and O, and key tiles
 // [w*D/64, (w+1)*D/64) of the state slice.
 // ---------------------------------------------------------------------------
-template <typename OT, int D>
+template <typename In, typename OT, int D>
 struct ScanFrags {
     typename Mfma<OT>::frag8 w[D / 32];   // -W rows of this wave
-    typename Mfma<OT>::frag8 q[D / 32];   // Q rows of this wave
+    Raw8<In> q[D / 32];                    // Q rows of this wave (raw input)
     typename Mfma<OT>::frag8 p[2];        // P rows of this wave
     typename Mfma<OT>::frag8 kt[D / 64][2];
     f32x4 u;                               // U (C layout)
@@ -338,7 +374,7 @@ struct ScanFrags {
 };
 
 template <typename In, int D>
-__device__ __forceinline__ void scan_load(ScanFrags<typename OpType<In>::type, D>& f,
+__device__ __forceinline__ void scan_load(ScanFrags<In, typename OpType<In>::type, D>& f,
                                           const In* __restrict__ q,
                                           const Ws<typename OpType<In>::type, D>& W, long bh,
                                           int c, int NC, int T, int H, int b, int h, int slice,
@@ -367,11 +403,11 @@ __device__ __forceinline__ void scan_load(ScanFrags<typename OpType<In>::type, D
                                           ((wave * (D / 16) + slice) * 64 + lane) * 4);
     f.gam = *reinterpret_cast<const f32x4*>(W.gam + ch * CH + 16 * wave + 4 * lg);
     f.gamC = W.gam[ch * CH + CH - 1];
-    const long r = t0 + 16 * wave + lc;
+    // rows past the end read the last row instead: their outputs are never stored
+    const long r = min(t0 + 16 * wave + lc, (long)T - 1);
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
-        f.q[kk] = r < T ? load8_in<OT>(q + ((((long)b * T + r) * H + h) * D + 32 * kk + 8 * lg))
-                        : zero8<OT>();
+        f.q[kk].load(q + ((((long)b * T + r) * H + h) * D + 32 * kk + 8 * lg));
 }
 
 template <typename In, int D>
@@ -417,7 +453,7 @@ __global__ __launch_bounds__(256) void chunk_scan(const In* __restrict__ q, cons
             hs[m][e] = state_in ? state_in[(bh * D + key) * D + col0 + lc] : 0.f;
         }
 
-    auto step = [&](const ScanFrags<OT, D>& f, int c) {
+    auto step = [&](const ScanFrags<In, OT, D>& f, int c) {
         const long t0 = (long)c * CH;
         // B operand copy of the state slice
 #pragma unroll
@@ -431,9 +467,9 @@ __global__ __launch_bounds__(256) void chunk_scan(const In* __restrict__ q, cons
             const auto s0 = ld8<OT>(&sS[lc * LS + 32 * kk + 8 * lg]);
             const auto s1 = ld8<OT>(&sS[lc * LS + 32 * (kk + 1) + 8 * lg]);
             d0 = M::k32(f.w[kk], s0, d0);
-            q0 = M::k32(f.q[kk], s0, q0);
+            q0 = M::k32(f.q[kk].template get<OT>(), s0, q0);
             d1 = M::k32(f.w[kk + 1], s1, d1);
-            q1 = M::k32(f.q[kk + 1], s1, q1);
+            q1 = M::k32(f.q[kk + 1].template get<OT>(), s1, q1);
         }
         const f32x4 dl = d0 + d1;
         f32x4 oq = q0 + q1, edl;
@@ -465,14 +501,16 @@ __global__ __launch_bounds__(256) void chunk_scan(const In* __restrict__ q, cons
         }
     };
 
-    ScanFrags<OT, D> fa, fb;
+    // Two register buffers in turn: chunk c + 1 loads while chunk c computes.  The
+    // loads are unconditional (past the last chunk they re-read it) so the
+    // compiler can count outstanding loads exactly and never drains them early.
+    ScanFrags<In, OT, D> fa, fb;
     scan_load<In, D>(fa, q, W, bh, 0, NC, T, H, b, h, slice, wave, lane);
     for (int c = 0; c < NC; c += 2) {
-        if (c + 1 < NC) scan_load<In, D>(fb, q, W, bh, c + 1, NC, T, H, b, h, slice, wave, lane);
+        scan_load<In, D>(fb, q, W, bh, min(c + 1, NC - 1), NC, T, H, b, h, slice, wave, lane);
         step(fa, c);
-        if (c + 1 >= NC) break;
-        if (c + 2 < NC) scan_load<In, D>(fa, q, W, bh, c + 2, NC, T, H, b, h, slice, wave, lane);
-        step(fb, c + 1);
+        scan_load<In, D>(fa, q, W, bh, min(c + 2, NC - 1), NC, T, H, b, h, slice, wave, lane);
+        if (c + 1 < NC) step(fb, c + 1);
     }
 
 #pragma unroll
