@@ -133,12 +133,16 @@ struct Ws {
     static constexpr size_t ktf = (size_t)(D / 16) * 2 * 64 * 8;
     static constexpr size_t uf = (size_t)4 * (D / 16) * 64 * 4;
     static constexpr size_t bytes_per_chunk = (wf + pf + ktf) * sizeof(OT) + (uf + CH) * 4;
+    // plus one sink of CH x D floats that absorbs output stores of rows past the
+    // end, so stores need no branches (its contents are never read)
+    static constexpr size_t sink_bytes = (size_t)CH * D * 4;
 
     OT* w;
     OT* p;
     OT* kt;
     float* u;
     float* gam;
+    float* sink;
     __device__ Ws(void* base, long nchunks_total) {
         char* b = static_cast<char*>(base);
         w = reinterpret_cast<OT*>(b);
@@ -150,6 +154,8 @@ struct Ws {
         u = reinterpret_cast<float*>(b);
         b += uf * 4 * nchunks_total;
         gam = reinterpret_cast<float*>(b);
+        b += (size_t)CH * 4 * nchunks_total;
+        sink = reinterpret_cast<float*>(b);
     }
 };
 
@@ -187,11 +193,35 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
     const long ch = ((long)b * H + h) * NC + c;
     Ws<OT, D> W(ws, nchunks_total);
 
+    // Issue every global load of the chunk first (rows past the end re-read the
+    // last row and are zeroed below), so they are all in flight together.
+    constexpr int NL = CH * D / 8 / 256;  // 8-element groups of k (and v) per thread
+    Raw8<In> rk[NL], rv[NL], rq[D / 32];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int idx = tid + 256 * i, r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+        const long off = (((long)b * T + t0 + min(r, n - 1)) * H + h) * D + c8;
+        rk[i].load(k + off);
+        rv[i].load(v + off);
+    }
+    const int mq = 3 - wave;  // Q rows of this wave's Q K^T block, straight to registers
+    {
+        const int r = min(16 * mq + lc, n - 1);
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+            rq[kk].load(q + ((((long)b * T + t0 + r) * H + h) * D + 32 * kk + 8 * lg));
+    }
+    float gv = 0.f, bv = 0.f;
+    if (wave == 0) {
+        const long tok = ((long)b * T + t0 + min(lane, n - 1)) * H + h;
+        gv = g[tok];
+        bv = beta[tok];
+    }
+
     // gates: gam = inclusive cumsum of g within the chunk (padded rows: g = b = 0)
     if (wave == 0) {
-        const long tok = ((long)b * T + t0 + lane) * H + h;
-        float gv = lane < n ? g[tok] : 0.f;
-        const float bv = lane < n ? beta[tok] : 0.f;
+        gv = lane < n ? gv : 0.f;
+        bv = lane < n ? bv : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float up = __shfl_up(gv, off, 64);
@@ -202,27 +232,20 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
         W.gam[ch * CH + lane] = gv;
     }
 
-    // k, v rows of the chunk into LDS as OT (zero rows past the end)
-    for (int idx = tid; idx < CH * D / 8; idx += 256) {
-        const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-        F8 fk = zero8<OT>(), fv = zero8<OT>();
-        if (r < n) {
-            const long off = (((long)b * T + t0 + r) * H + h) * D + c8;
-            fk = load8_in<OT>(k + off);
-            fv = load8_in<OT>(v + off);
-        }
-        *reinterpret_cast<F8*>(&sK[r * LD + c8]) = fk;
-        *reinterpret_cast<F8*>(&sV[r * LD + c8]) = fv;
-    }
-    // Q operand rows of this wave's Q K^T block straight from global memory
-    const int mq = 3 - wave;
-    F8 fq[D / 32];
-    {
-        const int r = 16 * mq + lc;
+    // k, v rows into LDS as OT (zero rows past the end)
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk)
-            fq[kk] = r < n ? load8_in<OT>(q + ((((long)b * T + t0 + r) * H + h) * D + 32 * kk + 8 * lg))
-                           : zero8<OT>();
+    for (int i = 0; i < NL; ++i) {
+        const int idx = tid + 256 * i, r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+        const F8 z = zero8<OT>();
+        const F8 fk = rk[i].template get<OT>(), fv = rv[i].template get<OT>();
+        *reinterpret_cast<F8*>(&sK[r * LD + c8]) = r < n ? fk : z;
+        *reinterpret_cast<F8*>(&sV[r * LD + c8]) = r < n ? fv : z;
+    }
+    F8 fq[D / 32];
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        const F8 x = rq[kk].template get<OT>();
+        fq[kk] = 16 * mq + lc < n ? x : zero8<OT>();
     }
     lds_sync();
 
@@ -496,21 +519,41 @@ __global__ __launch_bounds__(256) void chunk_scan(const In* __restrict__ q, cons
         if (wave >= 2) oq = M::k32(f.p[1], ld8<OT>(&sDT[lc * LT + 32 + 8 * lg]), oq);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const long r = t0 + 16 * wave + 4 * lg + e;
-            if (r < T) o[(((long)b * T + r) * H + h) * D + col0 + lc] = oq[e];
+            const int rr = 16 * wave + 4 * lg + e;
+            const long r = t0 + rr;
+            float* dst = r < T ? o + (((long)b * T + r) * H + h) * D + col0 + lc
+                               : W.sink + rr * D + col0 + lc;
+            *dst = oq[e];
         }
     };
 
-    // Two register buffers in turn: chunk c + 1 loads while chunk c computes.  The
+    // Register buffers in turn: chunk c + DEPTH loads while chunk c computes.  The
     // loads are unconditional (past the last chunk they re-read it) so the
-    // compiler can count outstanding loads exactly and never drains them early.
-    ScanFrags<In, OT, D> fa, fb;
-    scan_load<In, D>(fa, q, W, bh, 0, NC, T, H, b, h, slice, wave, lane);
-    for (int c = 0; c < NC; c += 2) {
-        scan_load<In, D>(fb, q, W, bh, min(c + 1, NC - 1), NC, T, H, b, h, slice, wave, lane);
-        step(fa, c);
-        scan_load<In, D>(fa, q, W, bh, min(c + 2, NC - 1), NC, T, H, b, h, slice, wave, lane);
-        if (c + 1 < NC) step(fb, c + 1);
+    // compiler counts outstanding loads exactly and never drains them early.
+    auto load = [&](ScanFrags<In, OT, D>& f, int c) {
+        scan_load<In, D>(f, q, W, bh, min(c, NC - 1), NC, T, H, b, h, slice, wave, lane);
+    };
+    if constexpr (sizeof(OT) == 2) {
+        ScanFrags<In, OT, D> fa, fb, fc;
+        load(fa, 0);
+        load(fb, 1);
+        for (int c = 0; c < NC; c += 3) {
+            load(fc, c + 2);
+            step(fa, c);
+            load(fa, c + 3);
+            if (c + 1 < NC) step(fb, c + 1);
+            load(fb, c + 4);
+            if (c + 2 < NC) step(fc, c + 2);
+        }
+    } else {
+        ScanFrags<In, OT, D> fa, fb;
+        load(fa, 0);
+        for (int c = 0; c < NC; c += 2) {
+            load(fb, c + 1);
+            step(fa, c);
+            load(fa, c + 2);
+            if (c + 1 < NC) step(fb, c + 1);
+        }
     }
 
 #pragma unroll
@@ -526,7 +569,7 @@ template <typename In, int D>
 static size_t ws_bytes_t(int B, int T, int H) {
     using OT = typename OpType<In>::type;
     const long nc = (T + CH - 1) / CH;
-    return Ws<OT, D>::bytes_per_chunk * (size_t)B * H * nc;
+    return Ws<OT, D>::bytes_per_chunk * (size_t)B * H * nc + Ws<OT, D>::sink_bytes;
 }
 
 size_t chunked_workspace_bytes(int B, int T, int H, int D, int dtype_bf16) {
