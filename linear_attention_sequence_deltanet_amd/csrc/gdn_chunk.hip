@@ -21,8 +21,8 @@
 //   chunk_prep  (one workgroup per chunk x head, fully parallel): gam, the Gram
 //               products K K^T and Q K^T, the triangular solve by 16-row
 //               blocks (diagonal blocks by forward substitution in fp32,
-//               off-diagonal corrections on matrix cores), and writes -W, U,
-//               P, K^T and gam to the workspace in the exact register-fragment
+//               off-diagonal corrections on matrix cores), and writes -W, Q,
+//               P, K^T, U and the decay factors to the workspace in the exact register-fragment
 //               order the scan consumes them (16-byte coalesced per lane).
 //   chunk_scan  (one workgroup per head x 16-column slice of the state,
 //               sequential over chunks): Delta, O and the state update, with
@@ -120,41 +120,47 @@ __device__ __forceinline__ typename Mfma<OT>::frag8 zero8() {
 
 // Workspace per (b, h, chunk), chunk-major, every block in lane order:
 //   Wf  [4 row blocks][D/32 k-steps][64 lanes][8]  OT   -W  (A operand of W H0)
+//   Qf  [4 row blocks][D/32 k-steps][64 lanes][8]  OT   Q   (A operand of Q H0)
 //   Pf  [4 row blocks][2 k-steps][64 lanes][8]     OT   P   (A operand of P Delta)
 //   KTf [D/16 key tiles][2 k-steps][64 lanes][8]   OT   K^T (A operand of K^T e Delta)
 //   Uf  [4 row blocks][D/16 col tiles][64 lanes][4] f32 U  (C layout)
-//   gam [64]                                       f32
+//   dec [4][64]                                    f32 Gam_r, exp(gam_C - gam_r), Gam_C
 // A-operand fragment (tile row block m, k-step kk) of lane (g, c) holds
 // X[16 m + c][32 kk + 8 g + j], j = 0..7; the C layout holds X[16 m + 4 g + e][16 n + c].
 template <typename OT, int D>
 struct Ws {
     static constexpr size_t wf = (size_t)4 * (D / 32) * 64 * 8;
+    static constexpr size_t qf = wf;
     static constexpr size_t pf = (size_t)4 * 2 * 64 * 8;
     static constexpr size_t ktf = (size_t)(D / 16) * 2 * 64 * 8;
     static constexpr size_t uf = (size_t)4 * (D / 16) * 64 * 4;
-    static constexpr size_t bytes_per_chunk = (wf + pf + ktf) * sizeof(OT) + (uf + CH) * 4;
+    static constexpr size_t df = (size_t)4 * CH;
+    static constexpr size_t bytes_per_chunk = (wf + qf + pf + ktf) * sizeof(OT) + (uf + df) * 4;
     // plus one sink of CH x D floats that absorbs output stores of rows past the
-    // end, so stores need no branches (its contents are never read)
+    // end, so stores need no per-lane branches (its contents are never read)
     static constexpr size_t sink_bytes = (size_t)CH * D * 4;
 
     OT* w;
+    OT* q;
     OT* p;
     OT* kt;
     float* u;
-    float* gam;
+    float* dec;
     float* sink;
     __device__ Ws(void* base, long nchunks_total) {
         char* b = static_cast<char*>(base);
         w = reinterpret_cast<OT*>(b);
         b += wf * sizeof(OT) * nchunks_total;
+        q = reinterpret_cast<OT*>(b);
+        b += qf * sizeof(OT) * nchunks_total;
         p = reinterpret_cast<OT*>(b);
         b += pf * sizeof(OT) * nchunks_total;
         kt = reinterpret_cast<OT*>(b);
         b += ktf * sizeof(OT) * nchunks_total;
         u = reinterpret_cast<float*>(b);
         b += uf * 4 * nchunks_total;
-        gam = reinterpret_cast<float*>(b);
-        b += (size_t)CH * 4 * nchunks_total;
+        dec = reinterpret_cast<float*>(b);
+        b += df * 4 * nchunks_total;
         sink = reinterpret_cast<float*>(b);
     }
 };
@@ -229,7 +235,12 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
         }
         sgam[lane] = gv;
         sbeta[lane] = bv;
-        W.gam[ch * CH + lane] = gv;
+        const float gC = __shfl(gv, 63, 64);
+        float* dec = W.dec + ch * Ws<OT, D>::df;
+        dec[lane] = __expf(gv);
+        dec[64 + lane] = __expf(gC - gv);
+        dec[128 + lane] = __expf(gC);
+        dec[192 + lane] = 0.f;
     }
 
     // k, v rows into LDS as OT (zero rows past the end)
@@ -242,10 +253,12 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
         *reinterpret_cast<F8*>(&sV[r * LD + c8]) = r < n ? fv : z;
     }
     F8 fq[D / 32];
+    OT* Qf = W.q + ch * Ws<OT, D>::qf;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
         const F8 x = rq[kk].template get<OT>();
         fq[kk] = 16 * mq + lc < n ? x : zero8<OT>();
+        *reinterpret_cast<F8*>(Qf + ((mq * (D / 32) + kk) * 64 + lane) * 8) = fq[kk];
     }
     lds_sync();
 
@@ -385,59 +398,53 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
 // Wave w owns token rows [16w, 16w+16) of Delta and O, and key tiles
 // [w*D/64, (w+1)*D/64) of the state slice.
 // ---------------------------------------------------------------------------
-template <typename In, typename OT, int D>
+template <typename OT, int D>
 struct ScanFrags {
     typename Mfma<OT>::frag8 w[D / 32];   // -W rows of this wave
-    Raw8<In> q[D / 32];                    // Q rows of this wave (raw input)
+    typename Mfma<OT>::frag8 q[D / 32];   // Q rows of this wave
     typename Mfma<OT>::frag8 p[2];        // P rows of this wave
     typename Mfma<OT>::frag8 kt[D / 64][2];
     f32x4 u;                               // U (C layout)
-    f32x4 gam;                             // gam of rows 16w + 4g + e
-    float gamC;
+    f32x4 gam, ed;                         // Gam_r and exp(gam_C - gam_r), rows 16w + 4g + e
+    float gc;                              // Gam_C
 };
 
-template <typename In, int D>
-__device__ __forceinline__ void scan_load(ScanFrags<In, typename OpType<In>::type, D>& f,
-                                          const In* __restrict__ q,
-                                          const Ws<typename OpType<In>::type, D>& W, long bh,
-                                          int c, int NC, int T, int H, int b, int h, int slice,
-                                          int wave, int lane) {
-    using OT = typename OpType<In>::type;
+// Loads of one chunk's operands.  `wave` is wave-uniform (scalar), so every
+// address is a scalar base plus the loop-invariant lane offset.
+template <typename OT, int D>
+__device__ __forceinline__ void scan_load(ScanFrags<OT, D>& f, const Ws<OT, D>& W, long ch,
+                                          int slice, int wave, int lane) {
     using F8 = typename Mfma<OT>::frag8;
-    const int lg = lane >> 4, lc = lane & 15;
-    const long ch = bh * NC + c;
-    const long t0 = (long)c * CH;
-    const OT* Wf = W.w + ch * Ws<OT, D>::wf;
+    const int lg = lane >> 4;
+    const OT* Wf = W.w + ch * Ws<OT, D>::wf + wave * (D / 32) * 512;
+    const OT* Qf = W.q + ch * Ws<OT, D>::qf + wave * (D / 32) * 512;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-        f.w[kk] = *reinterpret_cast<const F8*>(Wf + ((wave * (D / 32) + kk) * 64 + lane) * 8);
-    const OT* Pf = W.p + ch * Ws<OT, D>::pf;
+    for (int kk = 0; kk < D / 32; ++kk) {
+        f.w[kk] = *reinterpret_cast<const F8*>(Wf + kk * 512 + lane * 8);
+        f.q[kk] = *reinterpret_cast<const F8*>(Qf + kk * 512 + lane * 8);
+    }
+    const OT* Pf = W.p + ch * Ws<OT, D>::pf + wave * 2 * 512;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-        f.p[kk] = *reinterpret_cast<const F8*>(Pf + ((wave * 2 + kk) * 64 + lane) * 8);
-    const OT* KTf = W.kt + ch * Ws<OT, D>::ktf;
+    for (int kk = 0; kk < 2; ++kk) f.p[kk] = *reinterpret_cast<const F8*>(Pf + kk * 512 + lane * 8);
+    const OT* KTf = W.kt + ch * Ws<OT, D>::ktf + wave * (D / 64) * 2 * 512;
 #pragma unroll
     for (int m = 0; m < D / 64; ++m)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-            f.kt[m][kk] = *reinterpret_cast<const F8*>(
-                KTf + (((wave * (D / 64) + m) * 2 + kk) * 64 + lane) * 8);
+            f.kt[m][kk] = *reinterpret_cast<const F8*>(KTf + (m * 2 + kk) * 512 + lane * 8);
     f.u = *reinterpret_cast<const f32x4*>(W.u + ch * Ws<OT, D>::uf +
-                                          ((wave * (D / 16) + slice) * 64 + lane) * 4);
-    f.gam = *reinterpret_cast<const f32x4*>(W.gam + ch * CH + 16 * wave + 4 * lg);
-    f.gamC = W.gam[ch * CH + CH - 1];
-    // rows past the end read the last row instead: their outputs are never stored
-    const long r = min(t0 + 16 * wave + lc, (long)T - 1);
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-        f.q[kk].load(q + ((((long)b * T + r) * H + h) * D + 32 * kk + 8 * lg));
+                                          (wave * (D / 16) + slice) * 256 + lane * 4);
+    const float* dec = W.dec + ch * Ws<OT, D>::df;
+    f.gam = *reinterpret_cast<const f32x4*>(dec + 16 * wave + 4 * lg);
+    f.ed = *reinterpret_cast<const f32x4*>(dec + 64 + 16 * wave + 4 * lg);
+    f.gc = dec[128 + lane];
 }
 
 template <typename In, int D>
-__global__ __launch_bounds__(256) void chunk_scan(const In* __restrict__ q, const void* ws,
-                                                  const float* state_in, float* state_out,
-                                                  float* __restrict__ o, int T, int H, int B,
-                                                  int NC, long nchunks_total) {
+__global__ __launch_bounds__(256) void chunk_scan(const void* ws, const float* state_in,
+                                                  float* state_out, float* __restrict__ o,
+                                                  int T, int H, int B, int NC,
+                                                  long nchunks_total) {
     using OT = typename OpType<In>::type;
     using M = Mfma<OT>;
     constexpr int NS = D / 16;        // 16-column slices per head
@@ -461,7 +468,8 @@ __global__ __launch_bounds__(256) void chunk_scan(const In* __restrict__ q, cons
     }
     const int b = head / H, h = head % H;
     const long bh = head;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = lane >> 4, lc = lane & 15;
     const int col0 = slice * 16;
     Ws<OT, D> W(const_cast<void*>(ws), nchunks_total);
@@ -476,7 +484,13 @@ __global__ __launch_bounds__(256) void chunk_scan(const In* __restrict__ q, cons
             hs[m][e] = state_in ? state_in[(bh * D + key) * D + col0 + lc] : 0.f;
         }
 
-    auto step = [&](const ScanFrags<In, OT, D>& f, int c) {
+    // output offsets (elements) of this lane's rows 16*wave + 4*lg + e within a chunk
+    const long HD = (long)H * D;
+    int ooff[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ooff[e] = (int)((16 * wave + 4 * lg + e) * HD) + lc;
+
+    auto step = [&](const ScanFrags<OT, D>& f, int c) {
         const long t0 = (long)c * CH;
         // B operand copy of the state slice
 #pragma unroll
@@ -490,70 +504,55 @@ __global__ __launch_bounds__(256) void chunk_scan(const In* __restrict__ q, cons
             const auto s0 = ld8<OT>(&sS[lc * LS + 32 * kk + 8 * lg]);
             const auto s1 = ld8<OT>(&sS[lc * LS + 32 * (kk + 1) + 8 * lg]);
             d0 = M::k32(f.w[kk], s0, d0);
-            q0 = M::k32(f.q[kk].template get<OT>(), s0, q0);
+            q0 = M::k32(f.q[kk], s0, q0);
             d1 = M::k32(f.w[kk + 1], s1, d1);
-            q1 = M::k32(f.q[kk + 1].template get<OT>(), s1, q1);
+            q1 = M::k32(f.q[kk + 1], s1, q1);
         }
         const f32x4 dl = d0 + d1;
-        f32x4 oq = q0 + q1, edl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            edl[e] = __expf(f.gamC - f.gam[e]) * dl[e];
-            oq[e] *= __expf(f.gam[e]);
-        }
+        const f32x4 edl = f.ed * dl;
+        f32x4 oq = (q0 + q1) * f.gam;
         st4<OT>(&sDT[lc * LT + 16 * wave + 4 * lg], cvt4<OT>(dl));
         st4<OT>(&sET[lc * LT + 16 * wave + 4 * lg], cvt4<OT>(edl));
         lds_sync();
         // H = Gam_C H0 + K^T (e Delta)
-        const float GC = __expf(f.gamC);
         const auto e0 = ld8<OT>(&sET[lc * LT + 8 * lg]);
         const auto e1 = ld8<OT>(&sET[lc * LT + 32 + 8 * lg]);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            f32x4 acc = hs[m] * GC;
+            f32x4 acc = hs[m] * f.gc;
             acc = M::k32(f.kt[m][0], e0, acc);
             hs[m] = M::k32(f.kt[m][1], e1, acc);
         }
         // O = diag(Gam) Q H0 + P Delta (P is lower triangular)
         oq = M::k32(f.p[0], ld8<OT>(&sDT[lc * LT + 8 * lg]), oq);
         if (wave >= 2) oq = M::k32(f.p[1], ld8<OT>(&sDT[lc * LT + 32 + 8 * lg]), oq);
+        float* ob = o + ((long)b * T + t0) * HD + (long)h * D + col0;
+        if (t0 + CH <= T) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int rr = 16 * wave + 4 * lg + e;
-            const long r = t0 + rr;
-            float* dst = r < T ? o + (((long)b * T + r) * H + h) * D + col0 + lc
-                               : W.sink + rr * D + col0 + lc;
-            *dst = oq[e];
+            for (int e = 0; e < 4; ++e) ob[ooff[e]] = oq[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 16 * wave + 4 * lg + e;
+                float* dst = t0 + rr < T ? ob + ooff[e] : W.sink + rr * D + col0 + lc;
+                *dst = oq[e];
+            }
         }
     };
 
-    // Register buffers in turn: chunk c + DEPTH loads while chunk c computes.  The
+    // Register buffers in turn: chunk c + 1 loads while chunk c computes.  The
     // loads are unconditional (past the last chunk they re-read it) so the
     // compiler counts outstanding loads exactly and never drains them early.
-    auto load = [&](ScanFrags<In, OT, D>& f, int c) {
-        scan_load<In, D>(f, q, W, bh, min(c, NC - 1), NC, T, H, b, h, slice, wave, lane);
+    auto load = [&](ScanFrags<OT, D>& f, int c) {
+        scan_load<OT, D>(f, W, bh * NC + min(c, NC - 1), slice, wave, lane);
     };
-    if constexpr (sizeof(OT) == 2) {
-        ScanFrags<In, OT, D> fa, fb, fc;
-        load(fa, 0);
-        load(fb, 1);
-        for (int c = 0; c < NC; c += 3) {
-            load(fc, c + 2);
-            step(fa, c);
-            load(fa, c + 3);
-            if (c + 1 < NC) step(fb, c + 1);
-            load(fb, c + 4);
-            if (c + 2 < NC) step(fc, c + 2);
-        }
-    } else {
-        ScanFrags<In, OT, D> fa, fb;
-        load(fa, 0);
-        for (int c = 0; c < NC; c += 2) {
-            load(fb, c + 1);
-            step(fa, c);
-            load(fa, c + 2);
-            if (c + 1 < NC) step(fb, c + 1);
-        }
+    ScanFrags<OT, D> fa, fb;
+    load(fa, 0);
+    for (int c = 0; c < NC; c += 2) {
+        load(fb, c + 1);
+        step(fa, c);
+        load(fa, c + 2);
+        if (c + 1 < NC) step(fb, c + 1);
     }
 
 #pragma unroll
@@ -589,8 +588,8 @@ static hipError_t launch_chunked_t(const void* q, const void* k, const void* v, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_scan<In, D>), dim3((unsigned)(B * H * (D / 16))), dim3(256), 0,
-                       stream, static_cast<const In*>(q), static_cast<const void*>(ws), state_in,
-                       state_out, o, T, H, B, NC, total);
+                       stream, static_cast<const void*>(ws), state_in, state_out, o, T, H, B, NC,
+                       total);
     return hipGetLastError();
 }
 
