@@ -392,183 +392,387 @@ __global__ __launch_bounds__(256) void chunk_prep(const In* __restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// chunk_scan: 1-D grid of B*H*(D/16) workgroups, 256 threads; sequential over
-// the chunks.  All 16-column slices of one head run on the same XCD (blocks
-// are dealt to XCDs round-robin), so they share its L2 for the chunk operands.
-// Wave w owns token rows [16w, 16w+16) of Delta and O, and key tiles
-// [w*D/64, (w+1)*D/64) of the state slice.
+// Segment-parallel state chain.
+//
+// The chunks of each head are grouped into S segments of G chunks.  Over one
+// segment the state map is affine, H_end = M H_start + R (Appendix identity of
+// the chunked form: run the chain on the augmented state [H | P] from [0 | I]).
+//   chunk_chain<SUM>  (all segments in parallel) runs the chain from [0 | I] and
+//                     stores [R | M] for every segment;
+//   seg_combine       walks the segments in order, H_s = M_s H_{s-1} + R_s,
+//                     storing each segment's start state and the final state;
+//   chunk_chain<OUT>  (all segments in parallel) reruns every segment from its
+//                     true start state and writes the outputs.
+// With S = 1 only chunk_chain<OUT> runs, from state_in, and writes state_out.
+//
+// chunk_chain workgroup = (segment, head, DVT-column slice); wave w owns token
+// rows [16w, 16w+16) of Delta and O and key tiles [w*D/64, (w+1)*D/64) of the
+// state slice, which stays in registers (fp32) across the segment's chunks.
+// Slices of one (segment, head) run on one XCD (blocks are dealt to XCDs
+// round-robin) so they share its L2 for the chunk operands.
 // ---------------------------------------------------------------------------
-template <typename OT, int D>
-struct ScanFrags {
-    typename Mfma<OT>::frag8 w[D / 32];   // -W rows of this wave
-    typename Mfma<OT>::frag8 q[D / 32];   // Q rows of this wave
-    typename Mfma<OT>::frag8 p[2];        // P rows of this wave
-    typename Mfma<OT>::frag8 kt[D / 64][2];
-    f32x4 u;                               // U (C layout)
-    f32x4 gam, ed;                         // Gam_r and exp(gam_C - gam_r), rows 16w + 4g + e
-    float gc;                              // Gam_C
+enum { CHAIN_OUT = 0, CHAIN_SUM = 1 };
+
+template <typename OT, int D, int NT, bool OUT>
+struct ChainFrags {
+    typename Mfma<OT>::frag8 w[D / 32];            // -W rows of this wave
+    typename Mfma<OT>::frag8 q[OUT ? D / 32 : 1];  // Q rows of this wave
+    typename Mfma<OT>::frag8 p[OUT ? 2 : 1];       // P rows of this wave
+    typename Mfma<OT>::frag8 kt[D / 64][2];        // K^T key tiles of this wave
+    f32x4 u[NT];                                   // U (C layout), one per 16 columns
+    f32x4 gam, ed;  // Gam_r and exp(gam_C - gam_r), rows 16w + 4g + e
+    float gc;       // Gam_C
 };
 
 // Loads of one chunk's operands.  `wave` is wave-uniform (scalar), so every
-// address is a scalar base plus the loop-invariant lane offset.
-template <typename OT, int D>
-__device__ __forceinline__ void scan_load(ScanFrags<OT, D>& f, const Ws<OT, D>& W, long ch,
-                                          int slice, int wave, int lane) {
+// address is a scalar base plus a loop-invariant lane offset.
+template <typename OT, int D, int NT, bool OUT>
+__device__ __forceinline__ void chain_load(ChainFrags<OT, D, NT, OUT>& f, const Ws<OT, D>& W,
+                                           long ch, int tile0, bool has_u, int wave, int lane) {
     using F8 = typename Mfma<OT>::frag8;
     const int lg = lane >> 4;
     const OT* Wf = W.w + ch * Ws<OT, D>::wf + wave * (D / 32) * 512;
-    const OT* Qf = W.q + ch * Ws<OT, D>::qf + wave * (D / 32) * 512;
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-        f.w[kk] = *reinterpret_cast<const F8*>(Wf + kk * 512 + lane * 8);
-        f.q[kk] = *reinterpret_cast<const F8*>(Qf + kk * 512 + lane * 8);
+    for (int kk = 0; kk < D / 32; ++kk) f.w[kk] = *reinterpret_cast<const F8*>(Wf + kk * 512 + lane * 8);
+    if constexpr (OUT) {
+        const OT* Qf = W.q + ch * Ws<OT, D>::qf + wave * (D / 32) * 512;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+            f.q[kk] = *reinterpret_cast<const F8*>(Qf + kk * 512 + lane * 8);
+        const OT* Pf = W.p + ch * Ws<OT, D>::pf + wave * 2 * 512;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) f.p[kk] = *reinterpret_cast<const F8*>(Pf + kk * 512 + lane * 8);
     }
-    const OT* Pf = W.p + ch * Ws<OT, D>::pf + wave * 2 * 512;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) f.p[kk] = *reinterpret_cast<const F8*>(Pf + kk * 512 + lane * 8);
     const OT* KTf = W.kt + ch * Ws<OT, D>::ktf + wave * (D / 64) * 2 * 512;
 #pragma unroll
     for (int m = 0; m < D / 64; ++m)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
             f.kt[m][kk] = *reinterpret_cast<const F8*>(KTf + (m * 2 + kk) * 512 + lane * 8);
-    f.u = *reinterpret_cast<const f32x4*>(W.u + ch * Ws<OT, D>::uf +
-                                          (wave * (D / 16) + slice) * 256 + lane * 4);
+    const float* U = W.u + ch * Ws<OT, D>::uf + (wave * (D / 16) + tile0) * 256 + lane * 4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+        f.u[nt] = has_u ? *reinterpret_cast<const f32x4*>(U + nt * 256) : zero4();
     const float* dec = W.dec + ch * Ws<OT, D>::df;
     f.gam = *reinterpret_cast<const f32x4*>(dec + 16 * wave + 4 * lg);
     f.ed = *reinterpret_cast<const f32x4*>(dec + 64 + 16 * wave + 4 * lg);
     f.gc = dec[128 + lane];
 }
 
-template <typename In, int D>
-__global__ __launch_bounds__(256) void chunk_scan(const void* ws, const float* state_in,
-                                                  float* state_out, float* __restrict__ o,
-                                                  int T, int H, int B, int NC,
-                                                  long nchunks_total) {
+// Segment-level workspace behind the per-chunk blocks and the sink:
+//   summ  [S][B*H][D][2D] f32   [R | M] of each segment
+//   sst   [S][B*H][D][D]  f32   start state of each segment
+struct SegWs {
+    float* summ;
+    float* sst;
+};
+
+template <typename In, int D, int DVT, int MODE>
+__global__ __launch_bounds__(256) void chunk_chain(const void* ws, SegWs sw,
+                                                   const float* state_in, float* state_out,
+                                                   float* __restrict__ o, int T, int H, int B,
+                                                   int NC, int G, int S, long nchunks_total) {
     using OT = typename OpType<In>::type;
     using M = Mfma<OT>;
-    constexpr int NS = D / 16;        // 16-column slices per head
-    constexpr int MT = D / 64;        // key tiles per wave
-    constexpr int LS = D + 8;         // row stride of the OT state copy (per value column)
-    constexpr int LT = CH + 8;        // row stride of token-contiguous tiles
+    constexpr bool OUT = MODE == CHAIN_OUT;
+    constexpr int NT = DVT / 16;                  // 16-column tiles per workgroup
+    constexpr int NCOL = OUT ? D : 2 * D;         // columns of the chained state
+    constexpr int NSL = NCOL / DVT;               // slices per (segment, head)
+    constexpr int MT = D / 64;                    // key tiles per wave
+    constexpr int LS = D + 8;                     // row stride of the OT state copy
+    constexpr int LT = CH + 8;                    // row stride of token-contiguous tiles
 
-    __shared__ __align__(16) OT sS[16 * LS];   // state slice, S orientation [dv][dk]
-    __shared__ __align__(16) OT sDT[16 * LT];  // Delta^T [dv][t]
-    __shared__ __align__(16) OT sET[16 * LT];  // (e Delta)^T [dv][t]
+    __shared__ __align__(16) OT sS[DVT * LS];                 // state slice [col][key]
+    __shared__ __align__(16) OT sDT[OUT ? DVT * LT : 8];      // Delta^T [col][t]
+    __shared__ __align__(16) OT sET[DVT * LT];                // (e Delta)^T [col][t]
 
-    // XCD-aware placement: block L runs on XCD L % 8; keep a head's slices together.
-    const int L = blockIdx.x, G = B * H;
-    int head, slice;
-    if (G % 8 == 0) {
-        head = (L % 8) + 8 * ((L / 8) / NS);
-        slice = (L / 8) % NS;
+    const int L = blockIdx.x, BH = B * H, NG = BH * S;
+    int grp, slice;
+    if (NG % 8 == 0) {
+        grp = (L % 8) + 8 * ((L / 8) / NSL);
+        slice = (L / 8) % NSL;
     } else {
-        head = L / NS;
-        slice = L % NS;
+        grp = L / NSL;
+        slice = L % NSL;
     }
-    const int b = head / H, h = head % H;
-    const long bh = head;
+    const int bh = grp % BH, seg = grp / BH;
+    const int b = bh / H, h = bh % H;
+    const int c_begin = seg * G, c_end = min(c_begin + G, NC);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = lane >> 4, lc = lane & 15;
-    const int col0 = slice * 16;
+    const int col0 = slice * DVT;                 // first column (of NCOL)
+    const bool ident = !OUT && col0 >= D;         // columns of the transition part
+    const int tile0 = (col0 % D) / 16;            // first 16-column tile within D
     Ws<OT, D> W(const_cast<void*>(ws), nchunks_total);
 
-    // fp32 state slice in C layout: keys 16*(wave*MT + m) + 4*lg + e, column col0 + lc
+    // fp32 state slice in C layout: keys 16*(wave*MT + m) + 4*lg + e, columns col0 + 16 nt + lc
+    f32x4 hs[MT][NT];
+    {
+        const float* src = nullptr;
+        // one segment: straight from state_in; several: from the start states
+        // seg_combine stored (segment 0's is a copy of state_in, so an in-place
+        // state_out == state_in written by seg_combine is never read here)
+        if (OUT) src = S == 1 ? state_in : sw.sst + ((long)seg * BH + bh) * D * D;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int key = 16 * (wave * MT + m) + 4 * lg + e;
+                    const int col = col0 + 16 * nt + lc;
+                    float x = 0.f;
+                    if (OUT) {
+                        if (src) x = src[((long)(S == 1 ? bh : 0) * D + key) * D + col];
+                    } else if (ident) {
+                        x = key == col - D ? 1.f : 0.f;
+                    }
+                    hs[m][nt][e] = x;
+                }
+    }
+
+    const long HD = (long)H * D;
+    int ooff[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ooff[e] = (int)((16 * wave + 4 * lg + e) * HD) + lc;
+
+    auto step = [&](const ChainFrags<OT, D, NT, OUT>& f, int c) {
+        // B operand copy of the state slice
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                st4<OT>(&sS[(16 * nt + lc) * LS + 16 * (wave * MT + m) + 4 * lg], cvt4<OT>(hs[m][nt]));
+        lds_sync();
+        // Delta = U - W H0 (and Q H0), rows 16*wave + 4*lg + e
+        f32x4 dl[NT], oq[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4 d0 = f.u[nt], d1 = zero4(), q0 = zero4(), q1 = zero4();
+#pragma unroll
+            for (int kk = 0; kk < D / 32; kk += 2) {
+                const auto s0 = ld8<OT>(&sS[(16 * nt + lc) * LS + 32 * kk + 8 * lg]);
+                const auto s1 = ld8<OT>(&sS[(16 * nt + lc) * LS + 32 * (kk + 1) + 8 * lg]);
+                d0 = M::k32(f.w[kk], s0, d0);
+                d1 = M::k32(f.w[kk + 1], s1, d1);
+                if constexpr (OUT) {
+                    q0 = M::k32(f.q[kk], s0, q0);
+                    q1 = M::k32(f.q[kk + 1], s1, q1);
+                }
+            }
+            dl[nt] = d0 + d1;
+            oq[nt] = (q0 + q1) * f.gam;
+            if constexpr (OUT) st4<OT>(&sDT[(16 * nt + lc) * LT + 16 * wave + 4 * lg], cvt4<OT>(dl[nt]));
+            st4<OT>(&sET[(16 * nt + lc) * LT + 16 * wave + 4 * lg], cvt4<OT>(f.ed * dl[nt]));
+        }
+        lds_sync();
+        // H = Gam_C H0 + K^T (e Delta)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const auto e0 = ld8<OT>(&sET[(16 * nt + lc) * LT + 8 * lg]);
+            const auto e1 = ld8<OT>(&sET[(16 * nt + lc) * LT + 32 + 8 * lg]);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                f32x4 acc = hs[m][nt] * f.gc;
+                acc = M::k32(f.kt[m][0], e0, acc);
+                hs[m][nt] = M::k32(f.kt[m][1], e1, acc);
+            }
+        }
+        if constexpr (OUT) {
+            // O = diag(Gam) Q H0 + P Delta (P is lower triangular)
+            const long t0 = (long)c * CH;
+            float* ob = o + ((long)b * T + t0) * HD + (long)h * D + col0;
+            const bool full = t0 + CH <= T;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                oq[nt] = M::k32(f.p[0], ld8<OT>(&sDT[(16 * nt + lc) * LT + 8 * lg]), oq[nt]);
+                if (wave >= 2)
+                    oq[nt] = M::k32(f.p[1], ld8<OT>(&sDT[(16 * nt + lc) * LT + 32 + 8 * lg]), oq[nt]);
+                if (full) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ob[ooff[e] + 16 * nt] = oq[nt][e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int rr = 16 * wave + 4 * lg + e;
+                        float* dst = t0 + rr < T ? ob + ooff[e] + 16 * nt
+                                                 : W.sink + rr * D + col0 + 16 * nt + lc;
+                        *dst = oq[nt][e];
+                    }
+                }
+            }
+        }
+    };
+
+    // Register buffers in turn: chunk c + 1 loads while chunk c computes.  The
+    // loads are unconditional (past the segment's end they re-read its last
+    // chunk) so the compiler counts outstanding loads exactly.
+    const long ch0 = (long)bh * NC;
+    auto load = [&](ChainFrags<OT, D, NT, OUT>& f, int c) {
+        chain_load<OT, D, NT, OUT>(f, W, ch0 + min(c, c_end - 1), tile0, !ident, wave, lane);
+    };
+    ChainFrags<OT, D, NT, OUT> fa, fb;
+    load(fa, c_begin);
+    for (int c = c_begin; c < c_end; c += 2) {
+        load(fb, c + 1);
+        step(fa, c);
+        load(fa, c + 2);
+        if (c + 1 < c_end) step(fb, c + 1);
+    }
+
+    float* dst = nullptr;
+    long ld = D;
+    if (OUT) {
+        if (S == 1) dst = state_out + (long)bh * D * D;
+    } else {
+        dst = sw.summ + ((long)seg * BH + bh) * D * 2 * D;
+        ld = 2 * D;
+    }
+    if (dst) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int key = 16 * (wave * MT + m) + 4 * lg + e;
+                    dst[key * ld + col0 + 16 * nt + lc] = hs[m][nt][e];
+                }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// seg_combine: grid B*H*(D/16) workgroups of 256 threads, sequential over the
+// segments.  H_s = M_s H_{s-1} + R_s in fp32-grade arithmetic: both factors
+// are split into fp16 high and low parts and three products are accumulated.
+// Stores each segment's start state and the final state.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void seg_combine(SegWs sw, const float* state_in,
+                                                   float* state_out, int BH, int S) {
+    using M = Mfma<_Float16>;
+    using F8 = M::frag8;
+    constexpr int NS = D / 16, MT = D / 64, LS = D + 8;
+    __shared__ __align__(16) _Float16 sHi[16 * LS], sLo[16 * LS];
+
+    const int L = blockIdx.x;
+    int bh, slice;
+    if (BH % 8 == 0) {
+        bh = (L % 8) + 8 * ((L / 8) / NS);
+        slice = (L / 8) % NS;
+    } else {
+        bh = L / NS;
+        slice = L % NS;
+    }
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lg = lane >> 4, lc = lane & 15;
+    const int col = slice * 16 + lc;
+
     f32x4 hs[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int key = 16 * (wave * MT + m) + 4 * lg + e;
-            hs[m][e] = state_in ? state_in[(bh * D + key) * D + col0 + lc] : 0.f;
+            hs[m][e] = state_in ? state_in[((long)bh * D + key) * D + col] : 0.f;
         }
 
-    // output offsets (elements) of this lane's rows 16*wave + 4*lg + e within a chunk
-    const long HD = (long)H * D;
-    int ooff[4];
+    for (int s = 0; s < S; ++s) {
+        {
+            float* dst = sw.sst + ((long)s * BH + bh) * D * D;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ooff[e] = (int)((16 * wave + 4 * lg + e) * HD) + lc;
-
-    auto step = [&](const ScanFrags<OT, D>& f, int c) {
-        const long t0 = (long)c * CH;
-        // B operand copy of the state slice
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-            st4<OT>(&sS[lc * LS + 16 * (wave * MT + m) + 4 * lg], cvt4<OT>(hs[m]));
-        lds_sync();
-        // Delta = U - W H0 and Q H0, rows 16*wave + 4*lg + e; two accumulation chains each
-        f32x4 d0 = f.u, d1 = zero4(), q0 = zero4(), q1 = zero4();
-#pragma unroll
-        for (int kk = 0; kk < D / 32; kk += 2) {
-            const auto s0 = ld8<OT>(&sS[lc * LS + 32 * kk + 8 * lg]);
-            const auto s1 = ld8<OT>(&sS[lc * LS + 32 * (kk + 1) + 8 * lg]);
-            d0 = M::k32(f.w[kk], s0, d0);
-            q0 = M::k32(f.q[kk], s0, q0);
-            d1 = M::k32(f.w[kk + 1], s1, d1);
-            q1 = M::k32(f.q[kk + 1], s1, q1);
+                for (int e = 0; e < 4; ++e)
+                    dst[(16 * (wave * MT + m) + 4 * lg + e) * D + col] = hs[m][e];
         }
-        const f32x4 dl = d0 + d1;
-        const f32x4 edl = f.ed * dl;
-        f32x4 oq = (q0 + q1) * f.gam;
-        st4<OT>(&sDT[lc * LT + 16 * wave + 4 * lg], cvt4<OT>(dl));
-        st4<OT>(&sET[lc * LT + 16 * wave + 4 * lg], cvt4<OT>(edl));
-        lds_sync();
-        // H = Gam_C H0 + K^T (e Delta)
-        const auto e0 = ld8<OT>(&sET[lc * LT + 8 * lg]);
-        const auto e1 = ld8<OT>(&sET[lc * LT + 32 + 8 * lg]);
+        // B operand: the state split into high and low fp16 parts
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            f32x4 acc = hs[m] * f.gc;
-            acc = M::k32(f.kt[m][0], e0, acc);
-            hs[m] = M::k32(f.kt[m][1], e1, acc);
-        }
-        // O = diag(Gam) Q H0 + P Delta (P is lower triangular)
-        oq = M::k32(f.p[0], ld8<OT>(&sDT[lc * LT + 8 * lg]), oq);
-        if (wave >= 2) oq = M::k32(f.p[1], ld8<OT>(&sDT[lc * LT + 32 + 8 * lg]), oq);
-        float* ob = o + ((long)b * T + t0) * HD + (long)h * D + col0;
-        if (t0 + CH <= T) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ob[ooff[e]] = oq[e];
-        } else {
+            f32x4 lo;
+            typename M::frag4 hi;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int rr = 16 * wave + 4 * lg + e;
-                float* dst = t0 + rr < T ? ob + ooff[e] : W.sink + rr * D + col0 + lc;
-                *dst = oq[e];
+                hi[e] = static_cast<_Float16>(hs[m][e]);
+                lo[e] = hs[m][e] - static_cast<float>(hi[e]);
             }
+            st4<_Float16>(&sHi[lc * LS + 16 * (wave * MT + m) + 4 * lg], hi);
+            st4<_Float16>(&sLo[lc * LS + 16 * (wave * MT + m) + 4 * lg], cvt4<_Float16>(lo));
         }
-    };
-
-    // Register buffers in turn: chunk c + 1 loads while chunk c computes.  The
-    // loads are unconditional (past the last chunk they re-read it) so the
-    // compiler counts outstanding loads exactly and never drains them early.
-    auto load = [&](ScanFrags<OT, D>& f, int c) {
-        scan_load<OT, D>(f, W, bh * NC + min(c, NC - 1), slice, wave, lane);
-    };
-    ScanFrags<OT, D> fa, fb;
-    load(fa, 0);
-    for (int c = 0; c < NC; c += 2) {
-        load(fb, c + 1);
-        step(fa, c);
-        load(fa, c + 2);
-        if (c + 1 < NC) step(fb, c + 1);
+        lds_sync();
+        const float* sm = sw.summ + ((long)s * BH + bh) * D * 2 * D;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int key = 16 * (wave * MT + m);
+            f32x4 acc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = sm[(key + 4 * lg + e) * 2 * D + col];  // R_s
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const float* mrow = sm + (long)(key + lc) * 2 * D + D + 32 * kk + 8 * lg;
+                const float4 a0 = *reinterpret_cast<const float4*>(mrow);
+                const float4 a1 = *reinterpret_cast<const float4*>(mrow + 4);
+                const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                F8 ahi, alo;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    ahi[j] = static_cast<_Float16>(av[j]);
+                    alo[j] = static_cast<_Float16>(av[j] - static_cast<float>(ahi[j]));
+                }
+                const F8 bhi = ld8<_Float16>(&sHi[lc * LS + 32 * kk + 8 * lg]);
+                const F8 blo = ld8<_Float16>(&sLo[lc * LS + 32 * kk + 8 * lg]);
+                acc = M::k32(ahi, bhi, acc);
+                acc = M::k32(ahi, blo, acc);
+                acc = M::k32(alo, bhi, acc);
+            }
+            hs[m] = acc;
+        }
+        lds_sync();
     }
-
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int key = 16 * (wave * MT + m) + 4 * lg + e;
-            state_out[(bh * D + key) * D + col0 + lc] = hs[m][e];
-        }
+        for (int e = 0; e < 4; ++e)
+            state_out[((long)bh * D + 16 * (wave * MT + m) + 4 * lg + e) * D + col] = hs[m][e];
+}
+
+// ---------------------------------------------------------------------------
+// Host side: segmentation plan, workspace size, launches.
+// ---------------------------------------------------------------------------
+struct Plan {
+    int NC, S, G;
+};
+
+static Plan make_plan(int B, int T, int H, int D) {
+    Plan p;
+    p.NC = (T + CH - 1) / CH;
+    const long BH = (long)B * H;
+    // One segment when the heads alone give enough workgroups or the sequence
+    // is short; otherwise segments of about sqrt(NC / 2) chunks, balancing the
+    // parallel chain (G steps) against the sequential combine (S steps).
+    if (BH * (D / 16) >= 1024 || p.NC <= 16) {
+        p.S = 1;
+        p.G = p.NC;
+        return p;
+    }
+    int G = 1;
+    while ((long)G * G * 2 < p.NC) ++G;
+    G = G < 4 ? 4 : (G > 64 ? 64 : G);
+    p.G = G;
+    p.S = (p.NC + G - 1) / G;
+    return p;
 }
 
 template <typename In, int D>
 static size_t ws_bytes_t(int B, int T, int H) {
     using OT = typename OpType<In>::type;
-    const long nc = (T + CH - 1) / CH;
-    return Ws<OT, D>::bytes_per_chunk * (size_t)B * H * nc + Ws<OT, D>::sink_bytes;
+    const Plan p = make_plan(B, T, H, D);
+    const size_t BH = (size_t)B * H;
+    size_t bytes = Ws<OT, D>::bytes_per_chunk * BH * p.NC + Ws<OT, D>::sink_bytes;
+    if (p.S > 1) bytes += (size_t)p.S * BH * D * D * 4 * 3;  // summ (2 D^2) + sst (D^2)
+    return bytes;
 }
 
 size_t chunked_workspace_bytes(int B, int T, int H, int D, int dtype_bf16) {
@@ -580,16 +784,40 @@ template <typename In, int D>
 static hipError_t launch_chunked_t(const void* q, const void* k, const void* v, const float* g,
                                    const float* beta, const float* state_in, float* state_out,
                                    float* o, int B, int T, int H, void* ws, hipStream_t stream) {
-    const int NC = (T + CH - 1) / CH;
-    const long total = (long)B * H * NC;
-    hipLaunchKernelGGL((chunk_prep<In, D>), dim3(NC, H, B), dim3(256), 0, stream,
+    using OT = typename OpType<In>::type;
+    const Plan p = make_plan(B, T, H, D);
+    const long BH = (long)B * H;
+    const long total = BH * p.NC;
+    hipLaunchKernelGGL((chunk_prep<In, D>), dim3(p.NC, H, B), dim3(256), 0, stream,
                        static_cast<const In*>(q), static_cast<const In*>(k),
-                       static_cast<const In*>(v), g, beta, ws, T, H, NC, total);
+                       static_cast<const In*>(v), g, beta, ws, T, H, p.NC, total);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_scan<In, D>), dim3((unsigned)(B * H * (D / 16))), dim3(256), 0,
-                       stream, static_cast<const void*>(ws), state_in, state_out, o, T, H, B, NC,
-                       total);
+    SegWs sw{nullptr, nullptr};
+    if (p.S == 1) {
+        hipLaunchKernelGGL((chunk_chain<In, D, 16, CHAIN_OUT>), dim3((unsigned)(BH * (D / 16))),
+                           dim3(256), 0, stream, static_cast<const void*>(ws), sw, state_in,
+                           state_out, o, T, H, B, p.NC, p.G, 1, total);
+        return hipGetLastError();
+    }
+    char* base = static_cast<char*>(ws) + Ws<OT, D>::bytes_per_chunk * total + Ws<OT, D>::sink_bytes;
+    sw.summ = reinterpret_cast<float*>(base);
+    sw.sst = sw.summ + (size_t)p.S * BH * D * 2 * D;
+    constexpr int DVT = 64;
+    hipLaunchKernelGGL((chunk_chain<In, D, DVT, CHAIN_SUM>),
+                       dim3((unsigned)(BH * p.S * (2 * D / DVT))), dim3(256), 0, stream,
+                       static_cast<const void*>(ws), sw, state_in, state_out, o, T, H, B, p.NC,
+                       p.G, p.S, total);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((seg_combine<D>), dim3((unsigned)(BH * (D / 16))), dim3(256), 0, stream, sw,
+                       state_in, state_out, (int)BH, p.S);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_chain<In, D, DVT, CHAIN_OUT>),
+                       dim3((unsigned)(BH * p.S * (D / DVT))), dim3(256), 0, stream,
+                       static_cast<const void*>(ws), sw, state_in, state_out, o, T, H, B, p.NC,
+                       p.G, p.S, total);
     return hipGetLastError();
 }
 

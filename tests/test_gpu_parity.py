@@ -63,13 +63,35 @@ def test_edge_lengths_random_state(env, T, dtype, dim):
     _check("edge T=%d %s d=%d" % (T, dtype, dim), o, st, ro, rs, TOL[dtype])
 
 
-def test_long_memory_variant(env):
-    """Slow decay (a ~ 0.95): the carried state dominates; bf16, d=128."""
-    _note("case long memory T=1024")
-    d = gdn_inputs.random_inputs(1, 1024, 4, 128, 128, dtype="bf16", seed=77, g_shift=-3.0)
+@pytest.mark.parametrize("T", [1024, 5000])
+def test_long_memory_variant(env, T):
+    """Slow decay (a ~ 0.95): the carried state dominates; bf16, d=128.
+    T = 5000 runs the segment-parallel chain (several segments, ragged tail)."""
+    _note("case long memory T=%d" % T)
+    d = gdn_inputs.random_inputs(1, T, 4, 128, 128, dtype="bf16", seed=77, g_shift=-3.0,
+                                 state_std=0.1)
     o, st = _prefill(env, d)
     ro, rs = oracle_sequence(d)
     _check("long-memory", o, st, ro, rs, TOL["bf16"])
+
+
+@pytest.mark.parametrize("T", [1100, 3000])
+@pytest.mark.parametrize("dtype,dim", [("bf16", 128), ("f32", 64), ("bf16", 64), ("f32", 128)])
+def test_segmented_chain(env, T, dtype, dim):
+    """Long enough for several segments (segment summaries, sequential combine,
+    per-segment outputs), ragged last chunk and segment, random initial state,
+    in place."""
+    gdn, dev = env
+    import torch
+    _note("case segmented T=%d dtype=%s d=%d" % (T, dtype, dim))
+    d = gdn_inputs.random_inputs(1, T, 2, dim, dim, dtype=dtype, seed=T + dim, state_std=0.2)
+    x = stage(d, dev)
+    st = x["state0"].clone()
+    o, _ = gdn.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], st, state_out=st)
+    torch.cuda.synchronize()
+    ro, rs = oracle_sequence(d)
+    _check("segmented T=%d %s d=%d" % (T, dtype, dim), o.cpu().numpy(), st.cpu().numpy(), ro,
+           rs, TOL[dtype])
 
 
 def test_prefill8k_full(env):
