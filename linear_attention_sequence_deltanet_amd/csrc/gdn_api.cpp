@@ -73,8 +73,11 @@ int run_prefill(const void* q, const void* k, const void* v, int dtype, const fl
                 const float* beta, const float* state_in, float* state_out, float* o, int B,
                 int T, int H, int dk, void* ws, size_t ws_bytes, hipStream_t stream) {
     (void)ws_bytes;
-    return launch_status(gdn::launch_chunked(q, k, v, dtype == GDN_BF16, g, beta, state_in,
-                                             state_out, o, B, T, H, dk, ws, stream));
+    if (dtype == GDN_BF16)
+        return launch_status(gdn::launch_fused(q, k, v, g, beta, state_in, state_out, o, B, T, H,
+                                               dk, ws, stream));
+    return launch_status(gdn::launch_chunked(q, k, v, 0, g, beta, state_in, state_out, o, B, T,
+                                             H, dk, ws, stream));
 }
 
 }  // namespace
@@ -100,7 +103,8 @@ const char* gdn_status_str(int status) {
 
 size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype) {
     if (check_sizes(B, T, H, dk, dv, dtype) != GDN_OK) return 0;
-    return gdn::chunked_workspace_bytes(B, T, H, dk, dtype == GDN_BF16);
+    if (dtype == GDN_BF16) return gdn::fused_workspace_bytes(B, T, H, dk);
+    return gdn::chunked_workspace_bytes(B, T, H, dk, 0);
 }
 
 int gdn_prefill(const void* q, const void* k, const void* v, int dtype, const float* g,

@@ -821,6 +821,18 @@ static hipError_t launch_chunked_t(const void* q, const void* k, const void* v, 
     return hipGetLastError();
 }
 
+hipError_t launch_seg_combine(float* summ, float* sst, const float* state_in, float* state_out,
+                              int BH, int S, int D, hipStream_t stream) {
+    const SegWs sw{summ, sst};
+    if (D == 64)
+        hipLaunchKernelGGL((seg_combine<64>), dim3((unsigned)(BH * 4)), dim3(256), 0, stream, sw,
+                           state_in, state_out, BH, S);
+    else
+        hipLaunchKernelGGL((seg_combine<128>), dim3((unsigned)(BH * 8)), dim3(256), 0, stream, sw,
+                           state_in, state_out, BH, S);
+    return hipGetLastError();
+}
+
 hipError_t launch_chunked(const void* q, const void* k, const void* v, int dtype_bf16,
                           const float* g, const float* beta, const float* state_in,
                           float* state_out, float* o, int B, int T, int H, int D, void* ws,

@@ -22,4 +22,15 @@ hipError_t launch_chunked(const void* q, const void* k, const void* v, int dtype
                           float* state_out, float* o, int B, int T, int H, int D, void* ws,
                           hipStream_t stream);
 
+// Sequential combine of per-segment affine maps [R | M] ([S][BH][D][2D] f32):
+// writes every segment's start state to sst ([S][BH][D][D]) and the final state.
+hipError_t launch_seg_combine(float* summ, float* sst, const float* state_in, float* state_out,
+                              int BH, int S, int D, hipStream_t stream);
+
+// Fused bf16 prefill (chunk operands built in LDS, segment-parallel state chain).
+size_t fused_workspace_bytes(int B, int T, int H, int D);
+hipError_t launch_fused(const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const float* state_in, float* state_out, float* o,
+                        int B, int T, int H, int D, void* ws, hipStream_t stream);
+
 }  // namespace gdn
