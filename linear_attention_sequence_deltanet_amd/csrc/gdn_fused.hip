@@ -67,35 +67,48 @@ struct FusedSeg {
     float* sink;   // [64][D]         absorbs output stores of rows past the end
 };
 
+// Row-contiguous [rows][64] token tiles written by transposition (K^T, V^T):
+// 8-token groups are XOR-permuted by row so the transposing stores of 16
+// different rows do not fall into one LDS bank; reads of aligned 4- or 8-token
+// groups stay contiguous.
+template <int LA>
+__device__ __forceinline__ int tsw(int row, int t) {
+    return row * LA + (t ^ (((row >> 3) & 7) << 3));
+}
+
 template <int D, bool OUT>
-__global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
+__global__ __launch_bounds__(256) void gdn_fused(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, FusedSeg fs,
     const float* state_in, float* state_out, float* __restrict__ o, int T, int H, int B, int NC,
     int G, int S) {
-    constexpr int NW = D / 16;            // waves; wave w owns column tile w (and D/16 + w in SUM)
-    constexpr int NTH = 64 * NW;
-    constexpr int TPW = OUT ? 1 : 2;      // 16-column state tiles per wave
+    constexpr int NW = 4, NTH = 256;
+    constexpr int TPW = D / 64;           // 16-column state tiles per wave
     constexpr int MT = D / 16;            // key tiles of the state
     constexpr int LD = D + 8;             // row stride of [64][D] tiles
     constexpr int LA = FC + 8;            // row stride of [*][64] tiles
     constexpr int NL = FC * D / 8 / NTH;  // 8-element input groups per thread per tensor
     constexpr int STG = 2 * 16 * LA > 16 * LD ? 2 * 16 * LA : 16 * LD;  // staging per tile
-    static_assert(NL == 2, "tiling");
 
     __shared__ __align__(16) _Float16 sK[FC * LD];
     __shared__ __align__(16) _Float16 sQ[OUT ? FC * LD : 8];
-    __shared__ __align__(16) _Float16 sVW[FC * LD];     // V, then -W
-    __shared__ __align__(16) _Float16 sKT[D * LA];      // K^T [key][t]
+    __shared__ __align__(16) _Float16 sW[FC * LD];      // -W [t][key]
+    __shared__ __align__(16) _Float16 sKT[D * LA];      // K^T [key][t] (swizzled)
+    __shared__ __align__(16) _Float16 sVT[D * LA];      // V^T [col][t] (swizzled)
     __shared__ __align__(16) _Float16 sA[FC * LA];      // -A off-diagonal, (T_bb - I) diagonal blocks
     __shared__ __align__(16) _Float16 sP[OUT ? FC * LA : 8];
     __shared__ __align__(16) _Float16 sStg[NW * TPW * STG];  // per-wave staging
-    __shared__ float sAd[4][16][17];
-    __shared__ float sgam[FC], sbeta[FC], sGam[FC], sE[FC];
+    __shared__ __align__(16) float sAd[4][16][16];
+    __shared__ __align__(16) float sgam[FC], sbeta[FC], sGam[FC], sE[FC], sBG[FC];
     __shared__ float sGC;
 
+    // SUM runs two parts per (segment, head): part 0 the value columns (R),
+    // part 1 the identity columns (M), which need neither V nor U.
     const int BH = B * H;
-    const int bh = blockIdx.x % BH, seg = blockIdx.x / BH;
+    const int part = OUT ? 0 : (int)(blockIdx.x / (BH * S));
+    const int blk = OUT ? (int)blockIdx.x : (int)(blockIdx.x % (BH * S));
+    const int bh = blk % BH, seg = blk / BH;
+    const bool idn = part == 1;
     const int b = bh / H, h = bh % H;
     const int c_begin = seg * G, c_end = min(c_begin + G, NC);
     const int tid = threadIdx.x, lane = tid & 63;
@@ -103,8 +116,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     const int lg = lane >> 4, lc = lane & 15;
     const long HD = (long)H * D;
     _Float16* stg = sStg + wave * TPW * STG;
+    const int colw = 16 * TPW * wave;  // first state column of this wave
 
-    // ---- state tiles (fp32, C layout): key 16 m + 4 lg + e, column tile j of this wave
+    // ---- state tiles (fp32, C layout): key 16 m + 4 lg + e, column colw + 16 j + lc
     f32x4 hs[TPW][MT];
     {
         const float* src = nullptr;
@@ -116,13 +130,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int key = 16 * m + 4 * lg + e;
-                    const int col = 16 * (wave + j * NW) + lc;  // of D (OUT) or 2D (SUM)
+                    const int key = 16 * m + 4 * lg + e, col = colw + 16 * j + lc;
                     float x = 0.f;
                     if (OUT) {
                         if (src) x = src[key * D + col];
-                    } else if (j == 1) {
-                        x = key == col - D ? 1.f : 0.f;
+                    } else if (idn) {
+                        x = key == col ? 1.f : 0.f;
                     }
                     hs[j][m][e] = x;
                 }
@@ -140,7 +153,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             const long off = (((long)b * T + t0 + min(r, n - 1)) * H + h) * D + c8;
             if (OUT) rq[i] = *reinterpret_cast<const uint4*>(q + off);
             rk[i] = *reinterpret_cast<const uint4*>(k + off);
-            rv[i] = *reinterpret_cast<const uint4*>(v + off);
+            if (!idn) rv[i] = *reinterpret_cast<const uint4*>(v + off);
         }
         if (wave == 0) {
             const long tok = ((long)b * T + t0 + min(lane, n - 1)) * H + h;
@@ -150,26 +163,26 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     };
     issue_loads(c_begin);
 
-    int ooff[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ooff[e] = (int)((4 * lg + e) * HD) + 16 * wave + lc;
-
     for (int c = c_begin; c < c_end; ++c) {
         const long t0 = (long)c * FC;
         const int n = (int)min((long)FC, (long)T - t0);
         lds_sync();  // previous chunk's operands are no longer read
 
-        // ---- inputs into LDS (f16), K^T, gates
+        // ---- inputs into LDS (f16): row-major K, Q; transposed K^T, V^T; gates
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int idx = tid + NTH * i, r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
             const bool ok = r < n;
             const H8 fk = ok ? bf16x8_to_f16(rk[i]) : zero_h8();
             *reinterpret_cast<H8*>(&sK[r * LD + c8]) = fk;
-            *reinterpret_cast<H8*>(&sVW[r * LD + c8]) = ok ? bf16x8_to_f16(rv[i]) : zero_h8();
             if (OUT) *reinterpret_cast<H8*>(&sQ[r * LD + c8]) = ok ? bf16x8_to_f16(rq[i]) : zero_h8();
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sKT[(c8 + j) * LA + r] = fk[j];
+            for (int j = 0; j < 8; ++j) sKT[tsw<LA>(c8 + j, r)] = fk[j];
+            if (!idn) {
+                const H8 fv = ok ? bf16x8_to_f16(rv[i]) : zero_h8();
+#pragma unroll
+                for (int j = 0; j < 8; ++j) sVT[tsw<LA>(c8 + j, r)] = fv[j];
+            }
         }
         if (wave == 0) {
             float gv = lane < n ? rg : 0.f;
@@ -180,59 +193,61 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 if (lane >= off) gv += up;
             }
             const float gC = __shfl(gv, 63, 64);
+            const float eg = __expf(gv);
             sgam[lane] = gv;
             sbeta[lane] = bv;
-            sGam[lane] = __expf(gv);
+            sGam[lane] = eg;
+            sBG[lane] = bv * eg;
             sE[lane] = __expf(gC - gv);
             if (lane == 0) sGC = __expf(gC);
         }
         if (c + 1 < c_end) issue_loads(c + 1);
         lds_sync();
 
-        // ---- Gram tiles: KK^T lower (10), and for OUT QK^T lower (10) + zero upper (6)
+        // ---- Gram tiles: wave w does K K^T for row block w (tiles 0..w) and,
+        // for OUT, Q K^T for row block 3 - w (tiles 0..3, upper ones zero).
         {
-            constexpr int NKK = 10, NTILE = OUT ? 26 : 10;
-            for (int tt = wave; tt < NTILE; tt += NW) {
-                int mi, ni, kind;  // kind 0: KK^T, 1: QK^T, 2: zero upper tile of P
-                if (tt < NKK) {
-                    kind = 0;
-                    mi = tt < 1 ? 0 : tt < 3 ? 1 : tt < 6 ? 2 : 3;
-                    ni = tt - (mi * (mi + 1)) / 2;
-                } else if (tt < 2 * NKK) {
-                    kind = 1;
-                    const int u = tt - NKK;
-                    mi = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
-                    ni = u - (mi * (mi + 1)) / 2;
-                } else {
-                    kind = 2;
-                    const int u = tt - 2 * NKK;  // upper tiles (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-                    mi = u < 3 ? 0 : u < 5 ? 1 : 2;
-                    ni = mi == 0 ? 1 + u : mi == 1 ? u - 1 : 3;
-                }
-                if (kind == 2) {
+            const int mk = wave;
+            H8 af[D / 32];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        sP[(16 * mi + 4 * lg + e) * LA + 16 * ni + lc] = _Float16(0);
-                    continue;
-                }
-                const _Float16* X = kind == 0 ? sK : sQ;
+            for (int kk = 0; kk < D / 32; ++kk) af[kk] = ld8<_Float16>(&sK[(16 * mk + lc) * LD + 32 * kk + 8 * lg]);
+            const f32x4 gr = *reinterpret_cast<const f32x4*>(&sgam[16 * mk + 4 * lg]);
+            const f32x4 br = *reinterpret_cast<const f32x4*>(&sbeta[16 * mk + 4 * lg]);
+            for (int ni = 0; ni <= mk; ++ni) {
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int kk = 0; kk < D / 32; ++kk)
-                    acc = MF::k32(ld8<_Float16>(&X[(16 * mi + lc) * LD + 32 * kk + 8 * lg]),
-                                  ld8<_Float16>(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]), acc);
+                    acc = MF::k32(af[kk], ld8<_Float16>(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]), acc);
                 const int i = 16 * ni + lc;
+                const float gi = sgam[i];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * mi + 4 * lg + e;
-                    if (kind == 0) {
-                        const float a = i < r ? sbeta[r] * __expf(sgam[r] - sgam[i]) * acc[e] : 0.f;
-                        if (ni == mi)
-                            sAd[mi][r & 15][i & 15] = a;
-                        else
-                            sA[r * LA + i] = static_cast<_Float16>(-a);
-                    } else {
-                        const float pv = i <= r ? __expf(sgam[r] - sgam[i]) * acc[e] : 0.f;
+                    const int r = 16 * mk + 4 * lg + e;
+                    const float a = i < r ? br[e] * __expf(gr[e] - gi) * acc[e] : 0.f;
+                    if (ni == mk)
+                        sAd[mk][4 * lg + e][lc] = a;
+                    else
+                        sA[r * LA + i] = static_cast<_Float16>(-a);
+                }
+            }
+            if (OUT) {
+                const int mq = 3 - wave;
+#pragma unroll
+                for (int kk = 0; kk < D / 32; ++kk) af[kk] = ld8<_Float16>(&sQ[(16 * mq + lc) * LD + 32 * kk + 8 * lg]);
+                const f32x4 gq = *reinterpret_cast<const f32x4*>(&sgam[16 * mq + 4 * lg]);
+                for (int ni = 0; ni < 4; ++ni) {
+                    f32x4 acc = zero4();
+                    if (ni <= mq) {
+#pragma unroll
+                        for (int kk = 0; kk < D / 32; ++kk)
+                            acc = MF::k32(af[kk], ld8<_Float16>(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]), acc);
+                    }
+                    const int i = 16 * ni + lc;
+                    const float gi = sgam[i];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * mq + 4 * lg + e;
+                        const float pv = i <= r ? __expf(gq[e] - gi) * acc[e] : 0.f;
                         sP[r * LA + i] = static_cast<_Float16>(pv);
                     }
                 }
@@ -240,16 +255,25 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         }
         lds_sync();
 
-        // ---- diagonal blocks: (I + A_bb)^{-1} by fp32 forward substitution (waves 0-3)
-        if (wave < 4 && lane < 16) {
+        // ---- diagonal blocks: (I + A_bb)^{-1} by fp32 forward substitution
+        if (lane < 16) {
             const int cc = lane;
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float s = (r == cc) ? 1.f : 0.f;
+                float a[16];
 #pragma unroll
-                for (int i = 0; i < r; ++i) s -= sAd[wave][r][i] * x[i];
-                x[r] = s;
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 t4 = *reinterpret_cast<const f32x4*>(&sAd[wave][r][4 * q4]);
+                    a[4 * q4] = t4[0]; a[4 * q4 + 1] = t4[1]; a[4 * q4 + 2] = t4[2]; a[4 * q4 + 3] = t4[3];
+                }
+                float s0 = (r == cc) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+                for (int i = 0; i < r; ++i) {
+                    if (i & 1) s1 -= a[i] * x[i];
+                    else s0 -= a[i] * x[i];
+                }
+                x[r] = s0 + s1;
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r)
@@ -257,21 +281,20 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         }
         lds_sync();
 
-        // ---- blocked solve, right-hand side in fp32:
+        // ---- blocked solve with the right-hand side in fp32:
         //   Y_b = B_b - sum_{j<b} A_bj X_j,  X_b = Y_b + N_bb Y_b
-        // U tile `wave` stays in registers; -W tile `wave` goes to LDS (over V).
-        auto solve = [&](bool is_w, f32x4 res[4]) {
-            const int col = 16 * wave + lc;
+        // U tiles of this wave's columns stay in registers; -W tiles go to LDS.
+        auto solve = [&](bool is_w, int col, f32x4 res[4]) {
             H4 xh[4];
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
+                const f32x4 f4 = *reinterpret_cast<const f32x4*>(is_w ? &sBG[16 * bb + 4 * lg]
+                                                                      : &sbeta[16 * bb + 4 * lg]);
+                const H4 x4 = ld4<_Float16>(is_w ? &sKT[tsw<LA>(col, 16 * bb + 4 * lg)]
+                                                 : &sVT[tsw<LA>(col, 16 * bb + 4 * lg)]);
                 f32x4 acc;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * bb + 4 * lg + e;
-                    acc[e] = is_w ? sbeta[r] * sGam[r] * static_cast<float>(sK[r * LD + col])
-                                  : sbeta[r] * static_cast<float>(sVW[r * LD + col]);
-                }
+                for (int e = 0; e < 4; ++e) acc[e] = f4[e] * static_cast<float>(x4[e]);
 #pragma unroll
                 for (int j = 0; j < bb; ++j)
                     acc = MF::k16(ld4<_Float16>(&sA[(16 * bb + lc) * LA + 16 * j + 4 * lg]), xh[j], acc);
@@ -281,86 +304,116 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 res[bb] = acc;
             }
         };
-        f32x4 u[4];
-        solve(false, u);
-        lds_sync();  // V fully read
-        {
+        f32x4 u[TPW][4];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            if (!idn) {
+                solve(false, colw + 16 * j + lc, u[j]);
+            } else {
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) u[j][bb] = zero4();
+            }
             f32x4 wres[4];
-            solve(true, wres);
-            const int col = 16 * wave + lc;
+            const int col = colw + 16 * j + lc;
+            solve(true, col, wres);
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    sVW[(16 * bb + 4 * lg + e) * LD + col] = static_cast<_Float16>(-wres[bb][e]);
+                    sW[(16 * bb + 4 * lg + e) * LD + col] = static_cast<_Float16>(-wres[bb][e]);
         }
         lds_sync();  // -W complete
 
-        // ---- state update for this wave's column tiles (no workgroup barrier)
-        const float GC = sGC;
+        // ---- state update for this wave's columns (no workgroup barrier)
+        // fp16 copy of the state tiles, [col][key]
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            _Float16* st = stg + j * STG;
-            // fp16 copy of the state tile, [col][key]
+        for (int j = 0; j < TPW; ++j)
 #pragma unroll
-            for (int m = 0; m < MT; ++m) st4<_Float16>(&st[lc * LD + 16 * m + 4 * lg], cvt4<_Float16>(hs[j][m]));
-            f32x4 dl[4], oq[4];
+            for (int m = 0; m < MT; ++m)
+                st4<_Float16>(&stg[j * STG + lc * LD + 16 * m + 4 * lg], cvt4<_Float16>(hs[j][m]));
+        f32x4 dl[TPW][4], oq[TPW][4];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                dl[mt] = (j == 0) ? u[mt] : zero4();
-                oq[mt] = zero4();
+                dl[j][mt] = u[j][mt];
+                oq[j][mt] = zero4();
             }
 #pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                const H8 bs = ld8<_Float16>(&st[lc * LD + 32 * kk + 8 * lg]);
+        for (int kk = 0; kk < D / 32; ++kk) {
+            H8 bs[TPW];
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    dl[mt] = MF::k32(ld8<_Float16>(&sVW[(16 * mt + lc) * LD + 32 * kk + 8 * lg]), bs, dl[mt]);
-                    if (OUT)
-                        oq[mt] = MF::k32(ld8<_Float16>(&sQ[(16 * mt + lc) * LD + 32 * kk + 8 * lg]), bs, oq[mt]);
+            for (int j = 0; j < TPW; ++j) bs[j] = ld8<_Float16>(&stg[j * STG + lc * LD + 32 * kk + 8 * lg]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const H8 aw = ld8<_Float16>(&sW[(16 * mt + lc) * LD + 32 * kk + 8 * lg]);
+#pragma unroll
+                for (int j = 0; j < TPW; ++j) dl[j][mt] = MF::k32(aw, bs[j], dl[j][mt]);
+                if (OUT) {
+                    const H8 aq = ld8<_Float16>(&sQ[(16 * mt + lc) * LD + 32 * kk + 8 * lg]);
+#pragma unroll
+                    for (int j = 0; j < TPW; ++j) oq[j][mt] = MF::k32(aq, bs[j], oq[j][mt]);
                 }
             }
-            // Delta^T and (e Delta)^T staged as [col][t] (over the state copy)
-            _Float16* sD = st;
-            _Float16* sEt = st + 16 * LA;
+        }
+        // Delta^T and (e Delta)^T staged as [col][t] over the state copy
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                f32x4 ed;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ed[e] = sE[16 * mt + 4 * lg + e] * dl[mt][e];
-                if (OUT) st4<_Float16>(&sD[lc * LA + 16 * mt + 4 * lg], cvt4<_Float16>(dl[mt]));
-                st4<_Float16>(&sEt[lc * LA + 16 * mt + 4 * lg], cvt4<_Float16>(ed));
+                const f32x4 ed = *reinterpret_cast<const f32x4*>(&sE[16 * mt + 4 * lg]) * dl[j][mt];
+                if (OUT) st4<_Float16>(&stg[j * STG + lc * LA + 16 * mt + 4 * lg], cvt4<_Float16>(dl[j][mt]));
+                st4<_Float16>(&stg[j * STG + 16 * LA + lc * LA + 16 * mt + 4 * lg], cvt4<_Float16>(ed));
             }
-            if (OUT) {
-                // O = diag(Gam) Q H0 + P Delta
-                const H8 d0 = ld8<_Float16>(&sD[lc * LA + 8 * lg]);
-                const H8 d1 = ld8<_Float16>(&sD[lc * LA + 32 + 8 * lg]);
-                float* ob = o + ((long)b * T + t0) * HD + (long)h * D;
-                const bool full = n == FC;
+        if (OUT) {
+            // O = diag(Gam) Q H0 + P Delta
+            H8 d0[TPW], d1[TPW];
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    f32x4 acc;
+            for (int j = 0; j < TPW; ++j) {
+                d0[j] = ld8<_Float16>(&stg[j * STG + lc * LA + 8 * lg]);
+                d1[j] = ld8<_Float16>(&stg[j * STG + lc * LA + 32 + 8 * lg]);
+            }
+            float* ob = o + ((long)b * T + t0) * HD + (long)h * D + colw + lc;
+            const bool full = n == FC;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] = sGam[16 * mt + 4 * lg + e] * oq[mt][e];
-                    acc = MF::k32(ld8<_Float16>(&sP[(16 * mt + lc) * LA + 8 * lg]), d0, acc);
-                    if (mt >= 2) acc = MF::k32(ld8<_Float16>(&sP[(16 * mt + lc) * LA + 32 + 8 * lg]), d1, acc);
+            for (int mt = 0; mt < 4; ++mt) {
+                const H8 ap0 = ld8<_Float16>(&sP[(16 * mt + lc) * LA + 8 * lg]);
+                const H8 ap1 = ld8<_Float16>(&sP[(16 * mt + lc) * LA + 32 + 8 * lg]);
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(&sGam[16 * mt + 4 * lg]);
+#pragma unroll
+                for (int j = 0; j < TPW; ++j) {
+                    f32x4 acc = gm * oq[j][mt];
+                    acc = MF::k32(ap0, d0[j], acc);
+                    if (mt >= 2) acc = MF::k32(ap1, d1[j], acc);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int rr = 16 * mt + 4 * lg + e;
-                        float* dst = full || rr < n ? ob + (long)(16 * mt) * HD + ooff[e]
-                                                    : fs.sink + rr * D + 16 * wave + lc;
+                        float* dst = full || rr < n ? ob + rr * HD + 16 * j
+                                                    : fs.sink + rr * D + colw + 16 * j + lc;
                         *dst = acc[e];
                     }
                 }
             }
-            // H = Gam_C H0 + K^T (e Delta)
-            const H8 e0 = ld8<_Float16>(&sEt[lc * LA + 8 * lg]);
-            const H8 e1 = ld8<_Float16>(&sEt[lc * LA + 32 + 8 * lg]);
+        }
+        // H = Gam_C H0 + K^T (e Delta)
+        {
+            const float GC = sGC;
+            H8 e0[TPW], e1[TPW];
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                e0[j] = ld8<_Float16>(&stg[j * STG + 16 * LA + lc * LA + 8 * lg]);
+                e1[j] = ld8<_Float16>(&stg[j * STG + 16 * LA + lc * LA + 32 + 8 * lg]);
+            }
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                f32x4 acc = hs[j][m] * GC;
-                acc = MF::k32(ld8<_Float16>(&sKT[(16 * m + lc) * LA + 8 * lg]), e0, acc);
-                hs[j][m] = MF::k32(ld8<_Float16>(&sKT[(16 * m + lc) * LA + 32 + 8 * lg]), e1, acc);
+                const H8 ak0 = ld8<_Float16>(&sKT[tsw<LA>(16 * m + lc, 8 * lg)]);
+                const H8 ak1 = ld8<_Float16>(&sKT[tsw<LA>(16 * m + lc, 32 + 8 * lg)]);
+#pragma unroll
+                for (int j = 0; j < TPW; ++j) {
+                    f32x4 acc = hs[j][m] * GC;
+                    acc = MF::k32(ak0, e0[j], acc);
+                    hs[j][m] = MF::k32(ak1, e1[j], acc);
+                }
             }
         }
     }
@@ -371,7 +424,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     if (OUT) {
         if (S == 1) dst = state_out + (long)bh * D * D;
     } else {
-        dst = fs.summ + ((long)seg * BH + bh) * D * 2 * D;
+        dst = fs.summ + ((long)seg * BH + bh) * D * 2 * D + (idn ? D : 0);
         ldd = 2 * D;
     }
     if (dst) {
@@ -381,7 +434,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    dst[(16 * m + 4 * lg + e) * ldd + 16 * (wave + j * NW) + lc] = hs[j][m][e];
+                    dst[(16 * m + 4 * lg + e) * ldd + colw + 16 * j + lc] = hs[j][m][e];
     }
 }
 
@@ -436,13 +489,13 @@ static hipError_t launch_fused_t(const void* q, const void* k, const void* v, co
     const bf16_t* qq = static_cast<const bf16_t*>(q);
     const bf16_t* kk = static_cast<const bf16_t*>(k);
     const bf16_t* vv = static_cast<const bf16_t*>(v);
-    const dim3 block(64 * (D / 16));
+    const dim3 block(256);
     if (p.S == 1) {
         hipLaunchKernelGGL((gdn_fused<D, true>), dim3((unsigned)BH), block, 0, stream, qq, kk, vv, g,
                            beta, fs, state_in, state_out, o, T, H, B, p.NC, p.G, 1);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((gdn_fused<D, false>), dim3((unsigned)(BH * p.S)), block, 0, stream, qq, kk,
+    hipLaunchKernelGGL((gdn_fused<D, false>), dim3((unsigned)(2 * BH * p.S)), block, 0, stream, qq, kk,
                        vv, g, beta, fs, state_in, state_out, o, T, H, B, p.NC, p.G, p.S);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
