@@ -77,13 +77,13 @@ __device__ __forceinline__ int tsw(int row, int t) {
 }
 
 template <int D, bool OUT>
-__global__ __launch_bounds__(256) void gdn_fused(
+__global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, FusedSeg fs,
     const float* state_in, float* state_out, float* __restrict__ o, int T, int H, int B, int NC,
     int G, int S) {
-    constexpr int NW = 4, NTH = 256;
-    constexpr int TPW = D / 64;           // 16-column state tiles per wave
+    constexpr int NW = D / 16, NTH = 64 * NW;  // wave w owns state column tile w
+    constexpr int TPW = 1;                // 16-column state tiles per wave
     constexpr int MT = D / 16;            // key tiles of the state
     constexpr int LD = D + 8;             // row stride of [64][D] tiles
     constexpr int LA = FC + 8;            // row stride of [*][64] tiles
@@ -144,16 +144,21 @@ __global__ __launch_bounds__(256) void gdn_fused(
     // ---- raw input prefetch (one chunk ahead)
     uint4 rq[NL], rk[NL], rv[NL];
     float rg = 0.f, rb = 0.f;
+    // per-lane element offsets within a chunk (rows past the end re-read the last row)
     auto issue_loads = [&](int c) {
         const long t0 = (long)c * FC;
         const int n = (int)min((long)FC, (long)T - t0);
+        const long base = (((long)b * T + t0) * H + h) * D;  // scalar
+        const bf16_t* qb = q + base;
+        const bf16_t* kb = k + base;
+        const bf16_t* vb = v + base;
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int idx = tid + NTH * i, r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-            const long off = (((long)b * T + t0 + min(r, n - 1)) * H + h) * D + c8;
-            if (OUT) rq[i] = *reinterpret_cast<const uint4*>(q + off);
-            rk[i] = *reinterpret_cast<const uint4*>(k + off);
-            if (!idn) rv[i] = *reinterpret_cast<const uint4*>(v + off);
+            const unsigned off = (unsigned)(min(r, n - 1) * (int)HD + c8);
+            if (OUT) rq[i] = *reinterpret_cast<const uint4*>(qb + off);
+            rk[i] = *reinterpret_cast<const uint4*>(kb + off);
+            if (!idn) rv[i] = *reinterpret_cast<const uint4*>(vb + off);
         }
         if (wave == 0) {
             const long tok = ((long)b * T + t0 + min(lane, n - 1)) * H + h;
@@ -167,6 +172,13 @@ __global__ __launch_bounds__(256) void gdn_fused(
         const long t0 = (long)c * FC;
         const int n = (int)min((long)FC, (long)T - t0);
         lds_sync();  // previous chunk's operands are no longer read
+        // Re-derive the lane index through an opaque copy every chunk: otherwise
+        // the compiler hoists hundreds of lane-dependent addresses out of the
+        // loop, one register each, and spills.
+        int lane_i = lane;
+        asm volatile("" : "+v"(lane_i));
+        const int lg = lane_i >> 4, lc = lane_i & 15;
+        const int tid = wave * 64 + lane_i;
 
         // ---- inputs into LDS (f16): row-major K, Q; transposed K^T, V^T; gates
 #pragma unroll
@@ -204,9 +216,10 @@ __global__ __launch_bounds__(256) void gdn_fused(
         if (c + 1 < c_end) issue_loads(c + 1);
         lds_sync();
 
-        // ---- Gram tiles: wave w does K K^T for row block w (tiles 0..w) and,
-        // for OUT, Q K^T for row block 3 - w (tiles 0..3, upper ones zero).
-        {
+        // ---- Gram tiles: K K^T for row block w (tiles 0..w) on waves 0-3 and,
+        // for OUT, Q K^T for row block 3 - (w - 4) (tiles 0..3, upper ones zero)
+        // on waves 4-7 (on waves 0-3 too when there are only four).
+        if (NW == 8 ? wave < 4 : true) {
             const int mk = wave;
             H8 af[D / 32];
 #pragma unroll
@@ -230,8 +243,11 @@ __global__ __launch_bounds__(256) void gdn_fused(
                         sA[r * LA + i] = static_cast<_Float16>(-a);
                 }
             }
-            if (OUT) {
-                const int mq = 3 - wave;
+        }
+        if (OUT && (NW == 8 ? wave >= 4 : true)) {
+            {
+                const int mq = 3 - (wave & 3);
+                H8 af[D / 32];
 #pragma unroll
                 for (int kk = 0; kk < D / 32; ++kk) af[kk] = ld8<_Float16>(&sQ[(16 * mq + lc) * LD + 32 * kk + 8 * lg]);
                 const f32x4 gq = *reinterpret_cast<const f32x4*>(&sgam[16 * mq + 4 * lg]);
@@ -256,7 +272,7 @@ __global__ __launch_bounds__(256) void gdn_fused(
         lds_sync();
 
         // ---- diagonal blocks: (I + A_bb)^{-1} by fp32 forward substitution
-        if (lane < 16) {
+        if (wave < 4 && lane < 16) {
             const int cc = lane;
             float x[16];
 #pragma unroll
@@ -274,6 +290,7 @@ __global__ __launch_bounds__(256) void gdn_fused(
                     else s0 -= a[i] * x[i];
                 }
                 x[r] = s0 + s1;
+                if (r % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the hoisting of row loads
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r)
@@ -325,74 +342,87 @@ __global__ __launch_bounds__(256) void gdn_fused(
         lds_sync();  // -W complete
 
         // ---- state update for this wave's columns (no workgroup barrier)
-        // fp16 copy of the state tiles, [col][key]
+        // fp16 copy of the state tiles, [col][key], read back as B fragments
 #pragma unroll
         for (int j = 0; j < TPW; ++j)
 #pragma unroll
             for (int m = 0; m < MT; ++m)
                 st4<_Float16>(&stg[j * STG + lc * LD + 16 * m + 4 * lg], cvt4<_Float16>(hs[j][m]));
-        f32x4 dl[TPW][4], oq[TPW][4];
+        H8 bs[D / 32][TPW];
 #pragma unroll
-        for (int j = 0; j < TPW; ++j)
+        for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                dl[j][mt] = u[j][mt];
-                oq[j][mt] = zero4();
-            }
+            for (int j = 0; j < TPW; ++j) bs[kk][j] = ld8<_Float16>(&stg[j * STG + lc * LD + 32 * kk + 8 * lg]);
+        // Delta = U - W H0 one row tile at a time; Delta^T and (e Delta)^T staged
+        // as [col][t] over the state copy (already read into bs)
 #pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-            H8 bs[TPW];
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4 dl[TPW];
 #pragma unroll
-            for (int j = 0; j < TPW; ++j) bs[j] = ld8<_Float16>(&stg[j * STG + lc * LD + 32 * kk + 8 * lg]);
+            for (int j = 0; j < TPW; ++j) dl[j] = u[j][mt];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+            for (int kk = 0; kk < D / 32; ++kk) {
                 const H8 aw = ld8<_Float16>(&sW[(16 * mt + lc) * LD + 32 * kk + 8 * lg]);
 #pragma unroll
-                for (int j = 0; j < TPW; ++j) dl[j][mt] = MF::k32(aw, bs[j], dl[j][mt]);
-                if (OUT) {
-                    const H8 aq = ld8<_Float16>(&sQ[(16 * mt + lc) * LD + 32 * kk + 8 * lg]);
-#pragma unroll
-                    for (int j = 0; j < TPW; ++j) oq[j][mt] = MF::k32(aq, bs[j], oq[j][mt]);
-                }
+                for (int j = 0; j < TPW; ++j) dl[j] = MF::k32(aw, bs[kk][j], dl[j]);
             }
+            const f32x4 ev = *reinterpret_cast<const f32x4*>(&sE[16 * mt + 4 * lg]);
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                if (OUT) st4<_Float16>(&stg[j * STG + lc * LA + 16 * mt + 4 * lg], cvt4<_Float16>(dl[j]));
+                st4<_Float16>(&stg[j * STG + 16 * LA + lc * LA + 16 * mt + 4 * lg], cvt4<_Float16>(ev * dl[j]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // Delta^T and (e Delta)^T staged as [col][t] over the state copy
-#pragma unroll
-        for (int j = 0; j < TPW; ++j)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const f32x4 ed = *reinterpret_cast<const f32x4*>(&sE[16 * mt + 4 * lg]) * dl[j][mt];
-                if (OUT) st4<_Float16>(&stg[j * STG + lc * LA + 16 * mt + 4 * lg], cvt4<_Float16>(dl[j][mt]));
-                st4<_Float16>(&stg[j * STG + 16 * LA + lc * LA + 16 * mt + 4 * lg], cvt4<_Float16>(ed));
-            }
         if (OUT) {
-            // O = diag(Gam) Q H0 + P Delta
+            // O = diag(Gam) Q H0 + P Delta, one row tile at a time
             H8 d0[TPW], d1[TPW];
 #pragma unroll
             for (int j = 0; j < TPW; ++j) {
                 d0[j] = ld8<_Float16>(&stg[j * STG + lc * LA + 8 * lg]);
                 d1[j] = ld8<_Float16>(&stg[j * STG + lc * LA + 32 + 8 * lg]);
             }
-            float* ob = o + ((long)b * T + t0) * HD + (long)h * D + colw + lc;
             const bool full = n == FC;
+            float* ob = o + ((long)b * T + t0) * HD + (long)h * D + colw;  // scalar
+            unsigned ooff[4];  // this lane's rows 4 lg + e (elements)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ooff[e] = (unsigned)((4 * lg + e) * (int)HD + lc);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const H8 ap0 = ld8<_Float16>(&sP[(16 * mt + lc) * LA + 8 * lg]);
-                const H8 ap1 = ld8<_Float16>(&sP[(16 * mt + lc) * LA + 32 + 8 * lg]);
+                f32x4 oq[TPW];
+#pragma unroll
+                for (int j = 0; j < TPW; ++j) oq[j] = zero4();
+#pragma unroll
+                for (int kk = 0; kk < D / 32; ++kk) {
+                    const H8 aq = ld8<_Float16>(&sQ[(16 * mt + lc) * LD + 32 * kk + 8 * lg]);
+#pragma unroll
+                    for (int j = 0; j < TPW; ++j) oq[j] = MF::k32(aq, bs[kk][j], oq[j]);
+                }
                 const f32x4 gm = *reinterpret_cast<const f32x4*>(&sGam[16 * mt + 4 * lg]);
+                const H8 ap0 = ld8<_Float16>(&sP[(16 * mt + lc) * LA + 8 * lg]);
 #pragma unroll
                 for (int j = 0; j < TPW; ++j) {
-                    f32x4 acc = gm * oq[j][mt];
-                    acc = MF::k32(ap0, d0[j], acc);
-                    if (mt >= 2) acc = MF::k32(ap1, d1[j], acc);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int rr = 16 * mt + 4 * lg + e;
-                        float* dst = full || rr < n ? ob + rr * HD + 16 * j
-                                                    : fs.sink + rr * D + colw + 16 * j + lc;
-                        *dst = acc[e];
-                    }
+                    oq[j] = MF::k32(ap0, d0[j], gm * oq[j]);
+                    if (mt >= 2) oq[j] = MF::k32(ld8<_Float16>(&sP[(16 * mt + lc) * LA + 32 + 8 * lg]), d1[j], oq[j]);
                 }
+                if (full) {
+                    float* obm = ob + (long)16 * mt * HD;  // scalar
+#pragma unroll
+                    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) obm[ooff[e] + 16 * j] = oq[j][e];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int rr = 16 * mt + 4 * lg + e;
+                            float* dst = rr < n ? ob + rr * HD + 16 * j + lc
+                                                : fs.sink + rr * D + colw + 16 * j + lc;
+                            *dst = oq[j][e];
+                        }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         // H = Gam_C H0 + K^T (e Delta)
@@ -414,6 +444,7 @@ __global__ __launch_bounds__(256) void gdn_fused(
                     acc = MF::k32(ak0, e0[j], acc);
                     hs[j][m] = MF::k32(ak1, e1[j], acc);
                 }
+                if (m % 2 == 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -489,7 +520,7 @@ static hipError_t launch_fused_t(const void* q, const void* k, const void* v, co
     const bf16_t* qq = static_cast<const bf16_t*>(q);
     const bf16_t* kk = static_cast<const bf16_t*>(k);
     const bf16_t* vv = static_cast<const bf16_t*>(v);
-    const dim3 block(256);
+    const dim3 block(64 * (D / 16));
     if (p.S == 1) {
         hipLaunchKernelGGL((gdn_fused<D, true>), dim3((unsigned)BH), block, 0, stream, qq, kk, vv, g,
                            beta, fs, state_in, state_out, o, T, H, B, p.NC, p.G, 1);
