@@ -77,13 +77,13 @@ __device__ __forceinline__ int tsw(int row, int t) {
 }
 
 template <int D, bool OUT>
-__global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
+__global__ __launch_bounds__(256) void gdn_fused(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, FusedSeg fs,
     const float* state_in, float* state_out, float* __restrict__ o, int T, int H, int B, int NC,
     int G, int S) {
-    constexpr int NW = D / 16, NTH = 64 * NW;  // wave w owns state column tile w
-    constexpr int TPW = 1;                // 16-column state tiles per wave
+    constexpr int NW = 4, NTH = 256;
+    constexpr int TPW = D / 64;           // 16-column state tiles per wave
     constexpr int MT = D / 16;            // key tiles of the state
     constexpr int LD = D + 8;             // row stride of [64][D] tiles
     constexpr int LA = FC + 8;            // row stride of [*][64] tiles
@@ -216,10 +216,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         if (c + 1 < c_end) issue_loads(c + 1);
         lds_sync();
 
-        // ---- Gram tiles: K K^T for row block w (tiles 0..w) on waves 0-3 and,
-        // for OUT, Q K^T for row block 3 - (w - 4) (tiles 0..3, upper ones zero)
-        // on waves 4-7 (on waves 0-3 too when there are only four).
-        if (NW == 8 ? wave < 4 : true) {
+        // ---- Gram tiles.  Wave w: K K^T for row block w (tiles 0..w; the
+        // diagonal tile last, inverted right away by the same wave) and, for
+        // OUT, Q K^T for row block 3 - w (tiles 0..3, upper ones zero).
+        {
             const int mk = wave;
             H8 af[D / 32];
 #pragma unroll
@@ -243,11 +243,34 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                         sA[r * LA + i] = static_cast<_Float16>(-a);
                 }
             }
-        }
-        if (OUT && (NW == 8 ? wave >= 4 : true)) {
-            {
-                const int mq = 3 - (wave & 3);
-                H8 af[D / 32];
+            // (I + A_ww)^{-1} by fp32 forward substitution, one column per lane;
+            // only this wave touches sAd[w], so no workgroup barrier is needed.
+            if (lane_i < 16) {
+                const int cc = lane_i;
+                float x[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float a[16];
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const f32x4 t4 = *reinterpret_cast<const f32x4*>(&sAd[mk][r][4 * q4]);
+                        a[4 * q4] = t4[0]; a[4 * q4 + 1] = t4[1]; a[4 * q4 + 2] = t4[2]; a[4 * q4 + 3] = t4[3];
+                    }
+                    float s0 = (r == cc) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int i = 0; i < r; ++i) {
+                        if (i & 1) s1 -= a[i] * x[i];
+                        else s0 -= a[i] * x[i];
+                    }
+                    x[r] = s0 + s1;
+                    if (r % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the hoisting of row loads
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    sA[(16 * mk + r) * LA + 16 * mk + cc] = static_cast<_Float16>(r == cc ? 0.f : x[r]);
+            }
+            if (OUT) {
+                const int mq = 3 - wave;
 #pragma unroll
                 for (int kk = 0; kk < D / 32; ++kk) af[kk] = ld8<_Float16>(&sQ[(16 * mq + lc) * LD + 32 * kk + 8 * lg]);
                 const f32x4 gq = *reinterpret_cast<const f32x4*>(&sgam[16 * mq + 4 * lg]);
@@ -271,73 +294,59 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         }
         lds_sync();
 
-        // ---- diagonal blocks: (I + A_bb)^{-1} by fp32 forward substitution
-        if (wave < 4 && lane < 16) {
-            const int cc = lane;
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float a[16];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const f32x4 t4 = *reinterpret_cast<const f32x4*>(&sAd[wave][r][4 * q4]);
-                    a[4 * q4] = t4[0]; a[4 * q4 + 1] = t4[1]; a[4 * q4 + 2] = t4[2]; a[4 * q4 + 3] = t4[3];
-                }
-                float s0 = (r == cc) ? 1.f : 0.f, s1 = 0.f;
-#pragma unroll
-                for (int i = 0; i < r; ++i) {
-                    if (i & 1) s1 -= a[i] * x[i];
-                    else s0 -= a[i] * x[i];
-                }
-                x[r] = s0 + s1;
-                if (r % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the hoisting of row loads
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                sA[(16 * wave + r) * LA + 16 * wave + cc] = static_cast<_Float16>(r == cc ? 0.f : x[r]);
-        }
-        lds_sync();
-
         // ---- blocked solve with the right-hand side in fp32:
         //   Y_b = B_b - sum_{j<b} A_bj X_j,  X_b = Y_b + N_bb Y_b
-        // U tiles of this wave's columns stay in registers; -W tiles go to LDS.
-        auto solve = [&](bool is_w, int col, f32x4 res[4]) {
-            H4 xh[4];
+        // for all of this wave's right-hand sides at once (U tiles of its state
+        // columns, kept in registers, and -W tiles, written to LDS); the
+        // independent chains interleave on the matrix cores.
+        constexpr int NR = 2 * TPW;  // right-hand-side tiles: TPW of U then TPW of W
+        f32x4 res[NR][4];
+        {
+            H4 xh[NR][4];
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
-                const f32x4 f4 = *reinterpret_cast<const f32x4*>(is_w ? &sBG[16 * bb + 4 * lg]
-                                                                      : &sbeta[16 * bb + 4 * lg]);
-                const H4 x4 = ld4<_Float16>(is_w ? &sKT[tsw<LA>(col, 16 * bb + 4 * lg)]
-                                                 : &sVT[tsw<LA>(col, 16 * bb + 4 * lg)]);
-                f32x4 acc;
+                const f32x4 fb = *reinterpret_cast<const f32x4*>(&sbeta[16 * bb + 4 * lg]);
+                const f32x4 fg = *reinterpret_cast<const f32x4*>(&sBG[16 * bb + 4 * lg]);
+                f32x4 acc[NR];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = f4[e] * static_cast<float>(x4[e]);
+                for (int t = 0; t < NR; ++t) {
+                    const bool is_w = t >= TPW;
+                    const int col = colw + 16 * (t % TPW) + lc;
+                    if (!is_w && idn) {
+                        acc[t] = zero4();
+                        continue;
+                    }
+                    const H4 x4 = ld4<_Float16>(is_w ? &sKT[tsw<LA>(col, 16 * bb + 4 * lg)]
+                                                     : &sVT[tsw<LA>(col, 16 * bb + 4 * lg)]);
 #pragma unroll
-                for (int j = 0; j < bb; ++j)
-                    acc = MF::k16(ld4<_Float16>(&sA[(16 * bb + lc) * LA + 16 * j + 4 * lg]), xh[j], acc);
-                const H4 yh = cvt4<_Float16>(acc);
-                acc = MF::k16(ld4<_Float16>(&sA[(16 * bb + lc) * LA + 16 * bb + 4 * lg]), yh, acc);
-                xh[bb] = cvt4<_Float16>(acc);
-                res[bb] = acc;
+                    for (int e = 0; e < 4; ++e) acc[t][e] = (is_w ? fg[e] : fb[e]) * static_cast<float>(x4[e]);
+                }
+#pragma unroll
+                for (int j = 0; j < bb; ++j) {
+                    const H4 aj = ld4<_Float16>(&sA[(16 * bb + lc) * LA + 16 * j + 4 * lg]);
+#pragma unroll
+                    for (int t = 0; t < NR; ++t) acc[t] = MF::k16(aj, xh[t][j], acc[t]);
+                }
+                const H4 ab = ld4<_Float16>(&sA[(16 * bb + lc) * LA + 16 * bb + 4 * lg]);
+#pragma unroll
+                for (int t = 0; t < NR; ++t) {
+                    acc[t] = MF::k16(ab, cvt4<_Float16>(acc[t]), acc[t]);
+                    xh[t][bb] = cvt4<_Float16>(acc[t]);
+                    res[t][bb] = acc[t];
+                }
             }
-        };
+        }
         f32x4 u[TPW][4];
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
-            if (!idn) {
-                solve(false, colw + 16 * j + lc, u[j]);
-            } else {
 #pragma unroll
-                for (int bb = 0; bb < 4; ++bb) u[j][bb] = zero4();
-            }
-            f32x4 wres[4];
+            for (int bb = 0; bb < 4; ++bb) u[j][bb] = res[j][bb];
             const int col = colw + 16 * j + lc;
-            solve(true, col, wres);
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    sW[(16 * bb + 4 * lg + e) * LD + col] = static_cast<_Float16>(-wres[bb][e]);
+                    sW[(16 * bb + 4 * lg + e) * LD + col] = static_cast<_Float16>(-res[TPW + j][bb][e]);
         }
         lds_sync();  // -W complete
 
@@ -520,7 +529,7 @@ static hipError_t launch_fused_t(const void* q, const void* k, const void* v, co
     const bf16_t* qq = static_cast<const bf16_t*>(q);
     const bf16_t* kk = static_cast<const bf16_t*>(k);
     const bf16_t* vv = static_cast<const bf16_t*>(v);
-    const dim3 block(64 * (D / 16));
+    const dim3 block(256);
     if (p.S == 1) {
         hipLaunchKernelGGL((gdn_fused<D, true>), dim3((unsigned)BH), block, 0, stream, qq, kk, vv, g,
                            beta, fs, state_in, state_out, o, T, H, B, p.NC, p.G, 1);
