@@ -77,13 +77,13 @@ __device__ __forceinline__ int tsw(int row, int t) {
 }
 
 template <int D, bool OUT>
-__global__ __launch_bounds__(256) void gdn_fused(
+__global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, FusedSeg fs,
     const float* state_in, float* state_out, float* __restrict__ o, int T, int H, int B, int NC,
     int G, int S) {
-    constexpr int NW = 4, NTH = 256;
-    constexpr int TPW = D / 64;           // 16-column state tiles per wave
+    constexpr int NW = D / 16, NTH = 64 * NW;  // wave w owns column tile w
+    constexpr int TPW = OUT ? 1 : 2;      // state tiles per wave: value tile w (+ identity tile w)
     constexpr int MT = D / 16;            // key tiles of the state
     constexpr int LD = D + 8;             // row stride of [64][D] tiles
     constexpr int LA = FC + 8;            // row stride of [*][64] tiles
@@ -102,13 +102,10 @@ __global__ __launch_bounds__(256) void gdn_fused(
     __shared__ __align__(16) float sgam[FC], sbeta[FC], sGam[FC], sE[FC], sBG[FC];
     __shared__ float sGC;
 
-    // SUM runs two parts per (segment, head): part 0 the value columns (R),
-    // part 1 the identity columns (M), which need neither V nor U.
+    // SUM chains the value columns (tile w, giving R) and the identity columns
+    // (tile w of M) of the augmented state together; OUT only the value tile.
     const int BH = B * H;
-    const int part = OUT ? 0 : (int)(blockIdx.x / (BH * S));
-    const int blk = OUT ? (int)blockIdx.x : (int)(blockIdx.x % (BH * S));
-    const int bh = blk % BH, seg = blk / BH;
-    const bool idn = part == 1;
+    const int bh = (int)blockIdx.x % BH, seg = (int)blockIdx.x / BH;
     const int b = bh / H, h = bh % H;
     const int c_begin = seg * G, c_end = min(c_begin + G, NC);
     const int tid = threadIdx.x, lane = tid & 63;
@@ -116,7 +113,7 @@ __global__ __launch_bounds__(256) void gdn_fused(
     const int lg = lane >> 4, lc = lane & 15;
     const long HD = (long)H * D;
     _Float16* stg = sStg + wave * TPW * STG;
-    const int colw = 16 * TPW * wave;  // first state column of this wave
+    const int colw = 16 * wave;  // this wave's value columns (and identity columns in SUM)
 
     // ---- state tiles (fp32, C layout): key 16 m + 4 lg + e, column colw + 16 j + lc
     f32x4 hs[TPW][MT];
@@ -130,11 +127,11 @@ __global__ __launch_bounds__(256) void gdn_fused(
             for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int key = 16 * m + 4 * lg + e, col = colw + 16 * j + lc;
+                    const int key = 16 * m + 4 * lg + e, col = colw + lc;
                     float x = 0.f;
                     if (OUT) {
                         if (src) x = src[key * D + col];
-                    } else if (idn) {
+                    } else if (j == 1) {
                         x = key == col ? 1.f : 0.f;
                     }
                     hs[j][m][e] = x;
@@ -158,7 +155,7 @@ __global__ __launch_bounds__(256) void gdn_fused(
             const unsigned off = (unsigned)(min(r, n - 1) * (int)HD + c8);
             if (OUT) rq[i] = *reinterpret_cast<const uint4*>(qb + off);
             rk[i] = *reinterpret_cast<const uint4*>(kb + off);
-            if (!idn) rv[i] = *reinterpret_cast<const uint4*>(vb + off);
+            rv[i] = *reinterpret_cast<const uint4*>(vb + off);
         }
         if (wave == 0) {
             const long tok = ((long)b * T + t0 + min(lane, n - 1)) * H + h;
@@ -190,7 +187,7 @@ __global__ __launch_bounds__(256) void gdn_fused(
             if (OUT) *reinterpret_cast<H8*>(&sQ[r * LD + c8]) = ok ? bf16x8_to_f16(rq[i]) : zero_h8();
 #pragma unroll
             for (int j = 0; j < 8; ++j) sKT[tsw<LA>(c8 + j, r)] = fk[j];
-            if (!idn) {
+            {
                 const H8 fv = ok ? bf16x8_to_f16(rv[i]) : zero_h8();
 #pragma unroll
                 for (int j = 0; j < 8; ++j) sVT[tsw<LA>(c8 + j, r)] = fv[j];
@@ -216,33 +213,23 @@ __global__ __launch_bounds__(256) void gdn_fused(
         if (c + 1 < c_end) issue_loads(c + 1);
         lds_sync();
 
-        // ---- Gram tiles.  Wave w: K K^T for row block w (tiles 0..w; the
-        // diagonal tile last, inverted right away by the same wave) and, for
-        // OUT, Q K^T for row block 3 - w (tiles 0..3, upper ones zero).
-        {
+        // ---- Gram tiles.  Waves 0-3: diagonal K K^T tile (w, w), inverted right
+        // away by the same wave.  All waves: the six off-diagonal K K^T tiles and,
+        // for OUT, the Q K^T tiles (lower ones computed, upper ones zero).
+        if (wave < 4) {
             const int mk = wave;
-            H8 af[D / 32];
+            f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) af[kk] = ld8<_Float16>(&sK[(16 * mk + lc) * LD + 32 * kk + 8 * lg]);
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const H8 a = ld8<_Float16>(&sK[(16 * mk + lc) * LD + 32 * kk + 8 * lg]);
+                acc = MF::k32(a, a, acc);
+            }
             const f32x4 gr = *reinterpret_cast<const f32x4*>(&sgam[16 * mk + 4 * lg]);
             const f32x4 br = *reinterpret_cast<const f32x4*>(&sbeta[16 * mk + 4 * lg]);
-            for (int ni = 0; ni <= mk; ++ni) {
-                f32x4 acc = zero4();
+            const float gi = sgam[16 * mk + lc];
 #pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk)
-                    acc = MF::k32(af[kk], ld8<_Float16>(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]), acc);
-                const int i = 16 * ni + lc;
-                const float gi = sgam[i];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * mk + 4 * lg + e;
-                    const float a = i < r ? br[e] * __expf(gr[e] - gi) * acc[e] : 0.f;
-                    if (ni == mk)
-                        sAd[mk][4 * lg + e][lc] = a;
-                    else
-                        sA[r * LA + i] = static_cast<_Float16>(-a);
-                }
-            }
+            for (int e = 0; e < 4; ++e)
+                sAd[mk][4 * lg + e][lc] = lc < 4 * lg + e ? br[e] * __expf(gr[e] - gi) * acc[e] : 0.f;
             // (I + A_ww)^{-1} by fp32 forward substitution, one column per lane;
             // only this wave touches sAd[w], so no workgroup barrier is needed.
             if (lane_i < 16) {
@@ -269,27 +256,59 @@ __global__ __launch_bounds__(256) void gdn_fused(
                 for (int r = 0; r < 16; ++r)
                     sA[(16 * mk + r) * LA + 16 * mk + cc] = static_cast<_Float16>(r == cc ? 0.f : x[r]);
             }
-            if (OUT) {
-                const int mq = 3 - wave;
+        }
+        {
+            // Tile list: the 6 off-diagonal K K^T tiles, then (OUT) the 10 lower
+            // Q K^T tiles.  With 8 waves the four waves without a diagonal block
+            // take the first 12 tiles, the other four one Q K^T tile each.
+            constexpr int NREAL = OUT ? 16 : 6;
+            int tt = wave, tstep = NW, tend = NREAL;
+            if (NW == 8) {
+                tstep = 4;
+                if (wave >= 4) {
+                    tt = wave - 4;
+                    tend = OUT ? 12 : NREAL;
+                } else {
+                    tt = 12 + wave;
+                }
+            }
+            for (; tt < tend; tt += tstep) {
+                const bool kq = tt < 6;  // K K^T off-diagonal
+                int mi, ni;
+                if (kq) {
+                    mi = tt < 1 ? 1 : tt < 3 ? 2 : 3;
+                    ni = tt - (mi * (mi - 1)) / 2;
+                } else {
+                    const int u = tt - 6;
+                    mi = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
+                    ni = u - (mi * (mi + 1)) / 2;
+                }
+                const _Float16* X = kq ? sK : sQ;
+                f32x4 acc = zero4();
 #pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk) af[kk] = ld8<_Float16>(&sQ[(16 * mq + lc) * LD + 32 * kk + 8 * lg]);
-                const f32x4 gq = *reinterpret_cast<const f32x4*>(&sgam[16 * mq + 4 * lg]);
-                for (int ni = 0; ni < 4; ++ni) {
-                    f32x4 acc = zero4();
-                    if (ni <= mq) {
+                for (int kk = 0; kk < D / 32; ++kk)
+                    acc = MF::k32(ld8<_Float16>(&X[(16 * mi + lc) * LD + 32 * kk + 8 * lg]),
+                                  ld8<_Float16>(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]), acc);
+                const f32x4 gr = *reinterpret_cast<const f32x4*>(&sgam[16 * mi + 4 * lg]);
+                const f32x4 br = *reinterpret_cast<const f32x4*>(&sbeta[16 * mi + 4 * lg]);
+                const int i = 16 * ni + lc;
+                const float gi = sgam[i];
 #pragma unroll
-                        for (int kk = 0; kk < D / 32; ++kk)
-                            acc = MF::k32(af[kk], ld8<_Float16>(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]), acc);
-                    }
-                    const int i = 16 * ni + lc;
-                    const float gi = sgam[i];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * mq + 4 * lg + e;
-                        const float pv = i <= r ? __expf(gq[e] - gi) * acc[e] : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * mi + 4 * lg + e;
+                    if (kq) {
+                        sA[r * LA + i] = static_cast<_Float16>(-(br[e] * __expf(gr[e] - gi) * acc[e]));
+                    } else {
+                        const float pv = i <= r ? __expf(gr[e] - gi) * acc[e] : 0.f;
                         sP[r * LA + i] = static_cast<_Float16>(pv);
                     }
                 }
+            }
+            // the two upper P tiles that the output products read, (0,1) and (2,3)
+            if (OUT && wave < 2) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sP[(32 * wave + 4 * lg + e) * LA + 32 * wave + 16 + lc] = _Float16(0);
             }
         }
         lds_sync();
@@ -299,7 +318,7 @@ __global__ __launch_bounds__(256) void gdn_fused(
         // for all of this wave's right-hand sides at once (U tiles of its state
         // columns, kept in registers, and -W tiles, written to LDS); the
         // independent chains interleave on the matrix cores.
-        constexpr int NR = 2 * TPW;  // right-hand-side tiles: TPW of U then TPW of W
+        constexpr int NR = 2;  // right-hand-side tiles: U tile w, W tile w
         f32x4 res[NR][4];
         {
             H4 xh[NR][4];
@@ -310,12 +329,8 @@ __global__ __launch_bounds__(256) void gdn_fused(
                 f32x4 acc[NR];
 #pragma unroll
                 for (int t = 0; t < NR; ++t) {
-                    const bool is_w = t >= TPW;
-                    const int col = colw + 16 * (t % TPW) + lc;
-                    if (!is_w && idn) {
-                        acc[t] = zero4();
-                        continue;
-                    }
+                    const bool is_w = t == 1;
+                    const int col = colw + lc;
                     const H4 x4 = ld4<_Float16>(is_w ? &sKT[tsw<LA>(col, 16 * bb + 4 * lg)]
                                                      : &sVT[tsw<LA>(col, 16 * bb + 4 * lg)]);
 #pragma unroll
@@ -338,15 +353,12 @@ __global__ __launch_bounds__(256) void gdn_fused(
         }
         f32x4 u[TPW][4];
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) {
+        for (int bb = 0; bb < 4; ++bb) {
+            u[0][bb] = res[0][bb];
+            if (TPW == 2) u[TPW - 1][bb] = zero4();  // identity columns: no U
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb) u[j][bb] = res[j][bb];
-            const int col = colw + 16 * j + lc;
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sW[(16 * bb + 4 * lg + e) * LD + col] = static_cast<_Float16>(-res[TPW + j][bb][e]);
+            for (int e = 0; e < 4; ++e)
+                sW[(16 * bb + 4 * lg + e) * LD + colw + lc] = static_cast<_Float16>(-res[1][bb][e]);
         }
         lds_sync();  // -W complete
 
@@ -464,7 +476,7 @@ __global__ __launch_bounds__(256) void gdn_fused(
     if (OUT) {
         if (S == 1) dst = state_out + (long)bh * D * D;
     } else {
-        dst = fs.summ + ((long)seg * BH + bh) * D * 2 * D + (idn ? D : 0);
+        dst = fs.summ + ((long)seg * BH + bh) * D * 2 * D;
         ldd = 2 * D;
     }
     if (dst) {
@@ -474,7 +486,7 @@ __global__ __launch_bounds__(256) void gdn_fused(
             for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    dst[(16 * m + 4 * lg + e) * ldd + colw + 16 * j + lc] = hs[j][m][e];
+                    dst[(16 * m + 4 * lg + e) * ldd + j * D + colw + lc] = hs[j][m][e];
     }
 }
 
@@ -529,13 +541,13 @@ static hipError_t launch_fused_t(const void* q, const void* k, const void* v, co
     const bf16_t* qq = static_cast<const bf16_t*>(q);
     const bf16_t* kk = static_cast<const bf16_t*>(k);
     const bf16_t* vv = static_cast<const bf16_t*>(v);
-    const dim3 block(256);
+    const dim3 block(64 * (D / 16));
     if (p.S == 1) {
         hipLaunchKernelGGL((gdn_fused<D, true>), dim3((unsigned)BH), block, 0, stream, qq, kk, vv, g,
                            beta, fs, state_in, state_out, o, T, H, B, p.NC, p.G, 1);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((gdn_fused<D, false>), dim3((unsigned)(2 * BH * p.S)), block, 0, stream, qq, kk,
+    hipLaunchKernelGGL((gdn_fused<D, false>), dim3((unsigned)(BH * p.S)), block, 0, stream, qq, kk,
                        vv, g, beta, fs, state_in, state_out, o, T, H, B, p.NC, p.G, p.S);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
