@@ -460,7 +460,7 @@ __device__ __forceinline__ void chain_load(ChainFrags<OT, D, NT, OUT>& f, const 
 }
 
 // Segment-level workspace behind the per-chunk blocks and the sink:
-//   summ  [S][B*H][D][2D] f32   [R | M] of each segment
+//   summ  [S][B*H] summaries of 8 D^2 bytes: R (fp32), M (fp16 high, low)
 //   sst   [S][B*H][D][D]  f32   start state of each segment
 struct SegWs {
     float* summ;
@@ -621,41 +621,47 @@ __global__ __launch_bounds__(256) void chunk_chain(const void* ws, SegWs sw,
         if (c + 1 < c_end) step(fb, c + 1);
     }
 
-    float* dst = nullptr;
-    long ld = D;
     if (OUT) {
-        if (S == 1) dst = state_out + (long)bh * D * D;
+        if (S == 1) {
+            float* dst = state_out + (long)bh * D * D;
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        dst[(16 * (wave * MT + m) + 4 * lg + e) * D + col0 + 16 * nt + lc] = hs[m][nt][e];
+        }
     } else {
-        dst = sw.summ + ((long)seg * BH + bh) * D * 2 * D;
-        ld = 2 * D;
-    }
-    if (dst) {
+        float* sm = sw.summ + ((long)seg * BH + bh) * D * 2 * D;
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int key = 16 * (wave * MT + m) + 4 * lg + e;
-                    dst[key * ld + col0 + 16 * nt + lc] = hs[m][nt][e];
-                }
+                for (int e = 0; e < 4; ++e)
+                    summary_store<D>(sm, 16 * (wave * MT + m) + 4 * lg + e, col0 + 16 * nt + lc, hs[m][nt][e]);
     }
 }
 
 // ---------------------------------------------------------------------------
-// seg_combine: grid B*H*(D/16) workgroups of 256 threads, sequential over the
-// segments.  H_s = M_s H_{s-1} + R_s in fp32-grade arithmetic: both factors
-// are split into fp16 high and low parts and three products are accumulated.
+// seg_combine: grid B*H*(D/16) workgroups of D/16 waves (wave w: key tile w of
+// one 16-column slice), sequential over the segments.  H_s = M_s H_{s-1} + R_s
+// in fp32-grade arithmetic: both factors are split into fp16 high and low
+// parts (M already by the summary writer) and three products are accumulated.
 // Stores each segment's start state and the final state.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void seg_combine(SegWs sw, const float* state_in,
-                                                   float* state_out, int BH, int S) {
+__global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const float* state_in,
+                                                           float* state_out, int BH, int S) {
     using M = Mfma<_Float16>;
     using F8 = M::frag8;
-    constexpr int NS = D / 16, MT = D / 64, LS = D + 8;
-    __shared__ __align__(16) _Float16 sHi[16 * LS], sLo[16 * LS];
+    constexpr int NS = D / 16, LS = D + 8;
+    constexpr int NB = 3;  // segments whose summaries are in flight
+    // fp16 high / low parts of the chained state slice, [col][key], double-buffered
+    __shared__ __align__(16) _Float16 sHi[2][16 * LS], sLo[2][16 * LS];
 
+    // workgroup = (head, 16-column slice); the slices of one head share an XCD
     const int L = blockIdx.x;
     int bh, slice;
     if (BH % 8 == 0) {
@@ -666,76 +672,84 @@ __global__ __launch_bounds__(256) void seg_combine(SegWs sw, const float* state_
         slice = L % NS;
     }
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // key tile of this wave
     const int lg = lane >> 4, lc = lane & 15;
     const int col = slice * 16 + lc;
 
-    f32x4 hs[MT];
+    // state tile (C layout): keys 16 wave + 4 lg + e, column col
+    f32x4 hs;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int e = 0; e < 4; ++e)
+        hs[e] = state_in ? state_in[((long)bh * D + 16 * wave + 4 * lg + e) * D + col] : 0.f;
+
+    // Summaries do not depend on the chained state: those of the next NB
+    // segments are loaded while the current one is applied.  Loads past the
+    // last segment re-read it, so every load is unconditional.
+    struct Pre {
+        F8 hi[D / 32], lo[D / 32];  // rows of M (A operand)
+        f32x4 r;                    // R (C layout)
+    };
+    auto load = [&](Pre& p, int s) {
+        const float* sm = sw.summ + ((long)min(s, S - 1) * BH + bh) * D * 2 * D;
+        const _Float16* mh = reinterpret_cast<const _Float16*>(sm + D * D);
+        p.r = *reinterpret_cast<const f32x4*>(sm + ((slice * (D / 16) + wave) * 64 + lane) * 4);
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const int off = ((wave * (D / 32) + kk) * 64 + lane) * 8;
+            p.hi[kk] = *reinterpret_cast<const F8*>(mh + off);
+            p.lo[kk] = *reinterpret_cast<const F8*>(mh + D * D + off);
+        }
+    };
+    auto apply = [&](const Pre& p, int s) {
+        float* dst = sw.sst + ((long)s * BH + bh) * D * D;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(16 * wave + 4 * lg + e) * D + col] = hs[e];
+        // B operand: the state split into high and low fp16 parts.  The buffers
+        // alternate, so one barrier per segment suffices: a buffer is rewritten
+        // two segments later, after every wave passed the next barrier.
+        _Float16* bh_ = sHi[s & 1];
+        _Float16* bl_ = sLo[s & 1];
+        typename M::frag4 hi;
+        f32x4 lo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int key = 16 * (wave * MT + m) + 4 * lg + e;
-            hs[m][e] = state_in ? state_in[((long)bh * D + key) * D + col] : 0.f;
+            hi[e] = static_cast<_Float16>(hs[e]);
+            lo[e] = hs[e] - static_cast<float>(hi[e]);
         }
+        st4<_Float16>(&bh_[lc * LS + 16 * wave + 4 * lg], hi);
+        st4<_Float16>(&bl_[lc * LS + 16 * wave + 4 * lg], cvt4<_Float16>(lo));
+        lds_sync();
+        f32x4 a0 = p.r, a1 = zero4(), a2 = zero4();  // three independent chains
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const F8 bhi = ld8<_Float16>(&bh_[lc * LS + 32 * kk + 8 * lg]);
+            const F8 blo = ld8<_Float16>(&bl_[lc * LS + 32 * kk + 8 * lg]);
+            a0 = M::k32(p.hi[kk], bhi, a0);
+            a1 = M::k32(p.hi[kk], blo, a1);
+            a2 = M::k32(p.lo[kk], bhi, a2);
+        }
+        hs = a0 + (a1 + a2);
+    };
 
-    for (int s = 0; s < S; ++s) {
-        {
-            float* dst = sw.sst + ((long)s * BH + bh) * D * D;
+    Pre pb[NB];
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
+    for (int i = 0; i < NB; ++i) load(pb[i], i);
+    // whole groups of NB segments branch-free (so the compiler's load counting
+    // stays exact), then the remainder
+    int s = 0;
+    for (; s + NB <= S; s += NB) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    dst[(16 * (wave * MT + m) + 4 * lg + e) * D + col] = hs[m][e];
+        for (int i = 0; i < NB; ++i) {
+            apply(pb[i], s + i);
+            load(pb[i], s + i + NB);
         }
-        // B operand: the state split into high and low fp16 parts
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            f32x4 lo;
-            typename M::frag4 hi;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                hi[e] = static_cast<_Float16>(hs[m][e]);
-                lo[e] = hs[m][e] - static_cast<float>(hi[e]);
-            }
-            st4<_Float16>(&sHi[lc * LS + 16 * (wave * MT + m) + 4 * lg], hi);
-            st4<_Float16>(&sLo[lc * LS + 16 * (wave * MT + m) + 4 * lg], cvt4<_Float16>(lo));
-        }
-        lds_sync();
-        const float* sm = sw.summ + ((long)s * BH + bh) * D * 2 * D;
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int key = 16 * (wave * MT + m);
-            f32x4 acc;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = sm[(key + 4 * lg + e) * 2 * D + col];  // R_s
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                const float* mrow = sm + (long)(key + lc) * 2 * D + D + 32 * kk + 8 * lg;
-                const float4 a0 = *reinterpret_cast<const float4*>(mrow);
-                const float4 a1 = *reinterpret_cast<const float4*>(mrow + 4);
-                const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-                F8 ahi, alo;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    ahi[j] = static_cast<_Float16>(av[j]);
-                    alo[j] = static_cast<_Float16>(av[j] - static_cast<float>(ahi[j]));
-                }
-                const F8 bhi = ld8<_Float16>(&sHi[lc * LS + 32 * kk + 8 * lg]);
-                const F8 blo = ld8<_Float16>(&sLo[lc * LS + 32 * kk + 8 * lg]);
-                acc = M::k32(ahi, bhi, acc);
-                acc = M::k32(ahi, blo, acc);
-                acc = M::k32(alo, bhi, acc);
-            }
-            hs[m] = acc;
-        }
-        lds_sync();
     }
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int i = 0; i < NB - 1; ++i)
+        if (s + i < S) apply(pb[i], s + i);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            state_out[((long)bh * D + 16 * (wave * MT + m) + 4 * lg + e) * D + col] = hs[m][e];
+    for (int e = 0; e < 4; ++e)
+        state_out[((long)bh * D + 16 * wave + 4 * lg + e) * D + col] = hs[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -810,9 +824,7 @@ static hipError_t launch_chunked_t(const void* q, const void* k, const void* v, 
                        p.G, p.S, total);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((seg_combine<D>), dim3((unsigned)(BH * (D / 16))), dim3(256), 0, stream, sw,
-                       state_in, state_out, (int)BH, p.S);
-    e = hipGetLastError();
+    e = launch_seg_combine(sw.summ, sw.sst, state_in, state_out, (int)BH, p.S, D, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_chain<In, D, DVT, CHAIN_OUT>),
                        dim3((unsigned)(BH * p.S * (D / DVT))), dim3(256), 0, stream,
@@ -825,11 +837,11 @@ hipError_t launch_seg_combine(float* summ, float* sst, const float* state_in, fl
                               int BH, int S, int D, hipStream_t stream) {
     const SegWs sw{summ, sst};
     if (D == 64)
-        hipLaunchKernelGGL((seg_combine<64>), dim3((unsigned)(BH * 4)), dim3(256), 0, stream, sw,
-                           state_in, state_out, BH, S);
+        hipLaunchKernelGGL((seg_combine<64>), dim3((unsigned)(BH * 4)), dim3(64 * 4), 0, stream,
+                           sw, state_in, state_out, BH, S);
     else
-        hipLaunchKernelGGL((seg_combine<128>), dim3((unsigned)(BH * 8)), dim3(256), 0, stream, sw,
-                           state_in, state_out, BH, S);
+        hipLaunchKernelGGL((seg_combine<128>), dim3((unsigned)(BH * 8)), dim3(64 * 8), 0, stream,
+                           sw, state_in, state_out, BH, S);
     return hipGetLastError();
 }
 

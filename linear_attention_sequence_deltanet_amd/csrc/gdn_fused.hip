@@ -62,7 +62,7 @@ __device__ __forceinline__ H8 zero_h8() {
 }  // namespace
 
 struct FusedSeg {
-    float* summ;   // [S][BH][D][2D]  [R | M] per segment (SUM writes, combine reads)
+    float* summ;   // [S][BH] segment summaries of 8 D^2 bytes (SUM writes, combine reads)
     float* sst;    // [S][BH][D][D]   start state per segment (combine writes, OUT reads)
     float* sink;   // [64][D]         absorbs output stores of rows past the end
 };
@@ -471,22 +471,48 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     }
 
     // ---- segment result
-    float* dst = nullptr;
-    int ldd = D;
     if (OUT) {
-        if (S == 1) dst = state_out + (long)bh * D * D;
-    } else {
-        dst = fs.summ + ((long)seg * BH + bh) * D * 2 * D;
-        ldd = 2 * D;
-    }
-    if (dst) {
-#pragma unroll
-        for (int j = 0; j < TPW; ++j)
+        if (S == 1) {
+            float* dst = state_out + (long)bh * D * D;
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    dst[(16 * m + 4 * lg + e) * ldd + j * D + colw + lc] = hs[j][m][e];
+                for (int e = 0; e < 4; ++e) dst[(16 * m + 4 * lg + e) * D + colw + lc] = hs[0][m][e];
+        }
+    } else {
+        // segment summary in the combine's fragment order (summary_store()
+        // defines it element by element): R tiles are this wave's C-layout
+        // tiles as they are; M (fp16 high and low parts) goes through this
+        // wave's staging area as [part][key][16 columns] and leaves as 16-byte
+        // A-operand slots: its 16 input-key columns are half of the 32-key block
+        // colw / 32, lane groups 2 (wave & 1) and 2 (wave & 1) + 1.
+        float* sm = fs.summ + ((long)seg * BH + bh) * D * 2 * D;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            *reinterpret_cast<f32x4*>(sm + ((wave * (D / 16) + m) * 64 + lane) * 4) = hs[0][m];
+        _Float16* mt = stg;  // 2 D 16 halves, within this wave's staging
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * m + 4 * lg + e;
+                const float x = hs[TPW - 1][m][e];
+                const _Float16 hi = static_cast<_Float16>(x);
+                mt[row * 16 + lc] = hi;
+                mt[D * 16 + row * 16 + lc] = static_cast<_Float16>(x - static_cast<float>(hi));
+            }
+        lds_sync();
+        _Float16* mh = reinterpret_cast<_Float16*>(sm + D * D);
+#pragma unroll
+        for (int it = 0; it < D / 32; ++it) {
+            const int slot = it * 64 + lane;
+            const int m = slot >> 5, half = (slot >> 4) & 1, row = slot & 15;
+            const int lane_f = (2 * (wave & 1) + half) * 16 + row;
+            const int off = ((m * (D / 32) + (wave >> 1)) * 64 + lane_f) * 8;
+            const int src = (16 * m + row) * 16 + 8 * half;
+            *reinterpret_cast<H8*>(mh + off) = *reinterpret_cast<const H8*>(&mt[src]);
+            *reinterpret_cast<H8*>(mh + D * D + off) = *reinterpret_cast<const H8*>(&mt[D * 16 + src]);
+        }
     }
 }
 

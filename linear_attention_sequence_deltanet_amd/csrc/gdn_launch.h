@@ -22,8 +22,9 @@ hipError_t launch_chunked(const void* q, const void* k, const void* v, int dtype
                           float* state_out, float* o, int B, int T, int H, int D, void* ws,
                           hipStream_t stream);
 
-// Sequential combine of per-segment affine maps [R | M] ([S][BH][D][2D] f32):
-// writes every segment's start state to sst ([S][BH][D][D]) and the final state.
+// Sequential combine of per-segment affine maps ([S][BH] summaries of 8 D^2
+// bytes each, laid out as summary_store() writes them): writes every segment's
+// start state to sst ([S][BH][D][D] f32) and the final state.
 hipError_t launch_seg_combine(float* summ, float* sst, const float* state_in, float* state_out,
                               int BH, int S, int D, hipStream_t stream);
 
