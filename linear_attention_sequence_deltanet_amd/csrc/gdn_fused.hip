@@ -52,11 +52,41 @@ __device__ __forceinline__ H8 bf16x8_to_f16(uint4 w) {
     return r;
 }
 
-__device__ __forceinline__ H8 zero_h8() {
-    H8 r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = _Float16(0);
-    return r;
+// Raw buffer access with a per-chunk descriptor: the hardware bounds check
+// (offset >= `bytes`) returns zeros for loads and drops stores, which pads a
+// ragged last chunk and discards its missing rows without lane-level tests.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, unsigned off) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return uint4{x[0], x[1], x[2], x[3]};
+}
+__device__ __forceinline__ float buf_load4(rsrc_t r, unsigned off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void buf_store4(rsrc_t r, unsigned off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)off, 0, 0);
+}
+
+// DPP move of a wave's values (lanes without a source, or in rows outside
+// ROWS, read 0).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each
+// 16-lane row, then the broadcasts of lanes 15 and 31 into the later rows.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp_move<0x111, 0xf>(x);  // row_shr:1
+    x += dpp_move<0x112, 0xf>(x);  // row_shr:2
+    x += dpp_move<0x114, 0xf>(x);  // row_shr:4
+    x += dpp_move<0x118, 0xf>(x);  // row_shr:8
+    x += dpp_move<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_move<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
 }
 
 }  // namespace
@@ -64,7 +94,6 @@ __device__ __forceinline__ H8 zero_h8() {
 struct FusedSeg {
     float* summ;   // [S][BH] segment summaries of 8 D^2 bytes (SUM writes, combine reads)
     float* sst;    // [S][BH][D][D]   start state per segment (combine writes, OUT reads)
-    float* sink;   // [64][D]         absorbs output stores of rows past the end
 };
 
 // Row-contiguous [rows][64] token tiles written by transposition (K^T, V^T):
@@ -88,13 +117,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     constexpr int LD = D + 8;             // row stride of [64][D] tiles
     constexpr int LA = FC + 8;            // row stride of [*][64] tiles
     constexpr int NL = FC * D / 8 / NTH;  // 8-element input groups per thread per tensor
-    constexpr int STG = 2 * 16 * LA > 16 * LD ? 2 * 16 * LA : 16 * LD;  // staging per tile
+    constexpr int STG = 16 * LD;          // staging per tile: state copy, then Delta^T
 
     __shared__ __align__(16) _Float16 sK[FC * LD];
     __shared__ __align__(16) _Float16 sQ[OUT ? FC * LD : 8];
     __shared__ __align__(16) _Float16 sW[FC * LD];      // -W [t][key]
-    __shared__ __align__(16) _Float16 sKT[D * LA];      // K^T [key][t] (swizzled)
-    __shared__ __align__(16) _Float16 sVT[D * LA];      // V^T [col][t] (swizzled)
+    __shared__ __align__(16) _Float16 sV[FC * LD];
+    __shared__ __align__(16) _Float16 sKT[D * LA];      // (diag(e) K)^T [key][t] (swizzled)
     __shared__ __align__(16) _Float16 sA[FC * LA];      // -A off-diagonal, (T_bb - I) diagonal blocks
     __shared__ __align__(16) _Float16 sP[OUT ? FC * LA : 8];
     __shared__ __align__(16) _Float16 sStg[NW * TPW * STG];  // per-wave staging
@@ -138,29 +167,31 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 }
     }
 
-    // ---- raw input prefetch (one chunk ahead)
+    // ---- raw input prefetch (one chunk ahead).  Rows past the end of the
+    // sequence read as zeros (q, k, v, g, beta), which is the padding of a
+    // ragged last chunk.
     uint4 rq[NL], rk[NL], rv[NL];
     float rg = 0.f, rb = 0.f;
-    // per-lane element offsets within a chunk (rows past the end re-read the last row)
     auto issue_loads = [&](int c) {
         const long t0 = (long)c * FC;
         const int n = (int)min((long)FC, (long)T - t0);
         const long base = (((long)b * T + t0) * H + h) * D;  // scalar
-        const bf16_t* qb = q + base;
-        const bf16_t* kb = k + base;
-        const bf16_t* vb = v + base;
+        const unsigned bytes = (unsigned)(((n - 1) * HD + D) * 2);
+        const rsrc_t rsq = make_rsrc(q + base, bytes), rsk = make_rsrc(k + base, bytes),
+                     rsv = make_rsrc(v + base, bytes);
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int idx = tid + NTH * i, r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-            const unsigned off = (unsigned)(min(r, n - 1) * (int)HD + c8);
-            if (OUT) rq[i] = *reinterpret_cast<const uint4*>(qb + off);
-            rk[i] = *reinterpret_cast<const uint4*>(kb + off);
-            rv[i] = *reinterpret_cast<const uint4*>(vb + off);
+            const unsigned off = (unsigned)((r * (int)HD + c8) * 2);
+            if (OUT) rq[i] = buf_load16(rsq, off);
+            rk[i] = buf_load16(rsk, off);
+            rv[i] = buf_load16(rsv, off);
         }
         if (wave == 0) {
-            const long tok = ((long)b * T + t0 + min(lane, n - 1)) * H + h;
-            rg = g[tok];
-            rb = beta[tok];
+            const long tok = ((long)b * T + t0) * H + h;
+            const unsigned gbytes = (unsigned)(((n - 1) * H + 1) * 4);
+            rg = buf_load4(make_rsrc(g + tok, gbytes), (unsigned)(lane * H * 4));
+            rb = buf_load4(make_rsrc(beta + tok, gbytes), (unsigned)(lane * H * 4));
         }
     };
     issue_loads(c_begin);
@@ -177,31 +208,18 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         const int lg = lane_i >> 4, lc = lane_i & 15;
         const int tid = wave * 64 + lane_i;
 
-        // ---- inputs into LDS (f16): row-major K, Q; transposed K^T, V^T; gates
+        // ---- inputs into LDS (f16, row-major K, Q, V); gates
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int idx = tid + NTH * i, r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-            const bool ok = r < n;
-            const H8 fk = ok ? bf16x8_to_f16(rk[i]) : zero_h8();
-            *reinterpret_cast<H8*>(&sK[r * LD + c8]) = fk;
-            if (OUT) *reinterpret_cast<H8*>(&sQ[r * LD + c8]) = ok ? bf16x8_to_f16(rq[i]) : zero_h8();
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sKT[tsw<LA>(c8 + j, r)] = fk[j];
-            {
-                const H8 fv = ok ? bf16x8_to_f16(rv[i]) : zero_h8();
-#pragma unroll
-                for (int j = 0; j < 8; ++j) sVT[tsw<LA>(c8 + j, r)] = fv[j];
-            }
+            *reinterpret_cast<H8*>(&sK[r * LD + c8]) = bf16x8_to_f16(rk[i]);
+            if (OUT) *reinterpret_cast<H8*>(&sQ[r * LD + c8]) = bf16x8_to_f16(rq[i]);
+            *reinterpret_cast<H8*>(&sV[r * LD + c8]) = bf16x8_to_f16(rv[i]);
         }
         if (wave == 0) {
-            float gv = lane < n ? rg : 0.f;
-            const float bv = lane < n ? rb : 0.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float up = __shfl_up(gv, off, 64);
-                if (lane >= off) gv += up;
-            }
-            const float gC = __shfl(gv, 63, 64);
+            const float bv = rb;
+            const float gv = wave_prefix_sum(rg);
+            const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 63));
             const float eg = __expf(gv);
             sgam[lane] = gv;
             sbeta[lane] = bv;
@@ -213,66 +231,60 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         if (c + 1 < c_end) issue_loads(c + 1);
         lds_sync();
 
-        // ---- Gram tiles.  Waves 0-3: diagonal K K^T tile (w, w), inverted right
-        // away by the same wave.  All waves: the six off-diagonal K K^T tiles and,
-        // for OUT, the Q K^T tiles (lower ones computed, upper ones zero).
-        if (wave < 4) {
-            const int mk = wave;
-            f32x4 acc = zero4();
+        // ---- Gram tiles.  Wave 0: the four diagonal K K^T tiles and the
+        // inverses of the four (I + A_bb) blocks.  Waves 1..: the six
+        // off-diagonal K K^T tiles and, for OUT, the ten lower Q K^T tiles.
+        if (wave == 0) {
+            // A_bb (strictly lower, beta- and decay-scaled) column-major:
+            // sAd[b][i][r] = A[16 b + r][16 b + i]
 #pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                const H8 a = ld8<_Float16>(&sK[(16 * mk + lc) * LD + 32 * kk + 8 * lg]);
-                acc = MF::k32(a, a, acc);
+            for (int bb = 0; bb < 4; ++bb) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kk = 0; kk < D / 32; ++kk) {
+                    const H8 a = ld8<_Float16>(&sK[(16 * bb + lc) * LD + 32 * kk + 8 * lg]);
+                    acc = MF::k32(a, a, acc);
+                }
+                const f32x4 gr = *reinterpret_cast<const f32x4*>(&sgam[16 * bb + 4 * lg]);
+                const f32x4 br = *reinterpret_cast<const f32x4*>(&sbeta[16 * bb + 4 * lg]);
+                const float gi = sgam[16 * bb + lc];
+                f32x4 av;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ex = __expf(fminf(gr[e] - gi, 0.f));
+                    av[e] = lc < 4 * lg + e ? br[e] * ex * acc[e] : 0.f;
+                }
+                *reinterpret_cast<f32x4*>(&sAd[bb][lc][4 * lg]) = av;
             }
-            const f32x4 gr = *reinterpret_cast<const f32x4*>(&sgam[16 * mk + 4 * lg]);
-            const f32x4 br = *reinterpret_cast<const f32x4*>(&sbeta[16 * mk + 4 * lg]);
-            const float gi = sgam[16 * mk + lc];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                sAd[mk][4 * lg + e][lc] = lc < 4 * lg + e ? br[e] * __expf(gr[e] - gi) * acc[e] : 0.f;
-            // (I + A_ww)^{-1} by fp32 forward substitution, one column per lane;
-            // only this wave touches sAd[w], so no workgroup barrier is needed.
-            if (lane_i < 16) {
-                const int cc = lane_i;
+            // (I + A_bb)^{-1} in fp32: lane group g inverts block g, lane c of
+            // it computing column c by column-wise elimination (x_r -= A[r][i]
+            // x_i for r > i once x_i is final).  Only this wave touches sAd, and
+            // a wave's LDS accesses complete in order, so no barrier is needed.
+            {
                 float x[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
+                for (int r = 0; r < 16; ++r) x[r] = r == lc ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 0; i < 15; ++i) {
                     float a[16];
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const f32x4 t4 = *reinterpret_cast<const f32x4*>(&sAd[mk][r][4 * q4]);
+                    for (int q4 = (i + 1) / 4; q4 < 4; ++q4) {
+                        const f32x4 t4 = *reinterpret_cast<const f32x4*>(&sAd[lg][i][4 * q4]);
                         a[4 * q4] = t4[0]; a[4 * q4 + 1] = t4[1]; a[4 * q4 + 2] = t4[2]; a[4 * q4 + 3] = t4[3];
                     }
-                    float s0 = (r == cc) ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
-                    for (int i = 0; i < r; ++i) {
-                        if (i & 1) s1 -= a[i] * x[i];
-                        else s0 -= a[i] * x[i];
-                    }
-                    x[r] = s0 + s1;
-                    if (r % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bound the hoisting of row loads
+                    for (int r = i + 1; r < 16; ++r) x[r] -= a[r] * x[i];
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    sA[(16 * mk + r) * LA + 16 * mk + cc] = static_cast<_Float16>(r == cc ? 0.f : x[r]);
+                    sA[(16 * lg + r) * LA + 16 * lg + lc] = static_cast<_Float16>(r == lc ? 0.f : x[r]);
             }
-        }
-        {
+        } else {
             // Tile list: the 6 off-diagonal K K^T tiles, then (OUT) the 10 lower
-            // Q K^T tiles.  With 8 waves the four waves without a diagonal block
-            // take the first 12 tiles, the other four one Q K^T tile each.
+            // Q K^T tiles, dealt to waves 1 .. NW-1 in turn; fixed per-wave
+            // sequences let consecutive tiles overlap.
             constexpr int NREAL = OUT ? 16 : 6;
-            int tt = wave, tstep = NW, tend = NREAL;
-            if (NW == 8) {
-                tstep = 4;
-                if (wave >= 4) {
-                    tt = wave - 4;
-                    tend = OUT ? 12 : NREAL;
-                } else {
-                    tt = 12 + wave;
-                }
-            }
-            for (; tt < tend; tt += tstep) {
+            auto tile = [&](int tt) {
                 const bool kq = tt < 6;  // K K^T off-diagonal
                 int mi, ni;
                 if (kq) {
@@ -296,19 +308,30 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * mi + 4 * lg + e;
+                    const float ex = __expf(fminf(gr[e] - gi, 0.f));
                     if (kq) {
-                        sA[r * LA + i] = static_cast<_Float16>(-(br[e] * __expf(gr[e] - gi) * acc[e]));
+                        sA[r * LA + i] = static_cast<_Float16>(-(br[e] * ex * acc[e]));
                     } else {
-                        const float pv = i <= r ? __expf(gr[e] - gi) * acc[e] : 0.f;
-                        sP[r * LA + i] = static_cast<_Float16>(pv);
+                        sP[r * LA + i] = static_cast<_Float16>(i <= r ? ex * acc[e] : 0.f);
                     }
                 }
+            };
+            if (NW == 8) {
+                // OUT: waves 1, 2 take three tiles, waves 3..7 two; SUM: waves 1..6 one
+                if (OUT || wave - 1 < NREAL) tile(wave - 1);
+                if (OUT) {
+                    tile(wave + 6);
+                    if (wave <= 2) tile(wave + 13);
+                }
+            } else {
+                for (int tt = wave - 1; tt < NREAL; tt += NW - 1) tile(tt);
             }
             // the two upper P tiles that the output products read, (0,1) and (2,3)
-            if (OUT && wave < 2) {
+            if (OUT && wave >= NW - 2) {
+                const int z = wave - (NW - 2);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    sP[(32 * wave + 4 * lg + e) * LA + 32 * wave + 16 + lc] = _Float16(0);
+                    sP[(32 * z + 4 * lg + e) * LA + 32 * z + 16 + lc] = _Float16(0);
             }
         }
         lds_sync();
@@ -318,24 +341,30 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         // for all of this wave's right-hand sides at once (U tiles of its state
         // columns, kept in registers, and -W tiles, written to LDS); the
         // independent chains interleave on the matrix cores.
-        constexpr int NR = 2;  // right-hand-side tiles: U tile w, W tile w
+        // The right-hand-side tiles come from row-major V and K through a
+        // product with the 16x16 identity, which delivers them (exactly) in the
+        // accumulator layout, token rows 4 lg + e of column lc; the K tiles,
+        // scaled by the end factors e, are also this wave's 16 rows of
+        // (diag(e) K)^T for the state update.  The W right-hand side is negated,
+        // so the solve yields -W directly.
+        constexpr int NR = 2;  // right-hand-side tiles: U tile w, -W tile w
         f32x4 res[NR][4];
         {
+            H4 ident;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ident[e] = static_cast<_Float16>(4 * lg + e == lc ? 1.f : 0.f);
             H4 xh[NR][4];
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
                 const f32x4 fb = *reinterpret_cast<const f32x4*>(&sbeta[16 * bb + 4 * lg]);
                 const f32x4 fg = *reinterpret_cast<const f32x4*>(&sBG[16 * bb + 4 * lg]);
+                const f32x4 fe = *reinterpret_cast<const f32x4*>(&sE[16 * bb + 4 * lg]);
+                const f32x4 vt = MF::k16(ld4<_Float16>(&sV[(16 * bb + lc) * LD + colw + 4 * lg]), ident, zero4());
+                const f32x4 kt = MF::k16(ld4<_Float16>(&sK[(16 * bb + lc) * LD + colw + 4 * lg]), ident, zero4());
+                st4<_Float16>(&sKT[tsw<LA>(colw + lc, 16 * bb + 4 * lg)], cvt4<_Float16>(fe * kt));
                 f32x4 acc[NR];
-#pragma unroll
-                for (int t = 0; t < NR; ++t) {
-                    const bool is_w = t == 1;
-                    const int col = colw + lc;
-                    const H4 x4 = ld4<_Float16>(is_w ? &sKT[tsw<LA>(col, 16 * bb + 4 * lg)]
-                                                     : &sVT[tsw<LA>(col, 16 * bb + 4 * lg)]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[t][e] = (is_w ? fg[e] : fb[e]) * static_cast<float>(x4[e]);
-                }
+                acc[0] = fb * vt;
+                acc[1] = -(fg * kt);
 #pragma unroll
                 for (int j = 0; j < bb; ++j) {
                     const H4 aj = ld4<_Float16>(&sA[(16 * bb + lc) * LA + 16 * j + 4 * lg]);
@@ -358,9 +387,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             if (TPW == 2) u[TPW - 1][bb] = zero4();  // identity columns: no U
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                sW[(16 * bb + 4 * lg + e) * LD + colw + lc] = static_cast<_Float16>(-res[1][bb][e]);
+                sW[(16 * bb + 4 * lg + e) * LD + colw + lc] = static_cast<_Float16>(res[1][bb][e]);
         }
-        lds_sync();  // -W complete
+        lds_sync();  // -W and K^T complete
 
         // ---- state update for this wave's columns (no workgroup barrier)
         // fp16 copy of the state tiles, [col][key], read back as B fragments
@@ -374,8 +403,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
             for (int j = 0; j < TPW; ++j) bs[kk][j] = ld8<_Float16>(&stg[j * STG + lc * LD + 32 * kk + 8 * lg]);
-        // Delta = U - W H0 one row tile at a time; Delta^T and (e Delta)^T staged
-        // as [col][t] over the state copy (already read into bs)
+        // Delta = U - W H0 one row tile at a time; Delta^T staged as [col][t]
+        // over the state copy (already read into bs)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             f32x4 dl[TPW];
@@ -387,13 +416,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
 #pragma unroll
                 for (int j = 0; j < TPW; ++j) dl[j] = MF::k32(aw, bs[kk][j], dl[j]);
             }
-            const f32x4 ev = *reinterpret_cast<const f32x4*>(&sE[16 * mt + 4 * lg]);
 #pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-                if (OUT) st4<_Float16>(&stg[j * STG + lc * LA + 16 * mt + 4 * lg], cvt4<_Float16>(dl[j]));
-                st4<_Float16>(&stg[j * STG + 16 * LA + lc * LA + 16 * mt + 4 * lg], cvt4<_Float16>(ev * dl[j]));
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < TPW; ++j)
+                st4<_Float16>(&stg[j * STG + lc * LA + 16 * mt + 4 * lg], cvt4<_Float16>(dl[j]));
+            if (mt == 1) __builtin_amdgcn_sched_barrier(0);
         }
         if (OUT) {
             // O = diag(Gam) Q H0 + P Delta, one row tile at a time
@@ -403,11 +429,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 d0[j] = ld8<_Float16>(&stg[j * STG + lc * LA + 8 * lg]);
                 d1[j] = ld8<_Float16>(&stg[j * STG + lc * LA + 32 + 8 * lg]);
             }
-            const bool full = n == FC;
-            float* ob = o + ((long)b * T + t0) * HD + (long)h * D + colw;  // scalar
-            unsigned ooff[4];  // this lane's rows 4 lg + e (elements)
+            // output rows of row tile mt through a descriptor that ends at the
+            // sequence's last row, so rows past it are dropped
+            const float* ob = o + ((long)b * T + t0) * HD + (long)h * D + colw;  // scalar
+            unsigned ooff[4];  // this lane's rows 4 lg + e, bytes
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ooff[e] = (unsigned)((4 * lg + e) * (int)HD + lc);
+            for (int e = 0; e < 4; ++e) ooff[e] = (unsigned)(((4 * lg + e) * (int)HD + lc) * 4);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 f32x4 oq[TPW];
@@ -426,34 +453,24 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                     oq[j] = MF::k32(ap0, d0[j], gm * oq[j]);
                     if (mt >= 2) oq[j] = MF::k32(ld8<_Float16>(&sP[(16 * mt + lc) * LA + 32 + 8 * lg]), d1[j], oq[j]);
                 }
-                if (full) {
-                    float* obm = ob + (long)16 * mt * HD;  // scalar
+                {
+                    const int rows = n - 16 * mt;  // valid rows of this row tile (scalar)
+                    const rsrc_t ro = make_rsrc(ob + (long)16 * mt * HD,
+                                                rows > 0 ? (unsigned)(((rows - 1) * (int)HD + 16) * 4) : 0u);
 #pragma unroll
-                    for (int j = 0; j < TPW; ++j)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) obm[ooff[e] + 16 * j] = oq[j][e];
-                } else {
-#pragma unroll
-                    for (int j = 0; j < TPW; ++j)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int rr = 16 * mt + 4 * lg + e;
-                            float* dst = rr < n ? ob + rr * HD + 16 * j + lc
-                                                : fs.sink + rr * D + colw + 16 * j + lc;
-                            *dst = oq[j][e];
-                        }
+                    for (int e = 0; e < 4; ++e) buf_store4(ro, ooff[e], oq[0][e]);
                 }
-                __builtin_amdgcn_sched_barrier(0);
+                if (mt == 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // H = Gam_C H0 + K^T (e Delta)
+        // H = Gam_C H0 + (diag(e) K)^T Delta
         {
             const float GC = sGC;
             H8 e0[TPW], e1[TPW];
 #pragma unroll
             for (int j = 0; j < TPW; ++j) {
-                e0[j] = ld8<_Float16>(&stg[j * STG + 16 * LA + lc * LA + 8 * lg]);
-                e1[j] = ld8<_Float16>(&stg[j * STG + 16 * LA + lc * LA + 32 + 8 * lg]);
+                e0[j] = ld8<_Float16>(&stg[j * STG + lc * LA + 8 * lg]);
+                e1[j] = ld8<_Float16>(&stg[j * STG + lc * LA + 32 + 8 * lg]);
             }
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
@@ -549,9 +566,8 @@ FPlan fused_plan(int B, int T, int H) {
 
 size_t fused_workspace_bytes(int B, int T, int H, int D) {
     const FPlan p = fused_plan(B, T, H);
-    size_t bytes = (size_t)FC * D * 4;  // sink
-    if (p.S > 1) bytes += (size_t)p.S * B * H * D * D * 4 * 3;
-    return bytes;
+    // segment summaries (2 D^2 floats) and start states (D^2 floats)
+    return p.S > 1 ? (size_t)p.S * B * H * D * D * 4 * 3 : 0;
 }
 
 template <int D>
@@ -561,8 +577,7 @@ static hipError_t launch_fused_t(const void* q, const void* k, const void* v, co
     const FPlan p = fused_plan(B, T, H);
     const long BH = (long)B * H;
     FusedSeg fs;
-    fs.sink = static_cast<float*>(ws);
-    fs.summ = fs.sink + FC * D;
+    fs.summ = static_cast<float*>(ws);
     fs.sst = fs.summ + (size_t)p.S * BH * D * 2 * D;
     const bf16_t* qq = static_cast<const bf16_t*>(q);
     const bf16_t* kk = static_cast<const bf16_t*>(k);
