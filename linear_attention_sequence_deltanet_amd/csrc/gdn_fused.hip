@@ -70,6 +70,30 @@ __device__ __forceinline__ void buf_store4(rsrc_t r, unsigned off, float x) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)off, 0, 0);
 }
 
+// fp16 pair (round to nearest even) as one dword
+__device__ __forceinline__ unsigned pack_f16x2(float a, float b) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 p = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(unsigned, p);
+}
+
+// k32 B operand (fp16) from two accumulator-layout tiles t0, t1 that hold the
+// 32 contraction rows 0-15 and 16-31: lane group g has rows 4g..4g+3 of each
+// tile and needs rows 8g..8g+7 of the pair.  Two lane-group exchanges
+// (halves of the wave, then odd/even 16-lane rows) move the packed pairs there
+// without going through LDS.
+__device__ __forceinline__ H8 acc_to_b32(f32x4 t0, f32x4 t1) {
+    const unsigned a0 = pack_f16x2(t0[0], t0[1]), a1 = pack_f16x2(t0[2], t0[3]);
+    const unsigned b0 = pack_f16x2(t1[0], t1[1]), b1 = pack_f16x2(t1[2], t1[3]);
+    const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+    const auto u0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+    const auto u1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    const u4 w = {u0[0], u1[0], u0[1], u1[1]};
+    return __builtin_bit_cast(H8, w);
+}
+
 // DPP move of a wave's values (lanes without a source, or in rows outside
 // ROWS, read 0).
 template <int CTRL, int ROWS>
@@ -117,7 +141,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     constexpr int LD = D + 8;             // row stride of [64][D] tiles
     constexpr int LA = FC + 8;            // row stride of [*][64] tiles
     constexpr int NL = FC * D / 8 / NTH;  // 8-element input groups per thread per tensor
-    constexpr int STG = 16 * LD;          // staging per tile: state copy, then Delta^T
 
     __shared__ __align__(16) _Float16 sK[FC * LD];
     __shared__ __align__(16) _Float16 sQ[OUT ? FC * LD : 8];
@@ -126,7 +149,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     __shared__ __align__(16) _Float16 sKT[D * LA];      // (diag(e) K)^T [key][t] (swizzled)
     __shared__ __align__(16) _Float16 sA[FC * LA];      // -A off-diagonal, (T_bb - I) diagonal blocks
     __shared__ __align__(16) _Float16 sP[OUT ? FC * LA : 8];
-    __shared__ __align__(16) _Float16 sStg[NW * TPW * STG];  // per-wave staging
+    __shared__ __align__(16) _Float16 sStg[OUT ? 8 : NW * 2 * D * 16];  // SUM: summary transpose
     __shared__ __align__(16) float sAd[4][16][16];
     __shared__ __align__(16) float sgam[FC], sbeta[FC], sGam[FC], sE[FC], sBG[FC];
     __shared__ float sGC;
@@ -141,7 +164,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lg = lane >> 4, lc = lane & 15;
     const long HD = (long)H * D;
-    _Float16* stg = sStg + wave * TPW * STG;
     const int colw = 16 * wave;  // this wave's value columns (and identity columns in SUM)
 
     // ---- state tiles (fp32, C layout): key 16 m + 4 lg + e, column colw + 16 j + lc
@@ -391,87 +413,61 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         }
         lds_sync();  // -W and K^T complete
 
-        // ---- state update for this wave's columns (no workgroup barrier)
-        // fp16 copy of the state tiles, [col][key], read back as B fragments
-#pragma unroll
-        for (int j = 0; j < TPW; ++j)
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                st4<_Float16>(&stg[j * STG + lc * LD + 16 * m + 4 * lg], cvt4<_Float16>(hs[j][m]));
+        // ---- state update for this wave's columns (no workgroup barrier).
+        // The state and Delta enter the products as fp16 B operands built from
+        // their accumulator-layout tiles in registers.
         H8 bs[D / 32][TPW];
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
-            for (int j = 0; j < TPW; ++j) bs[kk][j] = ld8<_Float16>(&stg[j * STG + lc * LD + 32 * kk + 8 * lg]);
-        // Delta = U - W H0 one row tile at a time; Delta^T staged as [col][t]
-        // over the state copy (already read into bs)
+            for (int j = 0; j < TPW; ++j) bs[kk][j] = acc_to_b32(hs[j][2 * kk], hs[j][2 * kk + 1]);
+        // Delta = U - W H0, one row tile at a time
+        f32x4 dl[TPW][4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            f32x4 dl[TPW];
 #pragma unroll
-            for (int j = 0; j < TPW; ++j) dl[j] = u[j][mt];
+            for (int j = 0; j < TPW; ++j) dl[j][mt] = u[j][mt];
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk) {
                 const H8 aw = ld8<_Float16>(&sW[(16 * mt + lc) * LD + 32 * kk + 8 * lg]);
 #pragma unroll
-                for (int j = 0; j < TPW; ++j) dl[j] = MF::k32(aw, bs[kk][j], dl[j]);
+                for (int j = 0; j < TPW; ++j) dl[j][mt] = MF::k32(aw, bs[kk][j], dl[j][mt]);
             }
-#pragma unroll
-            for (int j = 0; j < TPW; ++j)
-                st4<_Float16>(&stg[j * STG + lc * LA + 16 * mt + 4 * lg], cvt4<_Float16>(dl[j]));
             if (mt == 1) __builtin_amdgcn_sched_barrier(0);
         }
-        if (OUT) {
-            // O = diag(Gam) Q H0 + P Delta, one row tile at a time
-            H8 d0[TPW], d1[TPW];
+        H8 db[2][TPW];  // Delta as B operand, token blocks 0-31 and 32-63
 #pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-                d0[j] = ld8<_Float16>(&stg[j * STG + lc * LA + 8 * lg]);
-                d1[j] = ld8<_Float16>(&stg[j * STG + lc * LA + 32 + 8 * lg]);
-            }
-            // output rows of row tile mt through a descriptor that ends at the
-            // sequence's last row, so rows past it are dropped
+        for (int j = 0; j < TPW; ++j) {
+            db[0][j] = acc_to_b32(dl[j][0], dl[j][1]);
+            db[1][j] = acc_to_b32(dl[j][2], dl[j][3]);
+        }
+        if (OUT) {
+            // O = diag(Gam) Q H0 + P Delta, one row tile at a time; output rows
+            // through a descriptor that ends at the sequence's last row
             const float* ob = o + ((long)b * T + t0) * HD + (long)h * D + colw;  // scalar
             unsigned ooff[4];  // this lane's rows 4 lg + e, bytes
 #pragma unroll
             for (int e = 0; e < 4; ++e) ooff[e] = (unsigned)(((4 * lg + e) * (int)HD + lc) * 4);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                f32x4 oq[TPW];
+                f32x4 oq = zero4();
 #pragma unroll
-                for (int j = 0; j < TPW; ++j) oq[j] = zero4();
-#pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk) {
-                    const H8 aq = ld8<_Float16>(&sQ[(16 * mt + lc) * LD + 32 * kk + 8 * lg]);
-#pragma unroll
-                    for (int j = 0; j < TPW; ++j) oq[j] = MF::k32(aq, bs[kk][j], oq[j]);
-                }
+                for (int kk = 0; kk < D / 32; ++kk)
+                    oq = MF::k32(ld8<_Float16>(&sQ[(16 * mt + lc) * LD + 32 * kk + 8 * lg]), bs[kk][0], oq);
                 const f32x4 gm = *reinterpret_cast<const f32x4*>(&sGam[16 * mt + 4 * lg]);
-                const H8 ap0 = ld8<_Float16>(&sP[(16 * mt + lc) * LA + 8 * lg]);
+                oq = MF::k32(ld8<_Float16>(&sP[(16 * mt + lc) * LA + 8 * lg]), db[0][0], gm * oq);
+                if (mt >= 2) oq = MF::k32(ld8<_Float16>(&sP[(16 * mt + lc) * LA + 32 + 8 * lg]), db[1][0], oq);
+                const int rows = n - 16 * mt;  // valid rows of this row tile (scalar)
+                const rsrc_t ro = make_rsrc(ob + (long)16 * mt * HD,
+                                            rows > 0 ? (unsigned)(((rows - 1) * (int)HD + 16) * 4) : 0u);
 #pragma unroll
-                for (int j = 0; j < TPW; ++j) {
-                    oq[j] = MF::k32(ap0, d0[j], gm * oq[j]);
-                    if (mt >= 2) oq[j] = MF::k32(ld8<_Float16>(&sP[(16 * mt + lc) * LA + 32 + 8 * lg]), d1[j], oq[j]);
-                }
-                {
-                    const int rows = n - 16 * mt;  // valid rows of this row tile (scalar)
-                    const rsrc_t ro = make_rsrc(ob + (long)16 * mt * HD,
-                                                rows > 0 ? (unsigned)(((rows - 1) * (int)HD + 16) * 4) : 0u);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) buf_store4(ro, ooff[e], oq[0][e]);
-                }
+                for (int e = 0; e < 4; ++e) buf_store4(ro, ooff[e], oq[e]);
                 if (mt == 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
         // H = Gam_C H0 + (diag(e) K)^T Delta
         {
             const float GC = sGC;
-            H8 e0[TPW], e1[TPW];
-#pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-                e0[j] = ld8<_Float16>(&stg[j * STG + lc * LA + 8 * lg]);
-                e1[j] = ld8<_Float16>(&stg[j * STG + lc * LA + 32 + 8 * lg]);
-            }
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 const H8 ak0 = ld8<_Float16>(&sKT[tsw<LA>(16 * m + lc, 8 * lg)]);
@@ -479,8 +475,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
 #pragma unroll
                 for (int j = 0; j < TPW; ++j) {
                     f32x4 acc = hs[j][m] * GC;
-                    acc = MF::k32(ak0, e0[j], acc);
-                    hs[j][m] = MF::k32(ak1, e1[j], acc);
+                    acc = MF::k32(ak0, db[0][j], acc);
+                    hs[j][m] = MF::k32(ak1, db[1][j], acc);
                 }
                 if (m % 2 == 1) __builtin_amdgcn_sched_barrier(0);
             }
@@ -507,7 +503,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
 #pragma unroll
         for (int m = 0; m < MT; ++m)
             *reinterpret_cast<f32x4*>(sm + ((wave * (D / 16) + m) * 64 + lane) * 4) = hs[0][m];
-        _Float16* mt = stg;  // 2 D 16 halves, within this wave's staging
+        _Float16* mt = sStg + wave * 2 * D * 16;  // this wave's 2 D 16 halves
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
