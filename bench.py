@@ -6,10 +6,16 @@ A step is one whole-path call over one batch of synthetic inputs already in HBM:
   * decode: gdn_decode_step for 64 sequences x 16 heads, d=128, fp32 state updated
     in place, 1000 consecutive steps with fresh inputs (tokens/s, reported beside).
 Timing uses HIP events on the stream the library launches on (torch's current
-stream).  The fp64 oracle is timed on the host cores as a reported CPU baseline.
-Prints ONE JSON line.
+stream).  A second pass over the same steps records events between the
+library's kernels (gdn_set_profile_events) to time each kernel; the roofline
+object is the dominant kernel's.  Its `traffic` comes from the committed
+rocprofv3 counter summary when that summary was taken on the current kernel
+sources (else null).  The fp64 oracle is timed on the host cores as a reported
+CPU baseline.  Prints ONE JSON line.
 """
 import argparse
+import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +38,17 @@ PREFILL_FLOPS_PER_TOKEN_HEAD = 6 * 128 * 128 + 64 * (3 * 128 + 2 * 128)
 # g, beta (8) + o fp32 (512)
 DECODE_BYTES_PER_HEAD = 2 * 128 * 128 * 4 + 3 * 256 + 8 + 512
 
+# Kernels of one bf16 prefill call of several segments, in launch order, with
+# the algorithmic bytes per token x head each reads or writes.
+PREFILL_KERNELS = [("summary pass (gdn_fused<128,false>)", 2 * 256 + 8),
+                   ("segment combine (seg_combine<128>)", None),
+                   ("output pass (gdn_fused<128,true>)", PREFILL_BYTES_PER_TOKEN_HEAD)]
+# Sources the prefill kernels are built from; the counter summary records their hash.
+KERNEL_SOURCES = ["gdn_fused.hip", "gdn_chunk.hip", "gdn_device.h", "gdn_mfma.h",
+                  "gdn_launch.h", "gdn_api.cpp"]
+TRAFFIC_FILES = [os.path.join(ROOT, "profiles", f)
+                 for f in ("prefill8k_hbm_traffic.txt", "decode64_hbm_traffic.txt")]
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -43,7 +60,89 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="first copy this many MiB device to device three times (a copy of "
+                        "known size that calibrates hardware byte counters)")
     return p.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def ms(self, a, b):
+        t = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def kernel_times(gdn, call, steps, nmax=4):
+    """Run `call` `steps` times with the library's timing hook; returns the mean
+    duration (ms) of each kernel of a call, in launch order."""
+    import torch
+    ev = HipEvents()
+    handles = [ev.create(nmax) for _ in range(steps)]
+    try:
+        marks = []
+        for s in range(steps):
+            gdn.set_profile_events(handles[s])
+            call()
+            marks.append(gdn.profile_marks())
+        gdn.set_profile_events(None)
+        torch.cuda.synchronize()
+        nk = min(marks) - 1
+        return [float(np.mean([ev.ms(handles[s][i], handles[s][i + 1]) for s in range(steps)]))
+                for i in range(nk)]
+    finally:
+        gdn.set_profile_events(None)
+        torch.cuda.synchronize()
+        for h in handles:
+            ev.destroy(h)
+
+
+def sources_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "linear_attention_sequence_deltanet_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if it
+    was taken on the current sources."""
+    for path in TRAFFIC_FILES:
+        try:
+            lines = open(path).read().splitlines()
+        except OSError:
+            continue
+        for ln in lines:
+            if ln.startswith("traffic-json:"):
+                rec = json.loads(ln[len("traffic-json:"):])
+                k = rec.get("kernels", {}).get(kernel)
+                if k is not None:
+                    return k["hbm_bytes"] if rec.get("sources_sha256") == sources_hash() else None
+    return None
 
 
 def stage_bf16(arr, dev):
@@ -64,18 +163,20 @@ def time_prefill(gdn, args, dev):
     ws = torch.empty(max(16, gdn.prefill_workspace_bytes(B, T, H, dk, dk)), dtype=torch.uint8,
                      device=dev)
     stream = torch.cuda.current_stream(dev)
+    call = lambda: gdn.prefill(q, k, v, g, beta, None, state_out=st, o=o, workspace=ws)
     for _ in range(args.warmup):
-        gdn.prefill(q, k, v, g, beta, None, state_out=st, o=o, workspace=ws)
+        call()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(args.steps):
-        gdn.prefill(q, k, v, g, beta, None, state_out=st, o=o, workspace=ws)
+        call()
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    return d, ms, (B, T, H, dk)
+    kms = kernel_times(gdn, call, args.steps)
+    return d, ms, kms, (B, T, H, dk)
 
 
 def time_decode(gdn, args, dev):
@@ -92,6 +193,13 @@ def time_decode(gdn, args, dev):
     stream = torch.cuda.current_stream(dev)
     for n in range(min(N, 50)):  # warm-up
         gdn.decode_step(q[n], k[n], v[n], g[n], beta[n], state, o=o[n])
+    state.copy_(s0)
+    nk = min(N, 200)
+    ctr = iter(range(nk))
+    def call():
+        n = next(ctr)
+        gdn.decode_step(q[n], k[n], v[n], g[n], beta[n], state, o=o[n])
+    kms = kernel_times(gdn, call, nk, nmax=2)
     times = []
     for _ in range(args.decode_reps):
         state.copy_(s0)
@@ -105,7 +213,7 @@ def time_decode(gdn, args, dev):
         torch.cuda.synchronize()
         times.append(start.elapsed_time(end) / N)
     ms = float(np.median(times))
-    return ms, (N, B, H, dk)
+    return ms, kms, (N, B, H, dk)
 
 
 def cpu_baseline(d, seconds):
@@ -149,13 +257,32 @@ def main():
         __graft_entry__.build()
     import linear_attention_sequence_deltanet_amd as gdn
     dev = torch.device("cuda:0")
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib * 2 ** 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
-    d, ms, (B, T, H, dk) = time_prefill(gdn, args, dev)
+    d, ms, kms, (B, T, H, dk) = time_prefill(gdn, args, dev)
     tok_s = B * T / (ms / 1e3)
-    bytes_call = PREFILL_BYTES_PER_TOKEN_HEAD * B * T * H
-    flops_call = PREFILL_FLOPS_PER_TOKEN_HEAD * B * T * H
+    units = B * T * H
+    bytes_call = PREFILL_BYTES_PER_TOKEN_HEAD * units
+    flops_call = PREFILL_FLOPS_PER_TOKEN_HEAD * units
     gbs = bytes_call / (ms / 1e3) / 1e9
     tfs = flops_call / (ms / 1e3) / 1e12
+    if len(kms) != len(PREFILL_KERNELS):
+        raise RuntimeError("expected %d kernels per prefill call, the hook saw %d"
+                           % (len(PREFILL_KERNELS), len(kms)))
+    kernels = [{"kernel": name, "us": t * 1e3, "share": t / sum(kms)}
+               for (name, _), t in zip(PREFILL_KERNELS, kms)]
+    dom = int(np.argmax(kms))
+    dname, dbytes_unit = PREFILL_KERNELS[dom]
+    dsec = kms[dom] / 1e3
+    dbytes = dbytes_unit * units
+    dgbs = dbytes / dsec / 1e9
+    dtfs = flops_call / dsec / 1e12 if dom == len(PREFILL_KERNELS) - 1 else None
     line = {
         "metric": "Gated DeltaNet prefill tokens/s at H=16, d=128 (decode tokens/s beside)",
         "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -164,22 +291,34 @@ def main():
         "config": {"workload": "prefill8k: B=1, H=16, T=8192, d_k=d_v=128, bf16 q/k/v, "
                                "fp32 g/beta/state/o, chunk 64, zero initial state",
                    "global_batch": B, "seq_len": T, "heads": H, "head_dim": dk},
-        "roofline": {"kernel": "gdn_prefill (whole call)", "bound": "hbm", "achieved": gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": None,
-                     "mfma_tflops": tfs, "mfma_frac": tfs / MFMA_F16_PEAK_TFS,
-                     "bytes_per_call": bytes_call, "flops_per_call": flops_call},
+        "roofline": {"kernel": dname, "bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
+                     "traffic": committed_traffic(dname),
+                     "us_per_launch": kms[dom] * 1e3, "bytes_per_launch": dbytes,
+                     "mfma_tflops": dtfs,
+                     "mfma_frac": None if dtfs is None else dtfs / MFMA_F16_PEAK_TFS},
+        "kernels": kernels,
+        "call_roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": gbs / HBM_PEAK_GBS, "mfma_tflops": tfs,
+                          "mfma_frac": tfs / MFMA_F16_PEAK_TFS, "bytes_per_call": bytes_call,
+                          "flops_per_call": flops_call,
+                          "us_per_call_with_hook": sum(kms) * 1e3},
     }
     if not args.no_decode:
-        dms, (N, DB, DH, ddk) = time_decode(gdn, args, dev)
+        dms, dkms, (N, DB, DH, ddk) = time_decode(gdn, args, dev)
         dbytes = DECODE_BYTES_PER_HEAD * DB * DH
-        dgbs = dbytes / (dms / 1e3) / 1e9
+        # one kernel per step: the step time over the timed loop is the kernel's
+        # average launch duration (the per-kernel hook pass is reported beside)
+        kgbs = dbytes / (dms / 1e3) / 1e9
         line["decode"] = {
             "workload": "decode64: B=64 sequences, H=16, d=128, %d steps, state in place" % N,
             "value": DB / (dms / 1e3), "unit": "tokens/s", "us_per_step": dms * 1e3,
-            "roofline": {"kernel": "gdn_decode_step", "bound": "hbm", "achieved": dgbs,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
-                         "traffic": None, "bytes_per_call": dbytes},
+            "roofline": {"kernel": "decode step (recurrent_kernel<bf16,128>)", "bound": "hbm",
+                         "achieved": kgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": kgbs / HBM_PEAK_GBS,
+                         "traffic": committed_traffic("decode step (recurrent_kernel<bf16,128>)"),
+                         "us_per_launch": dms * 1e3, "bytes_per_launch": dbytes,
+                         "us_per_launch_hook": dkms[0] * 1e3},
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -133,6 +133,29 @@ int gdn_stream_chunk(const void *q, const void *k, const void *v, int dtype,
 int gdn_decode_step(const void *q, const void *k, const void *v, int dtype,
                     const float *g, const float *beta, float *state, float *o,
                     int B, int H, int dk, int dv, void *stream);
+
+/*
+ * gdn_set_profile_events -- kernel timing hook for measurement tools; not part
+ * of the operation and without effect on results.
+ *
+ * With count > 0, each following gdn_prefill, gdn_stream_chunk or
+ * gdn_decode_step call records events[0] on its stream before its first kernel
+ * and events[i] after its i-th kernel, while events last (later kernels are
+ * not marked).  `events` holds hipEvent_t handles created by the caller, who
+ * keeps them and the array alive while the hook is set.  count = 0 turns the
+ * hook off.  The setting is process-wide and not synchronised: change it only
+ * while no other thread calls the library.  Kernel sequence of one call:
+ *   bf16 prefill, one segment:       output pass
+ *   bf16 prefill, several segments:  summary pass, combine, output pass
+ *   fp32 prefill:                    chunk prep, [summary pass, combine,] chain
+ *   decode:                          step
+ * Returns GDN_OK, or GDN_ERR_NULL for events == NULL with count > 0, or
+ * GDN_ERR_SHAPE for count < 0.
+ */
+int gdn_set_profile_events(void *const *events, int count);
+
+/* Number of events the last call recorded under the hook (0 when it is off). */
+int gdn_profile_marks(void);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
     stream_chunk(q, k, v, g, beta, state)         -> o        (state in place)
     decode_step(q, k, v, g, beta, state)          -> o        (state in place)
     prefill_workspace_bytes(B, T, H, dk, dv, dtype)
+    set_profile_events(handles), profile_marks()   (kernel timing hook)
 
 Shapes: q, k [B, T, H, dk]; v [B, T, H, dv]; g (log-decay), beta [B, T, H];
 state [B, H, dk, dv] fp32 with state[b, h, i, j] = S[j, i]; o fp32.  Decode drops
@@ -22,7 +23,7 @@ import ctypes
 import os
 
 __all__ = ["prefill", "stream_chunk", "decode_step", "prefill_workspace_bytes", "GdnError",
-           "library_path", "GDN_BF16", "GDN_F32"]
+           "library_path", "GDN_BF16", "GDN_F32", "set_profile_events", "profile_marks"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libgdn.so")
@@ -55,6 +56,10 @@ def _load():
     lib.gdn_stream_chunk.argtypes = [vp, vp, vp, i, fp, fp, fp, fp, i, i, i, i, i, vp, sz, vp]
     lib.gdn_decode_step.restype = i
     lib.gdn_decode_step.argtypes = [vp, vp, vp, i, fp, fp, fp, fp, i, i, i, i, vp]
+    lib.gdn_set_profile_events.restype = i
+    lib.gdn_set_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
+    lib.gdn_profile_marks.restype = i
+    lib.gdn_profile_marks.argtypes = []
     return lib
 
 
@@ -67,6 +72,27 @@ def library_path() -> str:
 
 def abi_version() -> int:
     return int(_lib.gdn_abi_version())
+
+
+_profile_keep = None  # the event-handle array the library holds while the hook is set
+
+
+def set_profile_events(handles) -> None:
+    """Kernel timing hook: the following calls record the given hipEvent_t
+    handles (ints) before their first kernel and after each kernel; None or an
+    empty list turns it off.  See gdn_set_profile_events in include/gdn.h."""
+    global _profile_keep
+    handles = list(handles or [])
+    arr = (ctypes.c_void_p * max(1, len(handles)))(*handles) if handles else None
+    st = _lib.gdn_set_profile_events(arr, len(handles))
+    if st != 0:
+        raise GdnError(st, "gdn_set_profile_events")
+    _profile_keep = arr
+
+
+def profile_marks() -> int:
+    """Events the last call recorded under the timing hook."""
+    return int(_lib.gdn_profile_marks())
 
 
 def _torch():

@@ -9,6 +9,11 @@
 
 namespace {
 
+// gdn_set_profile_events state (process-wide, see gdn.h)
+hipEvent_t* g_events = nullptr;
+int g_nevents = 0;
+int g_marks = 0;
+
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
 };
@@ -82,7 +87,33 @@ int run_prefill(const void* q, const void* k, const void* v, int dtype, const fl
 
 }  // namespace
 
+namespace gdn {
+
+void profile_begin(hipStream_t stream) {
+    g_marks = 0;
+    if (g_nevents > 0 && hipEventRecord(g_events[0], stream) == hipSuccess) g_marks = 1;
+}
+
+void profile_mark(hipStream_t stream) {
+    if (g_marks > 0 && g_marks < g_nevents && hipEventRecord(g_events[g_marks], stream) == hipSuccess)
+        ++g_marks;
+}
+
+}  // namespace gdn
+
 extern "C" {
+
+int gdn_set_profile_events(void* const* events, int count) {
+    if (count < 0) return GDN_ERR_SHAPE;
+    if (count > 0 && !events) return GDN_ERR_NULL;
+    g_events = count > 0 ? reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)) : nullptr;
+    g_nevents = count;
+    g_marks = 0;
+    return GDN_OK;
+}
+
+int gdn_profile_marks(void) { return g_marks; }
+
 
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 
@@ -119,6 +150,7 @@ int gdn_prefill(const void* q, const void* k, const void* v, int dtype, const fl
                  workspace ? workspace_bytes : 0);
     if (s != GDN_OK) return s;
     if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
+    gdn::profile_begin(static_cast<hipStream_t>(stream));
     return run_prefill(q, k, v, dtype, g, beta, state_in, state_out, o, B, T, H, dk, workspace,
                        workspace_bytes, static_cast<hipStream_t>(stream));
 }
@@ -139,6 +171,7 @@ int gdn_decode_step(const void* q, const void* k, const void* v, int dtype, cons
     if (!state) return GDN_ERR_NULL;
     s = check_io(q, k, v, dtype, g, beta, state, state, o, B, 1, H, dk, dv, nullptr, 0);
     if (s != GDN_OK) return s;
+    gdn::profile_begin(static_cast<hipStream_t>(stream));
     return launch_status(gdn::launch_recurrent(q, k, v, dtype == GDN_BF16, g, beta, state, state,
                                                o, B, 1, H, dk, static_cast<hipStream_t>(stream)));
 }

@@ -805,6 +805,7 @@ static hipError_t launch_chunked_t(const void* q, const void* k, const void* v, 
     hipLaunchKernelGGL((chunk_prep<In, D>), dim3(p.NC, H, B), dim3(256), 0, stream,
                        static_cast<const In*>(q), static_cast<const In*>(k),
                        static_cast<const In*>(v), g, beta, ws, T, H, p.NC, total);
+    profile_mark(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     SegWs sw{nullptr, nullptr};
@@ -812,6 +813,7 @@ static hipError_t launch_chunked_t(const void* q, const void* k, const void* v, 
         hipLaunchKernelGGL((chunk_chain<In, D, 16, CHAIN_OUT>), dim3((unsigned)(BH * (D / 16))),
                            dim3(256), 0, stream, static_cast<const void*>(ws), sw, state_in,
                            state_out, o, T, H, B, p.NC, p.G, 1, total);
+        profile_mark(stream);
         return hipGetLastError();
     }
     char* base = static_cast<char*>(ws) + Ws<OT, D>::bytes_per_chunk * total + Ws<OT, D>::sink_bytes;
@@ -822,6 +824,7 @@ static hipError_t launch_chunked_t(const void* q, const void* k, const void* v, 
                        dim3((unsigned)(BH * p.S * (2 * D / DVT))), dim3(256), 0, stream,
                        static_cast<const void*>(ws), sw, state_in, state_out, o, T, H, B, p.NC,
                        p.G, p.S, total);
+    profile_mark(stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_seg_combine(sw.summ, sw.sst, state_in, state_out, (int)BH, p.S, D, stream);
@@ -830,6 +833,7 @@ static hipError_t launch_chunked_t(const void* q, const void* k, const void* v, 
                        dim3((unsigned)(BH * p.S * (D / DVT))), dim3(256), 0, stream,
                        static_cast<const void*>(ws), sw, state_in, state_out, o, T, H, B, p.NC,
                        p.G, p.S, total);
+    profile_mark(stream);
     return hipGetLastError();
 }
 
@@ -842,6 +846,7 @@ hipError_t launch_seg_combine(float* summ, float* sst, const float* state_in, fl
     else
         hipLaunchKernelGGL((seg_combine<128>), dim3((unsigned)(BH * 8)), dim3(64 * 8), 0, stream,
                            sw, state_in, state_out, BH, S);
+    profile_mark(stream);
     return hipGetLastError();
 }
 

@@ -8,6 +8,11 @@
 
 namespace gdn {
 
+// Timing hook of gdn_set_profile_events: profile_begin() before a call's first
+// launch, profile_mark() after each launch; both do nothing while it is off.
+void profile_begin(hipStream_t stream);
+void profile_mark(hipStream_t stream);
+
 // Token-serial recurrence, one workgroup per (batch, head); also the decode step (T = 1).
 hipError_t launch_recurrent(const void* q, const void* k, const void* v, int dtype_bf16,
                             const float* g, const float* beta, const float* state_in,

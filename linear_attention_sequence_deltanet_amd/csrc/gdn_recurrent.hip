@@ -122,6 +122,7 @@ static hipError_t launch_recurrent_t(const void* q, const void* k, const void* v
     hipLaunchKernelGGL((recurrent_kernel<In, D>), dim3((unsigned)(B * H)), dim3(256), 0, stream,
                        static_cast<const In*>(q), static_cast<const In*>(k),
                        static_cast<const In*>(v), g, beta, state_in, state_out, o, T, H);
+    profile_mark(stream);
     return hipGetLastError();
 }
 

@@ -136,3 +136,16 @@ def test_decode_errors(lib):
     assert dec(d=32) == UNSUP
     assert dec(o=P["sout"] + 64) == ALIAS
     assert dec(k=P["k"] + 2) == ALIGN
+
+
+def test_profile_hook_host_paths(lib):
+    """The timing hook's argument checks and off state need no GPU."""
+    vpp = ctypes.POINTER(ctypes.c_void_p)
+    lib.gdn_set_profile_events.argtypes = [vpp, ctypes.c_int]
+    assert lib.gdn_set_profile_events(None, 0) == 0
+    assert lib.gdn_profile_marks() == 0
+    assert lib.gdn_set_profile_events(None, 2) == 1          # GDN_ERR_NULL
+    arr = (ctypes.c_void_p * 2)(None, None)
+    assert lib.gdn_set_profile_events(arr, -1) == 2          # GDN_ERR_SHAPE
+    assert lib.gdn_set_profile_events(None, 0) == 0
+
