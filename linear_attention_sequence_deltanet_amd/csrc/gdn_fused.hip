@@ -94,6 +94,25 @@ __device__ __forceinline__ H8 acc_to_b32(f32x4 t0, f32x4 t1) {
     return __builtin_bit_cast(H8, w);
 }
 
+// c + X Y for 16x16 tiles on the matrix cores, about fp32-accurate: X and Y
+// are split into fp16 high and low parts and three products accumulated.  X
+// enters through the accumulator-layout tile of its transpose (which is the
+// A-operand layout of X), Y through its own accumulator-layout tile (the
+// B-operand layout of the 16x16x16 product).
+__device__ __forceinline__ f32x4 mm_split(f32x4 xt, f32x4 y, f32x4 c) {
+    H4 ah, al, bh, bl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        ah[e] = static_cast<_Float16>(xt[e]);
+        al[e] = static_cast<_Float16>(xt[e] - static_cast<float>(ah[e]));
+        bh[e] = static_cast<_Float16>(y[e]);
+        bl[e] = static_cast<_Float16>(y[e] - static_cast<float>(bh[e]));
+    }
+    c = MF::k16(ah, bh, c);
+    c = MF::k16(ah, bl, c);
+    return MF::k16(al, bh, c);
+}
+
 // DPP move of a wave's values (lanes without a source, or in rows outside
 // ROWS, read 0).
 template <int CTRL, int ROWS>
@@ -150,8 +169,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     __shared__ __align__(16) _Float16 sA[FC * LA];      // -A off-diagonal, (T_bb - I) diagonal blocks
     __shared__ __align__(16) _Float16 sP[OUT ? FC * LA : 8];
     __shared__ __align__(16) _Float16 sStg[OUT ? 8 : NW * 2 * D * 16];  // SUM: summary transpose
-    __shared__ __align__(16) float sAd[4][16][16];
     __shared__ __align__(16) float sgam[FC], sbeta[FC], sGam[FC], sE[FC], sBG[FC];
+    // decay factors of the off-diagonal Gram tiles: sRF[r] = exp(gam_r - gam_{16 floor(r/16)}),
+    // sCF[m][i] = exp(gam_{16 m} - gam_i) for i < 16 m (both <= 1)
+    __shared__ __align__(16) float sRF[FC], sCF[4][FC];
     __shared__ float sGC;
 
     // SUM chains the value columns (tile w, giving R) and the identity columns
@@ -249,104 +270,133 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             sBG[lane] = bv * eg;
             sE[lane] = __expf(gC - gv);
             if (lane == 0) sGC = __expf(gC);
+            const float g16 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 16));
+            const float g32 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 32));
+            const float g48 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 48));
+            const float g00 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 0));
+            sRF[lane] = __expf(gv - (lane < 16 ? g00 : lane < 32 ? g16 : lane < 48 ? g32 : g48));
+            sCF[1][lane] = lane < 16 ? __expf(g16 - gv) : 0.f;
+            sCF[2][lane] = lane < 32 ? __expf(g32 - gv) : 0.f;
+            sCF[3][lane] = lane < 48 ? __expf(g48 - gv) : 0.f;
         }
         if (c + 1 < c_end) issue_loads(c + 1);
         lds_sync();
 
-        // ---- Gram tiles.  Wave 0: the four diagonal K K^T tiles and the
-        // inverses of the four (I + A_bb) blocks.  Waves 1..: the six
-        // off-diagonal K K^T tiles and, for OUT, the ten lower Q K^T tiles.
-        if (wave == 0) {
-            // A_bb (strictly lower, beta- and decay-scaled) column-major:
-            // sAd[b][i][r] = A[16 b + r][16 b + i]
+        // ---- Gram tiles.  Waves 0-3: diagonal block w of K K^T and the
+        // inverse of (I + A_ww).  All waves: the six off-diagonal K K^T tiles
+        // and, for OUT, the ten lower Q K^T tiles.
+        if (wave < 4) {
+            const int bb = wave;
+            f32x4 acc = zero4();  // G = K_b K_b^T, symmetric
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk) {
-                    const H8 a = ld8<_Float16>(&sK[(16 * bb + lc) * LD + 32 * kk + 8 * lg]);
-                    acc = MF::k32(a, a, acc);
-                }
-                const f32x4 gr = *reinterpret_cast<const f32x4*>(&sgam[16 * bb + 4 * lg]);
-                const f32x4 br = *reinterpret_cast<const f32x4*>(&sbeta[16 * bb + 4 * lg]);
-                const float gi = sgam[16 * bb + lc];
-                f32x4 av;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float ex = __expf(fminf(gr[e] - gi, 0.f));
-                    av[e] = lc < 4 * lg + e ? br[e] * ex * acc[e] : 0.f;
-                }
-                *reinterpret_cast<f32x4*>(&sAd[bb][lc][4 * lg]) = av;
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const H8 a = ld8<_Float16>(&sK[(16 * bb + lc) * LD + 32 * kk + 8 * lg]);
+                acc = MF::k32(a, a, acc);
             }
-            // (I + A_bb)^{-1} in fp32: lane group g inverts block g, lane c of
-            // it computing column c by column-wise elimination (x_r -= A[r][i]
-            // x_i for r > i once x_i is final).  Only this wave touches sAd, and
-            // a wave's LDS accesses complete in order, so no barrier is needed.
-            {
-                float x[16];
+            const f32x4 gr = *reinterpret_cast<const f32x4*>(&sgam[16 * bb + 4 * lg]);
+            const f32x4 br = *reinterpret_cast<const f32x4*>(&sbeta[16 * bb + 4 * lg]);
+            const float gi = sgam[16 * bb + lc], bi = sbeta[16 * bb + lc];
+            // A_bb and its transpose in accumulator layout (row 4 lg + e, column
+            // lc); by the symmetry of G both come from the same accumulator.
+            f32x4 ax, at, id;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] = r == lc ? 1.f : 0.f;
-#pragma unroll
-                for (int i = 0; i < 15; ++i) {
-                    float a[16];
-#pragma unroll
-                    for (int q4 = (i + 1) / 4; q4 < 4; ++q4) {
-                        const f32x4 t4 = *reinterpret_cast<const f32x4*>(&sAd[lg][i][4 * q4]);
-                        a[4 * q4] = t4[0]; a[4 * q4 + 1] = t4[1]; a[4 * q4 + 2] = t4[2]; a[4 * q4 + 3] = t4[3];
-                    }
-#pragma unroll
-                    for (int r = i + 1; r < 16; ++r) x[r] -= a[r] * x[i];
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    sA[(16 * lg + r) * LA + 16 * lg + lc] = static_cast<_Float16>(r == lc ? 0.f : x[r]);
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * lg + e;
+                const float ex = __expf(-fabsf(gr[e] - gi));
+                ax[e] = lc < r ? br[e] * ex * acc[e] : 0.f;
+                at[e] = r < lc ? bi * ex * acc[e] : 0.f;
+                id[e] = r == lc ? 1.f : 0.f;
             }
-        } else {
-            // Tile list: the 6 off-diagonal K K^T tiles, then (OUT) the 10 lower
-            // Q K^T tiles, dealt to waves 1 .. NW-1 in turn; fixed per-wave
-            // sequences let consecutive tiles overlap.
-            constexpr int NREAL = OUT ? 16 : 6;
-            auto tile = [&](int tt) {
-                const bool kq = tt < 6;  // K K^T off-diagonal
-                int mi, ni;
-                if (kq) {
-                    mi = tt < 1 ? 1 : tt < 3 ? 2 : 3;
-                    ni = tt - (mi * (mi - 1)) / 2;
-                } else {
-                    const int u = tt - 6;
-                    mi = u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : 3;
-                    ni = u - (mi * (mi + 1)) / 2;
-                }
-                const _Float16* X = kq ? sK : sQ;
+            // A is nilpotent (A^16 = 0): (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8),
+            // evaluated on transposes: N^T = (I - A^T) + A2^T (...) and so on.
+            const f32x4 a2 = mm_split(at, ax, zero4()), a2t = mm_split(ax, at, zero4());
+            const f32x4 a4 = mm_split(a2t, a2, zero4()), a4t = mm_split(a2, a2t, zero4());
+            const f32x4 a8 = mm_split(a4t, a4, zero4());
+            const f32x4 n1t = id - at;
+            const f32x4 n2t = mm_split(a2, n1t, n1t);  // ((I - A)(I + A^2))^T
+            const f32x4 n3t = mm_split(a4, n2t, n2t);  // (... (I + A^4))^T
+            const f32x4 nt = mm_split(a8, n3t, n3t);   // ((I + A)^{-1})^T
+            // N - I: row lc of the block, columns 4 lg .. 4 lg + 3
+            st4<_Float16>(&sA[(16 * bb + lc) * LA + 16 * bb + 4 * lg], cvt4<_Float16>(nt - id));
+        }
+        {
+            // A tile (mi, ni) is computed transposed, C = K_ni X_mi^T (X = K or Q),
+            // so lane (lg, lc) holds row r = 16 mi + lc, columns i = 16 ni + 4 lg + e
+            // and stores four consecutive halves.  Off-diagonal tiles (mi > ni) are
+            // numbered 0..5: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
+            auto off_coords = [](int k, int& mi, int& ni) {
+                mi = k < 1 ? 1 : k < 3 ? 2 : 3;
+                ni = k - (mi * (mi - 1)) / 2;
+            };
+            auto tile_acc = [&](const _Float16* X, int mi, int ni) {
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int kk = 0; kk < D / 32; ++kk)
-                    acc = MF::k32(ld8<_Float16>(&X[(16 * mi + lc) * LD + 32 * kk + 8 * lg]),
-                                  ld8<_Float16>(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]), acc);
-                const f32x4 gr = *reinterpret_cast<const f32x4*>(&sgam[16 * mi + 4 * lg]);
-                const f32x4 br = *reinterpret_cast<const f32x4*>(&sbeta[16 * mi + 4 * lg]);
-                const int i = 16 * ni + lc;
-                const float gi = sgam[i];
+                    acc = MF::k32(ld8<_Float16>(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]),
+                                  ld8<_Float16>(&X[(16 * mi + lc) * LD + 32 * kk + 8 * lg]), acc);
+                return acc;
+            };
+            // off-diagonal: exp(gam_r - gam_i) = sRF[r] sCF[mi][i]; -A (K K^T) or P (Q K^T)
+            auto store_off = [&](bool kq, int mi, int ni, f32x4 acc) {
+                const int r = 16 * mi + lc;
+                const f32x4 cf = *reinterpret_cast<const f32x4*>(&sCF[mi][16 * ni + 4 * lg]);
+                const float sc = kq ? -(sbeta[r] * sRF[r]) : sRF[r];
+                st4<_Float16>(&(kq ? sA : sP)[r * LA + 16 * ni + 4 * lg], cvt4<_Float16>((sc * cf) * acc));
+            };
+            // diagonal Q K^T tile m: P[r][i] for i <= r
+            auto store_qdiag = [&](int m, f32x4 acc) {
+                const int r = 16 * m + lc;
+                const float gr = sgam[r];
+                const f32x4 gi = *reinterpret_cast<const f32x4*>(&sgam[16 * m + 4 * lg]);
+                f32x4 val;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * mi + 4 * lg + e;
-                    const float ex = __expf(fminf(gr[e] - gi, 0.f));
-                    if (kq) {
-                        sA[r * LA + i] = static_cast<_Float16>(-(br[e] * ex * acc[e]));
-                    } else {
-                        sP[r * LA + i] = static_cast<_Float16>(i <= r ? ex * acc[e] : 0.f);
-                    }
-                }
+                for (int e = 0; e < 4; ++e)
+                    val[e] = 4 * lg + e <= lc ? __expf(fminf(gr - gi[e], 0.f)) * acc[e] : 0.f;
+                st4<_Float16>(&sP[r * LA + 16 * m + 4 * lg], cvt4<_Float16>(val));
             };
             if (NW == 8) {
-                // OUT: waves 1, 2 take three tiles, waves 3..7 two; SUM: waves 1..6 one
-                if (OUT || wave - 1 < NREAL) tile(wave - 1);
-                if (OUT) {
-                    tile(wave + 6);
-                    if (wave <= 2) tile(wave + 13);
+                // waves 4..7: K K^T tile w-4, then (OUT) Q K^T tile w-4 and, for
+                // waves 4, 5, K K^T tile w / for waves 6, 7, Q K^T tile w-2;
+                // SUM: K K^T tiles w-4 and (waves 4, 5) w.  Waves 0..3 (OUT): the
+                // diagonal Q K^T tile of their block.
+                if (wave >= 4) {
+                    int m0, n0, m1, n1, m2, n2;
+                    off_coords(wave - 4, m0, n0);
+                    const f32x4 c0 = tile_acc(sK, m0, n0);
+                    if (OUT) {
+                        off_coords(wave - 4, m1, n1);
+                        const f32x4 c1 = tile_acc(sQ, m1, n1);
+                        const bool third_kk = wave < 6;
+                        off_coords(third_kk ? wave : wave - 2, m2, n2);
+                        const f32x4 c2 = tile_acc(third_kk ? sK : sQ, m2, n2);
+                        store_off(true, m0, n0, c0);
+                        store_off(false, m1, n1, c1);
+                        if (third_kk) store_off(true, m2, n2, c2);
+                        else store_off(false, m2, n2, c2);
+                    } else {
+                        store_off(true, m0, n0, c0);
+                        if (wave < 6) {
+                            off_coords(wave, m1, n1);
+                            store_off(true, m1, n1, tile_acc(sK, m1, n1));
+                        }
+                    }
+                } else if (OUT) {
+                    store_qdiag(wave, tile_acc(sQ, wave, wave));
                 }
             } else {
-                for (int tt = wave - 1; tt < NREAL; tt += NW - 1) tile(tt);
+                // generic: the off-diagonal K K^T tiles, then (OUT) the off-diagonal
+                // and the diagonal Q K^T tiles, dealt to the waves in turn
+                constexpr int NREAL = OUT ? 16 : 6;
+                for (int tt = wave; tt < NREAL; tt += NW) {
+                    if (tt < 12) {
+                        int mi, ni;
+                        off_coords(tt % 6, mi, ni);
+                        const bool kq = tt < 6;
+                        store_off(kq, mi, ni, tile_acc(kq ? sK : sQ, mi, ni));
+                    } else {
+                        store_qdiag(tt - 12, tile_acc(sQ, tt - 12, tt - 12));
+                    }
+                }
             }
             // the two upper P tiles that the output products read, (0,1) and (2,3)
             if (OUT && wave >= NW - 2) {
