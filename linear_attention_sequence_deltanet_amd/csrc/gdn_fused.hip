@@ -94,23 +94,28 @@ __device__ __forceinline__ H8 acc_to_b32(f32x4 t0, f32x4 t1) {
     return __builtin_bit_cast(H8, w);
 }
 
-// c + X Y for 16x16 tiles on the matrix cores, about fp32-accurate: X and Y
-// are split into fp16 high and low parts and three products accumulated.  X
-// enters through the accumulator-layout tile of its transpose (which is the
-// A-operand layout of X), Y through its own accumulator-layout tile (the
-// B-operand layout of the 16x16x16 product).
-__device__ __forceinline__ f32x4 mm_split(f32x4 xt, f32x4 y, f32x4 c) {
-    H4 ah, al, bh, bl;
+// A 16x16 accumulator-layout tile split into fp16 high and low parts.
+struct Split {
+    H4 hi, lo;
+};
+__device__ __forceinline__ Split split(f32x4 x) {
+    Split r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        ah[e] = static_cast<_Float16>(xt[e]);
-        al[e] = static_cast<_Float16>(xt[e] - static_cast<float>(ah[e]));
-        bh[e] = static_cast<_Float16>(y[e]);
-        bl[e] = static_cast<_Float16>(y[e] - static_cast<float>(bh[e]));
+        r.hi[e] = static_cast<_Float16>(x[e]);
+        r.lo[e] = static_cast<_Float16>(x[e] - static_cast<float>(r.hi[e]));
     }
-    c = MF::k16(ah, bh, c);
-    c = MF::k16(ah, bl, c);
-    return MF::k16(al, bh, c);
+    return r;
+}
+
+// c + X Y for 16x16 tiles on the matrix cores, about fp32-accurate (three
+// products of the fp16 parts).  X enters through the split accumulator-layout
+// tile of its transpose (which is the A-operand layout of X), Y through its
+// own split tile (the B-operand layout of the 16x16x16 product).
+__device__ __forceinline__ f32x4 mm_split(const Split& xt, const Split& y, f32x4 c) {
+    c = MF::k16(xt.hi, y.hi, c);
+    c = MF::k16(xt.hi, y.lo, c);
+    return MF::k16(xt.lo, y.hi, c);
 }
 
 // DPP move of a wave's values (lanes without a source, or in rows outside
@@ -309,13 +314,17 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             }
             // A is nilpotent (A^16 = 0): (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8),
             // evaluated on transposes: N^T = (I - A^T) + A2^T (...) and so on.
-            const f32x4 a2 = mm_split(at, ax, zero4()), a2t = mm_split(ax, at, zero4());
-            const f32x4 a4 = mm_split(a2t, a2, zero4()), a4t = mm_split(a2, a2t, zero4());
-            const f32x4 a8 = mm_split(a4t, a4, zero4());
+            // (each factor is split into fp16 parts once)
+            const Split sx = split(ax), st = split(at);
+            const f32x4 a2 = mm_split(st, sx, zero4()), a2t = mm_split(sx, st, zero4());
+            const Split s2 = split(a2), s2t = split(a2t);
+            const f32x4 a4 = mm_split(s2t, s2, zero4()), a4t = mm_split(s2, s2t, zero4());
+            const Split s4 = split(a4);
+            const f32x4 a8 = mm_split(split(a4t), s4, zero4());
             const f32x4 n1t = id - at;
-            const f32x4 n2t = mm_split(a2, n1t, n1t);  // ((I - A)(I + A^2))^T
-            const f32x4 n3t = mm_split(a4, n2t, n2t);  // (... (I + A^4))^T
-            const f32x4 nt = mm_split(a8, n3t, n3t);   // ((I + A)^{-1})^T
+            const f32x4 n2t = mm_split(s2, split(n1t), n1t);  // ((I - A)(I + A^2))^T
+            const f32x4 n3t = mm_split(s4, split(n2t), n2t);  // (... (I + A^4))^T
+            const f32x4 nt = mm_split(split(a8), split(n3t), n3t);  // ((I + A)^{-1})^T
             // N - I: row lc of the block, columns 4 lg .. 4 lg + 3
             st4<_Float16>(&sA[(16 * bb + lc) * LA + 16 * bb + 4 * lg], cvt4<_Float16>(nt - id));
         }
