@@ -4,7 +4,11 @@ A step is one whole-path call over one batch of synthetic inputs already in HBM:
   * value: gdn_prefill over the 8192-token prompt, B=1, H=16, d_k=d_v=128, bf16
     q/k/v, fp32 gates/state/output, zero initial state (tokens/s);
   * decode: gdn_decode_step for 64 sequences x 16 heads, d=128, fp32 state updated
-    in place, 1000 consecutive steps with fresh inputs (tokens/s, reported beside).
+    in place, 1000 consecutive steps with fresh inputs (tokens/s, reported beside);
+  * long_prefill: gdn_prefill over 262144 tokens (tokens/s, beside);
+  * stream: gdn_stream_chunk calls of 272 tokens (256 visual + 16 text) carrying
+    the state in place; the first 200 frames of the stream are staged and replayed
+    in order (calls/s = frames/s, beside).
 Timing uses HIP events on the stream the library launches on (torch's current
 stream).  A second pass over the same steps records events between the
 library's kernels (gdn_set_profile_events) to time each kernel; the roofline
@@ -60,6 +64,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-long", action="store_true")
+    p.add_argument("--long-reps", type=int, default=3)
+    p.add_argument("--no-stream", action="store_true")
+    p.add_argument("--stream-calls", type=int, default=2000)
+    p.add_argument("--stream-frames", type=int, default=200)
     p.add_argument("--copy-mib", type=int, default=0,
                    help="first copy this many MiB device to device three times (a copy of "
                         "known size that calibrates hardware byte counters)")
@@ -216,6 +225,91 @@ def time_decode(gdn, args, dev):
     return ms, kms, (N, B, H, dk)
 
 
+def time_long_prefill(gdn, args, dev):
+    """prefill256k: one call over 262144 tokens, median of `long_reps`."""
+    import torch
+    import gdn_inputs
+    d = gdn_inputs.sequence_inputs("prefill256k")
+    B, T, H, dk = d["q"].shape
+    q, k, v = (stage_bf16(d[x], dev) for x in ("q", "k", "v"))
+    g = torch.from_numpy(d["g"]).to(dev)
+    beta = torch.from_numpy(d["beta"]).to(dev)
+    del d
+    o = torch.empty((B, T, H, dk), dtype=torch.float32, device=dev)
+    st = torch.empty((B, H, dk, dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, gdn.prefill_workspace_bytes(B, T, H, dk, dk)), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+    call = lambda: gdn.prefill(q, k, v, g, beta, None, state_out=st, o=o, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.long_reps):
+        a = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        e.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(e))
+    ms = float(np.median(times))
+    units = B * T * H
+    gbs = PREFILL_BYTES_PER_TOKEN_HEAD * units / (ms / 1e3) / 1e9
+    tfs = PREFILL_FLOPS_PER_TOKEN_HEAD * units / (ms / 1e3) / 1e12
+    return {"workload": "prefill256k: B=1, H=16, T=262144, d=128, bf16, g = -softplus(N+3)",
+            "value": B * T / (ms / 1e3), "unit": "tokens/s", "ms_per_call": ms,
+            "roofline": {"kernel": "gdn_prefill (whole call)", "bound": "hbm", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "mfma_frac": tfs / MFMA_F16_PEAK_TFS}}
+
+
+def time_stream(gdn, args, dev):
+    """stream: `stream_calls` calls of 272 tokens, state carried in place."""
+    import torch
+    import gdn_inputs
+    wl = gdn_inputs.WORKLOADS["stream"]
+    ct = wl.call_tokens
+    nf = min(args.stream_frames, wl.calls)
+    d = gdn_inputs.sequence_inputs("stream", T=nf * ct)
+    B, T, H, dk = d["q"].shape
+    q, k, v = (stage_bf16(d[x], dev) for x in ("q", "k", "v"))
+    g = torch.from_numpy(d["g"]).to(dev)
+    beta = torch.from_numpy(d["beta"]).to(dev)
+    state = torch.zeros((B, H, dk, dk), dtype=torch.float32, device=dev)
+    o = torch.empty((B, T, H, dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, gdn.prefill_workspace_bytes(B, ct, H, dk, dk)), dtype=torch.uint8,
+                     device=dev)
+    views = [(q[:, f * ct:(f + 1) * ct], k[:, f * ct:(f + 1) * ct], v[:, f * ct:(f + 1) * ct],
+              g[:, f * ct:(f + 1) * ct], beta[:, f * ct:(f + 1) * ct], o[:, f * ct:(f + 1) * ct])
+             for f in range(nf)]
+    stream = torch.cuda.current_stream(dev)
+    for f in range(min(nf, 20)):  # warm-up
+        qf, kf, vf, gf, bf, of = views[f]
+        gdn.stream_chunk(qf, kf, vf, gf, bf, state, o=of, workspace=ws)
+    state.zero_()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(args.stream_calls):
+        qf, kf, vf, gf, bf, of = views[i % nf]
+        gdn.stream_chunk(qf, kf, vf, gf, bf, state, o=of, workspace=ws)
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(e) / args.stream_calls
+    # algorithmic bytes per call: 272 x 16 token-heads plus the state read and written
+    cbytes = PREFILL_BYTES_PER_TOKEN_HEAD * B * ct * H + 2 * B * H * dk * dk * 4
+    gbs = cbytes / (ms / 1e3) / 1e9
+    return {"workload": "stream: B=1, H=16, d=128, %d calls x %d tokens (256 visual + 16 text), "
+                        "state in place; first %d frames staged, replayed in order"
+                        % (args.stream_calls, ct, nf),
+            "value": 1e3 / ms, "unit": "calls/s (frames/s)", "us_per_call": ms * 1e3,
+            "tokens_per_s": ct * 1e3 / ms,
+            "roofline": {"kernel": "gdn_stream_chunk (whole call)", "bound": "hbm",
+                         "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "bytes_per_call": cbytes}}
+
+
 def cpu_baseline(d, seconds):
     """Time the fp64 oracle on the host over (repeats of) the prefill workload."""
     import gdn_inputs
@@ -320,6 +414,10 @@ def main():
                          "us_per_launch": dms * 1e3, "bytes_per_launch": dbytes,
                          "us_per_launch_hook": dkms[0] * 1e3},
         }
+    if not args.no_long:
+        line["long_prefill"] = time_long_prefill(gdn, args, dev)
+    if not args.no_stream:
+        line["stream"] = time_stream(gdn, args, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
     print(json.dumps(line), flush=True)
