@@ -222,7 +222,39 @@ def time_decode(gdn, args, dev):
         torch.cuda.synchronize()
         times.append(start.elapsed_time(end) / N)
     ms = float(np.median(times))
-    return ms, kms, (N, B, H, dk)
+
+    def loop():
+        for n in range(N):
+            gdn.decode_step(q[n], k[n], v[n], g[n], beta[n], state, o=o[n])
+
+    state.copy_(s0)
+    gms = graph_ms(loop) / N
+    return ms, kms, gms, (N, B, H, dk)
+
+
+def graph_ms(loop, reps=3):
+    """Capture `loop` (a sequence of library calls on fixed buffers) into one HIP
+    graph and time its replays; returns the median replay time (ms)."""
+    import torch
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        loop()
+    torch.cuda.synchronize()
+    g.replay()  # warm-up
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        e.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(e))
+    del g
+    return float(np.median(times))
 
 
 def time_long_prefill(gdn, args, dev):
@@ -297,6 +329,14 @@ def time_stream(gdn, args, dev):
     e.record(stream)
     torch.cuda.synchronize()
     ms = a.elapsed_time(e) / args.stream_calls
+
+    def loop():
+        for i in range(args.stream_calls):
+            qf, kf, vf, gf, bf, of = views[i % nf]
+            gdn.stream_chunk(qf, kf, vf, gf, bf, state, o=of, workspace=ws)
+
+    state.zero_()
+    gms = graph_ms(loop) / args.stream_calls
     # algorithmic bytes per call: 272 x 16 token-heads plus the state read and written
     cbytes = PREFILL_BYTES_PER_TOKEN_HEAD * B * ct * H + 2 * B * H * dk * dk * 4
     gbs = cbytes / (ms / 1e3) / 1e9
@@ -305,6 +345,10 @@ def time_stream(gdn, args, dev):
                         % (args.stream_calls, ct, nf),
             "value": 1e3 / ms, "unit": "calls/s (frames/s)", "us_per_call": ms * 1e3,
             "tokens_per_s": ct * 1e3 / ms,
+            "graph": {"value": 1e3 / gms, "unit": "calls/s (frames/s)", "us_per_call": gms * 1e3,
+                      "tokens_per_s": ct * 1e3 / gms,
+                      "note": "the %d-call loop captured once as a HIP graph and replayed"
+                              % args.stream_calls},
             "roofline": {"kernel": "gdn_stream_chunk (whole call)", "bound": "hbm",
                          "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "bytes_per_call": cbytes}}
@@ -399,7 +443,7 @@ def main():
                           "us_per_call_with_hook": sum(kms) * 1e3},
     }
     if not args.no_decode:
-        dms, dkms, (N, DB, DH, ddk) = time_decode(gdn, args, dev)
+        dms, dkms, dgms, (N, DB, DH, ddk) = time_decode(gdn, args, dev)
         dbytes = DECODE_BYTES_PER_HEAD * DB * DH
         # one kernel per step: the step time over the timed loop is the kernel's
         # average launch duration (the per-kernel hook pass is reported beside)
@@ -413,6 +457,8 @@ def main():
                          "traffic": committed_traffic("decode step (recurrent_kernel<bf16,128>)"),
                          "us_per_launch": dms * 1e3, "bytes_per_launch": dbytes,
                          "us_per_launch_hook": dkms[0] * 1e3},
+            "graph": {"value": DB / (dgms / 1e3), "unit": "tokens/s", "us_per_step": dgms * 1e3,
+                      "note": "the %d-step loop captured once as a HIP graph and replayed" % N},
         }
     if not args.no_long:
         line["long_prefill"] = time_long_prefill(gdn, args, dev)
