@@ -221,3 +221,30 @@ def random_inputs(B, T, H, dk, dv, dtype="f32", seed=0, g_shift=2.0, state_std=0
                                   for b in range(B)])
     out["dtype"] = dtype
     return out
+
+
+def layer_inputs(B: int, T: int, H: int, d: int, seed: int = 0, with_state: bool = False,
+                 g_shift: float = 2.0) -> dict:
+    """Seeded inputs of the layer prologue and epilogue (no method arithmetic):
+    pre-convolution projections xq, xk, xv [B, T, H, d] (bf16 bits) ~ N(0, 1);
+    window-4 filters wq, wk, wv [H*d, 4] fp32 ~ N(0, 0.5^2); convolution state
+    [B, 3 (q, k, v), 3 (tokens), H*d] fp32 holding bf16-representable values
+    ~ N(0, 1) (or None); gate input z [B, T, H, d] (bf16 bits) ~ N(0, 1);
+    output norm weight wn [d] fp32 ~ 1 + 0.1 N(0, 1); and the recurrence's
+    g = -softplus(N + g_shift), beta = sigmoid(N) [B, T, H] fp32."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0x1A7E7]))
+    C = H * d
+    out = {}
+    for name in ("xq", "xk", "xv"):
+        out[name] = bf16_bits(rng.standard_normal((B, T, H, d), dtype=np.float32))
+    for name in ("wq", "wk", "wv"):
+        out[name] = (0.5 * rng.standard_normal((C, 4), dtype=np.float32)).astype(np.float32)
+    s = rng.standard_normal((B, 3, 3, C), dtype=np.float32)
+    out["conv_state"] = bf16_to_f32(bf16_bits(s)) if with_state else None
+    out["z"] = bf16_bits(rng.standard_normal((B, T, H, d), dtype=np.float32))
+    out["wn"] = (1.0 + 0.1 * rng.standard_normal(d, dtype=np.float32)).astype(np.float32)
+    x = rng.standard_normal((B, T, H), dtype=np.float32) + np.float32(g_shift)
+    out["g"] = (-np.logaddexp(np.float32(0.0), x)).astype(np.float32)
+    x = rng.standard_normal((B, T, H), dtype=np.float32)
+    out["beta"] = (1.0 / (1.0 + np.exp(-x))).astype(np.float32)
+    return out

@@ -29,8 +29,9 @@
  *     in fp16 inside the matrix cores and assume unit-norm-scale keys).
  *   - Supported sizes: d_k == d_v in {64, 128}; B, H >= 1; T >= 1 (any T).
  *   - Every pointer must be 16-byte aligned.
- *   - Outputs (o, state_out / state) must not overlap any input; the only
- *     allowed overlap is state_out == state_in exactly (in-place update).
+ *   - Outputs must not overlap any input or each other; the only allowed
+ *     overlaps are the exact in-place forms an entry point documents
+ *     (state_out == state_in, conv_state_out == conv_state_in, gate out == o).
  *   - The caller owns every buffer.  The library never allocates, frees or
  *     synchronises; work is enqueued on `stream` and completes asynchronously.
  *     Calls are graph-capturable (fixed pointers, no allocation).
@@ -38,8 +39,8 @@
  *     nothing is launched and no output byte changes.  A launch failure
  *     reported by the runtime returns GDN_ERR_LAUNCH.  Device faults surface
  *     at the caller's next synchronisation.  No exception crosses the ABI and
- *     nothing calls exit/abort.  The library keeps no global state; calls on
- *     different streams may run concurrently.
+ *     nothing calls exit/abort.  Apart from the timing hook below, the library
+ *     keeps no global state; calls on different streams may run concurrently.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -135,11 +136,64 @@ int gdn_decode_step(const void *q, const void *k, const void *v, int dtype,
                     int B, int H, int dk, int dv, void *stream);
 
 /*
+ * gdn_conv_qkv -- the layer prologue: the short causal convolution of q, k, v
+ * (explainer page "InfiniteVL: Synergizing Linear and Sparse Attention ...",
+ * section "Methodology", step 2: each Gated DeltaNet layer carries a 1D
+ * convolution of window size 4).  The pages give only the window; the readings
+ * taken are stated here.  Per channel c (channel = h * d + feature) of each of
+ * q, k, v, depthwise and causal, then SiLU:
+ *
+ *     y_c[t] = SiLU( w_c[0] x_c[t-3] + w_c[1] x_c[t-2] + w_c[2] x_c[t-1] + w_c[3] x_c[t] ),
+ *
+ * with x_c[-3..-1] taken from conv_state_in (zeros when it is NULL).  With
+ * l2norm_qk != 0, q and k are then scaled per (token, head) to unit L2 norm:
+ * y / sqrt(sum over the head's d features of y^2 + 1e-6).  Outputs are rounded
+ * to bf16 (nearest even), the recurrence's input type.
+ *
+ * xq, xk, xv      [B][T][H][d] bf16 (raw bits): the projections before the
+ *                 convolution.
+ * wq, wk, wv      [H*d][4] fp32 filters; tap 3 multiplies the current token.
+ * conv_state_in   [B][3 (q, k, v)][3 (tokens, oldest first)][H*d] fp32: the
+ *                 three input tokens before x of each stream, or NULL.
+ * conv_state_out  same layout, or NULL (not saved): the last three tokens of
+ *                 (conv_state_in, x), i.e. the conv_state_in of the next call
+ *                 of a stream.  May equal conv_state_in exactly (in place).
+ * q, k, v         [B][T][H][d] bf16 outputs (the recurrence's inputs).
+ * Successive calls with the state carried equal one call over the
+ * concatenated tokens, bit for bit.
+ * Sizes: d in {64, 128}; B, T, H >= 1.  Errors and conventions as above
+ * (every pointer 16-byte aligned; no output may overlap an input or another
+ * output, except conv_state_out == conv_state_in).
+ */
+int gdn_conv_qkv(const void *xq, const void *xk, const void *xv,
+                 const float *wq, const float *wk, const float *wv,
+                 const float *conv_state_in, float *conv_state_out,
+                 void *q, void *k, void *v, int l2norm_qk,
+                 int B, int T, int H, int d, void *stream);
+
+/*
+ * gdn_gate_out -- the layer epilogue: the output gate (explainer page, section
+ * "Methodology", step 2).  Reading taken: per (token, head) row, an RMS norm
+ * of the recurrence output with a learned per-feature weight, times SiLU of a
+ * gate projection:
+ *
+ *     out[b][t][h][:] = o / sqrt(mean over the d features of o^2 + 1e-6) * w * SiLU(z).
+ *
+ * o     [B][T][H][d] fp32 (the output of gdn_prefill / gdn_stream_chunk).
+ * z     [B][T][H][d] bf16 (raw bits), the gate projection.
+ * w     [d] fp32, shared by all heads.
+ * out   [B][T][H][d], bf16 (out_dtype GDN_BF16, nearest even) or fp32
+ *       (GDN_F32); with GDN_F32 it may equal o exactly (in place).
+ * Sizes: d in {64, 128}; B, T, H >= 1.  Errors and conventions as above.
+ */
+int gdn_gate_out(const float *o, const void *z, const float *w, void *out, int out_dtype,
+                 int B, int T, int H, int d, void *stream);
+
+/*
  * gdn_set_profile_events -- kernel timing hook for measurement tools; not part
  * of the operation and without effect on results.
  *
- * With count > 0, each following gdn_prefill, gdn_stream_chunk or
- * gdn_decode_step call records events[0] on its stream before its first kernel
+ * With count > 0, each following call of a compute entry point records events[0] on its stream before its first kernel
  * and events[i] after its i-th kernel, while events last (later kernels are
  * not marked).  `events` holds hipEvent_t handles created by the caller, who
  * keeps them and the array alive while the hook is set.  count = 0 turns the
@@ -149,6 +203,7 @@ int gdn_decode_step(const void *q, const void *k, const void *v, int dtype,
  *   bf16 prefill, several segments:  summary pass, combine, output pass
  *   fp32 prefill:                    chunk prep, [summary pass, combine,] chain
  *   decode:                          step
+ *   conv_qkv, gate_out:              one kernel each
  * Returns GDN_OK, or GDN_ERR_NULL for events == NULL with count > 0, or
  * GDN_ERR_SHAPE for count < 0.
  */

@@ -11,11 +11,16 @@ Entry points (same names as the C ABI):
     stream_chunk(q, k, v, g, beta, state)         -> o        (state in place)
     decode_step(q, k, v, g, beta, state)          -> o        (state in place)
     prefill_workspace_bytes(B, T, H, dk, dv, dtype)
+    conv_qkv(xq, xk, xv, wq, wk, wv, state=None)  -> (q, k, v, state_out)
+    gate_out(o, z, w)                             -> out
     set_profile_events(handles), profile_marks()   (kernel timing hook)
 
 Shapes: q, k [B, T, H, dk]; v [B, T, H, dv]; g (log-decay), beta [B, T, H];
 state [B, H, dk, dv] fp32 with state[b, h, i, j] = S[j, i]; o fp32.  Decode drops
 the T axis.  q/k/v are torch.bfloat16 or torch.float32.
+
+Layer prologue / epilogue: xq, xk, xv, z [B, T, H, d] bf16; filters wq, wk, wv
+[H*d, 4] fp32; convolution state [B, 3, 3, H*d] fp32; norm weight w [d] fp32.
 """
 from __future__ import annotations
 
@@ -23,6 +28,7 @@ import ctypes
 import os
 
 __all__ = ["prefill", "stream_chunk", "decode_step", "prefill_workspace_bytes", "GdnError",
+           "conv_qkv", "gate_out",
            "library_path", "GDN_BF16", "GDN_F32", "set_profile_events", "profile_marks"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +62,10 @@ def _load():
     lib.gdn_stream_chunk.argtypes = [vp, vp, vp, i, fp, fp, fp, fp, i, i, i, i, i, vp, sz, vp]
     lib.gdn_decode_step.restype = i
     lib.gdn_decode_step.argtypes = [vp, vp, vp, i, fp, fp, fp, fp, i, i, i, i, vp]
+    lib.gdn_conv_qkv.restype = i
+    lib.gdn_conv_qkv.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.gdn_gate_out.restype = i
+    lib.gdn_gate_out.argtypes = [fp, vp, fp, vp, i, i, i, i, i, vp]
     lib.gdn_set_profile_events.restype = i
     lib.gdn_set_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     lib.gdn_profile_marks.restype = i
@@ -125,6 +135,36 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _need(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def _check(t, shape, dtype, name):
+    """Shape and dtype of a tensor argument (None passes): the library reads
+    and writes every buffer at the sizes taken from the leading tensor."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    _need(t, dtype, name)
+
+
+def _check_mixer(q, k, v, g, beta, states, o, tok):
+    """q, k, v, g, beta, state(s) and o of the recurrence entry points; `tok` is
+    (B, T, H) or (B, H) for decode."""
+    torch = _torch()
+    dk, dv = q.shape[-1], v.shape[-1]
+    B, H = tok[0], tok[-1]
+    _check(k, tuple(tok) + (dk,), q.dtype, "k")
+    _check(v, tuple(tok) + (dv,), q.dtype, "v")
+    _check(g, tok, torch.float32, "g")
+    _check(beta, tok, torch.float32, "beta")
+    for st, nm in states:
+        _check(st, (B, H, dk, dv), torch.float32, nm)
+    _check(o, tuple(tok) + (dv,), torch.float32, "o")
+
+
 def prefill_workspace_bytes(B, T, H, dk, dv, dtype=GDN_BF16) -> int:
     if not isinstance(dtype, int):
         dtype = _dtype_code(_torch().empty(0, dtype=dtype))
@@ -147,6 +187,8 @@ def prefill(q, k, v, g, beta, state_in=None, *, state_out=None, o=None, workspac
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     code = _dtype_code(q)
+    _check_mixer(q, k, v, g, beta, ((state_in, "state_in"), (state_out, "state_out")), o,
+                 (B, T, H))
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
     if state_out is None:
@@ -166,6 +208,7 @@ def stream_chunk(q, k, v, g, beta, state, *, o=None, workspace=None, stream=None
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     code = _dtype_code(q)
+    _check_mixer(q, k, v, g, beta, ((state, "state"),), o, (B, T, H))
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
     workspace, nbytes = _workspace(workspace, B, T, H, dk, dv, code, q.device)
@@ -184,6 +227,7 @@ def decode_step(q, k, v, g, beta, state, *, o=None, stream=None):
     B, H, dk = q.shape
     dv = v.shape[-1]
     code = _dtype_code(q)
+    _check_mixer(q, k, v, g, beta, ((state, "state"),), o, (B, H))
     if o is None:
         o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
     st = _lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), _ptr(state),
@@ -191,3 +235,53 @@ def decode_step(q, k, v, g, beta, state, *, o=None, stream=None):
     if st != 0:
         raise GdnError(st, "gdn_decode_step")
     return o
+
+
+def conv_qkv(xq, xk, xv, wq, wk, wv, state=None, *, state_out=None, q=None, k=None, v=None,
+             l2norm_qk=True, stream=None):
+    """Layer prologue: causal window-4 depthwise convolution + SiLU of the
+    projections xq, xk, xv [B, T, H, d] (bf16), q and k L2-normalised per head
+    when l2norm_qk.  `state` [B, 3, 3, H*d] fp32 holds the three previous input
+    tokens of each stream (None = zeros).  Returns (q, k, v, state_out) with
+    q, k, v bf16; pass state_out=state to update a stream's state in place."""
+    torch = _torch()
+    B, T, H, d = xq.shape
+    for t, nm in ((xq, "xq"), (xk, "xk"), (xv, "xv"), (q, "q"), (k, "k"), (v, "v")):
+        _check(t, xq.shape, torch.bfloat16, nm)
+    for t, nm in ((wq, "wq"), (wk, "wk"), (wv, "wv")):
+        _check(t, (H * d, 4), torch.float32, nm)
+    _check(state, (B, 3, 3, H * d), torch.float32, "state")
+    _check(state_out, (B, 3, 3, H * d), torch.float32, "state_out")
+    dev = xq.device
+    q = torch.empty_like(xq) if q is None else q
+    k = torch.empty_like(xk) if k is None else k
+    v = torch.empty_like(xv) if v is None else v
+    if state_out is None:
+        state_out = torch.empty((B, 3, 3, H * d), dtype=torch.float32, device=dev)
+    st = _lib.gdn_conv_qkv(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv),
+                           _ptr(state), _ptr(state_out), _ptr(q), _ptr(k), _ptr(v),
+                           1 if l2norm_qk else 0, B, T, H, d, _stream(stream, dev))
+    if st != 0:
+        raise GdnError(st, "gdn_conv_qkv")
+    return q, k, v, state_out
+
+
+def gate_out(o, z, w, *, out=None, out_dtype=None, stream=None):
+    """Layer epilogue: out = o / sqrt(mean(o^2) + 1e-6) * w * SiLU(z) per
+    (token, head) row.  o [B, T, H, d] fp32, z bf16, w [d] fp32; out is fp32
+    (default) or bf16 (out_dtype=torch.bfloat16); out may be o itself (fp32)."""
+    torch = _torch()
+    B, T, H, d = o.shape
+    _need(o, torch.float32, "o")
+    _check(z, o.shape, torch.bfloat16, "z")
+    _check(w, (d,), torch.float32, "w")
+    if out is not None and tuple(out.shape) != tuple(o.shape):
+        raise ValueError("out must have shape %s, got %s" % (tuple(o.shape), tuple(out.shape)))
+    if out is None:
+        out = torch.empty(o.shape, dtype=out_dtype or torch.float32, device=o.device)
+    code = _dtype_code(out)
+    st = _lib.gdn_gate_out(_ptr(o), _ptr(z), _ptr(w), _ptr(out), code, B, T, H, d,
+                           _stream(stream, o.device))
+    if st != 0:
+        raise GdnError(st, "gdn_gate_out")
+    return out

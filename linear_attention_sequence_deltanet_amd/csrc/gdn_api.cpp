@@ -124,7 +124,7 @@ const char* gdn_status_str(int status) {
         case GDN_ERR_SHAPE: return "invalid sizes (B, T, H, d must be >= 1 and d_k == d_v)";
         case GDN_ERR_DTYPE: return "dtype must be GDN_BF16 or GDN_F32";
         case GDN_ERR_ALIGN: return "every pointer must be 16-byte aligned";
-        case GDN_ERR_ALIAS: return "an output overlaps an input (only state_out == state_in is allowed)";
+        case GDN_ERR_ALIAS: return "an output overlaps an input or another output (only the documented in-place forms are allowed)";
         case GDN_ERR_UNSUPPORTED: return "unsupported sizes (d must be 64 or 128)";
         case GDN_ERR_WORKSPACE: return "workspace missing or smaller than gdn_prefill_workspace_bytes()";
         case GDN_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
@@ -174,6 +174,60 @@ int gdn_decode_step(const void* q, const void* k, const void* v, int dtype, cons
     gdn::profile_begin(static_cast<hipStream_t>(stream));
     return launch_status(gdn::launch_recurrent(q, k, v, dtype == GDN_BF16, g, beta, state, state,
                                                o, B, 1, H, dk, static_cast<hipStream_t>(stream)));
+}
+
+
+int gdn_conv_qkv(const void* xq, const void* xk, const void* xv, const float* wq, const float* wk,
+                 const float* wv, const float* conv_state_in, float* conv_state_out, void* q,
+                 void* k, void* v, int l2norm_qk, int B, int T, int H, int d, void* stream) {
+    if (B < 1 || T < 1 || H < 1 || d < 1) return GDN_ERR_SHAPE;
+    if (d != 64 && d != 128) return GDN_ERR_UNSUPPORTED;
+    const long long C = (long long)H * d, tok = (long long)B * T;
+    // int channel index, grid of B * ceil(T / 16) * C / 8 threads
+    if (C > (1LL << 30) || tok * C > (1LL << 46)) return GDN_ERR_UNSUPPORTED;
+    if (!xq || !xk || !xv || !wq || !wk || !wv || !q || !k || !v) return GDN_ERR_NULL;
+    const void* ptrs[] = {xq, xk, xv, wq, wk, wv, conv_state_in, conv_state_out, q, k, v};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    const size_t xb = (size_t)tok * C * 2, wb = (size_t)C * 16, sb = (size_t)B * 9 * C * 4;
+    const Range ins[] = {span(xq, xb), span(xk, xb), span(xv, xb), span(wq, wb), span(wk, wb),
+                         span(wv, wb)};
+    const Range rsi = conv_state_in ? span(conv_state_in, sb) : Range{0, 0};
+    const Range rso = conv_state_out ? span(conv_state_out, sb) : Range{0, 0};
+    const Range outs[] = {span(q, xb), span(k, xb), span(v, xb), rso};
+    for (int i = 0; i < 4; ++i) {
+        for (const Range& in : ins)
+            if (overlap(outs[i], in)) return GDN_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return GDN_ERR_ALIAS;
+        if (i < 3 && overlap(outs[i], rsi)) return GDN_ERR_ALIAS;
+    }
+    if (overlap(rso, rsi) && conv_state_in != conv_state_out) return GDN_ERR_ALIAS;
+    gdn::profile_begin(static_cast<hipStream_t>(stream));
+    return launch_status(gdn::launch_conv_qkv(xq, xk, xv, wq, wk, wv, conv_state_in,
+                                              conv_state_out, q, k, v, l2norm_qk != 0, B, T, H,
+                                              d, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_gate_out(const float* o, const void* z, const float* w, void* out, int out_dtype, int B,
+                 int T, int H, int d, void* stream) {
+    if (out_dtype != GDN_BF16 && out_dtype != GDN_F32) return GDN_ERR_DTYPE;
+    if (B < 1 || T < 1 || H < 1 || d < 1) return GDN_ERR_SHAPE;
+    if (d != 64 && d != 128) return GDN_ERR_UNSUPPORTED;
+    const long long n = (long long)B * T * H * d;  // elements
+    if (n > (1LL << 46)) return GDN_ERR_UNSUPPORTED;
+    if (!o || !z || !w || !out) return GDN_ERR_NULL;
+    const void* ptrs[] = {o, z, w, out};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return GDN_ERR_ALIGN;
+    const Range ro = span(o, (size_t)n * 4), rz = span(z, (size_t)n * 2), rw = span(w, (size_t)d * 4),
+                rout = span(out, (size_t)n * (out_dtype == GDN_BF16 ? 2 : 4));
+    if (overlap(rout, rz) || overlap(rout, rw)) return GDN_ERR_ALIAS;
+    if (overlap(rout, ro) && !(out_dtype == GDN_F32 && out == static_cast<const void*>(o)))
+        return GDN_ERR_ALIAS;
+    gdn::profile_begin(static_cast<hipStream_t>(stream));
+    return launch_status(gdn::launch_gate_out(o, z, w, out, out_dtype == GDN_BF16, B, T, H, d,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

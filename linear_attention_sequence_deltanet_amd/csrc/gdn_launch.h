@@ -39,4 +39,15 @@ hipError_t launch_fused(const void* q, const void* k, const void* v, const float
                         const float* beta, const float* state_in, float* state_out, float* o,
                         int B, int T, int H, int D, void* ws, hipStream_t stream);
 
+// Layer prologue: causal window-4 depthwise convolution + SiLU of q, k, v
+// (optional q/k L2 norm), bf16 outputs, carried 3-token convolution state.
+hipError_t launch_conv_qkv(const void* xq, const void* xk, const void* xv, const float* wq,
+                           const float* wk, const float* wv, const float* state_in,
+                           float* state_out, void* q, void* k, void* v, int l2norm, int B, int T,
+                           int H, int D, hipStream_t stream);
+
+// Layer epilogue: per (token, head) RMS norm of o, times w and SiLU(z).
+hipError_t launch_gate_out(const float* o, const void* z, const float* w, void* out, int out_bf16,
+                           int B, int T, int H, int D, hipStream_t stream);
+
 }  // namespace gdn

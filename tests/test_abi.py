@@ -149,3 +149,58 @@ def test_profile_hook_host_paths(lib):
     assert lib.gdn_set_profile_events(arr, -1) == 2          # GDN_ERR_SHAPE
     assert lib.gdn_set_profile_events(None, 0) == 0
 
+
+
+L = {n: BASE + (16 + i) * GB
+     for i, n in enumerate(["xq", "xk", "xv", "wq", "wk", "wv", "csin", "csout", "q", "k", "v"])}
+
+
+def _conv(lib, B=1, T=100, H=2, d=128, l2=1, **over):
+    a = dict(L)
+    a.update(over)
+    return lib.gdn_conv_qkv(a["xq"], a["xk"], a["xv"], a["wq"], a["wk"], a["wv"], a["csin"],
+                            a["csout"], a["q"], a["k"], a["v"], l2, B, T, H, d, None)
+
+
+def test_conv_qkv_errors(lib):
+    for name in ("xq", "xk", "xv", "wq", "wk", "wv", "q", "k", "v"):
+        assert _conv(lib, **{name: None}) == NULL, name
+    for name in L:
+        assert _conv(lib, **{name: L[name] + 8}) == ALIGN, name
+    assert _conv(lib, B=0) == SHAPE
+    assert _conv(lib, T=0) == SHAPE
+    assert _conv(lib, d=96) == UNSUP
+    assert _conv(lib, q=L["xk"] + 4096) == ALIAS        # output inside an input
+    assert _conv(lib, v=L["q"] + 16) == ALIAS           # two outputs overlap
+    assert _conv(lib, csout=L["wq"]) == ALIAS
+    assert _conv(lib, k=L["csin"]) == ALIAS
+    assert _conv(lib, csout=L["csin"] + 16) == ALIAS    # partial in-place overlap
+
+
+def test_conv_qkv_optional_state_is_accepted_on_the_host(lib):
+    """NULL states are valid; with a huge T the size check fires before any
+    launch, so no device memory is touched."""
+    assert _conv(lib, csin=None, csout=None, T=1 << 30, H=1 << 10) == UNSUP
+    assert _conv(lib, csout=L["csin"], T=1 << 30, H=1 << 10) == UNSUP
+
+
+G_ = {n: BASE + (40 + i) * GB for i, n in enumerate(["o", "z", "w", "out"])}
+
+
+def _gate(lib, B=1, T=100, H=2, d=128, dt=1, **over):
+    a = dict(G_)
+    a.update(over)
+    return lib.gdn_gate_out(a["o"], a["z"], a["w"], a["out"], dt, B, T, H, d, None)
+
+
+def test_gate_out_errors(lib):
+    for name in G_:
+        assert _gate(lib, **{name: None}) == NULL, name
+        assert _gate(lib, **{name: G_[name] + 4}) == ALIGN, name
+    assert _gate(lib, dt=2) == DTYPE
+    assert _gate(lib, H=0) == SHAPE
+    assert _gate(lib, d=32) == UNSUP
+    assert _gate(lib, out=G_["z"]) == ALIAS
+    assert _gate(lib, out=G_["o"], dt=0) == ALIAS       # in place only for fp32 out
+    assert _gate(lib, out=G_["o"] + 16) == ALIAS
+    assert _gate(lib, out=G_["w"] - 16) == ALIAS
