@@ -4,8 +4,14 @@ A step is one whole-path call over one batch of synthetic inputs already in HBM:
   * value: gdn_prefill over the 8192-token prompt, B=1, H=16, d_k=d_v=128, bf16
     q/k/v, fp32 gates/state/output, zero initial state (tokens/s);
   * decode: gdn_decode_step for 64 sequences x 16 heads, d=128, fp32 state updated
-    in place, 1000 consecutive steps with fresh inputs (tokens/s, reported beside);
+    in place, 1000 consecutive steps with fresh inputs (tokens/s, reported beside),
+    and decode512: the same at 512 sequences, whose 537 MB state exceeds the
+    256 MB last-level cache;
+  * cold figures: single calls (or loops) timed right after a 1 GiB write that
+    evicts the caches;
   * long_prefill: gdn_prefill over 262144 tokens (tokens/s, beside);
+  * layer: the layer around the recurrence at the prefill shapes, conv_qkv ->
+    prefill -> gate_out (bf16 output), tokens/s with each kernel's HBM rate;
   * stream: gdn_stream_chunk calls of 272 tokens (256 visual + 16 text) carrying
     the state in place; the first 200 frames of the stream are staged and replayed
     in order (calls/s = frames/s, beside).
@@ -42,6 +48,12 @@ PREFILL_FLOPS_PER_TOKEN_HEAD = 6 * 128 * 128 + 64 * (3 * 128 + 2 * 128)
 # g, beta (8) + o fp32 (512)
 DECODE_BYTES_PER_HEAD = 2 * 128 * 128 * 4 + 3 * 256 + 8 + 512
 
+# Layer prologue / epilogue per token x head at d = 128: conv reads xq, xk, xv
+# and writes q, k, v (bf16, 6 x 256); the gate reads o (fp32, 512) and z (bf16,
+# 256) and writes the bf16 output (256).
+CONV_BYTES_PER_TOKEN_HEAD = 6 * 256
+GATE_BYTES_PER_TOKEN_HEAD = 512 + 256 + 256
+
 # Kernels of one bf16 prefill call of several segments, in launch order, with
 # the algorithmic bytes per token x head each reads or writes.
 PREFILL_KERNELS = [("summary pass (gdn_fused<128,false>)", 2 * 256 + 8),
@@ -67,6 +79,10 @@ def parse():
     p.add_argument("--no-long", action="store_true")
     p.add_argument("--long-reps", type=int, default=3)
     p.add_argument("--no-stream", action="store_true")
+    p.add_argument("--no-layer", action="store_true")
+    p.add_argument("--cold-reps", type=int, default=20)
+    p.add_argument("--no-b512", action="store_true")
+    p.add_argument("--b512-steps", type=int, default=100)
     p.add_argument("--stream-calls", type=int, default=2000)
     p.add_argument("--stream-frames", type=int, default=200)
     p.add_argument("--copy-mib", type=int, default=0,
@@ -159,6 +175,36 @@ def stage_bf16(arr, dev):
     return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
+class Flush:
+    """Evicts the caches (including the 256 MB last-level cache) by writing a
+    1 GiB scratch buffer on the stream before a cold rep."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(float(self.n))
+
+
+def cold_ms(call, reps, flush, stream):
+    """Median over `reps` of one call timed alone right after a cache flush."""
+    import torch
+    times = []
+    for _ in range(reps):
+        flush()
+        a = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        e.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(e))
+    return float(np.median(times))
+
+
 def time_prefill(gdn, args, dev):
     import torch
     import gdn_inputs
@@ -185,7 +231,10 @@ def time_prefill(gdn, args, dev):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     kms = kernel_times(gdn, call, args.steps)
-    return d, ms, kms, (B, T, H, dk)
+    flush = Flush(dev)
+    cms = cold_ms(call, args.cold_reps, flush, stream)
+    del flush
+    return d, ms, kms, cms, (B, T, H, dk)
 
 
 def time_decode(gdn, args, dev):
@@ -229,7 +278,55 @@ def time_decode(gdn, args, dev):
 
     state.copy_(s0)
     gms = graph_ms(loop) / N
-    return ms, kms, gms, (N, B, H, dk)
+    # cold: the whole loop right after a cache flush (only its first steps can miss)
+    flush = Flush(dev)
+    state.copy_(s0)
+    cms = cold_ms(loop, 1, flush, stream) / N
+    del flush
+    return ms, kms, gms, cms, (N, B, H, dk)
+
+
+def time_decode_b512(gdn, args, dev):
+    """decode512: B=512 sequences, 537 MB of state (beyond the 256 MB last-level
+    cache), `b512_steps` steps, median of 3 loops."""
+    import torch
+    import gdn_inputs
+    d = gdn_inputs.decode_inputs("decode64", steps=args.b512_steps, B=512)
+    N, B, H, dk = d["q"].shape
+    q, k, v = (stage_bf16(d[x], dev) for x in ("q", "k", "v"))
+    g = torch.from_numpy(d["g"]).to(dev)
+    beta = torch.from_numpy(d["beta"]).to(dev)
+    s0 = torch.from_numpy(d["state0"]).to(dev)
+    del d
+    state = s0.clone()
+    o = torch.empty((N, B, H, dk), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def loop():
+        for n in range(N):
+            gdn.decode_step(q[n], k[n], v[n], g[n], beta[n], state, o=o[n])
+
+    loop()
+    times = []
+    for _ in range(3):
+        state.copy_(s0)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        loop()
+        e.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(e) / N)
+    ms = float(np.median(times))
+    nbytes = DECODE_BYTES_PER_HEAD * B * H
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"workload": "decode512: B=512 sequences, H=16, d=128, %d steps, 537 MB state in place"
+                        % N,
+            "value": B / (ms / 1e3), "unit": "tokens/s", "us_per_step": ms * 1e3,
+            "roofline": {"kernel": "decode step (decode_kernel<bf16,128>)", "bound": "hbm",
+                         "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": nbytes}}
 
 
 def graph_ms(loop, reps=3):
@@ -354,6 +451,61 @@ def time_stream(gdn, args, dev):
                          "frac": gbs / HBM_PEAK_GBS, "bytes_per_call": cbytes}}
 
 
+def time_layer(gdn, args, dev):
+    """layer8k: conv_qkv -> prefill -> gate_out over the prefill8k shapes."""
+    import torch
+    import gdn_inputs
+    B, T, H, dk = 1, 8192, 16, 128
+    x = gdn_inputs.layer_inputs(B, T, H, dk, seed=8192)
+    t = {n: (stage_bf16(x[n], dev) if x[n].dtype == np.uint16 else torch.from_numpy(x[n]).to(dev))
+         for n in ("xq", "xk", "xv", "z", "wq", "wk", "wv", "wn", "g", "beta")}
+    del x
+    q, k, v = (torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    cst = torch.empty((B, 3, 3, H * dk), dtype=torch.float32, device=dev)
+    o = torch.empty((B, T, H, dk), dtype=torch.float32, device=dev)
+    st = torch.empty((B, H, dk, dk), dtype=torch.float32, device=dev)
+    out = torch.empty((B, T, H, dk), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(16, gdn.prefill_workspace_bytes(B, T, H, dk, dk)), dtype=torch.uint8,
+                     device=dev)
+    conv = lambda: gdn.conv_qkv(t["xq"], t["xk"], t["xv"], t["wq"], t["wk"], t["wv"], None,
+                                state_out=cst, q=q, k=k, v=v)
+    rec = lambda: gdn.prefill(q, k, v, t["g"], t["beta"], None, state_out=st, o=o, workspace=ws)
+    gate = lambda: gdn.gate_out(o, t["z"], t["wn"], out=out)
+
+    def layer():
+        conv()
+        rec()
+        gate()
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        layer()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        layer()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(e) / args.steps
+    units = B * T * H
+    res = []
+    for name, call, per_unit, extra in (
+            ("conv_qkv (conv_qkv_kernel<128,16>)", conv, CONV_BYTES_PER_TOKEN_HEAD,
+             3 * H * dk * 16 + 9 * B * H * dk * 4),
+            ("gate_out (gate_out_kernel<128,4,bf16>)", gate, GATE_BYTES_PER_TOKEN_HEAD, dk * 4)):
+        kt = kernel_times(gdn, call, args.steps)[0]
+        nbytes = per_unit * units + extra
+        gbs = nbytes / (kt / 1e3) / 1e9
+        res.append({"kernel": name, "us": kt * 1e3, "bytes_per_launch": nbytes, "bound": "hbm",
+                    "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": gbs / HBM_PEAK_GBS})
+    return {"workload": "layer8k: conv_qkv (window 4, q/k L2 norm) -> gdn_prefill -> gate_out "
+                        "(bf16 out), B=1, H=16, T=8192, d=128, zero states",
+            "value": B * T / (ms / 1e3), "unit": "tokens/s", "ms_per_call": ms, "kernels": res}
+
+
 def cpu_baseline(d, seconds):
     """Time the fp64 oracle on the host over (repeats of) the prefill workload."""
     import gdn_inputs
@@ -403,7 +555,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    d, ms, kms, (B, T, H, dk) = time_prefill(gdn, args, dev)
+    d, ms, kms, cms, (B, T, H, dk) = time_prefill(gdn, args, dev)
     tok_s = B * T / (ms / 1e3)
     units = B * T * H
     bytes_call = PREFILL_BYTES_PER_TOKEN_HEAD * units
@@ -436,6 +588,9 @@ def main():
                      "mfma_tflops": dtfs,
                      "mfma_frac": None if dtfs is None else dtfs / MFMA_F16_PEAK_TFS},
         "kernels": kernels,
+        "cold": {"ms_per_call": cms, "value": B * T / (cms / 1e3), "unit": "tokens/s",
+                 "note": "median of %d single calls, each after a 1 GiB cache-evicting write"
+                         % args.cold_reps},
         "call_roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": gbs / HBM_PEAK_GBS, "mfma_tflops": tfs,
                           "mfma_frac": tfs / MFMA_F16_PEAK_TFS, "bytes_per_call": bytes_call,
@@ -443,7 +598,7 @@ def main():
                           "us_per_call_with_hook": sum(kms) * 1e3},
     }
     if not args.no_decode:
-        dms, dkms, dgms, (N, DB, DH, ddk) = time_decode(gdn, args, dev)
+        dms, dkms, dgms, dcms, (N, DB, DH, ddk) = time_decode(gdn, args, dev)
         dbytes = DECODE_BYTES_PER_HEAD * DB * DH
         # one kernel per step: the step time over the timed loop is the kernel's
         # average launch duration (the per-kernel hook pass is reported beside)
@@ -451,15 +606,22 @@ def main():
         line["decode"] = {
             "workload": "decode64: B=64 sequences, H=16, d=128, %d steps, state in place" % N,
             "value": DB / (dms / 1e3), "unit": "tokens/s", "us_per_step": dms * 1e3,
-            "roofline": {"kernel": "decode step (recurrent_kernel<bf16,128>)", "bound": "hbm",
+            "roofline": {"kernel": "decode step (decode_kernel<bf16,128>)", "bound": "hbm",
                          "achieved": kgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": kgbs / HBM_PEAK_GBS,
-                         "traffic": committed_traffic("decode step (recurrent_kernel<bf16,128>)"),
+                         "traffic": committed_traffic("decode step (decode_kernel<bf16,128>)"),
                          "us_per_launch": dms * 1e3, "bytes_per_launch": dbytes,
                          "us_per_launch_hook": dkms[0] * 1e3},
             "graph": {"value": DB / (dgms / 1e3), "unit": "tokens/s", "us_per_step": dgms * 1e3,
                       "note": "the %d-step loop captured once as a HIP graph and replayed" % N},
+            "cold": {"value": DB / (dcms / 1e3), "unit": "tokens/s", "us_per_step": dcms * 1e3,
+                     "note": "the %d-step loop right after a 1 GiB cache-evicting write; the "
+                             "67 MB state fits the 256 MB last-level cache, see decode512" % N},
         }
+        if not args.no_b512:
+            line["decode512"] = time_decode_b512(gdn, args, dev)
+    if not args.no_layer:
+        line["layer"] = time_layer(gdn, args, dev)
     if not args.no_long:
         line["long_prefill"] = time_long_prefill(gdn, args, dev)
     if not args.no_stream:

@@ -168,12 +168,13 @@ int gdn_decode_step(const void* q, const void* k, const void* v, int dtype, cons
                     void* stream) {
     int s = check_sizes(B, 1, H, dk, dv, dtype);
     if (s != GDN_OK) return s;
+    if ((long long)B * H > (1LL << 30)) return GDN_ERR_UNSUPPORTED;  // grid of B*H*d/64 blocks
     if (!state) return GDN_ERR_NULL;
     s = check_io(q, k, v, dtype, g, beta, state, state, o, B, 1, H, dk, dv, nullptr, 0);
     if (s != GDN_OK) return s;
     gdn::profile_begin(static_cast<hipStream_t>(stream));
-    return launch_status(gdn::launch_recurrent(q, k, v, dtype == GDN_BF16, g, beta, state, state,
-                                               o, B, 1, H, dk, static_cast<hipStream_t>(stream)));
+    return launch_status(gdn::launch_decode(q, k, v, dtype == GDN_BF16, g, beta, state, o, B, H,
+                                            dk, static_cast<hipStream_t>(stream)));
 }
 
 

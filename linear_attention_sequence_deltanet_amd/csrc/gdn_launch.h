@@ -13,11 +13,11 @@ namespace gdn {
 void profile_begin(hipStream_t stream);
 void profile_mark(hipStream_t stream);
 
-// Token-serial recurrence, one workgroup per (batch, head); also the decode step (T = 1).
-hipError_t launch_recurrent(const void* q, const void* k, const void* v, int dtype_bf16,
-                            const float* g, const float* beta, const float* state_in,
-                            float* state_out, float* o, int B, int T, int H, int D,
-                            hipStream_t stream);
+// Decode step: one token per (batch, head), state updated in place; one wave
+// per 32-column slice of a head's state.
+hipError_t launch_decode(const void* q, const void* k, const void* v, int dtype_bf16,
+                         const float* g, const float* beta, float* state, float* o, int B, int H,
+                         int D, hipStream_t stream);
 
 // Chunkwise-parallel prefill (prep + scan kernels) using a caller workspace of
 // chunked_workspace_bytes() bytes.

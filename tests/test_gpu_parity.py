@@ -136,6 +136,44 @@ def test_decode64_1000_steps(env):
     _check("decode64", outs.cpu().numpy(), state.cpu().numpy(), ro, rs, TOL["bf16"])
 
 
+def _decode_run(gdn, dev, d):
+    import torch
+    x = stage(d, dev)
+    state = x["state0"].clone()
+    N, B, H, dv = d["v"].shape
+    outs = torch.empty((N, B, H, dv), dtype=torch.float32, device=dev)
+    for n in range(N):
+        gdn.decode_step(x["q"][n], x["k"][n], x["v"][n], x["g"][n], x["beta"][n], state,
+                        o=outs[n])
+    torch.cuda.synchronize()
+    f = lambda a: gdn_inputs.to_f64(a, d["dtype"])
+    ro, rs = oracle.decode_steps(f(d["q"]), f(d["k"]), f(d["v"]), d["g"], d["beta"],
+                                 d["state0"])
+    return outs.cpu().numpy(), state.cpu().numpy(), ro, rs
+
+
+def test_decode_streamed_state(env):
+    """B=160, H=16, d=128: a 160 MiB state, above the size from which the step
+    streams the state with non-temporal accesses; 20 steps, every head."""
+    gdn, dev = env
+    _note("case decode B=160 (streamed state) 20 steps")
+    d = gdn_inputs.decode_inputs("decode64", steps=20, B=160)
+    _check("decode160", *_decode_run(gdn, dev, d), TOL["bf16"])
+
+
+@pytest.mark.parametrize("dk,dtype", [(64, "bf16"), (64, "f32"), (128, "f32")])
+def test_decode_small(env, dk, dtype):
+    """B=4, H=5, 6 steps from a random state, d in {64, 128}, bf16 and fp32 inputs
+    (B*H = 20 keeps every per-step slice of g and beta 16-byte aligned)."""
+    gdn, dev = env
+    _note("case decode small d=%d %s" % (dk, dtype))
+    d0 = gdn_inputs.random_inputs(4, 6, 5, dk, dk, dtype=dtype, seed=31 + dk, state_std=0.2)
+    d = {n: np.ascontiguousarray(np.moveaxis(d0[n], 1, 0)) for n in ("q", "k", "v", "g", "beta")}
+    d["state0"] = d0["state0"]
+    d["dtype"] = dtype
+    _check("decode small", *_decode_run(gdn, dev, d), TOL[dtype])
+
+
 def test_stream_sampled(env):
     """2000 calls x 272 tokens (256 visual + 16 text), state carried in place.
     GPU runs all 16 heads; oracle checks 2 heads over the whole 544,000 tokens."""
