@@ -248,3 +248,13 @@ def layer_inputs(B: int, T: int, H: int, d: int, seed: int = 0, with_state: bool
     x = rng.standard_normal((B, T, H), dtype=np.float32)
     out["beta"] = (1.0 / (1.0 + np.exp(-x))).astype(np.float32)
     return out
+
+
+def swa_inputs(B: int, T: int, Hq: int = 16, Hkv: int = 2, d: int = 128, seed: int = 0) -> dict:
+    """Seeded inputs of the sliding-window attention layer (no method
+    arithmetic): q [B, T, Hq, d], k, v [B, T, Hkv, d] as bf16 bits ~ N(0, 1),
+    the post-projection activations the layer receives."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0x5A11]))
+    return {"q": bf16_bits(rng.standard_normal((B, T, Hq, d), dtype=np.float32)),
+            "k": bf16_bits(rng.standard_normal((B, T, Hkv, d), dtype=np.float32)),
+            "v": bf16_bits(rng.standard_normal((B, T, Hkv, d), dtype=np.float32))}
