@@ -190,6 +190,64 @@ int gdn_gate_out(const float *o, const void *z, const float *w, void *out, int o
                  int B, int T, int H, int d, void *stream);
 
 /*
+ * Sliding-window attention (SWA): the other token mixer of InfiniteVL's hybrid
+ * blocks (explainer page "InfiniteVL: Synergizing Linear and Sparse Attention
+ * ...", section "The Concept: Sliding Window Attention": attention restricted to
+ * a moving window of recent tokens; section "Methodology", step 2: RoPE
+ * positions, grouped-query attention with 16 query heads over 2 key-value
+ * heads, an 8K window in the example).  Readings taken where the pages are
+ * silent:
+ *   - window W: the query at absolute position t attends to the keys at
+ *     positions s with t - W < s <= t (itself and the W - 1 before it);
+ *   - rotary embedding as in RoFormer (on the page's reading list): feature
+ *     pairs (2i, 2i+1) of q and k rotated by the angle p * base^(-2i/d) at
+ *     absolute position p;
+ *   - query head h reads key-value head h / (Hq / Hkv); scores q.k / sqrt(d),
+ *     softmax over the window; output o = softmax-weighted sum of v.
+ *
+ * q [B][T][Hq][d], k, v [B][T][Hkv][d] bf16 (raw bits); o [B][T][Hq][d] fp32.
+ * Sizes: d = 128; Hq a multiple of Hkv; W >= 1; rope_base > 1 (RoFormer: 10000).
+ * Matrix-core operands are fp16 (rotated q, k and v rounded once), with fp32
+ * accumulation and softmax.
+ */
+
+/* Workspace bytes of gdn_swa_prefill / gdn_swa_stream_chunk (0 for invalid sizes). */
+size_t gdn_swa_workspace_bytes(int B, int T, int Hq, int Hkv, int d);
+
+/*
+ * Bytes of EACH of the two ring caches (k_cache, v_cache) a stream of window W
+ * needs: [B][Hkv][W - 1][d] fp16 (rotated keys; values).  0 for W < 2 (no
+ * history is needed) or invalid sizes.
+ */
+size_t gdn_swa_cache_bytes(int B, int Hkv, int d, int window);
+
+/*
+ * gdn_swa_prefill -- SWA over T tokens at positions 0 .. T-1, no history.
+ * workspace: at least gdn_swa_workspace_bytes() bytes, contents ignored.
+ */
+int gdn_swa_prefill(const void *q, const void *k, const void *v, float *o,
+                    int B, int T, int Hq, int Hkv, int d, int window, float rope_base,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_swa_stream_chunk -- the next T tokens of B streams at absolute positions
+ * pos0 .. pos0 + T - 1 (InfiniteVL's streaming keeps a constant-size window
+ * cache).  k_cache, v_cache (gdn_swa_cache_bytes() bytes each, or both NULL
+ * when W = 1) hold the rotated keys and the values of the positions before
+ * pos0, in ring slots (position mod (W - 1)); the call reads the ones inside
+ * the window (positions >= max(0, pos0 - W + 1)), then writes its own last
+ * min(T, W - 1) tokens into their slots.  Start a stream with pos0 = 0 (the
+ * caches' contents are then ignored) and pass pos0 = the number of tokens
+ * already streamed on each following call; successive calls equal one
+ * gdn_swa_prefill over the concatenated tokens, up to rounding.
+ * No argument may overlap another.
+ */
+int gdn_swa_stream_chunk(const void *q, const void *k, const void *v,
+                         void *k_cache, void *v_cache, long long pos0, float *o,
+                         int B, int T, int Hq, int Hkv, int d, int window, float rope_base,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * gdn_set_profile_events -- kernel timing hook for measurement tools; not part
  * of the operation and without effect on results.
  *
@@ -204,6 +262,8 @@ int gdn_gate_out(const float *o, const void *z, const float *w, void *out, int o
  *   fp32 prefill:                    chunk prep, [summary pass, combine,] chain
  *   decode:                          step
  *   conv_qkv, gate_out:              one kernel each
+ *   swa prefill:                     rotary prep, attention
+ *   swa stream chunk:                rotary prep, attention, cache update
  * Returns GDN_OK, or GDN_ERR_NULL for events == NULL with count > 0, or
  * GDN_ERR_SHAPE for count < 0.
  */

@@ -13,6 +13,9 @@ Entry points (same names as the C ABI):
     prefill_workspace_bytes(B, T, H, dk, dv, dtype)
     conv_qkv(xq, xk, xv, wq, wk, wv, state=None)  -> (q, k, v, state_out)
     gate_out(o, z, w)                             -> out
+    swa_prefill(q, k, v, window)                  -> o   (sliding-window attention)
+    swa_stream_chunk(q, k, v, k_cache, v_cache, pos0, window) -> o
+    swa_workspace_bytes(...), swa_cache_bytes(...)
     set_profile_events(handles), profile_marks()   (kernel timing hook)
 
 Shapes: q, k [B, T, H, dk]; v [B, T, H, dv]; g (log-decay), beta [B, T, H];
@@ -28,7 +31,8 @@ import ctypes
 import os
 
 __all__ = ["prefill", "stream_chunk", "decode_step", "prefill_workspace_bytes", "GdnError",
-           "conv_qkv", "gate_out",
+           "conv_qkv", "gate_out", "swa_prefill", "swa_stream_chunk", "swa_workspace_bytes",
+           "swa_cache_bytes", "swa_new_cache",
            "library_path", "GDN_BF16", "GDN_F32", "set_profile_events", "profile_marks"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +70,16 @@ def _load():
     lib.gdn_conv_qkv.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, vp, vp, vp, i, i, i, i, i, vp]
     lib.gdn_gate_out.restype = i
     lib.gdn_gate_out.argtypes = [fp, vp, fp, vp, i, i, i, i, i, vp]
+    ll = ctypes.c_longlong
+    lib.gdn_swa_workspace_bytes.restype = sz
+    lib.gdn_swa_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.gdn_swa_cache_bytes.restype = sz
+    lib.gdn_swa_cache_bytes.argtypes = [i, i, i, i]
+    lib.gdn_swa_prefill.restype = i
+    lib.gdn_swa_prefill.argtypes = [vp, vp, vp, fp, i, i, i, i, i, i, ctypes.c_float, vp, sz, vp]
+    lib.gdn_swa_stream_chunk.restype = i
+    lib.gdn_swa_stream_chunk.argtypes = [vp, vp, vp, vp, vp, ll, fp, i, i, i, i, i, i,
+                                         ctypes.c_float, vp, sz, vp]
     lib.gdn_set_profile_events.restype = i
     lib.gdn_set_profile_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i]
     lib.gdn_profile_marks.restype = i
@@ -285,3 +299,79 @@ def gate_out(o, z, w, *, out=None, out_dtype=None, stream=None):
     if st != 0:
         raise GdnError(st, "gdn_gate_out")
     return out
+
+
+ROPE_BASE = 10000.0
+
+
+def swa_workspace_bytes(B, T, Hq, Hkv, d=128) -> int:
+    return int(_lib.gdn_swa_workspace_bytes(B, T, Hq, Hkv, d))
+
+
+def swa_cache_bytes(B, Hkv, d, window) -> int:
+    return int(_lib.gdn_swa_cache_bytes(B, Hkv, d, window))
+
+
+def swa_new_cache(B, Hkv, d, window, device):
+    """(k_cache, v_cache) fp16 ring buffers [B, Hkv, W-1, d] for a stream, or
+    (None, None) when W = 1."""
+    torch = _torch()
+    if window < 2:
+        return None, None
+    return tuple(torch.empty((B, Hkv, window - 1, d), dtype=torch.float16, device=device)
+                 for _ in range(2))
+
+
+def _swa_check(q, k, v, o):
+    torch = _torch()
+    B, T, Hq, d = q.shape
+    _need(q, torch.bfloat16, "q")
+    Hkv = k.shape[2]
+    _check(k, (B, T, Hkv, d), torch.bfloat16, "k")
+    _check(v, (B, T, Hkv, d), torch.bfloat16, "v")
+    _check(o, (B, T, Hq, d), torch.float32, "o")
+    return B, T, Hq, Hkv, d
+
+
+def swa_stream_chunk(q, k, v, k_cache, v_cache, pos0, window, *, rope_base=ROPE_BASE, o=None,
+                     workspace=None, stream=None):
+    """Sliding-window attention over the next T tokens of B streams (absolute
+    positions pos0 ..); the ring caches from swa_new_cache() carry the window
+    across calls and are updated in place.  q [B, T, Hq, d], k, v [B, T, Hkv, d]
+    bf16; returns o [B, T, Hq, d] fp32."""
+    torch = _torch()
+    B, T, Hq, Hkv, d = _swa_check(q, k, v, o)
+    if k_cache is not None:
+        _check(k_cache, (B, Hkv, window - 1, d), torch.float16, "k_cache")
+        _check(v_cache, (B, Hkv, window - 1, d), torch.float16, "v_cache")
+    if o is None:
+        o = torch.empty((B, T, Hq, d), dtype=torch.float32, device=q.device)
+    need = swa_workspace_bytes(B, T, Hq, Hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.gdn_swa_stream_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
+                                   int(pos0), _ptr(o), B, T, Hq, Hkv, d, window,
+                                   float(rope_base), _ptr(workspace), nbytes,
+                                   _stream(stream, q.device))
+    if st != 0:
+        raise GdnError(st, "gdn_swa_stream_chunk")
+    return o
+
+
+def swa_prefill(q, k, v, window, *, rope_base=ROPE_BASE, o=None, workspace=None, stream=None):
+    """Sliding-window attention over T tokens at positions 0 .. T-1 (no
+    history).  Returns o [B, T, Hq, d] fp32."""
+    torch = _torch()
+    B, T, Hq, Hkv, d = _swa_check(q, k, v, o)
+    if o is None:
+        o = torch.empty((B, T, Hq, d), dtype=torch.float32, device=q.device)
+    need = swa_workspace_bytes(B, T, Hq, Hkv, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.gdn_swa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, Hq, Hkv, d, window,
+                              float(rope_base), _ptr(workspace), nbytes, _stream(stream, q.device))
+    if st != 0:
+        raise GdnError(st, "gdn_swa_prefill")
+    return o

@@ -231,4 +231,61 @@ int gdn_gate_out(const float* o, const void* z, const float* w, void* out, int o
                                               static_cast<hipStream_t>(stream)));
 }
 
+
+size_t gdn_swa_workspace_bytes(int B, int T, int Hq, int Hkv, int d) {
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d != 128) return 0;
+    return gdn::swa_workspace_bytes(B, T, Hq, Hkv, d);
+}
+
+size_t gdn_swa_cache_bytes(int B, int Hkv, int d, int window) {
+    if (B < 1 || Hkv < 1 || d != 128 || window < 2) return 0;
+    return (size_t)B * Hkv * (size_t)(window - 1) * d * 2;
+}
+
+int gdn_swa_stream_chunk(const void* q, const void* k, const void* v, void* k_cache,
+                         void* v_cache, long long pos0, float* o, int B, int T, int Hq, int Hkv,
+                         int d, int window, float rope_base, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d < 1 || window < 1 || pos0 < 0)
+        return GDN_ERR_SHAPE;
+    if (Hq % Hkv != 0) return GDN_ERR_SHAPE;
+    if (d != 128) return GDN_ERR_UNSUPPORTED;
+    if (!(rope_base > 1.0f)) return GDN_ERR_SHAPE;
+    // grid (T / 128, Hq, B) and int token indices
+    if (B > 65535 || Hq > 65535 || (long long)B * T * (Hq + 2LL * Hkv) * d > (1LL << 46) ||
+        pos0 > (1LL << 52))
+        return GDN_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !o) return GDN_ERR_NULL;
+    if ((k_cache == nullptr) != (v_cache == nullptr)) return GDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, o, k_cache, v_cache, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    const size_t need = gdn::swa_workspace_bytes(B, T, Hq, Hkv, d);
+    if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+    const size_t tq = (size_t)B * T * Hq * d, tkv = (size_t)B * T * Hkv * d;
+    const size_t cb = gdn_swa_cache_bytes(B, Hkv, d, window);
+    const Range ins[] = {span(q, tq * 2), span(k, tkv * 2), span(v, tkv * 2)};
+    const Range outs[] = {span(o, tq * 4), span(workspace, need),
+                          k_cache ? span(k_cache, cb) : Range{0, 0},
+                          v_cache ? span(v_cache, cb) : Range{0, 0}};
+    for (int i = 0; i < 4; ++i) {
+        for (const Range& in : ins)
+            if (overlap(outs[i], in)) return GDN_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return GDN_ERR_ALIAS;
+    }
+    gdn::profile_begin(static_cast<hipStream_t>(stream));
+    return launch_status(gdn::launch_swa(q, k, v, window > 1 ? k_cache : nullptr,
+                                         window > 1 ? v_cache : nullptr, pos0, o, B, T, Hq, Hkv,
+                                         d, window, rope_base, workspace,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int gdn_swa_prefill(const void* q, const void* k, const void* v, float* o, int B, int T, int Hq,
+                    int Hkv, int d, int window, float rope_base, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    return gdn_swa_stream_chunk(q, k, v, nullptr, nullptr, 0, o, B, T, Hq, Hkv, d, window,
+                                rope_base, workspace, workspace_bytes, stream);
+}
+
 }  // extern "C"

@@ -1,0 +1,416 @@
+// gdn_swa.hip -- sliding-window attention (SWA) on gfx950: the other token mixer
+// of InfiniteVL's hybrid blocks (explainer page "InfiniteVL: Synergizing Linear
+// and Sparse Attention ...", sections "The Concept: Sliding Window Attention"
+// and "Methodology", step 2: attention inside a moving window of recent tokens,
+// RoPE positions, 16 query heads over 2 key-value heads).
+//
+// The query at absolute position t attends to the keys at positions s with
+// t - W < s <= t; scores are q.k / sqrt(d) after RoFormer rotary embedding of
+// q and k (feature pairs (2i, 2i+1) rotated by p * base^(-2i/d)); query head h
+// reads key-value head h / (Hq / Hkv).
+//
+// Three kernels per call, all on the caller's stream:
+//   swa_prep   rotates q and k at their absolute positions and converts q
+//              (pre-scaled by log2(e) / sqrt(d)), k and v to fp16 in the
+//              workspace, head-major ([B][H][T][d]).  bf16 inputs convert to
+//              fp16 exactly at activation magnitudes; rotated values keep
+//              3 more mantissa bits than bf16 would.
+//   swa_attn   flash-style attention: a workgroup owns 128 queries of one head
+//              (4 waves x 32) and walks 64-key blocks of their window.  A block
+//              of K (row-major) and V (transposed, two keys per dword) is
+//              staged in LDS, double-buffered.  Each wave forms S^T = K Q^T on
+//              the matrix cores, so lane column c of every tile is one query:
+//              the online softmax (running max m, sum l, base-2 exponentials),
+//              the rescale of O^T and the final 1/l are per-lane, and P^T feeds
+//              O^T += V^T P^T directly as the B operand of 16x16x32 fp16 MFMAs
+//              (the keys of a 32-key step are taken in the order the S^T tiles
+//              hold them, for both operands).
+//   swa_cache  (streaming only) writes the call's last W-1 rotated keys and
+//              values into the caller's ring cache for the next call.
+#include <algorithm>
+#include <cmath>
+
+#include "gdn_device.h"
+#include "gdn_launch.h"
+#include "gdn_mfma.h"
+
+namespace gdn {
+namespace {
+
+using H8 = f16x8;
+using H4 = f16x4;
+using MF = Mfma<_Float16>;
+
+constexpr int SD = 128;        // head dimension
+constexpr int QB = 128;        // queries per workgroup
+constexpr int KB = 64;         // keys per block
+constexpr int KLD = SD + 8;    // K tile row stride (halves)
+constexpr int VLD = KB + 8;    // V^T tile row stride (halves)
+constexpr float kNegBig = -1e30f;
+
+// ---------------------------------------------------------------------------
+// swa_prep: one thread per 8 features (4 rotation pairs) of one (b, t, head)
+// of q, k or v.
+// ---------------------------------------------------------------------------
+struct PrepArgs {
+    const uint16_t* q;  // bf16 [B][T][Hq][d]
+    const uint16_t* k;  // bf16 [B][T][Hkv][d]
+    const uint16_t* v;
+    _Float16* wq;       // [B][Hq][T][d]
+    _Float16* wk;       // [B][Hkv][T][d]
+    _Float16* wv;
+    long long pos0;
+    float qscale;
+    int B, T, Hq, Hkv;
+    double rev[SD / 2];  // base^(-2i/d) / (2 pi): rotation of pair i per position, in turns
+};
+
+__device__ __forceinline__ void bf16x8_to_f32(const uint4 u, float (&f)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+
+__global__ __launch_bounds__(256) void swa_prep(const PrepArgs a) {
+    const long item = (long)blockIdx.x * 256 + threadIdx.x;
+    constexpr int G = SD / 8;
+    const int heads = a.Hq + 2 * a.Hkv;
+    const long total = (long)a.B * a.T * heads * G;
+    if (item >= total) return;
+    const int part = (int)(item % G);
+    long rest = item / G;
+    const int hh = (int)(rest % heads);
+    rest /= heads;
+    const int t = (int)(rest % a.T);
+    const long b = rest / a.T;
+
+    const uint16_t* src;
+    _Float16* dst;
+    int kind;  // 0 q, 1 k, 2 v
+    if (hh < a.Hq) {
+        kind = 0;
+        src = a.q + ((b * a.T + t) * a.Hq + hh) * SD;
+        dst = a.wq + ((b * a.Hq + hh) * (long)a.T + t) * SD;
+    } else if (hh < a.Hq + a.Hkv) {
+        kind = 1;
+        const int h = hh - a.Hq;
+        src = a.k + ((b * a.T + t) * a.Hkv + h) * SD;
+        dst = a.wk + ((b * a.Hkv + h) * (long)a.T + t) * SD;
+    } else {
+        kind = 2;
+        const int h = hh - a.Hq - a.Hkv;
+        src = a.v + ((b * a.T + t) * a.Hkv + h) * SD;
+        dst = a.wv + ((b * a.Hkv + h) * (long)a.T + t) * SD;
+    }
+    float x[8];
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(src + part * 8), x);
+    if (kind < 2) {
+        const double p = (double)(a.pos0 + t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const double turns = p * a.rev[part * 4 + i];
+            const float fr = (float)(turns - floor(turns));  // [0, 1)
+            const float c = __builtin_amdgcn_cosf(fr), s = __builtin_amdgcn_sinf(fr);
+            const float x0 = x[2 * i], x1 = x[2 * i + 1];
+            x[2 * i] = x0 * c - x1 * s;
+            x[2 * i + 1] = x0 * s + x1 * c;
+        }
+        if (kind == 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] *= a.qscale;
+        }
+    }
+    H8 h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(x[i]);
+    *reinterpret_cast<H8*>(dst + part * 8) = h;
+}
+
+// ---------------------------------------------------------------------------
+// swa_attn
+// ---------------------------------------------------------------------------
+struct AttnArgs {
+    const _Float16* q;   // [B][Hq][T][d], scaled, rotated
+    const _Float16* k;   // [B][Hkv][T][d], rotated
+    const _Float16* v;   // [B][Hkv][T][d]
+    const _Float16* kc;  // ring [B][Hkv][R][d] (positions < pos0), or null
+    const _Float16* vc;
+    float* o;            // [B][T][Hq][d]
+    long long pos0;
+    int T, Hq, Hkv, W, R, hist, nqb;
+};
+
+// max / sum over the 4 lanes c, c+16, c+32, c+48 (one query of an S^T tile)
+__device__ __forceinline__ float qmax(float s) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    s = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float qsum(float s) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ unsigned pack_h2(_Float16 a, _Float16 b) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 p = {a, b};
+    return __builtin_bit_cast(unsigned, p);
+}
+
+__global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) _Float16 sK[2][KB * KLD];
+    __shared__ __attribute__((aligned(16))) _Float16 sV[2][SD * VLD];
+
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int g = lane / 16, c = lane % 16;
+    const int qb = a.nqb - 1 - (int)blockIdx.x;  // longest windows first
+    const int h = blockIdx.y;
+    const long b = blockIdx.z;
+    const int hk = h / (a.Hq / a.Hkv);
+    const int T = a.T, W = a.W;
+    const int t0 = qb * QB;
+
+    // key index j: j >= 0 is token j of this call, j < 0 is the ring entry of
+    // absolute position pos0 + j (available for j >= -hist)
+    const int jlo = max(t0 - W + 1, -a.hist);
+    const int jhi = min(t0 + QB - 1, T - 1);
+    const int nblk = (jhi - jlo) / KB + 1;
+
+    const _Float16* kbase = a.k + ((b * a.Hkv + hk) * (long)T) * SD;
+    const _Float16* vbase = a.v + ((b * a.Hkv + hk) * (long)T) * SD;
+    const _Float16* kcb = a.kc ? a.kc + ((b * a.Hkv + hk) * (long)a.R) * SD : nullptr;
+    const _Float16* vcb = a.vc ? a.vc + ((b * a.Hkv + hk) * (long)a.R) * SD : nullptr;
+
+    auto row_ptr = [&](const _Float16* base, const _Float16* ring, int j) -> const _Float16* {
+        if (j >= 0) return base + (long)j * SD;
+        const long pos = a.pos0 + j;
+        return ring + (pos % a.R) * SD;
+    };
+    // staging: K rows 16 i + tid / 16 (i < 4), V row pairs 2 (tid / 16) + {0, 1} + 32 i (i < 2);
+    // chunk tid % 16 of 16 bytes.  Rows outside [jlo, jhi] are zero.
+    const int ch = tid % 16, rw = tid / 16;
+    uint4 pk[4], pv[4];
+    auto load_block = [&](int j0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = j0 + 16 * i + rw;
+            pk[i] = (j <= jhi) ? *reinterpret_cast<const uint4*>(row_ptr(kbase, kcb, j) + ch * 8)
+                               : uint4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = j0 + 2 * rw + (i & 1) + 32 * (i >> 1);
+            pv[i] = (j <= jhi) ? *reinterpret_cast<const uint4*>(row_ptr(vbase, vcb, j) + ch * 8)
+                               : uint4{0, 0, 0, 0};
+        }
+    };
+    auto store_block = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4*>(&sK[buf][(16 * i + rw) * KLD + ch * 8]) = pk[i];
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+            const int r0 = 2 * rw + 32 * i2;
+            const H8 lo = __builtin_bit_cast(H8, pv[2 * i2]), hi = __builtin_bit_cast(H8, pv[2 * i2 + 1]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                *reinterpret_cast<unsigned*>(&sV[buf][(ch * 8 + e) * VLD + r0]) = pack_h2(lo[e], hi[e]);
+        }
+    };
+
+    // this wave's queries: t0 + 32 wave + 16 qt + c
+    const int qa = t0 + 32 * wave;
+    H8 qf[2][4];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        const int t = qa + 16 * qt + c;
+        const _Float16* qp = a.q + ((b * a.Hq + h) * (long)T + min(t, T - 1)) * SD;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[qt][s] = *reinterpret_cast<const H8*>(qp + 32 * s + 8 * g);
+    }
+    f32x4 acc[8][2];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[dt][0] = acc[dt][1] = zero4();
+    float m[2] = {kNegBig, kNegBig}, l[2] = {0.f, 0.f};
+
+    load_block(jlo);
+    store_block(0);
+    __syncthreads();
+
+    for (int bi = 0; bi < nblk; ++bi) {
+        const int j0 = jlo + bi * KB, buf = bi & 1;
+        if (bi + 1 < nblk) load_block(j0 + KB);
+
+        // does any query of this wave see a key of this block?
+        const bool live = qa < T && j0 <= qa + 31 && j0 + KB - 1 >= qa - W + 1;
+        if (live) {
+            f32x4 st[4][2];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) {
+                st[kt][0] = st[kt][1] = zero4();
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const H8 ka = *reinterpret_cast<const H8*>(&sK[buf][(16 * kt + c) * KLD + 32 * s + 8 * g]);
+                    st[kt][0] = MF::k32(ka, qf[0][s], st[kt][0]);
+                    st[kt][1] = MF::k32(ka, qf[1][s], st[kt][1]);
+                }
+            }
+            // masks: key j = j0 + 16 kt + 4 g + e, query t = qa + 16 qt + c
+            const bool full = j0 + KB - 1 <= qa && (qa + 31) - j0 < W && j0 + KB - 1 <= jhi;
+            if (!full) {
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) {
+                    const int t = qa + 16 * qt + c;
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int j = j0 + 16 * kt + 4 * g + e;
+                            const bool ok = j <= t && t - j < W && j <= jhi;
+                            st[kt][qt][e] = ok ? st[kt][qt][e] : -INFINITY;
+                        }
+                }
+            }
+            H8 pb[2][2];
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                float mx = st[0][qt][0];
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, st[kt][qt][e]);
+                const float mn = fmaxf(m[qt], qmax(mx));
+                const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);
+                m[qt] = mn;
+                float ps = 0.f;
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float p = __builtin_amdgcn_exp2f(st[kt][qt][e] - mn);
+                        ps += p;
+                        pb[qt][kt >> 1][4 * (kt & 1) + e] = static_cast<_Float16>(p);
+                    }
+                l[qt] = l[qt] * alpha + ps;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) acc[dt][qt] *= alpha;
+            }
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+                for (int j2 = 0; j2 < 2; ++j2) {
+                    const _Float16* vp = &sV[buf][(16 * dt + c) * VLD + 32 * j2 + 4 * g];
+                    const H4 v0 = *reinterpret_cast<const H4*>(vp);
+                    const H4 v1 = *reinterpret_cast<const H4*>(vp + 16);
+                    const H8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                    acc[dt][0] = MF::k32(va, pb[0][j2], acc[dt][0]);
+                    acc[dt][1] = MF::k32(va, pb[1][j2], acc[dt][1]);
+                }
+            }
+        }
+        if (bi + 1 < nblk) store_block(buf ^ 1);
+        __syncthreads();
+    }
+
+    // o[t][16 dt + 4 g + e] = acc / l
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        const int t = qa + 16 * qt + c;
+        const float inv = 1.0f / qsum(l[qt]);
+        if (t < T) {
+            float* op = a.o + ((b * T + t) * a.Hq + h) * (long)SD + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const f32x4 r = acc[dt][qt] * inv;
+                *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(r[0], r[1], r[2], r[3]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// swa_cache: the call's last min(T, R) rotated keys and values into the ring
+// (slot = absolute position mod R).  One thread per 16 bytes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void swa_cache(const _Float16* wk, const _Float16* wv,
+                                                 _Float16* kc, _Float16* vc, long long pos0,
+                                                 int B, int T, int Hkv, int R, int n) {
+    const long item = (long)blockIdx.x * 256 + threadIdx.x;
+    constexpr int G = SD / 8;
+    const long total = (long)B * Hkv * n * G * 2;
+    if (item >= total) return;
+    const int part = (int)(item % G);
+    long rest = item / G;
+    const int t = T - n + (int)(rest % n);
+    rest /= n;
+    const int kv = (int)(rest % 2);
+    const long bh = rest / 2;  // b * Hkv + h
+    const _Float16* src = (kv ? wv : wk) + (bh * T + t) * (long)SD + part * 8;
+    _Float16* dst = (kv ? vc : kc) + (bh * R + (pos0 + t) % R) * (long)SD + part * 8;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+}
+
+}  // namespace
+
+size_t swa_workspace_bytes(int B, int T, int Hq, int Hkv, int D) {
+    return (size_t)B * T * (Hq + 2 * (size_t)Hkv) * D * sizeof(_Float16);
+}
+
+hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
+                      long long pos0, float* o, int B, int T, int Hq, int Hkv, int D, int window,
+                      float rope_base, void* ws, hipStream_t stream) {
+    (void)D;  // 128 (checked by the caller)
+    _Float16* wq = static_cast<_Float16*>(ws);
+    _Float16* wk = wq + (size_t)B * Hq * T * SD;
+    _Float16* wv = wk + (size_t)B * Hkv * T * SD;
+
+    PrepArgs p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.wq = wq, p.wk = wk, p.wv = wv;
+    p.pos0 = pos0;
+    p.qscale = (float)(1.4426950408889634 / 11.313708498984761);  // log2(e) / sqrt(128)
+    p.B = B, p.T = T, p.Hq = Hq, p.Hkv = Hkv;
+    for (int i = 0; i < SD / 2; ++i)
+        p.rev[i] = std::pow((double)rope_base, -2.0 * i / SD) / (2.0 * 3.141592653589793);
+    const long items = (long)B * T * (Hq + 2 * Hkv) * (SD / 8);
+    hipLaunchKernelGGL(swa_prep, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    profile_mark(stream);
+    if (e != hipSuccess) return e;
+
+    const int R = window - 1;
+    const bool ring = k_cache && R > 0;
+    AttnArgs a;
+    a.q = wq, a.k = wk, a.v = wv;
+    a.kc = ring ? static_cast<const _Float16*>(k_cache) : nullptr;
+    a.vc = ring ? static_cast<const _Float16*>(v_cache) : nullptr;
+    a.o = o;
+    a.pos0 = pos0;
+    a.T = T, a.Hq = Hq, a.Hkv = Hkv, a.W = window, a.R = R > 0 ? R : 1;
+    a.hist = ring ? (int)std::min<long long>(R, pos0) : 0;
+    a.nqb = (T + QB - 1) / QB;
+    hipLaunchKernelGGL(swa_attn, dim3((unsigned)a.nqb, (unsigned)Hq, (unsigned)B), dim3(256), 0,
+                       stream, a);
+    e = hipGetLastError();
+    profile_mark(stream);
+    if (e != hipSuccess || !ring) return e;
+
+    const int n = std::min(T, R);
+    const long citems = (long)B * Hkv * n * (SD / 8) * 2;
+    hipLaunchKernelGGL(swa_cache, dim3((unsigned)((citems + 255) / 256)), dim3(256), 0, stream,
+                       wk, wv, static_cast<_Float16*>(k_cache), static_cast<_Float16*>(v_cache),
+                       pos0, B, T, Hkv, R, n);
+    e = hipGetLastError();
+    profile_mark(stream);
+    return e;
+}
+
+}  // namespace gdn

@@ -204,3 +204,37 @@ def test_gate_out_errors(lib):
     assert _gate(lib, out=G_["o"], dt=0) == ALIAS       # in place only for fp32 out
     assert _gate(lib, out=G_["o"] + 16) == ALIAS
     assert _gate(lib, out=G_["w"] - 16) == ALIAS
+
+
+S_ = {n: BASE + (60 + i) * GB for i, n in enumerate(["q", "k", "v", "o", "kc", "vc", "ws"])}
+
+
+def _swa(lib, B=1, T=100, Hq=16, Hkv=2, d=128, W=64, base=10000.0, pos0=5, **over):
+    a = dict(S_)
+    a.update(over)
+    lib.gdn_swa_stream_chunk.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_longlong, ctypes.c_void_p] + \
+        [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    return lib.gdn_swa_stream_chunk(a["q"], a["k"], a["v"], a["kc"], a["vc"], pos0, a["o"], B, T,
+                                    Hq, Hkv, d, W, base, a["ws"], GB, None)
+
+
+def test_swa_errors(lib):
+    for name in ("q", "k", "v", "o"):
+        assert _swa(lib, **{name: None}) == NULL, name
+    assert _swa(lib, kc=None) == NULL                      # one cache without the other
+    for name in S_:
+        assert _swa(lib, **{name: S_[name] + 8}) == ALIGN, name
+    assert _swa(lib, Hq=6, Hkv=4) == SHAPE                 # Hq not a multiple of Hkv
+    assert _swa(lib, W=0) == SHAPE
+    assert _swa(lib, pos0=-1) == SHAPE
+    assert _swa(lib, base=1.0) == SHAPE
+    assert _swa(lib, d=64) == UNSUP
+    assert _swa(lib, o=S_["q"] + 1024) == ALIAS
+    assert _swa(lib, kc=S_["ws"]) == ALIAS
+    assert _swa(lib, vc=S_["kc"] + 16) == ALIAS
+    assert _swa(lib, ws=None) == WS
+    lib.gdn_swa_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_swa_cache_bytes.restype = ctypes.c_size_t
+    assert lib.gdn_swa_workspace_bytes(1, 8192, 16, 2, 128) == 8192 * 20 * 128 * 2
+    assert lib.gdn_swa_cache_bytes(1, 2, 128, 8192) == 2 * 8191 * 128 * 2
+    assert lib.gdn_swa_cache_bytes(1, 2, 128, 1) == 0
