@@ -12,6 +12,9 @@ A step is one whole-path call over one batch of synthetic inputs already in HBM:
   * long_prefill: gdn_prefill over 262144 tokens (tokens/s, beside);
   * layer: the layer around the recurrence at the prefill shapes, conv_qkv ->
     prefill -> gate_out (bf16 output), tokens/s with each kernel's HBM rate;
+  * swa: sliding-window attention prefill over 8192 tokens (16 query / 2 kv
+    heads, W = 8192) with the attention kernel's matrix-core rate, and 272-token
+    stream calls against a full window;
   * stream: gdn_stream_chunk calls of 272 tokens (256 visual + 16 text) carrying
     the state in place; the first 200 frames of the stream are staged and replayed
     in order (calls/s = frames/s, beside).
@@ -80,6 +83,7 @@ def parse():
     p.add_argument("--long-reps", type=int, default=3)
     p.add_argument("--no-stream", action="store_true")
     p.add_argument("--no-layer", action="store_true")
+    p.add_argument("--no-swa", action="store_true")
     p.add_argument("--cold-reps", type=int, default=20)
     p.add_argument("--no-b512", action="store_true")
     p.add_argument("--b512-steps", type=int, default=100)
@@ -506,6 +510,77 @@ def time_layer(gdn, args, dev):
             "value": B * T / (ms / 1e3), "unit": "tokens/s", "ms_per_call": ms, "kernels": res}
 
 
+def swa_flops(T, Hq, d, window, pos0=0, hist=0):
+    """Matrix flops of sliding-window attention: 4 d per (query, key) pair in
+    the window (2 d for q.k, 2 d for p v)."""
+    t = np.arange(T, dtype=np.float64)
+    keys = np.minimum(t + 1 + min(hist, pos0), window)
+    return float(keys.sum()) * Hq * 4 * d
+
+
+def time_swa(gdn, args, dev):
+    """swa8k: sliding-window attention prefill, B=1, T=8192, 16 query / 2 kv
+    heads, d=128, W=8192; and steady-state stream calls of 272 tokens with a
+    full window in the ring cache."""
+    import torch
+    import gdn_inputs
+    B, T, Hq, Hkv, d, W = 1, 8192, 16, 2, 128, 8192
+    x = gdn_inputs.swa_inputs(B, T, Hq, Hkv, d, seed=8192)
+    q, k, v = (stage_bf16(x[n], dev) for n in ("q", "k", "v"))
+    o = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.swa_workspace_bytes(B, T, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+    call = lambda: gdn.swa_prefill(q, k, v, W, o=o, workspace=ws)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        call()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(e) / args.steps
+    kms = kernel_times(gdn, call, args.steps)
+    fl = swa_flops(T, Hq, d, W)
+    tfs = fl / (kms[1] / 1e3) / 1e12
+    out = {"workload": "swa8k: sliding-window attention prefill, B=1, T=8192, 16 query / 2 kv "
+                       "heads, d=128, W=8192, bf16 in, fp32 out",
+           "value": B * T / (ms / 1e3), "unit": "tokens/s", "ms_per_call": ms,
+           "kernels": [{"kernel": "rotary prep (swa_prep)", "us": kms[0] * 1e3},
+                       {"kernel": "attention (swa_attn)", "us": kms[1] * 1e3}],
+           "roofline": {"kernel": "attention (swa_attn)", "bound": "mfma", "achieved": tfs,
+                        "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+                        "frac": tfs / MFMA_F16_PEAK_TFS, "flops_per_launch": fl}}
+    # stream: 272-token calls after 8192 + 272 tokens of history (full window)
+    ct = 272
+    kc, vc = gdn.swa_new_cache(B, Hkv, d, W, dev)
+    wss = torch.empty(gdn.swa_workspace_bytes(B, ct, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+    os_ = torch.empty((B, ct, Hq, d), dtype=torch.float32, device=dev)
+    pieces = [tuple(t[:, i * ct:(i + 1) * ct].contiguous() for t in (q, k, v))
+              for i in range(T // ct)]
+    pos = 0
+    for i in range(len(pieces)):  # fill the ring (positions 0 .. 8159)
+        gdn.swa_stream_chunk(*pieces[i], kc, vc, pos, W, o=os_, workspace=wss)
+        pos += ct
+    torch.cuda.synchronize()
+    n = 200
+    a.record(stream)
+    for i in range(n):
+        gdn.swa_stream_chunk(*pieces[i % len(pieces)], kc, vc, pos + i * ct, W, o=os_, workspace=wss)
+    e.record(stream)
+    torch.cuda.synchronize()
+    sms = a.elapsed_time(e) / n
+    sfl = swa_flops(ct, Hq, d, W, pos0=pos, hist=W - 1)
+    out["stream"] = {"workload": "swa stream: calls of 272 tokens at positions >= 8160 (full "
+                                 "8192-token window from the ring cache), 16/2 heads, d=128",
+                     "value": 1e3 / sms, "unit": "calls/s", "us_per_call": sms * 1e3,
+                     "tokens_per_s": ct * 1e3 / sms,
+                     "tflops": sfl / (sms / 1e3) / 1e12}
+    return out
+
+
 def cpu_baseline(d, seconds):
     """Time the fp64 oracle on the host over (repeats of) the prefill workload."""
     import gdn_inputs
@@ -622,6 +697,8 @@ def main():
             line["decode512"] = time_decode_b512(gdn, args, dev)
     if not args.no_layer:
         line["layer"] = time_layer(gdn, args, dev)
+    if not args.no_swa:
+        line["swa"] = time_swa(gdn, args, dev)
     if not args.no_long:
         line["long_prefill"] = time_long_prefill(gdn, args, dev)
     if not args.no_stream:

@@ -140,7 +140,7 @@ struct AttnArgs {
     const _Float16* vc;
     float* o;            // [B][T][Hq][d]
     long long pos0;
-    int T, Hq, Hkv, W, R, hist, nqb;
+    int T, Hq, Hkv, W, R, hist, nqb, pmod;
 };
 
 // max / sum over the 4 lanes c, c+16, c+32, c+48 (one query of an S^T tile)
@@ -163,6 +163,7 @@ __device__ __forceinline__ unsigned pack_h2(_Float16 a, _Float16 b) {
     return __builtin_bit_cast(unsigned, p);
 }
 
+template <bool RING>
 __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
     __shared__ __attribute__((aligned(16))) _Float16 sK[2][KB * KLD];
     __shared__ __attribute__((aligned(16))) _Float16 sV[2][SD * VLD];
@@ -184,43 +185,51 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
 
     const _Float16* kbase = a.k + ((b * a.Hkv + hk) * (long)T) * SD;
     const _Float16* vbase = a.v + ((b * a.Hkv + hk) * (long)T) * SD;
-    const _Float16* kcb = a.kc ? a.kc + ((b * a.Hkv + hk) * (long)a.R) * SD : nullptr;
-    const _Float16* vcb = a.vc ? a.vc + ((b * a.Hkv + hk) * (long)a.R) * SD : nullptr;
+    const _Float16* kcb = RING ? a.kc + ((b * a.Hkv + hk) * (long)a.R) * SD : nullptr;
+    const _Float16* vcb = RING ? a.vc + ((b * a.Hkv + hk) * (long)a.R) * SD : nullptr;
 
-    auto row_ptr = [&](const _Float16* base, const _Float16* ring, int j) -> const _Float16* {
-        if (j >= 0) return base + (long)j * SD;
-        const long pos = a.pos0 + j;
-        return ring + (pos % a.R) * SD;
+    // row j of K or V (ring slot (pos0 + j) mod R for j < 0; pmod = pos0 mod R)
+    auto row = [&](const _Float16* base, const _Float16* ring, int j) -> const _Float16* {
+        if (RING && j < 0) {
+            int slot = a.pmod + j;
+            slot += slot < 0 ? a.R : 0;  // j >= -hist >= -R
+            return ring + (long)slot * SD;
+        }
+        return base + (long)j * SD;
     };
-    // staging: K rows 16 i + tid / 16 (i < 4), V row pairs 2 (tid / 16) + {0, 1} + 32 i (i < 2);
-    // chunk tid % 16 of 16 bytes.  Rows outside [jlo, jhi] are zero.
-    const int ch = tid % 16, rw = tid / 16;
+    // staging.  K: rows 16 i + tid / 16 (i < 4), chunk tid % 16 (16 bytes).
+    // V: key pair kp = tid % 32 (keys 2 kp, 2 kp + 1), chunks tid / 32 + 8 i
+    // (i < 2), so the transposed LDS writes of a wave fill 32 consecutive
+    // dwords of one row.  Rows beyond jhi are zero.
+    const int kch = tid % 16, krw = tid / 16;
+    const int kp = tid % 32, vch = tid / 32;
     uint4 pk[4], pv[4];
     auto load_block = [&](int j0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int j = j0 + 16 * i + rw;
-            pk[i] = (j <= jhi) ? *reinterpret_cast<const uint4*>(row_ptr(kbase, kcb, j) + ch * 8)
+            const int j = j0 + 16 * i + krw;
+            pk[i] = (j <= jhi) ? *reinterpret_cast<const uint4*>(row(kbase, kcb, j) + kch * 8)
                                : uint4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int j = j0 + 2 * rw + (i & 1) + 32 * (i >> 1);
-            pv[i] = (j <= jhi) ? *reinterpret_cast<const uint4*>(row_ptr(vbase, vcb, j) + ch * 8)
-                               : uint4{0, 0, 0, 0};
+            const int j = j0 + 2 * kp + (i & 1);
+            pv[i] = (j <= jhi)
+                        ? *reinterpret_cast<const uint4*>(row(vbase, vcb, j) + (vch + 8 * (i >> 1)) * 8)
+                        : uint4{0, 0, 0, 0};
         }
     };
     auto store_block = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4*>(&sK[buf][(16 * i + rw) * KLD + ch * 8]) = pk[i];
+            *reinterpret_cast<uint4*>(&sK[buf][(16 * i + krw) * KLD + kch * 8]) = pk[i];
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2) {
-            const int r0 = 2 * rw + 32 * i2;
             const H8 lo = __builtin_bit_cast(H8, pv[2 * i2]), hi = __builtin_bit_cast(H8, pv[2 * i2 + 1]);
+            const int d0 = (vch + 8 * i2) * 8;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<unsigned*>(&sV[buf][(ch * 8 + e) * VLD + r0]) = pack_h2(lo[e], hi[e]);
+                *reinterpret_cast<unsigned*>(&sV[buf][(d0 + e) * VLD + 2 * kp]) = pack_h2(lo[e], hi[e]);
         }
     };
 
@@ -250,13 +259,15 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
         // does any query of this wave see a key of this block?
         const bool live = qa < T && j0 <= qa + 31 && j0 + KB - 1 >= qa - W + 1;
         if (live) {
+            const _Float16* kt_base = &sK[buf][c * KLD + 8 * g];
             f32x4 st[4][2];
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                st[kt][0] = st[kt][1] = zero4();
+            for (int kt = 0; kt < 4; ++kt) st[kt][0] = st[kt][1] = zero4();
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const H8 ka = *reinterpret_cast<const H8*>(&sK[buf][(16 * kt + c) * KLD + 32 * s + 8 * g]);
+            for (int s = 0; s < 4; ++s) {
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    const H8 ka = *reinterpret_cast<const H8*>(kt_base + 16 * kt * KLD + 32 * s);
                     st[kt][0] = MF::k32(ka, qf[0][s], st[kt][0]);
                     st[kt][1] = MF::k32(ka, qf[1][s], st[kt][1]);
                 }
@@ -267,13 +278,13 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) {
                     const int t = qa + 16 * qt + c;
+                    const int lo_ok = t - W + 1, hi_ok = min(t, jhi);  // keys j in [lo_ok, hi_ok]
 #pragma unroll
                     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int j = j0 + 16 * kt + 4 * g + e;
-                            const bool ok = j <= t && t - j < W && j <= jhi;
-                            st[kt][qt][e] = ok ? st[kt][qt][e] : -INFINITY;
+                            st[kt][qt][e] = (j >= lo_ok && j <= hi_ok) ? st[kt][qt][e] : -INFINITY;
                         }
                 }
             }
@@ -286,6 +297,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) mx = fmaxf(mx, st[kt][qt][e]);
                 const float mn = fmaxf(m[qt], qmax(mx));
+                const bool grew = mn > m[qt];
                 const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);
                 m[qt] = mn;
                 float ps = 0.f;
@@ -298,14 +310,17 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
                         pb[qt][kt >> 1][4 * (kt & 1) + e] = static_cast<_Float16>(p);
                     }
                 l[qt] = l[qt] * alpha + ps;
+                if (__builtin_amdgcn_ballot_w64(grew)) {  // rescale only when a max moved
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt) acc[dt][qt] *= alpha;
+                    for (int dt = 0; dt < 8; ++dt) acc[dt][qt] *= alpha;
+                }
             }
+            const _Float16* vt_base = &sV[buf][c * VLD + 4 * g];
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
+            for (int j2 = 0; j2 < 2; ++j2) {
 #pragma unroll
-                for (int j2 = 0; j2 < 2; ++j2) {
-                    const _Float16* vp = &sV[buf][(16 * dt + c) * VLD + 32 * j2 + 4 * g];
+                for (int dt = 0; dt < 8; ++dt) {
+                    const _Float16* vp = vt_base + 16 * dt * VLD + 32 * j2;
                     const H4 v0 = *reinterpret_cast<const H4*>(vp);
                     const H4 v1 = *reinterpret_cast<const H4*>(vp + 16);
                     const H8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
@@ -397,8 +412,12 @@ hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache
     a.T = T, a.Hq = Hq, a.Hkv = Hkv, a.W = window, a.R = R > 0 ? R : 1;
     a.hist = ring ? (int)std::min<long long>(R, pos0) : 0;
     a.nqb = (T + QB - 1) / QB;
-    hipLaunchKernelGGL(swa_attn, dim3((unsigned)a.nqb, (unsigned)Hq, (unsigned)B), dim3(256), 0,
-                       stream, a);
+    a.pmod = (int)(pos0 % a.R);
+    const dim3 grid((unsigned)a.nqb, (unsigned)Hq, (unsigned)B);
+    if (ring)
+        hipLaunchKernelGGL(swa_attn<true>, grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(swa_attn<false>, grid, dim3(256), 0, stream, a);
     e = hipGetLastError();
     profile_mark(stream);
     if (e != hipSuccess || !ring) return e;
