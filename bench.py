@@ -528,7 +528,7 @@ def time_swa(gdn, args, dev):
     x = gdn_inputs.swa_inputs(B, T, Hq, Hkv, d, seed=8192)
     q, k, v = (stage_bf16(x[n], dev) for n in ("q", "k", "v"))
     o = torch.empty((B, T, Hq, d), dtype=torch.float32, device=dev)
-    ws = torch.empty(gdn.swa_workspace_bytes(B, T, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+    ws = torch.empty(gdn.swa_workspace_bytes(B, T, Hq, Hkv, d, W), dtype=torch.uint8, device=dev)
     call = lambda: gdn.swa_prefill(q, k, v, W, o=o, workspace=ws)
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
@@ -556,7 +556,7 @@ def time_swa(gdn, args, dev):
     # stream: 272-token calls after 8192 + 272 tokens of history (full window)
     ct = 272
     kc, vc = gdn.swa_new_cache(B, Hkv, d, W, dev)
-    wss = torch.empty(gdn.swa_workspace_bytes(B, ct, Hq, Hkv, d), dtype=torch.uint8, device=dev)
+    wss = torch.empty(gdn.swa_workspace_bytes(B, ct, Hq, Hkv, d, W), dtype=torch.uint8, device=dev)
     os_ = torch.empty((B, ct, Hq, d), dtype=torch.float32, device=dev)
     pieces = [tuple(t[:, i * ct:(i + 1) * ct].contiguous() for t in (q, k, v))
               for i in range(T // ct)]

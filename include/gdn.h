@@ -211,8 +211,13 @@ int gdn_gate_out(const float *o, const void *z, const float *w, void *out, int o
  * accumulation and softmax.
  */
 
-/* Workspace bytes of gdn_swa_prefill / gdn_swa_stream_chunk (0 for invalid sizes). */
-size_t gdn_swa_workspace_bytes(int B, int T, int Hq, int Hkv, int d);
+/*
+ * Workspace bytes of gdn_swa_prefill / gdn_swa_stream_chunk for these sizes and
+ * window (0 for invalid sizes): the fp16 rotated q, k, v and, when the call
+ * splits each query block's window over several workgroups (small grids, e.g.
+ * stream calls against a long window), their partial outputs.
+ */
+size_t gdn_swa_workspace_bytes(int B, int T, int Hq, int Hkv, int d, int window);
 
 /*
  * Bytes of EACH of the two ring caches (k_cache, v_cache) a stream of window W
@@ -262,8 +267,8 @@ int gdn_swa_stream_chunk(const void *q, const void *k, const void *v,
  *   fp32 prefill:                    chunk prep, [summary pass, combine,] chain
  *   decode:                          step
  *   conv_qkv, gate_out:              one kernel each
- *   swa prefill:                     rotary prep, attention
- *   swa stream chunk:                rotary prep, attention, cache update
+ *   swa prefill:                     rotary prep, attention [, combine]
+ *   swa stream chunk:                rotary prep, attention [, combine], cache update
  * Returns GDN_OK, or GDN_ERR_NULL for events == NULL with count > 0, or
  * GDN_ERR_SHAPE for count < 0.
  */

@@ -72,7 +72,7 @@ def _load():
     lib.gdn_gate_out.argtypes = [fp, vp, fp, vp, i, i, i, i, i, vp]
     ll = ctypes.c_longlong
     lib.gdn_swa_workspace_bytes.restype = sz
-    lib.gdn_swa_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.gdn_swa_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.gdn_swa_cache_bytes.restype = sz
     lib.gdn_swa_cache_bytes.argtypes = [i, i, i, i]
     lib.gdn_swa_prefill.restype = i
@@ -304,8 +304,8 @@ def gate_out(o, z, w, *, out=None, out_dtype=None, stream=None):
 ROPE_BASE = 10000.0
 
 
-def swa_workspace_bytes(B, T, Hq, Hkv, d=128) -> int:
-    return int(_lib.gdn_swa_workspace_bytes(B, T, Hq, Hkv, d))
+def swa_workspace_bytes(B, T, Hq, Hkv, d=128, window=8192) -> int:
+    return int(_lib.gdn_swa_workspace_bytes(B, T, Hq, Hkv, d, window))
 
 
 def swa_cache_bytes(B, Hkv, d, window) -> int:
@@ -346,7 +346,7 @@ def swa_stream_chunk(q, k, v, k_cache, v_cache, pos0, window, *, rope_base=ROPE_
         _check(v_cache, (B, Hkv, window - 1, d), torch.float16, "v_cache")
     if o is None:
         o = torch.empty((B, T, Hq, d), dtype=torch.float32, device=q.device)
-    need = swa_workspace_bytes(B, T, Hq, Hkv, d)
+    need = swa_workspace_bytes(B, T, Hq, Hkv, d, window)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     nbytes = workspace.numel() * workspace.element_size()
@@ -366,7 +366,7 @@ def swa_prefill(q, k, v, window, *, rope_base=ROPE_BASE, o=None, workspace=None,
     B, T, Hq, Hkv, d = _swa_check(q, k, v, o)
     if o is None:
         o = torch.empty((B, T, Hq, d), dtype=torch.float32, device=q.device)
-    need = swa_workspace_bytes(B, T, Hq, Hkv, d)
+    need = swa_workspace_bytes(B, T, Hq, Hkv, d, window)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     nbytes = workspace.numel() * workspace.element_size()

@@ -232,9 +232,9 @@ int gdn_gate_out(const float* o, const void* z, const float* w, void* out, int o
 }
 
 
-size_t gdn_swa_workspace_bytes(int B, int T, int Hq, int Hkv, int d) {
-    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d != 128) return 0;
-    return gdn::swa_workspace_bytes(B, T, Hq, Hkv, d);
+size_t gdn_swa_workspace_bytes(int B, int T, int Hq, int Hkv, int d, int window) {
+    if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || d != 128 || window < 1) return 0;
+    return gdn::swa_workspace_bytes(B, T, Hq, Hkv, d, window);
 }
 
 size_t gdn_swa_cache_bytes(int B, int Hkv, int d, int window) {
@@ -260,7 +260,7 @@ int gdn_swa_stream_chunk(const void* q, const void* k, const void* v, void* k_ca
     const void* ptrs[] = {q, k, v, o, k_cache, v_cache, workspace};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN_ERR_ALIGN;
-    const size_t need = gdn::swa_workspace_bytes(B, T, Hq, Hkv, d);
+    const size_t need = gdn::swa_workspace_bytes(B, T, Hq, Hkv, d, window);
     if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
     const size_t tq = (size_t)B * T * Hq * d, tkv = (size_t)B * T * Hkv * d;
     const size_t cb = gdn_swa_cache_bytes(B, Hkv, d, window);

@@ -53,7 +53,7 @@ hipError_t launch_gate_out(const float* o, const void* z, const float* w, void* 
 // Sliding-window attention (d = 128): rotary prep into the workspace, then
 // attention over the window (keys before pos0 from the ring cache when given),
 // then the ring update.
-size_t swa_workspace_bytes(int B, int T, int Hq, int Hkv, int D);
+size_t swa_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int window);
 hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
                       long long pos0, float* o, int B, int T, int Hq, int Hkv, int D, int window,
                       float rope_base, void* ws, hipStream_t stream);

@@ -139,8 +139,9 @@ struct AttnArgs {
     const _Float16* kc;  // ring [B][Hkv][R][d] (positions < pos0), or null
     const _Float16* vc;
     float* o;            // [B][T][Hq][d]
+    float* part;         // ns > 1: partial O [B][Hq][nqb][ns][QB][d], then (m, l) [..][QB][2]
     long long pos0;
-    int T, Hq, Hkv, W, R, hist, nqb, pmod;
+    int T, Hq, Hkv, W, R, hist, nqb, pmod, ns;
 };
 
 // max / sum over the 4 lanes c, c+16, c+32, c+48 (one query of an S^T tile)
@@ -170,7 +171,8 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
 
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
     const int g = lane / 16, c = lane % 16;
-    const int qb = a.nqb - 1 - (int)blockIdx.x;  // longest windows first
+    const int qb = a.nqb - 1 - (int)blockIdx.x / a.ns;  // longest windows first
+    const int split = (int)blockIdx.x % a.ns;
     const int h = blockIdx.y;
     const long b = blockIdx.z;
     const int hk = h / (a.Hq / a.Hkv);
@@ -179,9 +181,14 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
 
     // key index j: j >= 0 is token j of this call, j < 0 is the ring entry of
     // absolute position pos0 + j (available for j >= -hist)
-    const int jlo = max(t0 - W + 1, -a.hist);
+    const int jlo_all = max(t0 - W + 1, -a.hist);
     const int jhi = min(t0 + QB - 1, T - 1);
-    const int nblk = (jhi - jlo) / KB + 1;
+    const int nblk_all = (jhi - jlo_all) / KB + 1;
+    // this split's share of the key blocks (may be empty)
+    const int b_lo = (int)((long)nblk_all * split / a.ns);
+    const int b_hi = (int)((long)nblk_all * (split + 1) / a.ns);
+    const int nblk = b_hi - b_lo;
+    const int jlo = jlo_all + b_lo * KB;
 
     const _Float16* kbase = a.k + ((b * a.Hkv + hk) * (long)T) * SD;
     const _Float16* vbase = a.v + ((b * a.Hkv + hk) * (long)T) * SD;
@@ -248,8 +255,10 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
     for (int dt = 0; dt < 8; ++dt) acc[dt][0] = acc[dt][1] = zero4();
     float m[2] = {kNegBig, kNegBig}, l[2] = {0.f, 0.f};
 
-    load_block(jlo);
-    store_block(0);
+    if (nblk > 0) {
+        load_block(jlo);
+        store_block(0);
+    }
     __syncthreads();
 
     for (int bi = 0; bi < nblk; ++bi) {
@@ -333,20 +342,77 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
         __syncthreads();
     }
 
-    // o[t][16 dt + 4 g + e] = acc / l
+    if (a.ns == 1) {
+        // o[t][16 dt + 4 g + e] = acc / l
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-        const int t = qa + 16 * qt + c;
-        const float inv = 1.0f / qsum(l[qt]);
-        if (t < T) {
-            float* op = a.o + ((b * T + t) * a.Hq + h) * (long)SD + 4 * g;
+        for (int qt = 0; qt < 2; ++qt) {
+            const int t = qa + 16 * qt + c;
+            const float inv = 1.0f / qsum(l[qt]);
+            if (t < T) {
+                float* op = a.o + ((b * T + t) * a.Hq + h) * (long)SD + 4 * g;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const f32x4 r = acc[dt][qt] * inv;
-                *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(r[0], r[1], r[2], r[3]);
+                for (int dt = 0; dt < 8; ++dt) {
+                    const f32x4 r = acc[dt][qt] * inv;
+                    *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(r[0], r[1], r[2], r[3]);
+                }
+            }
+        }
+    } else {
+        // unnormalised partial of this split, merged by swa_combine
+        const long item = ((b * a.Hq + h) * a.nqb + qb) * a.ns + split;
+        const long nitems = (long)gridDim.z * a.Hq * a.nqb * a.ns;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            const int qi = 32 * wave + 16 * qt + c;
+            const float lt = qsum(l[qt]);
+            float* op = a.part + (item * QB + qi) * (long)SD + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+                *reinterpret_cast<float4*>(op + 16 * dt) =
+                    make_float4(acc[dt][qt][0], acc[dt][qt][1], acc[dt][qt][2], acc[dt][qt][3]);
+            if (g == 0) {
+                float* ml = a.part + nitems * QB * SD + (item * QB + qi) * 2;
+                *reinterpret_cast<float2*>(ml) = make_float2(m[qt], lt);
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// swa_combine: merge the ns partials of each query (base-2 log-sum-exp):
+//   M = max m_s,  o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// One thread per 4 features of one (b, t, head).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void swa_combine(const float* part, float* o, int B, int T,
+                                                   int Hq, int nqb, int ns) {
+    const long item = (long)blockIdx.x * 256 + threadIdx.x;
+    constexpr int G = SD / 4;
+    const long total = (long)B * T * Hq * G;
+    if (item >= total) return;
+    const int part4 = (int)(item % G);
+    long rest = item / G;
+    const int h = (int)(rest % Hq);
+    rest /= Hq;
+    const int t = (int)(rest % T);
+    const long b = rest / T;
+    const int qb = t / QB, qi = t % QB;
+    const long nitems = (long)B * Hq * nqb * ns;
+    const long base = ((b * Hq + h) * nqb + qb) * ns;
+    const float* ml = part + nitems * QB * SD;
+    float M = kNegBig;
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, ml[((base + sp) * QB + qi) * 2]);
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < ns; ++sp) {
+        const float2 x = *reinterpret_cast<const float2*>(ml + ((base + sp) * QB + qi) * 2);
+        const float w = __builtin_amdgcn_exp2f(x.x - M);
+        L += w * x.y;
+        const float4 p = *reinterpret_cast<const float4*>(part + ((base + sp) * QB + qi) * (long)SD + 4 * part4);
+        acc.x += w * p.x, acc.y += w * p.y, acc.z += w * p.z, acc.w += w * p.w;
+    }
+    const float inv = 1.0f / L;
+    *reinterpret_cast<float4*>(o + ((b * T + t) * Hq + h) * (long)SD + 4 * part4) =
+        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -373,8 +439,31 @@ __global__ __launch_bounds__(256) void swa_cache(const _Float16* wk, const _Floa
 
 }  // namespace
 
-size_t swa_workspace_bytes(int B, int T, int Hq, int Hkv, int D) {
-    return (size_t)B * T * (Hq + 2 * (size_t)Hkv) * D * sizeof(_Float16);
+// Key-range splits per query block: one while the (query block, head, batch)
+// grid already fills the chip twice, else enough to reach that, each split
+// keeping at least 4 key blocks (at most 32 splits).
+int swa_splits(int B, int T, int Hq, int window, long long pos0, bool ring) {
+    const long base = (long)((T + QB - 1) / QB) * Hq * B;
+    if (base >= 512) return 1;
+    const long hist = ring ? std::min<long long>(window - 1, pos0) : 0;
+    const long keys = std::min<long>((long)window + QB, (long)T + hist + QB);
+    const long maxblk = keys / KB + 1;
+    long ns = (512 + base - 1) / base;
+    ns = std::min<long>(ns, std::max<long>(1, maxblk / 4));
+    return (int)std::max<long>(1, std::min<long>(ns, 32));
+}
+
+static size_t swa_part_bytes(int B, int T, int Hq, int ns) {
+    if (ns <= 1) return 0;
+    const size_t items = (size_t)B * Hq * ((T + QB - 1) / QB) * ns;
+    return items * QB * (SD + 2) * sizeof(float);
+}
+
+size_t swa_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int window) {
+    // the largest split count any call of these sizes can use (full history)
+    const int ns = swa_splits(B, T, Hq, window, (long long)window, true);
+    return (size_t)B * T * (Hq + 2 * (size_t)Hkv) * D * sizeof(_Float16) +
+           swa_part_bytes(B, T, Hq, ns);
 }
 
 hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
@@ -413,14 +502,25 @@ hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache
     a.hist = ring ? (int)std::min<long long>(R, pos0) : 0;
     a.nqb = (T + QB - 1) / QB;
     a.pmod = (int)(pos0 % a.R);
-    const dim3 grid((unsigned)a.nqb, (unsigned)Hq, (unsigned)B);
+    a.ns = swa_splits(B, T, Hq, window, pos0, ring);
+    a.part = reinterpret_cast<float*>(wv + (size_t)B * Hkv * T * SD);
+    const dim3 grid((unsigned)(a.nqb * a.ns), (unsigned)Hq, (unsigned)B);
     if (ring)
         hipLaunchKernelGGL(swa_attn<true>, grid, dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL(swa_attn<false>, grid, dim3(256), 0, stream, a);
     e = hipGetLastError();
     profile_mark(stream);
-    if (e != hipSuccess || !ring) return e;
+    if (e != hipSuccess) return e;
+    if (a.ns > 1) {
+        const long items = (long)B * T * Hq * (SD / 4);
+        hipLaunchKernelGGL(swa_combine, dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
+                           stream, a.part, o, B, T, Hq, a.nqb, a.ns);
+        e = hipGetLastError();
+        profile_mark(stream);
+        if (e != hipSuccess) return e;
+    }
+    if (!ring) return e;
 
     const int n = std::min(T, R);
     const long citems = (long)B * Hkv * n * (SD / 8) * 2;

@@ -235,6 +235,8 @@ def test_swa_errors(lib):
     assert _swa(lib, ws=None) == WS
     lib.gdn_swa_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_swa_cache_bytes.restype = ctypes.c_size_t
-    assert lib.gdn_swa_workspace_bytes(1, 8192, 16, 2, 128) == 8192 * 20 * 128 * 2
+    assert lib.gdn_swa_workspace_bytes(1, 8192, 16, 2, 128, 8192) == 8192 * 20 * 128 * 2
+    # a 272-token call against an 8K window splits its key range: partials added
+    assert lib.gdn_swa_workspace_bytes(1, 272, 16, 2, 128, 8192) > 272 * 20 * 128 * 2
     assert lib.gdn_swa_cache_bytes(1, 2, 128, 8192) == 2 * 8191 * 128 * 2
     assert lib.gdn_swa_cache_bytes(1, 2, 128, 1) == 0

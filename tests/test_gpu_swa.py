@@ -52,6 +52,7 @@ def _oracle_range(x, window, t1, t2):
     (2, 200, 4, 4, 64),     # MHA, window of one key block
     (1, 130, 2, 1, 1),      # each query sees only itself
     (1, 257, 16, 2, 17),    # GQA 8:1, odd window
+    (1, 600, 2, 1, 1000),   # small grid: each query block's window split over workgroups
 ])
 def test_swa_prefill_matches_oracle(env, B, T, Hq, Hkv, W):
     gdn, dev = env
@@ -126,4 +127,32 @@ def test_swa_long_window_sampled(env):
                             W, t1, t2)
         e = rel_err(o[:, t1:t2, 5:6], ref)
         _note("swa long [%d, %d) head 5 rel err %.3e" % (t1, t2, e))
+        assert e <= TOL["bf16"]
+
+
+def test_swa_stream_calls_against_full_window(env):
+    """Stream calls of 272, 1 and 5 tokens after 8192 tokens of history (16/2
+    heads, W=8192): small grids whose 8K windows are split over many
+    workgroups and merged; sampled heads against the oracle."""
+    gdn, dev = env
+    import torch
+    _note("case swa stream calls after 8192 tokens of history")
+    B, Hq, Hkv, d, W = 1, 16, 2, 128, 8192
+    cuts = [0, 8192, 8192 + 272, 8192 + 273, 8192 + 278]
+    T = cuts[-1]
+    x = gdn_inputs.swa_inputs(B, T, Hq, Hkv, d, seed=4242)
+    t = _stage(x, dev)
+    kc, vc = gdn.swa_new_cache(B, Hkv, d, W, dev)
+    outs = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        piece = {n: t[n][:, a:b].contiguous() for n in ("q", "k", "v")}
+        outs.append(gdn.swa_stream_chunk(piece["q"], piece["k"], piece["v"], kc, vc, a, W))
+    o = torch.cat(outs, dim=1).cpu().numpy()
+    for h in (5, 13):
+        hk = h // 8
+        sub = {"q": x["q"][:, :, h:h + 1], "k": x["k"][:, :, hk:hk + 1], "v": x["v"][:, :, hk:hk + 1]}
+        t1 = 8192 - 64
+        ref = _oracle_range(sub, W, t1, T)
+        e = rel_err(o[:, t1:, h:h + 1], ref)
+        _note("swa split calls head %d rel err %.3e" % (h, e))
         assert e <= TOL["bf16"]
