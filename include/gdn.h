@@ -190,6 +190,30 @@ int gdn_gate_out(const float *o, const void *z, const float *w, void *out, int o
                  int B, int T, int H, int d, void *stream);
 
 /*
+ * gdn_backward -- gradients of the mixer for training (the pages train the
+ * Gated DeltaNet layers in three stages, explainer "Methodology"; they write no
+ * backward, so it is the exact gradient of the recurrence above).  For the loss
+ *     L = sum_t <d_o[t], o[t]> + <d_state_out, state_T>
+ * of a gdn_prefill from state_in, it writes dL/dq, dL/dk, dL/dv (fp32, the
+ * layouts of q, k, v), dL/dg and dL/dbeta ([B][T][H] fp32) and, when
+ * d_state_in is not NULL, dL/dstate_in ([B][H][d_k][d_v] fp32).
+ *
+ * q, k, v, g, beta, state_in (or NULL = zeros): the forward's inputs.
+ * d_o [B][T][H][d_v] fp32; d_state_out [B][H][d_k][d_v] fp32 or NULL (zero).
+ * workspace: at least gdn_backward_workspace_bytes() bytes (it holds per-chunk
+ * factors, chunk start states and chunk end gradients; contents ignored).
+ * Arithmetic is fp32 throughout (bf16 inputs are widened exactly).  Sizes and
+ * conventions as gdn_prefill; no argument may overlap another.
+ */
+size_t gdn_backward_workspace_bytes(int B, int T, int H, int dk, int dv);
+int gdn_backward(const void *q, const void *k, const void *v, int dtype,
+                 const float *g, const float *beta, const float *state_in,
+                 const float *d_o, const float *d_state_out,
+                 float *dq, float *dk, float *dv, float *dg, float *dbeta, float *d_state_in,
+                 int B, int T, int H, int dk_, int dv_,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Sliding-window attention (SWA): the other token mixer of InfiniteVL's hybrid
  * blocks (explainer page "InfiniteVL: Synergizing Linear and Sparse Attention
  * ...", section "The Concept: Sliding Window Attention": attention restricted to
@@ -267,6 +291,7 @@ int gdn_swa_stream_chunk(const void *q, const void *k, const void *v,
  *   fp32 prefill:                    chunk prep, [summary pass, combine,] chain
  *   decode:                          step
  *   conv_qkv, gate_out:              one kernel each
+ *   backward:                        prep, forward chain, backward chain, gradients
  *   swa prefill:                     rotary prep, attention [, combine]
  *   swa stream chunk:                rotary prep, attention [, combine], cache update
  * Returns GDN_OK, or GDN_ERR_NULL for events == NULL with count > 0, or

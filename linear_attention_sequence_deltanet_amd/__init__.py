@@ -16,6 +16,7 @@ Entry points (same names as the C ABI):
     swa_prefill(q, k, v, window)                  -> o   (sliding-window attention)
     swa_stream_chunk(q, k, v, k_cache, v_cache, pos0, window) -> o
     swa_workspace_bytes(...), swa_cache_bytes(...)
+    backward(q, k, v, g, beta, state_in, d_o, d_state_out) -> dict of gradients
     set_profile_events(handles), profile_marks()   (kernel timing hook)
 
 Shapes: q, k [B, T, H, dk]; v [B, T, H, dv]; g (log-decay), beta [B, T, H];
@@ -32,7 +33,7 @@ import os
 
 __all__ = ["prefill", "stream_chunk", "decode_step", "prefill_workspace_bytes", "GdnError",
            "conv_qkv", "gate_out", "swa_prefill", "swa_stream_chunk", "swa_workspace_bytes",
-           "swa_cache_bytes", "swa_new_cache",
+           "swa_cache_bytes", "swa_new_cache", "backward", "backward_workspace_bytes",
            "library_path", "GDN_BF16", "GDN_F32", "set_profile_events", "profile_marks"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -70,6 +71,11 @@ def _load():
     lib.gdn_conv_qkv.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, vp, vp, vp, i, i, i, i, i, vp]
     lib.gdn_gate_out.restype = i
     lib.gdn_gate_out.argtypes = [fp, vp, fp, vp, i, i, i, i, i, vp]
+    lib.gdn_backward_workspace_bytes.restype = sz
+    lib.gdn_backward_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.gdn_backward.restype = i
+    lib.gdn_backward.argtypes = [vp, vp, vp, i, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
+                                 i, i, i, i, i, vp, sz, vp]
     ll = ctypes.c_longlong
     lib.gdn_swa_workspace_bytes.restype = sz
     lib.gdn_swa_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -375,3 +381,38 @@ def swa_prefill(q, k, v, window, *, rope_base=ROPE_BASE, o=None, workspace=None,
     if st != 0:
         raise GdnError(st, "gdn_swa_prefill")
     return o
+
+
+def backward_workspace_bytes(B, T, H, dk, dv) -> int:
+    return int(_lib.gdn_backward_workspace_bytes(B, T, H, dk, dv))
+
+
+def backward(q, k, v, g, beta, state_in, d_o, d_state_out=None, *, want_dstate=True,
+             workspace=None, stream=None):
+    """Gradients of L = <d_o, o> + <d_state_out, state_T> for a prefill from
+    state_in (None = zeros).  Returns dict dq, dk, dv (fp32, shaped like q, k,
+    v), dg, dbeta [B, T, H] and dstate [B, H, dk, dv] (None unless want_dstate)."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    _check_mixer(q, k, v, g, beta, ((state_in, "state_in"), (d_state_out, "d_state_out")), d_o,
+                 (B, T, H))
+    dev = q.device
+    out = {"dq": torch.empty((B, T, H, dk), dtype=torch.float32, device=dev),
+           "dk": torch.empty((B, T, H, dk), dtype=torch.float32, device=dev),
+           "dv": torch.empty((B, T, H, dv), dtype=torch.float32, device=dev),
+           "dg": torch.empty((B, T, H), dtype=torch.float32, device=dev),
+           "dbeta": torch.empty((B, T, H), dtype=torch.float32, device=dev),
+           "dstate": torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dstate else None}
+    need = backward_workspace_bytes(B, T, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = _lib.gdn_backward(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), _ptr(state_in),
+                           _ptr(d_o), _ptr(d_state_out), _ptr(out["dq"]), _ptr(out["dk"]),
+                           _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dstate"]),
+                           B, T, H, dk, dv, _ptr(workspace), nbytes, _stream(stream, dev))
+    if st != 0:
+        raise GdnError(st, "gdn_backward")
+    return out

@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_chunk.hip", "gdn_fused.hip", "gdn_layer.hip", "gdn_swa.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_decode.hip", "gdn_chunk.hip", "gdn_fused.hip", "gdn_layer.hip", "gdn_swa.hip", "gdn_backward.hip"]
 ARCH = "gfx950"
 
 

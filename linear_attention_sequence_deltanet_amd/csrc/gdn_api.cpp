@@ -288,4 +288,49 @@ int gdn_swa_prefill(const void* q, const void* k, const void* v, float* o, int B
                                 rope_base, workspace, workspace_bytes, stream);
 }
 
+
+size_t gdn_backward_workspace_bytes(int B, int T, int H, int dk, int dv) {
+    if (check_sizes(B, T, H, dk, dv, GDN_F32) != GDN_OK) return 0;
+    return gdn::backward_workspace_bytes(B, T, H, dk);
+}
+
+int gdn_backward(const void* q, const void* k, const void* v, int dtype, const float* g,
+                 const float* beta, const float* state_in, const float* d_o,
+                 const float* d_state_out, float* dq, float* dk, float* dv, float* dg,
+                 float* dbeta, float* d_state_in, int B, int T, int H, int dk_, int dv_,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    int s = check_sizes(B, T, H, dk_, dv_, dtype);
+    if (s != GDN_OK) return s;
+    if (B > 65535 || H > 65535) return GDN_ERR_UNSUPPORTED;  // grid (chunks, H, B)
+    if (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta)
+        return GDN_ERR_NULL;
+    const void* ptrs[] = {q, k, v, g, beta, state_in, d_o, d_state_out, dq, dk, dv, dg, dbeta,
+                          d_state_in, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return GDN_ERR_ALIGN;
+    const size_t need = gdn::backward_workspace_bytes(B, T, H, dk_);
+    if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+    const size_t el = dtype == GDN_BF16 ? 2 : 4;
+    const size_t tok = (size_t)B * T * H, sb = (size_t)B * H * dk_ * dv_ * 4;
+    const Range ins[] = {span(q, tok * dk_ * el), span(k, tok * dk_ * el), span(v, tok * dv_ * el),
+                         span(g, tok * 4), span(beta, tok * 4),
+                         state_in ? span(state_in, sb) : Range{0, 0}, span(d_o, tok * dv_ * 4),
+                         d_state_out ? span(d_state_out, sb) : Range{0, 0}};
+    const Range outs[] = {span(dq, tok * dk_ * 4), span(dk, tok * dk_ * 4), span(dv, tok * dv_ * 4),
+                          span(dg, tok * 4), span(dbeta, tok * 4),
+                          d_state_in ? span(d_state_in, sb) : Range{0, 0},
+                          span(workspace, need)};
+    for (int i = 0; i < 7; ++i) {
+        for (const Range& in : ins)
+            if (overlap(outs[i], in)) return GDN_ERR_ALIAS;
+        for (int j = i + 1; j < 7; ++j)
+            if (overlap(outs[i], outs[j])) return GDN_ERR_ALIAS;
+    }
+    gdn::profile_begin(static_cast<hipStream_t>(stream));
+    return launch_status(gdn::launch_backward(q, k, v, dtype == GDN_BF16, g, beta, state_in, d_o,
+                                              d_state_out, dq, dk, dv, dg, dbeta, d_state_in, B,
+                                              T, H, dk_, workspace,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

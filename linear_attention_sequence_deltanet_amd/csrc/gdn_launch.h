@@ -58,4 +58,13 @@ hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache
                       long long pos0, float* o, int B, int T, int Hq, int Hkv, int D, int window,
                       float rope_base, void* ws, hipStream_t stream);
 
+// Backward of the gated delta rule (fp32): prep, forward chain, backward chain,
+// per-chunk gradients, using a workspace of backward_workspace_bytes().
+size_t backward_workspace_bytes(int B, int T, int H, int D);
+hipError_t launch_backward(const void* q, const void* k, const void* v, int dtype_bf16,
+                           const float* g, const float* beta, const float* state0,
+                           const float* d_o, const float* d_state, float* dq, float* dk, float* dv,
+                           float* dg, float* dbeta, float* dstate0, int B, int T, int H, int D,
+                           void* ws, hipStream_t stream);
+
 }  // namespace gdn

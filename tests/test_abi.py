@@ -240,3 +240,35 @@ def test_swa_errors(lib):
     assert lib.gdn_swa_workspace_bytes(1, 272, 16, 2, 128, 8192) > 272 * 20 * 128 * 2
     assert lib.gdn_swa_cache_bytes(1, 2, 128, 8192) == 2 * 8191 * 128 * 2
     assert lib.gdn_swa_cache_bytes(1, 2, 128, 1) == 0
+
+
+BW = {n: BASE + (80 + i) * GB for i, n in enumerate(
+    ["q", "k", "v", "g", "beta", "sin", "do", "dsout", "dq", "dk", "dv", "dg", "db", "dsin", "ws"])}
+
+
+def _bwd(lib, B=1, T=100, H=2, d=128, dtype=0, **over):
+    a = dict(BW)
+    a.update(over)
+    lib.gdn_backward.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] + [ctypes.c_void_p] * 11 + \
+        [ctypes.c_int] * 5 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    return lib.gdn_backward(a["q"], a["k"], a["v"], dtype, a["g"], a["beta"], a["sin"], a["do"],
+                            a["dsout"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dsin"],
+                            B, T, H, d, d, a["ws"], GB, None)
+
+
+def test_backward_errors(lib):
+    for name in ("q", "k", "v", "g", "beta", "do", "dq", "dk", "dv", "dg", "db"):
+        assert _bwd(lib, **{name: None}) == NULL, name
+    assert _bwd(lib, sin=None, dsout=None, dsin=None) != NULL  # optional ones
+    for name in BW:
+        assert _bwd(lib, **{name: BW[name] + 4}) == ALIGN, name
+    assert _bwd(lib, dtype=3) == DTYPE
+    assert _bwd(lib, T=0) == SHAPE
+    assert _bwd(lib, d=32) == UNSUP
+    assert _bwd(lib, dq=BW["q"] + 64) == ALIAS
+    assert _bwd(lib, dk=BW["dq"] + 16) == ALIAS
+    assert _bwd(lib, ws=BW["dg"]) == ALIAS
+    assert _bwd(lib, ws=None) == WS
+    lib.gdn_backward_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.gdn_backward_workspace_bytes(1, 8192, 16, 128, 128) > 0
+    assert lib.gdn_backward_workspace_bytes(1, 8192, 16, 96, 96) == 0
