@@ -15,6 +15,8 @@ A step is one whole-path call over one batch of synthetic inputs already in HBM:
   * swa: sliding-window attention prefill over 8192 tokens (16 query / 2 kv
     heads, W = 8192) with the attention kernel's matrix-core rate, and 272-token
     stream calls against a full window;
+  * backward: gradients of the prefill8k call (gdn_backward), tokens/s and the
+    fp32 arithmetic rate of the chunked form;
   * stream: gdn_stream_chunk calls of 272 tokens (256 visual + 16 text) carrying
     the state in place; the first 200 frames of the stream are staged and replayed
     in order (calls/s = frames/s, beside).
@@ -84,6 +86,7 @@ def parse():
     p.add_argument("--no-stream", action="store_true")
     p.add_argument("--no-layer", action="store_true")
     p.add_argument("--no-swa", action="store_true")
+    p.add_argument("--no-backward", action="store_true")
     p.add_argument("--cold-reps", type=int, default=20)
     p.add_argument("--no-b512", action="store_true")
     p.add_argument("--b512-steps", type=int, default=100)
@@ -581,6 +584,58 @@ def time_swa(gdn, args, dev):
     return out
 
 
+# Backward, per chunk x head (C = 64, d = 128): matrix products of the chunked
+# form: 9 of C x d x d (W H0, K^T Delta, K G, Q^T dO, K^T dR, dO H0^T, Delta G^T,
+# dR H0^T, and the C x d x d share of the prep is none) and 11 of C x C x d
+# (K K^T, Q K^T, Ti K, Ti V, P^T dO, Ti^T dDelta, dR Delta^T, dO Delta^T, dPL K,
+# dPL^T Q, dAs K), 2 flops each.
+BWD_FLOPS_PER_CHUNK_HEAD = 2 * (9 * 64 * 128 * 128 + 11 * 64 * 64 * 128)
+FP32_VALU_PEAK_TFS = 157.3
+
+
+def time_backward(gdn, args, dev):
+    """bwd8k: gradients of the prefill8k call (B=1, H=16, T=8192, d=128, bf16)
+    for random upstream gradients of o and of the final state."""
+    import torch
+    import gdn_inputs
+    d = gdn_inputs.sequence_inputs("prefill8k")
+    B, T, H, dk = d["q"].shape
+    q, k, v = (stage_bf16(d[x], dev) for x in ("q", "k", "v"))
+    g = torch.from_numpy(d["g"]).to(dev)
+    beta = torch.from_numpy(d["beta"]).to(dev)
+    gen = torch.Generator(device="cpu").manual_seed(8192)
+    d_o = torch.randn((B, T, H, dk), generator=gen).to(dev)
+    d_s = torch.randn((B, H, dk, dk), generator=gen).to(dev)
+    ws = torch.empty(gdn.backward_workspace_bytes(B, T, H, dk, dk), dtype=torch.uint8, device=dev)
+    call = lambda: gdn.backward(q, k, v, g, beta, None, d_o, d_s, workspace=ws)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    n = max(3, args.steps // 5)
+    a = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        call()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(e) / n
+    kms = kernel_times(gdn, call, n, nmax=6)
+    names = ["prep (bwd_prep)", "forward chain (bwd_fwd_chain)", "reverse chain (bwd_bwd_chain)",
+             "gradients (bwd_grads)"]
+    nch = B * H * ((T + 63) // 64)
+    fl = BWD_FLOPS_PER_CHUNK_HEAD * nch
+    tfs = fl / (ms / 1e3) / 1e12
+    return {"workload": "bwd8k: gradients of the prefill8k call (B=1, H=16, T=8192, d=128, bf16 "
+                        "q/k/v), fp32 arithmetic",
+            "value": B * T / (ms / 1e3), "unit": "tokens/s", "ms_per_call": ms,
+            "kernels": [{"kernel": nm, "us": t * 1e3} for nm, t in zip(names, kms)],
+            "roofline": {"kernel": "whole backward call", "bound": "alu", "achieved": tfs,
+                         "peak": FP32_VALU_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": tfs / FP32_VALU_PEAK_TFS, "flops_per_call": fl}}
+
+
 def cpu_baseline(d, seconds):
     """Time the fp64 oracle on the host over (repeats of) the prefill workload."""
     import gdn_inputs
@@ -699,6 +754,8 @@ def main():
         line["layer"] = time_layer(gdn, args, dev)
     if not args.no_swa:
         line["swa"] = time_swa(gdn, args, dev)
+    if not args.no_backward:
+        line["backward"] = time_backward(gdn, args, dev)
     if not args.no_long:
         line["long_prefill"] = time_long_prefill(gdn, args, dev)
     if not args.no_stream:

@@ -32,9 +32,9 @@
 // Kernels (all fp32, operands staged in LDS):
 //   bwd_prep       per chunk, in parallel: gates, the Gram and decayed QK^T
 //                  tiles, Ti by forward substitution, W and U;
-//   bwd_fwd_chain  per (b, h, 16-column state slice), chunks in order: stores
+//   bwd_fwd_chain  per (b, h, 8-column state slice), chunks in order: stores
 //                  every chunk's start state and Delta;
-//   bwd_bwd_chain  per (b, h, 16-column slice), chunks in reverse: stores every
+//   bwd_bwd_chain  per (b, h, 8-column slice), chunks in reverse: stores every
 //                  chunk's end gradient G and dR, writes dS_0;
 //   bwd_grads      per chunk, in parallel: dq, dk, dv, dbeta, dg.
 #include "gdn_device.h"
@@ -79,20 +79,80 @@ __device__ __forceinline__ float ld(const void* p, long i) {
     return to_f32(static_cast<const In*>(p)[i]);
 }
 
-// Chunk rows [t0, t0 + BC) of an input [B][T][H][D] into LDS (zeros past T).
+// Chunk rows [t0, t0 + BC) of an input [B][T][H][D] (bf16 or fp32), 16 bytes
+// per load, held in registers as raw words until stored (zeros past T).
+template <typename In, int D>
+struct RowRegs {
+    static constexpr int VPL = 16 / sizeof(In);      // values per 16-byte load
+    static constexpr int PPR = D / VPL;              // loads per row
+    static constexpr int N = BC * PPR / 256;         // loads per thread
+    uint4 r[N];
+    __device__ __forceinline__ void load(const void* src, long b, int h, int t0, int T, int H) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int p = threadIdx.x + 256 * i, row = p / PPR, col = (p % PPR) * VPL, t = t0 + row;
+            r[i] = t < T ? *reinterpret_cast<const uint4*>(static_cast<const In*>(src) +
+                                                           ((b * T + t) * H + h) * (long)D + col)
+                         : uint4{0, 0, 0, 0};
+        }
+    }
+    // dst row stride LD (floats, a multiple of 4)
+    template <int LD>
+    __device__ __forceinline__ void store(float* dst) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int p = threadIdx.x + 256 * i, row = p / PPR, col = (p % PPR) * VPL;
+            float* d = dst + row * LD + col;
+            if constexpr (sizeof(In) == 4) {
+                *reinterpret_cast<float4*>(d) = __builtin_bit_cast(float4, r[i]);
+            } else {
+                const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+                *reinterpret_cast<float4*>(d) = make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                                                            __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u));
+                *reinterpret_cast<float4*>(d + 4) = make_float4(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xFFFF0000u),
+                                                                __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xFFFF0000u));
+            }
+        }
+    }
+};
+
 template <typename In, int D, int LD>
 __device__ __forceinline__ void load_rows(float* dst, const void* src, long b, int h, int t0,
                                           int T, int H) {
-    for (int idx = threadIdx.x; idx < BC * D; idx += 256) {
-        const int r = idx / D, c = idx % D, t = t0 + r;
-        dst[r * LD + c] = t < T ? ld<In>(src, ((b * T + t) * H + h) * (long)D + c) : 0.f;
-    }
+    RowRegs<In, D> rr;
+    rr.load(src, b, h, t0, T, H);
+    rr.template store<LD>(dst);
 }
+
+// A contiguous [rows][cols] fp32 block (cols a multiple of 4) into registers.
+template <int ROWS, int COLS>
+struct BlockRegs {
+    static constexpr int PPR = COLS / 4, TOT = ROWS * PPR;
+    static constexpr int N = (TOT + 255) / 256;
+    float4 r[N];
+    __device__ __forceinline__ void load(const float* src, int stride) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int p = threadIdx.x + 256 * i;
+            if (TOT % 256 == 0 || p < TOT)
+                r[i] = *reinterpret_cast<const float4*>(src + (p / PPR) * (long)stride + (p % PPR) * 4);
+        }
+    }
+    template <int LD>
+    __device__ __forceinline__ void store(float* dst) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int p = threadIdx.x + 256 * i;
+            if (TOT % 256 == 0 || p < TOT)
+                *reinterpret_cast<float4*>(dst + (p / PPR) * LD + (p % PPR) * 4) = r[i];
+        }
+    }
+};
 
 // ---------------------------------------------------------------------------
 template <typename In, int D>
 __global__ __launch_bounds__(256) void bwd_prep(const BwdArgs a) {
-    constexpr int LD = D + 1, LC = BC + 1;
+    constexpr int LD = D + 4, LC = BC + 1;
     __shared__ float sK[BC * LD], sX[BC * LD], sL[BC * LC], sTi[BC * LC];
     __shared__ float sgam[BC], sb[BC];
     const int tid = threadIdx.x, c = blockIdx.x, h = blockIdx.y;
@@ -191,118 +251,186 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Chains: one workgroup per (b, h, 8-column slice of the state), chunks in
+// sequence.  The next chunk's operands are loaded into registers (16-byte
+// loads) while the current chunk computes, then written to LDS.
+constexpr int SW = 8;  // state columns per slice
+
 template <typename In, int D>
 __global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
-    constexpr int LD = D + 1;
-    __shared__ float sW[BC * LD], sKe[BC * LD], sH[D * 17], sDl[BC * 17];
+    constexpr int LD = D + 4;
+    __shared__ __attribute__((aligned(16))) float sW[BC * LD], sK[BC * LD];
+    __shared__ __attribute__((aligned(16))) float sH[D * SW], sU[BC * SW], sDe[BC * SW];
+    __shared__ float se[BC], sgc;
     const int tid = threadIdx.x, sl = blockIdx.x, h = blockIdx.y;
     const long b = blockIdx.z, n = b * a.H + h;
-    const int tr = tid / 16, tc = tid % 16, col = sl * 16 + tc;
-    for (int r = tr; r < D; r += 16)
-        sH[r * 17 + tc] = a.state0 ? a.state0[(n * D + r) * D + col] : 0.f;
+    const int c0 = sl * SW;
+    for (int idx = tid; idx < D * SW; idx += 256) {
+        const int r = idx / SW, cc = idx % SW;
+        sH[idx] = a.state0 ? a.state0[(n * D + r) * D + c0 + cc] : 0.f;
+    }
+    BlockRegs<BC, D> rw;
+    RowRegs<In, D> rk;
+    float4 ru = make_float4(0.f, 0.f, 0.f, 0.f);
+    float re = 0.f;
+    auto fetch = [&](int c) {
+        const long nc = n * a.NC + c;
+        rw.load(a.w + nc * BC * D, D);
+        rk.load(a.k, b, h, c * BC, a.T, a.H);
+        if (tid < BC * SW / 4) ru = *reinterpret_cast<const float4*>(a.u + (nc * BC + tid / 2) * D + c0 + (tid % 2) * 4);
+        if (tid < BC) re = a.sc[nc * 3 * BC + BC + tid];
+    };
+    fetch(0);
     for (int c = 0; c < a.NC; ++c) {
         const long nc = n * a.NC + c;
-        const float* scp = a.sc + nc * 3 * BC;
         __syncthreads();
-        for (int r = tr; r < D; r += 16) a.hs[(nc * D + r) * D + col] = sH[r * 17 + tc];
-        const float* wp = a.w + nc * BC * D;
-        for (int idx = tid; idx < BC * D; idx += 256) {
-            const int r = idx / D, x = idx % D, t = c * BC + r;
-            sW[r * LD + x] = wp[idx];
-            sKe[r * LD + x] = t < a.T ? scp[BC + r] * ld<In>(a.k, ((b * a.T + t) * a.H + h) * (long)D + x) : 0.f;
+        rw.template store<LD>(sW);
+        rk.template store<LD>(sK);
+        if (tid < BC * SW / 4) *reinterpret_cast<float4*>(&sU[(tid / 2) * SW + (tid % 2) * 4]) = ru;
+        if (tid < BC) se[tid] = re;
+        if (tid == 0) sgc = a.sc[nc * 3 * BC + BC - 1];
+        for (int idx = tid; idx < D * SW; idx += 256)
+            a.hs[(nc * D + idx / SW) * D + c0 + idx % SW] = sH[idx];
+        __syncthreads();
+        if (c + 1 < a.NC) fetch(c + 1);
+        // Delta = U - W H (row tid / 4, columns 2 (tid % 4) + {0, 1})
+        {
+            const int r = tid / 4, cc = 2 * (tid % 4);
+            float s0 = sU[r * SW + cc], s1 = sU[r * SW + cc + 1];
+#pragma unroll 8
+            for (int x = 0; x < D; ++x) {
+                const float w = sW[r * LD + x];
+                s0 = fmaf(-w, sH[x * SW + cc], s0);
+                s1 = fmaf(-w, sH[x * SW + cc + 1], s1);
+            }
+            *reinterpret_cast<float2*>(a.dl + (nc * BC + r) * D + c0 + cc) = make_float2(s0, s1);
+            sDe[r * SW + cc] = se[r] * s0;
+            sDe[r * SW + cc + 1] = se[r] * s1;
         }
         __syncthreads();
-        // Delta_s = U_s - W H_s
-        const float* up = a.u + nc * BC * D;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = tr + 16 * i;
-            float s = up[r * D + col];
-            for (int x = 0; x < D; ++x) s = fmaf(-sW[r * LD + x], sH[x * 17 + tc], s);
-            sDl[r * 17 + tc] = s;
-            a.dl[(nc * BC + r) * D + col] = s;
-        }
-        __syncthreads();
-        // H_s = Gam_C H_s + (diag(e) K)^T Delta_s
-        const float gc = scp[BC - 1];
-        for (int r = tr; r < D; r += 16) {
-            float s = gc * sH[r * 17 + tc];
-            for (int t = 0; t < BC; ++t) s = fmaf(sKe[t * LD + r], sDl[t * 17 + tc], s);
-            sH[r * 17 + tc] = s;
+        // H = Gam_C H + K^T diag(e) Delta (row tid / 2, columns 4 (tid % 2) + {0..3})
+        {
+            const int r = tid / 2, cc = 4 * (tid % 2);
+            float4 acc = *reinterpret_cast<const float4*>(&sH[r * SW + cc]);
+            const float gc = sgc;
+            acc.x *= gc, acc.y *= gc, acc.z *= gc, acc.w *= gc;
+#pragma unroll 8
+            for (int t = 0; t < BC; ++t) {
+                const float kv = sK[t * LD + r];
+                const float4 dv = *reinterpret_cast<const float4*>(&sDe[t * SW + cc]);
+                acc.x = fmaf(kv, dv.x, acc.x), acc.y = fmaf(kv, dv.y, acc.y);
+                acc.z = fmaf(kv, dv.z, acc.z), acc.w = fmaf(kv, dv.w, acc.w);
+            }
+            __syncthreads();
+            *reinterpret_cast<float4*>(&sH[r * SW + cc]) = acc;
         }
     }
 }
 
-// ---------------------------------------------------------------------------
 template <typename In, int D>
 __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
-    constexpr int LD = D + 1, LC = BC + 1;
-    __shared__ float sK[BC * LD], sQg[BC * LD], sP[BC * LC], sTi[BC * LC];
-    __shared__ float sG[D * 17], sdO[BC * 17], sX[BC * 17], sY[BC * 17], ssc[3 * BC];
+    constexpr int LD = D + 4, LC = BC + 4;
+    __shared__ __attribute__((aligned(16))) float sK[BC * LD], sQ[BC * LD], sP[BC * LC], sTi[BC * LC];
+    __shared__ __attribute__((aligned(16))) float sG[D * SW], sdO[BC * SW], sX[BC * SW], sdOg[BC * SW], sdRb[BC * SW];
+    __shared__ __attribute__((aligned(16))) float ssc[3 * BC];
     const int tid = threadIdx.x, sl = blockIdx.x, h = blockIdx.y;
     const long b = blockIdx.z, n = b * a.H + h;
-    const int tr = tid / 16, tc = tid % 16, col = sl * 16 + tc;
-    const int T = a.T;
-    for (int r = tr; r < D; r += 16)
-        sG[r * 17 + tc] = a.d_state ? a.d_state[(n * D + r) * D + col] : 0.f;
+    const int c0 = sl * SW, T = a.T;
+    for (int idx = tid; idx < D * SW; idx += 256) {
+        const int r = idx / SW, cc = idx % SW;
+        sG[idx] = a.d_state ? a.d_state[(n * D + r) * D + c0 + cc] : 0.f;
+    }
+    RowRegs<In, D> rk, rq;
+    BlockRegs<BC, BC> rp, rt;
+    float4 rdo = make_float4(0.f, 0.f, 0.f, 0.f), rsc = rdo;
+    auto fetch = [&](int c) {
+        const long nc = n * a.NC + c;
+        rk.load(a.k, b, h, c * BC, T, a.H);
+        rq.load(a.q, b, h, c * BC, T, a.H);
+        rp.load(a.pm + nc * BC * BC, BC);
+        rt.load(a.ti + nc * BC * BC, BC);
+        if (tid < BC * SW / 4) {
+            const int r = tid / 2, t = c * BC + r;
+            rdo = t < T ? *reinterpret_cast<const float4*>(a.d_o + ((b * T + t) * a.H + h) * (long)D + c0 + (tid % 2) * 4)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if (tid < 3 * BC / 4) rsc = *reinterpret_cast<const float4*>(a.sc + nc * 3 * BC + 4 * tid);
+    };
+    fetch(a.NC - 1);
     for (int c = a.NC - 1; c >= 0; --c) {
         const long nc = n * a.NC + c;
-        const int t0 = c * BC;
         __syncthreads();
-        for (int r = tr; r < D; r += 16) a.gs[(nc * D + r) * D + col] = sG[r * 17 + tc];
-        if (tid < 3 * BC) ssc[tid] = a.sc[nc * 3 * BC + tid];
+        rk.template store<LD>(sK);
+        rq.template store<LD>(sQ);
+        rp.template store<LC>(sP);
+        rt.template store<LC>(sTi);
+        if (tid < BC * SW / 4) *reinterpret_cast<float4*>(&sdO[(tid / 2) * SW + (tid % 2) * 4]) = rdo;
+        if (tid < 3 * BC / 4) *reinterpret_cast<float4*>(&ssc[4 * tid]) = rsc;
+        for (int idx = tid; idx < D * SW; idx += 256)
+            a.gs[(nc * D + idx / SW) * D + c0 + idx % SW] = sG[idx];
         __syncthreads();
-        for (int idx = tid; idx < BC * D; idx += 256) {
-            const int r = idx / D, x = idx % D, t = t0 + r;
-            const long gi = ((b * T + t) * a.H + h) * (long)D + x;
-            sK[r * LD + x] = t < T ? ld<In>(a.k, gi) : 0.f;
-            sQg[r * LD + x] = t < T ? ssc[r] * ld<In>(a.q, gi) : 0.f;
-        }
-        for (int idx = tid; idx < BC * BC; idx += 256) {
-            const int r = idx / BC, s = idx % BC;
-            sP[r * LC + s] = a.pm[nc * BC * BC + idx];
-            sTi[r * LC + s] = a.ti[nc * BC * BC + idx];
-        }
-        for (int r = tr; r < BC; r += 16) {
-            const int t = t0 + r;
-            sdO[r * 17 + tc] = t < T ? a.d_o[((b * T + t) * a.H + h) * (long)D + col] : 0.f;
-        }
-        __syncthreads();
-        // dDelta = P^T dO + diag(e) K G
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = tr + 16 * i;
-            float s = 0.f;
-            for (int j = r; j < BC; ++j) s = fmaf(sP[j * LC + r], sdO[j * 17 + tc], s);
-            float kg = 0.f;
-            for (int x = 0; x < D; ++x) kg = fmaf(sK[r * LD + x], sG[x * 17 + tc], kg);
-            sX[r * 17 + tc] = fmaf(ssc[BC + r], kg, s);
+        if (c > 0) fetch(c - 1);
+        // dDelta = P^T dO + diag(e) K G   (row tid / 4, columns 2 (tid % 4) + {0, 1})
+        {
+            const int r = tid / 4, cc = 2 * (tid % 4);
+            float s0 = 0.f, s1 = 0.f, k0 = 0.f, k1 = 0.f;
+            for (int j = r; j < BC; ++j) {
+                const float p = sP[j * LC + r];
+                s0 = fmaf(p, sdO[j * SW + cc], s0);
+                s1 = fmaf(p, sdO[j * SW + cc + 1], s1);
+            }
+#pragma unroll 8
+            for (int x = 0; x < D; ++x) {
+                const float kv = sK[r * LD + x];
+                k0 = fmaf(kv, sG[x * SW + cc], k0);
+                k1 = fmaf(kv, sG[x * SW + cc + 1], k1);
+            }
+            const float e = ssc[BC + r], gm = ssc[r];
+            sX[r * SW + cc] = fmaf(e, k0, s0);
+            sX[r * SW + cc + 1] = fmaf(e, k1, s1);
+            sdOg[r * SW + cc] = gm * sdO[r * SW + cc];
+            sdOg[r * SW + cc + 1] = gm * sdO[r * SW + cc + 1];
         }
         __syncthreads();
         // dR = Ti^T dDelta  (Ti lower)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = tr + 16 * i;
-            float s = 0.f;
-            for (int j = r; j < BC; ++j) s = fmaf(sTi[j * LC + r], sX[j * 17 + tc], s);
-            sY[r * 17 + tc] = s;
-            a.dr[(nc * BC + r) * D + col] = s;
+        {
+            const int r = tid / 4, cc = 2 * (tid % 4);
+            float s0 = 0.f, s1 = 0.f;
+            for (int j = r; j < BC; ++j) {
+                const float ti = sTi[j * LC + r];
+                s0 = fmaf(ti, sX[j * SW + cc], s0);
+                s1 = fmaf(ti, sX[j * SW + cc + 1], s1);
+            }
+            *reinterpret_cast<float2*>(a.dr + (nc * BC + r) * D + c0 + cc) = make_float2(s0, s1);
+            const float bg = ssc[2 * BC + r] * ssc[r];
+            sdRb[r * SW + cc] = bg * s0;
+            sdRb[r * SW + cc + 1] = bg * s1;
         }
         __syncthreads();
-        // G = Gam_C G + (diag(Gam) Q)^T dO - (diag(b Gam) K)^T dR
-        const float gc = ssc[BC - 1];
-        for (int r = tr; r < D; r += 16) {
-            float s = gc * sG[r * 17 + tc];
+        // G = Gam_C G + Q^T diag(Gam) dO - K^T diag(b Gam) dR  (row tid / 2, columns 4 (tid % 2) + {0..3})
+        {
+            const int r = tid / 2, cc = 4 * (tid % 2);
+            float4 acc = *reinterpret_cast<const float4*>(&sG[r * SW + cc]);
+            const float gc = ssc[BC - 1];
+            acc.x *= gc, acc.y *= gc, acc.z *= gc, acc.w *= gc;
+#pragma unroll 8
             for (int t = 0; t < BC; ++t) {
-                s = fmaf(sQg[t * LD + r], sdO[t * 17 + tc], s);
-                s = fmaf(-ssc[2 * BC + t] * ssc[t] * sK[t * LD + r], sY[t * 17 + tc], s);
+                const float qv = sQ[t * LD + r], kv = sK[t * LD + r];
+                const float4 o4 = *reinterpret_cast<const float4*>(&sdOg[t * SW + cc]);
+                const float4 d4 = *reinterpret_cast<const float4*>(&sdRb[t * SW + cc]);
+                acc.x = fmaf(qv, o4.x, fmaf(-kv, d4.x, acc.x));
+                acc.y = fmaf(qv, o4.y, fmaf(-kv, d4.y, acc.y));
+                acc.z = fmaf(qv, o4.z, fmaf(-kv, d4.z, acc.z));
+                acc.w = fmaf(qv, o4.w, fmaf(-kv, d4.w, acc.w));
             }
-            sG[r * 17 + tc] = s;
+            __syncthreads();
+            *reinterpret_cast<float4*>(&sG[r * SW + cc]) = acc;
         }
     }
     if (a.dstate0) {
         __syncthreads();
-        for (int r = tr; r < D; r += 16) a.dstate0[(n * D + r) * D + col] = sG[r * 17 + tc];
+        for (int idx = tid; idx < D * SW; idx += 256)
+            a.dstate0[(n * D + idx / SW) * D + c0 + idx % SW] = sG[idx];
     }
 }
 
@@ -318,9 +446,10 @@ __device__ __forceinline__ float block_sum(float x, float* red) {
 
 template <typename In, int D>
 __global__ __launch_bounds__(256) void bwd_grads(const BwdArgs a) {
-    constexpr int LD = D + 1, LC = BC + 1;
+    constexpr int LD = D + 4, LC = BC + 1;
     constexpr int CJ = D / 16;  // output columns per thread
-    __shared__ float sK[BC * LD], sQ[BC * LD], sDl[BC * LD], sdA[BC * LC], sdP[BC * LC];
+    __shared__ __attribute__((aligned(16))) float sK[BC * LD], sQ[BC * LD], sDl[BC * LD];
+    __shared__ float sdA[BC * LC], sdP[BC * LC];
     __shared__ float sgam[BC], sGam[BC], se[BC], sb[BC], sdg[BC], sdb[BC], red[8];
     __shared__ float sdot[3][BC * 17];  // per-thread-column partial row dots
     const int tid = threadIdx.x, c = blockIdx.x, h = blockIdx.y;
@@ -340,7 +469,11 @@ __global__ __launch_bounds__(256) void bwd_grads(const BwdArgs a) {
     const float* drp = a.dr + nc * BC * D;
     const float* h0 = a.hs + nc * D * D;
     const float* gp = a.gs + nc * D * D;
-    for (int idx = tid; idx < BC * D; idx += 256) sDl[(idx / D) * LD + idx % D] = dlp[idx];
+    {
+        BlockRegs<BC, D> rd;
+        rd.load(dlp, D);
+        rd.template store<LD>(sDl);
+    }
     __syncthreads();
     // gam: the same serial fp32 cumsum as bwd_prep, so L matches its P and lkk
     if (tid == 0) {
@@ -354,21 +487,23 @@ __global__ __launch_bounds__(256) void bwd_grads(const BwdArgs a) {
     // dA = -strict_lower(dR Delta^T), dP = lower(dO Delta^T)
     {
         float ga[4][4] = {}, gp2[4][4] = {};
-        for (int x = 0; x < D; ++x) {
-            float dr4[4], do4[4], dl4[4];
+        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 2
+        for (int x = 0; x < D; x += 4) {
+            float4 dr4[4], do4[4], dl4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = tr + 16 * i, t = t0 + r;
-                dr4[i] = drp[r * D + x];
-                do4[i] = t < T ? a.d_o[((b * T + t) * a.H + h) * (long)D + x] : 0.f;
-                dl4[i] = sDl[(tc + 16 * i) * LD + x];
+                dr4[i] = *reinterpret_cast<const float4*>(drp + r * D + x);
+                do4[i] = t < T ? *reinterpret_cast<const float4*>(a.d_o + ((b * T + t) * a.H + h) * (long)D + x) : z4;
+                dl4[i] = *reinterpret_cast<const float4*>(&sDl[(tc + 16 * i) * LD + x]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    ga[i][j] = fmaf(dr4[i], dl4[j], ga[i][j]);
-                    gp2[i][j] = fmaf(do4[i], dl4[j], gp2[i][j]);
+                    ga[i][j] = fmaf(dr4[i].x, dl4[j].x, fmaf(dr4[i].y, dl4[j].y, fmaf(dr4[i].z, dl4[j].z, fmaf(dr4[i].w, dl4[j].w, ga[i][j]))));
+                    gp2[i][j] = fmaf(do4[i].x, dl4[j].x, fmaf(do4[i].y, dl4[j].y, fmaf(do4[i].z, dl4[j].z, fmaf(do4[i].w, dl4[j].w, gp2[i][j]))));
                 }
         }
 #pragma unroll
@@ -409,19 +544,21 @@ __global__ __launch_bounds__(256) void bwd_grads(const BwdArgs a) {
     // dQ = diag(Gam) dO H0^T + dPL K ;  row dot (dO H0^T)_r . q_r
     {
         float x1[4][CJ] = {}, x2[4][CJ] = {};
-        for (int j = 0; j < D; ++j) {
-            float do4[4], hv[CJ];
+        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < D; j += 4) {
+            float4 do4[4], hv[CJ];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = t0 + tr + 16 * i;
-                do4[i] = t < T ? a.d_o[((b * T + t) * a.H + h) * (long)D + j] : 0.f;
+                do4[i] = t < T ? *reinterpret_cast<const float4*>(a.d_o + ((b * T + t) * a.H + h) * (long)D + j) : z4;
             }
 #pragma unroll
-            for (int jj = 0; jj < CJ; ++jj) hv[jj] = h0[(tc + 16 * jj) * D + j];
+            for (int jj = 0; jj < CJ; ++jj) hv[jj] = *reinterpret_cast<const float4*>(h0 + (tc + 16 * jj) * D + j);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int jj = 0; jj < CJ; ++jj) x1[i][jj] = fmaf(do4[i], hv[jj], x1[i][jj]);
+                for (int jj = 0; jj < CJ; ++jj)
+                    x1[i][jj] = fmaf(do4[i].x, hv[jj].x, fmaf(do4[i].y, hv[jj].y, fmaf(do4[i].z, hv[jj].z, fmaf(do4[i].w, hv[jj].w, x1[i][jj]))));
         }
         for (int s = 0; s < BC; ++s) {
             float p4[4], kv[CJ];
@@ -451,24 +588,24 @@ __global__ __launch_bounds__(256) void bwd_grads(const BwdArgs a) {
     // row dots (Delta G^T)_r . k_r and (dR H0^T)_r . k_r
     {
         float y1[4][CJ] = {}, y2[4][CJ] = {}, y3[4][CJ] = {};
-        for (int j = 0; j < D; ++j) {
-            float dl4[4], dr4[4], gv[CJ], hv[CJ];
+        for (int j = 0; j < D; j += 4) {
+            float4 dl4[4], dr4[4], gv[CJ], hv[CJ];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                dl4[i] = sDl[(tr + 16 * i) * LD + j];
-                dr4[i] = drp[(tr + 16 * i) * D + j];
+                dl4[i] = *reinterpret_cast<const float4*>(&sDl[(tr + 16 * i) * LD + j]);
+                dr4[i] = *reinterpret_cast<const float4*>(drp + (tr + 16 * i) * D + j);
             }
 #pragma unroll
             for (int jj = 0; jj < CJ; ++jj) {
-                gv[jj] = gp[(tc + 16 * jj) * D + j];
-                hv[jj] = h0[(tc + 16 * jj) * D + j];
+                gv[jj] = *reinterpret_cast<const float4*>(gp + (tc + 16 * jj) * D + j);
+                hv[jj] = *reinterpret_cast<const float4*>(h0 + (tc + 16 * jj) * D + j);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int jj = 0; jj < CJ; ++jj) {
-                    y1[i][jj] = fmaf(dl4[i], gv[jj], y1[i][jj]);
-                    y2[i][jj] = fmaf(dr4[i], hv[jj], y2[i][jj]);
+                    y1[i][jj] = fmaf(dl4[i].x, gv[jj].x, fmaf(dl4[i].y, gv[jj].y, fmaf(dl4[i].z, gv[jj].z, fmaf(dl4[i].w, gv[jj].w, y1[i][jj]))));
+                    y2[i][jj] = fmaf(dr4[i].x, hv[jj].x, fmaf(dr4[i].y, hv[jj].y, fmaf(dr4[i].z, hv[jj].z, fmaf(dr4[i].w, hv[jj].w, y2[i][jj]))));
                 }
         }
         for (int s = 0; s < BC; ++s) {
@@ -570,7 +707,7 @@ __global__ __launch_bounds__(256) void bwd_grads(const BwdArgs a) {
 
 template <typename In, int D>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
-    const dim3 gc((unsigned)a.NC, (unsigned)a.H, (unsigned)a.B), gs((unsigned)(D / 16), (unsigned)a.H, (unsigned)a.B);
+    const dim3 gc((unsigned)a.NC, (unsigned)a.H, (unsigned)a.B), gs((unsigned)(D / SW), (unsigned)a.H, (unsigned)a.B);
     hipLaunchKernelGGL((bwd_prep<In, D>), gc, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     profile_mark(stream);
