@@ -218,12 +218,15 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdArgs a) {
         for (int r = 0; r < BC; ++r) sTi[r * LC + tid] = r == tid ? 1.f : 0.f;
     }
     __syncthreads();
+    // column j = tid / 4; the 4 threads of a column split the dot product
     for (int r = 1; r < BC; ++r) {
-        if (tid < r) {
-            float s = 0.f;
-            for (int i = tid; i < r; ++i) s = fmaf(sL[r * LC + i], sTi[i * LC + tid], s);
-            sTi[r * LC + tid] = -sb[r] * s;
-        }
+        const int j = tid / 4, part = tid % 4;
+        float s = 0.f;
+        if (j < r)
+            for (int i = j + part; i < r; i += 4) s = fmaf(sL[r * LC + i], sTi[i * LC + j], s);
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        if (j < r && part == 0) sTi[r * LC + j] = -sb[r] * s;
         __syncthreads();
     }
     {
@@ -374,7 +377,8 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
         {
             const int r = tid / 4, cc = 2 * (tid % 4);
             float s0 = 0.f, s1 = 0.f, k0 = 0.f, k1 = 0.f;
-            for (int j = r; j < BC; ++j) {
+#pragma unroll 8
+            for (int j = 0; j < BC; ++j) {  // P is zero above the diagonal
                 const float p = sP[j * LC + r];
                 s0 = fmaf(p, sdO[j * SW + cc], s0);
                 s1 = fmaf(p, sdO[j * SW + cc + 1], s1);
@@ -396,7 +400,8 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
         {
             const int r = tid / 4, cc = 2 * (tid % 4);
             float s0 = 0.f, s1 = 0.f;
-            for (int j = r; j < BC; ++j) {
+#pragma unroll 8
+            for (int j = 0; j < BC; ++j) {  // Ti is zero above the diagonal
                 const float ti = sTi[j * LC + r];
                 s0 = fmaf(ti, sX[j * SW + cc], s0);
                 s1 = fmaf(ti, sX[j * SW + cc + 1], s1);
@@ -516,21 +521,38 @@ __global__ __launch_bounds__(256) void bwd_grads(const BwdArgs a) {
             }
     }
     __syncthreads();
-    // row / column sums of dP o P and dA o A, db's Gram term; then dP <- dP o L,
-    // dA <- dA o (b_r L)
-    if (tid < BC) {
-        const int r = tid;
+    // row / column sums of dP o P and dA o A and db's Gram term, from this
+    // thread's 16 entries (rows tr + 16 i, columns tc + 16 j) into LDS atomics;
+    // then dP <- dP o L, dA <- dA o (b_r L)
+    if (tid < BC) sdg[tid] = 0.f, sdb[tid] = 0.f;
+    __syncthreads();
+    {
         const float* pmp = a.pm + nc * BC * BC;
         const float* lkp = a.lkk + nc * BC * BC;
-        float g1 = 0.f, db3 = 0.f;
-        for (int s = 0; s < BC; ++s) {
-            g1 += sdP[r * LC + s] * pmp[r * BC + s] - sdP[s * LC + r] * pmp[s * BC + r];
-            const float lk_rs = lkp[r * BC + s], lk_sr = lkp[s * BC + r];
-            g1 += sdA[r * LC + s] * sb[r] * lk_rs - sdA[s * LC + r] * sb[s] * lk_sr;
-            db3 += sdA[r * LC + s] * lk_rs;
+        float pv[4][4], lv[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = tr + 16 * i, s = tc + 16 * j;
+                pv[i][j] = pmp[r * BC + s];
+                lv[i][j] = lkp[r * BC + s];
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = tr + 16 * i;
+            float rs = 0.f, db3 = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int s = tc + 16 * j;
+                const float x = sdP[r * LC + s] * pv[i][j] + sdA[r * LC + s] * sb[r] * lv[i][j];
+                rs += x;
+                atomicAdd(&sdg[s], -x);
+                db3 = fmaf(sdA[r * LC + s], lv[i][j], db3);
+            }
+            atomicAdd(&sdg[r], rs);
+            atomicAdd(&sdb[r], db3);
         }
-        sdg[r] = g1;
-        sdb[r] = db3;
     }
     __syncthreads();
     for (int idx = tid; idx < BC * BC; idx += 256) {
@@ -662,7 +684,11 @@ __global__ __launch_bounds__(256) void bwd_grads(const BwdArgs a) {
     }
     // <G, H0>
     float gh = 0.f;
-    for (int idx = tid; idx < D * D; idx += 256) gh = fmaf(gp[idx], h0[idx], gh);
+#pragma unroll 4
+    for (int idx = 4 * tid; idx < D * D; idx += 1024) {
+        const float4 x = *reinterpret_cast<const float4*>(gp + idx), y = *reinterpret_cast<const float4*>(h0 + idx);
+        gh = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, gh))));
+    }
     gh = block_sum(gh, red);  // contains barriers
     // reduce the row dots over the 16 column threads
 #pragma unroll
