@@ -158,6 +158,18 @@ __device__ __forceinline__ float qsum(float s) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Raw buffer loads: the descriptor's byte bound returns zeros past the valid
+// rows, so the staging loads need no lane tests or branches.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, unsigned off) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return uint4{x[0], x[1], x[2], x[3]};
+}
+constexpr unsigned kOob = 0x80000000u;  // an offset past every descriptor's bound
+
 __device__ __forceinline__ unsigned pack_h2(_Float16 a, _Float16 b) {
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     const h2 p = {a, b};
@@ -195,36 +207,45 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
     const _Float16* kcb = RING ? a.kc + ((b * a.Hkv + hk) * (long)a.R) * SD : nullptr;
     const _Float16* vcb = RING ? a.vc + ((b * a.Hkv + hk) * (long)a.R) * SD : nullptr;
 
-    // row j of K or V (ring slot (pos0 + j) mod R for j < 0; pmod = pos0 mod R)
-    auto row = [&](const _Float16* base, const _Float16* ring, int j) -> const _Float16* {
+    // Row j of K or V: token j of this call for j >= 0 (rows past jhi read as
+    // zeros through the descriptor bound), ring slot (pos0 + j) mod R for j < 0
+    // (pmod = pos0 mod R).  With the ring, both loads are issued and OR'ed: the
+    // one whose rows do not hold j returns zeros.
+    const rsrc_t kd = make_rsrc(kbase, (unsigned)(jhi + 1) * SD * 2);
+    const rsrc_t vd = make_rsrc(vbase, (unsigned)(jhi + 1) * SD * 2);
+    const rsrc_t kcd = make_rsrc(RING ? kcb : kbase, RING ? (unsigned)a.R * SD * 2 : 0u);
+    const rsrc_t vcd = make_rsrc(RING ? vcb : vbase, RING ? (unsigned)a.R * SD * 2 : 0u);
+    auto offs = [&](int j, int chunk, unsigned& cur, unsigned& ring) {
+        cur = j >= 0 ? (unsigned)j * SD * 2 + chunk * 16 : kOob;
+        ring = kOob;
         if (RING && j < 0) {
             int slot = a.pmod + j;
             slot += slot < 0 ? a.R : 0;  // j >= -hist >= -R
-            return ring + (long)slot * SD;
+            ring = (unsigned)slot * SD * 2 + chunk * 16;
         }
-        return base + (long)j * SD;
+    };
+    auto fetch = [&](rsrc_t cd, rsrc_t rd, int j, int chunk) -> uint4 {
+        unsigned oc, orr;
+        offs(j, chunk, oc, orr);
+        uint4 x = buf_load16(cd, oc);
+        if (RING) {
+            const uint4 y = buf_load16(rd, orr);
+            x.x |= y.x, x.y |= y.y, x.z |= y.z, x.w |= y.w;
+        }
+        return x;
     };
     // staging.  K: rows 16 i + tid / 16 (i < 4), chunk tid % 16 (16 bytes).
     // V: key pair kp = tid % 32 (keys 2 kp, 2 kp + 1), chunks tid / 32 + 8 i
     // (i < 2), so the transposed LDS writes of a wave fill 32 consecutive
-    // dwords of one row.  Rows beyond jhi are zero.
+    // dwords of one row.
     const int kch = tid % 16, krw = tid / 16;
     const int kp = tid % 32, vch = tid / 32;
     uint4 pk[4], pv[4];
     auto load_block = [&](int j0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j = j0 + 16 * i + krw;
-            pk[i] = (j <= jhi) ? *reinterpret_cast<const uint4*>(row(kbase, kcb, j) + kch * 8)
-                               : uint4{0, 0, 0, 0};
-        }
+        for (int i = 0; i < 4; ++i) pk[i] = fetch(kd, kcd, j0 + 16 * i + krw, kch);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j = j0 + 2 * kp + (i & 1);
-            pv[i] = (j <= jhi)
-                        ? *reinterpret_cast<const uint4*>(row(vbase, vcb, j) + (vch + 8 * (i >> 1)) * 8)
-                        : uint4{0, 0, 0, 0};
-        }
+        for (int i = 0; i < 4; ++i) pv[i] = fetch(vd, vcd, j0 + 2 * kp + (i & 1), vch + 8 * (i >> 1));
     };
     auto store_block = [&](int buf) {
 #pragma unroll
@@ -259,6 +280,10 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
         load_block(jlo);
         store_block(0);
     }
+    // Retire the query-fragment loads here: left outstanding into the loop,
+    // the in-order load counter would make every block's first use of a
+    // fragment also wait for that block's prefetch loads.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
     for (int bi = 0; bi < nblk; ++bi) {
