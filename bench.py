@@ -64,11 +64,12 @@ GATE_BYTES_PER_TOKEN_HEAD = 512 + 256 + 256
 PREFILL_KERNELS = [("summary pass (gdn_fused<128,false>)", 2 * 256 + 8),
                    ("segment combine (seg_combine<128>)", None),
                    ("output pass (gdn_fused<128,true>)", PREFILL_BYTES_PER_TOKEN_HEAD)]
-# Sources the prefill kernels are built from; the counter summary records their hash.
-KERNEL_SOURCES = ["gdn_fused.hip", "gdn_chunk.hip", "gdn_device.h", "gdn_mfma.h",
-                  "gdn_launch.h", "gdn_api.cpp"]
+# Sources of the prefill, decode and layer kernels; the counter summaries record their hash.
+KERNEL_SOURCES = ["gdn_fused.hip", "gdn_chunk.hip", "gdn_decode.hip", "gdn_layer.hip",
+                  "gdn_device.h", "gdn_mfma.h", "gdn_launch.h", "gdn_api.cpp"]
 TRAFFIC_FILES = [os.path.join(ROOT, "profiles", f)
-                 for f in ("prefill8k_hbm_traffic.txt", "decode64_hbm_traffic.txt")]
+                 for f in ("prefill8k_hbm_traffic.txt", "decode64_hbm_traffic.txt",
+                           "layer8k_hbm_traffic.txt")]
 
 
 def parse():
@@ -507,7 +508,7 @@ def time_layer(gdn, args, dev):
         gbs = nbytes / (kt / 1e3) / 1e9
         res.append({"kernel": name, "us": kt * 1e3, "bytes_per_launch": nbytes, "bound": "hbm",
                     "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": gbs / HBM_PEAK_GBS})
+                    "frac": gbs / HBM_PEAK_GBS, "traffic": committed_traffic(name)})
     return {"workload": "layer8k: conv_qkv (window 4, q/k L2 norm) -> gdn_prefill -> gate_out "
                         "(bf16 out), B=1, H=16, T=8192, d=128, zero states",
             "value": B * T / (ms / 1e3), "unit": "tokens/s", "ms_per_call": ms, "kernels": res}
