@@ -259,14 +259,33 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdArgs a) {
 // loads) while the current chunk computes, then written to LDS.
 constexpr int SW = 8;  // state columns per slice
 
+// 1D grid of nser * ns workgroups -> (series n, slice).  Workgroups are dealt
+// to the 8 XCDs round-robin; when the series count is a multiple of 8, all
+// slices of one series land on one XCD so the chunk operands they all read are
+// shared in its L2 (a bijection onto [0, nser) x [0, ns) exactly then).
+__device__ __forceinline__ void slice_of(int ns, int nser, long& n, int& sl) {
+    const int L = blockIdx.x;
+    if (nser % 8 == 0) {
+        n = (L % 8) + 8 * ((L / 8) / ns);
+        sl = (L / 8) % ns;
+    } else {
+        n = L / ns;
+        sl = L % ns;
+    }
+}
+
 template <typename In, int D>
 __global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
     constexpr int LD = D + 4;
     __shared__ __attribute__((aligned(16))) float sW[BC * LD], sK[BC * LD];
     __shared__ __attribute__((aligned(16))) float sH[D * SW], sU[BC * SW], sDe[BC * SW];
     __shared__ float se[BC], sgc;
-    const int tid = threadIdx.x, sl = blockIdx.x, h = blockIdx.y;
-    const long b = blockIdx.z, n = b * a.H + h;
+    const int tid = threadIdx.x;
+    long n;
+    int sl;
+    slice_of(D / SW, a.B * a.H, n, sl);
+    const long b = n / a.H;
+    const int h = (int)(n % a.H);
     const int c0 = sl * SW;
     for (int idx = tid; idx < D * SW; idx += 256) {
         const int r = idx / SW, cc = idx % SW;
@@ -336,8 +355,12 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float sK[BC * LD], sQ[BC * LD], sP[BC * LC], sTi[BC * LC];
     __shared__ __attribute__((aligned(16))) float sG[D * SW], sdO[BC * SW], sX[BC * SW], sdOg[BC * SW], sdRb[BC * SW];
     __shared__ __attribute__((aligned(16))) float ssc[3 * BC];
-    const int tid = threadIdx.x, sl = blockIdx.x, h = blockIdx.y;
-    const long b = blockIdx.z, n = b * a.H + h;
+    const int tid = threadIdx.x;
+    long n;
+    int sl;
+    slice_of(D / SW, a.B * a.H, n, sl);
+    const long b = n / a.H;
+    const int h = (int)(n % a.H);
     const int c0 = sl * SW, T = a.T;
     for (int idx = tid; idx < D * SW; idx += 256) {
         const int r = idx / SW, cc = idx % SW;
@@ -733,7 +756,7 @@ __global__ __launch_bounds__(256) void bwd_grads(const BwdArgs a) {
 
 template <typename In, int D>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
-    const dim3 gc((unsigned)a.NC, (unsigned)a.H, (unsigned)a.B), gs((unsigned)(D / SW), (unsigned)a.H, (unsigned)a.B);
+    const dim3 gc((unsigned)a.NC, (unsigned)a.H, (unsigned)a.B), gs((unsigned)(a.B * a.H * (D / SW)));
     hipLaunchKernelGGL((bwd_prep<In, D>), gc, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     profile_mark(stream);
