@@ -45,6 +45,13 @@ namespace {
 
 constexpr int BC = 64;  // chunk length
 
+// Native vector types for register-held data: HIP's fx4 / ux4 structs are
+// copied through memcpy, which keeps register arrays of them in scratch memory.
+typedef float fx4 __attribute__((ext_vector_type(4)));
+typedef float fx2 __attribute__((ext_vector_type(2)));
+typedef uint32_t ux4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ fx4 f4(float a, float b, float c, float d) { return fx4{a, b, c, d}; }
+
 struct BwdArgs {
     const void* q;
     const void* k;
@@ -86,14 +93,14 @@ struct RowRegs {
     static constexpr int VPL = 16 / sizeof(In);      // values per 16-byte load
     static constexpr int PPR = D / VPL;              // loads per row
     static constexpr int N = BC * PPR / 256;         // loads per thread
-    uint4 r[N];
+    ux4 r[N];
     __device__ __forceinline__ void load(const void* src, long b, int h, int t0, int T, int H) {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int p = threadIdx.x + 256 * i, row = p / PPR, col = (p % PPR) * VPL, t = t0 + row;
-            r[i] = t < T ? *reinterpret_cast<const uint4*>(static_cast<const In*>(src) +
+            r[i] = t < T ? *reinterpret_cast<const ux4*>(static_cast<const In*>(src) +
                                                            ((b * T + t) * H + h) * (long)D + col)
-                         : uint4{0, 0, 0, 0};
+                         : ux4{0u, 0u, 0u, 0u};
         }
     }
     // dst row stride LD (floats, a multiple of 4)
@@ -104,12 +111,12 @@ struct RowRegs {
             const int p = threadIdx.x + 256 * i, row = p / PPR, col = (p % PPR) * VPL;
             float* d = dst + row * LD + col;
             if constexpr (sizeof(In) == 4) {
-                *reinterpret_cast<float4*>(d) = __builtin_bit_cast(float4, r[i]);
+                *reinterpret_cast<fx4*>(d) = __builtin_bit_cast(fx4, r[i]);
             } else {
                 const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
-                *reinterpret_cast<float4*>(d) = make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                *reinterpret_cast<fx4*>(d) = f4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
                                                             __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u));
-                *reinterpret_cast<float4*>(d + 4) = make_float4(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xFFFF0000u),
+                *reinterpret_cast<fx4*>(d + 4) = f4(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xFFFF0000u),
                                                                 __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xFFFF0000u));
             }
         }
@@ -129,13 +136,13 @@ template <int ROWS, int COLS>
 struct BlockRegs {
     static constexpr int PPR = COLS / 4, TOT = ROWS * PPR;
     static constexpr int N = (TOT + 255) / 256;
-    float4 r[N];
+    fx4 r[N];
     __device__ __forceinline__ void load(const float* src, int stride) {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int p = threadIdx.x + 256 * i;
             if (TOT % 256 == 0 || p < TOT)
-                r[i] = *reinterpret_cast<const float4*>(src + (p / PPR) * (long)stride + (p % PPR) * 4);
+                r[i] = *reinterpret_cast<const fx4*>(src + (p / PPR) * (long)stride + (p % PPR) * 4);
         }
     }
     template <int LD>
@@ -144,7 +151,7 @@ struct BlockRegs {
         for (int i = 0; i < N; ++i) {
             const int p = threadIdx.x + 256 * i;
             if (TOT % 256 == 0 || p < TOT)
-                *reinterpret_cast<float4*>(dst + (p / PPR) * LD + (p % PPR) * 4) = r[i];
+                *reinterpret_cast<fx4*>(dst + (p / PPR) * LD + (p % PPR) * 4) = r[i];
         }
     }
 };
@@ -293,13 +300,13 @@ __global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
     }
     BlockRegs<BC, D> rw;
     RowRegs<In, D> rk;
-    float4 ru = make_float4(0.f, 0.f, 0.f, 0.f);
+    fx4 ru = f4(0.f, 0.f, 0.f, 0.f);
     float re = 0.f;
-    auto fetch = [&](int c) {
+    auto fetch = [&](int c) __attribute__((always_inline)) {
         const long nc = n * a.NC + c;
         rw.load(a.w + nc * BC * D, D);
         rk.load(a.k, b, h, c * BC, a.T, a.H);
-        if (tid < BC * SW / 4) ru = *reinterpret_cast<const float4*>(a.u + (nc * BC + tid / 2) * D + c0 + (tid % 2) * 4);
+        if (tid < BC * SW / 4) ru = *reinterpret_cast<const fx4*>(a.u + (nc * BC + tid / 2) * D + c0 + (tid % 2) * 4);
         if (tid < BC) re = a.sc[nc * 3 * BC + BC + tid];
     };
     fetch(0);
@@ -308,13 +315,13 @@ __global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
         __syncthreads();
         rw.template store<LD>(sW);
         rk.template store<LD>(sK);
-        if (tid < BC * SW / 4) *reinterpret_cast<float4*>(&sU[(tid / 2) * SW + (tid % 2) * 4]) = ru;
+        if (tid < BC * SW / 4) *reinterpret_cast<fx4*>(&sU[(tid / 2) * SW + (tid % 2) * 4]) = ru;
         if (tid < BC) se[tid] = re;
         if (tid == 0) sgc = a.sc[nc * 3 * BC + BC - 1];
         for (int idx = tid; idx < D * SW; idx += 256)
             a.hs[(nc * D + idx / SW) * D + c0 + idx % SW] = sH[idx];
         __syncthreads();
-        if (c + 1 < a.NC) fetch(c + 1);
+        fetch(min(c + 1, a.NC - 1));  // unconditional: the last one re-reads valid rows
         // Delta = U - W H (row tid / 4, columns 2 (tid % 4) + {0, 1})
         {
             const int r = tid / 4, cc = 2 * (tid % 4);
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
                 s0 = fmaf(-w, sH[x * SW + cc], s0);
                 s1 = fmaf(-w, sH[x * SW + cc + 1], s1);
             }
-            *reinterpret_cast<float2*>(a.dl + (nc * BC + r) * D + c0 + cc) = make_float2(s0, s1);
+            *reinterpret_cast<fx2*>(a.dl + (nc * BC + r) * D + c0 + cc) = fx2{s0, s1};
             sDe[r * SW + cc] = se[r] * s0;
             sDe[r * SW + cc + 1] = se[r] * s1;
         }
@@ -333,18 +340,18 @@ __global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
         // H = Gam_C H + K^T diag(e) Delta (row tid / 2, columns 4 (tid % 2) + {0..3})
         {
             const int r = tid / 2, cc = 4 * (tid % 2);
-            float4 acc = *reinterpret_cast<const float4*>(&sH[r * SW + cc]);
+            fx4 acc = *reinterpret_cast<const fx4*>(&sH[r * SW + cc]);
             const float gc = sgc;
             acc.x *= gc, acc.y *= gc, acc.z *= gc, acc.w *= gc;
 #pragma unroll 8
             for (int t = 0; t < BC; ++t) {
                 const float kv = sK[t * LD + r];
-                const float4 dv = *reinterpret_cast<const float4*>(&sDe[t * SW + cc]);
+                const fx4 dv = *reinterpret_cast<const fx4*>(&sDe[t * SW + cc]);
                 acc.x = fmaf(kv, dv.x, acc.x), acc.y = fmaf(kv, dv.y, acc.y);
                 acc.z = fmaf(kv, dv.z, acc.z), acc.w = fmaf(kv, dv.w, acc.w);
             }
             __syncthreads();
-            *reinterpret_cast<float4*>(&sH[r * SW + cc]) = acc;
+            *reinterpret_cast<fx4*>(&sH[r * SW + cc]) = acc;
         }
     }
 }
@@ -368,8 +375,8 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
     }
     RowRegs<In, D> rk, rq;
     BlockRegs<BC, BC> rp, rt;
-    float4 rdo = make_float4(0.f, 0.f, 0.f, 0.f), rsc = rdo;
-    auto fetch = [&](int c) {
+    fx4 rdo = f4(0.f, 0.f, 0.f, 0.f), rsc = rdo;
+    auto fetch = [&](int c) __attribute__((always_inline)) {
         const long nc = n * a.NC + c;
         rk.load(a.k, b, h, c * BC, T, a.H);
         rq.load(a.q, b, h, c * BC, T, a.H);
@@ -377,10 +384,10 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
         rt.load(a.ti + nc * BC * BC, BC);
         if (tid < BC * SW / 4) {
             const int r = tid / 2, t = c * BC + r;
-            rdo = t < T ? *reinterpret_cast<const float4*>(a.d_o + ((b * T + t) * a.H + h) * (long)D + c0 + (tid % 2) * 4)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
+            rdo = t < T ? *reinterpret_cast<const fx4*>(a.d_o + ((b * T + t) * a.H + h) * (long)D + c0 + (tid % 2) * 4)
+                        : f4(0.f, 0.f, 0.f, 0.f);
         }
-        if (tid < 3 * BC / 4) rsc = *reinterpret_cast<const float4*>(a.sc + nc * 3 * BC + 4 * tid);
+        if (tid < 3 * BC / 4) rsc = *reinterpret_cast<const fx4*>(a.sc + nc * 3 * BC + 4 * tid);
     };
     fetch(a.NC - 1);
     for (int c = a.NC - 1; c >= 0; --c) {
@@ -390,12 +397,12 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
         rq.template store<LD>(sQ);
         rp.template store<LC>(sP);
         rt.template store<LC>(sTi);
-        if (tid < BC * SW / 4) *reinterpret_cast<float4*>(&sdO[(tid / 2) * SW + (tid % 2) * 4]) = rdo;
-        if (tid < 3 * BC / 4) *reinterpret_cast<float4*>(&ssc[4 * tid]) = rsc;
+        if (tid < BC * SW / 4) *reinterpret_cast<fx4*>(&sdO[(tid / 2) * SW + (tid % 2) * 4]) = rdo;
+        if (tid < 3 * BC / 4) *reinterpret_cast<fx4*>(&ssc[4 * tid]) = rsc;
         for (int idx = tid; idx < D * SW; idx += 256)
             a.gs[(nc * D + idx / SW) * D + c0 + idx % SW] = sG[idx];
         __syncthreads();
-        if (c > 0) fetch(c - 1);
+        fetch(max(c - 1, 0));  // unconditional: the last one re-reads valid rows
         // dDelta = P^T dO + diag(e) K G   (row tid / 4, columns 2 (tid % 4) + {0, 1})
         {
             const int r = tid / 4, cc = 2 * (tid % 4);
@@ -429,7 +436,7 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
                 s0 = fmaf(ti, sX[j * SW + cc], s0);
                 s1 = fmaf(ti, sX[j * SW + cc + 1], s1);
             }
-            *reinterpret_cast<float2*>(a.dr + (nc * BC + r) * D + c0 + cc) = make_float2(s0, s1);
+            *reinterpret_cast<fx2*>(a.dr + (nc * BC + r) * D + c0 + cc) = fx2{s0, s1};
             const float bg = ssc[2 * BC + r] * ssc[r];
             sdRb[r * SW + cc] = bg * s0;
             sdRb[r * SW + cc + 1] = bg * s1;
@@ -438,21 +445,21 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
         // G = Gam_C G + Q^T diag(Gam) dO - K^T diag(b Gam) dR  (row tid / 2, columns 4 (tid % 2) + {0..3})
         {
             const int r = tid / 2, cc = 4 * (tid % 2);
-            float4 acc = *reinterpret_cast<const float4*>(&sG[r * SW + cc]);
+            fx4 acc = *reinterpret_cast<const fx4*>(&sG[r * SW + cc]);
             const float gc = ssc[BC - 1];
             acc.x *= gc, acc.y *= gc, acc.z *= gc, acc.w *= gc;
 #pragma unroll 8
             for (int t = 0; t < BC; ++t) {
                 const float qv = sQ[t * LD + r], kv = sK[t * LD + r];
-                const float4 o4 = *reinterpret_cast<const float4*>(&sdOg[t * SW + cc]);
-                const float4 d4 = *reinterpret_cast<const float4*>(&sdRb[t * SW + cc]);
+                const fx4 o4 = *reinterpret_cast<const fx4*>(&sdOg[t * SW + cc]);
+                const fx4 d4 = *reinterpret_cast<const fx4*>(&sdRb[t * SW + cc]);
                 acc.x = fmaf(qv, o4.x, fmaf(-kv, d4.x, acc.x));
                 acc.y = fmaf(qv, o4.y, fmaf(-kv, d4.y, acc.y));
                 acc.z = fmaf(qv, o4.z, fmaf(-kv, d4.z, acc.z));
                 acc.w = fmaf(qv, o4.w, fmaf(-kv, d4.w, acc.w));
             }
             __syncthreads();
-            *reinterpret_cast<float4*>(&sG[r * SW + cc]) = acc;
+            *reinterpret_cast<fx4*>(&sG[r * SW + cc]) = acc;
         }
     }
     if (a.dstate0) {
@@ -515,16 +522,16 @@ __global__ __launch_bounds__(256) void bwd_grads(const BwdArgs a) {
     // dA = -strict_lower(dR Delta^T), dP = lower(dO Delta^T)
     {
         float ga[4][4] = {}, gp2[4][4] = {};
-        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        const fx4 z4 = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 2
         for (int x = 0; x < D; x += 4) {
-            float4 dr4[4], do4[4], dl4[4];
+            fx4 dr4[4], do4[4], dl4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = tr + 16 * i, t = t0 + r;
-                dr4[i] = *reinterpret_cast<const float4*>(drp + r * D + x);
-                do4[i] = t < T ? *reinterpret_cast<const float4*>(a.d_o + ((b * T + t) * a.H + h) * (long)D + x) : z4;
-                dl4[i] = *reinterpret_cast<const float4*>(&sDl[(tc + 16 * i) * LD + x]);
+                dr4[i] = *reinterpret_cast<const fx4*>(drp + r * D + x);
+                do4[i] = t < T ? *reinterpret_cast<const fx4*>(a.d_o + ((b * T + t) * a.H + h) * (long)D + x) : z4;
+                dl4[i] = *reinterpret_cast<const fx4*>(&sDl[(tc + 16 * i) * LD + x]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -589,16 +596,16 @@ __global__ __launch_bounds__(256) void bwd_grads(const BwdArgs a) {
     // dQ = diag(Gam) dO H0^T + dPL K ;  row dot (dO H0^T)_r . q_r
     {
         float x1[4][CJ] = {}, x2[4][CJ] = {};
-        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        const fx4 z4 = f4(0.f, 0.f, 0.f, 0.f);
         for (int j = 0; j < D; j += 4) {
-            float4 do4[4], hv[CJ];
+            fx4 do4[4], hv[CJ];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = t0 + tr + 16 * i;
-                do4[i] = t < T ? *reinterpret_cast<const float4*>(a.d_o + ((b * T + t) * a.H + h) * (long)D + j) : z4;
+                do4[i] = t < T ? *reinterpret_cast<const fx4*>(a.d_o + ((b * T + t) * a.H + h) * (long)D + j) : z4;
             }
 #pragma unroll
-            for (int jj = 0; jj < CJ; ++jj) hv[jj] = *reinterpret_cast<const float4*>(h0 + (tc + 16 * jj) * D + j);
+            for (int jj = 0; jj < CJ; ++jj) hv[jj] = *reinterpret_cast<const fx4*>(h0 + (tc + 16 * jj) * D + j);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -634,16 +641,16 @@ __global__ __launch_bounds__(256) void bwd_grads(const BwdArgs a) {
     {
         float y1[4][CJ] = {}, y2[4][CJ] = {}, y3[4][CJ] = {};
         for (int j = 0; j < D; j += 4) {
-            float4 dl4[4], dr4[4], gv[CJ], hv[CJ];
+            fx4 dl4[4], dr4[4], gv[CJ], hv[CJ];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                dl4[i] = *reinterpret_cast<const float4*>(&sDl[(tr + 16 * i) * LD + j]);
-                dr4[i] = *reinterpret_cast<const float4*>(drp + (tr + 16 * i) * D + j);
+                dl4[i] = *reinterpret_cast<const fx4*>(&sDl[(tr + 16 * i) * LD + j]);
+                dr4[i] = *reinterpret_cast<const fx4*>(drp + (tr + 16 * i) * D + j);
             }
 #pragma unroll
             for (int jj = 0; jj < CJ; ++jj) {
-                gv[jj] = *reinterpret_cast<const float4*>(gp + (tc + 16 * jj) * D + j);
-                hv[jj] = *reinterpret_cast<const float4*>(h0 + (tc + 16 * jj) * D + j);
+                gv[jj] = *reinterpret_cast<const fx4*>(gp + (tc + 16 * jj) * D + j);
+                hv[jj] = *reinterpret_cast<const fx4*>(h0 + (tc + 16 * jj) * D + j);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -709,7 +716,7 @@ __global__ __launch_bounds__(256) void bwd_grads(const BwdArgs a) {
     float gh = 0.f;
 #pragma unroll 4
     for (int idx = 4 * tid; idx < D * D; idx += 1024) {
-        const float4 x = *reinterpret_cast<const float4*>(gp + idx), y = *reinterpret_cast<const float4*>(h0 + idx);
+        const fx4 x = *reinterpret_cast<const fx4*>(gp + idx), y = *reinterpret_cast<const fx4*>(h0 + idx);
         gh = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, gh))));
     }
     gh = block_sum(gh, red);  // contains barriers
