@@ -161,7 +161,7 @@ template <typename In, int D>
 __global__ __launch_bounds__(256) void bwd_prep(const BwdArgs a) {
     constexpr int LD = D + 4, LC = BC + 1;
     __shared__ float sK[BC * LD], sX[BC * LD], sL[BC * LC], sTi[BC * LC];
-    __shared__ float sgam[BC], sb[BC];
+    __shared__ float sgam[BC], sb[BC], sbg[BC];
     const int tid = threadIdx.x, c = blockIdx.x, h = blockIdx.y;
     const long b = blockIdx.z, n = b * a.H + h, nc = n * a.NC + c;
     const int t0 = c * BC, T = a.T;
@@ -238,25 +238,38 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdArgs a) {
     }
     {
         float* tip = a.ti + nc * BC * BC;
-        for (int idx = tid; idx < BC * BC; idx += 256) tip[idx] = sTi[(idx / BC) * LC + idx % BC];
+        for (int idx = 4 * tid; idx < BC * BC; idx += 1024) {
+            const float* t4 = &sTi[(idx / BC) * LC + idx % BC];
+            *reinterpret_cast<fx4*>(tip + idx) = fx4{t4[0], t4[1], t4[2], t4[3]};
+        }
+        if (tid < BC) sbg[tid] = sb[tid] * __expf(sgam[tid]);
     }
-    // W = Ti diag(b Gam) K, then U = Ti diag(b) V
+    // W = Ti diag(b Gam) K, then U = Ti diag(b) V; thread rows tr + 16 i,
+    // columns tc + 16 j (4 x 8 outputs, 12 LDS reads per 32 FMA)
     load_rows<In, D, LD>(sX, a.v, b, h, t0, T, a.H);
     __syncthreads();
+    constexpr int CJ = D / 16;
     for (int pass = 0; pass < 2; ++pass) {
         const float* src = pass == 0 ? sK : sX;
+        const float* scl = pass == 0 ? sbg : sb;
         float* dst = (pass == 0 ? a.w : a.u) + nc * BC * D;
-        for (int c0 = 0; c0 < D; c0 += 16) {
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int i = 0; i < BC; ++i) {
-                const float wi = sb[i] * (pass == 0 ? __expf(sgam[i]) : 1.f);
-                const float x = wi * src[i * LD + c0 + tc];
+        float acc[4][CJ] = {};
+        for (int i = 0; i < BC; ++i) {
+            float t4[4], x8[CJ];
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) acc[ii] = fmaf(sTi[(tr + 16 * ii) * LC + i], x, acc[ii]);
-            }
+            for (int ii = 0; ii < 4; ++ii) t4[ii] = sTi[(tr + 16 * ii) * LC + i];
+            const float sc = scl[i];
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) dst[(tr + 16 * ii) * D + c0 + tc] = acc[ii];
+            for (int jj = 0; jj < CJ; ++jj) x8[jj] = sc * src[i * LD + tc + 16 * jj];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+                for (int jj = 0; jj < CJ; ++jj) acc[ii][jj] = fmaf(t4[ii], x8[jj], acc[ii][jj]);
         }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+            for (int jj = 0; jj < CJ; ++jj) dst[(tr + 16 * ii) * D + tc + 16 * jj] = acc[ii][jj];
     }
 }
 
