@@ -25,8 +25,11 @@
 //   SUM mode: state columns = [value | identity] (2 d_v); starts from [0 | I]
 //             and stores the segment's affine map [R | M] (H_end = M H_start + R).
 //
-// Matrix-core operands are fp16 (bf16 inputs are exact in fp16 at these
-// magnitudes), accumulation fp32; b V, b Gam K, U and the state stay fp32.
+// Matrix-core products of two inputs (the Gram tiles, the identity products
+// that transpose K and V) take the bf16 inputs as stored; every product with a
+// computed operand (the state, Delta, -W, the decayed tiles) runs on fp16
+// operands, Q converted once per chunk.  Accumulation is fp32; b V, b Gam K, U
+// and the state stay fp32.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 #include "gdn_mfma.h"
@@ -40,6 +43,20 @@ constexpr int FC = 64;  // chunk length
 using H8 = f16x8;
 using H4 = f16x4;
 using MF = Mfma<_Float16>;
+
+// Raw bf16 operands: products of two input tensors (the Gram tiles) and the
+// identity products that transpose V and K take the inputs as they are stored,
+// with no conversion; only Q, which also meets the fp16 state, is converted.
+typedef __bf16 B8 __attribute__((ext_vector_type(8)));
+typedef short B4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma_b32(B8 a, B8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_b16(B4 a, B4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ B8 ldb8(const uint16_t* p) { return *reinterpret_cast<const B8*>(p); }
+__device__ __forceinline__ B4 ldb4(const uint16_t* p) { return *reinterpret_cast<const B4*>(p); }
 
 __device__ __forceinline__ H8 bf16x8_to_f16(uint4 w) {
     const uint32_t u[4] = {w.x, w.y, w.z, w.w};
@@ -166,10 +183,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     constexpr int LA = FC + 8;            // row stride of [*][64] tiles
     constexpr int NL = FC * D / 8 / NTH;  // 8-element input groups per thread per tensor
 
-    __shared__ __align__(16) _Float16 sK[FC * LD];
-    __shared__ __align__(16) _Float16 sQ[OUT ? FC * LD : 8];
+    __shared__ __align__(16) uint16_t sK[FC * LD];             // raw bf16
+    __shared__ __align__(16) _Float16 sQ[OUT ? FC * LD : 8];    // fp16 (Q H0)
+    __shared__ __align__(16) uint16_t sQb[OUT ? FC * LD : 8];   // raw bf16 (Q K^T)
     __shared__ __align__(16) _Float16 sW[FC * LD];      // -W [t][key]
-    __shared__ __align__(16) _Float16 sV[FC * LD];
+    __shared__ __align__(16) uint16_t sV[FC * LD];             // raw bf16
     __shared__ __align__(16) _Float16 sKT[D * LA];      // (diag(e) K)^T [key][t] (swizzled)
     __shared__ __align__(16) _Float16 sA[FC * LA];      // -A off-diagonal, (T_bb - I) diagonal blocks
     __shared__ __align__(16) _Float16 sP[OUT ? FC * LA : 8];
@@ -260,9 +278,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int idx = tid + NTH * i, r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-            *reinterpret_cast<H8*>(&sK[r * LD + c8]) = bf16x8_to_f16(rk[i]);
-            if (OUT) *reinterpret_cast<H8*>(&sQ[r * LD + c8]) = bf16x8_to_f16(rq[i]);
-            *reinterpret_cast<H8*>(&sV[r * LD + c8]) = bf16x8_to_f16(rv[i]);
+            *reinterpret_cast<uint4*>(&sK[r * LD + c8]) = rk[i];
+            if (OUT) {
+                *reinterpret_cast<H8*>(&sQ[r * LD + c8]) = bf16x8_to_f16(rq[i]);
+                *reinterpret_cast<uint4*>(&sQb[r * LD + c8]) = rq[i];
+            }
+            *reinterpret_cast<uint4*>(&sV[r * LD + c8]) = rv[i];
         }
         if (wave == 0) {
             const float bv = rb;
@@ -295,8 +316,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             f32x4 acc = zero4();  // G = K_b K_b^T, symmetric
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk) {
-                const H8 a = ld8<_Float16>(&sK[(16 * bb + lc) * LD + 32 * kk + 8 * lg]);
-                acc = MF::k32(a, a, acc);
+                const B8 a = ldb8(&sK[(16 * bb + lc) * LD + 32 * kk + 8 * lg]);
+                acc = mfma_b32(a, a, acc);
             }
             const f32x4 gr = *reinterpret_cast<const f32x4*>(&sgam[16 * bb + 4 * lg]);
             const f32x4 br = *reinterpret_cast<const f32x4*>(&sbeta[16 * bb + 4 * lg]);
@@ -337,12 +358,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 mi = k < 1 ? 1 : k < 3 ? 2 : 3;
                 ni = k - (mi * (mi - 1)) / 2;
             };
-            auto tile_acc = [&](const _Float16* X, int mi, int ni) {
+            auto tile_acc = [&](const uint16_t* X, int mi, int ni) {
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int kk = 0; kk < D / 32; ++kk)
-                    acc = MF::k32(ld8<_Float16>(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]),
-                                  ld8<_Float16>(&X[(16 * mi + lc) * LD + 32 * kk + 8 * lg]), acc);
+                    acc = mfma_b32(ldb8(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]),
+                                   ldb8(&X[(16 * mi + lc) * LD + 32 * kk + 8 * lg]), acc);
                 return acc;
             };
             // off-diagonal: exp(gam_r - gam_i) = sRF[r] sCF[mi][i]; -A (K K^T) or P (Q K^T)
@@ -374,10 +395,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                     const f32x4 c0 = tile_acc(sK, m0, n0);
                     if (OUT) {
                         off_coords(wave - 4, m1, n1);
-                        const f32x4 c1 = tile_acc(sQ, m1, n1);
+                        const f32x4 c1 = tile_acc(sQb, m1, n1);
                         const bool third_kk = wave < 6;
                         off_coords(third_kk ? wave : wave - 2, m2, n2);
-                        const f32x4 c2 = tile_acc(third_kk ? sK : sQ, m2, n2);
+                        const f32x4 c2 = tile_acc(third_kk ? sK : sQb, m2, n2);
                         store_off(true, m0, n0, c0);
                         store_off(false, m1, n1, c1);
                         if (third_kk) store_off(true, m2, n2, c2);
@@ -390,7 +411,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                         }
                     }
                 } else if (OUT) {
-                    store_qdiag(wave, tile_acc(sQ, wave, wave));
+                    store_qdiag(wave, tile_acc(sQb, wave, wave));
                 }
             } else {
                 // generic: the off-diagonal K K^T tiles, then (OUT) the off-diagonal
@@ -401,9 +422,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                         int mi, ni;
                         off_coords(tt % 6, mi, ni);
                         const bool kq = tt < 6;
-                        store_off(kq, mi, ni, tile_acc(kq ? sK : sQ, mi, ni));
+                        store_off(kq, mi, ni, tile_acc(kq ? sK : sQb, mi, ni));
                     } else {
-                        store_qdiag(tt - 12, tile_acc(sQ, tt - 12, tt - 12));
+                        store_qdiag(tt - 12, tile_acc(sQb, tt - 12, tt - 12));
                     }
                 }
             }
@@ -431,17 +452,17 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         constexpr int NR = 2;  // right-hand-side tiles: U tile w, -W tile w
         f32x4 res[NR][4];
         {
-            H4 ident;
+            B4 ident;  // bf16 1.0 = 0x3f80
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ident[e] = static_cast<_Float16>(4 * lg + e == lc ? 1.f : 0.f);
+            for (int e = 0; e < 4; ++e) ident[e] = (short)(4 * lg + e == lc ? 0x3f80 : 0);
             H4 xh[NR][4];
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
                 const f32x4 fb = *reinterpret_cast<const f32x4*>(&sbeta[16 * bb + 4 * lg]);
                 const f32x4 fg = *reinterpret_cast<const f32x4*>(&sBG[16 * bb + 4 * lg]);
                 const f32x4 fe = *reinterpret_cast<const f32x4*>(&sE[16 * bb + 4 * lg]);
-                const f32x4 vt = MF::k16(ld4<_Float16>(&sV[(16 * bb + lc) * LD + colw + 4 * lg]), ident, zero4());
-                const f32x4 kt = MF::k16(ld4<_Float16>(&sK[(16 * bb + lc) * LD + colw + 4 * lg]), ident, zero4());
+                const f32x4 vt = mfma_b16(ldb4(&sV[(16 * bb + lc) * LD + colw + 4 * lg]), ident, zero4());
+                const f32x4 kt = mfma_b16(ldb4(&sK[(16 * bb + lc) * LD + colw + 4 * lg]), ident, zero4());
                 st4<_Float16>(&sKT[tsw<LA>(colw + lc, 16 * bb + 4 * lg)], cvt4<_Float16>(fe * kt));
                 f32x4 acc[NR];
                 acc[0] = fb * vt;
