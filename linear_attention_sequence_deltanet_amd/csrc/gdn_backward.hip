@@ -29,21 +29,23 @@
 // dO_r.(Q H0)_r = (dO H0^T)_r.q_r, dR_r.(K H0)_r = (dR H0^T)_r.k_r and
 // (K G)_r.Delta_r = (Delta G^T)_r.k_r.
 //
-// Kernels (all fp32, operands staged in LDS):
+// Kernels (all fp32 arithmetic):
 //   bwd_prep       per chunk, in parallel: gates, the Gram and decayed QK^T
 //                  tiles, Ti by forward substitution, W and U;
 //   bwd_fwd_chain  per (b, h, 8-column state slice), chunks in order: stores
 //                  every chunk's start state and Delta;
 //   bwd_bwd_chain  per (b, h, 8-column slice), chunks in reverse: stores every
 //                  chunk's end gradient G and dR, writes dS_0;
-//   bwd_grads      per chunk, in parallel: dq, dk, dv, dbeta, dg.
+//   bwd_grads      per chunk, in parallel, on fp32 matrix-core products:
+//                  dq, dk, dv, dbeta, dg.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 namespace {
 
-constexpr int BC = 64;  // chunk length
+constexpr int BC = 64;   // chunk length
+constexpr int SCN = 4;   // per-chunk gate rows in the workspace: Gam, e, b, gam
 
 // Native vector types for register-held data: HIP's fx4 / ux4 structs are
 // copied through memcpy, which keeps register arrays of them in scratch memory.
@@ -68,7 +70,7 @@ struct BwdArgs {
     float* dbeta;
     float* dstate0;        // or null
     // workspace, per series n = b H + h and chunk c (index n * NC + c):
-    float* sc;   // [.][3][BC]: Gam, e, b
+    float* sc;   // [.][SCN][BC]: Gam, e, b, gam
     float* ti;   // [.][BC][BC]
     float* pm;   // [.][BC][BC]  lower(L o QK^T)
     float* lkk;  // [.][BC][BC]  strict_lower(L o KK^T)
@@ -88,16 +90,16 @@ __device__ __forceinline__ float ld(const void* p, long i) {
 
 // Chunk rows [t0, t0 + BC) of an input [B][T][H][D] (bf16 or fp32), 16 bytes
 // per load, held in registers as raw words until stored (zeros past T).
-template <typename In, int D>
+template <typename In, int D, int NT = 256>
 struct RowRegs {
     static constexpr int VPL = 16 / sizeof(In);      // values per 16-byte load
     static constexpr int PPR = D / VPL;              // loads per row
-    static constexpr int N = BC * PPR / 256;         // loads per thread
+    static constexpr int N = BC * PPR / NT;          // loads per thread
     ux4 r[N];
     __device__ __forceinline__ void load(const void* src, long b, int h, int t0, int T, int H) {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int p = threadIdx.x + 256 * i, row = p / PPR, col = (p % PPR) * VPL, t = t0 + row;
+            const int p = threadIdx.x + NT * i, row = p / PPR, col = (p % PPR) * VPL, t = t0 + row;
             r[i] = t < T ? *reinterpret_cast<const ux4*>(static_cast<const In*>(src) +
                                                            ((b * T + t) * H + h) * (long)D + col)
                          : ux4{0u, 0u, 0u, 0u};
@@ -108,7 +110,7 @@ struct RowRegs {
     __device__ __forceinline__ void store(float* dst) const {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int p = threadIdx.x + 256 * i, row = p / PPR, col = (p % PPR) * VPL;
+            const int p = threadIdx.x + NT * i, row = p / PPR, col = (p % PPR) * VPL;
             float* d = dst + row * LD + col;
             if constexpr (sizeof(In) == 4) {
                 *reinterpret_cast<fx4*>(d) = __builtin_bit_cast(fx4, r[i]);
@@ -180,10 +182,11 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdArgs a) {
     }
     __syncthreads();
     if (tid < BC) {
-        float* scp = a.sc + nc * 3 * BC;
+        float* scp = a.sc + nc * SCN * BC;
         scp[tid] = __expf(sgam[tid]);
         scp[BC + tid] = __expf(sgam[BC - 1] - sgam[tid]);
         scp[2 * BC + tid] = sb[tid];
+        scp[3 * BC + tid] = sgam[tid];
     }
     // KK and QK tiles: thread rows tr + 16 i, columns tc + 16 j
     const int tr = tid / 16, tc = tid % 16;
@@ -320,7 +323,7 @@ __global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
         rw.load(a.w + nc * BC * D, D);
         rk.load(a.k, b, h, c * BC, a.T, a.H);
         if (tid < BC * SW / 4) ru = *reinterpret_cast<const fx4*>(a.u + (nc * BC + tid / 2) * D + c0 + (tid % 2) * 4);
-        if (tid < BC) re = a.sc[nc * 3 * BC + BC + tid];
+        if (tid < BC) re = a.sc[nc * SCN * BC + BC + tid];
     };
     fetch(0);
     for (int c = 0; c < a.NC; ++c) {
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
         rk.template store<LD>(sK);
         if (tid < BC * SW / 4) *reinterpret_cast<fx4*>(&sU[(tid / 2) * SW + (tid % 2) * 4]) = ru;
         if (tid < BC) se[tid] = re;
-        if (tid == 0) sgc = a.sc[nc * 3 * BC + BC - 1];
+        if (tid == 0) sgc = a.sc[nc * SCN * BC + BC - 1];
         for (int idx = tid; idx < D * SW; idx += 256)
             a.hs[(nc * D + idx / SW) * D + c0 + idx % SW] = sH[idx];
         __syncthreads();
@@ -400,7 +403,7 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
             rdo = t < T ? *reinterpret_cast<const fx4*>(a.d_o + ((b * T + t) * a.H + h) * (long)D + c0 + (tid % 2) * 4)
                         : f4(0.f, 0.f, 0.f, 0.f);
         }
-        if (tid < 3 * BC / 4) rsc = *reinterpret_cast<const fx4*>(a.sc + nc * 3 * BC + 4 * tid);
+        if (tid < 3 * BC / 4) rsc = *reinterpret_cast<const fx4*>(a.sc + nc * SCN * BC + 4 * tid);
     };
     fetch(a.NC - 1);
     for (int c = a.NC - 1; c >= 0; --c) {
@@ -483,294 +486,333 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float block_sum(float x, float* red) {
-    // 256 threads
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    __syncthreads();
-    if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = x;
-    __syncthreads();
-    return red[0] + red[1] + red[2] + red[3];
+// fp32 matrix-core product step: c += a b over one K = 4 slice, lane (l % 16,
+// l / 16) giving A[l % 16][k] and B[k][l % 16] for the slice's k = l / 16.
+__device__ __forceinline__ fx4 mma4(float a, float b, fx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Sum over the 16 lanes of each lane group (the c index of a 16x16 tile).
+__device__ __forceinline__ float group16_sum(float x) {
+    x += __shfl_xor(x, 8, 16);
+    x += __shfl_xor(x, 4, 16);
+    x += __shfl_xor(x, 2, 16);
+    x += __shfl_xor(x, 1, 16);
+    return x;
+}
+
+// bwd_grads: one workgroup of D/16 waves per (chunk, head).  Every product is
+// an fp32 matrix-core product of 16x16 tiles (exact fp32 operands).  Layout:
+// tile fragments follow the 16x16x4 instruction, lane l = 16 g + c holds
+// A row c / B column c at contraction index k = 4 (step) + g within a 16-wide
+// slice, or k = 8 g + step within a 32-wide slice of a row-major operand, which
+// lets a lane read 8 consecutive floats; the output holds rows 4 g + e, column c.
+//   phase 1  (LDS: dO, Delta, dR)   the ten lower 16x16 tiles of dR Delta^T and
+//            dO Delta^T (masked, their row/column sums for db and dgam, then
+//            dPL = dP o L and dAs = dA o (b_r L) kept in registers), and the
+//            state products dO H0^T, Delta G^T, dR H0^T: wave w owns key
+//            columns [16 w, 16 w + 16) of all 64 rows, H0 and G rows read from
+//            the workspace once per workgroup;
+//   phase 2  (LDS: K, Q, dPL, dAs)  dPL K, dPL^T Q and (dAs + dAs^T) K for
+//            the same columns, then dq, dk and the row dots.
 template <typename In, int D>
-__global__ __launch_bounds__(256) void bwd_grads(const BwdArgs a) {
-    constexpr int LD = D + 4, LC = BC + 1;
-    constexpr int CJ = D / 16;  // output columns per thread
-    __shared__ __attribute__((aligned(16))) float sK[BC * LD], sQ[BC * LD], sDl[BC * LD];
-    __shared__ float sdA[BC * LC], sdP[BC * LC];
-    __shared__ float sgam[BC], sGam[BC], se[BC], sb[BC], sdg[BC], sdb[BC], red[8];
-    __shared__ float sdot[3][BC * 17];  // per-thread-column partial row dots
-    const int tid = threadIdx.x, c = blockIdx.x, h = blockIdx.y;
+__global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
+    constexpr int NW = D / 16, NT = 64 * NW;
+    constexpr int LD = D + 4, LC = BC + 4;
+    constexpr int KB = D / 32;            // 32-wide contraction slices over D
+    constexpr int RT = BC / 16;           // row tiles of a chunk
+    constexpr int NPAIR = RT * (RT + 1) / 2;
+    constexpr int PPW = (NPAIR + NW - 1) / NW;  // lower tiles per wave
+    constexpr int S1 = 3 * BC * LD, S2 = 2 * BC * LD + 2 * BC * LC;
+    __shared__ __attribute__((aligned(16))) float smem[S1 > S2 ? S1 : S2];
+    float* const sdO = smem;
+    float* const sDl = smem + BC * LD;
+    float* const sdR = smem + 2 * BC * LD;
+    float* const sK = smem;
+    float* const sQ = smem + BC * LD;
+    float* const sPL = smem + 2 * BC * LD;
+    float* const sAS = sPL + BC * LC;
+    __shared__ float sgam[BC], sGam[BC], se[BC], sb[BC], sdg[BC], sdb[BC], sq1[BC], sk1[BC], sk2[BC];
+    __shared__ float red[NW];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lg = lane >> 4, lc = lane & 15;
+    const int c = blockIdx.x, h = blockIdx.y;
     const long b = blockIdx.z, n = b * a.H + h, nc = n * a.NC + c;
     const int t0 = c * BC, T = a.T;
-    const int tr = tid / 16, tc = tid % 16;
-
-    if (tid < BC) {
-        const float* scp = a.sc + nc * 3 * BC;
-        sGam[tid] = scp[tid];
-        se[tid] = scp[BC + tid];
-        sb[tid] = scp[2 * BC + tid];
-    }
-    load_rows<In, D, LD>(sK, a.k, b, h, t0, T, a.H);
-    load_rows<In, D, LD>(sQ, a.q, b, h, t0, T, a.H);
+    const long HD = (long)a.H * D;
+    const long row0 = (b * T + t0) * HD + (long)h * D;  // element offset of chunk row 0
+    const float* scp = a.sc + nc * SCN * BC;
     const float* dlp = a.dl + nc * BC * D;
     const float* drp = a.dr + nc * BC * D;
     const float* h0 = a.hs + nc * D * D;
     const float* gp = a.gs + nc * D * D;
-    {
-        BlockRegs<BC, D> rd;
-        rd.load(dlp, D);
-        rd.template store<LD>(sDl);
-    }
-    __syncthreads();
-    // gam: the same serial fp32 cumsum as bwd_prep, so L matches its P and lkk
-    if (tid == 0) {
-        float s = 0.f;
-        for (int r = 0; r < BC; ++r) {
-            const int t = t0 + r;
-            s += t < T ? a.g[(b * T + t) * a.H + h] : 0.f;
-            sgam[r] = s;
-        }
-    }
-    // dA = -strict_lower(dR Delta^T), dP = lower(dO Delta^T)
-    {
-        float ga[4][4] = {}, gp2[4][4] = {};
-        const fx4 z4 = f4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 2
-        for (int x = 0; x < D; x += 4) {
-            fx4 dr4[4], do4[4], dl4[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = tr + 16 * i, t = t0 + r;
-                dr4[i] = *reinterpret_cast<const fx4*>(drp + r * D + x);
-                do4[i] = t < T ? *reinterpret_cast<const fx4*>(a.d_o + ((b * T + t) * a.H + h) * (long)D + x) : z4;
-                dl4[i] = *reinterpret_cast<const fx4*>(&sDl[(tc + 16 * i) * LD + x]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    ga[i][j] = fmaf(dr4[i].x, dl4[j].x, fmaf(dr4[i].y, dl4[j].y, fmaf(dr4[i].z, dl4[j].z, fmaf(dr4[i].w, dl4[j].w, ga[i][j]))));
-                    gp2[i][j] = fmaf(do4[i].x, dl4[j].x, fmaf(do4[i].y, dl4[j].y, fmaf(do4[i].z, dl4[j].z, fmaf(do4[i].w, dl4[j].w, gp2[i][j]))));
-                }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = tr + 16 * i, s = tc + 16 * j;
-                sdA[r * LC + s] = s < r ? -ga[i][j] : 0.f;
-                sdP[r * LC + s] = s <= r ? gp2[i][j] : 0.f;
-            }
-    }
-    __syncthreads();
-    // row / column sums of dP o P and dA o A and db's Gram term, from this
-    // thread's 16 entries (rows tr + 16 i, columns tc + 16 j) into LDS atomics;
-    // then dP <- dP o L, dA <- dA o (b_r L)
-    if (tid < BC) sdg[tid] = 0.f, sdb[tid] = 0.f;
-    __syncthreads();
-    {
-        const float* pmp = a.pm + nc * BC * BC;
-        const float* lkp = a.lkk + nc * BC * BC;
-        float pv[4][4], lv[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = tr + 16 * i, s = tc + 16 * j;
-                pv[i][j] = pmp[r * BC + s];
-                lv[i][j] = lkp[r * BC + s];
-            }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = tr + 16 * i;
-            float rs = 0.f, db3 = 0.f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int s = tc + 16 * j;
-                const float x = sdP[r * LC + s] * pv[i][j] + sdA[r * LC + s] * sb[r] * lv[i][j];
-                rs += x;
-                atomicAdd(&sdg[s], -x);
-                db3 = fmaf(sdA[r * LC + s], lv[i][j], db3);
-            }
-            atomicAdd(&sdg[r], rs);
-            atomicAdd(&sdb[r], db3);
-        }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < BC * BC; idx += 256) {
-        const int r = idx / BC, s = idx % BC;
-        const float L = s <= r ? __expf(sgam[r] - sgam[s]) : 0.f;
-        sdP[r * LC + s] *= L;
-        sdA[r * LC + s] *= sb[r] * L;
-    }
-    __syncthreads();
 
-    // dQ = diag(Gam) dO H0^T + dPL K ;  row dot (dO H0^T)_r . q_r
+    if (tid < BC) {
+        sGam[tid] = scp[tid];
+        se[tid] = scp[BC + tid];
+        sb[tid] = scp[2 * BC + tid];
+        sgam[tid] = scp[3 * BC + tid];
+        sdg[tid] = 0.f, sdb[tid] = 0.f, sq1[tid] = 0.f, sk1[tid] = 0.f, sk2[tid] = 0.f;
+    }
+    // ---- phase 0: dO, Delta, dR into LDS; dv = b dR and the row dots dR.v
+    constexpr int NF = BC * D / 4 / NT;  // float4 per thread per matrix
+    float vdp[NF];
     {
-        float x1[4][CJ] = {}, x2[4][CJ] = {};
         const fx4 z4 = f4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < D; j += 4) {
-            fx4 do4[4], hv[CJ];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = t0 + tr + 16 * i;
-                do4[i] = t < T ? *reinterpret_cast<const fx4*>(a.d_o + ((b * T + t) * a.H + h) * (long)D + j) : z4;
+        for (int i = 0; i < NF; ++i) {
+            const int idx = tid + NT * i, r = idx / (D / 4), c4 = (idx % (D / 4)) * 4;
+            const bool ok = t0 + r < T;
+            const long gi = row0 + r * HD + c4;
+            const fx4 o4 = ok ? *reinterpret_cast<const fx4*>(a.d_o + gi) : z4;
+            const fx4 d4 = *reinterpret_cast<const fx4*>(dlp + r * D + c4);
+            const fx4 r4 = *reinterpret_cast<const fx4*>(drp + r * D + c4);
+            *reinterpret_cast<fx4*>(&sdO[r * LD + c4]) = o4;
+            *reinterpret_cast<fx4*>(&sDl[r * LD + c4]) = d4;
+            *reinterpret_cast<fx4*>(&sdR[r * LD + c4]) = r4;
+            vdp[i] = 0.f;
+            if (ok) {
+                const float br = scp[2 * BC + r];
+                *reinterpret_cast<fx4*>(a.dv + gi) = f4(br * r4.x, br * r4.y, br * r4.z, br * r4.w);
+                vdp[i] = r4.x * ld<In>(a.v, gi) + r4.y * ld<In>(a.v, gi + 1) +
+                         r4.z * ld<In>(a.v, gi + 2) + r4.w * ld<In>(a.v, gi + 3);
             }
-#pragma unroll
-            for (int jj = 0; jj < CJ; ++jj) hv[jj] = *reinterpret_cast<const fx4*>(h0 + (tc + 16 * jj) * D + j);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int jj = 0; jj < CJ; ++jj)
-                    x1[i][jj] = fmaf(do4[i].x, hv[jj].x, fmaf(do4[i].y, hv[jj].y, fmaf(do4[i].z, hv[jj].z, fmaf(do4[i].w, hv[jj].w, x1[i][jj]))));
-        }
-        for (int s = 0; s < BC; ++s) {
-            float p4[4], kv[CJ];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p4[i] = sdP[(tr + 16 * i) * LC + s];
-#pragma unroll
-            for (int jj = 0; jj < CJ; ++jj) kv[jj] = sK[s * LD + tc + 16 * jj];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int jj = 0; jj < CJ; ++jj) x2[i][jj] = fmaf(p4[i], kv[jj], x2[i][jj]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = tr + 16 * i, t = t0 + r;
-            float dot = 0.f;
-#pragma unroll
-            for (int jj = 0; jj < CJ; ++jj) {
-                const int x = tc + 16 * jj;
-                dot = fmaf(x1[i][jj], sQ[r * LD + x], dot);
-                if (t < T) a.dq[((b * T + t) * a.H + h) * (long)D + x] = fmaf(sGam[r], x1[i][jj], x2[i][jj]);
-            }
-            sdot[0][r * 17 + tc] = dot;
         }
     }
-    // dK = dPL^T Q + diag(e) Delta G^T - diag(b Gam) dR H0^T + (dAs + dAs^T) K
-    // row dots (Delta G^T)_r . k_r and (dR H0^T)_r . k_r
-    {
-        float y1[4][CJ] = {}, y2[4][CJ] = {}, y3[4][CJ] = {};
-        for (int j = 0; j < D; j += 4) {
-            fx4 dl4[4], dr4[4], gv[CJ], hv[CJ];
+    // K and Q for phase 2, held as raw words
+    RowRegs<In, D, NT> rk, rq;
+    rk.load(a.k, b, h, t0, T, a.H);
+    rq.load(a.q, b, h, t0, T, a.H);
+    // P and the decayed K K^T at this wave's lower tiles (output layout)
+    float pv[PPW][4], lv[PPW][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                dl4[i] = *reinterpret_cast<const fx4*>(&sDl[(tr + 16 * i) * LD + j]);
-                dr4[i] = *reinterpret_cast<const fx4*>(drp + (tr + 16 * i) * D + j);
+    for (int p = 0; p < PPW; ++p) {
+        const int pi = wave + NW * p;
+        if (pi < NPAIR) {
+            int tr = 0;
+            while ((tr + 1) * (tr + 2) / 2 <= pi) ++tr;
+            const int sc = pi - tr * (tr + 1) / 2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * tr + 4 * lg + e, s = 16 * sc + lc;
+                pv[p][e] = a.pm[nc * BC * BC + r * BC + s];
+                lv[p][e] = a.lkk[nc * BC * BC + r * BC + s];
             }
+        }
+    }
+    __syncthreads();
 #pragma unroll
-            for (int jj = 0; jj < CJ; ++jj) {
-                gv[jj] = *reinterpret_cast<const fx4*>(gp + (tc + 16 * jj) * D + j);
-                hv[jj] = *reinterpret_cast<const fx4*>(h0 + (tc + 16 * jj) * D + j);
-            }
+    for (int i = 0; i < NF; ++i) {
+        // 32 (d = 128) or 16 (d = 64) consecutive lanes share a row
+        float x = vdp[i];
+        for (int off = D / 8; off > 0; off >>= 1) x += __shfl_xor(x, off, D / 4);
+        if (lane % (D / 4) == 0) atomicAdd(&sdb[(tid + NT * i) / (D / 4)], x);
+    }
+
+    // ---- phase 1a: lower tiles of dR Delta^T and dO Delta^T
+    fx4 plt[PPW], ast[PPW];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+    for (int p = 0; p < PPW; ++p) {
+        const int pi = wave + NW * p;
+        plt[p] = f4(0.f, 0.f, 0.f, 0.f), ast[p] = plt[p];
+        if (pi < NPAIR) {
+            int tr = 0;
+            while ((tr + 1) * (tr + 2) / 2 <= pi) ++tr;
+            const int sc = pi - tr * (tr + 1) / 2;
+            fx4 ga = f4(0.f, 0.f, 0.f, 0.f), gq = ga;
 #pragma unroll
-                for (int jj = 0; jj < CJ; ++jj) {
-                    y1[i][jj] = fmaf(dl4[i].x, gv[jj].x, fmaf(dl4[i].y, gv[jj].y, fmaf(dl4[i].z, gv[jj].z, fmaf(dl4[i].w, gv[jj].w, y1[i][jj]))));
-                    y2[i][jj] = fmaf(dr4[i].x, hv[jj].x, fmaf(dr4[i].y, hv[jj].y, fmaf(dr4[i].z, hv[jj].z, fmaf(dr4[i].w, hv[jj].w, y2[i][jj]))));
+            for (int kb = 0; kb < KB; ++kb) {
+                const int off = 32 * kb + 8 * lg;
+                const float* pr = &sdR[(16 * tr + lc) * LD + off];
+                const float* po = &sdO[(16 * tr + lc) * LD + off];
+                const float* pd = &sDl[(16 * sc + lc) * LD + off];
+                const fx4 r0 = *reinterpret_cast<const fx4*>(pr), r1 = *reinterpret_cast<const fx4*>(pr + 4);
+                const fx4 o0 = *reinterpret_cast<const fx4*>(po), o1 = *reinterpret_cast<const fx4*>(po + 4);
+                const fx4 d0 = *reinterpret_cast<const fx4*>(pd), d1 = *reinterpret_cast<const fx4*>(pd + 4);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    ga = mma4(r0[s], d0[s], ga);
+                    gq = mma4(o0[s], d0[s], gq);
                 }
-        }
-        for (int s = 0; s < BC; ++s) {
-            float p4[4], a4[4], qv[CJ], kv[CJ];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = tr + 16 * i;
-                p4[i] = sdP[s * LC + r];
-                a4[i] = sdA[r * LC + s] + sdA[s * LC + r];
+                for (int s = 0; s < 4; ++s) {
+                    ga = mma4(r1[s], d1[s], ga);
+                    gq = mma4(o1[s], d1[s], gq);
+                }
             }
+            // masks; row / column sums of dP o P and dA o A, db's Gram term
+            float cs = 0.f;
+            const int s = 16 * sc + lc;
 #pragma unroll
-            for (int jj = 0; jj < CJ; ++jj) {
-                qv[jj] = sQ[s * LD + tc + 16 * jj];
-                kv[jj] = sK[s * LD + tc + 16 * jj];
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * tr + 4 * lg + e;
+                const float dpm = s <= r ? gq[e] : 0.f;
+                const float dam = s < r ? -ga[e] : 0.f;
+                const float x = dpm * pv[p][e] + dam * sb[r] * lv[p][e];
+                cs += x;
+                const float rs = group16_sum(x), d3 = group16_sum(dam * lv[p][e]);
+                if (lc == 0) atomicAdd(&sdg[r], rs), atomicAdd(&sdb[r], d3);
+                const float L = s <= r ? __expf(sgam[r] - sgam[s]) : 0.f;
+                plt[p][e] = dpm * L;
+                ast[p][e] = dam * sb[r] * L;
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int jj = 0; jj < CJ; ++jj)
-                    y3[i][jj] = fmaf(p4[i], qv[jj], fmaf(a4[i], kv[jj], y3[i][jj]));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = tr + 16 * i, t = t0 + r;
-            float d1 = 0.f, d2 = 0.f;
-#pragma unroll
-            for (int jj = 0; jj < CJ; ++jj) {
-                const int x = tc + 16 * jj;
-                const float kx = sK[r * LD + x];
-                d1 = fmaf(y1[i][jj], kx, d1);
-                d2 = fmaf(y2[i][jj], kx, d2);
-                const float v = y3[i][jj] + se[r] * y1[i][jj] - sb[r] * sGam[r] * y2[i][jj];
-                if (t < T) a.dk[((b * T + t) * a.H + h) * (long)D + x] = v;
-            }
-            sdot[1][r * 17 + tc] = d1;
-            sdot[2][r * 17 + tc] = d2;
+            cs += __shfl_xor(cs, 16);
+            cs += __shfl_xor(cs, 32);
+            if (lg == 0) atomicAdd(&sdg[s], -cs);
         }
     }
-    // dV = diag(b) dR and the row dot dR_r . v_r (into sdb)
-    float vd[4] = {0.f, 0.f, 0.f, 0.f};
+
+    // ---- phase 1b: state products for key columns [16 wave, 16 wave + 16)
+    fx4 x1q[RT], x1k[RT], x2k[RT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = tr + 16 * i, t = t0 + r;
+    for (int t = 0; t < RT; ++t) x1q[t] = f4(0.f, 0.f, 0.f, 0.f), x1k[t] = x1q[t], x2k[t] = x1q[t];
+    float gh = 0.f;
+    {
+        const float* hrow = h0 + (16 * wave + lc) * D + 8 * lg;
+        const float* grow = gp + (16 * wave + lc) * D + 8 * lg;
+        fx4 hb0 = *reinterpret_cast<const fx4*>(hrow), hb1 = *reinterpret_cast<const fx4*>(hrow + 4);
+        fx4 gb0 = *reinterpret_cast<const fx4*>(grow), gb1 = *reinterpret_cast<const fx4*>(grow + 4);
 #pragma unroll
-        for (int jj = 0; jj < CJ; ++jj) {
-            const int x = tc + 16 * jj;
-            const float drv = drp[r * D + x];
-            if (t < T) {
-                const long gi = ((b * T + t) * a.H + h) * (long)D + x;
-                a.dv[gi] = sb[r] * drv;
-                vd[i] = fmaf(drv, ld<In>(a.v, gi), vd[i]);
+        for (int kb = 0; kb < KB; ++kb) {
+            const fx4 h0c = hb0, h1c = hb1, g0c = gb0, g1c = gb1;
+            if (kb + 1 < KB) {
+                hb0 = *reinterpret_cast<const fx4*>(hrow + 32 * (kb + 1));
+                hb1 = *reinterpret_cast<const fx4*>(hrow + 32 * (kb + 1) + 4);
+                gb0 = *reinterpret_cast<const fx4*>(grow + 32 * (kb + 1));
+                gb1 = *reinterpret_cast<const fx4*>(grow + 32 * (kb + 1) + 4);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) gh = fmaf(h0c[s], g0c[s], fmaf(h1c[s], g1c[s], gh));
+            const int off = 32 * kb + 8 * lg;
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                const int ro = (16 * t + lc) * LD + off;
+                const fx4 o0 = *reinterpret_cast<const fx4*>(&sdO[ro]), o1 = *reinterpret_cast<const fx4*>(&sdO[ro + 4]);
+                const fx4 d0 = *reinterpret_cast<const fx4*>(&sDl[ro]), d1 = *reinterpret_cast<const fx4*>(&sDl[ro + 4]);
+                const fx4 r0 = *reinterpret_cast<const fx4*>(&sdR[ro]), r1 = *reinterpret_cast<const fx4*>(&sdR[ro + 4]);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    x1q[t] = mma4(o0[s], h0c[s], x1q[t]);
+                    x1k[t] = mma4(d0[s], g0c[s], x1k[t]);
+                    x2k[t] = mma4(r0[s], h0c[s], x2k[t]);
+                }
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    x1q[t] = mma4(o1[s], h1c[s], x1q[t]);
+                    x1k[t] = mma4(d1[s], g1c[s], x1k[t]);
+                    x2k[t] = mma4(r1[s], h1c[s], x2k[t]);
+                }
+            }
+        }
+    }
+    __syncthreads();  // dO, Delta, dR no longer read
+
+    // ---- phase 2: K, Q, dPL, dAs into LDS (lower tiles; the upper ones are
+    // never read)
+    rk.template store<LD>(sK);
+    rq.template store<LD>(sQ);
+#pragma unroll
+    for (int p = 0; p < PPW; ++p) {
+        const int pi = wave + NW * p;
+        if (pi < NPAIR) {
+            int tr = 0;
+            while ((tr + 1) * (tr + 2) / 2 <= pi) ++tr;
+            const int sc = pi - tr * (tr + 1) / 2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int o = (16 * tr + 4 * lg + e) * LC + 16 * sc + lc;
+                sPL[o] = plt[p][e];
+                sAS[o] = ast[p][e];
+            }
+        }
+    }
+    __syncthreads();
+    const int col = 16 * wave + lc;  // this lane's output column
+    fx4 bk[RT], bq[RT];  // K and Q rows 16 kt + 4 g + s, column col
+#pragma unroll
+    for (int kt = 0; kt < RT; ++kt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bk[kt][s] = sK[(16 * kt + 4 * lg + s) * LD + col];
+            bq[kt][s] = sQ[(16 * kt + 4 * lg + s) * LD + col];
+        }
+    fx4 x2q[RT], x3k[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        x2q[t] = f4(0.f, 0.f, 0.f, 0.f), x3k[t] = x2q[t];
+#pragma unroll
+        for (int kt = 0; kt < RT; ++kt) {
+            // dPL K (lower: kt <= t)
+            if (kt <= t) {
+                const fx4 a4 = *reinterpret_cast<const fx4*>(&sPL[(16 * t + lc) * LC + 16 * kt + 4 * lg]);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) x2q[t] = mma4(a4[s], bk[kt][s], x2q[t]);
+            }
+            // dPL^T Q (kt >= t) and (dAs + dAs^T) K
+            fx4 pt = f4(0.f, 0.f, 0.f, 0.f), sy = pt;
+            if (kt >= t) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int o = (16 * kt + 4 * lg + s) * LC + 16 * t + lc;
+                    pt[s] = sPL[o];
+                    sy[s] = sAS[o];
+                }
+            }
+            if (kt <= t) sy += *reinterpret_cast<const fx4*>(&sAS[(16 * t + lc) * LC + 16 * kt + 4 * lg]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (kt >= t) x3k[t] = mma4(pt[s], bq[kt][s], x3k[t]);
+                x3k[t] = mma4(sy[s], bk[kt][s], x3k[t]);
+            }
+        }
+    }
+    // ---- outputs and row dots
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * t + 4 * lg + e;
+            const float qx = sQ[r * LD + col], kx = sK[r * LD + col];
+            const float q1 = group16_sum(x1q[t][e] * qx);
+            const float k1 = group16_sum(x1k[t][e] * kx);
+            const float k2 = group16_sum(x2k[t][e] * kx);
+            if (lc == 0) atomicAdd(&sq1[r], q1), atomicAdd(&sk1[r], k1), atomicAdd(&sk2[r], k2);
+            if (t0 + r < T) {
+                const long gi = row0 + r * HD + col;
+                a.dq[gi] = fmaf(sGam[r], x1q[t][e], x2q[t][e]);
+                a.dk[gi] = x3k[t][e] + se[r] * x1k[t][e] - sb[r] * sGam[r] * x2k[t][e];
             }
         }
     }
     // <G, H0>
-    float gh = 0.f;
-#pragma unroll 4
-    for (int idx = 4 * tid; idx < D * D; idx += 1024) {
-        const fx4 x = *reinterpret_cast<const fx4*>(gp + idx), y = *reinterpret_cast<const fx4*>(h0 + idx);
-        gh = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, gh))));
-    }
-    gh = block_sum(gh, red);  // contains barriers
-    // reduce the row dots over the 16 column threads
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float x = vd[i];
-        for (int off = 8; off > 0; off >>= 1) x += __shfl_xor(x, off, 16);
-        vd[i] = x;
-    }
-    if (tid < BC) {
-        const int r = tid;
-        float q1 = 0.f, k1 = 0.f, k2 = 0.f;
-        for (int j = 0; j < 16; ++j) {
-            q1 += sdot[0][r * 17 + j];
-            k1 += sdot[1][r * 17 + j];
-            k2 += sdot[2][r * 17 + j];
+    for (int off = 32; off > 0; off >>= 1) gh += __shfl_xor(gh, off);
+    if (lane == 0) red[wave] = gh;
+    __syncthreads();
+    if (wave == 0) {  // lane = chunk row r
+        const int r = lane;
+        float ghs = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) ghs += red[w];
+        const float k1 = sk1[r], k2 = sk2[r];
+        float dgr = sdg[r] + sGam[r] * (sq1[r] - sb[r] * k2) - se[r] * k1;
+        float ek = se[r] * k1;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) ek += __shfl_xor(ek, off);
+        if (r == BC - 1) dgr += sGam[BC - 1] * ghs + ek;
+        // dg = reverse inclusive cumsum of dgam within the chunk
+#pragma unroll
+        for (int off = 1; off < BC; off <<= 1) {
+            const float y = __shfl_down(dgr, off);
+            if (r + off < BC) dgr += y;
         }
-        // dgam_r (without the last-row terms); keep e_r k1 for the last row
-        sdg[r] += sGam[r] * (q1 - sb[r] * k2) - se[r] * k1;
-        sdot[0][r * 17] = se[r] * k1;  // reuse: e_r (K G)_r . Delta_r
-        sdb[r] += -sGam[r] * k2;
-    }
-    __syncthreads();
-    if (tc == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sdb[tr + 16 * i] += vd[i];
-    }
-    __syncthreads();
-    if (tid == 0) {
-        float ek = 0.f;
-        for (int r = 0; r < BC; ++r) ek += sdot[0][r * 17];
-        sdg[BC - 1] += sGam[BC - 1] * gh + ek;
-        float s = 0.f;  // reverse cumsum
-        for (int r = BC - 1; r >= 0; --r) s += sdg[r], sdg[r] = s;
-    }
-    __syncthreads();
-    if (tid < BC && t0 + tid < T) {
-        const long gi = (b * T + t0 + tid) * a.H + h;
-        a.dg[gi] = sdg[tid];
-        a.dbeta[gi] = sdb[tid];
+        if (t0 + r < T) {
+            const long gi = (b * T + t0 + r) * a.H + h;
+            a.dg[gi] = dgr;
+            a.dbeta[gi] = sdb[r] - sGam[r] * k2;
+        }
     }
 }
 
@@ -789,7 +831,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
     e = hipGetLastError();
     profile_mark(stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_grads<In, D>), gc, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_grads<In, D>), gc, dim3(64 * (D / 16)), 0, stream, a);
     e = hipGetLastError();
     profile_mark(stream);
     return e;
@@ -799,7 +841,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
 
 size_t backward_workspace_bytes(int B, int T, int H, int D) {
     const size_t NC = (size_t)(T + BC - 1) / BC, chunks = NC * B * H;
-    const size_t per = 3 * BC + 3 * BC * BC + 4 * (size_t)BC * D + 2 * (size_t)D * D;
+    const size_t per = SCN * BC + 3 * BC * BC + 4 * (size_t)BC * D + 2 * (size_t)D * D;
     return chunks * per * sizeof(float);
 }
 
@@ -815,7 +857,7 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, int dtyp
     a.B = B, a.T = T, a.H = H, a.NC = (T + BC - 1) / BC;
     const size_t chunks = (size_t)a.NC * B * H;
     float* p = static_cast<float*>(ws);
-    a.sc = p, p += chunks * 3 * BC;
+    a.sc = p, p += chunks * SCN * BC;
     a.ti = p, p += chunks * BC * BC;
     a.pm = p, p += chunks * BC * BC;
     a.lkk = p, p += chunks * BC * BC;
