@@ -80,6 +80,11 @@ struct BwdArgs {
     float* dl;   // [.][BC][D]   Delta
     float* gs;   // [.][D][D]    gradients at chunk ends
     float* dr;   // [.][BC][D]   dR
+    float* m1;   // [.][BC][BC]  Ti^T P^T (upper tiles)
+    float* m2;   // [.][BC][D]   Ti^T diag(e) K
+    float* ekt;  // [.][D][BC]   (diag(e) K)^T
+    float* qgt;  // [.][D][BC]   (diag(Gam) Q)^T
+    float* kbt;  // [.][D][BC]   (diag(b Gam) K)^T
     int B, T, H, NC;
 };
 
@@ -159,120 +164,260 @@ struct BlockRegs {
 };
 
 // ---------------------------------------------------------------------------
+// fp32 matrix-core product step: c += a b over one K = 4 slice, lane (l % 16,
+// l / 16) giving A[l % 16][k] and B[k][l % 16] for the slice's k = l / 16.
+__device__ __forceinline__ fx4 mma4(float a, float b, fx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// X Y for 16x16 tiles held in the output layout (lane 16 g + c: rows 4 g + e,
+// column c): X enters through its transpose's tile, which is X's A-operand
+// layout, Y through its own tile, which is the B-operand layout.
+__device__ __forceinline__ fx4 mm16(fx4 xt, fx4 y) {
+    fx4 c = f4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = mma4(xt[s], y[s], c);
+    return c;
+}
+
+// Lower 16x16 tile (tr >= sc) of a 4x4 tile grid from its index 0..9.
+__device__ __forceinline__ void lower_tile(int pi, int& tr, int& sc) {
+    tr = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
+    sc = pi - tr * (tr + 1) / 2;
+}
+
+// bwd_prep: one workgroup of D/16 waves per (chunk, head), every product an
+// fp32 matrix-core product of 16x16 tiles.
+//   gates     gam (wave prefix sum), Gam, e, b into the workspace;
+//   Gram      the ten lower tiles of K K^T and of Q K^T, masked with L:
+//             lkk = strict_lower(L o K K^T), P = lower(L o Q K^T);
+//   Ti        (I + A)^-1, A = diag(b) lkk: diagonal 16x16 blocks by the
+//             nilpotent product (I - A)(I + A^2)(I + A^4)(I + A^8), then the
+//             off-diagonal blocks Ti_ij = -Ti_ii sum_{j<=k<i} A_ik Ti_kj by
+//             block distance;
+//   products  W = Ti diag(b Gam) K, U = Ti diag(b) V, M2 = Ti^T diag(e) K
+//             (wave w: column tile w), M1 = Ti^T P^T (its ten upper tiles),
+//             and the transposes (diag(e) K)^T, (diag(Gam) Q)^T and
+//             (diag(b Gam) K)^T that the chains take as row operands.
 template <typename In, int D>
-__global__ __launch_bounds__(256) void bwd_prep(const BwdArgs a) {
-    constexpr int LD = D + 4, LC = BC + 1;
-    __shared__ float sK[BC * LD], sX[BC * LD], sL[BC * LC], sTi[BC * LC];
-    __shared__ float sgam[BC], sb[BC], sbg[BC];
-    const int tid = threadIdx.x, c = blockIdx.x, h = blockIdx.y;
+__global__ __launch_bounds__(64 * (D / 16)) void bwd_prep(const BwdArgs a) {
+    constexpr int NW = D / 16, NT = 64 * NW;
+    constexpr int LD = D + 4, LC = BC + 4, KB = D / 32, RT = BC / 16;
+    constexpr int NL = RT * (RT + 1) / 2;  // lower tiles
+    __shared__ __attribute__((aligned(16))) float sK[BC * LD], sX[BC * LD];
+    __shared__ __attribute__((aligned(16))) float sA[BC * LC], sP[BC * LC], sTi[BC * LC];
+    __shared__ float sgam[BC], sb[BC], sGam[BC], se[BC], sbg[BC];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lg = lane >> 4, lc = lane & 15;
+    const int c = blockIdx.x, h = blockIdx.y;
     const long b = blockIdx.z, n = b * a.H + h, nc = n * a.NC + c;
     const int t0 = c * BC, T = a.T;
 
-    if (tid < BC) {
-        const int t = t0 + tid;
-        sgam[tid] = t < T ? a.g[(b * T + t) * a.H + h] : 0.f;
-        sb[tid] = t < T ? a.beta[(b * T + t) * a.H + h] : 0.f;
-    }
-    load_rows<In, D, LD>(sK, a.k, b, h, t0, T, a.H);
-    load_rows<In, D, LD>(sX, a.q, b, h, t0, T, a.H);
-    __syncthreads();
-    if (tid == 0) {
-        float s = 0.f;
-        for (int r = 0; r < BC; ++r) s += sgam[r], sgam[r] = s;
-    }
-    __syncthreads();
-    if (tid < BC) {
-        float* scp = a.sc + nc * SCN * BC;
-        scp[tid] = __expf(sgam[tid]);
-        scp[BC + tid] = __expf(sgam[BC - 1] - sgam[tid]);
-        scp[2 * BC + tid] = sb[tid];
-        scp[3 * BC + tid] = sgam[tid];
-    }
-    // KK and QK tiles: thread rows tr + 16 i, columns tc + 16 j
-    const int tr = tid / 16, tc = tid % 16;
-    {
-        float kk[4][4] = {}, qk[4][4] = {};
-        for (int x = 0; x < D; ++x) {
-            float kr[4], qr[4], kc[4];
+    if (wave == 0) {
+        const int t = t0 + lane;
+        const long gi = (b * T + t) * a.H + h;
+        float gv = t < T ? a.g[gi] : 0.f;
+        const float bv = t < T ? a.beta[gi] : 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                kr[i] = sK[(tr + 16 * i) * LD + x];
-                qr[i] = sX[(tr + 16 * i) * LD + x];
-                kc[i] = sK[(tc + 16 * i) * LD + x];
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    kk[i][j] = fmaf(kr[i], kc[j], kk[i][j]);
-                    qk[i][j] = fmaf(qr[i], kc[j], qk[i][j]);
-                }
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(gv, off);
+            if (lane >= off) gv += y;
         }
-        float* pmp = a.pm + nc * BC * BC;
+        const float gC = __shfl(gv, 63);
+        const float G = __expf(gv), e = __expf(gC - gv);
+        sgam[lane] = gv, sb[lane] = bv, sGam[lane] = G, se[lane] = e, sbg[lane] = bv * G;
+        float* scp = a.sc + nc * SCN * BC;
+        scp[lane] = G, scp[BC + lane] = e, scp[2 * BC + lane] = bv, scp[3 * BC + lane] = gv;
+    }
+    RowRegs<In, D, NT> rv;
+    rv.load(a.v, b, h, t0, T, a.H);
+    {
+        RowRegs<In, D, NT> rk, rq;
+        rk.load(a.k, b, h, t0, T, a.H);
+        rq.load(a.q, b, h, t0, T, a.H);
+        rk.template store<LD>(sK);
+        rq.template store<LD>(sX);
+    }
+    __syncthreads();
+
+    // ---- Gram tiles: index q < NL is K K^T tile q, q >= NL is Q K^T tile q - NL
+    {
         float* lkp = a.lkk + nc * BC * BC;
+        float* pmp = a.pm + nc * BC * BC;
+        for (int q = wave; q < 2 * NL; q += NW) {
+            const bool isq = q >= NL;
+            int tr, sc;
+            lower_tile(isq ? q - NL : q, tr, sc);
+            const float* X = isq ? sX : sK;
+            fx4 acc = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int kb = 0; kb < KB; ++kb) {
+                const int off = 32 * kb + 8 * lg;
+                const float* px = &X[(16 * tr + lc) * LD + off];
+                const float* pk = &sK[(16 * sc + lc) * LD + off];
+                const fx4 x0 = *reinterpret_cast<const fx4*>(px), x1 = *reinterpret_cast<const fx4*>(px + 4);
+                const fx4 k0 = *reinterpret_cast<const fx4*>(pk), k1 = *reinterpret_cast<const fx4*>(pk + 4);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = tr + 16 * i, s = tc + 16 * j;
-                const float L = s <= r ? __expf(sgam[r] - sgam[s]) : 0.f;
-                const float lk = s < r ? L * kk[i][j] : 0.f;
-                sL[r * LC + s] = lk;
-                lkp[r * BC + s] = lk;
-                pmp[r * BC + s] = s <= r ? L * qk[i][j] : 0.f;
+                for (int s = 0; s < 4; ++s) acc = mma4(x0[s], k0[s], acc);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mma4(x1[s], k1[s], acc);
             }
+            const int s = 16 * sc + lc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * tr + 4 * lg + e;
+                const float L = s <= r ? __expf(sgam[r] - sgam[s]) : 0.f;
+                if (!isq) {
+                    const float lk = s < r ? L * acc[e] : 0.f;
+                    lkp[r * BC + s] = lk;
+                    sA[r * LC + s] = sb[r] * lk;
+                } else {
+                    const float p = L * acc[e];
+                    pmp[r * BC + s] = p;
+                    sP[r * LC + s] = p;
+                }
+            }
+        }
+        // zero upper tiles of P and lkk in the workspace
+        for (int idx = tid; idx < BC * BC; idx += NT) {
+            const int r = idx / BC, s = idx % BC;
+            if (s / 16 > r / 16) lkp[idx] = 0.f, pmp[idx] = 0.f;
+        }
+    }
+    // transposes [D][BC] the chains take as row operands: (diag(e) K)^T,
+    // (diag(Gam) Q)^T, (diag(b Gam) K)^T; lanes run along d, 4 tokens each
+    {
+        float* ekp = a.ekt + nc * D * BC;
+        float* qgp = a.qgt + nc * D * BC;
+        float* kbp = a.kbt + nc * D * BC;
+        for (int idx = tid; idx < D * BC / 4; idx += NT) {
+            const int x = idx % D, t = 4 * (idx / D);
+            fx4 ek, qg, kb;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float kx = sK[(t + s) * LD + x];
+                ek[s] = se[t + s] * kx;
+                kb[s] = sbg[t + s] * kx;
+                qg[s] = sGam[t + s] * sX[(t + s) * LD + x];
+            }
+            *reinterpret_cast<fx4*>(ekp + x * BC + t) = ek;
+            *reinterpret_cast<fx4*>(qgp + x * BC + t) = qg;
+            *reinterpret_cast<fx4*>(kbp + x * BC + t) = kb;
+        }
     }
     __syncthreads();
-    // Ti = (I + A)^-1, A = b_r lkk: row-serial forward substitution, columns in parallel
-    if (tid < BC) {
-        for (int r = 0; r < BC; ++r) sTi[r * LC + tid] = r == tid ? 1.f : 0.f;
+    rv.template store<LD>(sX);  // V replaces Q (read after the Ti barriers)
+
+    // ---- Ti: diagonal blocks (wave b)
+    if (wave < RT) {
+        const int o = 16 * wave;
+        fx4 ax, at, id;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * lg + e;
+            ax[e] = sA[(o + r) * LC + o + lc];
+            at[e] = sA[(o + lc) * LC + o + r];
+            id[e] = r == lc ? 1.f : 0.f;
+        }
+        const fx4 a2 = mm16(at, ax), a2t = mm16(ax, at);
+        const fx4 a4 = mm16(a2t, a2), a4t = mm16(a2, a2t);
+        const fx4 a8 = mm16(a4t, a4);
+        const fx4 n1t = id - at;
+        const fx4 n2t = n1t + mm16(a2, n1t);  // ((I - A)(I + A^2))^T
+        const fx4 n3t = n2t + mm16(a4, n2t);
+        const fx4 nt = n3t + mm16(a8, n3t);   // ((I + A)^-1)^T: row lc of the block, columns 4 lg + e
+        *reinterpret_cast<fx4*>(&sTi[(o + lc) * LC + o + 4 * lg]) = nt;
     }
     __syncthreads();
-    // column j = tid / 4; the 4 threads of a column split the dot product
-    for (int r = 1; r < BC; ++r) {
-        const int j = tid / 4, part = tid % 4;
-        float s = 0.f;
-        if (j < r)
-            for (int i = j + part; i < r; i += 4) s = fmaf(sL[r * LC + i], sTi[i * LC + j], s);
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        if (j < r && part == 0) sTi[r * LC + j] = -sb[r] * s;
+    // off-diagonal blocks by distance
+#pragma unroll
+    for (int dist = 1; dist < RT; ++dist) {
+        if (wave < RT - dist) {
+            const int j = wave, i = wave + dist;
+            fx4 y = f4(0.f, 0.f, 0.f, 0.f);
+            for (int k = j; k < i; ++k) {
+                const fx4 a4 = *reinterpret_cast<const fx4*>(&sA[(16 * i + lc) * LC + 16 * k + 4 * lg]);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) y = mma4(a4[s], sTi[(16 * k + 4 * lg + s) * LC + 16 * j + lc], y);
+            }
+            const fx4 n4 = *reinterpret_cast<const fx4*>(&sTi[(16 * i + lc) * LC + 16 * i + 4 * lg]);
+            fx4 t = f4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) t = mma4(n4[s], y[s], t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sTi[(16 * i + 4 * lg + e) * LC + 16 * j + lc] = -t[e];
+        }
         __syncthreads();
     }
     {
         float* tip = a.ti + nc * BC * BC;
-        for (int idx = 4 * tid; idx < BC * BC; idx += 1024) {
-            const float* t4 = &sTi[(idx / BC) * LC + idx % BC];
-            *reinterpret_cast<fx4*>(tip + idx) = fx4{t4[0], t4[1], t4[2], t4[3]};
+        for (int idx = 4 * tid; idx < BC * BC; idx += 4 * NT) {
+            const int r = idx / BC, s = idx % BC;
+            const fx4 v = s / 16 > r / 16 ? f4(0.f, 0.f, 0.f, 0.f) : *reinterpret_cast<const fx4*>(&sTi[r * LC + s]);
+            *reinterpret_cast<fx4*>(tip + idx) = v;
         }
-        if (tid < BC) sbg[tid] = sb[tid] * __expf(sgam[tid]);
     }
-    // W = Ti diag(b Gam) K, then U = Ti diag(b) V; thread rows tr + 16 i,
-    // columns tc + 16 j (4 x 8 outputs, 12 LDS reads per 32 FMA)
-    load_rows<In, D, LD>(sX, a.v, b, h, t0, T, a.H);
-    __syncthreads();
-    constexpr int CJ = D / 16;
-    for (int pass = 0; pass < 2; ++pass) {
-        const float* src = pass == 0 ? sK : sX;
-        const float* scl = pass == 0 ? sbg : sb;
-        float* dst = (pass == 0 ? a.w : a.u) + nc * BC * D;
-        float acc[4][CJ] = {};
-        for (int i = 0; i < BC; ++i) {
-            float t4[4], x8[CJ];
+
+    // ---- W, U, M2 for column tile `wave`
+    const int col = 16 * wave + lc;
+    {
+        fx4 bw[RT], bu[RT], bm[RT];
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) t4[ii] = sTi[(tr + 16 * ii) * LC + i];
-            const float sc = scl[i];
+        for (int j = 0; j < RT; ++j)
 #pragma unroll
-            for (int jj = 0; jj < CJ; ++jj) x8[jj] = sc * src[i * LD + tc + 16 * jj];
+            for (int s = 0; s < 4; ++s) {
+                const int t = 16 * j + 4 * lg + s;
+                const float kx = sK[t * LD + col];
+                bw[j][s] = sbg[t] * kx;
+                bm[j][s] = se[t] * kx;
+                bu[j][s] = sb[t] * sX[t * LD + col];
+            }
+        float* wp = a.w + nc * BC * D;
+        float* up = a.u + nc * BC * D;
+        float* mp = a.m2 + nc * BC * D;
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
+        for (int i = 0; i < RT; ++i) {
+            fx4 w = f4(0.f, 0.f, 0.f, 0.f), u = w, m = w;
 #pragma unroll
-                for (int jj = 0; jj < CJ; ++jj) acc[ii][jj] = fmaf(t4[ii], x8[jj], acc[ii][jj]);
+            for (int j = 0; j < RT; ++j) {
+                if (j <= i) {
+                    const fx4 t4 = *reinterpret_cast<const fx4*>(&sTi[(16 * i + lc) * LC + 16 * j + 4 * lg]);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        w = mma4(t4[s], bw[j][s], w);
+                        u = mma4(t4[s], bu[j][s], u);
+                    }
+                }
+                if (j >= i) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) m = mma4(sTi[(16 * j + 4 * lg + s) * LC + 16 * i + lc], bm[j][s], m);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * i + 4 * lg + e;
+                wp[r * D + col] = w[e];
+                up[r * D + col] = u[e];
+                mp[r * D + col] = m[e];
+            }
         }
+    }
+    // ---- M1 = Ti^T P^T: upper tiles (i <= jt), the lower ones are never read
+    {
+        float* m1p = a.m1 + nc * BC * BC;
+        for (int q = wave; q < NL; q += NW) {
+            int jt, i;
+            lower_tile(q, jt, i);  // jt >= i
+            fx4 m = f4(0.f, 0.f, 0.f, 0.f);
+            for (int k = i; k <= jt; ++k) {
+                const fx4 p4 = *reinterpret_cast<const fx4*>(&sP[(16 * jt + lc) * LC + 16 * k + 4 * lg]);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
+                for (int s = 0; s < 4; ++s) m = mma4(sTi[(16 * k + 4 * lg + s) * LC + 16 * i + lc], p4[s], m);
+            }
 #pragma unroll
-            for (int jj = 0; jj < CJ; ++jj) dst[(tr + 16 * ii) * D + tc + 16 * jj] = acc[ii][jj];
+            for (int e = 0; e < 4; ++e) m1p[(16 * i + 4 * lg + e) * BC + 16 * jt + lc] = m[e];
+        }
     }
 }
 
@@ -486,11 +631,6 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 matrix-core product step: c += a b over one K = 4 slice, lane (l % 16,
-// l / 16) giving A[l % 16][k] and B[k][l % 16] for the slice's k = l / 16.
-__device__ __forceinline__ fx4 mma4(float a, float b, fx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 // Sum over the 16 lanes of each lane group (the c index of a 16x16 tile).
 __device__ __forceinline__ float group16_sum(float x) {
@@ -819,7 +959,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
 template <typename In, int D>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
     const dim3 gc((unsigned)a.NC, (unsigned)a.H, (unsigned)a.B), gs((unsigned)(a.B * a.H * (D / SW)));
-    hipLaunchKernelGGL((bwd_prep<In, D>), gc, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_prep<In, D>), gc, dim3(64 * (D / 16)), 0, stream, a);
     hipError_t e = hipGetLastError();
     profile_mark(stream);
     if (e != hipSuccess) return e;
@@ -841,7 +981,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
 
 size_t backward_workspace_bytes(int B, int T, int H, int D) {
     const size_t NC = (size_t)(T + BC - 1) / BC, chunks = NC * B * H;
-    const size_t per = SCN * BC + 3 * BC * BC + 4 * (size_t)BC * D + 2 * (size_t)D * D;
+    const size_t per = SCN * BC + 4 * BC * BC + 8 * (size_t)BC * D + 2 * (size_t)D * D;
     return chunks * per * sizeof(float);
 }
 
@@ -866,7 +1006,12 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, int dtyp
     a.dl = p, p += chunks * BC * D;
     a.dr = p, p += chunks * BC * D;
     a.hs = p, p += chunks * (size_t)D * D;
-    a.gs = p;
+    a.gs = p, p += chunks * (size_t)D * D;
+    a.m1 = p, p += chunks * BC * BC;
+    a.m2 = p, p += chunks * BC * D;
+    a.ekt = p, p += chunks * BC * D;
+    a.qgt = p, p += chunks * BC * D;
+    a.kbt = p;
     if (dtype_bf16)
         return D == 64 ? launch_t<bf16_t, 64>(a, stream) : launch_t<bf16_t, 128>(a, stream);
     return D == 64 ? launch_t<float, 64>(a, stream) : launch_t<float, 128>(a, stream);
