@@ -29,17 +29,19 @@
 // dO_r.(Q H0)_r = (dO H0^T)_r.q_r, dR_r.(K H0)_r = (dR H0^T)_r.k_r and
 // (K G)_r.Delta_r = (Delta G^T)_r.k_r.
 //
-// Kernels (all fp32 arithmetic):
+// Kernels (all fp32 arithmetic, every product on the fp32 matrix cores):
 //   bwd_prep       per chunk, in parallel: gates, the Gram and decayed QK^T
-//                  tiles, Ti by forward substitution, W and U;
-//   bwd_fwd_chain  per (b, h, 8-column state slice), chunks in order: stores
+//                  tiles, Ti = (I + A)^-1 (blocked), W, U and the chain
+//                  operands M1 = Ti^T P^T, M2 = Ti^T diag(e) K (so that
+//                  dR = M1 dO + M2 G) and transposed row operands;
+//   bwd_fwd_chain  per (b, h, 16-column state slice), chunks in order: stores
 //                  every chunk's start state and Delta;
-//   bwd_bwd_chain  per (b, h, 8-column slice), chunks in reverse: stores every
+//   bwd_bwd_chain  per (b, h, 16-column slice), chunks in reverse: stores every
 //                  chunk's end gradient G and dR, writes dS_0;
-//   bwd_grads      per chunk, in parallel, on fp32 matrix-core products:
-//                  dq, dk, dv, dbeta, dg.
+//   bwd_grads      per chunk, in parallel: dq, dk, dv, dbeta, dg.
 #include "gdn_device.h"
 #include "gdn_launch.h"
+#include "gdn_mfma.h"  // lds_sync
 
 namespace gdn {
 namespace {
@@ -74,17 +76,24 @@ struct BwdArgs {
     float* ti;   // [.][BC][BC]
     float* pm;   // [.][BC][BC]  lower(L o QK^T)
     float* lkk;  // [.][BC][BC]  strict_lower(L o KK^T)
-    float* w;    // [.][BC][D]
-    float* u;    // [.][BC][D]
+    float* w;    // [.] W,  row-operand fragments (see below)
+    float* u;    // [.] U,  output-layout tiles
     float* hs;   // [.][D][D]    chunk start states
     float* dl;   // [.][BC][D]   Delta
     float* gs;   // [.][D][D]    gradients at chunk ends
     float* dr;   // [.][BC][D]   dR
-    float* m1;   // [.][BC][BC]  Ti^T P^T (upper tiles)
-    float* m2;   // [.][BC][D]   Ti^T diag(e) K
-    float* ekt;  // [.][D][BC]   (diag(e) K)^T
-    float* qgt;  // [.][D][BC]   (diag(Gam) Q)^T
-    float* kbt;  // [.][D][BC]   (diag(b Gam) K)^T
+    float* m1;   // [.] Ti^T P^T (upper tiles), row-operand fragments
+    float* m2;   // [.] Ti^T diag(e) K,         row-operand fragments
+    float* ekt;  // [.] (diag(e) K)^T,          row-operand fragments
+    float* qgt;  // [.] (diag(Gam) Q)^T,        row-operand fragments
+    float* kbt;  // [.] (diag(b Gam) K)^T,      row-operand fragments
+    // The chain operands are stored as the 1 KB fragments the chains load, one
+    // 16-byte load per lane: a row-operand fragment (row tile i, contraction
+    // tile k) holds at lane 16 g + r the four values [16 i + r][16 k + 4 g + s],
+    // s = 0..3 (the A operand of four 16x16x4 steps); an output-layout tile
+    // holds at lane 16 g + c the values [16 i + 4 g + e][16 k + c].  Fragment
+    // (i, k) of chunk nc starts at ((nc NI + i) NK + k) 256 floats, NI x NK the
+    // tile grid of the matrix.
     int B, T, H, NC;
 };
 
@@ -285,14 +294,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_prep(const BwdArgs a) {
             if (s / 16 > r / 16) lkp[idx] = 0.f, pmp[idx] = 0.f;
         }
     }
-    // transposes [D][BC] the chains take as row operands: (diag(e) K)^T,
-    // (diag(Gam) Q)^T, (diag(b Gam) K)^T; lanes run along d, 4 tokens each
+    // transposes the chains take as row operands, as fragments (m, tt) of the
+    // D x 64 matrices: (diag(e) K)^T, (diag(Gam) Q)^T, (diag(b Gam) K)^T
     {
-        float* ekp = a.ekt + nc * D * BC;
-        float* qgp = a.qgt + nc * D * BC;
-        float* kbp = a.kbt + nc * D * BC;
-        for (int idx = tid; idx < D * BC / 4; idx += NT) {
-            const int x = idx % D, t = 4 * (idx / D);
+        for (int idx = tid; idx < NW * RT * 64; idx += NT) {
+            const int ln = idx & 63, f = idx >> 6, m = f / RT, tt = f % RT;
+            const int x = 16 * m + (ln & 15), t = 16 * tt + 4 * (ln >> 4);
             fx4 ek, qg, kb;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -301,9 +308,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_prep(const BwdArgs a) {
                 kb[s] = sbg[t + s] * kx;
                 qg[s] = sGam[t + s] * sX[(t + s) * LD + x];
             }
-            *reinterpret_cast<fx4*>(ekp + x * BC + t) = ek;
-            *reinterpret_cast<fx4*>(qgp + x * BC + t) = qg;
-            *reinterpret_cast<fx4*>(kbp + x * BC + t) = kb;
+            const long fb = ((nc * NW + m) * RT + tt) * 256 + 4 * ln;
+            *reinterpret_cast<fx4*>(a.ekt + fb) = ek;
+            *reinterpret_cast<fx4*>(a.qgt + fb) = qg;
+            *reinterpret_cast<fx4*>(a.kbt + fb) = kb;
         }
     }
     __syncthreads();
@@ -373,9 +381,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_prep(const BwdArgs a) {
                 bm[j][s] = se[t] * kx;
                 bu[j][s] = sb[t] * sX[t * LD + col];
             }
-        float* wp = a.w + nc * BC * D;
-        float* up = a.u + nc * BC * D;
-        float* mp = a.m2 + nc * BC * D;
+        // fragment offset of this lane's element (row 4 lg + e, column lc)
+        const int fo = (16 * (lc / 4) + 4 * lg) * 4 + lc % 4;
 #pragma unroll
         for (int i = 0; i < RT; ++i) {
             fx4 w = f4(0.f, 0.f, 0.f, 0.f), u = w, m = w;
@@ -394,18 +401,18 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_prep(const BwdArgs a) {
                     for (int s = 0; s < 4; ++s) m = mma4(sTi[(16 * j + 4 * lg + s) * LC + 16 * i + lc], bm[j][s], m);
                 }
             }
+            const long fb = ((nc * RT + i) * NW + wave) * 256;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 16 * i + 4 * lg + e;
-                wp[r * D + col] = w[e];
-                up[r * D + col] = u[e];
-                mp[r * D + col] = m[e];
+                a.w[fb + fo + 4 * e] = w[e];
+                a.m2[fb + fo + 4 * e] = m[e];
             }
+            *reinterpret_cast<fx4*>(a.u + fb + 4 * lane) = u;
         }
     }
     // ---- M1 = Ti^T P^T: upper tiles (i <= jt), the lower ones are never read
     {
-        float* m1p = a.m1 + nc * BC * BC;
+        const int fo = (16 * (lc / 4) + 4 * lg) * 4 + lc % 4;
         for (int q = wave; q < NL; q += NW) {
             int jt, i;
             lower_tile(q, jt, i);  // jt >= i
@@ -415,17 +422,23 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_prep(const BwdArgs a) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s) m = mma4(sTi[(16 * k + 4 * lg + s) * LC + 16 * i + lc], p4[s], m);
             }
+            const long fb = ((nc * RT + i) * RT + jt) * 256;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) m1p[(16 * i + 4 * lg + e) * BC + 16 * jt + lc] = m[e];
+            for (int e = 0; e < 4; ++e) a.m1[fb + fo + 4 * e] = m[e];
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Chains: one workgroup per (b, h, 8-column slice of the state), chunks in
-// sequence.  The next chunk's operands are loaded into registers (16-byte
-// loads) while the current chunk computes, then written to LDS.
-constexpr int SW = 8;  // state columns per slice
+// Chains: one workgroup of 4 waves per (b, h, 16-column slice of the state),
+// chunks in sequence, every product an fp32 matrix-core product of 16x16
+// tiles.  The slice (D x 16, fp32) lives in registers as D/16 row tiles in the
+// output layout, tiles m = w, w + 4, ... on wave w; this layout is also the
+// B-operand layout of a 16-deep contraction over its rows, so tiles pass
+// between waves through LDS in lane order with no reshuffling.  Row operands
+// (W, M1, M2 and the transposes) are read from the workspace as 16-byte A
+// fragments, one chunk ahead.
+constexpr int CW = 16;  // state columns per chain workgroup
 
 // 1D grid of nser * ns workgroups -> (series n, slice).  Workgroups are dealt
 // to the 8 XCDs round-robin; when the series count is a multiple of 8, all
@@ -442,191 +455,222 @@ __device__ __forceinline__ void slice_of(int ns, int nser, long& n, int& sl) {
     }
 }
 
-template <typename In, int D>
-__global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
-    constexpr int LD = D + 4;
-    __shared__ __attribute__((aligned(16))) float sW[BC * LD], sK[BC * LD];
-    __shared__ __attribute__((aligned(16))) float sH[D * SW], sU[BC * SW], sDe[BC * SW];
-    __shared__ float se[BC], sgc;
-    const int tid = threadIdx.x;
-    long n;
-    int sl;
-    slice_of(D / SW, a.B * a.H, n, sl);
-    const long b = n / a.H;
-    const int h = (int)(n % a.H);
-    const int c0 = sl * SW;
-    for (int idx = tid; idx < D * SW; idx += 256) {
-        const int r = idx / SW, cc = idx % SW;
-        sH[idx] = a.state0 ? a.state0[(n * D + r) * D + c0 + cc] : 0.f;
-    }
-    BlockRegs<BC, D> rw;
-    RowRegs<In, D> rk;
-    fx4 ru = f4(0.f, 0.f, 0.f, 0.f);
-    float re = 0.f;
-    auto fetch = [&](int c) __attribute__((always_inline)) {
-        const long nc = n * a.NC + c;
-        rw.load(a.w + nc * BC * D, D);
-        rk.load(a.k, b, h, c * BC, a.T, a.H);
-        if (tid < BC * SW / 4) ru = *reinterpret_cast<const fx4*>(a.u + (nc * BC + tid / 2) * D + c0 + (tid % 2) * 4);
-        if (tid < BC) re = a.sc[nc * SCN * BC + BC + tid];
-    };
-    fetch(0);
-    for (int c = 0; c < a.NC; ++c) {
-        const long nc = n * a.NC + c;
-        __syncthreads();
-        rw.template store<LD>(sW);
-        rk.template store<LD>(sK);
-        if (tid < BC * SW / 4) *reinterpret_cast<fx4*>(&sU[(tid / 2) * SW + (tid % 2) * 4]) = ru;
-        if (tid < BC) se[tid] = re;
-        if (tid == 0) sgc = a.sc[nc * SCN * BC + BC - 1];
-        for (int idx = tid; idx < D * SW; idx += 256)
-            a.hs[(nc * D + idx / SW) * D + c0 + idx % SW] = sH[idx];
-        __syncthreads();
-        fetch(min(c + 1, a.NC - 1));  // unconditional: the last one re-reads valid rows
-        // Delta = U - W H (row tid / 4, columns 2 (tid % 4) + {0, 1})
-        {
-            const int r = tid / 4, cc = 2 * (tid % 4);
-            float s0 = sU[r * SW + cc], s1 = sU[r * SW + cc + 1];
-#pragma unroll 8
-            for (int x = 0; x < D; ++x) {
-                const float w = sW[r * LD + x];
-                s0 = fmaf(-w, sH[x * SW + cc], s0);
-                s1 = fmaf(-w, sH[x * SW + cc + 1], s1);
-            }
-            *reinterpret_cast<fx2*>(a.dl + (nc * BC + r) * D + c0 + cc) = fx2{s0, s1};
-            sDe[r * SW + cc] = se[r] * s0;
-            sDe[r * SW + cc + 1] = se[r] * s1;
-        }
-        __syncthreads();
-        // H = Gam_C H + K^T diag(e) Delta (row tid / 2, columns 4 (tid % 2) + {0..3})
-        {
-            const int r = tid / 2, cc = 4 * (tid % 2);
-            fx4 acc = *reinterpret_cast<const fx4*>(&sH[r * SW + cc]);
-            const float gc = sgc;
-            acc.x *= gc, acc.y *= gc, acc.z *= gc, acc.w *= gc;
-#pragma unroll 8
-            for (int t = 0; t < BC; ++t) {
-                const float kv = sK[t * LD + r];
-                const fx4 dv = *reinterpret_cast<const fx4*>(&sDe[t * SW + cc]);
-                acc.x = fmaf(kv, dv.x, acc.x), acc.y = fmaf(kv, dv.y, acc.y);
-                acc.z = fmaf(kv, dv.z, acc.z), acc.w = fmaf(kv, dv.w, acc.w);
-            }
-            __syncthreads();
-            *reinterpret_cast<fx4*>(&sH[r * SW + cc]) = acc;
-        }
-    }
+__device__ __forceinline__ fx4 ld4g(const float* p) { return *reinterpret_cast<const fx4*>(p); }
+
+// A uniform value through a vector load: a scalar-cache load would be counted
+// with LDS traffic, and every LDS barrier would wait for it.
+__device__ __forceinline__ float ld_vec(const float* p) {
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    return p[z];
 }
 
+// Forward chain: stores every chunk's start state H (hs) and Delta (dl).
+//   Delta = U - W H            wave w: chunk rows [16 w, 16 w + 16)
+//   H = Gam_C H + (diag(e) K)^T Delta
 template <typename In, int D>
-__global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
-    constexpr int LD = D + 4, LC = BC + 4;
-    __shared__ __attribute__((aligned(16))) float sK[BC * LD], sQ[BC * LD], sP[BC * LC], sTi[BC * LC];
-    __shared__ __attribute__((aligned(16))) float sG[D * SW], sdO[BC * SW], sX[BC * SW], sdOg[BC * SW], sdRb[BC * SW];
-    __shared__ __attribute__((aligned(16))) float ssc[3 * BC];
-    const int tid = threadIdx.x;
+__global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
+    constexpr int MT = D / 16, MW = MT / 4;  // row tiles of the slice, per wave
+    __shared__ fx4 sH[MT][64];
+    __shared__ fx4 sD[4][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lg = lane >> 4, lc = lane & 15;
     long n;
     int sl;
-    slice_of(D / SW, a.B * a.H, n, sl);
-    const long b = n / a.H;
-    const int h = (int)(n % a.H);
-    const int c0 = sl * SW, T = a.T;
-    for (int idx = tid; idx < D * SW; idx += 256) {
-        const int r = idx / SW, cc = idx % SW;
-        sG[idx] = a.d_state ? a.d_state[(n * D + r) * D + c0 + cc] : 0.f;
-    }
-    RowRegs<In, D> rk, rq;
-    BlockRegs<BC, BC> rp, rt;
-    fx4 rdo = f4(0.f, 0.f, 0.f, 0.f), rsc = rdo;
-    auto fetch = [&](int c) __attribute__((always_inline)) {
-        const long nc = n * a.NC + c;
-        rk.load(a.k, b, h, c * BC, T, a.H);
-        rq.load(a.q, b, h, c * BC, T, a.H);
-        rp.load(a.pm + nc * BC * BC, BC);
-        rt.load(a.ti + nc * BC * BC, BC);
-        if (tid < BC * SW / 4) {
-            const int r = tid / 2, t = c * BC + r;
-            rdo = t < T ? *reinterpret_cast<const fx4*>(a.d_o + ((b * T + t) * a.H + h) * (long)D + c0 + (tid % 2) * 4)
-                        : f4(0.f, 0.f, 0.f, 0.f);
-        }
-        if (tid < 3 * BC / 4) rsc = *reinterpret_cast<const fx4*>(a.sc + nc * SCN * BC + 4 * tid);
+    slice_of(D / CW, a.B * a.H, n, sl);
+    const int col = CW * sl + lc;
+    fx4 hr[MW];
+#pragma unroll
+    for (int j = 0; j < MW; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            hr[j][e] = a.state0 ? a.state0[(n * D + 16 * (wave + 4 * j) + 4 * lg + e) * D + col] : 0.f;
+    // operands of one chunk: W row tile `wave` (fragments over all D),
+    // (diag(e) K)^T row tiles of this wave's state tiles, the U tile, Gam_C
+    struct Ops {
+        fx4 w[MT], ek[MW][4], u;
+        float gc;
     };
-    fetch(a.NC - 1);
-    for (int c = a.NC - 1; c >= 0; --c) {
+    auto fetch = [&](Ops& o, int c) __attribute__((always_inline)) {
         const long nc = n * a.NC + c;
-        __syncthreads();
-        rk.template store<LD>(sK);
-        rq.template store<LD>(sQ);
-        rp.template store<LC>(sP);
-        rt.template store<LC>(sTi);
-        if (tid < BC * SW / 4) *reinterpret_cast<fx4*>(&sdO[(tid / 2) * SW + (tid % 2) * 4]) = rdo;
-        if (tid < 3 * BC / 4) *reinterpret_cast<fx4*>(&ssc[4 * tid]) = rsc;
-        for (int idx = tid; idx < D * SW; idx += 256)
-            a.gs[(nc * D + idx / SW) * D + c0 + idx % SW] = sG[idx];
-        __syncthreads();
-        fetch(max(c - 1, 0));  // unconditional: the last one re-reads valid rows
-        // dDelta = P^T dO + diag(e) K G   (row tid / 4, columns 2 (tid % 4) + {0, 1})
-        {
-            const int r = tid / 4, cc = 2 * (tid % 4);
-            float s0 = 0.f, s1 = 0.f, k0 = 0.f, k1 = 0.f;
-#pragma unroll 8
-            for (int j = 0; j < BC; ++j) {  // P is zero above the diagonal
-                const float p = sP[j * LC + r];
-                s0 = fmaf(p, sdO[j * SW + cc], s0);
-                s1 = fmaf(p, sdO[j * SW + cc + 1], s1);
-            }
-#pragma unroll 8
-            for (int x = 0; x < D; ++x) {
-                const float kv = sK[r * LD + x];
-                k0 = fmaf(kv, sG[x * SW + cc], k0);
-                k1 = fmaf(kv, sG[x * SW + cc + 1], k1);
-            }
-            const float e = ssc[BC + r], gm = ssc[r];
-            sX[r * SW + cc] = fmaf(e, k0, s0);
-            sX[r * SW + cc + 1] = fmaf(e, k1, s1);
-            sdOg[r * SW + cc] = gm * sdO[r * SW + cc];
-            sdOg[r * SW + cc + 1] = gm * sdO[r * SW + cc + 1];
+        const float* wp = a.w + (nc * 4 + wave) * MT * 256 + 4 * lane;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) o.w[m] = ld4g(wp + 256 * m);
+#pragma unroll
+        for (int j = 0; j < MW; ++j) {
+            const float* ep = a.ekt + (nc * MT + wave + 4 * j) * 4 * 256 + 4 * lane;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) o.ek[j][tt] = ld4g(ep + 256 * tt);
         }
-        __syncthreads();
-        // dR = Ti^T dDelta  (Ti lower)
-        {
-            const int r = tid / 4, cc = 2 * (tid % 4);
-            float s0 = 0.f, s1 = 0.f;
-#pragma unroll 8
-            for (int j = 0; j < BC; ++j) {  // Ti is zero above the diagonal
-                const float ti = sTi[j * LC + r];
-                s0 = fmaf(ti, sX[j * SW + cc], s0);
-                s1 = fmaf(ti, sX[j * SW + cc + 1], s1);
-            }
-            *reinterpret_cast<fx2*>(a.dr + (nc * BC + r) * D + c0 + cc) = fx2{s0, s1};
-            const float bg = ssc[2 * BC + r] * ssc[r];
-            sdRb[r * SW + cc] = bg * s0;
-            sdRb[r * SW + cc + 1] = bg * s1;
+        o.u = ld4g(a.u + ((nc * 4 + wave) * MT + sl) * 256 + 4 * lane);
+        o.gc = ld_vec(a.sc + nc * SCN * BC + BC - 1);
+    };
+    // one chunk: `cur` holds its operands, `nxt` receives those of the chunk
+    // two ahead (three buffers used in turn, so no register copies wait on
+    // loads still in flight and each load has two chunks to arrive)
+    auto step = [&](Ops& cur, Ops& nxt, int c) __attribute__((always_inline)) {
+        const long nc = n * a.NC + c;
+#pragma unroll
+        for (int j = 0; j < MW; ++j) {
+            const int m = wave + 4 * j;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.hs[(nc * D + 16 * m + 4 * lg + e) * D + col] = hr[j][e];
+            sH[m][lane] = hr[j];
         }
-        __syncthreads();
-        // G = Gam_C G + Q^T diag(Gam) dO - K^T diag(b Gam) dR  (row tid / 2, columns 4 (tid % 2) + {0..3})
-        {
-            const int r = tid / 2, cc = 4 * (tid % 2);
-            fx4 acc = *reinterpret_cast<const fx4*>(&sG[r * SW + cc]);
-            const float gc = ssc[BC - 1];
-            acc.x *= gc, acc.y *= gc, acc.z *= gc, acc.w *= gc;
-#pragma unroll 8
-            for (int t = 0; t < BC; ++t) {
-                const float qv = sQ[t * LD + r], kv = sK[t * LD + r];
-                const fx4 o4 = *reinterpret_cast<const fx4*>(&sdOg[t * SW + cc]);
-                const fx4 d4 = *reinterpret_cast<const fx4*>(&sdRb[t * SW + cc]);
-                acc.x = fmaf(qv, o4.x, fmaf(-kv, d4.x, acc.x));
-                acc.y = fmaf(qv, o4.y, fmaf(-kv, d4.y, acc.y));
-                acc.z = fmaf(qv, o4.z, fmaf(-kv, d4.z, acc.z));
-                acc.w = fmaf(qv, o4.w, fmaf(-kv, d4.w, acc.w));
-            }
-            __syncthreads();
-            *reinterpret_cast<fx4*>(&sG[r * SW + cc]) = acc;
+        lds_sync();
+        fetch(nxt, min(c + 2, a.NC - 1));  // the last ones re-read valid rows
+        fx4 p = f4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const fx4 hb = sH[m][lane];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) p = mma4(cur.w[m][s], hb[s], p);
         }
+        const fx4 dl = cur.u - p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a.dl[(nc * BC + 16 * wave + 4 * lg + e) * D + col] = dl[e];
+        sD[wave][lane] = dl;
+        lds_sync();
+#pragma unroll
+        for (int j = 0; j < MW; ++j) {
+            fx4 acc = hr[j] * cur.gc;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const fx4 db = sD[tt][lane];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc = mma4(cur.ek[j][tt][s], db[s], acc);
+            }
+            hr[j] = acc;
+        }
+    };
+    Ops o0, o1, o2;
+    fetch(o0, 0);
+    fetch(o1, min(1, a.NC - 1));
+    int c = 0;
+    for (; c + 2 < a.NC; c += 3) {
+        step(o0, o2, c);
+        step(o1, o0, c + 1);
+        step(o2, o1, c + 2);
     }
+    if (c < a.NC) step(o0, o2, c);
+    if (c + 1 < a.NC) step(o1, o0, c + 1);
+}
+
+// Reverse chain: stores every chunk's end gradient G (gs) and dR (dr), writes dS_0.
+//   dR = M1 dO + M2 G                      wave w: chunk rows [16 w, 16 w + 16)
+//   G = Gam_C G + (diag(Gam) Q)^T dO - (diag(b Gam) K)^T dR
+template <typename In, int D>
+__global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
+    constexpr int MT = D / 16, MW = MT / 4;
+    __shared__ fx4 sG[MT][64];
+    __shared__ fx4 sR[4][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lg = lane >> 4, lc = lane & 15;
+    long n;
+    int sl;
+    slice_of(D / CW, a.B * a.H, n, sl);
+    const long b = n / a.H;
+    const int h = (int)(n % a.H), T = a.T;
+    const int col = CW * sl + lc;
+    fx4 gr[MW];
+#pragma unroll
+    for (int j = 0; j < MW; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            gr[j][e] = a.d_state ? a.d_state[(n * D + 16 * (wave + 4 * j) + 4 * lg + e) * D + col] : 0.f;
+    // dO tiles of a chunk (rows 16 tt + 4 lg + e, column col), zero past T
+    auto fetch_do = [&](fx4* d, int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = c * BC + 16 * tt + 4 * lg + e;
+                d[tt][e] = t < T ? a.d_o[((b * T + t) * a.H + h) * (long)D + col] : 0.f;
+            }
+    };
+    struct Ops {
+        fx4 m1[4], m2[MT], qg[MW][4], kb[MW][4], d[4];
+        float gc;
+    };
+    auto fetch = [&](Ops& o, int c) __attribute__((always_inline)) {
+        const long nc = n * a.NC + c;
+        const float* p1 = a.m1 + (nc * 4 + wave) * 4 * 256 + 4 * lane;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o.m1[j] = j >= wave ? ld4g(p1 + 256 * j) : f4(0.f, 0.f, 0.f, 0.f);
+        const float* p2 = a.m2 + (nc * 4 + wave) * MT * 256 + 4 * lane;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) o.m2[m] = ld4g(p2 + 256 * m);
+#pragma unroll
+        for (int j = 0; j < MW; ++j) {
+            const long ro = (nc * MT + wave + 4 * j) * 4 * 256 + 4 * lane;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                o.qg[j][tt] = ld4g(a.qgt + ro + 256 * tt);
+                o.kb[j][tt] = ld4g(a.kbt + ro + 256 * tt);
+            }
+        }
+        fetch_do(o.d, c);
+        o.gc = ld_vec(a.sc + nc * SCN * BC + BC - 1);
+    };
+    auto step = [&](Ops& cur, Ops& nxt, int c) __attribute__((always_inline)) {
+        const long nc = n * a.NC + c;
+#pragma unroll
+        for (int j = 0; j < MW; ++j) {
+            const int m = wave + 4 * j;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.gs[(nc * D + 16 * m + 4 * lg + e) * D + col] = gr[j][e];
+            sG[m][lane] = gr[j];
+        }
+        lds_sync();
+        fetch(nxt, max(c - 1, 0));  // the last one re-reads valid rows
+        fx4 r = f4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (j >= wave) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) r = mma4(cur.m1[j][s], cur.d[j][s], r);
+            }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const fx4 gb = sG[m][lane];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) r = mma4(cur.m2[m][s], gb[s], r);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a.dr[(nc * BC + 16 * wave + 4 * lg + e) * D + col] = r[e];
+        sR[wave][lane] = r;
+        lds_sync();
+#pragma unroll
+        for (int j = 0; j < MW; ++j) {
+            fx4 acc = gr[j] * cur.gc, neg = f4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const fx4 rb = sR[tt][lane];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    acc = mma4(cur.qg[j][tt][s], cur.d[tt][s], acc);
+                    neg = mma4(cur.kb[j][tt][s], rb[s], neg);
+                }
+            }
+            gr[j] = acc - neg;
+        }
+    };
+    Ops o0, o1;
+    fetch(o0, a.NC - 1);
+    int c = a.NC - 1;
+    for (; c >= 1; c -= 2) {
+        step(o0, o1, c);
+        step(o1, o0, c - 1);
+    }
+    if (c == 0) step(o0, o1, 0);
     if (a.dstate0) {
-        __syncthreads();
-        for (int idx = tid; idx < D * SW; idx += 256)
-            a.dstate0[(n * D + idx / SW) * D + c0 + idx % SW] = sG[idx];
+#pragma unroll
+        for (int j = 0; j < MW; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                a.dstate0[(n * D + 16 * (wave + 4 * j) + 4 * lg + e) * D + col] = gr[j][e];
     }
 }
 
@@ -958,7 +1002,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
 
 template <typename In, int D>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
-    const dim3 gc((unsigned)a.NC, (unsigned)a.H, (unsigned)a.B), gs((unsigned)(a.B * a.H * (D / SW)));
+    const dim3 gc((unsigned)a.NC, (unsigned)a.H, (unsigned)a.B), gs((unsigned)(a.B * a.H * (D / CW)));
     hipLaunchKernelGGL((bwd_prep<In, D>), gc, dim3(64 * (D / 16)), 0, stream, a);
     hipError_t e = hipGetLastError();
     profile_mark(stream);
