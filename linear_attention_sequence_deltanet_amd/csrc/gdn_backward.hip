@@ -492,25 +492,27 @@ __global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
         fx4 w[MT], ek[MW][4], u;
         float gc;
     };
+    const float* wb = a.w + wave * MT * 256 + 4 * lane;  // + chunk * 4 MT 256
+    const float* eb = a.ekt + wave * 4 * 256 + 4 * lane;  // + (chunk MT + 4 j) 4 256
+    const float* ub = a.u + (wave * MT + sl) * 256 + 4 * lane;
     auto fetch = [&](Ops& o, int c) __attribute__((always_inline)) {
         const long nc = n * a.NC + c;
-        const float* wp = a.w + (nc * 4 + wave) * MT * 256 + 4 * lane;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) o.w[m] = ld4g(wp + 256 * m);
+        for (int m = 0; m < MT; ++m) o.w[m] = ld4g(wb + nc * 4 * MT * 256 + 256 * m);
 #pragma unroll
-        for (int j = 0; j < MW; ++j) {
-            const float* ep = a.ekt + (nc * MT + wave + 4 * j) * 4 * 256 + 4 * lane;
+        for (int j = 0; j < MW; ++j)
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) o.ek[j][tt] = ld4g(ep + 256 * tt);
-        }
-        o.u = ld4g(a.u + ((nc * 4 + wave) * MT + sl) * 256 + 4 * lane);
+            for (int tt = 0; tt < 4; ++tt) o.ek[j][tt] = ld4g(eb + (nc * MT + 4 * j) * 4 * 256 + 256 * tt);
+        o.u = ld4g(ub + nc * 4 * MT * 256);
         o.gc = ld_vec(a.sc + nc * SCN * BC + BC - 1);
     };
-    // one chunk: `cur` holds its operands, `nxt` receives those of the chunk
+    // One chunk: `cur` holds its operands, `nxt` receives those of the chunk
     // two ahead (three buffers used in turn, so no register copies wait on
-    // loads still in flight and each load has two chunks to arrive)
+    // loads still in flight).  The loads are spread one per matrix-core group:
+    // issued together, the four waves' 1 KB fragments queue at the CU's load
+    // unit and the waves stall at issue while the matrix cores idle.
     auto step = [&](Ops& cur, Ops& nxt, int c) __attribute__((always_inline)) {
-        const long nc = n * a.NC + c;
+        const long nc = n * a.NC + c, nn = n * a.NC + min(c + 2, a.NC - 1);
 #pragma unroll
         for (int j = 0; j < MW; ++j) {
             const int m = wave + 4 * j;
@@ -519,14 +521,17 @@ __global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
             sH[m][lane] = hr[j];
         }
         lds_sync();
-        fetch(nxt, min(c + 2, a.NC - 1));  // the last ones re-read valid rows
         fx4 p = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const fx4 hb = sH[m][lane];
+            nxt.w[m] = ld4g(wb + nn * 4 * MT * 256 + 256 * m);
 #pragma unroll
             for (int s = 0; s < 4; ++s) p = mma4(cur.w[m][s], hb[s], p);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        nxt.u = ld4g(ub + nn * 4 * MT * 256);
+        nxt.gc = ld_vec(a.sc + nn * SCN * BC + BC - 1);
         const fx4 dl = cur.u - p;
 #pragma unroll
         for (int e = 0; e < 4; ++e) a.dl[(nc * BC + 16 * wave + 4 * lg + e) * D + col] = dl[e];
@@ -538,8 +543,10 @@ __global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 const fx4 db = sD[tt][lane];
+                nxt.ek[j][tt] = ld4g(eb + (nn * MT + 4 * j) * 4 * 256 + 256 * tt);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) acc = mma4(cur.ek[j][tt][s], db[s], acc);
+                __builtin_amdgcn_sched_barrier(0);
             }
             hr[j] = acc;
         }
@@ -594,28 +601,30 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
         fx4 m1[4], m2[MT], qg[MW][4], kb[MW][4], d[4];
         float gc;
     };
+    const float* m1b = a.m1 + wave * 4 * 256 + 4 * lane;    // + chunk 16 256
+    const float* m2b = a.m2 + wave * MT * 256 + 4 * lane;   // + chunk 4 MT 256
+    const long tb = wave * 4 * 256 + 4 * lane;              // + (chunk MT + 4 j) 4 256
     auto fetch = [&](Ops& o, int c) __attribute__((always_inline)) {
         const long nc = n * a.NC + c;
-        const float* p1 = a.m1 + (nc * 4 + wave) * 4 * 256 + 4 * lane;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o.m1[j] = j >= wave ? ld4g(p1 + 256 * j) : f4(0.f, 0.f, 0.f, 0.f);
-        const float* p2 = a.m2 + (nc * 4 + wave) * MT * 256 + 4 * lane;
+        for (int j = 0; j < 4; ++j) o.m1[j] = j >= wave ? ld4g(m1b + nc * 16 * 256 + 256 * j) : f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) o.m2[m] = ld4g(p2 + 256 * m);
+        for (int m = 0; m < MT; ++m) o.m2[m] = ld4g(m2b + nc * 4 * MT * 256 + 256 * m);
 #pragma unroll
-        for (int j = 0; j < MW; ++j) {
-            const long ro = (nc * MT + wave + 4 * j) * 4 * 256 + 4 * lane;
+        for (int j = 0; j < MW; ++j)
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                o.qg[j][tt] = ld4g(a.qgt + ro + 256 * tt);
-                o.kb[j][tt] = ld4g(a.kbt + ro + 256 * tt);
+                o.qg[j][tt] = ld4g(a.qgt + tb + (nc * MT + 4 * j) * 4 * 256 + 256 * tt);
+                o.kb[j][tt] = ld4g(a.kbt + tb + (nc * MT + 4 * j) * 4 * 256 + 256 * tt);
             }
-        }
         fetch_do(o.d, c);
         o.gc = ld_vec(a.sc + nc * SCN * BC + BC - 1);
     };
+    // one chunk; as in the forward chain, the next operands' loads (two
+    // chunks ahead) are spread over the matrix-core groups
     auto step = [&](Ops& cur, Ops& nxt, int c) __attribute__((always_inline)) {
-        const long nc = n * a.NC + c;
+        const int cn = max(c - 2, 0);
+        const long nc = n * a.NC + c, nn = n * a.NC + cn;
 #pragma unroll
         for (int j = 0; j < MW; ++j) {
             const int m = wave + 4 * j;
@@ -624,23 +633,27 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
             sG[m][lane] = gr[j];
         }
         lds_sync();
-        fetch(nxt, max(c - 1, 0));  // the last one re-reads valid rows
         fx4 r = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             if (j >= wave) {
+                nxt.m1[j] = ld4g(m1b + nn * 16 * 256 + 256 * j);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) r = mma4(cur.m1[j][s], cur.d[j][s], r);
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const fx4 gb = sG[m][lane];
+            nxt.m2[m] = ld4g(m2b + nn * 4 * MT * 256 + 256 * m);
 #pragma unroll
             for (int s = 0; s < 4; ++s) r = mma4(cur.m2[m][s], gb[s], r);
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) a.dr[(nc * BC + 16 * wave + 4 * lg + e) * D + col] = r[e];
         sR[wave][lane] = r;
+        nxt.gc = ld_vec(a.sc + nn * SCN * BC + BC - 1);
         lds_sync();
 #pragma unroll
         for (int j = 0; j < MW; ++j) {
@@ -648,23 +661,36 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 const fx4 rb = sR[tt][lane];
+                nxt.qg[j][tt] = ld4g(a.qgt + tb + (nn * MT + 4 * j) * 4 * 256 + 256 * tt);
+                nxt.kb[j][tt] = ld4g(a.kbt + tb + (nn * MT + 4 * j) * 4 * 256 + 256 * tt);
+                if (j == 0) {  // the dO tiles of chunk cn
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = cn * BC + 16 * tt + 4 * lg + e;
+                        nxt.d[tt][e] = t < T ? a.d_o[((b * T + t) * a.H + h) * (long)D + col] : 0.f;
+                    }
+                }
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     acc = mma4(cur.qg[j][tt][s], cur.d[tt][s], acc);
                     neg = mma4(cur.kb[j][tt][s], rb[s], neg);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
             gr[j] = acc - neg;
         }
     };
-    Ops o0, o1;
+    Ops o0, o1, o2;
     fetch(o0, a.NC - 1);
+    fetch(o1, max(a.NC - 2, 0));
     int c = a.NC - 1;
-    for (; c >= 1; c -= 2) {
-        step(o0, o1, c);
+    for (; c >= 2; c -= 3) {
+        step(o0, o2, c);
         step(o1, o0, c - 1);
+        step(o2, o1, c - 2);
     }
-    if (c == 0) step(o0, o1, 0);
+    if (c >= 0) step(o0, o2, c);
+    if (c >= 1) step(o1, o0, c - 1);
     if (a.dstate0) {
 #pragma unroll
         for (int j = 0; j < MW; ++j)
