@@ -521,35 +521,43 @@ __global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
             sH[m][lane] = hr[j];
         }
         lds_sync();
-        fx4 p = f4(0.f, 0.f, 0.f, 0.f);
+        // all LDS tiles first: a read inside a pinned group would expose its latency
+        fx4 hb[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) hb[m] = sH[m][lane];
+        fx4 p[2] = {f4(0.f, 0.f, 0.f, 0.f), f4(0.f, 0.f, 0.f, 0.f)};  // even / odd m
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const fx4 hb = sH[m][lane];
             nxt.w[m] = ld4g(wb + nn * 4 * MT * 256 + 256 * m);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) p = mma4(cur.w[m][s], hb[s], p);
+            for (int s = 0; s < 4; ++s) p[m & 1] = mma4(cur.w[m][s], hb[m][s], p[m & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
         nxt.u = ld4g(ub + nn * 4 * MT * 256);
         nxt.gc = ld_vec(a.sc + nn * SCN * BC + BC - 1);
-        const fx4 dl = cur.u - p;
+        const fx4 dl = cur.u - (p[0] + p[1]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) a.dl[(nc * BC + 16 * wave + 4 * lg + e) * D + col] = dl[e];
         sD[wave][lane] = dl;
         lds_sync();
+        fx4 db[4];
 #pragma unroll
-        for (int j = 0; j < MW; ++j) {
-            fx4 acc = hr[j] * cur.gc;
+        for (int tt = 0; tt < 4; ++tt) db[tt] = sD[tt][lane];
+        fx4 acc[MW];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const fx4 db = sD[tt][lane];
+        for (int j = 0; j < MW; ++j) acc[j] = hr[j] * cur.gc;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+            for (int j = 0; j < MW; ++j) {
                 nxt.ek[j][tt] = ld4g(eb + (nn * MT + 4 * j) * 4 * 256 + 256 * tt);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) acc = mma4(cur.ek[j][tt][s], db[s], acc);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int s = 0; s < 4; ++s) acc[j] = mma4(cur.ek[j][tt][s], db[tt][s], acc[j]);
             }
-            hr[j] = acc;
+            __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int j = 0; j < MW; ++j) hr[j] = acc[j];
     };
     Ops o0, o1, o2;
     fetch(o0, 0);
@@ -633,52 +641,59 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
             sG[m][lane] = gr[j];
         }
         lds_sync();
-        fx4 r = f4(0.f, 0.f, 0.f, 0.f);
+        fx4 gb[MT];  // all LDS tiles first
+#pragma unroll
+        for (int m = 0; m < MT; ++m) gb[m] = sG[m][lane];
+        fx4 rp[3] = {f4(0.f, 0.f, 0.f, 0.f), f4(0.f, 0.f, 0.f, 0.f), f4(0.f, 0.f, 0.f, 0.f)};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             if (j >= wave) {
                 nxt.m1[j] = ld4g(m1b + nn * 16 * 256 + 256 * j);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) r = mma4(cur.m1[j][s], cur.d[j][s], r);
+                for (int s = 0; s < 4; ++s) rp[2] = mma4(cur.m1[j][s], cur.d[j][s], rp[2]);
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const fx4 gb = sG[m][lane];
             nxt.m2[m] = ld4g(m2b + nn * 4 * MT * 256 + 256 * m);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) r = mma4(cur.m2[m][s], gb[s], r);
+            for (int s = 0; s < 4; ++s) rp[m & 1] = mma4(cur.m2[m][s], gb[m][s], rp[m & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
+        const fx4 r = rp[0] + rp[1] + rp[2];
 #pragma unroll
         for (int e = 0; e < 4; ++e) a.dr[(nc * BC + 16 * wave + 4 * lg + e) * D + col] = r[e];
         sR[wave][lane] = r;
         nxt.gc = ld_vec(a.sc + nn * SCN * BC + BC - 1);
         lds_sync();
+        fx4 rbs[4];
 #pragma unroll
-        for (int j = 0; j < MW; ++j) {
-            fx4 acc = gr[j] * cur.gc, neg = f4(0.f, 0.f, 0.f, 0.f);
+        for (int tt = 0; tt < 4; ++tt) rbs[tt] = sR[tt][lane];
+        fx4 acc[MW], neg[MW];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const fx4 rb = sR[tt][lane];
+        for (int j = 0; j < MW; ++j) acc[j] = gr[j] * cur.gc, neg[j] = f4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const fx4 rb = rbs[tt];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {  // the dO tile tt of chunk cn
+                const int t = cn * BC + 16 * tt + 4 * lg + e;
+                nxt.d[tt][e] = t < T ? a.d_o[((b * T + t) * a.H + h) * (long)D + col] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < MW; ++j) {
                 nxt.qg[j][tt] = ld4g(a.qgt + tb + (nn * MT + 4 * j) * 4 * 256 + 256 * tt);
                 nxt.kb[j][tt] = ld4g(a.kbt + tb + (nn * MT + 4 * j) * 4 * 256 + 256 * tt);
-                if (j == 0) {  // the dO tiles of chunk cn
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = cn * BC + 16 * tt + 4 * lg + e;
-                        nxt.d[tt][e] = t < T ? a.d_o[((b * T + t) * a.H + h) * (long)D + col] : 0.f;
-                    }
-                }
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    acc = mma4(cur.qg[j][tt][s], cur.d[tt][s], acc);
-                    neg = mma4(cur.kb[j][tt][s], rb[s], neg);
+                    acc[j] = mma4(cur.qg[j][tt][s], cur.d[tt][s], acc[j]);
+                    neg[j] = mma4(cur.kb[j][tt][s], rb[s], neg[j]);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
-            gr[j] = acc - neg;
+            __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int j = 0; j < MW; ++j) gr[j] = acc[j] - neg[j];
     };
     Ops o0, o1, o2;
     fetch(o0, a.NC - 1);
