@@ -618,23 +618,34 @@ struct FPlan {
     int NC, S, G;
 };
 
-// One segment when the heads alone give a workgroup per CU or the sequence is
-// short; otherwise about sqrt(NC / 2) chunks per segment, balancing the parallel
-// segment work against the sequential combine.
+// Segmentation by a cost model of the three kernels on the 256 CUs of an
+// MI355X, measured at d = 128: a chunk takes about 6.5 us in the output pass and
+// 5.7 us in the summary pass (one workgroup per CU; more workgroups than CUs run
+// in further rounds), a combine step about 1.2 us per round of its D/16
+// workgroups per head, and the two extra launches about 5 us together.  One
+// segment runs the output pass alone.  Candidates: G = 1..32 chunks per segment
+// and the G that fill k rounds of workgroups exactly.
 FPlan fused_plan(int B, int T, int H) {
+    constexpr long kCUs = 256;
+    constexpr double kOut = 6.5, kSum = 5.7, kComb = 1.2, kLaunch = 5.0;
     FPlan p;
     p.NC = (T + FC - 1) / FC;
     const long BH = (long)B * H;
-    if (BH >= 256 || p.NC <= 8) {
-        p.S = 1;
-        p.G = p.NC;
-        return p;
+    auto rounds = [](long wgs) { return (double)((wgs + kCUs - 1) / kCUs); };
+    p.S = 1;
+    p.G = p.NC;
+    double best = p.NC * kOut * rounds(BH);
+    auto consider = [&](long G) {
+        if (G < 1 || G >= p.NC) return;
+        const long S = (p.NC + G - 1) / G;
+        const double t = G * (kOut + kSum) * rounds(S * BH) + S * kComb * rounds(BH * 8) + kLaunch;
+        if (t < best) best = t, p.G = (int)G, p.S = (int)S;
+    };
+    for (long G = 1; G <= 32; ++G) consider(G);
+    for (long k = 1; k <= 16; ++k) {
+        const long segs = k * kCUs / BH;  // segments per head that fill k rounds
+        if (segs >= 2) consider((p.NC + segs - 1) / segs);
     }
-    int G = 1;
-    while ((long)G * G * 2 < p.NC) ++G;
-    if (G < 4) G = 4;
-    p.G = G;
-    p.S = (p.NC + G - 1) / G;
     return p;
 }
 
