@@ -238,27 +238,39 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     // ragged last chunk.
     uint4 rq[NL], rk[NL], rv[NL];
     float rg = 0.f, rb = 0.f;
-    auto issue_loads = [&](int c) {
+    // Loads of one tensor's chunk rows (and, with K, the gates).  The three
+    // tensors of the next chunk are issued at three points of the current one:
+    // issued together, the waves' loads queue at the CU's load unit and stall
+    // the waves at issue.
+    auto chunk_rsrc = [&](const bf16_t* x, int c) {
         const long t0 = (long)c * FC;
         const int n = (int)min((long)FC, (long)T - t0);
         const long base = (((long)b * T + t0) * H + h) * D;  // scalar
-        const unsigned bytes = (unsigned)(((n - 1) * HD + D) * 2);
-        const rsrc_t rsq = make_rsrc(q + base, bytes), rsk = make_rsrc(k + base, bytes),
-                     rsv = make_rsrc(v + base, bytes);
+        return make_rsrc(x + base, (unsigned)(((n - 1) * HD + D) * 2));
+    };
+    auto issue = [&](uint4* r, const bf16_t* x, int c) {
+        const rsrc_t rs = chunk_rsrc(x, c);
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
-            const int idx = tid + NTH * i, r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-            const unsigned off = (unsigned)((r * (int)HD + c8) * 2);
-            if (OUT) rq[i] = buf_load16(rsq, off);
-            rk[i] = buf_load16(rsk, off);
-            rv[i] = buf_load16(rsv, off);
+            const int idx = tid + NTH * i, rr = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+            r[i] = buf_load16(rs, (unsigned)((rr * (int)HD + c8) * 2));
         }
+    };
+    auto issue_gates = [&](int c) {
         if (wave == 0) {
+            const long t0 = (long)c * FC;
+            const int n = (int)min((long)FC, (long)T - t0);
             const long tok = ((long)b * T + t0) * H + h;
             const unsigned gbytes = (unsigned)(((n - 1) * H + 1) * 4);
             rg = buf_load4(make_rsrc(g + tok, gbytes), (unsigned)(lane * H * 4));
             rb = buf_load4(make_rsrc(beta + tok, gbytes), (unsigned)(lane * H * 4));
         }
+    };
+    auto issue_loads = [&](int c) {
+        if (OUT) issue(rq, q, c);
+        issue(rk, k, c);
+        issue(rv, v, c);
+        issue_gates(c);
     };
     issue_loads(c_begin);
 
@@ -305,7 +317,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             sCF[2][lane] = lane < 32 ? __expf(g32 - gv) : 0.f;
             sCF[3][lane] = lane < 48 ? __expf(g48 - gv) : 0.f;
         }
-        if (c + 1 < c_end) issue_loads(c + 1);
+        const bool more = c + 1 < c_end;
+        if (more) {
+            issue(rk, k, c + 1);
+            issue_gates(c + 1);
+        }
         lds_sync();
 
         // ---- Gram tiles.  Waves 0-3: diagonal block w of K K^T and the
@@ -437,6 +453,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             }
         }
         lds_sync();
+        if (more) issue(rv, v, c + 1);
 
         // ---- blocked solve with the right-hand side in fp32:
         //   Y_b = B_b - sum_{j<b} A_bj X_j,  X_b = Y_b + N_bb Y_b
@@ -492,6 +509,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 sW[(16 * bb + 4 * lg + e) * LD + colw + lc] = static_cast<_Float16>(res[1][bb][e]);
         }
         lds_sync();  // -W and K^T complete
+        if (OUT && more) issue(rq, q, c + 1);
 
         // ---- state update for this wave's columns (no workgroup barrier).
         // The state and Delta enter the products as fp16 B operands built from
