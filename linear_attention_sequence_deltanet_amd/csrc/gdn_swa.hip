@@ -237,9 +237,13 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
     // staging.  K: rows 16 i + tid / 16 (i < 4), chunk tid % 16 (16 bytes).
     // V: key pair kp = tid % 32 (keys 2 kp, 2 kp + 1), chunks tid / 32 + 8 i
     // (i < 2), so the transposed LDS writes of a wave fill 32 consecutive
-    // dwords of one row.
+    // dwords of one row.  Within each 32-key step the keys of V^T are stored
+    // in the order the S^T tiles hold them (key 32 j + 16 u + 4 g + e at
+    // position 32 j + 8 g + 4 u + e), so a lane's 8 keys of a step are one
+    // 16-byte read.
     const int kch = tid % 16, krw = tid / 16;
     const int kp = tid % 32, vch = tid / 32;
+    const int kq = 2 * kp, vpos = (kq & 32) | (((kq >> 2) & 3) << 3) | (((kq >> 4) & 1) << 2) | (kq & 3);
     uint4 pk[4], pv[4];
     auto load_block = [&](int j0) {
 #pragma unroll
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
             const int d0 = (vch + 8 * i2) * 8;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<unsigned*>(&sV[buf][(d0 + e) * VLD + 2 * kp]) = pack_h2(lo[e], hi[e]);
+                *reinterpret_cast<unsigned*>(&sV[buf][(d0 + e) * VLD + vpos]) = pack_h2(lo[e], hi[e]);
         }
     };
 
@@ -349,15 +353,12 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
                     for (int dt = 0; dt < 8; ++dt) acc[dt][qt] *= alpha;
                 }
             }
-            const _Float16* vt_base = &sV[buf][c * VLD + 4 * g];
+            const _Float16* vt_base = &sV[buf][c * VLD + 8 * g];
 #pragma unroll
             for (int j2 = 0; j2 < 2; ++j2) {
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt) {
-                    const _Float16* vp = vt_base + 16 * dt * VLD + 32 * j2;
-                    const H4 v0 = *reinterpret_cast<const H4*>(vp);
-                    const H4 v1 = *reinterpret_cast<const H4*>(vp + 16);
-                    const H8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                    const H8 va = *reinterpret_cast<const H8*>(vt_base + 16 * dt * VLD + 32 * j2);
                     acc[dt][0] = MF::k32(va, pb[0][j2], acc[dt][0]);
                     acc[dt][1] = MF::k32(va, pb[1][j2], acc[dt][1]);
                 }
