@@ -657,7 +657,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
     using M = Mfma<_Float16>;
     using F8 = M::frag8;
     constexpr int NS = D / 16, LS = D + 8;
-    constexpr int NB = 3;  // segments whose summaries are in flight
+    constexpr int NB = 2;  // segments whose summaries are in flight
     // fp16 high / low parts of the chained state slice, [col][key], double-buffered
     __shared__ __align__(16) _Float16 sHi[2][16 * LS], sLo[2][16 * LS];
 
@@ -689,18 +689,26 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
         F8 hi[D / 32], lo[D / 32];  // rows of M (A operand)
         f32x4 r;                    // R (C layout)
     };
-    auto load = [&](Pre& p, int s) {
-        const float* sm = sw.summ + ((long)min(s, S - 1) * BH + bh) * D * 2 * D;
-        const _Float16* mh = reinterpret_cast<const _Float16*>(sm + D * D);
+    auto sum_of = [&](int s) { return sw.summ + ((long)min(s, S - 1) * BH + bh) * D * 2 * D; };
+    auto load_r = [&](Pre& p, const float* sm) {
         p.r = *reinterpret_cast<const f32x4*>(sm + ((slice * (D / 16) + wave) * 64 + lane) * 4);
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-            const int off = ((wave * (D / 32) + kk) * 64 + lane) * 8;
-            p.hi[kk] = *reinterpret_cast<const F8*>(mh + off);
-            p.lo[kk] = *reinterpret_cast<const F8*>(mh + D * D + off);
-        }
     };
-    auto apply = [&](const Pre& p, int s) {
+    auto load_m = [&](Pre& p, const float* sm, int kk) {
+        const _Float16* mh = reinterpret_cast<const _Float16*>(sm + D * D);
+        const int off = ((wave * (D / 32) + kk) * 64 + lane) * 8;
+        p.hi[kk] = *reinterpret_cast<const F8*>(mh + off);
+        p.lo[kk] = *reinterpret_cast<const F8*>(mh + D * D + off);
+    };
+    auto load = [&](Pre& p, int s) {
+        const float* sm = sum_of(s);
+        load_r(p, sm);
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) load_m(p, sm, kk);
+    };
+    // applies segment s from p and refills p with segment `next`, each
+    // fragment right after its product: issued together, the waves' loads
+    // would queue at the CU's load unit and stall the waves at issue
+    auto apply = [&](Pre& p, int s, int next) {
         float* dst = sw.sst + ((long)s * BH + bh) * D * D;
 #pragma unroll
         for (int e = 0; e < 4; ++e) dst[(16 * wave + 4 * lg + e) * D + col] = hs[e];
@@ -719,14 +727,22 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
         st4<_Float16>(&bh_[lc * LS + 16 * wave + 4 * lg], hi);
         st4<_Float16>(&bl_[lc * LS + 16 * wave + 4 * lg], cvt4<_Float16>(lo));
         lds_sync();
-        f32x4 a0 = p.r, a1 = zero4(), a2 = zero4();  // three independent chains
+        F8 bhi[D / 32], blo[D / 32];
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
-            const F8 bhi = ld8<_Float16>(&bh_[lc * LS + 32 * kk + 8 * lg]);
-            const F8 blo = ld8<_Float16>(&bl_[lc * LS + 32 * kk + 8 * lg]);
-            a0 = M::k32(p.hi[kk], bhi, a0);
-            a1 = M::k32(p.hi[kk], blo, a1);
-            a2 = M::k32(p.lo[kk], bhi, a2);
+            bhi[kk] = ld8<_Float16>(&bh_[lc * LS + 32 * kk + 8 * lg]);
+            blo[kk] = ld8<_Float16>(&bl_[lc * LS + 32 * kk + 8 * lg]);
+        }
+        const float* nsm = sum_of(next);
+        f32x4 a0 = p.r, a1 = zero4(), a2 = zero4();  // three independent chains
+        load_r(p, nsm);
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            a0 = M::k32(p.hi[kk], bhi[kk], a0);
+            a1 = M::k32(p.hi[kk], blo[kk], a1);
+            a2 = M::k32(p.lo[kk], bhi[kk], a2);
+            load_m(p, nsm, kk);
+            __builtin_amdgcn_sched_barrier(0);
         }
         hs = a0 + (a1 + a2);
     };
@@ -739,14 +755,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
     int s = 0;
     for (; s + NB <= S; s += NB) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            apply(pb[i], s + i);
-            load(pb[i], s + i + NB);
-        }
+        for (int i = 0; i < NB; ++i) apply(pb[i], s + i, s + i + NB);
     }
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i)
-        if (s + i < S) apply(pb[i], s + i);
+        if (s + i < S) apply(pb[i], s + i, S - 1);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         state_out[((long)bh * D + 16 * wave + 4 * lg + e) * D + col] = hs[e];
