@@ -73,9 +73,8 @@ struct BwdArgs {
     float* dstate0;        // or null
     // workspace, per series n = b H + h and chunk c (index n * NC + c):
     float* sc;   // [.][SCN][BC]: Gam, e, b, gam
-    float* ti;   // [.][BC][BC]
-    float* pm;   // [.][BC][BC]  lower(L o QK^T)
-    float* lkk;  // [.][BC][BC]  strict_lower(L o KK^T)
+    float* pm;   // [.][BC][BC]  lower(L o QK^T), lower 16x16 tiles only
+    float* lkk;  // [.][BC][BC]  strict_lower(L o KK^T), lower 16x16 tiles only
     float* w;    // [.] W,  row-operand fragments (see below)
     float* u;    // [.] U,  output-layout tiles
     float* hs;   // [.][D][D]    chunk start states
@@ -288,11 +287,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_prep(const BwdArgs a) {
                 }
             }
         }
-        // zero upper tiles of P and lkk in the workspace
-        for (int idx = tid; idx < BC * BC; idx += NT) {
-            const int r = idx / BC, s = idx % BC;
-            if (s / 16 > r / 16) lkp[idx] = 0.f, pmp[idx] = 0.f;
-        }
     }
     // transposes the chains take as row operands, as fragments (m, tt) of the
     // D x 64 matrices: (diag(e) K)^T, (diag(Gam) Q)^T, (diag(b Gam) K)^T
@@ -357,14 +351,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_prep(const BwdArgs a) {
             for (int e = 0; e < 4; ++e) sTi[(16 * i + 4 * lg + e) * LC + 16 * j + lc] = -t[e];
         }
         __syncthreads();
-    }
-    {
-        float* tip = a.ti + nc * BC * BC;
-        for (int idx = 4 * tid; idx < BC * BC; idx += 4 * NT) {
-            const int r = idx / BC, s = idx % BC;
-            const fx4 v = s / 16 > r / 16 ? f4(0.f, 0.f, 0.f, 0.f) : *reinterpret_cast<const fx4*>(&sTi[r * LC + s]);
-            *reinterpret_cast<fx4*>(tip + idx) = v;
-        }
     }
 
     // ---- W, U, M2 for column tile `wave`
@@ -1066,7 +1052,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
 
 size_t backward_workspace_bytes(int B, int T, int H, int D) {
     const size_t NC = (size_t)(T + BC - 1) / BC, chunks = NC * B * H;
-    const size_t per = SCN * BC + 4 * BC * BC + 8 * (size_t)BC * D + 2 * (size_t)D * D;
+    const size_t per = SCN * BC + 3 * BC * BC + 8 * (size_t)BC * D + 2 * (size_t)D * D;
     return chunks * per * sizeof(float);
 }
 
@@ -1083,7 +1069,6 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, int dtyp
     const size_t chunks = (size_t)a.NC * B * H;
     float* p = static_cast<float*>(ws);
     a.sc = p, p += chunks * SCN * BC;
-    a.ti = p, p += chunks * BC * BC;
     a.pm = p, p += chunks * BC * BC;
     a.lkk = p, p += chunks * BC * BC;
     a.w = p, p += chunks * BC * D;
