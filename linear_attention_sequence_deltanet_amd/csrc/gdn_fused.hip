@@ -498,15 +498,23 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                     res[t][bb] = acc[t];
                 }
             }
+            // -W to LDS row-major.  Lane (lc, lg) holds rows 4 lg + e of key
+            // column lc; as an A operand that tile is its transpose, so a product
+            // with the 16x16 identity (exact) leaves each lane 4 consecutive keys
+            // of token lc: one 8-byte store instead of four 2-byte ones.
+            H4 identh;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) identh[e] = static_cast<_Float16>(4 * lg + e == lc ? 1.f : 0.f);
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+                st4<_Float16>(&sW[(16 * bb + lc) * LD + colw + 4 * lg],
+                              cvt4<_Float16>(MF::k16(xh[1][bb], identh, zero4())));
         }
         f32x4 u[TPW][4];
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
             u[0][bb] = res[0][bb];
             if (TPW == 2) u[TPW - 1][bb] = zero4();  // identity columns: no U
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                sW[(16 * bb + 4 * lg + e) * LD + colw + lc] = static_cast<_Float16>(res[1][bb][e]);
         }
         lds_sync();  // -W and K^T complete
         if (OUT && more) issue(rq, q, c + 1);
