@@ -787,8 +787,16 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
             if (ok) {
                 const float br = scp[2 * BC + r];
                 *reinterpret_cast<fx4*>(a.dv + gi) = f4(br * r4.x, br * r4.y, br * r4.z, br * r4.w);
-                vdp[i] = r4.x * ld<In>(a.v, gi) + r4.y * ld<In>(a.v, gi + 1) +
-                         r4.z * ld<In>(a.v, gi + 2) + r4.w * ld<In>(a.v, gi + 3);
+                fx4 v4;  // v[gi .. gi + 3], one 8- or 16-byte load
+                if constexpr (sizeof(In) == 4) {
+                    v4 = *reinterpret_cast<const fx4*>(static_cast<const float*>(a.v) + gi);
+                } else {
+                    typedef uint32_t ux2 __attribute__((ext_vector_type(2)));
+                    const ux2 w = *reinterpret_cast<const ux2*>(static_cast<const bf16_t*>(a.v) + gi);
+                    v4 = f4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                            __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+                }
+                vdp[i] = r4.x * v4.x + r4.y * v4.y + r4.z * v4.z + r4.w * v4.w;
             }
         }
     }
@@ -821,6 +829,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
         for (int off = D / 8; off > 0; off >>= 1) x += __shfl_xor(x, off, D / 4);
         if (lane % (D / 4) == 0) atomicAdd(&sdb[(tid + NT * i) / (D / 4)], x);
     }
+
+    // the first H0 / G fragments of phase 1b, loaded ahead of phase 1a
+    const float* hrow = h0 + (16 * wave + lc) * D + 8 * lg;
+    const float* grow = gp + (16 * wave + lc) * D + 8 * lg;
+    fx4 hb0 = *reinterpret_cast<const fx4*>(hrow), hb1 = *reinterpret_cast<const fx4*>(hrow + 4);
+    fx4 gb0 = *reinterpret_cast<const fx4*>(grow), gb1 = *reinterpret_cast<const fx4*>(grow + 4);
 
     // ---- phase 1a: lower tiles of dR Delta^T and dO Delta^T
     fx4 plt[PPW], ast[PPW];
@@ -881,10 +895,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
     for (int t = 0; t < RT; ++t) x1q[t] = f4(0.f, 0.f, 0.f, 0.f), x1k[t] = x1q[t], x2k[t] = x1q[t];
     float gh = 0.f;
     {
-        const float* hrow = h0 + (16 * wave + lc) * D + 8 * lg;
-        const float* grow = gp + (16 * wave + lc) * D + 8 * lg;
-        fx4 hb0 = *reinterpret_cast<const fx4*>(hrow), hb1 = *reinterpret_cast<const fx4*>(hrow + 4);
-        fx4 gb0 = *reinterpret_cast<const fx4*>(grow), gb1 = *reinterpret_cast<const fx4*>(grow + 4);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const fx4 h0c = hb0, h1c = hb1, g0c = gb0, g1c = gb1;
