@@ -703,14 +703,30 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 
-// Sum over the 16 lanes of each lane group (the c index of a 16x16 tile).
+// Cross-lane sums in registers (DPP and lane-group swaps; a shuffle would be an
+// LDS permute).  group16_sum: over the 16 lanes of each lane group (the c index
+// of a 16x16 tile, one DPP row) by rotations within the row; every lane of the
+// group gets the sum.  xor16_add / xor32_add: x plus x of lane l ^ 16 / l ^ 32.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float group16_sum(float x) {
-    x += __shfl_xor(x, 8, 16);
-    x += __shfl_xor(x, 4, 16);
-    x += __shfl_xor(x, 2, 16);
-    x += __shfl_xor(x, 1, 16);
+    x += dpp_f<0x128>(x);  // row_ror:8
+    x += dpp_f<0x124>(x);  // row_ror:4
+    x += dpp_f<0x122>(x);  // row_ror:2
+    x += dpp_f<0x121>(x);  // row_ror:1
     return x;
 }
+__device__ __forceinline__ float xor16_add(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_add(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float wave_sum(float x) { return xor32_add(xor16_add(group16_sum(x))); }
 
 // bwd_grads: one workgroup of D/16 waves per (chunk, head).  Every product is
 // an fp32 matrix-core product of 16x16 tiles (exact fp32 operands).  Layout:
@@ -826,7 +842,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
     for (int i = 0; i < NF; ++i) {
         // 32 (d = 128) or 16 (d = 64) consecutive lanes share a row
         float x = vdp[i];
-        for (int off = D / 8; off > 0; off >>= 1) x += __shfl_xor(x, off, D / 4);
+        x = group16_sum(x);
+        if (D / 4 == 32) x = xor16_add(x);
         if (lane % (D / 4) == 0) atomicAdd(&sdb[(tid + NT * i) / (D / 4)], x);
     }
 
@@ -883,8 +900,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
                 plt[p][e] = dpm * L;
                 ast[p][e] = dam * sb[r] * L;
             }
-            cs += __shfl_xor(cs, 16);
-            cs += __shfl_xor(cs, 32);
+            cs = xor32_add(xor16_add(cs));
             if (lg == 0) atomicAdd(&sdg[s], -cs);
         }
     }
@@ -1008,8 +1024,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
         }
     }
     // <G, H0>
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) gh += __shfl_xor(gh, off);
+    gh = wave_sum(gh);
     if (lane == 0) red[wave] = gh;
     __syncthreads();
     if (wave == 0) {  // lane = chunk row r
@@ -1020,8 +1035,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
         const float k1 = sk1[r], k2 = sk2[r];
         float dgr = sdg[r] + sGam[r] * (sq1[r] - sb[r] * k2) - se[r] * k1;
         float ek = se[r] * k1;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) ek += __shfl_xor(ek, off);
+        ek = wave_sum(ek);
         if (r == BC - 1) dgr += sGam[BC - 1] * ghs + ek;
         // dg = reverse inclusive cumsum of dgam within the chunk
 #pragma unroll
