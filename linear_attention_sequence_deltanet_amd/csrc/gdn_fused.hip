@@ -161,13 +161,12 @@ struct FusedSeg {
     float* sst;    // [S][BH][D][D]   start state per segment (combine writes, OUT reads)
 };
 
-// Row-contiguous [rows][64] token tiles written by transposition (K^T, V^T):
-// 8-token groups are XOR-permuted by row so the transposing stores of 16
-// different rows do not fall into one LDS bank; reads of aligned 4- or 8-token
-// groups stay contiguous.
+// Row-contiguous [rows][64] token tiles ((diag(e) K)^T): the padded row stride
+// (LA halves = 36 dwords) already spreads the 16 rows of a 4-token store or an
+// 8-token read over distinct banks of the 64-bank LDS.
 template <int LA>
 __device__ __forceinline__ int tsw(int row, int t) {
-    return row * LA + (t ^ (((row >> 3) & 7) << 3));
+    return row * LA + t;
 }
 
 template <int D, bool OUT>
@@ -188,7 +187,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     __shared__ __align__(16) uint16_t sQb[OUT ? FC * LD : 8];   // raw bf16 (Q K^T)
     __shared__ __align__(16) _Float16 sW[FC * LD];      // -W [t][key]
     __shared__ __align__(16) uint16_t sV[FC * LD];             // raw bf16
-    __shared__ __align__(16) _Float16 sKT[D * LA];      // (diag(e) K)^T [key][t] (swizzled)
+    __shared__ __align__(16) _Float16 sKT[D * LA];      // (diag(e) K)^T [key][t]
     __shared__ __align__(16) _Float16 sA[FC * LA];      // -A off-diagonal, (T_bb - I) diagonal blocks
     __shared__ __align__(16) _Float16 sP[OUT ? FC * LA : 8];
     __shared__ __align__(16) _Float16 sStg[OUT ? 8 : NW * 2 * D * 16];  // SUM: summary transpose
