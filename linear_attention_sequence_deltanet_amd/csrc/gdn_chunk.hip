@@ -653,7 +653,8 @@ __global__ __launch_bounds__(256) void chunk_chain(const void* ws, SegWs sw,
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const float* state_in,
-                                                           float* state_out, int BH, int S) {
+                                                           float* state_out, int BH, int S,
+                                                           int direct) {
     using M = Mfma<_Float16>;
     using F8 = M::frag8;
     constexpr int NS = D / 16, LS = D + 8;
@@ -682,14 +683,25 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
     for (int e = 0; e < 4; ++e)
         hs[e] = state_in ? state_in[((long)bh * D + 16 * wave + 4 * lg + e) * D + col] : 0.f;
 
+    // Segments applied: [s0, s1).  In direct mode segment 0's R is segment 1's
+    // start state and the last segment has no summary.
+    const int s0 = direct ? 1 : 0, s1 = direct ? S - 1 : S;
+    auto store_start = [&](int s) {
+        float* dst = sw.sst + ((long)s * BH + bh) * D * D;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(16 * wave + 4 * lg + e) * D + col] = hs[e];
+    };
+
     // Summaries do not depend on the chained state: those of the next NB
     // segments are loaded while the current one is applied.  Loads past the
-    // last segment re-read it, so every load is unconditional.
+    // last applied segment re-read it, so every load is unconditional.
     struct Pre {
         F8 hi[D / 32], lo[D / 32];  // rows of M (A operand)
         f32x4 r;                    // R (C layout)
     };
-    auto sum_of = [&](int s) { return sw.summ + ((long)min(s, S - 1) * BH + bh) * D * 2 * D; };
+    auto sum_of = [&](int s) {
+        return sw.summ + ((long)max(min(s, s1 - 1), 0) * BH + bh) * D * 2 * D;
+    };
     auto load_r = [&](Pre& p, const float* sm) {
         p.r = *reinterpret_cast<const f32x4*>(sm + ((slice * (D / 16) + wave) * 64 + lane) * 4);
     };
@@ -709,9 +721,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
     // fragment right after its product: issued together, the waves' loads
     // would queue at the CU's load unit and stall the waves at issue
     auto apply = [&](Pre& p, int s, int next) {
-        float* dst = sw.sst + ((long)s * BH + bh) * D * D;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(16 * wave + 4 * lg + e) * D + col] = hs[e];
+        store_start(s);
         // B operand: the state split into high and low fp16 parts.  The buffers
         // alternate, so one barrier per segment suffices: a buffer is rewritten
         // two segments later, after every wave passed the next barrier.
@@ -747,22 +757,31 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
         hs = a0 + (a1 + a2);
     };
 
+    if (direct) {
+        store_start(0);
+        hs = *reinterpret_cast<const f32x4*>(sw.summ + (long)bh * D * 2 * D +
+                                             ((slice * (D / 16) + wave) * 64 + lane) * 4);
+    }
     Pre pb[NB];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) load(pb[i], i);
+    for (int i = 0; i < NB; ++i) load(pb[i], s0 + i);
     // whole groups of NB segments branch-free (so the compiler's load counting
     // stays exact), then the remainder
-    int s = 0;
-    for (; s + NB <= S; s += NB) {
+    int s = s0;
+    for (; s + NB <= s1; s += NB) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) apply(pb[i], s + i, s + i + NB);
     }
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i)
-        if (s + i < S) apply(pb[i], s + i, S - 1);
+        if (s + i < s1) apply(pb[i], s + i, s1 - 1);
+    if (direct) {
+        if (S > 1) store_start(S - 1);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        state_out[((long)bh * D + 16 * wave + 4 * lg + e) * D + col] = hs[e];
+        for (int e = 0; e < 4; ++e)
+            state_out[((long)bh * D + 16 * wave + 4 * lg + e) * D + col] = hs[e];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -840,7 +859,7 @@ static hipError_t launch_chunked_t(const void* q, const void* k, const void* v, 
     profile_mark(stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_seg_combine(sw.summ, sw.sst, state_in, state_out, (int)BH, p.S, D, stream);
+    e = launch_seg_combine(sw.summ, sw.sst, state_in, state_out, (int)BH, p.S, D, 0, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_chain<In, D, DVT, CHAIN_OUT>),
                        dim3((unsigned)(BH * p.S * (D / DVT))), dim3(256), 0, stream,
@@ -851,14 +870,14 @@ static hipError_t launch_chunked_t(const void* q, const void* k, const void* v, 
 }
 
 hipError_t launch_seg_combine(float* summ, float* sst, const float* state_in, float* state_out,
-                              int BH, int S, int D, hipStream_t stream) {
+                              int BH, int S, int D, int direct, hipStream_t stream) {
     const SegWs sw{summ, sst};
     if (D == 64)
         hipLaunchKernelGGL((seg_combine<64>), dim3((unsigned)(BH * 4)), dim3(64 * 4), 0, stream,
-                           sw, state_in, state_out, BH, S);
+                           sw, state_in, state_out, BH, S, direct);
     else
         hipLaunchKernelGGL((seg_combine<128>), dim3((unsigned)(BH * 8)), dim3(64 * 8), 0, stream,
-                           sw, state_in, state_out, BH, S);
+                           sw, state_in, state_out, BH, S, direct);
     profile_mark(stream);
     return hipGetLastError();
 }

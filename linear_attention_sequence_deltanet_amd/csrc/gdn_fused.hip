@@ -209,12 +209,18 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     const long HD = (long)H * D;
     const int colw = 16 * wave;  // this wave's value columns (and identity columns in SUM)
 
+    // The last segment needs no summary (its output pass writes the final
+    // state), and the first segment's summary pass starts from the true initial
+    // state, so that its R is already the second segment's start state.
+    if (!OUT && seg == S - 1) return;
+
     // ---- state tiles (fp32, C layout): key 16 m + 4 lg + e, column colw + 16 j + lc
     f32x4 hs[TPW][MT];
     {
         const float* src = nullptr;
         if (OUT) src = S == 1 ? (state_in ? state_in + (long)bh * D * D : nullptr)
                               : fs.sst + ((long)seg * BH + bh) * D * D;
+        else if (seg == 0 && state_in) src = state_in + (long)bh * D * D;
 #pragma unroll
         for (int j = 0; j < TPW; ++j)
 #pragma unroll
@@ -223,10 +229,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 for (int e = 0; e < 4; ++e) {
                     const int key = 16 * m + 4 * lg + e, col = colw + lc;
                     float x = 0.f;
-                    if (OUT) {
+                    if (j == 0) {
                         if (src) x = src[key * D + col];
-                    } else if (j == 1) {
-                        x = key == col ? 1.f : 0.f;
+                    } else {
+                        x = key == col ? 1.f : 0.f;  // identity columns (summary pass)
                     }
                     hs[j][m][e] = x;
                 }
@@ -590,7 +596,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
 
     // ---- segment result
     if (OUT) {
-        if (S == 1) {
+        if (seg == S - 1) {
             float* dst = state_out + (long)bh * D * D;
 #pragma unroll
             for (int m = 0; m < MT; ++m)
@@ -706,7 +712,7 @@ static hipError_t launch_fused_t(const void* q, const void* k, const void* v, co
     profile_mark(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_seg_combine(fs.summ, fs.sst, state_in, state_out, (int)BH, p.S, D, stream);
+    e = launch_seg_combine(fs.summ, fs.sst, state_in, state_out, (int)BH, p.S, D, 1, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gdn_fused<D, true>), dim3((unsigned)(BH * p.S)), block, 0, stream, qq, kk,
                        vv, g, beta, fs, state_in, state_out, o, T, H, B, p.NC, p.G, p.S);
