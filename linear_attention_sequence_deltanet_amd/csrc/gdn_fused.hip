@@ -652,8 +652,8 @@ struct FPlan {
 // Segmentation by a cost model of the three kernels on the 256 CUs of an
 // MI355X, measured at d = 128: a chunk takes about 6.5 us in the output pass and
 // 5.7 us in the summary pass (one workgroup per CU; more workgroups than CUs run
-// in further rounds), a combine step about 1.2 us per round of its D/16
-// workgroups per head, and the two extra launches about 5 us together.  One
+// in further rounds), each of the S - 2 combine steps about 1.2 us per round of
+// its D/16 workgroups per head, and the two extra launches about 5 us together.  One
 // segment runs the output pass alone.  Candidates: G = 1..32 chunks per segment
 // and the G that fill k rounds of workgroups exactly.
 FPlan fused_plan(int B, int T, int H) {
@@ -669,7 +669,7 @@ FPlan fused_plan(int B, int T, int H) {
     auto consider = [&](long G) {
         if (G < 1 || G >= p.NC) return;
         const long S = (p.NC + G - 1) / G;
-        const double t = G * (kOut + kSum) * rounds(S * BH) + S * kComb * rounds(BH * 8) + kLaunch;
+        const double t = G * (kOut + kSum) * rounds(S * BH) + (S - 2) * kComb * rounds(BH * 8) + kLaunch;
         if (t < best) best = t, p.G = (int)G, p.S = (int)S;
     };
     for (long G = 1; G <= 32; ++G) consider(G);

@@ -94,6 +94,27 @@ def test_segmented_chain(env, T, dtype, dim):
            rs, TOL[dtype])
 
 
+def test_two_segments_sampled(env):
+    """B=2, T=3000, H=64, d=128, bf16: 128 series of 47 chunks split into two
+    segments (the first one's summary starts from the random initial state, no
+    combine step between them), ragged last chunk, state updated in place; the
+    oracle runs four sampled series, every token."""
+    gdn, dev = env
+    import torch
+    _note("case two segments B=2 T=3000 H=64 (sampled heads)")
+    d = gdn_inputs.random_inputs(2, 3000, 64, 128, 128, dtype="bf16", seed=3064, state_std=0.2)
+    x = stage(d, dev)
+    st = x["state0"].clone()
+    o, _ = gdn.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], st, state_out=st)
+    torch.cuda.synchronize()
+    o, st = o.cpu().numpy(), st.cpu().numpy()
+    heads = [(0, 0), (0, 31), (1, 17), (1, 63)]
+    ro, rs = oracle_heads(d, heads)
+    for n, (b, h) in enumerate(heads):
+        _check("two segments b%d h%d" % (b, h), o[b, :, h], st[b, h], ro[n], rs[n], TOL["bf16"])
+    assert np.isfinite(o).all() and np.isfinite(st).all()
+
+
 def test_prefill8k_full(env):
     """B=1, H=16, T=8192, d=128, bf16: every output and state element."""
     _note("case prefill8k full")
