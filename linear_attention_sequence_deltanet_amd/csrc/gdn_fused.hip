@@ -94,20 +94,22 @@ __device__ __forceinline__ unsigned pack_f16x2(float a, float b) {
     return __builtin_bit_cast(unsigned, p);
 }
 
+// Stored column order of the chain's A operands (-W, Q, P, (diag(e) K)^T):
+// within each block of 32 contraction columns, column 16 h + 4 g + e sits at
+// 8 g + 4 h + e.  A k32 A fragment (stored columns 8 g .. 8 g + 7 of lane group
+// g) then covers the contraction indices 4 g + e and 16 + 4 g + e, which are
+// exactly the rows that lane group g holds of two accumulator-layout tiles, so
+// the B operands (state, Delta) are packed from the accumulators in place.
+__device__ __forceinline__ int kperm(int col) {
+    return (col & ~31) | (((col >> 2) & 3) << 3) | (((col >> 4) & 1) << 2) | (col & 3);
+}
+
 // k32 B operand (fp16) from two accumulator-layout tiles t0, t1 that hold the
-// 32 contraction rows 0-15 and 16-31: lane group g has rows 4g..4g+3 of each
-// tile and needs rows 8g..8g+7 of the pair.  Two lane-group exchanges
-// (halves of the wave, then odd/even 16-lane rows) move the packed pairs there
-// without going through LDS.
+// contraction rows 0-15 and 16-31 of a block, in the stored order of kperm.
 __device__ __forceinline__ H8 acc_to_b32(f32x4 t0, f32x4 t1) {
-    const unsigned a0 = pack_f16x2(t0[0], t0[1]), a1 = pack_f16x2(t0[2], t0[3]);
-    const unsigned b0 = pack_f16x2(t1[0], t1[1]), b1 = pack_f16x2(t1[2], t1[3]);
-    const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-    const auto u0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
-    const auto u1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
     typedef unsigned u4 __attribute__((ext_vector_type(4)));
-    const u4 w = {u0[0], u1[0], u0[1], u1[1]};
+    const u4 w = {pack_f16x2(t0[0], t0[1]), pack_f16x2(t0[2], t0[3]), pack_f16x2(t1[0], t1[1]),
+                  pack_f16x2(t1[2], t1[3])};
     return __builtin_bit_cast(H8, w);
 }
 
@@ -161,9 +163,17 @@ struct FusedSeg {
     float* sst;    // [S][BH][D][D]   start state per segment (combine writes, OUT reads)
 };
 
-// Row-contiguous [rows][64] token tiles ((diag(e) K)^T): the padded row stride
-// (LA halves = 36 dwords) already spreads the 16 rows of a 4-token store or an
-// 8-token read over distinct banks of the 64-bank LDS.
+// Per-chunk gate factors in LDS (gam = within-chunk cumsum of g):
+// gam, beta, Gam = exp(gam), E = exp(gam_C - gam), BG = beta Gam; the
+// factored decays of the off-diagonal Gram tiles RF[r] = exp(gam_r -
+// gam_{16 floor(r/16)}) and CF[m][i] = exp(gam_{16 m} - gam_i) for i < 16 m
+// (both <= 1); GC = exp(gam_C).
+struct ChunkGates {
+    float gam[FC], beta[FC], Gam[FC], E[FC], BG[FC], RF[FC], CF[4][FC];
+    float GC, pad[3];
+};
+
+// Row-contiguous [rows][64] token tiles ((diag(e) K)^T).
 template <int LA>
 __device__ __forceinline__ int tsw(int row, int t) {
     return row * LA + t;
@@ -178,24 +188,31 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     constexpr int NW = D / 16, NTH = 64 * NW;  // wave w owns column tile w
     constexpr int TPW = OUT ? 1 : 2;      // state tiles per wave: value tile w (+ identity tile w)
     constexpr int MT = D / 16;            // key tiles of the state
-    constexpr int LD = D + 8;             // row stride of [64][D] tiles
-    constexpr int LA = FC + 8;            // row stride of [*][64] tiles
+    // Row strides (halves) of the LDS tiles, chosen per tile by its main
+    // access (measured on gfx950): 16-byte matrix-core fragment reads (lane
+    // group g: 16 rows, chunk g) run free of bank conflicts at 256 bytes per
+    // clock when a row is 2 mod 4 chunks of 16 bytes long, and at half that
+    // rate for an odd chunk count; 8-byte accesses of the same shape take 8
+    // clocks per instruction with an odd chunk count and 16 with 2 mod 4.
+    constexpr int LDF = D + 16;           // K, Q, -W: [64][D], fragment reads
+    constexpr int LDV = D + 8;            // V: [64][D], 8-byte reads only
+    constexpr int LAF = FC + 16;          // (diag(e) K)^T: [D][64], fragment reads
+    constexpr int LAA = FC + 8;           // A, P: [64][64], mostly 8-byte accesses
     constexpr int NL = FC * D / 8 / NTH;  // 8-element input groups per thread per tensor
 
-    __shared__ __align__(16) uint16_t sK[FC * LD];             // raw bf16
-    __shared__ __align__(16) _Float16 sQ[OUT ? FC * LD : 8];    // fp16 (Q H0)
-    __shared__ __align__(16) uint16_t sQb[OUT ? FC * LD : 8];   // raw bf16 (Q K^T)
-    __shared__ __align__(16) _Float16 sW[FC * LD];      // -W [t][key]
-    __shared__ __align__(16) uint16_t sV[FC * LD];             // raw bf16
-    __shared__ __align__(16) _Float16 sKT[D * LA];      // (diag(e) K)^T [key][t]
-    __shared__ __align__(16) _Float16 sA[FC * LA];      // -A off-diagonal, (T_bb - I) diagonal blocks
-    __shared__ __align__(16) _Float16 sP[OUT ? FC * LA : 8];
+    __shared__ __align__(16) uint16_t sK[FC * LDF];             // raw bf16
+    __shared__ __align__(16) _Float16 sQ[OUT ? FC * LDF : 8];    // fp16 (Q H0)
+    __shared__ __align__(16) uint16_t sQb[OUT ? FC * LDF : 8];   // raw bf16 (Q K^T)
+    __shared__ __align__(16) _Float16 sW[FC * LDF];      // -W [t][key]
+    __shared__ __align__(16) uint16_t sV[FC * LDV];             // raw bf16
+    __shared__ __align__(16) _Float16 sKT[D * LAF];      // (diag(e) K)^T [key][t]
+    __shared__ __align__(16) _Float16 sA[FC * LAA];      // -A off-diagonal, (T_bb - I) diagonal blocks
+    __shared__ __align__(16) _Float16 sP[OUT ? FC * LAA : 8];
     __shared__ __align__(16) _Float16 sStg[OUT ? 8 : NW * 2 * D * 16];  // SUM: summary transpose
-    __shared__ __align__(16) float sgam[FC], sbeta[FC], sGam[FC], sE[FC], sBG[FC];
-    // decay factors of the off-diagonal Gram tiles: sRF[r] = exp(gam_r - gam_{16 floor(r/16)}),
-    // sCF[m][i] = exp(gam_{16 m} - gam_i) for i < 16 m (both <= 1)
-    __shared__ __align__(16) float sRF[FC], sCF[4][FC];
-    __shared__ float sGC;
+    // gates of chunk c in sG[c & 1]: wave 0 forms the next chunk's at the end
+    // of its part of the state update, while the other waves still read the
+    // current chunk's
+    __shared__ __align__(16) ChunkGates sG[2];
 
     // SUM chains the value columns (tile w, giving R) and the identity columns
     // (tile w of M) of the augmented state together; OUT only the value tile.
@@ -278,6 +295,28 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         issue_gates(c);
     };
     issue_loads(c_begin);
+    // wave 0: the chunk's gate factors from its g and beta (in rg, rb)
+    auto form_gates = [&](ChunkGates& gt) {
+        const float bv = rb;
+        const float gv = wave_prefix_sum(rg);
+        const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 63));
+        const float eg = __expf(gv);
+        gt.gam[lane] = gv;
+        gt.beta[lane] = bv;
+        gt.Gam[lane] = eg;
+        gt.BG[lane] = bv * eg;
+        gt.E[lane] = __expf(gC - gv);
+        if (lane == 0) gt.GC = __expf(gC);
+        const float g16 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 16));
+        const float g32 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 32));
+        const float g48 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 48));
+        const float g00 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 0));
+        gt.RF[lane] = __expf(gv - (lane < 16 ? g00 : lane < 32 ? g16 : lane < 48 ? g32 : g48));
+        gt.CF[1][lane] = lane < 16 ? __expf(g16 - gv) : 0.f;
+        gt.CF[2][lane] = lane < 32 ? __expf(g32 - gv) : 0.f;
+        gt.CF[3][lane] = lane < 48 ? __expf(g48 - gv) : 0.f;
+    };
+    if (wave == 0) form_gates(sG[c_begin & 1]);
 
     for (int c = c_begin; c < c_end; ++c) {
         const long t0 = (long)c * FC;
@@ -290,37 +329,20 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         asm volatile("" : "+v"(lane_i));
         const int lg = lane_i >> 4, lc = lane_i & 15;
         const int tid = wave * 64 + lane_i;
+        ChunkGates& gt = sG[c & 1];
 
-        // ---- inputs into LDS (f16, row-major K, Q, V); gates
+        // ---- inputs into LDS (row-major K, V raw; Q raw and fp16)
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int idx = tid + NTH * i, r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-            *reinterpret_cast<uint4*>(&sK[r * LD + c8]) = rk[i];
+            *reinterpret_cast<uint4*>(&sK[r * LDF + c8]) = rk[i];
             if (OUT) {
-                *reinterpret_cast<H8*>(&sQ[r * LD + c8]) = bf16x8_to_f16(rq[i]);
-                *reinterpret_cast<uint4*>(&sQb[r * LD + c8]) = rq[i];
+                const H8 qh = bf16x8_to_f16(rq[i]);
+                st4<_Float16>(&sQ[r * LDF + kperm(c8)], __builtin_shufflevector(qh, qh, 0, 1, 2, 3));
+                st4<_Float16>(&sQ[r * LDF + kperm(c8 + 4)], __builtin_shufflevector(qh, qh, 4, 5, 6, 7));
+                *reinterpret_cast<uint4*>(&sQb[r * LDF + c8]) = rq[i];
             }
-            *reinterpret_cast<uint4*>(&sV[r * LD + c8]) = rv[i];
-        }
-        if (wave == 0) {
-            const float bv = rb;
-            const float gv = wave_prefix_sum(rg);
-            const float gC = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 63));
-            const float eg = __expf(gv);
-            sgam[lane] = gv;
-            sbeta[lane] = bv;
-            sGam[lane] = eg;
-            sBG[lane] = bv * eg;
-            sE[lane] = __expf(gC - gv);
-            if (lane == 0) sGC = __expf(gC);
-            const float g16 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 16));
-            const float g32 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 32));
-            const float g48 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 48));
-            const float g00 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), 0));
-            sRF[lane] = __expf(gv - (lane < 16 ? g00 : lane < 32 ? g16 : lane < 48 ? g32 : g48));
-            sCF[1][lane] = lane < 16 ? __expf(g16 - gv) : 0.f;
-            sCF[2][lane] = lane < 32 ? __expf(g32 - gv) : 0.f;
-            sCF[3][lane] = lane < 48 ? __expf(g48 - gv) : 0.f;
+            *reinterpret_cast<uint4*>(&sV[r * LDV + c8]) = rv[i];
         }
         const bool more = c + 1 < c_end;
         if (more) {
@@ -337,12 +359,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             f32x4 acc = zero4();  // G = K_b K_b^T, symmetric
 #pragma unroll
             for (int kk = 0; kk < D / 32; ++kk) {
-                const B8 a = ldb8(&sK[(16 * bb + lc) * LD + 32 * kk + 8 * lg]);
+                const B8 a = ldb8(&sK[(16 * bb + lc) * LDF + 32 * kk + 8 * lg]);
                 acc = mfma_b32(a, a, acc);
             }
-            const f32x4 gr = *reinterpret_cast<const f32x4*>(&sgam[16 * bb + 4 * lg]);
-            const f32x4 br = *reinterpret_cast<const f32x4*>(&sbeta[16 * bb + 4 * lg]);
-            const float gi = sgam[16 * bb + lc], bi = sbeta[16 * bb + lc];
+            const f32x4 gr = *reinterpret_cast<const f32x4*>(&gt.gam[16 * bb + 4 * lg]);
+            const f32x4 br = *reinterpret_cast<const f32x4*>(&gt.beta[16 * bb + 4 * lg]);
+            const float gi = gt.gam[16 * bb + lc], bi = gt.beta[16 * bb + lc];
             // A_bb and its transpose in accumulator layout (row 4 lg + e, column
             // lc); by the symmetry of G both come from the same accumulator.
             f32x4 ax, at, id;
@@ -368,7 +390,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             const f32x4 n3t = mm_split(s4, split(n2t), n2t);  // (... (I + A^4))^T
             const f32x4 nt = mm_split(split(a8), split(n3t), n3t);  // ((I + A)^{-1})^T
             // N - I: row lc of the block, columns 4 lg .. 4 lg + 3
-            st4<_Float16>(&sA[(16 * bb + lc) * LA + 16 * bb + 4 * lg], cvt4<_Float16>(nt - id));
+            st4<_Float16>(&sA[(16 * bb + lc) * LAA + 16 * bb + 4 * lg], cvt4<_Float16>(nt - id));
         }
         {
             // A tile (mi, ni) is computed transposed, C = K_ni X_mi^T (X = K or Q),
@@ -383,27 +405,28 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int kk = 0; kk < D / 32; ++kk)
-                    acc = mfma_b32(ldb8(&sK[(16 * ni + lc) * LD + 32 * kk + 8 * lg]),
-                                   ldb8(&X[(16 * mi + lc) * LD + 32 * kk + 8 * lg]), acc);
+                    acc = mfma_b32(ldb8(&sK[(16 * ni + lc) * LDF + 32 * kk + 8 * lg]),
+                                   ldb8(&X[(16 * mi + lc) * LDF + 32 * kk + 8 * lg]), acc);
                 return acc;
             };
-            // off-diagonal: exp(gam_r - gam_i) = sRF[r] sCF[mi][i]; -A (K K^T) or P (Q K^T)
+            // off-diagonal: exp(gam_r - gam_i) = RF[r] CF[mi][i]; -A (K K^T) or P (Q K^T)
             auto store_off = [&](bool kq, int mi, int ni, f32x4 acc) {
                 const int r = 16 * mi + lc;
-                const f32x4 cf = *reinterpret_cast<const f32x4*>(&sCF[mi][16 * ni + 4 * lg]);
-                const float sc = kq ? -(sbeta[r] * sRF[r]) : sRF[r];
-                st4<_Float16>(&(kq ? sA : sP)[r * LA + 16 * ni + 4 * lg], cvt4<_Float16>((sc * cf) * acc));
+                const f32x4 cf = *reinterpret_cast<const f32x4*>(&gt.CF[mi][16 * ni + 4 * lg]);
+                const float sc = kq ? -(gt.beta[r] * gt.RF[r]) : gt.RF[r];
+                _Float16* dst = kq ? &sA[r * LAA + 16 * ni + 4 * lg] : &sP[r * LAA + kperm(16 * ni + 4 * lg)];
+                st4<_Float16>(dst, cvt4<_Float16>((sc * cf) * acc));
             };
             // diagonal Q K^T tile m: P[r][i] for i <= r
             auto store_qdiag = [&](int m, f32x4 acc) {
                 const int r = 16 * m + lc;
-                const float gr = sgam[r];
-                const f32x4 gi = *reinterpret_cast<const f32x4*>(&sgam[16 * m + 4 * lg]);
+                const float gr = gt.gam[r];
+                const f32x4 gi = *reinterpret_cast<const f32x4*>(&gt.gam[16 * m + 4 * lg]);
                 f32x4 val;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     val[e] = 4 * lg + e <= lc ? __expf(fminf(gr - gi[e], 0.f)) * acc[e] : 0.f;
-                st4<_Float16>(&sP[r * LA + 16 * m + 4 * lg], cvt4<_Float16>(val));
+                st4<_Float16>(&sP[r * LAA + kperm(16 * m + 4 * lg)], cvt4<_Float16>(val));
             };
             if (NW == 8) {
                 // waves 4..7: K K^T tile w-4, then (OUT) Q K^T tile w-4 and, for
@@ -454,7 +477,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 const int z = wave - (NW - 2);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    sP[(32 * z + 4 * lg + e) * LA + 32 * z + 16 + lc] = _Float16(0);
+                    sP[(32 * z + 4 * lg + e) * LAA + kperm(32 * z + 16 + lc)] = _Float16(0);
             }
         }
         lds_sync();
@@ -478,24 +501,32 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
 #pragma unroll
             for (int e = 0; e < 4; ++e) ident[e] = (short)(4 * lg + e == lc ? 0x3f80 : 0);
             H4 xh[NR][4];
+            H4 kte_prev;
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
-                const f32x4 fb = *reinterpret_cast<const f32x4*>(&sbeta[16 * bb + 4 * lg]);
-                const f32x4 fg = *reinterpret_cast<const f32x4*>(&sBG[16 * bb + 4 * lg]);
-                const f32x4 fe = *reinterpret_cast<const f32x4*>(&sE[16 * bb + 4 * lg]);
-                const f32x4 vt = mfma_b16(ldb4(&sV[(16 * bb + lc) * LD + colw + 4 * lg]), ident, zero4());
-                const f32x4 kt = mfma_b16(ldb4(&sK[(16 * bb + lc) * LD + colw + 4 * lg]), ident, zero4());
-                st4<_Float16>(&sKT[tsw<LA>(colw + lc, 16 * bb + 4 * lg)], cvt4<_Float16>(fe * kt));
+                const f32x4 fb = *reinterpret_cast<const f32x4*>(&gt.beta[16 * bb + 4 * lg]);
+                const f32x4 fg = *reinterpret_cast<const f32x4*>(&gt.BG[16 * bb + 4 * lg]);
+                const f32x4 fe = *reinterpret_cast<const f32x4*>(&gt.E[16 * bb + 4 * lg]);
+                const f32x4 vt = mfma_b16(ldb4(&sV[(16 * bb + lc) * LDV + colw + 4 * lg]), ident, zero4());
+                const f32x4 kt = mfma_b16(ldb4(&sK[(16 * bb + lc) * LDF + colw + 4 * lg]), ident, zero4());
+                // (diag(e) K)^T: token blocks 2 i and 2 i + 1 fill one 16-byte chunk
+                // of the kperm order; stored together after the odd block
+                const H4 kte = cvt4<_Float16>(fe * kt);
+                if (bb & 1)
+                    *reinterpret_cast<H8*>(&sKT[tsw<LAF>(colw + lc, 32 * (bb >> 1) + 8 * lg)]) =
+                        __builtin_shufflevector(kte_prev, kte, 0, 1, 2, 3, 4, 5, 6, 7);
+                else
+                    kte_prev = kte;
                 f32x4 acc[NR];
                 acc[0] = fb * vt;
                 acc[1] = -(fg * kt);
 #pragma unroll
                 for (int j = 0; j < bb; ++j) {
-                    const H4 aj = ld4<_Float16>(&sA[(16 * bb + lc) * LA + 16 * j + 4 * lg]);
+                    const H4 aj = ld4<_Float16>(&sA[(16 * bb + lc) * LAA + 16 * j + 4 * lg]);
 #pragma unroll
                     for (int t = 0; t < NR; ++t) acc[t] = MF::k16(aj, xh[t][j], acc[t]);
                 }
-                const H4 ab = ld4<_Float16>(&sA[(16 * bb + lc) * LA + 16 * bb + 4 * lg]);
+                const H4 ab = ld4<_Float16>(&sA[(16 * bb + lc) * LAA + 16 * bb + 4 * lg]);
 #pragma unroll
                 for (int t = 0; t < NR; ++t) {
                     acc[t] = MF::k16(ab, cvt4<_Float16>(acc[t]), acc[t]);
@@ -512,7 +543,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             for (int e = 0; e < 4; ++e) identh[e] = static_cast<_Float16>(4 * lg + e == lc ? 1.f : 0.f);
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb)
-                st4<_Float16>(&sW[(16 * bb + lc) * LD + colw + 4 * lg],
+                st4<_Float16>(&sW[(16 * bb + lc) * LDF + kperm(colw + 4 * lg)],
                               cvt4<_Float16>(MF::k16(xh[1][bb], identh, zero4())));
         }
         f32x4 u[TPW][4];
@@ -525,27 +556,61 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         if (OUT && more) issue(rq, q, c + 1);
 
         // ---- state update for this wave's columns (no workgroup barrier).
-        // The state and Delta enter the products as fp16 B operands built from
-        // their accumulator-layout tiles in registers.
+        // The state and Delta enter the products as fp16 B operands packed from
+        // their accumulator-layout tiles in registers.  Delta = U - W H0 and
+        // (OUT) Q H0 run with the contraction step outermost, so the four row
+        // tiles' accumulators form independent chains on the matrix cores; the
+        // A fragments of step kk + 1 are read while step kk multiplies.
+        constexpr int NQ = OUT ? 4 : 1;
+        H8 fw[2][4], fq[2][NQ];
+        auto load_step = [&](int kk) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                fw[kk & 1][mt] = ld8<_Float16>(&sW[(16 * mt + lc) * LDF + 32 * kk + 8 * lg]);
+                if (OUT) fq[kk & 1][mt] = ld8<_Float16>(&sQ[(16 * mt + lc) * LDF + 32 * kk + 8 * lg]);
+            }
+        };
+        load_step(0);
         H8 bs[D / 32][TPW];
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
             for (int j = 0; j < TPW; ++j) bs[kk][j] = acc_to_b32(hs[j][2 * kk], hs[j][2 * kk + 1]);
-        // Delta = U - W H0, one row tile at a time
-        f32x4 dl[TPW][4];
+        f32x4 dl[TPW][4], oq[NQ];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
             for (int j = 0; j < TPW; ++j) dl[j][mt] = u[j][mt];
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                const H8 aw = ld8<_Float16>(&sW[(16 * mt + lc) * LD + 32 * kk + 8 * lg]);
-#pragma unroll
-                for (int j = 0; j < TPW; ++j) dl[j][mt] = MF::k32(aw, bs[kk][j], dl[j][mt]);
-            }
-            if (mt == 1) __builtin_amdgcn_sched_barrier(0);
+            if (OUT) oq[mt] = zero4();
         }
+        H8 fp[OUT ? 6 : 1];  // P fragments: row tiles 0..3 (tokens 0-31), 2, 3 (tokens 32-63)
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            if (kk + 1 < D / 32) {
+                load_step(kk + 1);
+            } else if (OUT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) fp[i] = ld8<_Float16>(&sP[(16 * i + lc) * LAA + 8 * lg]);
+                fp[4] = ld8<_Float16>(&sP[(32 + lc) * LAA + 32 + 8 * lg]);
+                fp[5] = ld8<_Float16>(&sP[(48 + lc) * LAA + 32 + 8 * lg]);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // the reads above go out before this step's products
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+                for (int j = 0; j < TPW; ++j) dl[j][mt] = MF::k32(fw[kk & 1][mt], bs[kk][j], dl[j][mt]);
+                if (OUT) oq[mt] = MF::k32(fq[kk & 1][mt], bs[kk][0], oq[mt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // (diag(e) K)^T fragments of the first half of the key tiles
+        H8 fk[MT][2];
+        auto load_kt = [&](int m) {
+            fk[m][0] = ld8<_Float16>(&sKT[tsw<LAF>(16 * m + lc, 8 * lg)]);
+            fk[m][1] = ld8<_Float16>(&sKT[tsw<LAF>(16 * m + lc, 32 + 8 * lg)]);
+        };
+#pragma unroll
+        for (int m = 0; m < MT / 2; ++m) load_kt(m);
         H8 db[2][TPW];  // Delta as B operand, token blocks 0-31 and 32-63
 #pragma unroll
         for (int j = 0; j < TPW; ++j) {
@@ -553,45 +618,56 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             db[1][j] = acc_to_b32(dl[j][2], dl[j][3]);
         }
         if (OUT) {
-            // O = diag(Gam) Q H0 + P Delta, one row tile at a time; output rows
-            // through a descriptor that ends at the sequence's last row
+            // O = diag(Gam) Q H0 + P Delta (the first products of all row tiles,
+            // then the second ones); output rows through a descriptor that ends
+            // at the sequence's last row
             const float* ob = o + ((long)b * T + t0) * HD + (long)h * D + colw;  // scalar
             unsigned ooff[4];  // this lane's rows 4 lg + e, bytes
 #pragma unroll
             for (int e = 0; e < 4; ++e) ooff[e] = (unsigned)(((4 * lg + e) * (int)HD + lc) * 4);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                f32x4 oq = zero4();
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(&gt.Gam[16 * mt + 4 * lg]);
+                oq[mt] = MF::k32(fp[mt], db[0][0], gm * oq[mt]);
+            }
 #pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk)
-                    oq = MF::k32(ld8<_Float16>(&sQ[(16 * mt + lc) * LD + 32 * kk + 8 * lg]), bs[kk][0], oq);
-                const f32x4 gm = *reinterpret_cast<const f32x4*>(&sGam[16 * mt + 4 * lg]);
-                oq = MF::k32(ld8<_Float16>(&sP[(16 * mt + lc) * LA + 8 * lg]), db[0][0], gm * oq);
-                if (mt >= 2) oq = MF::k32(ld8<_Float16>(&sP[(16 * mt + lc) * LA + 32 + 8 * lg]), db[1][0], oq);
+            for (int mt = 2; mt < 4; ++mt) oq[mt] = MF::k32(fp[2 + mt], db[1][0], oq[mt]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const f32x4 ov = oq[mt];
                 const int rows = n - 16 * mt;  // valid rows of this row tile (scalar)
                 const rsrc_t ro = make_rsrc(ob + (long)16 * mt * HD,
                                             rows > 0 ? (unsigned)(((rows - 1) * (int)HD + 16) * 4) : 0u);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) buf_store4(ro, ooff[e], oq[e]);
-                if (mt == 1) __builtin_amdgcn_sched_barrier(0);
+                for (int e = 0; e < 4; ++e) buf_store4(ro, ooff[e], ov[e]);
             }
         }
-        // H = Gam_C H0 + (diag(e) K)^T Delta
+        // H = Gam_C H0 + (diag(e) K)^T Delta, half of the key tiles at a time
+        // (independent chains); the second half's fragments are read while the
+        // first half is applied
         {
-            const float GC = sGC;
+            const float GC = gt.GC;
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const H8 ak0 = ld8<_Float16>(&sKT[tsw<LA>(16 * m + lc, 8 * lg)]);
-                const H8 ak1 = ld8<_Float16>(&sKT[tsw<LA>(16 * m + lc, 32 + 8 * lg)]);
+            for (int half = 0; half < 2; ++half) {
+                if (half == 0) {
 #pragma unroll
-                for (int j = 0; j < TPW; ++j) {
-                    f32x4 acc = hs[j][m] * GC;
-                    acc = MF::k32(ak0, db[0][j], acc);
-                    hs[j][m] = MF::k32(ak1, db[1][j], acc);
+                    for (int m = MT / 2; m < MT; ++m) load_kt(m);
                 }
-                if (m % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4 acc[TPW][MT / 2];
+#pragma unroll
+                for (int i = 0; i < MT / 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < TPW; ++j)
+                        acc[j][i] = MF::k32(fk[half * MT / 2 + i][0], db[0][j], hs[j][half * MT / 2 + i] * GC);
+#pragma unroll
+                for (int i = 0; i < MT / 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < TPW; ++j)
+                        hs[j][half * MT / 2 + i] = MF::k32(fk[half * MT / 2 + i][1], db[1][j], acc[j][i]);
             }
         }
+        if (wave == 0 && more) form_gates(sG[(c + 1) & 1]);
     }
 
     // ---- segment result
