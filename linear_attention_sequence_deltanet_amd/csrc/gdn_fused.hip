@@ -179,6 +179,35 @@ __device__ __forceinline__ int tsw(int row, int t) {
     return row * LA + t;
 }
 
+// Products C_t = K_{ni_t} X_t^T of NT 16x16 tiles over the D columns of
+// bf16 row-major LDS tiles (row stride LDF): the contraction step is
+// outermost, so the tiles' accumulators are independent chains on the matrix
+// cores, and the fragments of step kk + 1 are read while step kk multiplies.
+template <int NT, int D, int LDF>
+__device__ __forceinline__ void gram_tiles(const uint16_t* sK, const uint16_t* const* X,
+                                           const int* mi, const int* ni, int lg, int lc,
+                                           f32x4* acc) {
+    B8 fa[2][NT], fb[2][NT];
+    auto load = [&](int kk) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            fa[kk & 1][t] = ldb8(&sK[(16 * ni[t] + lc) * LDF + 32 * kk + 8 * lg]);
+            fb[kk & 1][t] = ldb8(&X[t][(16 * mi[t] + lc) * LDF + 32 * kk + 8 * lg]);
+        }
+    };
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = zero4();
+    load(0);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        if (kk + 1 < D / 32) load(kk + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = mfma_b32(fa[kk & 1][t], fb[kk & 1][t], acc[t]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 template <int D, bool OUT>
 __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -351,20 +380,42 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         }
         lds_sync();
 
-        // ---- Gram tiles.  Waves 0-3: diagonal block w of K K^T and the
-        // inverse of (I + A_ww).  All waves: the six off-diagonal K K^T tiles
-        // and, for OUT, the ten lower Q K^T tiles.
+        // ---- Gram tiles.  Waves 0-3: diagonal block w of K K^T, the inverse
+        // of (I + A_ww) and (OUT) the diagonal Q K^T tile w.  The other waves:
+        // the six off-diagonal K K^T tiles and, for OUT, the six off-diagonal
+        // Q K^T tiles.  A tile (mi, ni) is computed transposed, C = K_ni X_mi^T
+        // (X = K or Q), so lane (lg, lc) holds row r = 16 mi + lc, columns
+        // i = 16 ni + 4 lg + e and stores four consecutive halves.  Off-diagonal
+        // tiles (mi > ni) are numbered 0..5: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
+        auto off_coords = [](int k, int& mi, int& ni) {
+            mi = k < 1 ? 1 : k < 3 ? 2 : 3;
+            ni = k - (mi * (mi - 1)) / 2;
+        };
+        // off-diagonal tile: exp(gam_r - gam_i) = RF[r] CF[mi][i]; -A (K K^T)
+        // or P (Q K^T).  The factors are read before the products.
+        auto off_factors = [&](bool kq, int mi, int ni, f32x4& cf, float& sc) {
+            const int r = 16 * mi + lc;
+            cf = *reinterpret_cast<const f32x4*>(&gt.CF[mi][16 * ni + 4 * lg]);
+            sc = kq ? -(gt.beta[r] * gt.RF[r]) : gt.RF[r];
+        };
+        auto store_off = [&](bool kq, int mi, int ni, f32x4 acc, f32x4 cf, float sc) {
+            const int r = 16 * mi + lc;
+            _Float16* dst = kq ? &sA[r * LAA + 16 * ni + 4 * lg] : &sP[r * LAA + kperm(16 * ni + 4 * lg)];
+            st4<_Float16>(dst, cvt4<_Float16>((sc * cf) * acc));
+        };
         if (wave < 4) {
             const int bb = wave;
-            f32x4 acc = zero4();  // G = K_b K_b^T, symmetric
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                const B8 a = ldb8(&sK[(16 * bb + lc) * LDF + 32 * kk + 8 * lg]);
-                acc = mfma_b32(a, a, acc);
-            }
             const f32x4 gr = *reinterpret_cast<const f32x4*>(&gt.gam[16 * bb + 4 * lg]);
             const f32x4 br = *reinterpret_cast<const f32x4*>(&gt.beta[16 * bb + 4 * lg]);
             const float gi = gt.gam[16 * bb + lc], bi = gt.beta[16 * bb + lc];
+            // G = K_b K_b^T (symmetric) and, for OUT, K_b Q_b^T
+            f32x4 cc[OUT ? 2 : 1];
+            {
+                const uint16_t* X[2] = {sK, sQb};
+                const int mi[2] = {bb, bb}, ni[2] = {bb, bb};
+                gram_tiles<OUT ? 2 : 1, D, LDF>(sK, X, mi, ni, lg, lc, cc);
+            }
+            const f32x4 acc = cc[0];
             // A_bb and its transpose in accumulator layout (row 4 lg + e, column
             // lc); by the symmetry of G both come from the same accumulator.
             f32x4 ax, at, id;
@@ -381,6 +432,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             // (each factor is split into fp16 parts once)
             const Split sx = split(ax), st = split(at);
             const f32x4 a2 = mm_split(st, sx, zero4()), a2t = mm_split(sx, st, zero4());
+            if (OUT) {
+                // diagonal Q K^T tile: P[r][i] = exp(gam_r - gam_i) q_r.k_i for i <= r
+                // (independent of the inverse; fills its latencies)
+                f32x4 val;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    val[e] = 4 * lg + e <= lc ? __expf(fminf(gi - gr[e], 0.f)) * cc[OUT ? 1 : 0][e] : 0.f;
+                st4<_Float16>(&sP[(16 * bb + lc) * LAA + kperm(16 * bb + 4 * lg)], cvt4<_Float16>(val));
+            }
             const Split s2 = split(a2), s2t = split(a2t);
             const f32x4 a4 = mm_split(s2t, s2, zero4()), a4t = mm_split(s2, s2t, zero4());
             const Split s4 = split(a4);
@@ -392,93 +452,61 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             // N - I: row lc of the block, columns 4 lg .. 4 lg + 3
             st4<_Float16>(&sA[(16 * bb + lc) * LAA + 16 * bb + 4 * lg], cvt4<_Float16>(nt - id));
         }
-        {
-            // A tile (mi, ni) is computed transposed, C = K_ni X_mi^T (X = K or Q),
-            // so lane (lg, lc) holds row r = 16 mi + lc, columns i = 16 ni + 4 lg + e
-            // and stores four consecutive halves.  Off-diagonal tiles (mi > ni) are
-            // numbered 0..5: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
-            auto off_coords = [](int k, int& mi, int& ni) {
-                mi = k < 1 ? 1 : k < 3 ? 2 : 3;
-                ni = k - (mi * (mi - 1)) / 2;
-            };
-            auto tile_acc = [&](const uint16_t* X, int mi, int ni) {
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk)
-                    acc = mfma_b32(ldb8(&sK[(16 * ni + lc) * LDF + 32 * kk + 8 * lg]),
-                                   ldb8(&X[(16 * mi + lc) * LDF + 32 * kk + 8 * lg]), acc);
-                return acc;
-            };
-            // off-diagonal: exp(gam_r - gam_i) = RF[r] CF[mi][i]; -A (K K^T) or P (Q K^T)
-            auto store_off = [&](bool kq, int mi, int ni, f32x4 acc) {
-                const int r = 16 * mi + lc;
-                const f32x4 cf = *reinterpret_cast<const f32x4*>(&gt.CF[mi][16 * ni + 4 * lg]);
-                const float sc = kq ? -(gt.beta[r] * gt.RF[r]) : gt.RF[r];
-                _Float16* dst = kq ? &sA[r * LAA + 16 * ni + 4 * lg] : &sP[r * LAA + kperm(16 * ni + 4 * lg)];
-                st4<_Float16>(dst, cvt4<_Float16>((sc * cf) * acc));
-            };
-            // diagonal Q K^T tile m: P[r][i] for i <= r
-            auto store_qdiag = [&](int m, f32x4 acc) {
-                const int r = 16 * m + lc;
-                const float gr = gt.gam[r];
-                const f32x4 gi = *reinterpret_cast<const f32x4*>(&gt.gam[16 * m + 4 * lg]);
-                f32x4 val;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    val[e] = 4 * lg + e <= lc ? __expf(fminf(gr - gi[e], 0.f)) * acc[e] : 0.f;
-                st4<_Float16>(&sP[r * LAA + kperm(16 * m + 4 * lg)], cvt4<_Float16>(val));
-            };
-            if (NW == 8) {
-                // waves 4..7: K K^T tile w-4, then (OUT) Q K^T tile w-4 and, for
-                // waves 4, 5, K K^T tile w / for waves 6, 7, Q K^T tile w-2;
-                // SUM: K K^T tiles w-4 and (waves 4, 5) w.  Waves 0..3 (OUT): the
-                // diagonal Q K^T tile of their block.
-                if (wave >= 4) {
-                    int m0, n0, m1, n1, m2, n2;
-                    off_coords(wave - 4, m0, n0);
-                    const f32x4 c0 = tile_acc(sK, m0, n0);
-                    if (OUT) {
-                        off_coords(wave - 4, m1, n1);
-                        const f32x4 c1 = tile_acc(sQb, m1, n1);
-                        const bool third_kk = wave < 6;
-                        off_coords(third_kk ? wave : wave - 2, m2, n2);
-                        const f32x4 c2 = tile_acc(third_kk ? sK : sQb, m2, n2);
-                        store_off(true, m0, n0, c0);
-                        store_off(false, m1, n1, c1);
-                        if (third_kk) store_off(true, m2, n2, c2);
-                        else store_off(false, m2, n2, c2);
-                    } else {
-                        store_off(true, m0, n0, c0);
-                        if (wave < 6) {
-                            off_coords(wave, m1, n1);
-                            store_off(true, m1, n1, tile_acc(sK, m1, n1));
-                        }
-                    }
-                } else if (OUT) {
-                    store_qdiag(wave, tile_acc(sQb, wave, wave));
+        if (NW == 8) {
+            // waves 4..7: K K^T tile w-4, then (OUT) Q K^T tile w-4 and, for
+            // waves 4, 5, K K^T tile w / for waves 6, 7, Q K^T tile w-2;
+            // SUM: K K^T tiles w-4 and (waves 4, 5) w
+            if (wave >= 4) {
+                int mi[3], ni[3];
+                const uint16_t* X[3];
+                bool kq[3];
+                off_coords(wave - 4, mi[0], ni[0]);
+                X[0] = sK, kq[0] = true;
+                const bool third_kk = wave < 6;
+                if (OUT) {
+                    off_coords(wave - 4, mi[1], ni[1]);
+                    X[1] = sQb, kq[1] = false;
+                    off_coords(third_kk ? wave : wave - 2, mi[2], ni[2]);
+                    X[2] = third_kk ? sK : sQb, kq[2] = third_kk;
+                } else {
+                    off_coords(third_kk ? wave : 0, mi[1], ni[1]);
+                    X[1] = sK, kq[1] = true;
+                    mi[2] = mi[1], ni[2] = ni[1], X[2] = sK, kq[2] = true;
                 }
-            } else {
-                // generic: the off-diagonal K K^T tiles, then (OUT) the off-diagonal
-                // and the diagonal Q K^T tiles, dealt to the waves in turn
-                constexpr int NREAL = OUT ? 16 : 6;
-                for (int tt = wave; tt < NREAL; tt += NW) {
-                    if (tt < 12) {
-                        int mi, ni;
-                        off_coords(tt % 6, mi, ni);
-                        const bool kq = tt < 6;
-                        store_off(kq, mi, ni, tile_acc(kq ? sK : sQb, mi, ni));
-                    } else {
-                        store_qdiag(tt - 12, tile_acc(sQb, tt - 12, tt - 12));
-                    }
-                }
-            }
-            // the two upper P tiles that the output products read, (0,1) and (2,3)
-            if (OUT && wave >= NW - 2) {
-                const int z = wave - (NW - 2);
+                const int ntl = OUT ? 3 : third_kk ? 2 : 1;
+                f32x4 cf[3], cc[3];
+                float sc[3];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sP[(32 * z + 4 * lg + e) * LAA + kperm(32 * z + 16 + lc)] = _Float16(0);
+                for (int t = 0; t < 3; ++t) off_factors(kq[t], mi[t], ni[t], cf[t], sc[t]);
+                if (OUT) gram_tiles<3, D, LDF>(sK, X, mi, ni, lg, lc, cc);
+                else if (third_kk) gram_tiles<2, D, LDF>(sK, X, mi, ni, lg, lc, cc);
+                else gram_tiles<1, D, LDF>(sK, X, mi, ni, lg, lc, cc);
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+                    if (t < ntl) store_off(kq[t], mi[t], ni[t], cc[t], cf[t], sc[t]);
             }
+        } else {
+            // generic: the off-diagonal K K^T and (OUT) Q K^T tiles, dealt to
+            // the waves in turn
+            constexpr int NREAL = OUT ? 12 : 6;
+            for (int tt = wave; tt < NREAL; tt += NW) {
+                int mi, ni;
+                off_coords(tt % 6, mi, ni);
+                const bool kq = tt < 6;
+                const uint16_t* X[1] = {kq ? sK : sQb};
+                f32x4 cf, cc[1];
+                float sc;
+                off_factors(kq, mi, ni, cf, sc);
+                gram_tiles<1, D, LDF>(sK, X, &mi, &ni, lg, lc, cc);
+                store_off(kq, mi, ni, cc[0], cf, sc);
+            }
+        }
+        // the two upper P tiles that the output products read, (0,1) and (2,3)
+        if (OUT && wave >= NW - 2) {
+            const int z = wave - (NW - 2);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sP[(32 * z + 4 * lg + e) * LAA + kperm(32 * z + 16 + lc)] = _Float16(0);
         }
         lds_sync();
         if (more) issue(rv, v, c + 1);
