@@ -44,8 +44,12 @@ using MF = Mfma<_Float16>;
 constexpr int SD = 128;        // head dimension
 constexpr int QB = 128;        // queries per workgroup
 constexpr int KB = 64;         // keys per block
-constexpr int KLD = SD + 8;    // K tile row stride (halves)
-constexpr int VLD = KB + 8;    // V^T tile row stride (halves)
+// Row strides (halves) of the K and V^T tiles.  Both are read as 16-byte
+// matrix-core fragments (lane group g: 16 rows, chunk g of a 32-element step),
+// which run free of bank conflicts on gfx950 when a row is 2 mod 4 chunks of
+// 16 bytes long, and at half rate for an odd chunk count (measured).
+constexpr int KLD = SD + 16;   // K tile row stride (halves)
+constexpr int VLD = KB + 16;   // V^T tile row stride (halves)
 constexpr float kNegBig = -1e30f;
 
 // ---------------------------------------------------------------------------
