@@ -75,8 +75,12 @@ TRAFFIC_FILES = [os.path.join(ROOT, "profiles", f)
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=300)
+    p.add_argument("--warmup", type=int, default=30)
+    p.add_argument("--settle-ms", type=float, default=50.0,
+                   help="untimed prefill calls for this long (wall time) before the warmup "
+                        "steps: the GPU clocks ramp up over the first milliseconds of work "
+                        "after idle")
     p.add_argument("--decode-steps", type=int, default=1000)
     p.add_argument("--decode-reps", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -227,6 +231,13 @@ def time_prefill(gdn, args, dev):
                      device=dev)
     stream = torch.cuda.current_stream(dev)
     call = lambda: gdn.prefill(q, k, v, g, beta, None, state_out=st, o=o, workspace=ws)
+    # Settle: the prefill is the process's first GPU work; after idle the clocks
+    # ramp up over several milliseconds (a 5 ms timed region measured ~10% slow).
+    t_end = time.perf_counter() + args.settle_ms / 1e3
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -707,7 +718,8 @@ def main():
     line = {
         "metric": "Gated DeltaNet prefill tokens/s at H=16, d=128 (decode tokens/s beside)",
         "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "prefill8k: B=1, H=16, T=8192, d_k=d_v=128, bf16 q/k/v, "
                                "fp32 g/beta/state/o, chunk 64, zero initial state",
