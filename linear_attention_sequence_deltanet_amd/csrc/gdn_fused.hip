@@ -230,7 +230,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     constexpr int NL = FC * D / 8 / NTH;  // 8-element input groups per thread per tensor
 
     __shared__ __align__(16) uint16_t sK[FC * LDF];             // raw bf16
-    __shared__ __align__(16) _Float16 sQ[OUT ? FC * LDF : 8];    // fp16 (Q H0)
+    // fp16 Q (Q H0) of chunk c in sQ[c & 1]: a wave stages the next chunk's
+    // inputs right after its part of the state update, while others may still
+    // read the current chunk's Q there
+    __shared__ __align__(16) _Float16 sQ[OUT ? 2 * FC * LDF : 8];
     __shared__ __align__(16) uint16_t sQb[OUT ? FC * LDF : 8];   // raw bf16 (Q K^T)
     __shared__ __align__(16) _Float16 sW[FC * LDF];      // -W [t][key]
     __shared__ __align__(16) uint16_t sV[FC * LDV];             // raw bf16
@@ -324,6 +327,25 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         issue_gates(c);
     };
     issue_loads(c_begin);
+    // chunk c's inputs (in rq, rk, rv) into LDS: K and V raw, Q raw and as fp16
+    // (kperm order).  Every wave stages its own rows.
+    auto stage_inputs = [&](int c, int lane_i) {
+        const int tid = wave * 64 + lane_i;
+        _Float16* q16 = sQ + (OUT ? (c & 1) * FC * LDF : 0);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int idx = tid + NTH * i, r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+            *reinterpret_cast<uint4*>(&sK[r * LDF + c8]) = rk[i];
+            if (OUT) {
+                const H8 qh = bf16x8_to_f16(rq[i]);
+                st4<_Float16>(&q16[r * LDF + kperm(c8)], __builtin_shufflevector(qh, qh, 0, 1, 2, 3));
+                st4<_Float16>(&q16[r * LDF + kperm(c8 + 4)], __builtin_shufflevector(qh, qh, 4, 5, 6, 7));
+                *reinterpret_cast<uint4*>(&sQb[r * LDF + c8]) = rq[i];
+            }
+            *reinterpret_cast<uint4*>(&sV[r * LDV + c8]) = rv[i];
+        }
+    };
+    stage_inputs(c_begin, lane);
     // wave 0: the chunk's gate factors from its g and beta (in rg, rb)
     auto form_gates = [&](ChunkGates& gt) {
         const float bv = rb;
@@ -350,7 +372,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     for (int c = c_begin; c < c_end; ++c) {
         const long t0 = (long)c * FC;
         const int n = (int)min((long)FC, (long)T - t0);
-        lds_sync();  // previous chunk's operands are no longer read
+        lds_sync();  // chunk c's inputs and gates staged; the previous chunk's operands no longer read
         // Re-derive the lane index through an opaque copy every chunk: otherwise
         // the compiler hoists hundreds of lane-dependent addresses out of the
         // loop, one register each, and spills.
@@ -360,25 +382,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         const int tid = wave * 64 + lane_i;
         ChunkGates& gt = sG[c & 1];
 
-        // ---- inputs into LDS (row-major K, V raw; Q raw and fp16)
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const int idx = tid + NTH * i, r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-            *reinterpret_cast<uint4*>(&sK[r * LDF + c8]) = rk[i];
-            if (OUT) {
-                const H8 qh = bf16x8_to_f16(rq[i]);
-                st4<_Float16>(&sQ[r * LDF + kperm(c8)], __builtin_shufflevector(qh, qh, 0, 1, 2, 3));
-                st4<_Float16>(&sQ[r * LDF + kperm(c8 + 4)], __builtin_shufflevector(qh, qh, 4, 5, 6, 7));
-                *reinterpret_cast<uint4*>(&sQb[r * LDF + c8]) = rq[i];
-            }
-            *reinterpret_cast<uint4*>(&sV[r * LDV + c8]) = rv[i];
-        }
         const bool more = c + 1 < c_end;
         if (more) {
             issue(rk, k, c + 1);
             issue_gates(c + 1);
         }
-        lds_sync();
 
         // ---- Gram tiles.  Waves 0-3: diagonal block w of K K^T, the inverse
         // of (I + A_ww) and (OUT) the diagonal Q K^T tile w.  The other waves:
@@ -595,7 +603,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 fw[kk & 1][mt] = ld8<_Float16>(&sW[(16 * mt + lc) * LDF + 32 * kk + 8 * lg]);
-                if (OUT) fq[kk & 1][mt] = ld8<_Float16>(&sQ[(16 * mt + lc) * LDF + 32 * kk + 8 * lg]);
+                if (OUT) fq[kk & 1][mt] = ld8<_Float16>(&sQ[(c & 1) * FC * LDF + (16 * mt + lc) * LDF + 32 * kk + 8 * lg]);
             }
         };
         load_step(0);
@@ -696,6 +704,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             }
         }
         if (wave == 0 && more) form_gates(sG[(c + 1) & 1]);
+        // the next chunk's inputs: sK, sV and sQb are no longer read in this
+        // chunk once a wave has passed the solve
+        if (more) stage_inputs(c + 1, lane_i);
     }
 
     // ---- segment result
