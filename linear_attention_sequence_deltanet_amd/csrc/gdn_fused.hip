@@ -517,7 +517,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 sP[(32 * z + 4 * lg + e) * LAA + kperm(32 * z + 16 + lc)] = _Float16(0);
         }
         lds_sync();
-        if (more) issue(rv, v, c + 1);
+        if (more) {
+            issue(rv, v, c + 1);
+            if (OUT) issue(rq, q, c + 1);
+        }
 
         // ---- blocked solve with the right-hand side in fp32:
         //   Y_b = B_b - sum_{j<b} A_bj X_j,  X_b = Y_b + N_bb Y_b
@@ -589,7 +592,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             if (TPW == 2) u[TPW - 1][bb] = zero4();  // identity columns: no U
         }
         lds_sync();  // -W and K^T complete
-        if (OUT && more) issue(rq, q, c + 1);
 
         // ---- state update for this wave's columns (no workgroup barrier).
         // The state and Delta enter the products as fp16 B operands packed from
