@@ -11,19 +11,22 @@
 // Linear and Sparse Attention ...", "The Concept: Gated DeltaNet".
 //
 // One workgroup owns one (segment, head) and walks the segment's chunks.  Per
-// chunk it first builds every chunk operand in LDS -- q, k, v tiles, K^T, the
-// Gram tiles, the blocked triangular solve, -W, U, P -- so nothing of the
-// chunk goes back to HBM, then advances the state.  The workgroup has D/16
-// waves; wave w owns a 16-column slice of the state (fp32, registers), which
-// makes the state update free of workgroup barriers: each wave only exchanges
-// its own slice with LDS.  Inputs of the next chunk are prefetched into
-// registers while the current one computes.
+// chunk it first builds every chunk operand in LDS -- the Gram tiles, the
+// blocked triangular solve, -W, U, P, (diag(e) K)^T -- so nothing of the chunk
+// goes back to HBM, then advances the state.  The workgroup has D/16 waves;
+// wave w owns a 16-column slice of the state (fp32, registers), which makes
+// the state update free of workgroup barriers: the state and Delta enter the
+// matrix-core products as fp16 operands packed in registers.  The next chunk's
+// inputs are loaded into registers while the current one computes, and each
+// wave stages its rows of them in LDS right after its part of the state update.
 //
 //   OUT mode: state columns = the d_v value columns; starts from state_in (one
 //             segment) or from the segment's start state; writes o (and the
-//             final state when there is one segment).
+//             final state from the last segment).
 //   SUM mode: state columns = [value | identity] (2 d_v); starts from [0 | I]
-//             and stores the segment's affine map [R | M] (H_end = M H_start + R).
+//             ([state_in | I] for the first segment) and stores the segment's
+//             affine map [R | M] (H_end = M H_start + R); the last segment has
+//             none.
 //
 // Matrix-core products of two inputs (the Gram tiles, the identity products
 // that transpose K and V) take the bf16 inputs as stored; every product with a
