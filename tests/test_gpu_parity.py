@@ -115,6 +115,26 @@ def test_two_segments_sampled(env):
     assert np.isfinite(o).all() and np.isfinite(st).all()
 
 
+def test_segments_in_rounds_sampled(env):
+    """B=2, T=1024, H=48, d=128, bf16: 96 series of 16 chunks planned as 8 segments
+    of 2 chunks, so each pass runs 768 workgroups in three rounds over the CUs;
+    random initial state updated in place; the oracle runs four sampled series."""
+    gdn, dev = env
+    import torch
+    _note("case segments in rounds B=2 T=1024 H=48 (sampled heads)")
+    d = gdn_inputs.random_inputs(2, 1024, 48, 128, 128, dtype="bf16", seed=1048, state_std=0.2)
+    x = stage(d, dev)
+    st = x["state0"].clone()
+    o, _ = gdn.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], st, state_out=st)
+    torch.cuda.synchronize()
+    o, st = o.cpu().numpy(), st.cpu().numpy()
+    heads = [(0, 0), (0, 47), (1, 5), (1, 30)]
+    ro, rs = oracle_heads(d, heads)
+    for n, (b, h) in enumerate(heads):
+        _check("rounds b%d h%d" % (b, h), o[b, :, h], st[b, h], ro[n], rs[n], TOL["bf16"])
+    assert np.isfinite(o).all() and np.isfinite(st).all()
+
+
 def test_prefill8k_full(env):
     """B=1, H=16, T=8192, d=128, bf16: every output and state element."""
     _note("case prefill8k full")
