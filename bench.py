@@ -709,7 +709,10 @@ def main():
                            % (len(PREFILL_KERNELS), len(kms)))
     kernels = [{"kernel": name, "us": t * 1e3, "share": t / sum(kms)}
                for (name, _), t in zip(PREFILL_KERNELS, kms)]
-    dom = int(np.argmax(kms))
+    # the dominant kernel among those with a per-token byte count (the
+    # combine has none: its traffic scales with segments, not tokens)
+    dom = max((i for i, (_, unit) in enumerate(PREFILL_KERNELS) if unit is not None),
+              key=lambda i: kms[i])
     dname, dbytes_unit = PREFILL_KERNELS[dom]
     dsec = kms[dom] / 1e3
     dbytes = dbytes_unit * units
