@@ -647,18 +647,20 @@ __global__ __launch_bounds__(256) void chunk_chain(const void* ws, SegWs sw,
 // ---------------------------------------------------------------------------
 // seg_combine: grid B*H*(D/16) workgroups of D/16 waves (wave w: key tile w of
 // one 16-column slice), sequential over the segments.  H_s = M_s H_{s-1} + R_s
-// in fp32-grade arithmetic: both factors are split into fp16 high and low
-// parts (M already by the summary writer) and three products are accumulated.
-// Stores each segment's start state and the final state.
+// with the state split into fp16 high and low parts.  LO: M's low part is
+// applied too (three products, fp32-grade, for fp32 inputs); otherwise M's
+// fp16 high part only (two products: the bf16-input chain that wrote M already
+// rounds its state operands to fp16 every chunk).  Stores each segment's start
+// state and the final state.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool LO>
 __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const float* state_in,
                                                            float* state_out, int BH, int S,
                                                            int direct) {
     using M = Mfma<_Float16>;
     using F8 = M::frag8;
     constexpr int NS = D / 16, LS = D + 8;
-    constexpr int NB = 2;  // segments whose summaries are in flight
+    constexpr int NB = LO ? 2 : 3;  // segments whose summaries are in flight
     // fp16 high / low parts of the chained state slice, [col][key], double-buffered
     __shared__ __align__(16) _Float16 sHi[2][16 * LS], sLo[2][16 * LS];
 
@@ -709,7 +711,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
         const _Float16* mh = reinterpret_cast<const _Float16*>(sm + D * D);
         const int off = ((wave * (D / 32) + kk) * 64 + lane) * 8;
         p.hi[kk] = *reinterpret_cast<const F8*>(mh + off);
-        p.lo[kk] = *reinterpret_cast<const F8*>(mh + D * D + off);
+        if constexpr (LO) p.lo[kk] = *reinterpret_cast<const F8*>(mh + D * D + off);
     };
     auto load = [&](Pre& p, int s) {
         const float* sm = sum_of(s);
@@ -744,17 +746,20 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
             blo[kk] = ld8<_Float16>(&bl_[lc * LS + 32 * kk + 8 * lg]);
         }
         const float* nsm = sum_of(next);
-        f32x4 a0 = p.r, a1 = zero4(), a2 = zero4();  // three independent chains
+        f32x4 a0 = p.r, a1 = zero4(), a2 = zero4();  // independent chains
         load_r(p, nsm);
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             a0 = M::k32(p.hi[kk], bhi[kk], a0);
             a1 = M::k32(p.hi[kk], blo[kk], a1);
-            a2 = M::k32(p.lo[kk], bhi[kk], a2);
+            if constexpr (LO) a2 = M::k32(p.lo[kk], bhi[kk], a2);
             load_m(p, nsm, kk);
             __builtin_amdgcn_sched_barrier(0);
         }
-        hs = a0 + (a1 + a2);
+        if constexpr (LO)
+            hs = a0 + (a1 + a2);
+        else
+            hs = a0 + a1;
     };
 
     if (direct) {
@@ -859,7 +864,7 @@ static hipError_t launch_chunked_t(const void* q, const void* k, const void* v, 
     profile_mark(stream);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_seg_combine(sw.summ, sw.sst, state_in, state_out, (int)BH, p.S, D, 0, stream);
+    e = launch_seg_combine(sw.summ, sw.sst, state_in, state_out, (int)BH, p.S, D, 0, 1, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_chain<In, D, DVT, CHAIN_OUT>),
                        dim3((unsigned)(BH * p.S * (D / DVT))), dim3(256), 0, stream,
@@ -870,14 +875,24 @@ static hipError_t launch_chunked_t(const void* q, const void* k, const void* v, 
 }
 
 hipError_t launch_seg_combine(float* summ, float* sst, const float* state_in, float* state_out,
-                              int BH, int S, int D, int direct, hipStream_t stream) {
+                              int BH, int S, int D, int direct, int m_lo, hipStream_t stream) {
     const SegWs sw{summ, sst};
-    if (D == 64)
-        hipLaunchKernelGGL((seg_combine<64>), dim3((unsigned)(BH * 4)), dim3(64 * 4), 0, stream,
-                           sw, state_in, state_out, BH, S, direct);
-    else
-        hipLaunchKernelGGL((seg_combine<128>), dim3((unsigned)(BH * 8)), dim3(64 * 8), 0, stream,
-                           sw, state_in, state_out, BH, S, direct);
+    const dim3 grid((unsigned)(BH * (D / 16))), block(64 * (D / 16));
+    if (D == 64) {
+        if (m_lo)
+            hipLaunchKernelGGL((seg_combine<64, true>), grid, block, 0, stream, sw, state_in,
+                               state_out, BH, S, direct);
+        else
+            hipLaunchKernelGGL((seg_combine<64, false>), grid, block, 0, stream, sw, state_in,
+                               state_out, BH, S, direct);
+    } else {
+        if (m_lo)
+            hipLaunchKernelGGL((seg_combine<128, true>), grid, block, 0, stream, sw, state_in,
+                               state_out, BH, S, direct);
+        else
+            hipLaunchKernelGGL((seg_combine<128, false>), grid, block, 0, stream, sw, state_in,
+                               state_out, BH, S, direct);
+    }
     profile_mark(stream);
     return hipGetLastError();
 }

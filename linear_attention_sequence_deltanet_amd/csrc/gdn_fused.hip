@@ -832,7 +832,7 @@ static hipError_t launch_fused_t(const void* q, const void* k, const void* v, co
     profile_mark(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_seg_combine(fs.summ, fs.sst, state_in, state_out, (int)BH, p.S, D, 1, stream);
+    e = launch_seg_combine(fs.summ, fs.sst, state_in, state_out, (int)BH, p.S, D, 1, 0, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gdn_fused<D, true>), dim3((unsigned)(BH * p.S)), block, 0, stream, qq, kk,
                        vv, g, beta, fs, state_in, state_out, o, T, H, B, p.NC, p.G, p.S);

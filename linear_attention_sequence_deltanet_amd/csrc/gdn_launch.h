@@ -32,9 +32,10 @@ hipError_t launch_chunked(const void* q, const void* k, const void* v, int dtype
 // start state to sst ([S][BH][D][D] f32).  direct = 0: every segment has a
 // summary from a zero start; the final state goes to state_out.  direct = 1:
 // segment 0's R is already segment 1's start state, the last segment has no
-// summary, and state_out is left to the last segment's output pass.
+// summary, and state_out is left to the last segment's output pass.  m_lo = 1
+// applies M's fp16 low part too (fp32 inputs); 0 its high part only.
 hipError_t launch_seg_combine(float* summ, float* sst, const float* state_in, float* state_out,
-                              int BH, int S, int D, int direct, hipStream_t stream);
+                              int BH, int S, int D, int direct, int m_lo, hipStream_t stream);
 
 // Fused bf16 prefill (chunk operands built in LDS, segment-parallel state chain).
 size_t fused_workspace_bytes(int B, int T, int H, int D);
