@@ -243,7 +243,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     __shared__ __align__(16) _Float16 sKT[D * LAF];      // (diag(e) K)^T [key][t]
     __shared__ __align__(16) _Float16 sA[FC * LAA];      // -A off-diagonal, (T_bb - I) diagonal blocks
     __shared__ __align__(16) _Float16 sP[OUT ? FC * LAA : 8];
-    __shared__ __align__(16) _Float16 sStg[OUT ? 8 : NW * 2 * D * 16];  // SUM: summary transpose
+    __shared__ __align__(16) _Float16 sStg[OUT ? 8 : NW * D * 16];  // SUM: summary transpose
     // gates of chunk c in sG[c & 1]: wave 0 forms the next chunk's at the end
     // of its part of the state update, while the other waves still read the
     // current chunk's
@@ -726,25 +726,21 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     } else {
         // segment summary in the combine's fragment order (summary_store()
         // defines it element by element): R tiles are this wave's C-layout
-        // tiles as they are; M (fp16 high and low parts) goes through this
-        // wave's staging area as [part][key][16 columns] and leaves as 16-byte
+        // tiles as they are; M's fp16 high part (the combine of this path
+        // applies no low part, which is left unwritten) goes through this
+        // wave's staging area as [key][16 columns] and leaves as 16-byte
         // A-operand slots: its 16 input-key columns are half of the 32-key block
         // colw / 32, lane groups 2 (wave & 1) and 2 (wave & 1) + 1.
         float* sm = fs.summ + ((long)seg * BH + bh) * D * 2 * D;
 #pragma unroll
         for (int m = 0; m < MT; ++m)
             *reinterpret_cast<f32x4*>(sm + ((wave * (D / 16) + m) * 64 + lane) * 4) = hs[0][m];
-        _Float16* mt = sStg + wave * 2 * D * 16;  // this wave's 2 D 16 halves
+        _Float16* mt = sStg + wave * D * 16;  // this wave's D 16 halves
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * m + 4 * lg + e;
-                const float x = hs[TPW - 1][m][e];
-                const _Float16 hi = static_cast<_Float16>(x);
-                mt[row * 16 + lc] = hi;
-                mt[D * 16 + row * 16 + lc] = static_cast<_Float16>(x - static_cast<float>(hi));
-            }
+            for (int e = 0; e < 4; ++e)
+                mt[(16 * m + 4 * lg + e) * 16 + lc] = static_cast<_Float16>(hs[TPW - 1][m][e]);
         lds_sync();
         _Float16* mh = reinterpret_cast<_Float16*>(sm + D * D);
 #pragma unroll
@@ -755,7 +751,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             const int off = ((m * (D / 32) + (wave >> 1)) * 64 + lane_f) * 8;
             const int src = (16 * m + row) * 16 + 8 * half;
             *reinterpret_cast<H8*>(mh + off) = *reinterpret_cast<const H8*>(&mt[src]);
-            *reinterpret_cast<H8*>(mh + D * D + off) = *reinterpret_cast<const H8*>(&mt[D * 16 + src]);
         }
     }
 }
