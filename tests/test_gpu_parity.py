@@ -94,6 +94,37 @@ def test_segmented_chain(env, T, dtype, dim):
            rs, TOL[dtype])
 
 
+def test_near_unit_gates_prefill8k_sampled(env):
+    """B=1, H=16, T=8192, d=128, bf16 with gates a = exp(-softplus(N - 9)) ~ 0.9999
+    and a random initial state: the segment maps M stay far from zero (over a
+    512-token segment only the delta-rule projections shrink the state), so the
+    combine's rounding of M and of the chained state reaches the outputs of every
+    later segment; the prefill8k plan (16 segments, 14 combine steps); oracle on
+    four sampled heads, every token."""
+    gdn, dev = env
+    _note("case near-unit gates prefill8k shape (sampled heads)")
+    d = gdn_inputs.random_inputs(1, 8192, 16, 128, 128, dtype="bf16", seed=8191, g_shift=-9.0,
+                                 state_std=0.2)
+    o, st = _prefill(env, d)
+    heads = [(0, 0), (0, 5), (0, 10), (0, 15)]
+    ro, rs = oracle_heads(d, heads)
+    for n, (b, h) in enumerate(heads):
+        _check("near-unit gates h%d" % h, o[b, :, h], st[b, h], ro[n], rs[n], TOL["bf16"])
+    assert np.isfinite(o).all() and np.isfinite(st).all()
+
+
+@pytest.mark.parametrize("dim", [64, 128])
+def test_near_unit_gates_f32_segmented(env, dim):
+    """fp32 inputs, gates ~ 0.9999, T=3000 (several segments, ragged tail), random
+    initial state: the fp32-grade combine under long memory, every element."""
+    _note("case near-unit gates f32 d=%d T=3000" % dim)
+    d = gdn_inputs.random_inputs(1, 3000, 2, dim, dim, dtype="f32", seed=3000 + dim, g_shift=-9.0,
+                                 state_std=0.2)
+    o, st = _prefill(env, d)
+    ro, rs = oracle_sequence(d)
+    _check("near-unit gates f32 d=%d" % dim, o, st, ro, rs, TOL["f32"])
+
+
 def test_two_segments_sampled(env):
     """B=2, T=3000, H=64, d=128, bf16: 128 series of 47 chunks split into two
     segments (the first one's summary starts from the random initial state, no
