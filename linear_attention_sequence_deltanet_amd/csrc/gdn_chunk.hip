@@ -660,7 +660,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
     using M = Mfma<_Float16>;
     using F8 = M::frag8;
     constexpr int NS = D / 16, LS = D + 8;
-    constexpr int NB = LO ? 2 : 3;  // segments whose summaries are in flight
+    constexpr int NB = 2;  // segments whose summaries are in flight
     // fp16 high / low parts of the chained state slice, [col][key], double-buffered
     __shared__ __align__(16) _Float16 sHi[2][16 * LS], sLo[2][16 * LS];
 
@@ -746,8 +746,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
             blo[kk] = ld8<_Float16>(&bl_[lc * LS + 32 * kk + 8 * lg]);
         }
         const float* nsm = sum_of(next);
-        f32x4 a0 = p.r, a1 = zero4(), a2 = zero4();  // independent chains
-        load_r(p, nsm);
+        f32x4 a0 = zero4(), a1 = zero4(), a2 = zero4();  // independent chains
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             a0 = M::k32(p.hi[kk], bhi[kk], a0);
@@ -756,10 +755,14 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
             load_m(p, nsm, kk);
             __builtin_amdgcn_sched_barrier(0);
         }
+        // R is read here, after the products, and only then reloaded: taken as
+        // the first product's accumulator it made the compiler copy it and wait
+        // for its reload within the same segment
         if constexpr (LO)
-            hs = a0 + (a1 + a2);
+            hs = p.r + (a0 + (a1 + a2));
         else
-            hs = a0 + a1;
+            hs = p.r + (a0 + a1);
+        load_r(p, nsm);
     };
 
     if (direct) {
