@@ -62,7 +62,7 @@ GATE_BYTES_PER_TOKEN_HEAD = 512 + 256 + 256
 # Kernels of one bf16 prefill call of several segments, in launch order, with
 # the algorithmic bytes per token x head each reads or writes.
 PREFILL_KERNELS = [("summary pass (gdn_fused<128,false>)", 2 * 256 + 8),
-                   ("segment combine (seg_combine<128>)", None),
+                   ("segment combine (seg_combine<128, false>)", None),
                    ("output pass (gdn_fused<128,true>)", PREFILL_BYTES_PER_TOKEN_HEAD)]
 # Sources of the prefill, decode and layer kernels; the counter summaries record their hash.
 KERNEL_SOURCES = ["gdn_fused.hip", "gdn_chunk.hip", "gdn_decode.hip", "gdn_layer.hip",
