@@ -273,6 +273,32 @@ def test_stream_sampled(env):
         _check("stream head %d" % h, on[b, :, h], sn[b, h], ro[n], rs[n], TOL["bf16"])
 
 
+def test_stream_near_unit_gates(env):
+    """B=1, H=16, d=128 (the stream workload's shape), bf16: 40 calls x 272 tokens
+    with gates ~ 0.9999 and a random initial state carried in place; each call
+    runs five one-chunk segments, so the combine's rounding enters the state 3
+    times per call and the error must not build up over the calls; oracle over
+    all 10,880 tokens, every element."""
+    gdn, dev = env
+    import torch
+    _note("case stream near-unit gates 40 x 272")
+    ct, calls = 272, 40
+    d = gdn_inputs.random_inputs(1, ct * calls, 16, 128, 128, dtype="bf16", seed=272,
+                                 g_shift=-9.0, state_std=0.2)
+    x = stage(d, dev)
+    state = x["state0"].clone()
+    o = torch.empty((1, ct * calls, 16, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, gdn.prefill_workspace_bytes(1, ct, 16, 128, 128)), dtype=torch.uint8,
+                     device=dev)
+    for c in range(calls):
+        sl = slice(c * ct, (c + 1) * ct)
+        gdn.stream_chunk(x["q"][:, sl], x["k"][:, sl], x["v"][:, sl], x["g"][:, sl],
+                         x["beta"][:, sl], state, o=o[:, sl], workspace=ws)
+    torch.cuda.synchronize()
+    ro, rs = oracle_sequence(d)
+    _check("stream near-unit gates", o.cpu().numpy(), state.cpu().numpy(), ro, rs, TOL["bf16"])
+
+
 def test_stream_equals_prefill(env):
     """Stream calls of uneven sizes equal one prefill over the concatenation."""
     gdn, dev = env
