@@ -18,15 +18,17 @@ A step is one whole-path call over one batch of synthetic inputs already in HBM:
   * backward: gradients of the prefill8k call (gdn_backward), tokens/s and the
     fp32 arithmetic rate of the chunked form;
   * stream: gdn_stream_chunk calls of 272 tokens (256 visual + 16 text) carrying
-    the state in place; the first 200 frames of the stream are staged and replayed
-    in order (calls/s = frames/s, beside).
+    the state in place over the 2000 distinct frames of the stream workload, all
+    staged in HBM beforehand (calls/s = frames/s, beside).
 Timing uses HIP events on the stream the library launches on (torch's current
 stream).  A second pass over the same steps records events between the
 library's kernels (gdn_set_profile_events) to time each kernel; the roofline
 object is the dominant kernel's.  Its `traffic` comes from the committed
 rocprofv3 counter summary when that summary was taken on the current kernel
 sources (else null).  The fp64 oracle is timed on the host cores as a reported
-CPU baseline.  Prints ONE JSON line.
+CPU baseline; its outputs also give the GPU's parity maxima on the same bytes.
+The line records the host (cores, CPU model), the GPU (name, compute units) and
+a hash of the kernel sources.  Prints ONE JSON line.
 """
 import argparse
 import ctypes
@@ -96,7 +98,8 @@ def parse():
     p.add_argument("--no-b512", action="store_true")
     p.add_argument("--b512-steps", type=int, default=100)
     p.add_argument("--stream-calls", type=int, default=2000)
-    p.add_argument("--stream-frames", type=int, default=200)
+    p.add_argument("--stream-frames", type=int, default=2000,
+                   help="distinct frames staged (calls beyond them replay frames in order)")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="first copy this many MiB device to device three times (a copy of "
                         "known size that calibrates hardware byte counters)")
@@ -253,7 +256,8 @@ def time_prefill(gdn, args, dev):
     flush = Flush(dev)
     cms = cold_ms(call, args.cold_reps, flush, stream)
     del flush
-    return d, ms, kms, cms, (B, T, H, dk)
+    gpu_out = (o.cpu().numpy(), st.cpu().numpy())  # every call writes the same bytes
+    return d, ms, kms, cms, (B, T, H, dk), gpu_out
 
 
 def time_decode(gdn, args, dev):
@@ -297,10 +301,15 @@ def time_decode(gdn, args, dev):
 
     state.copy_(s0)
     gms = graph_ms(loop) / N
-    # cold: the whole loop right after a cache flush (only its first steps can miss)
+    # cold: single steps, each right after a cache-evicting write (the state and
+    # the step's inputs come from HBM)
     flush = Flush(dev)
+    ctr = iter(range(N))
+    def one():
+        n = next(ctr) % N
+        gdn.decode_step(q[n], k[n], v[n], g[n], beta[n], state, o=o[n])
     state.copy_(s0)
-    cms = cold_ms(loop, 1, flush, stream) / N
+    cms = cold_ms(one, args.cold_reps, flush, stream)
     del flush
     return ms, kms, gms, cms, (N, B, H, dk)
 
@@ -457,8 +466,9 @@ def time_stream(gdn, args, dev):
     cbytes = PREFILL_BYTES_PER_TOKEN_HEAD * B * ct * H + 2 * B * H * dk * dk * 4
     gbs = cbytes / (ms / 1e3) / 1e9
     return {"workload": "stream: B=1, H=16, d=128, %d calls x %d tokens (256 visual + 16 text), "
-                        "state in place; first %d frames staged, replayed in order"
-                        % (args.stream_calls, ct, nf),
+                        "state in place; %d distinct frames staged in HBM%s"
+                        % (args.stream_calls, ct, nf,
+                           "" if nf >= args.stream_calls else ", replayed in order"),
             "value": 1e3 / ms, "unit": "calls/s (frames/s)", "us_per_call": ms * 1e3,
             "tokens_per_s": ct * 1e3 / ms,
             "graph": {"value": 1e3 / gms, "unit": "calls/s (frames/s)", "us_per_call": gms * 1e3,
@@ -597,12 +607,13 @@ def time_swa(gdn, args, dev):
 
 
 # Backward, per chunk x head (C = 64, d = 128): matrix products of the chunked
-# form: 9 of C x d x d (W H0, K^T Delta, K G, Q^T dO, K^T dR, dO H0^T, Delta G^T,
-# dR H0^T, and the C x d x d share of the prep is none) and 11 of C x C x d
-# (K K^T, Q K^T, Ti K, Ti V, P^T dO, Ti^T dDelta, dR Delta^T, dO Delta^T, dPL K,
-# dPL^T Q, dAs K), 2 flops each.
-BWD_FLOPS_PER_CHUNK_HEAD = 2 * (9 * 64 * 128 * 128 + 11 * 64 * 64 * 128)
-FP32_VALU_PEAK_TFS = 157.3
+# form, 2 flops per multiply-add: 9 of C x d x d (W H0, K^T Delta, K G, Q^T dO,
+# K^T dR, dO H0^T, Delta G^T, dR H0^T, Gam_C-scaled state terms) and 11 of
+# C x C x d whose C x C factor is triangular (K K^T, Q K^T, Ti K, Ti V, P^T dO,
+# Ti^T dDelta, dR Delta^T, dO Delta^T, dPL K, dPL^T Q, dAs K), counted at half,
+# as the forward's triangles are.
+BWD_FLOPS_PER_CHUNK_HEAD = 2 * (9 * 64 * 128 * 128 + 11 * 64 * 64 * 128 // 2)
+FP32_MFMA_PEAK_TFS = 157.3
 
 
 def time_backward(gdn, args, dev):
@@ -643,9 +654,11 @@ def time_backward(gdn, args, dev):
                         "q/k/v), fp32 arithmetic",
             "value": B * T / (ms / 1e3), "unit": "tokens/s", "ms_per_call": ms,
             "kernels": [{"kernel": nm, "us": t * 1e3} for nm, t in zip(names, kms)],
-            "roofline": {"kernel": "whole backward call", "bound": "alu", "achieved": tfs,
-                         "peak": FP32_VALU_PEAK_TFS, "unit": "TFLOP/s",
-                         "frac": tfs / FP32_VALU_PEAK_TFS, "flops_per_call": fl}}
+            "roofline": {"kernel": "whole backward call", "bound": "mfma", "achieved": tfs,
+                         "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": tfs / FP32_MFMA_PEAK_TFS, "flops_per_call": fl,
+                         "note": "every product on the fp32 matrix cores (16x16x4); "
+                                 "triangular C x C factors counted at half"}}
 
 
 def cpu_baseline(d, seconds):
@@ -663,7 +676,7 @@ def cpu_baseline(d, seconds):
              d["beta"][:, :Ts])
         t0 = time.time()
         for _ in range(reps):
-            oracle.recurrence(*x, None, threads=threads)
+            ref = oracle.recurrence(*x, None, threads=threads)
         dt = time.time() - t0
         if dt >= seconds or dt >= 0.5 * seconds and Ts == T:
             break
@@ -672,9 +685,41 @@ def cpu_baseline(d, seconds):
             Ts = min(T, int(Ts * grow))
         else:
             reps = int(reps * grow) + 1
-    return {"value": reps * B * Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "fp64 token-serial oracle on the first %d of %d tokens of the prefill8k "
-                      "workload (B=1, H=16, d=128), %d repeat(s), %.1f s wall" % (Ts, T, reps, dt)}
+    return ({"value": reps * B * Ts / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+             "sample": "fp64 token-serial oracle on the first %d of %d tokens of the prefill8k "
+                       "workload (B=1, H=16, d=128), %d repeat(s), %.1f s wall"
+                       % (Ts, T, reps, dt)}, Ts, ref)
+
+
+def rel_err(x, ref):
+    den = float(np.max(np.abs(ref)))
+    return float(np.max(np.abs(np.asarray(x, np.float64) - ref)) / (den if den > 0 else 1.0))
+
+
+def host_info(dev):
+    """Host cores and CPU model, GPU name and compute units, kernel-source hash."""
+    import subprocess
+    import torch
+    cpu = None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    props = torch.cuda.get_device_properties(dev)
+    sha = None
+    try:
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                             text=True, timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return {"nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu, "gpu_name": props.name,
+            "gpu_arch": getattr(props, "gcnArchName", None),
+            "gpu_compute_units": props.multi_processor_count,
+            "kernel_sources_sha256": sources_hash(), "git_sha": sha}
 
 
 def main():
@@ -697,7 +742,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    d, ms, kms, cms, (B, T, H, dk) = time_prefill(gdn, args, dev)
+    d, ms, kms, cms, (B, T, H, dk), gpu_out = time_prefill(gdn, args, dev)
     tok_s = B * T / (ms / 1e3)
     units = B * T * H
     bytes_call = PREFILL_BYTES_PER_TOKEN_HEAD * units
@@ -719,7 +764,8 @@ def main():
     dgbs = dbytes / dsec / 1e9
     dtfs = flops_call / dsec / 1e12 if dom == len(PREFILL_KERNELS) - 1 else None
     line = {
-        "metric": "Gated DeltaNet prefill tokens/s at H=16, d=128 (decode tokens/s beside)",
+        "metric": "Gated DeltaNet prefill tokens/s and decode tokens/s at H=16,d=128; "
+                  "% of roofline",
         "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "settle_ms": args.settle_ms, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak",
@@ -738,10 +784,14 @@ def main():
                  "note": "median of %d single calls, each after a 1 GiB cache-evicting write"
                          % args.cold_reps},
         "call_roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": gbs / HBM_PEAK_GBS, "mfma_tflops": tfs,
-                          "mfma_frac": tfs / MFMA_F16_PEAK_TFS, "bytes_per_call": bytes_call,
-                          "flops_per_call": flops_call,
-                          "us_per_call_with_hook": sum(kms) * 1e3},
+                          "frac": gbs / HBM_PEAK_GBS,
+                          "frac_cold": bytes_call / (cms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                          "mfma_tflops": tfs, "mfma_frac": tfs / MFMA_F16_PEAK_TFS,
+                          "bytes_per_call": bytes_call, "flops_per_call": flops_call,
+                          "us_per_call_with_hook": sum(kms) * 1e3,
+                          "note": "the whole timed call (every kernel): algorithmic bytes and "
+                                  "flops over ms_per_step (warm) and over the cold median"},
+        "host": host_info(dev),
     }
     if not args.no_decode:
         dms, dkms, dgms, dcms, (N, DB, DH, ddk) = time_decode(gdn, args, dev)
@@ -761,8 +811,11 @@ def main():
             "graph": {"value": DB / (dgms / 1e3), "unit": "tokens/s", "us_per_step": dgms * 1e3,
                       "note": "the %d-step loop captured once as a HIP graph and replayed" % N},
             "cold": {"value": DB / (dcms / 1e3), "unit": "tokens/s", "us_per_step": dcms * 1e3,
-                     "note": "the %d-step loop right after a 1 GiB cache-evicting write; the "
-                             "67 MB state fits the 256 MB last-level cache, see decode512" % N},
+                     "frac": dbytes / (dcms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     "note": "median of %d single steps, each right after a 1 GiB "
+                             "cache-evicting write (between steps the 67 MB state otherwise "
+                             "stays in the 256 MB last-level cache; see decode512)"
+                             % args.cold_reps},
         }
         if not args.no_b512:
             line["decode512"] = time_decode_b512(gdn, args, dev)
@@ -777,7 +830,14 @@ def main():
     if not args.no_stream:
         line["stream"] = time_stream(gdn, args, dev)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(d, args.cpu_seconds)
+        line["cpu_baseline"], Ts, (ro, rs) = cpu_baseline(d, args.cpu_seconds)
+        o_gpu, st_gpu = gpu_out
+        line["parity"] = {"workload": "prefill8k, first %d tokens (every head)" % Ts,
+                          "o_max_rel_err": rel_err(o_gpu[:, :Ts], ro),
+                          "state_max_rel_err": rel_err(st_gpu, rs) if Ts == T else None,
+                          "tol": 2e-3,
+                          "metric": "max |gpu - oracle| / max |oracle| per tensor, against the "
+                                    "fp64 oracle run of cpu_baseline on the same bytes"}
     print(json.dumps(line), flush=True)
 
 

@@ -258,3 +258,67 @@ def swa_inputs(B: int, T: int, Hq: int = 16, Hkv: int = 2, d: int = 128, seed: i
     return {"q": bf16_bits(rng.standard_normal((B, T, Hq, d), dtype=np.float32)),
             "k": bf16_bits(rng.standard_normal((B, T, Hkv, d), dtype=np.float32)),
             "v": bf16_bits(rng.standard_normal((B, T, Hkv, d), dtype=np.float32))}
+
+
+def edge_inputs(kind: str, B: int, T: int, H: int, d: int, dtype: str = "bf16", seed: int = 0,
+                decode: bool = False) -> dict:
+    """Seeded inputs for the recurrence's exact special cases (explainer page,
+    "The Concept: Gated DeltaNet": keep old memory by a gate, correct the entry
+    a key addresses, write, read).  No method arithmetic: only draws, QR for
+    orthonormal key sets, and fixed gate values.
+
+    kind "retrieval": per (b, h) an orthonormal key set (columns of the Q factor
+      of a Gaussian d x d matrix, L2-normalised again after the storage cast).
+      Tokens 0..d-1 write key j with value v_j ~ N(0, 1), beta = 1, g = 0; every
+      later token reads with q = key j (j cycling) and beta = 0, g = 0, except
+      tokens T/2 .. T/2 + d/2 - 1, which overwrite keys 0..d/2-1 with fresh
+      values (beta = 1).  Zero initial state.
+    kind "decay": beta = 0 on every token (no writes),
+      with g = -softplus(N - 9) (gates ~ 0.9999), random unit q, k,
+      state0 ~ N(0, 1).
+    kind "nodecay": g = 0 exactly (gate 1), beta = sigmoid(N), random unit q, k,
+      v ~ N(0, 1), state0 ~ N(0, 0.2).
+
+    Returns the token-major dict of random_inputs ([B, T, H, d] ...); with
+    decode=True the arrays are step-major ([T, B, H, d], [T, B, H]) as the
+    decode tests read them."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0xED6E, ["retrieval", "decay",
+                                                                         "nodecay"].index(kind)]))
+    f32 = np.float32
+    q = _l2norm_rows(rng.standard_normal((B, T, H, d), dtype=f32))
+    k = _l2norm_rows(rng.standard_normal((B, T, H, d), dtype=f32))
+    v = rng.standard_normal((B, T, H, d), dtype=f32)
+    g = np.zeros((B, T, H), f32)
+    beta = np.zeros((B, T, H), f32)
+    state0 = None
+    if kind == "retrieval":
+        nw = min(d, T)
+        for b in range(B):
+            for h in range(H):
+                basis, _ = np.linalg.qr(rng.standard_normal((d, d)))
+                keys = _l2norm_rows(basis.T.astype(f32))  # rows are the keys
+                k[b, :nw, h] = keys[:nw]
+                beta[b, :nw, h] = 1.0
+                for t in range(nw, T):
+                    q[b, t, h] = keys[(t - nw) % nw]
+                lo = T // 2
+                if lo >= nw:
+                    hi = min(T, lo + nw // 2)
+                    k[b, lo:hi, h] = keys[:hi - lo]
+                    beta[b, lo:hi, h] = 1.0
+    elif kind == "decay":
+        x = rng.standard_normal((B, T, H), dtype=f32) - f32(9.0)
+        g = (-np.logaddexp(f32(0.0), x)).astype(f32)
+        state0 = rng.standard_normal((B, H, d, d), dtype=f32)
+    elif kind == "nodecay":
+        x = rng.standard_normal((B, T, H), dtype=f32)
+        beta = (1.0 / (1.0 + np.exp(-x))).astype(f32)
+        state0 = (0.2 * rng.standard_normal((B, H, d, d), dtype=f32)).astype(f32)
+    else:
+        raise ValueError(kind)
+    out = {"q": _store(q, dtype), "k": _store(k, dtype), "v": _store(v, dtype), "g": g,
+           "beta": beta, "state0": state0, "dtype": dtype}
+    if decode:
+        for n in ("q", "k", "v", "g", "beta"):
+            out[n] = np.ascontiguousarray(np.moveaxis(out[n], 1, 0))
+    return out

@@ -53,7 +53,16 @@ extern "C" {
 
 #define GDN_ABI_VERSION 3
 
-typedef enum gdn_status {
+/* The enums have int as their underlying type in C++ too, so that any int a C
+ * caller passes (valid or not) is a value of the type; in C they are int-sized
+ * on every supported ABI. */
+#ifdef __cplusplus
+#define GDN_ENUM_INT : int
+#else
+#define GDN_ENUM_INT
+#endif
+
+typedef enum gdn_status GDN_ENUM_INT {
     GDN_OK = 0,
     GDN_ERR_NULL = 1,         /* a required pointer is NULL                      */
     GDN_ERR_SHAPE = 2,        /* a size is < 1, or d_k != d_v                    */
@@ -65,19 +74,19 @@ typedef enum gdn_status {
     GDN_ERR_LAUNCH = 8        /* the HIP runtime rejected a launch                */
 } gdn_status;
 
-typedef enum gdn_dtype { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
+typedef enum gdn_dtype GDN_ENUM_INT { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
 
 /* GDN_ABI_VERSION of the built library. */
 int gdn_abi_version(void);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
-const char *gdn_status_str(int status);
+const char *gdn_status_str(gdn_status status);
 
 /*
  * Bytes of device workspace gdn_prefill / gdn_stream_chunk need for these sizes
  * (0 is a valid answer).  Pure host arithmetic; returns 0 for invalid sizes.
  */
-size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype);
+size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, gdn_dtype dtype);
 
 /*
  * gdn_prefill -- the whole recurrence over T tokens (chunkwise-parallel form).
@@ -99,7 +108,7 @@ size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int dtyp
  *                   are ignored; it must not overlap any other argument and
  *                   must not be shared by calls that can run concurrently.
  */
-int gdn_prefill(const void *q, const void *k, const void *v, int dtype,
+gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dtype,
                 const float *g, const float *beta,
                 const float *state_in, float *state_out, float *o,
                 int B, int T, int H, int dk, int dv,
@@ -116,7 +125,7 @@ int gdn_prefill(const void *q, const void *k, const void *v, int dtype,
  * Any T >= 1; successive calls with the same state equal one gdn_prefill over
  * the concatenated tokens, up to rounding.
  */
-int gdn_stream_chunk(const void *q, const void *k, const void *v, int dtype,
+gdn_status gdn_stream_chunk(const void *q, const void *k, const void *v, gdn_dtype dtype,
                      const float *g, const float *beta, float *state, float *o,
                      int B, int T, int H, int dk, int dv,
                      void *workspace, size_t workspace_bytes, void *stream);
@@ -131,14 +140,15 @@ int gdn_stream_chunk(const void *q, const void *k, const void *v, int dtype,
  * Equivalent to gdn_prefill with T = 1 and the state in place.  Needs no
  * workspace.  Each head's state is read once and written once.
  */
-int gdn_decode_step(const void *q, const void *k, const void *v, int dtype,
+gdn_status gdn_decode_step(const void *q, const void *k, const void *v, gdn_dtype dtype,
                     const float *g, const float *beta, float *state, float *o,
                     int B, int H, int dk, int dv, void *stream);
 
 /*
  * gdn_conv_qkv -- the layer prologue: the short causal convolution of q, k, v
  * (explainer page "InfiniteVL: Synergizing Linear and Sparse Attention ...",
- * section "Methodology", step 2: each Gated DeltaNet layer carries a 1D
+ * section "Step 2: Process tokens with Hybrid Blocks (1 SWA + 3 Gated
+ * DeltaNet)": each Gated DeltaNet layer carries a 1D
  * convolution of window size 4).  The pages give only the window; the readings
  * taken are stated here.  Per channel c (channel = h * d + feature) of each of
  * q, k, v, depthwise and causal, then SiLU:
@@ -165,7 +175,7 @@ int gdn_decode_step(const void *q, const void *k, const void *v, int dtype,
  * (every pointer 16-byte aligned; no output may overlap an input or another
  * output, except conv_state_out == conv_state_in).
  */
-int gdn_conv_qkv(const void *xq, const void *xk, const void *xv,
+gdn_status gdn_conv_qkv(const void *xq, const void *xk, const void *xv,
                  const float *wq, const float *wk, const float *wv,
                  const float *conv_state_in, float *conv_state_out,
                  void *q, void *k, void *v, int l2norm_qk,
@@ -173,7 +183,7 @@ int gdn_conv_qkv(const void *xq, const void *xk, const void *xv,
 
 /*
  * gdn_gate_out -- the layer epilogue: the output gate (explainer page, section
- * "Methodology", step 2).  Reading taken: per (token, head) row, an RMS norm
+ * "Step 2: Process tokens with Hybrid Blocks (1 SWA + 3 Gated DeltaNet)").  Reading taken: per (token, head) row, an RMS norm
  * of the recurrence output with a learned per-feature weight, times SiLU of a
  * gate projection:
  *
@@ -186,12 +196,12 @@ int gdn_conv_qkv(const void *xq, const void *xk, const void *xv,
  *       (GDN_F32); with GDN_F32 it may equal o exactly (in place).
  * Sizes: d in {64, 128}; B, T, H >= 1.  Errors and conventions as above.
  */
-int gdn_gate_out(const float *o, const void *z, const float *w, void *out, int out_dtype,
+gdn_status gdn_gate_out(const float *o, const void *z, const float *w, void *out, gdn_dtype out_dtype,
                  int B, int T, int H, int d, void *stream);
 
 /*
  * gdn_backward -- gradients of the mixer for training (the pages train the
- * Gated DeltaNet layers in three stages, explainer "Methodology"; they write no
+ * Gated DeltaNet layers, explainer "Training: Three Stages"; they write no
  * backward, so it is the exact gradient of the recurrence above).  For the loss
  *     L = sum_t <d_o[t], o[t]> + <d_state_out, state_T>
  * of a gdn_prefill from state_in, it writes dL/dq, dL/dk, dL/dv (fp32, the
@@ -206,7 +216,7 @@ int gdn_gate_out(const float *o, const void *z, const float *w, void *out, int o
  * conventions as gdn_prefill; no argument may overlap another.
  */
 size_t gdn_backward_workspace_bytes(int B, int T, int H, int dk, int dv);
-int gdn_backward(const void *q, const void *k, const void *v, int dtype,
+gdn_status gdn_backward(const void *q, const void *k, const void *v, gdn_dtype dtype,
                  const float *g, const float *beta, const float *state_in,
                  const float *d_o, const float *d_state_out,
                  float *dq, float *dk, float *dv, float *dg, float *dbeta, float *d_state_in,
@@ -217,7 +227,8 @@ int gdn_backward(const void *q, const void *k, const void *v, int dtype,
  * Sliding-window attention (SWA): the other token mixer of InfiniteVL's hybrid
  * blocks (explainer page "InfiniteVL: Synergizing Linear and Sparse Attention
  * ...", section "The Concept: Sliding Window Attention": attention restricted to
- * a moving window of recent tokens; section "Methodology", step 2: RoPE
+ * a moving window of recent tokens; section "Step 2: Process tokens with
+ * Hybrid Blocks (1 SWA + 3 Gated DeltaNet)": RoPE
  * positions, grouped-query attention with 16 query heads over 2 key-value
  * heads, an 8K window in the example).  Readings taken where the pages are
  * silent:
@@ -254,7 +265,7 @@ size_t gdn_swa_cache_bytes(int B, int Hkv, int d, int window);
  * gdn_swa_prefill -- SWA over T tokens at positions 0 .. T-1, no history.
  * workspace: at least gdn_swa_workspace_bytes() bytes, contents ignored.
  */
-int gdn_swa_prefill(const void *q, const void *k, const void *v, float *o,
+gdn_status gdn_swa_prefill(const void *q, const void *k, const void *v, float *o,
                     int B, int T, int Hq, int Hkv, int d, int window, float rope_base,
                     void *workspace, size_t workspace_bytes, void *stream);
 
@@ -271,7 +282,7 @@ int gdn_swa_prefill(const void *q, const void *k, const void *v, float *o,
  * gdn_swa_prefill over the concatenated tokens, up to rounding.
  * No argument may overlap another.
  */
-int gdn_swa_stream_chunk(const void *q, const void *k, const void *v,
+gdn_status gdn_swa_stream_chunk(const void *q, const void *k, const void *v,
                          void *k_cache, void *v_cache, long long pos0, float *o,
                          int B, int T, int Hq, int Hkv, int d, int window, float rope_base,
                          void *workspace, size_t workspace_bytes, void *stream);
@@ -297,7 +308,7 @@ int gdn_swa_stream_chunk(const void *q, const void *k, const void *v,
  * Returns GDN_OK, or GDN_ERR_NULL for events == NULL with count > 0, or
  * GDN_ERR_SHAPE for count < 0.
  */
-int gdn_set_profile_events(void *const *events, int count);
+gdn_status gdn_set_profile_events(void *const *events, int count);
 
 /* Number of events the last call recorded under the hook (0 when it is off). */
 int gdn_profile_marks(void);

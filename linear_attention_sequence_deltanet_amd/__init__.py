@@ -149,6 +149,18 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _empty(shape, dtype, device, stream):
+    """torch.empty for a buffer the library writes on `stream`.  When that is
+    not torch's current stream, the block is recorded on it, so the caching
+    allocator does not hand it to other work before the library's kernels on
+    `stream` are done with it (internal workspaces are freed on return)."""
+    torch = _torch()
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        t.record_stream(stream)
+    return t
+
+
 def _stream(stream, device):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream(device)
@@ -191,11 +203,10 @@ def prefill_workspace_bytes(B, T, H, dk, dv, dtype=GDN_BF16) -> int:
     return int(_lib.gdn_prefill_workspace_bytes(B, T, H, dk, dv, dtype))
 
 
-def _workspace(workspace, B, T, H, dk, dv, code, device):
+def _workspace(workspace, B, T, H, dk, dv, code, device, stream):
     need = int(_lib.gdn_prefill_workspace_bytes(B, T, H, dk, dv, code))
     if workspace is None and need > 0:
-        torch = _torch()
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        workspace = _empty(need, _torch().uint8, device, stream)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return workspace, nbytes
 
@@ -210,10 +221,10 @@ def prefill(q, k, v, g, beta, state_in=None, *, state_out=None, o=None, workspac
     _check_mixer(q, k, v, g, beta, ((state_in, "state_in"), (state_out, "state_out")), o,
                  (B, T, H))
     if o is None:
-        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+        o = _empty((B, T, H, dv), torch.float32, q.device, stream)
     if state_out is None:
-        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
-    workspace, nbytes = _workspace(workspace, B, T, H, dk, dv, code, q.device)
+        state_out = _empty((B, H, dk, dv), torch.float32, q.device, stream)
+    workspace, nbytes = _workspace(workspace, B, T, H, dk, dv, code, q.device, stream)
     st = _lib.gdn_prefill(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), _ptr(state_in),
                           _ptr(state_out), _ptr(o), B, T, H, dk, dv, _ptr(workspace), nbytes,
                           _stream(stream, q.device))
@@ -230,8 +241,8 @@ def stream_chunk(q, k, v, g, beta, state, *, o=None, workspace=None, stream=None
     code = _dtype_code(q)
     _check_mixer(q, k, v, g, beta, ((state, "state"),), o, (B, T, H))
     if o is None:
-        o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
-    workspace, nbytes = _workspace(workspace, B, T, H, dk, dv, code, q.device)
+        o = _empty((B, T, H, dv), torch.float32, q.device, stream)
+    workspace, nbytes = _workspace(workspace, B, T, H, dk, dv, code, q.device, stream)
     st = _lib.gdn_stream_chunk(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), _ptr(state),
                                _ptr(o), B, T, H, dk, dv, _ptr(workspace), nbytes,
                                _stream(stream, q.device))
@@ -249,7 +260,7 @@ def decode_step(q, k, v, g, beta, state, *, o=None, stream=None):
     code = _dtype_code(q)
     _check_mixer(q, k, v, g, beta, ((state, "state"),), o, (B, H))
     if o is None:
-        o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+        o = _empty((B, H, dv), torch.float32, q.device, stream)
     st = _lib.gdn_decode_step(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), _ptr(state),
                               _ptr(o), B, H, dk, dv, _stream(stream, q.device))
     if st != 0:
@@ -273,11 +284,11 @@ def conv_qkv(xq, xk, xv, wq, wk, wv, state=None, *, state_out=None, q=None, k=No
     _check(state, (B, 3, 3, H * d), torch.float32, "state")
     _check(state_out, (B, 3, 3, H * d), torch.float32, "state_out")
     dev = xq.device
-    q = torch.empty_like(xq) if q is None else q
-    k = torch.empty_like(xk) if k is None else k
-    v = torch.empty_like(xv) if v is None else v
+    q = _empty(xq.shape, torch.bfloat16, dev, stream) if q is None else q
+    k = _empty(xk.shape, torch.bfloat16, dev, stream) if k is None else k
+    v = _empty(xv.shape, torch.bfloat16, dev, stream) if v is None else v
     if state_out is None:
-        state_out = torch.empty((B, 3, 3, H * d), dtype=torch.float32, device=dev)
+        state_out = _empty((B, 3, 3, H * d), torch.float32, dev, stream)
     st = _lib.gdn_conv_qkv(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv),
                            _ptr(state), _ptr(state_out), _ptr(q), _ptr(k), _ptr(v),
                            1 if l2norm_qk else 0, B, T, H, d, _stream(stream, dev))
@@ -298,7 +309,7 @@ def gate_out(o, z, w, *, out=None, out_dtype=None, stream=None):
     if out is not None and tuple(out.shape) != tuple(o.shape):
         raise ValueError("out must have shape %s, got %s" % (tuple(o.shape), tuple(out.shape)))
     if out is None:
-        out = torch.empty(o.shape, dtype=out_dtype or torch.float32, device=o.device)
+        out = _empty(o.shape, out_dtype or torch.float32, o.device, stream)
     code = _dtype_code(out)
     st = _lib.gdn_gate_out(_ptr(o), _ptr(z), _ptr(w), _ptr(out), code, B, T, H, d,
                            _stream(stream, o.device))
@@ -324,7 +335,7 @@ def swa_new_cache(B, Hkv, d, window, device):
     torch = _torch()
     if window < 2:
         return None, None
-    return tuple(torch.empty((B, Hkv, window - 1, d), dtype=torch.float16, device=device)
+    return tuple(_empty((B, Hkv, window - 1, d), torch.float16, device, None)
                  for _ in range(2))
 
 
@@ -351,10 +362,10 @@ def swa_stream_chunk(q, k, v, k_cache, v_cache, pos0, window, *, rope_base=ROPE_
         _check(k_cache, (B, Hkv, window - 1, d), torch.float16, "k_cache")
         _check(v_cache, (B, Hkv, window - 1, d), torch.float16, "v_cache")
     if o is None:
-        o = torch.empty((B, T, Hq, d), dtype=torch.float32, device=q.device)
+        o = _empty((B, T, Hq, d), torch.float32, q.device, stream)
     need = swa_workspace_bytes(B, T, Hq, Hkv, d, window)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _empty(max(need, 16), torch.uint8, q.device, stream)
     nbytes = workspace.numel() * workspace.element_size()
     st = _lib.gdn_swa_stream_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
                                    int(pos0), _ptr(o), B, T, Hq, Hkv, d, window,
@@ -371,10 +382,10 @@ def swa_prefill(q, k, v, window, *, rope_base=ROPE_BASE, o=None, workspace=None,
     torch = _torch()
     B, T, Hq, Hkv, d = _swa_check(q, k, v, o)
     if o is None:
-        o = torch.empty((B, T, Hq, d), dtype=torch.float32, device=q.device)
+        o = _empty((B, T, Hq, d), torch.float32, q.device, stream)
     need = swa_workspace_bytes(B, T, Hq, Hkv, d, window)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _empty(max(need, 16), torch.uint8, q.device, stream)
     nbytes = workspace.numel() * workspace.element_size()
     st = _lib.gdn_swa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, T, Hq, Hkv, d, window,
                               float(rope_base), _ptr(workspace), nbytes, _stream(stream, q.device))
@@ -399,15 +410,15 @@ def backward(q, k, v, g, beta, state_in, d_o, d_state_out=None, *, want_dstate=T
     _check_mixer(q, k, v, g, beta, ((state_in, "state_in"), (d_state_out, "d_state_out")), d_o,
                  (B, T, H))
     dev = q.device
-    out = {"dq": torch.empty((B, T, H, dk), dtype=torch.float32, device=dev),
-           "dk": torch.empty((B, T, H, dk), dtype=torch.float32, device=dev),
-           "dv": torch.empty((B, T, H, dv), dtype=torch.float32, device=dev),
-           "dg": torch.empty((B, T, H), dtype=torch.float32, device=dev),
-           "dbeta": torch.empty((B, T, H), dtype=torch.float32, device=dev),
-           "dstate": torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dstate else None}
+    out = {"dq": _empty((B, T, H, dk), torch.float32, dev, stream),
+           "dk": _empty((B, T, H, dk), torch.float32, dev, stream),
+           "dv": _empty((B, T, H, dv), torch.float32, dev, stream),
+           "dg": _empty((B, T, H), torch.float32, dev, stream),
+           "dbeta": _empty((B, T, H), torch.float32, dev, stream),
+           "dstate": _empty((B, H, dk, dv), torch.float32, dev, stream) if want_dstate else None}
     need = backward_workspace_bytes(B, T, H, dk, dv)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        workspace = _empty(max(need, 16), torch.uint8, dev, stream)
     nbytes = workspace.numel() * workspace.element_size()
     st = _lib.gdn_backward(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta), _ptr(state_in),
                            _ptr(d_o), _ptr(d_state_out), _ptr(out["dq"]), _ptr(out["dk"]),

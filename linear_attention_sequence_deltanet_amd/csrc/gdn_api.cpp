@@ -31,7 +31,7 @@ inline bool overlap(Range a, Range b) {
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Checks shared by every entry point. T = 1 for decode.
-int check_sizes(int B, int T, int H, int dk, int dv, int dtype) {
+gdn_status check_sizes(int B, int T, int H, int dk, int dv, gdn_dtype dtype) {
     if (dtype != GDN_BF16 && dtype != GDN_F32) return GDN_ERR_DTYPE;
     if (B < 1 || T < 1 || H < 1 || dk < 1 || dv < 1) return GDN_ERR_SHAPE;
     if (dk != dv) return GDN_ERR_SHAPE;
@@ -43,7 +43,7 @@ int check_sizes(int B, int T, int H, int dk, int dv, int dtype) {
     return GDN_OK;
 }
 
-int check_io(const void* q, const void* k, const void* v, int dtype, const float* g,
+gdn_status check_io(const void* q, const void* k, const void* v, gdn_dtype dtype, const float* g,
              const float* beta, const float* state_in, const float* state_out, const float* o,
              int B, int T, int H, int dk, int dv, const void* ws, size_t ws_bytes) {
     if (!q || !k || !v || !g || !beta || !state_out || !o) return GDN_ERR_NULL;
@@ -72,17 +72,17 @@ int check_io(const void* q, const void* k, const void* v, int dtype, const float
     return GDN_OK;
 }
 
-inline int launch_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
+inline gdn_status launch_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
 
-int run_prefill(const void* q, const void* k, const void* v, int dtype, const float* g,
+gdn_status run_prefill(const void* q, const void* k, const void* v, gdn_dtype dtype, const float* g,
                 const float* beta, const float* state_in, float* state_out, float* o, int B,
                 int T, int H, int dk, void* ws, size_t ws_bytes, hipStream_t stream) {
     (void)ws_bytes;
     if (dtype == GDN_BF16)
         return launch_status(gdn::launch_fused(q, k, v, g, beta, state_in, state_out, o, B, T, H,
                                                dk, ws, stream));
-    return launch_status(gdn::launch_chunked(q, k, v, 0, g, beta, state_in, state_out, o, B, T,
-                                             H, dk, ws, stream));
+    return launch_status(gdn::launch_chunked(q, k, v, g, beta, state_in, state_out, o, B, T, H,
+                                             dk, ws, stream));
 }
 
 }  // namespace
@@ -103,7 +103,7 @@ void profile_mark(hipStream_t stream) {
 
 extern "C" {
 
-int gdn_set_profile_events(void* const* events, int count) {
+gdn_status gdn_set_profile_events(void* const* events, int count) {
     if (count < 0) return GDN_ERR_SHAPE;
     if (count > 0 && !events) return GDN_ERR_NULL;
     g_events = count > 0 ? reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)) : nullptr;
@@ -117,7 +117,7 @@ int gdn_profile_marks(void) { return g_marks; }
 
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 
-const char* gdn_status_str(int status) {
+const char* gdn_status_str(gdn_status status) {
     switch (status) {
         case GDN_OK: return "ok";
         case GDN_ERR_NULL: return "a required pointer is NULL";
@@ -132,17 +132,17 @@ const char* gdn_status_str(int status) {
     }
 }
 
-size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype) {
+size_t gdn_prefill_workspace_bytes(int B, int T, int H, int dk, int dv, gdn_dtype dtype) {
     if (check_sizes(B, T, H, dk, dv, dtype) != GDN_OK) return 0;
     if (dtype == GDN_BF16) return gdn::fused_workspace_bytes(B, T, H, dk);
-    return gdn::chunked_workspace_bytes(B, T, H, dk, 0);
+    return gdn::chunked_workspace_bytes(B, T, H, dk);
 }
 
-int gdn_prefill(const void* q, const void* k, const void* v, int dtype, const float* g,
+gdn_status gdn_prefill(const void* q, const void* k, const void* v, gdn_dtype dtype, const float* g,
                 const float* beta, const float* state_in, float* state_out, float* o, int B,
                 int T, int H, int dk, int dv, void* workspace, size_t workspace_bytes,
                 void* stream) {
-    int s = check_sizes(B, T, H, dk, dv, dtype);
+    gdn_status s = check_sizes(B, T, H, dk, dv, dtype);
     if (s != GDN_OK) return s;
     if (B > 65535 || H > 65535) return GDN_ERR_UNSUPPORTED;  // grid (chunks, H, B)
     const size_t need = gdn_prefill_workspace_bytes(B, T, H, dk, dv, dtype);
@@ -155,7 +155,7 @@ int gdn_prefill(const void* q, const void* k, const void* v, int dtype, const fl
                        workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
-int gdn_stream_chunk(const void* q, const void* k, const void* v, int dtype, const float* g,
+gdn_status gdn_stream_chunk(const void* q, const void* k, const void* v, gdn_dtype dtype, const float* g,
                      const float* beta, float* state, float* o, int B, int T, int H, int dk,
                      int dv, void* workspace, size_t workspace_bytes, void* stream) {
     if (!state) return GDN_ERR_NULL;
@@ -163,10 +163,10 @@ int gdn_stream_chunk(const void* q, const void* k, const void* v, int dtype, con
                        workspace_bytes, stream);
 }
 
-int gdn_decode_step(const void* q, const void* k, const void* v, int dtype, const float* g,
+gdn_status gdn_decode_step(const void* q, const void* k, const void* v, gdn_dtype dtype, const float* g,
                     const float* beta, float* state, float* o, int B, int H, int dk, int dv,
                     void* stream) {
-    int s = check_sizes(B, 1, H, dk, dv, dtype);
+    gdn_status s = check_sizes(B, 1, H, dk, dv, dtype);
     if (s != GDN_OK) return s;
     if ((long long)B * H > (1LL << 30)) return GDN_ERR_UNSUPPORTED;  // grid of B*H*d/64 blocks
     if (!state) return GDN_ERR_NULL;
@@ -178,7 +178,7 @@ int gdn_decode_step(const void* q, const void* k, const void* v, int dtype, cons
 }
 
 
-int gdn_conv_qkv(const void* xq, const void* xk, const void* xv, const float* wq, const float* wk,
+gdn_status gdn_conv_qkv(const void* xq, const void* xk, const void* xv, const float* wq, const float* wk,
                  const float* wv, const float* conv_state_in, float* conv_state_out, void* q,
                  void* k, void* v, int l2norm_qk, int B, int T, int H, int d, void* stream) {
     if (B < 1 || T < 1 || H < 1 || d < 1) return GDN_ERR_SHAPE;
@@ -210,7 +210,7 @@ int gdn_conv_qkv(const void* xq, const void* xk, const void* xv, const float* wq
                                               d, static_cast<hipStream_t>(stream)));
 }
 
-int gdn_gate_out(const float* o, const void* z, const float* w, void* out, int out_dtype, int B,
+gdn_status gdn_gate_out(const float* o, const void* z, const float* w, void* out, gdn_dtype out_dtype, int B,
                  int T, int H, int d, void* stream) {
     if (out_dtype != GDN_BF16 && out_dtype != GDN_F32) return GDN_ERR_DTYPE;
     if (B < 1 || T < 1 || H < 1 || d < 1) return GDN_ERR_SHAPE;
@@ -242,7 +242,7 @@ size_t gdn_swa_cache_bytes(int B, int Hkv, int d, int window) {
     return (size_t)B * Hkv * (size_t)(window - 1) * d * 2;
 }
 
-int gdn_swa_stream_chunk(const void* q, const void* k, const void* v, void* k_cache,
+gdn_status gdn_swa_stream_chunk(const void* q, const void* k, const void* v, void* k_cache,
                          void* v_cache, long long pos0, float* o, int B, int T, int Hq, int Hkv,
                          int d, int window, float rope_base, void* workspace,
                          size_t workspace_bytes, void* stream) {
@@ -281,7 +281,7 @@ int gdn_swa_stream_chunk(const void* q, const void* k, const void* v, void* k_ca
                                          static_cast<hipStream_t>(stream)));
 }
 
-int gdn_swa_prefill(const void* q, const void* k, const void* v, float* o, int B, int T, int Hq,
+gdn_status gdn_swa_prefill(const void* q, const void* k, const void* v, float* o, int B, int T, int Hq,
                     int Hkv, int d, int window, float rope_base, void* workspace,
                     size_t workspace_bytes, void* stream) {
     return gdn_swa_stream_chunk(q, k, v, nullptr, nullptr, 0, o, B, T, Hq, Hkv, d, window,
@@ -294,12 +294,12 @@ size_t gdn_backward_workspace_bytes(int B, int T, int H, int dk, int dv) {
     return gdn::backward_workspace_bytes(B, T, H, dk);
 }
 
-int gdn_backward(const void* q, const void* k, const void* v, int dtype, const float* g,
+gdn_status gdn_backward(const void* q, const void* k, const void* v, gdn_dtype dtype, const float* g,
                  const float* beta, const float* state_in, const float* d_o,
                  const float* d_state_out, float* dq, float* dk, float* dv, float* dg,
                  float* dbeta, float* d_state_in, int B, int T, int H, int dk_, int dv_,
                  void* workspace, size_t workspace_bytes, void* stream) {
-    int s = check_sizes(B, T, H, dk_, dv_, dtype);
+    gdn_status s = check_sizes(B, T, H, dk_, dv_, dtype);
     if (s != GDN_OK) return s;
     if (B > 65535 || H > 65535) return GDN_ERR_UNSUPPORTED;  // grid (chunks, H, B)
     if (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta)

@@ -1,7 +1,7 @@
 // gdn_backward.hip -- gradients of the gated delta rule on gfx950 (fp32).
 //
 // The pages train the Gated DeltaNet layers (explainer page "InfiniteVL:
-// Synergizing Linear and Sparse Attention ...", "Methodology", training stages)
+// Synergizing Linear and Sparse Attention ...", "Training: Three Stages")
 // but never write a backward pass; it is the exact gradient of the forward
 // recurrence ("The Concept: Gated DeltaNet") for the loss
 //     L = sum_t <dO_t, o_t> + <dH_T, H_T> ,      H = S^T (d_k x d_v).

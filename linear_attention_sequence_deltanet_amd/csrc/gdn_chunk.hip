@@ -17,21 +17,25 @@
 // overflows and long chunks of strong decay underflow cleanly to 0.  Padding a
 // ragged tail with g = b = 0 and q = k = v = 0 leaves every real row unchanged.
 //
-// Two kernels:
-//   chunk_prep  (one workgroup per chunk x head, fully parallel): gam, the Gram
-//               products K K^T and Q K^T, the triangular solve by 16-row
-//               blocks (diagonal blocks by forward substitution in fp32,
-//               off-diagonal corrections on matrix cores), and writes -W, Q,
-//               P, K^T, U and the decay factors to the workspace in the exact register-fragment
-//               order the scan consumes them (16-byte coalesced per lane).
-//   chunk_scan  (one workgroup per head x 16-column slice of the state,
-//               sequential over chunks): Delta, O and the state update, with
-//               the fp32 state tile held in registers across chunks and the
-//               next chunk's operands prefetched into registers.
-// bf16 inputs run the products on fp16 operands (bf16 values are exact in
-// fp16 at these magnitudes) with fp32 accumulation; the dominant terms
-// (b V, b Gam K in the solve, the state itself) stay fp32.  fp32 inputs run the
-// same code on fp32 operands.
+// This file holds the prefill of fp32 inputs and the segment combine that both
+// input types use:
+//   chunk_prep   (one workgroup per chunk x head, fully parallel): gam, the
+//                Gram products K K^T and Q K^T, the triangular solve by 16-row
+//                blocks (diagonal blocks by forward substitution in fp32,
+//                off-diagonal corrections on matrix cores), and writes -W, Q,
+//                P, K^T, U and the decay factors to the workspace in the exact
+//                register-fragment order the chain consumes them (16-byte
+//                coalesced per lane).
+//   chunk_chain  (one workgroup per head x column slice of the state and
+//                segment, sequential over the segment's chunks): Delta, O and
+//                the state update, with the fp32 state tile in registers and
+//                the next chunk's operands prefetched; in the summary mode it
+//                chains the augmented state [H | M] and stores the segment's
+//                affine map.
+//   seg_combine  applies the segment maps in order to give every segment's
+//                start state (fp16 matrix-core products on split operands).
+// Every product runs on the fp32 matrix cores (16x16x4) with exact fp32
+// operands.  bf16 inputs use the fused kernel of gdn_fused.hip instead.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 #include "gdn_mfma.h"
@@ -43,27 +47,11 @@ constexpr int CH = 64;  // chunk length (tokens)
 template <typename In>
 struct OpType;
 template <>
-struct OpType<bf16_t> {
-    using type = _Float16;
-};
-template <>
 struct OpType<float> {
     using type = float;
 };
 
-// Eight consecutive input elements (16- or 32-byte aligned) converted to OT.
-template <typename OT>
-__device__ __forceinline__ typename Mfma<OT>::frag8 load8_in(const bf16_t* p) {
-    const uint4 w = *reinterpret_cast<const uint4*>(p);
-    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-    typename Mfma<OT>::frag8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        r[2 * i] = static_cast<OT>(__uint_as_float(u[i] << 16));
-        r[2 * i + 1] = static_cast<OT>(__uint_as_float(u[i] & 0xffff0000u));
-    }
-    return r;
-}
+// Eight consecutive fp32 input elements (32-byte aligned) as an OT fragment.
 template <typename OT>
 __device__ __forceinline__ typename Mfma<OT>::frag8 load8_in(const float* p) {
     const float4 a = *reinterpret_cast<const float4*>(p);
@@ -78,22 +66,6 @@ __device__ __forceinline__ typename Mfma<OT>::frag8 load8_in(const float* p) {
 // the fragment is converted at its first use.
 template <typename In>
 struct Raw8;
-template <>
-struct Raw8<bf16_t> {
-    uint4 w;
-    __device__ __forceinline__ void load(const bf16_t* p) { w = *reinterpret_cast<const uint4*>(p); }
-    template <typename OT>
-    __device__ __forceinline__ typename Mfma<OT>::frag8 get() const {
-        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-        typename Mfma<OT>::frag8 r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            r[2 * i] = static_cast<OT>(__uint_as_float(u[i] << 16));
-            r[2 * i + 1] = static_cast<OT>(__uint_as_float(u[i] & 0xffff0000u));
-        }
-        return r;
-    }
-};
 template <>
 struct Raw8<float> {
     float4 a, b;
@@ -829,8 +801,7 @@ static size_t ws_bytes_t(int B, int T, int H) {
     return bytes;
 }
 
-size_t chunked_workspace_bytes(int B, int T, int H, int D, int dtype_bf16) {
-    if (dtype_bf16) return D == 64 ? ws_bytes_t<bf16_t, 64>(B, T, H) : ws_bytes_t<bf16_t, 128>(B, T, H);
+size_t chunked_workspace_bytes(int B, int T, int H, int D) {
     return D == 64 ? ws_bytes_t<float, 64>(B, T, H) : ws_bytes_t<float, 128>(B, T, H);
 }
 
@@ -900,15 +871,9 @@ hipError_t launch_seg_combine(float* summ, float* sst, const float* state_in, fl
     return hipGetLastError();
 }
 
-hipError_t launch_chunked(const void* q, const void* k, const void* v, int dtype_bf16,
-                          const float* g, const float* beta, const float* state_in,
-                          float* state_out, float* o, int B, int T, int H, int D, void* ws,
-                          hipStream_t stream) {
-    if (dtype_bf16) {
-        if (D == 64)
-            return launch_chunked_t<bf16_t, 64>(q, k, v, g, beta, state_in, state_out, o, B, T, H, ws, stream);
-        return launch_chunked_t<bf16_t, 128>(q, k, v, g, beta, state_in, state_out, o, B, T, H, ws, stream);
-    }
+hipError_t launch_chunked(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const float* state_in, float* state_out, float* o,
+                          int B, int T, int H, int D, void* ws, hipStream_t stream) {
     if (D == 64)
         return launch_chunked_t<float, 64>(q, k, v, g, beta, state_in, state_out, o, B, T, H, ws, stream);
     return launch_chunked_t<float, 128>(q, k, v, g, beta, state_in, state_out, o, B, T, H, ws, stream);

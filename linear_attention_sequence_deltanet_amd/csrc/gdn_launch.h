@@ -19,13 +19,12 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, int dtype_
                          const float* g, const float* beta, float* state, float* o, int B, int H,
                          int D, hipStream_t stream);
 
-// Chunkwise-parallel prefill (prep + scan kernels) using a caller workspace of
-// chunked_workspace_bytes() bytes.
-size_t chunked_workspace_bytes(int B, int T, int H, int D, int dtype_bf16);
-hipError_t launch_chunked(const void* q, const void* k, const void* v, int dtype_bf16,
-                          const float* g, const float* beta, const float* state_in,
-                          float* state_out, float* o, int B, int T, int H, int D, void* ws,
-                          hipStream_t stream);
+// Chunkwise-parallel prefill of fp32 inputs (prep + chain kernels) using a
+// caller workspace of chunked_workspace_bytes() bytes.
+size_t chunked_workspace_bytes(int B, int T, int H, int D);
+hipError_t launch_chunked(const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const float* state_in, float* state_out, float* o,
+                          int B, int T, int H, int D, void* ws, hipStream_t stream);
 
 // Sequential combine of per-segment affine maps ([S][BH] summaries of 8 D^2
 // bytes each, laid out as summary_store() writes them): writes every segment's

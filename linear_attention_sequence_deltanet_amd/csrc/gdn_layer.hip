@@ -2,7 +2,8 @@
 // recurrence, on gfx950.
 //
 // The explainer page ("InfiniteVL: Synergizing Linear and Sparse Attention ...",
-// section "Methodology", step 2) gives the layer a 1D convolution of window 4
+// section "Step 2: Process tokens with Hybrid Blocks (1 SWA + 3 Gated
+// DeltaNet)") gives the layer a 1D convolution of window 4
 // and an output gate.  Both are elementwise or per-(token, head) work, so both
 // kernels are bound by HBM bandwidth: every byte is read once and written once
 // with 16-byte accesses, and the per-head reductions stay inside one DPP row.

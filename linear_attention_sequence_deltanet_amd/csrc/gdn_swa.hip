@@ -1,8 +1,9 @@
 // gdn_swa.hip -- sliding-window attention (SWA) on gfx950: the other token mixer
 // of InfiniteVL's hybrid blocks (explainer page "InfiniteVL: Synergizing Linear
 // and Sparse Attention ...", sections "The Concept: Sliding Window Attention"
-// and "Methodology", step 2: attention inside a moving window of recent tokens,
-// RoPE positions, 16 query heads over 2 key-value heads).
+// (attention inside a moving window of recent tokens) and "Step 2: Process
+// tokens with Hybrid Blocks (1 SWA + 3 Gated DeltaNet)" (RoPE positions, 16
+// query heads over 2 key-value heads).
 //
 // The query at absolute position t attends to the keys at positions s with
 // t - W < s <= t; scores are q.k / sqrt(d) after RoFormer rotary embedding of

@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE ONLY: imported by the tests, never by the product path; it
 shares no code with the HIP library.
 
 The pages train the Gated DeltaNet layers (explainer page "InfiniteVL:
-Synergizing Linear and Sparse Attention ...", section "Methodology", training
-stages) but never write a backward pass.  The backward is therefore the exact
+Synergizing Linear and Sparse Attention ...", section "Training: Three
+Stages") but never write a backward pass.  The backward is therefore the exact
 gradient of the forward recurrence (explainer, "The Concept: Gated DeltaNet"),
 with the stored state H = S^T (d_k x d_v):
 

@@ -5,7 +5,7 @@ TEST INFRASTRUCTURE ONLY: imported by the tests and the smoke check, never by th
 product path; it shares no code with the HIP library.
 
 The explainer page ("InfiniteVL: Synergizing Linear and Sparse Attention ...",
-section "Methodology", step 2) gives each Gated DeltaNet layer a 1D convolution
+section "Step 2: Process tokens with Hybrid Blocks (1 SWA + 3 Gated DeltaNet)") gives each Gated DeltaNet layer a 1D convolution
 of window size 4 and an output gate, and nothing more.  The readings taken here
 (each is also listed among the design readings):
 

@@ -5,8 +5,8 @@ TEST INFRASTRUCTURE ONLY: imported by the tests and the smoke check, never by th
 product path; it shares no code with the HIP library.
 
 The explainer page ("InfiniteVL: Synergizing Linear and Sparse Attention ...",
-section "The Concept: Sliding Window Attention", and section "Methodology",
-step 2) describes the layer as attention restricted to a moving window of the
+section "The Concept: Sliding Window Attention", and section "Step 2: Process
+tokens with Hybrid Blocks (1 SWA + 3 Gated DeltaNet)") describes the layer as attention restricted to a moving window of the
 most recent tokens (8K in its example), with RoPE positions and grouped-query
 attention of 16 query heads over 2 key-value heads.  It gives nothing more;
 the readings taken here (each is also listed among the design readings):

@@ -21,8 +21,8 @@ OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, UNSUP, WS, LAUNCH = range(9)
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from linear_attention_sequence_deltanet_amd import build
-        build.build()
+        import __graft_entry__
+        __graft_entry__.build()
     import linear_attention_sequence_deltanet_amd as gdn
     return gdn._lib
 
@@ -104,16 +104,20 @@ def test_prefill_aliasing(lib):
     assert _prefill(lib, ws=P["o"]) == ALIAS
 
 
-def test_prefill_workspace_too_small(lib):
-    need = lib.gdn_prefill_workspace_bytes(1, 100, 2, 128, 128, 0)
-    if need == 0:
-        pytest.skip("no workspace needed for these sizes")
-    r = lib.gdn_prefill(P["q"], P["k"], P["v"], 0, P["g"], P["beta"], P["sin"], P["sout"],
-                        P["o"], 1, 100, 2, 128, 128, P["ws"], need - 1, None)
-    assert r == WS
-    r = lib.gdn_prefill(P["q"], P["k"], P["v"], 0, P["g"], P["beta"], P["sin"], P["sout"],
-                        P["o"], 1, 100, 2, 128, 128, None, 0, None)
-    assert r == WS
+@pytest.mark.parametrize("T,dtype", [(3000, 0), (100, 1)])
+def test_prefill_workspace_too_small(lib, T, dtype):
+    """bf16 at T = 3000, H = 2 plans several segments; fp32 always stages its
+    chunk operands: both need a workspace, and one byte less (or none) is
+    refused before any launch."""
+    need = lib.gdn_prefill_workspace_bytes(1, T, 2, 128, 128, dtype)
+    assert need > 0
+    for ws, nbytes in ((P["ws"], need - 1), (None, 0)):
+        r = lib.gdn_prefill(P["q"], P["k"], P["v"], dtype, P["g"], P["beta"], P["sin"],
+                            P["sout"], P["o"], 1, T, 2, 128, 128, ws, nbytes, None)
+        assert r == WS
+        r = lib.gdn_stream_chunk(P["q"], P["k"], P["v"], dtype, P["g"], P["beta"], P["sout"],
+                                 P["o"], 1, T, 2, 128, 128, ws, nbytes, None)
+        assert r == WS
 
 
 def test_stream_chunk_requires_state(lib):

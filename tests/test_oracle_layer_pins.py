@@ -100,3 +100,68 @@ def test_conv_qkv_shapes_and_state():
     assert q.shape == (B, T, H, d) and st.shape == (B, 3, 3, H * d)
     np.testing.assert_allclose(np.linalg.norm(q, axis=-1), 1.0, atol=1e-2)  # bf16 of unit rows
     np.testing.assert_array_equal(st[:, 2], xs[2].reshape(B, T, H * d)[:, -3:])
+
+
+def test_gate_normalises_each_row_separately():
+    """The norm is per (token, head) row: scaling one row by any positive factor
+    leaves that row's output unchanged (eps is negligible at these magnitudes),
+    and changing one row changes no other row.  A norm over the whole tensor, or
+    over the token's heads together, fails both."""
+    r = _rng(8)
+    B, T, H, dv = 2, 5, 3, 16
+    o = 1e4 * r.standard_normal((B, T, H, dv))
+    z = r.standard_normal((B, T, H, dv))
+    w = 1.0 + 0.1 * r.standard_normal(dv)
+    base = layer.gate_out(o, z, w)
+    scale = np.exp(r.uniform(-3.0, 3.0, (B, T, H, 1)))  # 0.05 .. 20, per row
+    np.testing.assert_allclose(layer.gate_out(o * scale, z, w), base, rtol=1e-9, atol=0)
+    o2 = o.copy()
+    o2[1, 2, 1] *= -7.0
+    got = layer.gate_out(o2, z, w)
+    mask = np.ones((B, T, H), bool)
+    mask[1, 2, 1] = False
+    np.testing.assert_array_equal(got[mask], base[mask])
+    # the changed row: sign flips, magnitude is unchanged
+    np.testing.assert_allclose(got[1, 2, 1], -base[1, 2, 1], rtol=1e-9)
+
+
+def test_gate_known_row_rms():
+    """A row with entries (3, 4, 0, ..., 0) over dv = 8 has mean square 25 / 8,
+    so with w = 1 and a large z (SiLU(z) = z to double precision) the output is
+    o * z / sqrt(25 / 8 + eps); rows of other heads keep their own scale."""
+    dv = 8
+    o = np.zeros((1, 1, 2, dv))
+    o[0, 0, 0, :2] = (3.0, 4.0)
+    o[0, 0, 1, :] = 0.5  # mean square 0.25
+    z = np.full_like(o, 40.0)
+    got = layer.gate_out(o, z, np.ones(dv))
+    sig = 40.0 / (1.0 + np.exp(-40.0))
+    np.testing.assert_allclose(got[0, 0, 0, :2], np.array([3.0, 4.0]) * sig / np.sqrt(25.0 / 8 + layer.EPS),
+                               rtol=1e-13)
+    np.testing.assert_allclose(got[0, 0, 1], 0.5 * sig / np.sqrt(0.25 + layer.EPS), rtol=1e-13)
+
+
+def test_conv_qkv_normalises_q_and_k_only():
+    """With l2norm on, q and k rows are unit vectors per (token, head) up to their
+    bf16 rounding, and v is the convolution output itself, rounded to bf16 and
+    not normalised (its rows are far from unit norm here).  With l2norm off, q
+    and k are the plain convolution outputs too."""
+    r = _rng(9)
+    B, T, H, d = 2, 11, 3, 8
+    xs = [5.0 * r.standard_normal((B, T, H, d)) for _ in range(3)]
+    ws = [r.standard_normal((H * d, 4)) for _ in range(3)]
+    q, k, v, _ = layer.conv_qkv(*xs, *ws)
+    for x in (q, k):
+        np.testing.assert_allclose(np.linalg.norm(x, axis=-1), 1.0, atol=2e-2)
+    plain = [layer.conv_silu(x.reshape(B, T, H * d), w)[0].reshape(B, T, H, d)
+             for x, w in zip(xs, ws)]
+    np.testing.assert_array_equal(v, layer.bf16_round(plain[2]))
+    assert np.max(np.abs(np.linalg.norm(v, axis=-1) - 1.0)) > 1.0
+    # normalised per head, not per token over all heads: each head's own row norm
+    zq = plain[0]
+    np.testing.assert_allclose(q, layer.bf16_round(zq / np.linalg.norm(zq, axis=-1, keepdims=True)),
+                               rtol=0, atol=1e-2 * np.max(np.abs(q)))
+    q0, k0, v0, _ = layer.conv_qkv(*xs, *ws, l2norm_qk=False)
+    np.testing.assert_array_equal(q0, layer.bf16_round(plain[0]))
+    np.testing.assert_array_equal(k0, layer.bf16_round(plain[1]))
+    np.testing.assert_array_equal(v0, v)
