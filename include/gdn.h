@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 /* The enums have int as their underlying type in C++ too, so that any int a C
  * caller passes (valid or not) is a value of the type; in C they are int-sized
@@ -71,7 +71,9 @@ typedef enum gdn_status GDN_ENUM_INT {
     GDN_ERR_ALIAS = 5,        /* an output overlaps an input (other than in place) */
     GDN_ERR_UNSUPPORTED = 6,  /* d not in {64, 128}, or sizes beyond 2^31 elements */
     GDN_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than required          */
-    GDN_ERR_LAUNCH = 8        /* the HIP runtime rejected a launch                */
+    GDN_ERR_LAUNCH = 8,       /* the HIP runtime rejected a launch                */
+    GDN_ERR_SCRATCH = 9       /* gdn_prefill_noalloc: the sizes need more workspace
+                                 than its static scratch holds                    */
 } gdn_status;
 
 typedef enum gdn_dtype GDN_ENUM_INT { GDN_BF16 = 0, GDN_F32 = 1 } gdn_dtype;
@@ -113,6 +115,35 @@ gdn_status gdn_prefill(const void *q, const void *k, const void *v, gdn_dtype dt
                 const float *state_in, float *state_out, float *o,
                 int B, int T, int H, int dk, int dv,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_prefill_noalloc -- gdn_prefill for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same operation and kernels, with the workspace taken
+ * from a static device array of GDN_NOALLOC_SCRATCH_BYTES instead of a caller
+ * buffer.
+ *
+ * Arguments, layouts, in-place rules and checks are those of gdn_prefill,
+ * minus the workspace.  Sizes whose gdn_prefill_workspace_bytes() exceeds
+ * GDN_NOALLOC_SCRATCH_BYTES are refused with GDN_ERR_SCRATCH before anything
+ * is enqueued (64 MiB covers the bf16 plans of any T at B * H = 16, e.g. the
+ * 8K and 256K prompts and 272-token stream calls; the fp32 path needs more
+ * from a few thousand tokens at 16 heads).  The library calls no hipMalloc,
+ * hipFree or allocating routine on this path.
+ *
+ * Each GPU holds one copy of the array (its own address, looked up once per
+ * device at the first call made with that device current, and kept until the
+ * process ends); every call on that GPU uses it.  Its contents between calls
+ * are stale and never read before being written, so nothing needs clearing.
+ * Calls that can overlap in time on one GPU (concurrent streams, host
+ * threads) race on the array: serialise them, or use gdn_prefill with
+ * separate workspaces.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status gdn_prefill_noalloc(const void *q, const void *k, const void *v, gdn_dtype dtype,
+                               const float *g, const float *beta,
+                               const float *state_in, float *state_out, float *o,
+                               int B, int T, int H, int dk, int dv, void *stream);
 
 /*
  * gdn_stream_chunk -- one call of a stream: the next T tokens of B sequences

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
     stream_chunk(q, k, v, g, beta, state)         -> o        (state in place)
     decode_step(q, k, v, g, beta, state)          -> o        (state in place)
     prefill_workspace_bytes(B, T, H, dk, dv, dtype)
+    prefill_noalloc(q, k, v, g, beta, state_in=None) -> (o, state_out)  (static scratch)
     conv_qkv(xq, xk, xv, wq, wk, wv, state=None)  -> (q, k, v, state_out)
     gate_out(o, z, w)                             -> out
     swa_prefill(q, k, v, window)                  -> o   (sliding-window attention)
@@ -31,7 +32,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["prefill", "stream_chunk", "decode_step", "prefill_workspace_bytes", "GdnError",
+__all__ = ["prefill", "prefill_noalloc", "NOALLOC_SCRATCH_BYTES", "stream_chunk", "decode_step", "prefill_workspace_bytes", "GdnError",
            "conv_qkv", "gate_out", "swa_prefill", "swa_stream_chunk", "swa_workspace_bytes",
            "swa_cache_bytes", "swa_new_cache", "backward", "backward_workspace_bytes",
            "library_path", "GDN_BF16", "GDN_F32", "set_profile_events", "profile_marks"]
@@ -41,6 +42,7 @@ _LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
 GDN_BF16 = 0
 GDN_F32 = 1
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
 
 
 class GdnError(RuntimeError):
@@ -63,6 +65,8 @@ def _load():
     lib.gdn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.gdn_prefill.restype = i
     lib.gdn_prefill.argtypes = [vp, vp, vp, i, fp, fp, fp, fp, fp, i, i, i, i, i, vp, sz, vp]
+    lib.gdn_prefill_noalloc.restype = i
+    lib.gdn_prefill_noalloc.argtypes = [vp, vp, vp, i, fp, fp, fp, fp, fp, i, i, i, i, i, vp]
     lib.gdn_stream_chunk.restype = i
     lib.gdn_stream_chunk.argtypes = [vp, vp, vp, i, fp, fp, fp, fp, i, i, i, i, i, vp, sz, vp]
     lib.gdn_decode_step.restype = i
@@ -230,6 +234,29 @@ def prefill(q, k, v, g, beta, state_in=None, *, state_out=None, o=None, workspac
                           _stream(stream, q.device))
     if st != 0:
         raise GdnError(st, "gdn_prefill")
+    return o, state_out
+
+
+def prefill_noalloc(q, k, v, g, beta, state_in=None, *, state_out=None, o=None, stream=None):
+    """prefill() through gdn_prefill_noalloc: the library's static per-GPU
+    scratch replaces the workspace (the C call allocates nothing; pass o and
+    state_out to keep this wrapper from allocating them).  Calls that overlap
+    on one GPU race on that scratch."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    code = _dtype_code(q)
+    _check_mixer(q, k, v, g, beta, ((state_in, "state_in"), (state_out, "state_out")), o,
+                 (B, T, H))
+    if o is None:
+        o = _empty((B, T, H, dv), torch.float32, q.device, stream)
+    if state_out is None:
+        state_out = _empty((B, H, dk, dv), torch.float32, q.device, stream)
+    st = _lib.gdn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), code, _ptr(g), _ptr(beta),
+                                  _ptr(state_in), _ptr(state_out), _ptr(o), B, T, H, dk, dv,
+                                  _stream(stream, q.device))
+    if st != 0:
+        raise GdnError(st, "gdn_prefill_noalloc")
     return o, state_out
 
 

@@ -5,6 +5,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gdn_launch.h"
 
 namespace {
@@ -72,6 +74,30 @@ gdn_status check_io(const void* q, const void* k, const void* v, gdn_dtype dtype
     return GDN_OK;
 }
 
+// Workspace of gdn_prefill_noalloc: one copy per GPU, at its own address on
+// each device.  In host code `scratch` names a host-side stand-in, never the
+// device memory: kernels and copies only ever get the device address looked up
+// below (per device, with that device current).
+__device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+gdn_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GDN_ERR_LAUNCH;
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return GDN_OK;
+}
+
 inline gdn_status launch_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
 
 gdn_status run_prefill(const void* q, const void* k, const void* v, gdn_dtype dtype, const float* g,
@@ -128,6 +154,7 @@ const char* gdn_status_str(gdn_status status) {
         case GDN_ERR_UNSUPPORTED: return "unsupported sizes (d must be 64 or 128)";
         case GDN_ERR_WORKSPACE: return "workspace missing or smaller than gdn_prefill_workspace_bytes()";
         case GDN_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+        case GDN_ERR_SCRATCH: return "gdn_prefill_noalloc: these sizes need more workspace than its static scratch (GDN_NOALLOC_SCRATCH_BYTES) holds";
         default: return "unknown status";
     }
 }
@@ -153,6 +180,27 @@ gdn_status gdn_prefill(const void* q, const void* k, const void* v, gdn_dtype dt
     gdn::profile_begin(static_cast<hipStream_t>(stream));
     return run_prefill(q, k, v, dtype, g, beta, state_in, state_out, o, B, T, H, dk, workspace,
                        workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_prefill_noalloc(const void* q, const void* k, const void* v, gdn_dtype dtype,
+                               const float* g, const float* beta, const float* state_in,
+                               float* state_out, float* o, int B, int T, int H, int dk, int dv,
+                               void* stream) {
+    gdn_status s = check_sizes(B, T, H, dk, dv, dtype);
+    if (s != GDN_OK) return s;
+    if (B > 65535 || H > 65535) return GDN_ERR_UNSUPPORTED;
+    const size_t need = gdn_prefill_workspace_bytes(B, T, H, dk, dv, dtype);
+    if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_SCRATCH;
+    s = check_io(q, k, v, dtype, g, beta, state_in, state_out, o, B, T, H, dk, dv, nullptr, 0);
+    if (s != GDN_OK) return s;
+    void* ws = nullptr;
+    if (need > 0) {
+        s = scratch_address(&ws);
+        if (s != GDN_OK) return s;
+    }
+    gdn::profile_begin(static_cast<hipStream_t>(stream));
+    return run_prefill(q, k, v, dtype, g, beta, state_in, state_out, o, B, T, H, dk, ws, need,
+                       static_cast<hipStream_t>(stream));
 }
 
 gdn_status gdn_stream_chunk(const void* q, const void* k, const void* v, gdn_dtype dtype, const float* g,

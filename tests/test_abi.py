@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn.h")
 LIB = os.path.join(ROOT, "linear_attention_sequence_deltanet_amd", "libgdn.so")
 
-OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, UNSUP, WS, LAUNCH = range(9)
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, UNSUP, WS, LAUNCH, SCRATCH = range(10)
 
 
 @pytest.fixture(scope="module")
@@ -51,7 +51,7 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    for s in range(9):
+    for s in range(10):
         assert lib.gdn_status_str(s) and lib.gdn_status_str(s) != b"unknown status"
     assert lib.gdn_status_str(1234) == b"unknown status"
 
@@ -118,6 +118,27 @@ def test_prefill_workspace_too_small(lib, T, dtype):
         r = lib.gdn_stream_chunk(P["q"], P["k"], P["v"], dtype, P["g"], P["beta"], P["sout"],
                                  P["o"], 1, T, 2, 128, 128, ws, nbytes, None)
         assert r == WS
+
+
+def test_noalloc_limit_matches_header_and_rejects_large_plans(lib):
+    """gdn_prefill_noalloc refuses sizes whose workspace exceeds its static
+    scratch (fp32 at T = 8192, 16 heads: 338 MiB) on the host, before any HIP
+    call; sizes that fit pass to the pointer checks (here: a NULL q)."""
+    import linear_attention_sequence_deltanet_amd as gdn
+    m = re.search(r"#define\s+GDN_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    limit = int(m.group(1)) << int(m.group(2))
+    assert limit == gdn.NOALLOC_SCRATCH_BYTES
+    assert lib.gdn_prefill_workspace_bytes(1, 8192, 16, 128, 128, 1) > limit
+    r = lib.gdn_prefill_noalloc(P["q"], P["k"], P["v"], 1, P["g"], P["beta"], P["sin"],
+                                P["sout"], P["o"], 1, 8192, 16, 128, 128, None)
+    assert r == SCRATCH
+    # the bf16 plans of the benchmark shapes fit
+    for T in (272, 8192, 262144):
+        assert 0 < lib.gdn_prefill_workspace_bytes(1, T, 16, 128, 128, 0) <= limit
+    r = lib.gdn_prefill_noalloc(None, P["k"], P["v"], 0, P["g"], P["beta"], P["sin"],
+                                P["sout"], P["o"], 1, 8192, 16, 128, 128, None)
+    assert r == NULL
 
 
 def test_stream_chunk_requires_state(lib):
