@@ -618,12 +618,16 @@ __global__ __launch_bounds__(256) void chunk_chain(const void* ws, SegWs sw,
 
 // ---------------------------------------------------------------------------
 // seg_combine: grid B*H*(D/16) workgroups of D/16 waves (wave w: key tile w of
-// one 16-column slice), sequential over the segments.  H_s = M_s H_{s-1} + R_s
-// with the state split into fp16 high and low parts.  LO: M's low part is
-// applied too (three products, fp32-grade, for fp32 inputs); otherwise M's
-// fp16 high part only (two products: the bf16-input chain that wrote M already
-// rounds its state operands to fp16 every chunk).  Stores each segment's start
-// state and the final state.
+// one 16-column slice), sequential over the segments: H_s = M_s H_{s-1} + R_s.
+// Stores each segment's start state and (direct = 0) the final state.
+//   LO (fp32 inputs; chunk_chain reads the start states): the state split
+//      into fp16 high and low parts times M's high and low parts, three
+//      products, fp32-grade; start states row-major [key][column].
+//   otherwise (bf16 inputs; gdn_fused reads them): M's high part times the
+//      state rounded to fp16 -- the rounding of the state operand that the
+//      chain which wrote M applies every chunk; start states in fragment
+//      order, the 16x16 C-layout tile (key tile m, column tile n) at float
+//      offset ((n D/16 + m) 64 + lane) 4, one 16-byte store per lane.
 // ---------------------------------------------------------------------------
 template <int D, bool LO>
 __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const float* state_in,
@@ -632,9 +636,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
     using M = Mfma<_Float16>;
     using F8 = M::frag8;
     constexpr int NS = D / 16, LS = D + 8;
-    constexpr int NB = 2;  // segments whose summaries are in flight
+    constexpr int NB = 2;  // segments whose summaries are in flight (deeper measured slower)
     // fp16 high / low parts of the chained state slice, [col][key], double-buffered
-    __shared__ __align__(16) _Float16 sHi[2][16 * LS], sLo[2][16 * LS];
+    __shared__ __align__(16) _Float16 sHi[2][16 * LS], sLo[LO ? 2 : 1][LO ? 16 * LS : 8];
 
     // workgroup = (head, 16-column slice); the slices of one head share an XCD
     const int L = blockIdx.x;
@@ -662,8 +666,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
     const int s0 = direct ? 1 : 0, s1 = direct ? S - 1 : S;
     auto store_start = [&](int s) {
         float* dst = sw.sst + ((long)s * BH + bh) * D * D;
+        if constexpr (LO) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(16 * wave + 4 * lg + e) * D + col] = hs[e];
+            for (int e = 0; e < 4; ++e) dst[(16 * wave + 4 * lg + e) * D + col] = hs[e];
+        } else {
+            *reinterpret_cast<f32x4*>(dst + ((slice * (D / 16) + wave) * 64 + lane) * 4) = hs;
+        }
     };
 
     // Summaries do not depend on the chained state: those of the next NB
@@ -700,7 +708,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
         // alternate, so one barrier per segment suffices: a buffer is rewritten
         // two segments later, after every wave passed the next barrier.
         _Float16* bh_ = sHi[s & 1];
-        _Float16* bl_ = sLo[s & 1];
+        _Float16* bl_ = sLo[LO ? s & 1 : 0];
         typename M::frag4 hi;
         f32x4 lo;
 #pragma unroll
@@ -709,21 +717,28 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
             lo[e] = hs[e] - static_cast<float>(hi[e]);
         }
         st4<_Float16>(&bh_[lc * LS + 16 * wave + 4 * lg], hi);
-        st4<_Float16>(&bl_[lc * LS + 16 * wave + 4 * lg], cvt4<_Float16>(lo));
+        if constexpr (LO) st4<_Float16>(&bl_[lc * LS + 16 * wave + 4 * lg], cvt4<_Float16>(lo));
         lds_sync();
         F8 bhi[D / 32], blo[D / 32];
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             bhi[kk] = ld8<_Float16>(&bh_[lc * LS + 32 * kk + 8 * lg]);
-            blo[kk] = ld8<_Float16>(&bl_[lc * LS + 32 * kk + 8 * lg]);
+            if constexpr (LO) blo[kk] = ld8<_Float16>(&bl_[lc * LS + 32 * kk + 8 * lg]);
         }
         const float* nsm = sum_of(next);
-        f32x4 a0 = zero4(), a1 = zero4(), a2 = zero4();  // independent chains
+        // independent chains: LO the three products, otherwise even and odd kk
+        f32x4 a0 = zero4(), a1 = zero4(), a2 = zero4();
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
-            a0 = M::k32(p.hi[kk], bhi[kk], a0);
-            a1 = M::k32(p.hi[kk], blo[kk], a1);
-            if constexpr (LO) a2 = M::k32(p.lo[kk], bhi[kk], a2);
+            if constexpr (LO) {
+                a0 = M::k32(p.hi[kk], bhi[kk], a0);
+                a1 = M::k32(p.hi[kk], blo[kk], a1);
+                a2 = M::k32(p.lo[kk], bhi[kk], a2);
+            } else if (kk & 1) {
+                a1 = M::k32(p.hi[kk], bhi[kk], a1);
+            } else {
+                a0 = M::k32(p.hi[kk], bhi[kk], a0);
+            }
             load_m(p, nsm, kk);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -762,6 +777,112 @@ __global__ __launch_bounds__(64 * (D / 16)) void seg_combine(SegWs sw, const flo
         for (int e = 0; e < 4; ++e)
             state_out[((long)bh * D + 16 * wave + 4 * lg + e) * D + col] = hs[e];
     }
+}
+
+// ---------------------------------------------------------------------------
+// map_chain: the per-chunk maps of the fused MAP pass applied in order from
+// state_in, each chunk's output on the way:
+//     O_c = P U + (diag(Gam) Q - P W) H_c ,
+//     H_{c+1} = Gam_C H_c + N_c H_c + R_c ,   N_c = -K~^T W .
+// Grid B*H*(D/16) workgroups of D/16 waves, workgroup = (head, 16-column
+// slice); wave w: key tile w of the state slice and, for w < 4, token tile w
+// of the chunk's output slice.  Both products take the state rounded to fp16
+// once per chunk, as the fused output pass does; the decay Gam_C multiplies
+// the fp32 state.  The chunks' operands do not
+// depend on the state: those of the next two chunks are loaded while the
+// current one is applied.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64 * (D / 16)) void map_chain(MapWs mw, const float* state_in,
+                                                         float* state_out, float* o, int T,
+                                                         int H, int BH, int NC) {
+    using M = Mfma<_Float16>;
+    using F8 = M::frag8;
+    constexpr int NS = D / 16, LS = D + 8, KB = D / 32;
+    __shared__ __align__(16) _Float16 sHi[2][16 * LS];  // fp16 state slice [col][key], by chunk parity
+
+    const int L = blockIdx.x;
+    int bh, slice;
+    if (BH % 8 == 0) {  // the slices of one head on one XCD
+        bh = (L % 8) + 8 * ((L / 8) / NS);
+        slice = (L / 8) % NS;
+    } else {
+        bh = L / NS;
+        slice = L % NS;
+    }
+    const int b = bh / H, h = bh % H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lg = lane >> 4, lc = lane & 15;
+    const int col = slice * 16 + lc;
+    const bool outw = wave < 4;  // wave-uniform
+
+    f32x4 hs;  // state tile (C layout): keys 16 wave + 4 lg + e, column col
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        hs[e] = state_in ? state_in[((long)bh * D + 16 * wave + 4 * lg + e) * D + col] : 0.f;
+
+    struct Pre {
+        F8 m[KB], qa[KB];  // rows of N and of diag(Gam) Q - P W (A operands)
+        f32x4 r, oi;       // R and P U (C layout)
+        float gc;          // Gam_C
+    };
+    auto blk = [&](int c) { return (long)min(c, NC - 1) * BH + bh; };  // past the end: re-read the last
+    auto load_ro = [&](Pre& p, int c) {
+        const float* sm = mw.summ + blk(c) * D * 2 * D;
+        p.r = *reinterpret_cast<const f32x4*>(sm + ((slice * NS + wave) * 64 + lane) * 4);
+        p.gc = sm[D * D + D * D / 2];
+        if (outw) p.oi = *reinterpret_cast<const f32x4*>(mw.oin + blk(c) * 64 * D + ((slice * 4 + wave) * 64 + lane) * 4);
+    };
+    auto load_mq = [&](Pre& p, int c, int kk) {
+        const _Float16* mh = reinterpret_cast<const _Float16*>(mw.summ + blk(c) * D * 2 * D + D * D);
+        p.m[kk] = *reinterpret_cast<const F8*>(mh + ((wave * KB + kk) * 64 + lane) * 8);
+        if (outw) p.qa[kk] = *reinterpret_cast<const F8*>(mw.qpr + blk(c) * 64 * D + ((wave * KB + kk) * 64 + lane) * 8);
+    };
+    auto load = [&](Pre& p, int c) {
+        load_ro(p, c);
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) load_mq(p, c, kk);
+    };
+    auto apply = [&](Pre& p, int c, int next) {
+        _Float16* sh = sHi[c & 1];  // rewritten two chunks later, past the next barrier
+        st4<_Float16>(&sh[lc * LS + 16 * wave + 4 * lg], cvt4<_Float16>(hs));
+        lds_sync();
+        F8 bhi[KB];
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) bhi[kk] = ld8<_Float16>(&sh[lc * LS + 32 * kk + 8 * lg]);
+        f32x4 a0 = zero4(), a1 = zero4(), ao = zero4();
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+            if (kk & 1) a1 = M::k32(p.m[kk], bhi[kk], a1);
+            else a0 = M::k32(p.m[kk], bhi[kk], a0);
+            if (outw) ao = M::k32(p.qa[kk], bhi[kk], ao);
+            load_mq(p, next, kk);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (outw) {
+            ao += p.oi;
+            const int t0 = c * 64 + 16 * wave + 4 * lg;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (t0 + e < T) o[(((long)b * T + t0 + e) * H + h) * D + col] = ao[e];
+        }
+        hs = p.gc * hs + (p.r + (a0 + a1));
+        load_ro(p, next);
+    };
+
+    constexpr int NB = 2;
+    Pre pb[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) load(pb[i], i);
+    int c = 0;
+    for (; c + NB <= NC; c += NB) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) apply(pb[i], c + i, c + i + NB);
+    }
+    if (c < NC) apply(pb[0], c, NC - 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) state_out[((long)bh * D + 16 * wave + 4 * lg + e) * D + col] = hs[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -867,6 +988,20 @@ hipError_t launch_seg_combine(float* summ, float* sst, const float* state_in, fl
             hipLaunchKernelGGL((seg_combine<128, false>), grid, block, 0, stream, sw, state_in,
                                state_out, BH, S, direct);
     }
+    profile_mark(stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_map_chain(MapWs mw, const float* state_in, float* state_out, float* o, int B,
+                            int T, int H, int D, int NC, hipStream_t stream) {
+    const int BH = B * H;
+    const dim3 grid((unsigned)(BH * (D / 16))), block(64 * (D / 16));
+    if (D == 64)
+        hipLaunchKernelGGL((map_chain<64>), grid, block, 0, stream, mw, state_in, state_out, o, T,
+                           H, BH, NC);
+    else
+        hipLaunchKernelGGL((map_chain<128>), grid, block, 0, stream, mw, state_in, state_out, o, T,
+                           H, BH, NC);
     profile_mark(stream);
     return hipGetLastError();
 }

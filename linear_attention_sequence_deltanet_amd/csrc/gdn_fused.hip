@@ -27,6 +27,15 @@
 //             ([state_in | I] for the first segment) and stores the segment's
 //             affine map [R | M] (H_end = M H_start + R); the last segment has
 //             none.
+//   MAP mode: one chunk per workgroup with Delta = [U | -W] (the start
+//             [0 | I]): stores the chunk's map H_C = Gam_C H0 + N H0 + R as
+//             R = K~^T U, N = -K~^T W (K~ = diag(e) K) and Gam_C -- the decay
+//             stays an exact fp32 factor, out of the fp16 operand N -- and, from
+//             the output products on the same columns, P U and
+//             diag(Gam) Q - P W, so that the chunk's output is
+//             O = P U + (diag(Gam) Q - P W) H0 for any start state H0.  The
+//             chain over the chunks then runs in map_chain (gdn_chunk.hip); no
+//             output pass follows.
 //
 // Matrix-core products of two inputs (the Gram tiles, the identity products
 // that transpose K and V) take the bf16 inputs as stored; every product with a
@@ -139,8 +148,12 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 
 struct FusedSeg {
     float* summ;   // [S][BH] segment summaries of 8 D^2 bytes (SUM writes, combine reads)
-    float* sst;    // [S][BH][D][D]   start state per segment (combine writes, OUT reads)
+    float* sst;    // [S][BH][D^2]    start state per segment, fragment order (combine writes, OUT reads)
+    float* oin;    // MAP: [NC][BH][64 D] P U, fragment order (token tile m, column tile n)
+    _Float16* qpr; // MAP: [NC][BH][64 D] diag(Gam) Q - P W, A-operand order
 };
+
+enum FusedMode { kSum = 0, kOut = 1, kMap = 2 };
 
 // Per-chunk gate factors in LDS (gam = within-chunk cumsum of g):
 // gam, beta, Gam = exp(gam), E = exp(gam_C - gam), BG = beta Gam; the
@@ -187,12 +200,14 @@ __device__ __forceinline__ void gram_tiles(const uint16_t* sK, const uint16_t* c
     }
 }
 
-template <int D, bool OUT>
+template <int D, int MODE>
 __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, FusedSeg fs,
     const float* state_in, float* state_out, float* __restrict__ o, int T, int H, int B, int NC,
     int G, int S) {
+    constexpr bool OUT = MODE == kOut, MAP = MODE == kMap;
+    constexpr bool QK = OUT || MAP;       // Q staged, Q K^T tiles and output products
     constexpr int NW = D / 16, NTH = 64 * NW;  // wave w owns column tile w
     constexpr int TPW = OUT ? 1 : 2;      // state tiles per wave: value tile w (+ identity tile w)
     constexpr int MT = D / 16;            // key tiles of the state
@@ -213,13 +228,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     // inputs right after its part of the state update, while others may still
     // read the current chunk's Q there
     __shared__ __align__(16) _Float16 sQ[OUT ? 2 * FC * LDF : 8];
-    __shared__ __align__(16) uint16_t sQb[OUT ? FC * LDF : 8];   // raw bf16 (Q K^T)
+    __shared__ __align__(16) uint16_t sQb[QK ? FC * LDF : 8];    // raw bf16 (Q K^T)
     __shared__ __align__(16) _Float16 sW[FC * LDF];      // -W [t][key]
     __shared__ __align__(16) uint16_t sV[FC * LDV];             // raw bf16
     __shared__ __align__(16) _Float16 sKT[D * LAF];      // (diag(e) K)^T [key][t]
     __shared__ __align__(16) _Float16 sA[FC * LAA];      // -A off-diagonal, (T_bb - I) diagonal blocks
-    __shared__ __align__(16) _Float16 sP[OUT ? FC * LAA : 8];
-    __shared__ __align__(16) _Float16 sStg[OUT ? 8 : NW * D * 16];  // SUM: summary transpose
+    __shared__ __align__(16) _Float16 sP[QK ? FC * LAA : 8];
+    __shared__ __align__(16) _Float16 sStg[OUT ? 8 : NW * D * 16];  // SUM, MAP: transposes to A-operand order
     // gates of chunk c in sG[c & 1]: wave 0 forms the next chunk's at the end
     // of its part of the state update, while the other waves still read the
     // current chunk's
@@ -240,30 +255,36 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     // The last segment needs no summary (its output pass writes the final
     // state), and the first segment's summary pass starts from the true initial
     // state, so that its R is already the second segment's start state.
-    if (!OUT && seg == S - 1) return;
+    if (MODE == kSum && seg == S - 1) return;
 
     // ---- state tiles (fp32, C layout): key 16 m + 4 lg + e, column colw + 16 j + lc
     f32x4 hs[TPW][MT];
     {
         const float* src = nullptr;
-        if (OUT) src = S == 1 ? (state_in ? state_in + (long)bh * D * D : nullptr)
-                              : fs.sst + ((long)seg * BH + bh) * D * D;
-        else if (seg == 0 && state_in) src = state_in + (long)bh * D * D;
+        if (OUT && S == 1) src = state_in ? state_in + (long)bh * D * D : nullptr;
+        else if (MODE == kSum && seg == 0 && state_in) src = state_in + (long)bh * D * D;
+        if (OUT && S > 1) {
+            // start state from the combine, in fragment order: tile (m, wave)
+            const float* st = fs.sst + ((long)seg * BH + bh) * D * D + (wave * MT * 64 + lane) * 4;
 #pragma unroll
-        for (int j = 0; j < TPW; ++j)
+            for (int m = 0; m < MT; ++m) hs[0][m] = *reinterpret_cast<const f32x4*>(st + m * 256);
+        } else {
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
+            for (int j = 0; j < TPW; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int key = 16 * m + 4 * lg + e, col = colw + lc;
-                    float x = 0.f;
-                    if (j == 0) {
-                        if (src) x = src[key * D + col];
-                    } else {
-                        x = key == col ? 1.f : 0.f;  // identity columns (summary pass)
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = 16 * m + 4 * lg + e, col = colw + lc;
+                        float x = 0.f;
+                        if (j == 0) {
+                            if (src) x = src[key * D + col];
+                        } else if (!MAP) {
+                            x = key == col ? 1.f : 0.f;  // identity columns (summary pass)
+                        }
+                        hs[j][m][e] = x;
                     }
-                    hs[j][m][e] = x;
-                }
+        }
     }
 
     // ---- raw input prefetch (one chunk ahead).  Rows past the end of the
@@ -300,7 +321,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         }
     };
     auto issue_loads = [&](int c) {
-        if (OUT) issue(rq, q, c);
+        if (QK) issue(rq, q, c);
         issue(rk, k, c);
         issue(rv, v, c);
         issue_gates(c);
@@ -319,8 +340,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 const H8 qh = bf16x8_to_f16(rq[i]);
                 st4<_Float16>(&q16[r * LDF + kperm(c8)], __builtin_shufflevector(qh, qh, 0, 1, 2, 3));
                 st4<_Float16>(&q16[r * LDF + kperm(c8 + 4)], __builtin_shufflevector(qh, qh, 4, 5, 6, 7));
-                *reinterpret_cast<uint4*>(&sQb[r * LDF + c8]) = rq[i];
             }
+            if (QK) *reinterpret_cast<uint4*>(&sQb[r * LDF + c8]) = rq[i];
             *reinterpret_cast<uint4*>(&sV[r * LDV + c8]) = rv[i];
         }
     };
@@ -396,11 +417,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             const f32x4 br = *reinterpret_cast<const f32x4*>(&gt.beta[16 * bb + 4 * lg]);
             const float gi = gt.gam[16 * bb + lc], bi = gt.beta[16 * bb + lc];
             // G = K_b K_b^T (symmetric) and, for OUT, K_b Q_b^T
-            f32x4 cc[OUT ? 2 : 1];
+            f32x4 cc[QK ? 2 : 1];
             {
                 const uint16_t* X[2] = {sK, sQb};
                 const int mi[2] = {bb, bb}, ni[2] = {bb, bb};
-                gram_tiles<OUT ? 2 : 1, D, LDF>(sK, X, mi, ni, lg, lc, cc);
+                gram_tiles<QK ? 2 : 1, D, LDF>(sK, X, mi, ni, lg, lc, cc);
             }
             const f32x4 acc = cc[0];
             // A_bb and its transpose in accumulator layout (row 4 lg + e, column
@@ -423,13 +444,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             // the rounded factors are as accurate as that.
             const H4 hx = cvt4<_Float16>(ax), hxt = cvt4<_Float16>(at);
             const f32x4 a2 = MF::k16(hxt, hx, zero4()), a2t = MF::k16(hx, hxt, zero4());
-            if (OUT) {
+            if (QK) {
                 // diagonal Q K^T tile: P[r][i] = exp(gam_r - gam_i) q_r.k_i for i <= r
                 // (independent of the inverse; fills its latencies)
                 f32x4 val;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    val[e] = 4 * lg + e <= lc ? __expf(fminf(gi - gr[e], 0.f)) * cc[OUT ? 1 : 0][e] : 0.f;
+                    val[e] = 4 * lg + e <= lc ? __expf(fminf(gi - gr[e], 0.f)) * cc[QK ? 1 : 0][e] : 0.f;
                 st4<_Float16>(&sP[(16 * bb + lc) * LAA + kperm(16 * bb + 4 * lg)], cvt4<_Float16>(val));
             }
             const H4 h2 = cvt4<_Float16>(a2), h2t = cvt4<_Float16>(a2t);
@@ -454,7 +475,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 off_coords(wave - 4, mi[0], ni[0]);
                 X[0] = sK, kq[0] = true;
                 const bool third_kk = wave < 6;
-                if (OUT) {
+                if (QK) {
                     off_coords(wave - 4, mi[1], ni[1]);
                     X[1] = sQb, kq[1] = false;
                     off_coords(third_kk ? wave : wave - 2, mi[2], ni[2]);
@@ -464,12 +485,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                     X[1] = sK, kq[1] = true;
                     mi[2] = mi[1], ni[2] = ni[1], X[2] = sK, kq[2] = true;
                 }
-                const int ntl = OUT ? 3 : third_kk ? 2 : 1;
+                const int ntl = QK ? 3 : third_kk ? 2 : 1;
                 f32x4 cf[3], cc[3];
                 float sc[3];
 #pragma unroll
                 for (int t = 0; t < 3; ++t) off_factors(kq[t], mi[t], ni[t], cf[t], sc[t]);
-                if (OUT) gram_tiles<3, D, LDF>(sK, X, mi, ni, lg, lc, cc);
+                if (QK) gram_tiles<3, D, LDF>(sK, X, mi, ni, lg, lc, cc);
                 else if (third_kk) gram_tiles<2, D, LDF>(sK, X, mi, ni, lg, lc, cc);
                 else gram_tiles<1, D, LDF>(sK, X, mi, ni, lg, lc, cc);
 #pragma unroll
@@ -479,7 +500,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         } else {
             // generic: the off-diagonal K K^T and (OUT) Q K^T tiles, dealt to
             // the waves in turn
-            constexpr int NREAL = OUT ? 12 : 6;
+            constexpr int NREAL = QK ? 12 : 6;
             for (int tt = wave; tt < NREAL; tt += NW) {
                 int mi, ni;
                 off_coords(tt % 6, mi, ni);
@@ -493,7 +514,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             }
         }
         // the two upper P tiles that the output products read, (0,1) and (2,3)
-        if (OUT && wave >= NW - 2) {
+        if (QK && wave >= NW - 2) {
             const int z = wave - (NW - 2);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -502,7 +523,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         lds_sync();
         if (more) {
             issue(rv, v, c + 1);
-            if (OUT) issue(rq, q, c + 1);
+            if (QK) issue(rq, q, c + 1);
         }
 
         // ---- blocked solve with the right-hand side in fp32:
@@ -583,6 +604,20 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         // tiles' accumulators form independent chains on the matrix cores; the
         // A fragments of step kk + 1 are read while step kk multiplies.
         constexpr int NQ = OUT ? 4 : 1;
+        f32x4 dl[TPW][4], oq[NQ];
+        H8 fp[QK ? 6 : 1];  // P fragments: row tiles 0..3 (tokens 0-31), 2, 3 (tokens 32-63)
+        auto load_p = [&] {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fp[i] = ld8<_Float16>(&sP[(16 * i + lc) * LAA + 8 * lg]);
+            fp[4] = ld8<_Float16>(&sP[(32 + lc) * LAA + 32 + 8 * lg]);
+            fp[5] = ld8<_Float16>(&sP[(48 + lc) * LAA + 32 + 8 * lg]);
+        };
+        if constexpr (MAP) {
+            // start [0 | I]: Delta = [U | -W], the solve's right-hand sides
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) dl[0][mt] = res[0][mt], dl[1][mt] = res[1][mt];
+            load_p();
+        } else {
         H8 fw[2][4], fq[2][NQ];
         auto load_step = [&](int kk) {
 #pragma unroll
@@ -597,23 +632,18 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
             for (int j = 0; j < TPW; ++j) bs[kk][j] = acc_to_b32(hs[j][2 * kk], hs[j][2 * kk + 1]);
-        f32x4 dl[TPW][4], oq[NQ];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
             for (int j = 0; j < TPW; ++j) dl[j][mt] = u[j][mt];
             if (OUT) oq[mt] = zero4();
         }
-        H8 fp[OUT ? 6 : 1];  // P fragments: row tiles 0..3 (tokens 0-31), 2, 3 (tokens 32-63)
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
             if (kk + 1 < D / 32) {
                 load_step(kk + 1);
             } else if (OUT) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) fp[i] = ld8<_Float16>(&sP[(16 * i + lc) * LAA + 8 * lg]);
-                fp[4] = ld8<_Float16>(&sP[(32 + lc) * LAA + 32 + 8 * lg]);
-                fp[5] = ld8<_Float16>(&sP[(48 + lc) * LAA + 32 + 8 * lg]);
+                load_p();
             }
             __builtin_amdgcn_sched_barrier(0);  // the reads above go out before this step's products
 #pragma unroll
@@ -624,6 +654,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        }  // !MAP
         // (diag(e) K)^T fragments of the first half of the key tiles
         H8 fk[MT][2];
         auto load_kt = [&](int m) {
@@ -637,6 +668,54 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         for (int j = 0; j < TPW; ++j) {
             db[0][j] = acc_to_b32(dl[j][0], dl[j][1]);
             db[1][j] = acc_to_b32(dl[j][2], dl[j][3]);
+        }
+        if constexpr (MAP) {
+            // From [0 | I]: P U on the value columns and diag(Gam) Q_w - P W_w on
+            // the identity columns (Q_w, W_w: key columns colw.. of Q and W;
+            // the Q tile reaches the accumulator layout through a product with
+            // the 16x16 identity, exactly)
+            B4 ident;  // bf16 1.0 = 0x3f80
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ident[e] = (short)(4 * lg + e == lc ? 0x3f80 : 0);
+            f32x4 om[2][4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(&gt.Gam[16 * mt + 4 * lg]);
+                const f32x4 qt = mfma_b16(ldb4(&sQb[(16 * mt + lc) * LDF + colw + 4 * lg]), ident, zero4());
+                om[0][mt] = MF::k32(fp[mt], db[0][0], zero4());
+                om[1][mt] = MF::k32(fp[mt], db[0][1], gm * qt);
+            }
+#pragma unroll
+            for (int mt = 2; mt < 4; ++mt)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) om[j][mt] = MF::k32(fp[2 + mt], db[1][j], om[j][mt]);
+            const long blk = (long)seg * BH + bh;
+            // Gam_C in the summary block's float D^2 + D^2 / 2 (the slot of M's
+            // unused fp16 low part)
+            if (tid == 0) fs.summ[blk * D * 2 * D + D * D + D * D / 2] = gt.GC;
+            float* oi = fs.oin + blk * FC * D;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                *reinterpret_cast<f32x4*>(oi + ((wave * 4 + mt) * 64 + lane) * 4) = om[0][mt];
+            // diag(Gam) Q - P W to A-operand slots, through this wave's staging
+            // area as [token][16 key columns] (the summary's transpose below,
+            // with 64 rows)
+            _Float16* st = sStg + wave * D * 16;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    st[(16 * mt + 4 * lg + e) * 16 + lc] = static_cast<_Float16>(om[1][mt][e]);
+            lds_sync();
+            _Float16* qp = fs.qpr + blk * FC * D;
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                const int slot = it * 64 + lane;
+                const int m = slot >> 5, half = (slot >> 4) & 1, row = slot & 15;
+                const int lane_f = (2 * (wave & 1) + half) * 16 + row;
+                *reinterpret_cast<H8*>(qp + ((m * (D / 32) + (wave >> 1)) * 64 + lane_f) * 8) =
+                    *reinterpret_cast<const H8*>(&st[(16 * m + row) * 16 + 8 * half]);
+            }
         }
         if (OUT) {
             // O = diag(Gam) Q H0 + P Delta (the first products of all row tiles,
@@ -742,6 +821,7 @@ namespace {
 
 struct FPlan {
     int NC, S, G;
+    bool map;  // MAP pass + map_chain (S = NC segments of one chunk)
 };
 
 // Segmentation by a cost model of the three kernels on the 256 CUs of an
@@ -751,15 +831,23 @@ struct FPlan {
 // its D/16 workgroups per head, and the two extra launches about 5 us together.  One
 // segment runs the output pass alone.  Candidates: G = 1..32 chunks per segment
 // and the G that fill k rounds of workgroups exactly.
-FPlan fused_plan(int B, int T, int H) {
+// The map plan (short sequences): the MAP pass, about kMap us per round of its
+// chunk x head workgroups, then map_chain, about kStep us per chunk per round
+// of its D/16 workgroups per head, one extra launch.  Its workspace (the chunk
+// maps, 8 D^2 + 384 D bytes per chunk x head) is held to kMapBytes.
+constexpr double kMapBytes = 64.0 * 1024 * 1024;
+static double map_bytes(int NC, long BH, int D) { return (double)NC * BH * (8.0 * D * D + 384.0 * D); }
+
+FPlan fused_plan(int B, int T, int H, int D) {
     constexpr long kCUs = 256;
-    constexpr double kOut = 6.5, kSum = 5.7, kComb = 1.2, kLaunch = 5.0;
+    constexpr double kOut = 6.5, kSum = 5.7, kComb = 1.2, kLaunch = 5.0, kMap = 7.0, kStep = 0.8;
     FPlan p;
     p.NC = (T + FC - 1) / FC;
     const long BH = (long)B * H;
     auto rounds = [](long wgs) { return (double)((wgs + kCUs - 1) / kCUs); };
     p.S = 1;
     p.G = p.NC;
+    p.map = false;
     double best = p.NC * kOut * rounds(BH);
     auto consider = [&](long G) {
         if (G < 1 || G >= p.NC) return;
@@ -772,13 +860,18 @@ FPlan fused_plan(int B, int T, int H) {
         const long segs = k * kCUs / BH;  // segments per head that fill k rounds
         if (segs >= 2) consider((p.NC + segs - 1) / segs);
     }
+    if (p.NC >= 2 && map_bytes(p.NC, BH, D) <= kMapBytes) {
+        const double t = kMap * rounds(p.NC * BH) + p.NC * kStep * rounds(BH * (D / 16)) + kLaunch / 2;
+        if (t < best) best = t, p.map = true, p.S = p.NC, p.G = 1;
+    }
     return p;
 }
 
 }  // namespace
 
 size_t fused_workspace_bytes(int B, int T, int H, int D) {
-    const FPlan p = fused_plan(B, T, H);
+    const FPlan p = fused_plan(B, T, H, D);
+    if (p.map) return (size_t)map_bytes(p.NC, (long)B * H, D);
     // segment summaries (2 D^2 floats) and start states (D^2 floats)
     return p.S > 1 ? (size_t)p.S * B * H * D * D * 4 * 3 : 0;
 }
@@ -787,29 +880,40 @@ template <int D>
 static hipError_t launch_fused_t(const void* q, const void* k, const void* v, const float* g,
                                  const float* beta, const float* state_in, float* state_out,
                                  float* o, int B, int T, int H, void* ws, hipStream_t stream) {
-    const FPlan p = fused_plan(B, T, H);
+    const FPlan p = fused_plan(B, T, H, D);
     const long BH = (long)B * H;
     FusedSeg fs;
     fs.summ = static_cast<float*>(ws);
     fs.sst = fs.summ + (size_t)p.S * BH * D * 2 * D;
+    fs.oin = fs.sst;  // map plan: [NC][BH][64 D] f32, then [NC][BH][64 D] f16
+    fs.qpr = reinterpret_cast<_Float16*>(fs.oin + (size_t)p.NC * BH * FC * D);
     const bf16_t* qq = static_cast<const bf16_t*>(q);
     const bf16_t* kk = static_cast<const bf16_t*>(k);
     const bf16_t* vv = static_cast<const bf16_t*>(v);
     const dim3 block(64 * (D / 16));
+    if (p.map) {
+        hipLaunchKernelGGL((gdn_fused<D, kMap>), dim3((unsigned)(BH * p.NC)), block, 0, stream, qq,
+                           kk, vv, g, beta, fs, nullptr, nullptr, o, T, H, B, p.NC, 1, p.NC);
+        profile_mark(stream);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_map_chain(MapWs{fs.summ, fs.oin, fs.qpr}, state_in, state_out, o, B, T, H, D,
+                                p.NC, stream);
+    }
     if (p.S == 1) {
-        hipLaunchKernelGGL((gdn_fused<D, true>), dim3((unsigned)BH), block, 0, stream, qq, kk, vv, g,
+        hipLaunchKernelGGL((gdn_fused<D, kOut>), dim3((unsigned)BH), block, 0, stream, qq, kk, vv, g,
                            beta, fs, state_in, state_out, o, T, H, B, p.NC, p.G, 1);
         profile_mark(stream);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((gdn_fused<D, false>), dim3((unsigned)(BH * p.S)), block, 0, stream, qq, kk,
+    hipLaunchKernelGGL((gdn_fused<D, kSum>), dim3((unsigned)(BH * p.S)), block, 0, stream, qq, kk,
                        vv, g, beta, fs, state_in, state_out, o, T, H, B, p.NC, p.G, p.S);
     profile_mark(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_seg_combine(fs.summ, fs.sst, state_in, state_out, (int)BH, p.S, D, 1, 0, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gdn_fused<D, true>), dim3((unsigned)(BH * p.S)), block, 0, stream, qq, kk,
+    hipLaunchKernelGGL((gdn_fused<D, kOut>), dim3((unsigned)(BH * p.S)), block, 0, stream, qq, kk,
                        vv, g, beta, fs, state_in, state_out, o, T, H, B, p.NC, p.G, p.S);
     profile_mark(stream);
     return hipGetLastError();

@@ -28,13 +28,29 @@ hipError_t launch_chunked(const void* q, const void* k, const void* v, const flo
 
 // Sequential combine of per-segment affine maps ([S][BH] summaries of 8 D^2
 // bytes each, laid out as summary_store() writes them): writes every segment's
-// start state to sst ([S][BH][D][D] f32).  direct = 0: every segment has a
-// summary from a zero start; the final state goes to state_out.  direct = 1:
-// segment 0's R is already segment 1's start state, the last segment has no
-// summary, and state_out is left to the last segment's output pass.  m_lo = 1
-// applies M's fp16 low part too (fp32 inputs); 0 its high part only.
+// start state to sst ([S][BH] blocks of D^2 f32).  direct = 0: every segment
+// has a summary from a zero start; the final state goes to state_out.
+// direct = 1: segment 0's R is already segment 1's start state, the last
+// segment has no summary, and state_out is left to the last segment's output
+// pass.  m_lo = 1 (fp32 inputs): fp32-grade products, start states row-major;
+// 0 (bf16 inputs): M's fp16 high part times the fp16-rounded state, start
+// states in MFMA fragment order (the layout gdn_fused reads).
 hipError_t launch_seg_combine(float* summ, float* sst, const float* state_in, float* state_out,
                               int BH, int S, int D, int direct, int m_lo, hipStream_t stream);
+
+// Per-chunk maps of the fused MAP pass ([NC][BH] blocks): summ as
+// summary_store() lays out [R | M], with N = M - Gam_C I in M's place and
+// Gam_C at float D^2 + D^2/2 of the block; oin = P U (64 x D f32, fragment
+// order); qpr = diag(Gam) Q - P W (64 x D f16, A-operand order).
+struct MapWs {
+    const float* summ;
+    const float* oin;
+    const _Float16* qpr;
+};
+// Applies the NC chunk maps in order from state_in (null: zeros), writing every
+// chunk's output rows (< T) to o and the final state to state_out.
+hipError_t launch_map_chain(MapWs mw, const float* state_in, float* state_out, float* o, int B,
+                            int T, int H, int D, int NC, hipStream_t stream);
 
 // Fused bf16 prefill (chunk operands built in LDS, segment-parallel state chain).
 size_t fused_workspace_bytes(int B, int T, int H, int D);

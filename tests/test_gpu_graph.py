@@ -181,11 +181,15 @@ def test_profile_hook_marks(env):
         assert hip.hipEventCreate(ctypes.byref(e)) == 0
         evs.append(e.value)
     try:
-        d = gdn_inputs.random_inputs(1, 3000, 2, 128, 128, dtype="bf16", seed=5)
-        x = stage(d, dev)
         gdn.set_profile_events(evs)
+        d = gdn_inputs.random_inputs(1, 272, 2, 128, 128, dtype="bf16", seed=4)
+        x = stage(d, dev)
         gdn.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], None)
-        assert gdn.profile_marks() == 4  # summary pass, combine, output pass
+        assert gdn.profile_marks() == 3  # chunk-map plan: map pass, chain
+        d = gdn_inputs.random_inputs(1, 5000, 2, 128, 128, dtype="bf16", seed=5)
+        x = stage(d, dev)
+        gdn.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], None)
+        assert gdn.profile_marks() == 4  # segment plan: summary pass, combine, output pass
         d1 = gdn_inputs.random_inputs(2, 1, 2, 128, 128, dtype="bf16", seed=6, state_std=0.1)
         y = stage(d1, dev)
         gdn.decode_step(y["q"][:, 0].contiguous(), y["k"][:, 0].contiguous(),

@@ -75,12 +75,14 @@ def test_long_memory_variant(env, T):
     _check("long-memory", o, st, ro, rs, TOL["bf16"])
 
 
-@pytest.mark.parametrize("T", [1100, 3000])
+@pytest.mark.parametrize("T", [1100, 3000, 5000])
 @pytest.mark.parametrize("dtype,dim", [("bf16", 128), ("f32", 64), ("bf16", 64), ("f32", 128)])
 def test_segmented_chain(env, T, dtype, dim):
-    """Long enough for several segments (segment summaries, sequential combine,
-    per-segment outputs), ragged last chunk and segment, random initial state,
-    in place."""
+    """Two heads, long enough for a chained plan: fp32 inputs run segments of
+    the chunked path; bf16 inputs run the chunk-map plan (per-chunk maps and
+    an 18- or 47-step chain) at T = 1100 and 3000 and segments of three chunks
+    (summaries, sequential combine, per-segment outputs) at T = 5000.  Ragged
+    last chunk and segment, random initial state, in place."""
     gdn, dev = env
     import torch
     _note("case segmented T=%d dtype=%s d=%d" % (T, dtype, dim))
