@@ -27,15 +27,15 @@
 //             ([state_in | I] for the first segment) and stores the segment's
 //             affine map [R | M] (H_end = M H_start + R); the last segment has
 //             none.
-//   MAP mode: one chunk per workgroup with Delta = [U | -W] (the start
-//             [0 | I]): stores the chunk's map H_C = Gam_C H0 + N H0 + R as
-//             R = K~^T U, N = -K~^T W (K~ = diag(e) K) and Gam_C -- the decay
-//             stays an exact fp32 factor, out of the fp16 operand N -- and, from
-//             the output products on the same columns, P U and
-//             diag(Gam) Q - P W, so that the chunk's output is
-//             O = P U + (diag(Gam) Q - P W) H0 for any start state H0.  The
-//             chain over the chunks then runs in map_chain (gdn_chunk.hip); no
-//             output pass follows.
+//   MAP mode: two workgroups per chunk, Delta = U (value half) or -W
+//             (identity half; the start [0 | I]).  They store the chunk's map
+//             H_C = Gam_C H0 + N H0 + R as R = K~^T U, N = -K~^T W
+//             (K~ = diag(e) K) and Gam_C -- the decay stays an exact fp32
+//             factor, out of the fp16 operand N -- and, from the output
+//             products on the same columns, P U and diag(Gam) Q - P W, so that
+//             the chunk's output is O = P U + (diag(Gam) Q - P W) H0 for any
+//             start state H0.  The chain over the chunks then runs in
+//             map_chain (gdn_chunk.hip); no output pass follows.
 //
 // Matrix-core products of two inputs (the Gram tiles, the identity products
 // that transpose K and V) take the bf16 inputs as stored; every product with a
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     constexpr bool OUT = MODE == kOut, MAP = MODE == kMap;
     constexpr bool QK = OUT || MAP;       // Q staged, Q K^T tiles and output products
     constexpr int NW = D / 16, NTH = 64 * NW;  // wave w owns column tile w
-    constexpr int TPW = OUT ? 1 : 2;      // state tiles per wave: value tile w (+ identity tile w)
+    constexpr int TPW = QK ? 1 : 2;       // state tiles per wave: value tile w (+ identity tile w)
     constexpr int MT = D / 16;            // key tiles of the state
     // Row strides (halves) of the LDS tiles, chosen per tile by its main
     // access (measured on gfx950): 16-byte matrix-core fragment reads (lane
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     // read the current chunk's Q there
     __shared__ __align__(16) _Float16 sQ[OUT ? 2 * FC * LDF : 8];
     __shared__ __align__(16) uint16_t sQb[QK ? FC * LDF : 8];    // raw bf16 (Q K^T)
-    __shared__ __align__(16) _Float16 sW[FC * LDF];      // -W [t][key]
+    __shared__ __align__(16) _Float16 sW[MAP ? 8 : FC * LDF];  // -W [t][key]
     __shared__ __align__(16) uint16_t sV[FC * LDV];             // raw bf16
     __shared__ __align__(16) _Float16 sKT[D * LAF];      // (diag(e) K)^T [key][t]
     __shared__ __align__(16) _Float16 sA[FC * LAA];      // -A off-diagonal, (T_bb - I) diagonal blocks
@@ -243,7 +243,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     // SUM chains the value columns (tile w, giving R) and the identity columns
     // (tile w of M) of the augmented state together; OUT only the value tile.
     const int BH = B * H;
-    const int bh = (int)blockIdx.x % BH, seg = (int)blockIdx.x / BH;
+    // MAP: blocks [0, BH NC) the value halves, [BH NC, 2 BH NC) the identity halves
+    const int blk_x = MAP ? (int)blockIdx.x % (BH * S) : (int)blockIdx.x;
+    const bool idc = MAP && (int)blockIdx.x >= BH * S;  // identity half (workgroup-uniform)
+    const int bh = blk_x % BH, seg = blk_x / BH;
     const int b = bh / H, h = bh % H;
     const int c_begin = seg * G, c_end = min(c_begin + G, NC);
     const int tid = threadIdx.x, lane = tid & 63;
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     auto issue_loads = [&](int c) {
         if (QK) issue(rq, q, c);
         issue(rk, k, c);
-        issue(rv, v, c);
+        if (!idc) issue(rv, v, c);  // the identity half of MAP reads no V
         issue_gates(c);
     };
     issue_loads(c_begin);
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 st4<_Float16>(&q16[r * LDF + kperm(c8 + 4)], __builtin_shufflevector(qh, qh, 4, 5, 6, 7));
             }
             if (QK) *reinterpret_cast<uint4*>(&sQb[r * LDF + c8]) = rq[i];
-            *reinterpret_cast<uint4*>(&sV[r * LDV + c8]) = rv[i];
+            if (!idc) *reinterpret_cast<uint4*>(&sV[r * LDV + c8]) = rv[i];
         }
     };
     stage_inputs(c_begin, lane);
@@ -537,7 +540,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         // scaled by the end factors e, are also this wave's 16 rows of
         // (diag(e) K)^T for the state update.  The W right-hand side is negated,
         // so the solve yields -W directly.
-        constexpr int NR = 2;  // right-hand-side tiles: U tile w, -W tile w
+        constexpr int NR = MAP ? 1 : 2;  // right-hand-side tiles: U tile w, -W tile w (MAP: one of them)
         f32x4 res[NR][4];
         {
             B4 ident;  // bf16 1.0 = 0x3f80
@@ -561,8 +564,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 else
                     kte_prev = kte;
                 f32x4 acc[NR];
-                acc[0] = fb * vt;
-                acc[1] = -(fg * kt);
+                if constexpr (MAP) {
+                    acc[0] = idc ? -(fg * kt) : fb * vt;
+                } else {
+                    acc[0] = fb * vt;
+                    acc[1] = -(fg * kt);
+                }
 #pragma unroll
                 for (int j = 0; j < bb; ++j) {
                     const H4 aj = ld4<_Float16>(&sA[(16 * bb + lc) * LAA + 16 * j + 4 * lg]);
@@ -577,17 +584,19 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                     res[t][bb] = acc[t];
                 }
             }
-            // -W to LDS row-major.  Lane (lc, lg) holds rows 4 lg + e of key
-            // column lc; as an A operand that tile is its transpose, so a product
-            // with the 16x16 identity (exact) leaves each lane 4 consecutive keys
-            // of token lc: one 8-byte store instead of four 2-byte ones.
-            H4 identh;
+            if constexpr (!MAP) {
+                // -W to LDS row-major.  Lane (lc, lg) holds rows 4 lg + e of key
+                // column lc; as an A operand that tile is its transpose, so a product
+                // with the 16x16 identity (exact) leaves each lane 4 consecutive keys
+                // of token lc: one 8-byte store instead of four 2-byte ones.
+                H4 identh;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) identh[e] = static_cast<_Float16>(4 * lg + e == lc ? 1.f : 0.f);
+                for (int e = 0; e < 4; ++e) identh[e] = static_cast<_Float16>(4 * lg + e == lc ? 1.f : 0.f);
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
-                st4<_Float16>(&sW[(16 * bb + lc) * LDF + kperm(colw + 4 * lg)],
-                              cvt4<_Float16>(MF::k16(xh[1][bb], identh, zero4())));
+                for (int bb = 0; bb < 4; ++bb)
+                    st4<_Float16>(&sW[(16 * bb + lc) * LDF + kperm(colw + 4 * lg)],
+                                  cvt4<_Float16>(MF::k16(xh[1][bb], identh, zero4())));
+            }
         }
         f32x4 u[TPW][4];
 #pragma unroll
@@ -613,9 +622,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             fp[5] = ld8<_Float16>(&sP[(48 + lc) * LAA + 32 + 8 * lg]);
         };
         if constexpr (MAP) {
-            // start [0 | I]: Delta = [U | -W], the solve's right-hand sides
+            // start [0 | I]: Delta = U or -W, the solve's right-hand side
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) dl[0][mt] = res[0][mt], dl[1][mt] = res[1][mt];
+            for (int mt = 0; mt < 4; ++mt) dl[0][mt] = res[0][mt];
             load_p();
         } else {
         H8 fw[2][4], fq[2][NQ];
@@ -670,51 +679,56 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
             db[1][j] = acc_to_b32(dl[j][2], dl[j][3]);
         }
         if constexpr (MAP) {
-            // From [0 | I]: P U on the value columns and diag(Gam) Q_w - P W_w on
+            // From [0 | I]: P U on the value columns, diag(Gam) Q_w - P W_w on
             // the identity columns (Q_w, W_w: key columns colw.. of Q and W;
             // the Q tile reaches the accumulator layout through a product with
             // the 16x16 identity, exactly)
             B4 ident;  // bf16 1.0 = 0x3f80
 #pragma unroll
             for (int e = 0; e < 4; ++e) ident[e] = (short)(4 * lg + e == lc ? 0x3f80 : 0);
-            f32x4 om[2][4];
+            f32x4 om[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const f32x4 gm = *reinterpret_cast<const f32x4*>(&gt.Gam[16 * mt + 4 * lg]);
-                const f32x4 qt = mfma_b16(ldb4(&sQb[(16 * mt + lc) * LDF + colw + 4 * lg]), ident, zero4());
-                om[0][mt] = MF::k32(fp[mt], db[0][0], zero4());
-                om[1][mt] = MF::k32(fp[mt], db[0][1], gm * qt);
+                f32x4 acc = zero4();
+                if (idc) {
+                    const f32x4 gm = *reinterpret_cast<const f32x4*>(&gt.Gam[16 * mt + 4 * lg]);
+                    acc = gm * mfma_b16(ldb4(&sQb[(16 * mt + lc) * LDF + colw + 4 * lg]), ident, zero4());
+                }
+                om[mt] = MF::k32(fp[mt], db[0][0], acc);
             }
 #pragma unroll
-            for (int mt = 2; mt < 4; ++mt)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) om[j][mt] = MF::k32(fp[2 + mt], db[1][j], om[j][mt]);
+            for (int mt = 2; mt < 4; ++mt) om[mt] = MF::k32(fp[2 + mt], db[1][0], om[mt]);
             const long blk = (long)seg * BH + bh;
-            // Gam_C in the summary block's float D^2 + D^2 / 2 (the slot of M's
-            // unused fp16 low part)
-            if (tid == 0) fs.summ[blk * D * 2 * D + D * D + D * D / 2] = gt.GC;
-            float* oi = fs.oin + blk * FC * D;
+            if (!idc) {
+                float* oi = fs.oin + blk * FC * D;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                *reinterpret_cast<f32x4*>(oi + ((wave * 4 + mt) * 64 + lane) * 4) = om[0][mt];
-            // diag(Gam) Q - P W to A-operand slots, through this wave's staging
-            // area as [token][16 key columns] (the summary's transpose below,
-            // with 64 rows)
-            _Float16* st = sStg + wave * D * 16;
+                for (int mt = 0; mt < 4; ++mt)
+                    *reinterpret_cast<f32x4*>(oi + ((wave * 4 + mt) * 64 + lane) * 4) = om[mt];
+            } else {
+                // Gam_C in the summary block's float D^2 + D^2 / 2 (the slot of
+                // M's unused fp16 low part)
+                if (tid == 0) fs.summ[blk * D * 2 * D + D * D + D * D / 2] = gt.GC;
+                // diag(Gam) Q - P W to A-operand slots, through this wave's
+                // staging area as [token][16 key columns] (the summary's
+                // transpose below, with 64 rows)
+                _Float16* st = sStg + wave * D * 16;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+                for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    st[(16 * mt + 4 * lg + e) * 16 + lc] = static_cast<_Float16>(om[1][mt][e]);
-            lds_sync();
-            _Float16* qp = fs.qpr + blk * FC * D;
+                    for (int e = 0; e < 4; ++e)
+                        st[(16 * mt + 4 * lg + e) * 16 + lc] = static_cast<_Float16>(om[mt][e]);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                _Float16* qp = fs.qpr + blk * FC * D;
 #pragma unroll
-            for (int it = 0; it < 2; ++it) {
-                const int slot = it * 64 + lane;
-                const int m = slot >> 5, half = (slot >> 4) & 1, row = slot & 15;
-                const int lane_f = (2 * (wave & 1) + half) * 16 + row;
-                *reinterpret_cast<H8*>(qp + ((m * (D / 32) + (wave >> 1)) * 64 + lane_f) * 8) =
-                    *reinterpret_cast<const H8*>(&st[(16 * m + row) * 16 + 8 * half]);
+                for (int it = 0; it < 2; ++it) {
+                    const int slot = it * 64 + lane;
+                    const int m = slot >> 5, half = (slot >> 4) & 1, row = slot & 15;
+                    const int lane_f = (2 * (wave & 1) + half) * 16 + row;
+                    *reinterpret_cast<H8*>(qp + ((m * (D / 32) + (wave >> 1)) * 64 + lane_f) * 8) =
+                        *reinterpret_cast<const H8*>(&st[(16 * m + row) * 16 + 8 * half]);
+                }
             }
         }
         if (OUT) {
@@ -790,10 +804,14 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         // wave's staging area as [key][16 columns] and leaves as 16-byte
         // A-operand slots: its 16 input-key columns are half of the 32-key block
         // colw / 32, lane groups 2 (wave & 1) and 2 (wave & 1) + 1.
+        // MAP: the value half stores R, the identity half N in M's place.
         float* sm = fs.summ + ((long)seg * BH + bh) * D * 2 * D;
+        if (!idc) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-            *reinterpret_cast<f32x4*>(sm + ((wave * (D / 16) + m) * 64 + lane) * 4) = hs[0][m];
+            for (int m = 0; m < MT; ++m)
+                *reinterpret_cast<f32x4*>(sm + ((wave * (D / 16) + m) * 64 + lane) * 4) = hs[0][m];
+        }
+        if (MAP && !idc) return;
         _Float16* mt = sStg + wave * D * 16;  // this wave's D 16 halves
 #pragma unroll
         for (int m = 0; m < MT; ++m)
@@ -892,7 +910,7 @@ static hipError_t launch_fused_t(const void* q, const void* k, const void* v, co
     const bf16_t* vv = static_cast<const bf16_t*>(v);
     const dim3 block(64 * (D / 16));
     if (p.map) {
-        hipLaunchKernelGGL((gdn_fused<D, kMap>), dim3((unsigned)(BH * p.NC)), block, 0, stream, qq,
+        hipLaunchKernelGGL((gdn_fused<D, kMap>), dim3((unsigned)(2 * BH * p.NC)), block, 0, stream, qq,
                            kk, vv, g, beta, fs, nullptr, nullptr, o, T, H, B, p.NC, 1, p.NC);
         profile_mark(stream);
         hipError_t e = hipGetLastError();
