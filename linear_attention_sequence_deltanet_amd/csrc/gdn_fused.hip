@@ -171,6 +171,22 @@ __device__ __forceinline__ int tsw(int row, int t) {
     return row * LA + t;
 }
 
+// A C-layout tile (lane (lc, lg): rows 4 lg + e, column lc) of column tile
+// colw / 16 of a matrix with `rows` rows, stored in fp16 as the A-operand
+// fragments of 16x16x32 products: fragment (row tile m, 32-column block kk) at
+// halves ((m kcols/32 + kk) 64 + lane_f) 8, lane_f = 16 g + r holding row
+// 16 m + r, columns 32 kk + 8 g .. + 7.  A product with the 16x16 identity
+// (exact) turns each lane's column of four rows into four consecutive columns
+// of row lc, one 8-byte store.
+template <int KCOLS>
+__device__ __forceinline__ void store_afrag(_Float16* dst, int m, int colw, int lg, int lc, f32x4 x,
+                                            H4 identh) {
+    const H4 t = cvt4<_Float16>(MF::k16(cvt4<_Float16>(x), identh, zero4()));
+    const int kin = (colw & 31) + 4 * lg;  // column within the 32-column block
+    const int off = ((m * (KCOLS / 32) + (colw >> 5)) * 64 + (kin >> 3) * 16 + lc) * 8 + (kin & 7);
+    *reinterpret_cast<H4*>(dst + off) = t;
+}
+
 // Products C_t = K_{ni_t} X_t^T of NT 16x16 tiles over the D columns of
 // bf16 row-major LDS tiles (row stride LDF): the contraction step is
 // outermost, so the tiles' accumulators are independent chains on the matrix
@@ -234,7 +250,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     __shared__ __align__(16) _Float16 sKT[D * LAF];      // (diag(e) K)^T [key][t]
     __shared__ __align__(16) _Float16 sA[FC * LAA];      // -A off-diagonal, (T_bb - I) diagonal blocks
     __shared__ __align__(16) _Float16 sP[QK ? FC * LAA : 8];
-    __shared__ __align__(16) _Float16 sStg[OUT ? 8 : NW * D * 16];  // SUM, MAP: transposes to A-operand order
     // gates of chunk c in sG[c & 1]: wave 0 forms the next chunk's at the end
     // of its part of the state update, while the other waves still read the
     // current chunk's
@@ -708,27 +723,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 // Gam_C in the summary block's float D^2 + D^2 / 2 (the slot of
                 // M's unused fp16 low part)
                 if (tid == 0) fs.summ[blk * D * 2 * D + D * D + D * D / 2] = gt.GC;
-                // diag(Gam) Q - P W to A-operand slots, through this wave's
-                // staging area as [token][16 key columns] (the summary's
-                // transpose below, with 64 rows)
-                _Float16* st = sStg + wave * D * 16;
+                // diag(Gam) Q - P W as A-operand fragments (rows = tokens)
+                H4 identh;
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        st[(16 * mt + 4 * lg + e) * 16 + lc] = static_cast<_Float16>(om[mt][e]);
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                for (int e = 0; e < 4; ++e) identh[e] = static_cast<_Float16>(4 * lg + e == lc ? 1.f : 0.f);
                 _Float16* qp = fs.qpr + blk * FC * D;
 #pragma unroll
-                for (int it = 0; it < 2; ++it) {
-                    const int slot = it * 64 + lane;
-                    const int m = slot >> 5, half = (slot >> 4) & 1, row = slot & 15;
-                    const int lane_f = (2 * (wave & 1) + half) * 16 + row;
-                    *reinterpret_cast<H8*>(qp + ((m * (D / 32) + (wave >> 1)) * 64 + lane_f) * 8) =
-                        *reinterpret_cast<const H8*>(&st[(16 * m + row) * 16 + 8 * half]);
-                }
+                for (int mt = 0; mt < 4; ++mt) store_afrag<D>(qp, mt, colw, lg, lc, om[mt], identh);
             }
         }
         if (OUT) {
@@ -800,10 +801,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
         // segment summary in the combine's fragment order (summary_store()
         // defines it element by element): R tiles are this wave's C-layout
         // tiles as they are; M's fp16 high part (the combine of this path
-        // applies no low part, which is left unwritten) goes through this
-        // wave's staging area as [key][16 columns] and leaves as 16-byte
-        // A-operand slots: its 16 input-key columns are half of the 32-key block
-        // colw / 32, lane groups 2 (wave & 1) and 2 (wave & 1) + 1.
+        // applies no low part, which is left unwritten) as A-operand fragments
+        // (rows = output keys, columns = this wave's 16 input keys).
         // MAP: the value half stores R, the identity half N in M's place.
         float* sm = fs.summ + ((long)seg * BH + bh) * D * 2 * D;
         if (!idc) {
@@ -812,23 +811,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
                 *reinterpret_cast<f32x4*>(sm + ((wave * (D / 16) + m) * 64 + lane) * 4) = hs[0][m];
         }
         if (MAP && !idc) return;
-        _Float16* mt = sStg + wave * D * 16;  // this wave's D 16 halves
+        H4 identh;
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                mt[(16 * m + 4 * lg + e) * 16 + lc] = static_cast<_Float16>(hs[TPW - 1][m][e]);
-        lds_sync();
+        for (int e = 0; e < 4; ++e) identh[e] = static_cast<_Float16>(4 * lg + e == lc ? 1.f : 0.f);
         _Float16* mh = reinterpret_cast<_Float16*>(sm + D * D);
 #pragma unroll
-        for (int it = 0; it < D / 32; ++it) {
-            const int slot = it * 64 + lane;
-            const int m = slot >> 5, half = (slot >> 4) & 1, row = slot & 15;
-            const int lane_f = (2 * (wave & 1) + half) * 16 + row;
-            const int off = ((m * (D / 32) + (wave >> 1)) * 64 + lane_f) * 8;
-            const int src = (16 * m + row) * 16 + 8 * half;
-            *reinterpret_cast<H8*>(mh + off) = *reinterpret_cast<const H8*>(&mt[src]);
-        }
+        for (int m = 0; m < MT; ++m) store_afrag<D>(mh, m, colw, lg, lc, hs[TPW - 1][m], identh);
     }
 }
 
