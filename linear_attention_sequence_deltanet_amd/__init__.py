@@ -144,13 +144,15 @@ def _dtype_code(t) -> int:
 
 
 def _ptr(t):
+    """Device address of a contiguous GPU tensor (an int: ctypes converts it
+    for the c_void_p parameters), None for None."""
     if t is None:
         return None
     if not t.is_cuda:
         raise ValueError("tensors must be on the GPU (got %s)" % t.device)
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
 def _empty(shape, dtype, device, stream):
@@ -165,10 +167,22 @@ def _empty(shape, dtype, device, stream):
     return t
 
 
+_raw_stream = None  # torch's current-stream query without building a Stream object
+
+
 def _stream(stream, device):
+    """The HIP stream handle (an int) to launch on: `stream`, else torch's
+    current stream on `device`."""
+    global _raw_stream
+    if stream is not None:
+        return stream.cuda_stream
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+    if _raw_stream is None:
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if _raw_stream:
+        return _raw_stream(idx)
+    return torch.cuda.current_stream(idx).cuda_stream
 
 
 def _need(t, dtype, name):
@@ -181,24 +195,26 @@ def _check(t, shape, dtype, name):
     and writes every buffer at the sizes taken from the leading tensor."""
     if t is None:
         return
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
-    _need(t, dtype, name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
 
 
 def _check_mixer(q, k, v, g, beta, states, o, tok):
     """q, k, v, g, beta, state(s) and o of the recurrence entry points; `tok` is
     (B, T, H) or (B, H) for decode."""
-    torch = _torch()
+    f32 = _torch().float32
     dk, dv = q.shape[-1], v.shape[-1]
     B, H = tok[0], tok[-1]
-    _check(k, tuple(tok) + (dk,), q.dtype, "k")
-    _check(v, tuple(tok) + (dv,), q.dtype, "v")
-    _check(g, tok, torch.float32, "g")
-    _check(beta, tok, torch.float32, "beta")
+    tok = tuple(tok)
+    _check(k, tok + (dk,), q.dtype, "k")
+    _check(v, tok + (dv,), q.dtype, "v")
+    _check(g, tok, f32, "g")
+    _check(beta, tok, f32, "beta")
     for st, nm in states:
-        _check(st, (B, H, dk, dv), torch.float32, nm)
-    _check(o, tuple(tok) + (dv,), torch.float32, "o")
+        _check(st, (B, H, dk, dv), f32, nm)
+    _check(o, tok + (dv,), f32, "o")
 
 
 def prefill_workspace_bytes(B, T, H, dk, dv, dtype=GDN_BF16) -> int:
@@ -208,9 +224,12 @@ def prefill_workspace_bytes(B, T, H, dk, dv, dtype=GDN_BF16) -> int:
 
 
 def _workspace(workspace, B, T, H, dk, dv, code, device, stream):
-    need = int(_lib.gdn_prefill_workspace_bytes(B, T, H, dk, dv, code))
-    if workspace is None and need > 0:
-        workspace = _empty(need, _torch().uint8, device, stream)
+    """A caller's workspace as it is (the library checks its size), else one of
+    the size the call needs (none when it needs none)."""
+    if workspace is None:
+        need = int(_lib.gdn_prefill_workspace_bytes(B, T, H, dk, dv, code))
+        if need > 0:
+            workspace = _empty(need, _torch().uint8, device, stream)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return workspace, nbytes
 

@@ -799,7 +799,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void map_chain(MapWs mw, const float
     using M = Mfma<_Float16>;
     using F8 = M::frag8;
     constexpr int NS = D / 16, LS = D + 8, KB = D / 32;
-    __shared__ __align__(16) _Float16 sHi[2][16 * LS];  // fp16 state slice [col][key], by chunk parity
+    __shared__ __align__(16) _Float16 sHi[2][16 * LS];  // fp16 state slice [col][key], H_c in [c & 1]
 
     const int L = blockIdx.x;
     int bh, slice;
@@ -834,20 +834,26 @@ __global__ __launch_bounds__(64 * (D / 16)) void map_chain(MapWs mw, const float
         p.gc = sm[D * D + D * D / 2];
         if (outw) p.oi = *reinterpret_cast<const f32x4*>(mw.oin + blk(c) * 64 * D + ((slice * 4 + wave) * 64 + lane) * 4);
     };
-    auto load_mq = [&](Pre& p, int c, int kk) {
+    auto load_m = [&](int c, int kk) {
         const _Float16* mh = reinterpret_cast<const _Float16*>(mw.summ + blk(c) * D * 2 * D + D * D);
-        p.m[kk] = *reinterpret_cast<const F8*>(mh + ((wave * KB + kk) * 64 + lane) * 8);
-        if (outw) p.qa[kk] = *reinterpret_cast<const F8*>(mw.qpr + blk(c) * 64 * D + ((wave * KB + kk) * 64 + lane) * 8);
+        return *reinterpret_cast<const F8*>(mh + ((wave * KB + kk) * 64 + lane) * 8);
+    };
+    auto load_q = [&](int c, int kk) {
+        return *reinterpret_cast<const F8*>(mw.qpr + blk(c) * 64 * D + ((wave * KB + kk) * 64 + lane) * 8);
     };
     auto load = [&](Pre& p, int c) {
         load_ro(p, c);
 #pragma unroll
-        for (int kk = 0; kk < KB; ++kk) load_mq(p, c, kk);
+        for (int kk = 0; kk < KB; ++kk) {
+            p.m[kk] = load_m(c, kk);
+            if (outw) p.qa[kk] = load_q(c, kk);
+        }
     };
+    // Chunk c: sHi[c & 1] holds H_c (all waves' tiles, past a barrier).  The
+    // next state goes to the other buffer before this chunk's output products
+    // and stores, which then overlap the other waves' way to the barrier.
     auto apply = [&](Pre& p, int c, int next) {
-        _Float16* sh = sHi[c & 1];  // rewritten two chunks later, past the next barrier
-        st4<_Float16>(&sh[lc * LS + 16 * wave + 4 * lg], cvt4<_Float16>(hs));
-        lds_sync();
+        const _Float16* sh = sHi[c & 1];
         F8 bhi[KB];
 #pragma unroll
         for (int kk = 0; kk < KB; ++kk) bhi[kk] = ld8<_Float16>(&sh[lc * LS + 32 * kk + 8 * lg]);
@@ -856,25 +862,33 @@ __global__ __launch_bounds__(64 * (D / 16)) void map_chain(MapWs mw, const float
         for (int kk = 0; kk < KB; ++kk) {
             if (kk & 1) a1 = M::k32(p.m[kk], bhi[kk], a1);
             else a0 = M::k32(p.m[kk], bhi[kk], a0);
-            if (outw) ao = M::k32(p.qa[kk], bhi[kk], ao);
-            load_mq(p, next, kk);
+            p.m[kk] = load_m(next, kk);
             __builtin_amdgcn_sched_barrier(0);
         }
+        hs = p.gc * hs + (p.r + (a0 + a1));
+        st4<_Float16>(&sHi[(c + 1) & 1][lc * LS + 16 * wave + 4 * lg], cvt4<_Float16>(hs));
         if (outw) {
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+                ao = M::k32(p.qa[kk], bhi[kk], ao);
+                p.qa[kk] = load_q(next, kk);
+            }
             ao += p.oi;
             const int t0 = c * 64 + 16 * wave + 4 * lg;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (t0 + e < T) o[(((long)b * T + t0 + e) * H + h) * D + col] = ao[e];
         }
-        hs = p.gc * hs + (p.r + (a0 + a1));
         load_ro(p, next);
+        lds_sync();  // H_{c+1} complete; every wave is done reading sHi[c & 1]
     };
 
     constexpr int NB = 2;
     Pre pb[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) load(pb[i], i);
+    st4<_Float16>(&sHi[0][lc * LS + 16 * wave + 4 * lg], cvt4<_Float16>(hs));
+    lds_sync();
     int c = 0;
     for (; c + NB <= NC; c += NB) {
 #pragma unroll
