@@ -24,6 +24,13 @@ A ragged last chunk is padded with g = b = 0 and zero q, k, v rows, which leaves
 the real rows and H_C unchanged.  Over several chunks the state map is affine,
 H_end = M H_start + R, and [R | M] is the same chunk recursion run on the
 augmented state [H | M] from [0 | I] with v padded by zero columns.
+
+Chunk-map form (the short-sequence plan): substituting Delta = U - W H0 into
+O and H_C gives, with K~ = diag(exp(gam_C - gam)) K,
+    H_C = Gam_C H0 + N H0 + R,   N = -K~^T W,  R = K~^T U,
+    O   = P U + (diag(Gam) Q - P W) H0,   P = L o Q K^T,
+so each chunk reduces to (R, N, Gam_C, P U, diag(Gam) Q - P W), computed
+without the state, and the state only passes through these maps.
 """
 from __future__ import annotations
 
@@ -86,3 +93,39 @@ def segment_map(k, v, g, beta, C=64):
     X0 = np.concatenate([np.zeros((dk, dv)), np.eye(dk)], axis=1)
     _, X = chunk_forward(np.zeros_like(k), k, vaug, g, beta, X0, C)
     return X[:, :dv], X[:, dv:]
+
+
+def chunk_map(Q, K, V, g, b):
+    """The chunk-map form of one chunk (rows padded to the chunk length):
+    (R, N, Gam_C, PU, Qeff) with H_C = Gam_C H0 + N H0 + R and
+    O = PU + Qeff H0 for every start state H0."""
+    C = len(g)
+    gam = np.cumsum(g)
+    Gam = np.exp(gam)
+    A = b[:, None] * _decay_lower(gam, True) * (K @ K.T)
+    Tm = np.linalg.solve(np.eye(C) + A, np.eye(C))
+    W = Tm @ ((b * Gam)[:, None] * K)
+    U = Tm @ (b[:, None] * V)
+    P = _decay_lower(gam, False) * (Q @ K.T)
+    Kt = np.exp(gam[-1] - gam)[:, None] * K
+    return Kt.T @ U, -(Kt.T @ W), Gam[-1], P @ U, Gam[:, None] * Q - P @ W
+
+
+def map_forward(q, k, v, g, beta, state0=None, C=64):
+    """chunk_forward through the chunk maps: all maps first (state-free), then
+    the chain H <- Gam_C H + N H + R with each chunk's output on the way."""
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    g, beta = np.asarray(g, np.float64), np.asarray(beta, np.float64)
+    T, dk = k.shape
+    dv = v.shape[1]
+    maps = []
+    for c0 in range(0, T, C):
+        n = min(C, T - c0)
+        pad = lambda x: np.concatenate([x[c0:c0 + n], np.zeros((C - n,) + x.shape[1:])])
+        maps.append((c0, n, chunk_map(pad(q), pad(k), pad(v), pad(g), pad(beta))))
+    H = np.zeros((dk, dv)) if state0 is None else np.array(state0, np.float64)
+    o = np.zeros((T, dv))
+    for c0, n, (R, N, GC, PU, Qe) in maps:
+        o[c0:c0 + n] = (PU + Qe @ H)[:n]
+        H = GC * H + N @ H + R
+    return o, H

@@ -13,7 +13,7 @@ import pytest
 
 import gdn_inputs
 import oracle
-from chunk_model import chunk_forward, segment_map
+from chunk_model import chunk_forward, chunk_map, chunk_step, map_forward, segment_map
 
 
 def _series(T, d, seed, g_shift=2.0, state_std=0.3):
@@ -96,3 +96,45 @@ def test_padding_rows_leave_chunk_exact():
     O2, H2 = chunk_step(z(q), z(k), z(v), z(g), z(b), H0)
     np.testing.assert_allclose(O2[:40], O1, rtol=1e-13, atol=1e-15)
     np.testing.assert_allclose(H2, H1, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("C", [1, 7, 64])
+@pytest.mark.parametrize("T", [1, 63, 65, 257])
+def test_chunk_maps_equal_oracle(C, T):
+    """The chunk-map form (all per-chunk maps first, then the state chain with
+    the outputs) equals the token-serial oracle for any chunk length and ragged
+    tails."""
+    s = _series(T, 16, seed=300 * C + T)
+    ro, rs = _oracle(s)
+    o, st = map_forward(s["q"], s["k"], s["v"], s["g"], s["beta"], s["state0"], C)
+    assert _rel(o, ro) <= 1e-12, (C, T, _rel(o, ro))
+    assert _rel(st, rs) <= 1e-12, (C, T, _rel(st, rs))
+
+
+@pytest.mark.parametrize("g_shift", [-9.0, 3.0])
+def test_chunk_maps_gate_extremes_d64(g_shift):
+    """d = 64, C = 64, 200 tokens: gates near one and strong decay (the decay
+    Gam_C kept apart from N stays an exact factor; N and R stay finite)."""
+    s = _series(200, 64, seed=9, g_shift=g_shift)
+    ro, rs = _oracle(s)
+    o, st = map_forward(s["q"], s["k"], s["v"], s["g"], s["beta"], s["state0"], 64)
+    assert np.isfinite(o).all() and np.isfinite(st).all()
+    assert _rel(o, ro) <= 1e-12 and _rel(st, rs) <= 1e-12, g_shift
+
+
+def test_chunk_map_is_affine_in_the_start_state():
+    """One chunk: the map's (O, H_C) equal chunk_step's for several start
+    states, and pure decay (b = 0) gives N = R = 0, PU = 0 and
+    Qeff = diag(Gam) Q exactly."""
+    s = _series(64, 16, seed=13)
+    q, k, v, g, b = (s[n] for n in ("q", "k", "v", "g", "beta"))
+    R, N, GC, PU, Qe = chunk_map(q, k, v, g, b)
+    rng = np.random.default_rng(5)
+    for H0 in (np.zeros((16, 16)), s["state0"], rng.standard_normal((16, 16))):
+        O, HC = chunk_step(q, k, v, g, b, H0)
+        assert _rel(PU + Qe @ H0, O) <= 1e-12
+        assert _rel(GC * H0 + N @ H0 + R, HC) <= 1e-12
+    R0, N0, GC0, PU0, Qe0 = chunk_map(q, k, v, g, np.zeros_like(b))
+    assert not R0.any() and not N0.any() and not PU0.any()
+    np.testing.assert_array_equal(Qe0, np.exp(np.cumsum(g))[:, None] * q)
+    assert GC0 == np.exp(np.cumsum(g))[-1]
