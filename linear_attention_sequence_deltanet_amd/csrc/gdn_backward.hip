@@ -79,8 +79,8 @@ struct BwdArgs {
     float* u;    // [.] U,  output-layout tiles
     float* hs;   // [.][D][D]    chunk start states
     float* dl;   // [.][BC][D]   Delta
-    float* gs;   // [.][D][D]    gradients at chunk ends
-    float* dr;   // [.][BC][D]   dR
+    float* gs;   // [.][D][D]    gradients at chunk ends (in the space of w and u)
+    float* dr;   // [.][BC][D]   dR (in the space of ekt)
     float* m1;   // [.] Ti^T P^T (upper tiles), row-operand fragments
     float* m2;   // [.] Ti^T diag(e) K,         row-operand fragments
     float* ekt;  // [.] (diag(e) K)^T,          row-operand fragments
@@ -1074,9 +1074,13 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// The reverse chain's outputs reuse the forward chain's operands, which nothing
+// reads after the forward chain: the end gradients G (D^2 floats per chunk)
+// take the place of W and U (2 BC D >= D^2 for D <= 128), dR that of
+// (diag(e) K)^T (BC D each).
 size_t backward_workspace_bytes(int B, int T, int H, int D) {
     const size_t NC = (size_t)(T + BC - 1) / BC, chunks = NC * B * H;
-    const size_t per = SCN * BC + 3 * BC * BC + 8 * (size_t)BC * D + 2 * (size_t)D * D;
+    const size_t per = SCN * BC + 3 * BC * BC + 7 * (size_t)BC * D + (size_t)D * D;
     return chunks * per * sizeof(float);
 }
 
@@ -1097,13 +1101,13 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, int dtyp
     a.lkk = p, p += chunks * BC * BC;
     a.w = p, p += chunks * BC * D;
     a.u = p, p += chunks * BC * D;
+    a.gs = a.w;  // over W and U (dead after the forward chain)
     a.dl = p, p += chunks * BC * D;
-    a.dr = p, p += chunks * BC * D;
     a.hs = p, p += chunks * (size_t)D * D;
-    a.gs = p, p += chunks * (size_t)D * D;
     a.m1 = p, p += chunks * BC * BC;
     a.m2 = p, p += chunks * BC * D;
     a.ekt = p, p += chunks * BC * D;
+    a.dr = a.ekt;  // over (diag(e) K)^T (dead after the forward chain)
     a.qgt = p, p += chunks * BC * D;
     a.kbt = p;
     if (dtype_bf16)
