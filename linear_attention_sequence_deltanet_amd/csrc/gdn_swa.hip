@@ -147,6 +147,7 @@ struct AttnArgs {
     float* part;         // ns > 1: partial O [B][Hq][nqb][ns][QB][d], then (m, l) [..][QB][2]
     long long pos0;
     int T, Hq, Hkv, W, R, hist, nqb, pmod, ns;
+    int flat;  // 1-D grid, items dealt to the XCDs in contiguous ranges
 };
 
 // max / sum over the 4 lanes c, c+16, c+32, c+48 (one query of an S^T tile)
@@ -188,10 +189,20 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
 
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
     const int g = lane / 16, c = lane % 16;
-    const int qb = a.nqb - 1 - (int)blockIdx.x / a.ns;  // longest windows first
-    const int split = (int)blockIdx.x % a.ns;
-    const int h = blockIdx.y;
-    const long b = blockIdx.z;
+    // Workgroups are dealt to the 8 XCDs in turn (XCD = id mod 8), so item
+    // (id mod 8) N / 8 + id / 8 gives each XCD a contiguous range of items:
+    // ordered by (batch, head, query block, split), its workgroups share one or
+    // two heads and their key-value head in the XCD's L2.  Within a range the
+    // longest windows come first.
+    // (With more items than a 1-D grid holds, the grid is (query block x
+    // split, head, batch) in the hardware's order.)
+    const long N = (long)gridDim.x * gridDim.y * gridDim.z;
+    const long L = blockIdx.x + (long)gridDim.x * (blockIdx.y + (long)gridDim.y * blockIdx.z);
+    const long I = a.flat && a.ns == 1 && N % 8 == 0 ? (L % 8) * (N / 8) + L / 8 : L;
+    const int split = (int)(I % a.ns);
+    const int qb = a.nqb - 1 - (int)((I / a.ns) % a.nqb);  // longest windows first
+    const int h = (int)((I / ((long)a.ns * a.nqb)) % a.Hq);
+    const long b = I / ((long)a.ns * a.nqb * a.Hq);
     const int hk = h / (a.Hq / a.Hkv);
     const int T = a.T, W = a.W;
     const int t0 = qb * QB;
@@ -391,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
     } else {
         // unnormalised partial of this split, merged by swa_combine
         const long item = ((b * a.Hq + h) * a.nqb + qb) * a.ns + split;
-        const long nitems = (long)gridDim.z * a.Hq * a.nqb * a.ns;
+        const long nitems = N;
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
             const int qi = 32 * wave + 16 * qt + c;
@@ -535,7 +546,9 @@ hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache
     a.pmod = (int)(pos0 % a.R);
     a.ns = swa_splits(B, T, Hq, window, pos0, ring);
     a.part = reinterpret_cast<float*>(wv + (size_t)B * Hkv * T * SD);
-    const dim3 grid((unsigned)(a.nqb * a.ns), (unsigned)Hq, (unsigned)B);
+    const long nall = (long)a.nqb * a.ns * Hq * B;
+    a.flat = nall <= 0x7fffffffL;
+    const dim3 grid = a.flat ? dim3((unsigned)nall) : dim3((unsigned)(a.nqb * a.ns), (unsigned)Hq, (unsigned)B);
     if (ring)
         hipLaunchKernelGGL(swa_attn<true>, grid, dim3(256), 0, stream, a);
     else
