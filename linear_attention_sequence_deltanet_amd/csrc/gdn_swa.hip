@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
     // split, head, batch) in the hardware's order.)
     const long N = (long)gridDim.x * gridDim.y * gridDim.z;
     const long L = blockIdx.x + (long)gridDim.x * (blockIdx.y + (long)gridDim.y * blockIdx.z);
-    const long I = a.flat && a.ns == 1 && N % 8 == 0 ? (L % 8) * (N / 8) + L / 8 : L;
+    const long I = a.flat && N % 8 == 0 ? (L % 8) * (N / 8) + L / 8 : L;
     const int split = (int)(I % a.ns);
     const int qb = a.nqb - 1 - (int)((I / a.ns) % a.nqb);  // longest windows first
     const int h = (int)((I / ((long)a.ns * a.nqb)) % a.Hq);
