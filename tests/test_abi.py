@@ -106,9 +106,9 @@ def test_prefill_aliasing(lib):
 
 @pytest.mark.parametrize("T,dtype", [(3000, 0), (100, 1)])
 def test_prefill_workspace_too_small(lib, T, dtype):
-    """bf16 at T = 3000, H = 2 plans several segments; fp32 always stages its
-    chunk operands: both need a workspace, and one byte less (or none) is
-    refused before any launch."""
+    """bf16 at T = 3000, H = 2 plans the chunk-map form (its per-chunk maps live
+    in the workspace); fp32 always stages its chunk operands: both need a
+    workspace, and one byte less (or none) is refused before any launch."""
     need = lib.gdn_prefill_workspace_bytes(1, T, 2, 128, 128, dtype)
     assert need > 0
     for ws, nbytes in ((P["ws"], need - 1), (None, 0)):
@@ -133,9 +133,15 @@ def test_noalloc_limit_matches_header_and_rejects_large_plans(lib):
     r = lib.gdn_prefill_noalloc(P["q"], P["k"], P["v"], 1, P["g"], P["beta"], P["sin"],
                                 P["sout"], P["o"], 1, 8192, 16, 128, 128, None)
     assert r == SCRATCH
-    # the bf16 plans of the benchmark shapes fit
+    # the bf16 plans of the benchmark shapes fit; at B H = 16 every length does
+    # (segment plans, and the chunk-map plan, whose maps are held to 64 MiB)
     for T in (272, 8192, 262144):
         assert 0 < lib.gdn_prefill_workspace_bytes(1, T, 16, 128, 128, 0) <= limit
+    for T in (1, 63, 64, 65, 127, 200, 1000, 1471, 1472, 1473, 1536, 2048, 3000, 4096, 5000,
+              16384, 65536, 100000):
+        for B, H in ((1, 16), (2, 8), (16, 1)):
+            assert lib.gdn_prefill_workspace_bytes(B, T, H, 128, 128, 0) <= limit, (B, T, H)
+            assert lib.gdn_prefill_workspace_bytes(B, T, H, 64, 64, 0) <= limit, (B, T, H)
     r = lib.gdn_prefill_noalloc(None, P["k"], P["v"], 0, P["g"], P["beta"], P["sin"],
                                 P["sout"], P["o"], 1, 8192, 16, 128, 128, None)
     assert r == NULL
