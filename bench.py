@@ -521,9 +521,9 @@ def time_layer(gdn, args, dev):
     units = B * T * H
     res = []
     for name, call, per_unit, extra in (
-            ("conv_qkv (conv_qkv_kernel<128,16>)", conv, CONV_BYTES_PER_TOKEN_HEAD,
+            ("conv_qkv (conv_qkv_kernel<128,32,2>)", conv, CONV_BYTES_PER_TOKEN_HEAD,
              3 * H * dk * 16 + 9 * B * H * dk * 4),
-            ("gate_out (gate_out_kernel<128,4,bf16>)", gate, GATE_BYTES_PER_TOKEN_HEAD, dk * 4)):
+            ("gate_out (gate_out_kernel<128,2,bf16>)", gate, GATE_BYTES_PER_TOKEN_HEAD, dk * 4)):
         kt = kernel_times(gdn, call, args.steps)[0]
         nbytes = per_unit * units + extra
         gbs = nbytes / (kt / 1e3) / 1e9

@@ -92,7 +92,7 @@ def _exact_conv(x, l2=True):
     (1, 130, 4, 64, True, True),     # d = 64 heads, carried history
     (2, 2, 2, 128, True, False),     # T < 3: new state mixes old state and x
     (1, 1, 16, 128, True, True),     # one token
-    (3, 48, 1, 64, True, False),     # whole token blocks only, v-style (no norm)
+    (3, 96, 1, 64, True, False),     # whole token blocks only, v-style (no norm)
 ])
 def test_conv_qkv_matches_oracle(env, B, T, H, d, with_state, l2):
     gdn, dev = env
