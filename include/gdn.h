@@ -279,9 +279,12 @@ gdn_status gdn_backward(const void *q, const void *k, const void *v, gdn_dtype d
 
 /*
  * Workspace bytes of gdn_swa_prefill / gdn_swa_stream_chunk for these sizes and
- * window (0 for invalid sizes): the fp16 rotated q, k, v and, when the call
- * splits each query block's window over several workgroups (small grids, e.g.
- * stream calls against a long window), their partial outputs.
+ * window (0 for invalid sizes): the fp16 rotated q; k and v, either as rows
+ * (calls with a ring cache) or as the per-64-key-block tiles that the attention
+ * copies into on-chip memory (calls without one), whichever is larger; and,
+ * when the call splits each query block's window over several workgroups
+ * (small grids, e.g. stream calls against a long window), their partial
+ * outputs.
  */
 size_t gdn_swa_workspace_bytes(int B, int T, int Hq, int Hkv, int d, int window);
 

@@ -13,13 +13,18 @@
 // Three kernels per call, all on the caller's stream:
 //   swa_prep   rotates q and k at their absolute positions and converts q
 //              (pre-scaled by log2(e) / sqrt(d)), k and v to fp16 in the
-//              workspace, head-major ([B][H][T][d]).  bf16 inputs convert to
-//              fp16 exactly at activation magnitudes; rotated values keep
-//              3 more mantissa bits than bf16 would.
+//              workspace: q head-major ([B][H][T][d]); k and v the same for
+//              calls with a ring cache, otherwise as the image of each 64-key
+//              block in on-chip memory (the K tile and the V^T tile, padded
+//              rows, keys past T zero).  bf16 inputs convert to fp16 exactly
+//              at activation magnitudes; rotated values keep 3 more mantissa
+//              bits than bf16 would.
 //   swa_attn   flash-style attention: a workgroup owns 128 queries of one head
 //              (4 waves x 32) and walks 64-key blocks of their window.  A block
-//              of K (row-major) and V (transposed, two keys per dword) is
-//              staged in LDS, double-buffered.  Each wave forms S^T = K Q^T on
+//              of K (row-major) and V (transposed) sits in LDS, double-buffered:
+//              copied from its image by direct-to-LDS loads, or, with a ring
+//              cache, staged through registers (rows from the call or the
+//              ring, V transposed two keys per dword).  Each wave forms S^T = K Q^T on
 //              the matrix cores, so lane column c of every tile is one query:
 //              the online softmax (running max m, sum l, base-2 exponentials),
 //              the rescale of O^T and the final 1/l are per-lane, and P^T feeds
@@ -30,6 +35,7 @@
 //              values into the caller's ring cache for the next call.
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -51,7 +57,19 @@ constexpr int KB = 64;         // keys per block
 // 16 bytes long, and at half rate for an odd chunk count (measured).
 constexpr int KLD = SD + 16;   // K tile row stride (halves)
 constexpr int VLD = KB + 16;   // V^T tile row stride (halves)
+constexpr int KIMG = KB * KLD;          // K tile of one key block in LDS (halves)
+constexpr int IMG = KIMG + SD * VLD;    // K and V^T tiles of one key block (halves)
 constexpr float kNegBig = -1e30f;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Position of key kk (< 64) of a block inside each V^T row: within a 32-key
+// step, key 32 j + 16 u + 4 g + e sits at 32 j + 8 g + 4 u + e, the order in
+// which the S^T tiles hold the keys, so that a lane's 8 keys of a step are one
+// 16-byte read.
+__device__ __forceinline__ int vperm(int kk) {
+    return (kk & 32) | (((kk >> 2) & 3) << 3) | (((kk >> 4) & 1) << 2) | (kk & 3);
+}
 
 // ---------------------------------------------------------------------------
 // swa_prep: one thread per 8 features (4 rotation pairs) of one (b, t, head)
@@ -62,11 +80,13 @@ struct PrepArgs {
     const uint16_t* k;  // bf16 [B][T][Hkv][d]
     const uint16_t* v;
     _Float16* wq;       // [B][Hq][T][d]
-    _Float16* wk;       // [B][Hkv][T][d]
+    _Float16* wk;       // row layout: [B][Hkv][T][d]
     _Float16* wv;
+    _Float16* img;      // block layout: [B][Hkv][NKB][IMG], the LDS image of each key block
     long long pos0;
     float qscale;
     int B, T, Hq, Hkv;
+    int blocked, NKB;   // blocked: K and V go to img (keys T .. 64 NKB - 1 as zeros)
     double rev[SD / 2];  // base^(-2i/d) / (2 pi): rotation of pair i per position, in turns
 };
 
@@ -80,17 +100,64 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 u, float (&f)[8]) {
 }
 
 __global__ __launch_bounds__(256) void swa_prep(const PrepArgs a) {
-    const long item = (long)blockIdx.x * 256 + threadIdx.x;
+    long item = (long)blockIdx.x * 256 + threadIdx.x;
     constexpr int G = SD / 8;
-    const int heads = a.Hq + 2 * a.Hkv;
-    const long total = (long)a.B * a.T * heads * G;
-    if (item >= total) return;
+    // Items: with the block layout first the V^T chunks (in waves of their own,
+    // and first so that their longer latency overlaps the rest), then the rows
+    // of q and k; otherwise the rows of q, k and v.  Token rows: T, or with the
+    // block layout the whole last key block.
+    const int heads = a.Hq + (a.blocked ? 1 : 2) * a.Hkv;
+    const int TR = a.blocked ? a.NKB * KB : a.T;
+    const long nvt = a.blocked ? (long)a.B * a.Hkv * a.NKB * 8 * G : 0;
+    if (item < nvt) {
+        // V^T of key block jb in the image: item (b, h, jb, r, part) writes
+        // 16-byte chunk r < 8 (the 8 keys at positions 8 r .. 8 r + 7 of the
+        // vperm order) of the 8 feature rows part 8 .. part 8 + 7: 8 row loads,
+        // a transpose in registers, 8 16-byte stores.  Keys past the sequence
+        // are zeros.
+        long rest = item;
+        const int part = (int)(rest % G);
+        rest /= G;
+        const int r = (int)(rest % 8);
+        rest /= 8;
+        const int jb = (int)(rest % a.NKB);
+        rest /= a.NKB;
+        const int h = (int)(rest % a.Hkv);
+        const long b = rest / a.Hkv;
+        H8 col[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int tt = jb * KB + 32 * (r >> 2) + 16 * (i >> 2) + 4 * (r & 3) + (i & 3);
+            float x[8];
+            if (tt < a.T) {
+                bf16x8_to_f32(*reinterpret_cast<const uint4*>(a.v + ((b * a.T + tt) * a.Hkv + h) * SD + part * 8), x);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) col[i][e] = static_cast<_Float16>(x[e]);
+        }
+        _Float16* dst = a.img + ((b * a.Hkv + h) * a.NKB + jb) * (long)IMG + KIMG + 8 * r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            H8 row;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) row[i] = col[i][e];
+            *reinterpret_cast<H8*>(dst + (part * 8 + e) * VLD) = row;
+        }
+        return;
+    }
+    item -= nvt;
+    if (item >= (long)a.B * TR * heads * G) return;
     const int part = (int)(item % G);
     long rest = item / G;
     const int hh = (int)(rest % heads);
     rest /= heads;
-    const int t = (int)(rest % a.T);
-    const long b = rest / a.T;
+    const int t = (int)(rest % TR);
+    const long b = rest / TR;
+    const bool pad = t >= a.T;  // block layout only: a key row past the sequence, zeros
+    if (pad && hh < a.Hq) return;
 
     const uint16_t* src;
     _Float16* dst;
@@ -103,16 +170,22 @@ __global__ __launch_bounds__(256) void swa_prep(const PrepArgs a) {
         kind = 1;
         const int h = hh - a.Hq;
         src = a.k + ((b * a.T + t) * a.Hkv + h) * SD;
-        dst = a.wk + ((b * a.Hkv + h) * (long)a.T + t) * SD;
+        dst = a.blocked ? a.img + ((b * a.Hkv + h) * a.NKB + t / KB) * (long)IMG + (t % KB) * KLD
+                        : a.wk + ((b * a.Hkv + h) * (long)a.T + t) * SD;
     } else {
-        kind = 2;
+        kind = 2;  // row layout only
         const int h = hh - a.Hq - a.Hkv;
         src = a.v + ((b * a.T + t) * a.Hkv + h) * SD;
         dst = a.wv + ((b * a.Hkv + h) * (long)a.T + t) * SD;
     }
     float x[8];
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(src + part * 8), x);
-    if (kind < 2) {
+    if (pad) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    } else {
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(src + part * 8), x);
+    }
+    if (kind < 2 && !pad) {
         const double p = (double)(a.pos0 + t);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -139,14 +212,15 @@ __global__ __launch_bounds__(256) void swa_prep(const PrepArgs a) {
 // ---------------------------------------------------------------------------
 struct AttnArgs {
     const _Float16* q;   // [B][Hq][T][d], scaled, rotated
-    const _Float16* k;   // [B][Hkv][T][d], rotated
-    const _Float16* v;   // [B][Hkv][T][d]
+    const _Float16* k;   // ring calls: [B][Hkv][T][d], rotated
+    const _Float16* v;   // ring calls: [B][Hkv][T][d]
+    const _Float16* img; // other calls: [B][Hkv][NKB][IMG], each key block's LDS image
     const _Float16* kc;  // ring [B][Hkv][R][d] (positions < pos0), or null
     const _Float16* vc;
     float* o;            // [B][T][Hq][d]
     float* part;         // ns > 1: partial O [B][Hq][nqb][ns][QB][d], then (m, l) [..][QB][2]
     long long pos0;
-    int T, Hq, Hkv, W, R, hist, nqb, pmod, ns;
+    int T, Hq, Hkv, W, R, hist, nqb, pmod, ns, NKB;
     int flat;  // 1-D grid, items dealt to the XCDs in contiguous ranges
 };
 
@@ -184,8 +258,11 @@ __device__ __forceinline__ unsigned pack_h2(_Float16 a, _Float16 b) {
 
 template <bool RING>
 __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) _Float16 sK[2][KB * KLD];
-    __shared__ __attribute__((aligned(16))) _Float16 sV[2][SD * VLD];
+    // two key-block buffers, each the K tile then the V^T tile; two arrays, not
+    // one indexed by parity, so that the compiler sees that the copies into one
+    // do not alias the reads of the other and does not wait for them
+    __shared__ __attribute__((aligned(16))) _Float16 sB0[IMG];
+    __shared__ __attribute__((aligned(16))) _Float16 sB1[IMG];
 
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
     const int g = lane / 16, c = lane % 16;
@@ -208,8 +285,10 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
     const int t0 = qb * QB;
 
     // key index j: j >= 0 is token j of this call, j < 0 is the ring entry of
-    // absolute position pos0 + j (available for j >= -hist)
-    const int jlo_all = max(t0 - W + 1, -a.hist);
+    // absolute position pos0 + j (available for j >= -hist).  Without a ring
+    // the key blocks are the aligned blocks of the image (the masks drop the
+    // keys before the window).
+    const int jlo_all = RING ? max(t0 - W + 1, -a.hist) : max(t0 - W + 1, 0) / KB * KB;
     const int jhi = min(t0 + QB - 1, T - 1);
     const int nblk_all = (jhi - jlo_all) / KB + 1;
     // this split's share of the key blocks (may be empty)
@@ -250,16 +329,14 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
         }
         return x;
     };
-    // staging.  K: rows 16 i + tid / 16 (i < 4), chunk tid % 16 (16 bytes).
-    // V: key pair kp = tid % 32 (keys 2 kp, 2 kp + 1), chunks tid / 32 + 8 i
-    // (i < 2), so the transposed LDS writes of a wave fill 32 consecutive
-    // dwords of one row.  Within each 32-key step the keys of V^T are stored
-    // in the order the S^T tiles hold them (key 32 j + 16 u + 4 g + e at
-    // position 32 j + 8 g + 4 u + e), so a lane's 8 keys of a step are one
-    // 16-byte read.
+    // Ring calls stage each block through registers.  K: rows 16 i + tid / 16
+    // (i < 4), chunk tid % 16 (16 bytes).  V: key pair kp = tid % 32 (keys
+    // 2 kp, 2 kp + 1), chunks tid / 32 + 8 i (i < 2), so the transposed LDS
+    // writes of a wave fill 32 consecutive dwords of one row (keys in the
+    // vperm order).
     const int kch = tid % 16, krw = tid / 16;
     const int kp = tid % 32, vch = tid / 32;
-    const int kq = 2 * kp, vpos = (kq & 32) | (((kq >> 2) & 3) << 3) | (((kq >> 4) & 1) << 2) | (kq & 3);
+    const int vpos = vperm(2 * kp);
     uint4 pk[4], pv[4];
     auto load_block = [&](int j0) {
 #pragma unroll
@@ -267,17 +344,35 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) pv[i] = fetch(vd, vcd, j0 + 2 * kp + (i & 1), vch + 8 * (i >> 1));
     };
-    auto store_block = [&](int buf) {
+    auto store_block = [&](_Float16* dst) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4*>(&sK[buf][(16 * i + krw) * KLD + kch * 8]) = pk[i];
+            *reinterpret_cast<uint4*>(&dst[(16 * i + krw) * KLD + kch * 8]) = pk[i];
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2) {
             const H8 lo = __builtin_bit_cast(H8, pv[2 * i2]), hi = __builtin_bit_cast(H8, pv[2 * i2 + 1]);
             const int d0 = (vch + 8 * i2) * 8;
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<unsigned*>(&sV[buf][(d0 + e) * VLD + vpos]) = pack_h2(lo[e], hi[e]);
+                *reinterpret_cast<unsigned*>(&dst[KIMG + (d0 + e) * VLD + vpos]) = pack_h2(lo[e], hi[e]);
+        }
+    };
+    // Other calls copy the block's image (written by swa_prep in the LDS
+    // layout) straight into LDS with direct-to-LDS loads: 38 pieces of 1 KB,
+    // wave w taking pieces w, w + 4, ...; lane l moves bytes 16 l .. 16 l + 15
+    // of a piece.  No registers, no VALU work, no LDS writes by the waves.
+    constexpr int kPieces = IMG * 2 / 1024;
+    static_assert(IMG * 2 % 1024 == 0, "whole 1 KB pieces");
+    const char* img = RING ? nullptr
+                           : reinterpret_cast<const char*>(a.img + (b * a.Hkv + hk) * (long)a.NKB * IMG) + lane * 16;
+    auto copy_block = [&](int j0, _Float16* dst) {
+        const char* src = img + (long)(j0 / KB) * (IMG * 2);
+#pragma unroll
+        for (int ii = 0; ii < (kPieces + 3) / 4; ++ii) {
+            const int i = wave + 4 * ii;
+            if (i < kPieces)
+                __builtin_amdgcn_global_load_lds(src + i * 1024,
+                                                 (lds_void*)(reinterpret_cast<char*>(dst) + i * 1024), 16, 0, 0);
         }
     };
 
@@ -297,23 +392,36 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
     float m[2] = {kNegBig, kNegBig}, l[2] = {0.f, 0.f};
 
     if (nblk > 0) {
-        load_block(jlo);
-        store_block(0);
+        if (RING) {
+            load_block(jlo);
+            store_block(sB0);
+        } else {
+            copy_block(jlo, sB0);
+        }
     }
-    // Retire the query-fragment loads here: left outstanding into the loop,
-    // the in-order load counter would make every block's first use of a
-    // fragment also wait for that block's prefetch loads.
+    // Retire the query-fragment loads (and the first block's copies) here:
+    // left outstanding into the loop, the in-order load counter would make
+    // every block's first use of a fragment also wait for that block's
+    // prefetch loads.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
-    for (int bi = 0; bi < nblk; ++bi) {
-        const int j0 = jlo + bi * KB, buf = bi & 1;
-        if (bi + 1 < nblk) load_block(j0 + KB);
+    // one key block from buffer BUF while the next one is fetched into the
+    // other buffer; the loop below alternates the buffers at compile time
+    auto run_block = [&](auto bufc, int bi) {
+        constexpr int BUF = decltype(bufc)::value;
+        _Float16* const cur = BUF ? sB1 : sB0;
+        _Float16* const nxt = BUF ? sB0 : sB1;
+        const int j0 = jlo + bi * KB;
+        if (bi + 1 < nblk) {
+            if (RING) load_block(j0 + KB);
+            else copy_block(j0 + KB, nxt);
+        }
 
         // does any query of this wave see a key of this block?
         const bool live = qa < T && j0 <= qa + 31 && j0 + KB - 1 >= qa - W + 1;
         if (live) {
-            const _Float16* kt_base = &sK[buf][c * KLD + 8 * g];
+            const _Float16* kt_base = &cur[c * KLD + 8 * g];
             f32x4 st[4][2];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) st[kt][0] = st[kt][1] = zero4();
@@ -369,7 +477,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
                     for (int dt = 0; dt < 8; ++dt) acc[dt][qt] *= alpha;
                 }
             }
-            const _Float16* vt_base = &sV[buf][c * VLD + 8 * g];
+            const _Float16* vt_base = &cur[KIMG + c * VLD + 8 * g];
 #pragma unroll
             for (int j2 = 0; j2 < 2; ++j2) {
 #pragma unroll
@@ -380,8 +488,16 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
                 }
             }
         }
-        if (bi + 1 < nblk) store_block(buf ^ 1);
+        if (RING) {
+            if (bi + 1 < nblk) store_block(nxt);
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+        }
         __syncthreads();
+    };
+    for (int bi = 0; bi < nblk; bi += 2) {
+        run_block(std::integral_constant<int, 0>{}, bi);
+        if (bi + 1 < nblk) run_block(std::integral_constant<int, 1>{}, bi + 1);
     }
 
     if (a.ns == 1) {
@@ -501,10 +617,21 @@ static size_t swa_part_bytes(int B, int T, int Hq, int ns) {
     return items * QB * (SD + 2) * sizeof(float);
 }
 
+// K and V of one call: rows [B][Hkv][T][d] each (ring calls), or the block
+// image [B][Hkv][NKB][IMG] (other calls)
+static size_t swa_kv_bytes(int B, int T, int Hkv, bool ring) {
+    if (ring) return (size_t)2 * B * Hkv * T * SD * sizeof(_Float16);
+    const size_t nkb = (size_t)(T + KB - 1) / KB;
+    return (size_t)B * Hkv * nkb * IMG * sizeof(_Float16);
+}
+
 size_t swa_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int window) {
-    // the largest split count any call of these sizes can use (full history)
+    (void)D;  // 128
+    // the larger K/V layout and the largest split count any call of these
+    // sizes can use (full history)
     const int ns = swa_splits(B, T, Hq, window, (long long)window, true);
-    return (size_t)B * T * (Hq + 2 * (size_t)Hkv) * D * sizeof(_Float16) +
+    return (size_t)B * T * Hq * SD * sizeof(_Float16) +
+           std::max(swa_kv_bytes(B, T, Hkv, true), swa_kv_bytes(B, T, Hkv, false)) +
            swa_part_bytes(B, T, Hq, ns);
 }
 
@@ -512,30 +639,37 @@ hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache
                       long long pos0, float* o, int B, int T, int Hq, int Hkv, int D, int window,
                       float rope_base, void* ws, hipStream_t stream) {
     (void)D;  // 128 (checked by the caller)
+    const int R = window - 1;
+    const bool ring = k_cache && R > 0;
+    const int NKB = (T + KB - 1) / KB;
     _Float16* wq = static_cast<_Float16*>(ws);
-    _Float16* wk = wq + (size_t)B * Hq * T * SD;
+    _Float16* wk = wq + (size_t)B * Hq * T * SD;  // ring calls: rows of K, then of V
     _Float16* wv = wk + (size_t)B * Hkv * T * SD;
+    _Float16* img = wk;                           // other calls: the block image
+    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(wk) + swa_kv_bytes(B, T, Hkv, ring));
 
     PrepArgs p;
     p.q = static_cast<const uint16_t*>(q);
     p.k = static_cast<const uint16_t*>(k);
     p.v = static_cast<const uint16_t*>(v);
-    p.wq = wq, p.wk = wk, p.wv = wv;
+    p.wq = wq, p.wk = wk, p.wv = wv, p.img = img;
     p.pos0 = pos0;
     p.qscale = (float)(1.4426950408889634 / 11.313708498984761);  // log2(e) / sqrt(128)
     p.B = B, p.T = T, p.Hq = Hq, p.Hkv = Hkv;
+    p.blocked = ring ? 0 : 1;
+    p.NKB = NKB;
     for (int i = 0; i < SD / 2; ++i)
         p.rev[i] = std::pow((double)rope_base, -2.0 * i / SD) / (2.0 * 3.141592653589793);
-    const long items = (long)B * T * (Hq + 2 * Hkv) * (SD / 8);
+    const long items = ring ? (long)B * T * (Hq + 2 * Hkv) * (SD / 8)
+                            : (long)B * NKB * KB * (Hq + Hkv) * (SD / 8) + (long)B * Hkv * NKB * 8 * (SD / 8);
     hipLaunchKernelGGL(swa_prep, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     profile_mark(stream);
     if (e != hipSuccess) return e;
 
-    const int R = window - 1;
-    const bool ring = k_cache && R > 0;
     AttnArgs a;
-    a.q = wq, a.k = wk, a.v = wv;
+    a.q = wq, a.k = wk, a.v = wv, a.img = img;
+    a.NKB = NKB;
     a.kc = ring ? static_cast<const _Float16*>(k_cache) : nullptr;
     a.vc = ring ? static_cast<const _Float16*>(v_cache) : nullptr;
     a.o = o;
@@ -545,7 +679,7 @@ hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache
     a.nqb = (T + QB - 1) / QB;
     a.pmod = (int)(pos0 % a.R);
     a.ns = swa_splits(B, T, Hq, window, pos0, ring);
-    a.part = reinterpret_cast<float*>(wv + (size_t)B * Hkv * T * SD);
+    a.part = part;
     const long nall = (long)a.nqb * a.ns * Hq * B;
     a.flat = nall <= 0x7fffffffL;
     const dim3 grid = a.flat ? dim3((unsigned)nall) : dim3((unsigned)(a.nqb * a.ns), (unsigned)Hq, (unsigned)B);
