@@ -645,7 +645,7 @@ def time_backward(gdn, args, dev):
     torch.cuda.synchronize()
     ms = a.elapsed_time(e) / n
     kms = kernel_times(gdn, call, n, nmax=6)
-    names = ["prep (bwd_prep)", "forward chain (bwd_fwd_chain)", "reverse chain (bwd_bwd_chain)",
+    names = ["prep (bwd_prep)", "forward and reverse chains side by side (bwd_chains)",
              "gradients (bwd_grads)"]
     nch = B * H * ((T + 63) // 64)
     fl = BWD_FLOPS_PER_CHUNK_HEAD * nch

@@ -34,10 +34,13 @@
 //                  tiles, Ti = (I + A)^-1 (blocked), W, U and the chain
 //                  operands M1 = Ti^T P^T, M2 = Ti^T diag(e) K (so that
 //                  dR = M1 dO + M2 G) and transposed row operands;
-//   bwd_fwd_chain  per (b, h, 16-column state slice), chunks in order: stores
-//                  every chunk's start state and Delta;
-//   bwd_bwd_chain  per (b, h, 16-column slice), chunks in reverse: stores every
-//                  chunk's end gradient G and dR, writes dS_0;
+//   bwd_chains     two independent chains in one launch, side by side on the
+//                  chip (neither reads what the other writes):
+//                  the forward chain per (b, h, 16-column state slice), chunks
+//                  in order, stores every chunk's start state and Delta;
+//                  the reverse chain per (b, h, 16-column slice), chunks in
+//                  reverse, stores every chunk's end gradient G and dR and
+//                  writes dS_0;
 //   bwd_grads      per chunk, in parallel: dq, dk, dv, dbeta, dg.
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -426,12 +429,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_prep(const BwdArgs a) {
 // fragments, one chunk ahead.
 constexpr int CW = 16;  // state columns per chain workgroup
 
-// 1D grid of nser * ns workgroups -> (series n, slice).  Workgroups are dealt
-// to the 8 XCDs round-robin; when the series count is a multiple of 8, all
-// slices of one series land on one XCD so the chunk operands they all read are
-// shared in its L2 (a bijection onto [0, nser) x [0, ns) exactly then).
-__device__ __forceinline__ void slice_of(int ns, int nser, long& n, int& sl) {
-    const int L = blockIdx.x;
+// Workgroup L of a chain's nser * ns -> (series n, slice).  Workgroups are
+// dealt to the 8 XCDs round-robin; when the series count is a multiple of 8,
+// all slices of one series land on one XCD so the chunk operands they all read
+// are shared in its L2 (a bijection onto [0, nser) x [0, ns) exactly then).
+__device__ __forceinline__ void slice_of(int L, int ns, int nser, long& n, int& sl) {
     if (nser % 8 == 0) {
         n = (L % 8) + 8 * ((L / 8) / ns);
         sl = (L / 8) % ns;
@@ -455,7 +457,7 @@ __device__ __forceinline__ float ld_vec(const float* p) {
 //   Delta = U - W H            wave w: chunk rows [16 w, 16 w + 16)
 //   H = Gam_C H + (diag(e) K)^T Delta
 template <typename In, int D>
-__global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
+__device__ __forceinline__ void fwd_chain(const BwdArgs& a, int L) {
     constexpr int MT = D / 16, MW = MT / 4;  // row tiles of the slice, per wave
     __shared__ fx4 sH[MT][64];
     __shared__ fx4 sD[4][64];
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
     const int lg = lane >> 4, lc = lane & 15;
     long n;
     int sl;
-    slice_of(D / CW, a.B * a.H, n, sl);
+    slice_of(L, D / CW, a.B * a.H, n, sl);
     const int col = CW * sl + lc;
     fx4 hr[MW];
 #pragma unroll
@@ -562,7 +564,7 @@ __global__ __launch_bounds__(256) void bwd_fwd_chain(const BwdArgs a) {
 //   dR = M1 dO + M2 G                      wave w: chunk rows [16 w, 16 w + 16)
 //   G = Gam_C G + (diag(Gam) Q)^T dO - (diag(b Gam) K)^T dR
 template <typename In, int D>
-__global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
+__device__ __forceinline__ void bwd_chain(const BwdArgs& a, int L) {
     constexpr int MT = D / 16, MW = MT / 4;
     __shared__ fx4 sG[MT][64];
     __shared__ fx4 sR[4][64];
@@ -571,7 +573,7 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
     const int lg = lane >> 4, lc = lane & 15;
     long n;
     int sl;
-    slice_of(D / CW, a.B * a.H, n, sl);
+    slice_of(L, D / CW, a.B * a.H, n, sl);
     const long b = n / a.H;
     const int h = (int)(n % a.H), T = a.T;
     const int col = CW * sl + lc;
@@ -699,6 +701,18 @@ __global__ __launch_bounds__(256) void bwd_bwd_chain(const BwdArgs a) {
             for (int e = 0; e < 4; ++e)
                 a.dstate0[(n * D + 16 * (wave + 4 * j) + 4 * lg + e) * D + col] = gr[j][e];
     }
+}
+
+// The two chains in one launch of 2 nser ns workgroups: the first half runs the
+// forward chain, the second the reverse chain.  Neither reads what the other
+// writes, so at 8K (128 workgroups each) they fill the 256 CUs together
+// instead of half of them one after the other.
+template <typename In, int D>
+__global__ __launch_bounds__(256) void bwd_chains(const BwdArgs a) {
+    const int nw = a.B * a.H * (D / CW);
+    const int L = blockIdx.x;
+    if (L < nw) fwd_chain<In, D>(a, L);
+    else bwd_chain<In, D>(a, L - nw);
 }
 
 // ---------------------------------------------------------------------------
@@ -1053,16 +1067,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
 
 template <typename In, int D>
 hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
-    const dim3 gc((unsigned)a.NC, (unsigned)a.H, (unsigned)a.B), gs((unsigned)(a.B * a.H * (D / CW)));
+    const dim3 gc((unsigned)a.NC, (unsigned)a.H, (unsigned)a.B), gs((unsigned)(2 * a.B * a.H * (D / CW)));
     hipLaunchKernelGGL((bwd_prep<In, D>), gc, dim3(64 * (D / 16)), 0, stream, a);
     hipError_t e = hipGetLastError();
     profile_mark(stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_fwd_chain<In, D>), gs, dim3(256), 0, stream, a);
-    e = hipGetLastError();
-    profile_mark(stream);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_bwd_chain<In, D>), gs, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_chains<In, D>), gs, dim3(256), 0, stream, a);
     e = hipGetLastError();
     profile_mark(stream);
     if (e != hipSuccess) return e;
@@ -1074,13 +1084,14 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// The reverse chain's outputs reuse the forward chain's operands, which nothing
-// reads after the forward chain: the end gradients G (D^2 floats per chunk)
-// take the place of W and U (2 BC D >= D^2 for D <= 128), dR that of
-// (diag(e) K)^T (BC D each).
+// Per chunk: gates, the P, L o K K^T and M1 tiles, W, U, Delta, M2 and the
+// three transposed row operands (BC x D each), the start state and the end
+// gradient (D x D each), dR (BC x D).  The two chains run at the same time, so
+// the reverse chain's outputs (G, dR) cannot take the place of the forward
+// chain's operands.
 size_t backward_workspace_bytes(int B, int T, int H, int D) {
     const size_t NC = (size_t)(T + BC - 1) / BC, chunks = NC * B * H;
-    const size_t per = SCN * BC + 3 * BC * BC + 7 * (size_t)BC * D + (size_t)D * D;
+    const size_t per = SCN * BC + 3 * BC * BC + 8 * (size_t)BC * D + 2 * (size_t)D * D;
     return chunks * per * sizeof(float);
 }
 
@@ -1101,15 +1112,15 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, int dtyp
     a.lkk = p, p += chunks * BC * BC;
     a.w = p, p += chunks * BC * D;
     a.u = p, p += chunks * BC * D;
-    a.gs = a.w;  // over W and U (dead after the forward chain)
     a.dl = p, p += chunks * BC * D;
     a.hs = p, p += chunks * (size_t)D * D;
     a.m1 = p, p += chunks * BC * BC;
     a.m2 = p, p += chunks * BC * D;
     a.ekt = p, p += chunks * BC * D;
-    a.dr = a.ekt;  // over (diag(e) K)^T (dead after the forward chain)
     a.qgt = p, p += chunks * BC * D;
-    a.kbt = p;
+    a.kbt = p, p += chunks * BC * D;
+    a.gs = p, p += chunks * (size_t)D * D;
+    a.dr = p;
     if (dtype_bf16)
         return D == 64 ? launch_t<bf16_t, 64>(a, stream) : launch_t<bf16_t, 128>(a, stream);
     return D == 64 ? launch_t<float, 64>(a, stream) : launch_t<float, 128>(a, stream);
