@@ -9,9 +9,10 @@ d = 128 (fp16 operands in the state products), the fp32 prefill at d = 64, and
 the decode step, against the fp64 oracle on the same bytes; the retrieval and
 decay cases are also checked against their closed forms.
 
-Also here: workspaces filled with NaN before the call (a read of workspace bytes
-the call did not write first would poison the outputs), and internal
-allocations on a side stream.
+Also here: workspaces filled with NaN before the call (prefill, stream,
+sliding-window attention and backward; a read of workspace bytes the call did
+not write first would poison the outputs), and internal allocations on a side
+stream.
 """
 import numpy as np
 import pytest
@@ -188,3 +189,59 @@ def test_side_stream_internal_allocations(env):
     del junk
     ro, rs = oracle_sequence(d)
     _check("side stream prefill", o.cpu().numpy(), st.cpu().numpy(), ro, rs, TOL["bf16"])
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,W", [
+    (300, 4, 2, 1000),  # causal; the last key block of the image is partly past T
+    (300, 4, 2, 100),   # band; blocks aligned to 64 keys start before the window
+    (600, 2, 1, 1000),  # small grid: split windows, partials in the workspace
+])
+def test_nan_workspace_swa(env, T, Hq, Hkv, W):
+    """A sliding-window prefill whose workspace holds NaN before the call: the
+    key-block image must be written in full (its rows past T as zeros) before
+    the attention reads it."""
+    gdn, dev = env
+    import torch
+    from oracle import swa as oswa
+    from parity_util import to_dev
+    _note("case NaN workspace swa T=%d Hq=%d Hkv=%d W=%d" % (T, Hq, Hkv, W))
+    x = gdn_inputs.swa_inputs(1, T, Hq, Hkv, 128, seed=T + W + 1)
+    t = {n: to_dev(x[n], "bf16", dev) for n in ("q", "k", "v")}
+    need = gdn.swa_workspace_bytes(1, T, Hq, Hkv, 128, W)
+    ws = torch.full(((need + 3) // 4,), float("nan"), dtype=torch.float32, device=dev)
+    o = gdn.swa_prefill(t["q"], t["k"], t["v"], W, workspace=ws.view(torch.uint8)).cpu().numpy()
+    f = lambda a: gdn_inputs.to_f64(a, "bf16")
+    ref = oswa.swa(f(x["q"]), f(x["k"]), f(x["v"]), W)
+    e = rel_err(o, ref)
+    _note("NaN workspace swa rel err %.3e" % e)
+    assert np.isfinite(o).all()
+    assert e <= TOL["bf16"]
+
+
+def test_nan_workspace_backward(env):
+    """A backward call whose workspace holds NaN before the call (ragged last
+    chunk, initial state, both chains side by side)."""
+    gdn, dev = env
+    import torch
+    from oracle import backward as obwd
+    from parity_util import to_dev
+    _note("case NaN workspace backward T=150 H=2 d=128 f32")
+    B, T, H, dim = 1, 150, 2, 128
+    d = gdn_inputs.random_inputs(B, T, H, dim, dim, dtype="f32", seed=1501, state_std=0.1)
+    r = np.random.default_rng(np.random.SeedSequence([1501, 0xBAC]))
+    d_o = r.standard_normal((B, T, H, dim)).astype(np.float32)
+    d_s = r.standard_normal((B, H, dim, dim)).astype(np.float32)
+    need = gdn.backward_workspace_bytes(B, T, H, dim, dim)
+    ws = torch.full(((need + 3) // 4,), float("nan"), dtype=torch.float32, device=dev)
+    x = stage(d, dev)
+    got = gdn.backward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state0"],
+                       to_dev(d_o, "f32", dev), to_dev(d_s, "f32", dev), workspace=ws.view(torch.uint8))
+    f = lambda a: gdn_inputs.to_f64(a, "f32")
+    ref = obwd.backward(f(d["q"]), f(d["k"]), f(d["v"]), d["g"], d["beta"], d["state0"], d_o, d_s)
+    for gk, rk in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dg", "dg"), ("dbeta", "dbeta"),
+                   ("dstate", "dstate0")):
+        x_ = got[gk].cpu().numpy()
+        e = rel_err(x_, ref[rk])
+        _note("NaN workspace backward %s rel err %.3e" % (gk, e))
+        assert np.isfinite(x_).all(), gk
+        assert e <= TOL["f32"], (gk, e)
