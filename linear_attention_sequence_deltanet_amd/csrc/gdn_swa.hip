@@ -423,16 +423,23 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
         const bool live = qa < T && j0 <= qa + 31 && j0 + KB - 1 >= qa - W + 1;
         if (live) {
             const _Float16* kt_base = &cur[c * KLD + 8 * g];
-            f32x4 st[4][2];
+            // Scores relative to the reference max, S - ref: the first product of
+            // each tile starts from -ref (ref = m, or 0 before the query's first key)
+            float ref[2];
+            f32x4 nref[2];
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) st[kt][0] = st[kt][1] = zero4();
+            for (int qt = 0; qt < 2; ++qt) {
+                ref[qt] = m[qt] > 0.5f * kNegBig ? m[qt] : 0.f;
+                nref[qt] = f32x4{-ref[qt], -ref[qt], -ref[qt], -ref[qt]};
+            }
+            f32x4 st[4][2];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
                     const H8 ka = *reinterpret_cast<const H8*>(kt_base + 16 * kt * KLD + 32 * s);
-                    st[kt][0] = MF::k32(ka, qf[0][s], st[kt][0]);
-                    st[kt][1] = MF::k32(ka, qf[1][s], st[kt][1]);
+                    st[kt][0] = MF::k32(ka, qf[0][s], s == 0 ? nref[0] : st[kt][0]);
+                    st[kt][1] = MF::k32(ka, qf[1][s], s == 0 ? nref[1] : st[kt][1]);
                 }
             }
             // masks: key j = j0 + 16 kt + 4 g + e, query t = qa + 16 qt + c
@@ -451,7 +458,12 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
                         }
                 }
             }
-            H8 pb[2][2];
+            // The reference m moves only when a block's max passes it by more
+            // than kSlack (base 2): the probabilities then stay below 2^kSlack,
+            // well inside fp16, and most blocks need neither a rescale nor a
+            // shift of the scores.
+            bool grew[2];
+            float dlt[2];
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
                 float mx = st[0][qt][0];
@@ -459,28 +471,36 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
                 for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) mx = fmaxf(mx, st[kt][qt][e]);
-                // The reference m moves only when a block's max passes it by more
-                // than kSlack (base 2): the probabilities then stay below
-                // 2^kSlack, well inside fp16, and most blocks need no rescale.
-                const float bm = qmax(mx);
-                const bool grew = bm > m[qt] + kSlack;
-                const float mn = grew ? bm : m[qt];
-                const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);
-                m[qt] = mn;
+                const float bm = qmax(mx);  // block max - ref
+                grew[qt] = bm > (m[qt] - ref[qt]) + kSlack;
+                dlt[qt] = grew[qt] ? bm : 0.f;
+            }
+            if (__builtin_amdgcn_ballot_w64(grew[0] || grew[1])) {
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) {
+                    // 1 where the reference stays; 0 before the query's first key
+                    const float alpha = __builtin_amdgcn_exp2f((m[qt] - ref[qt]) - dlt[qt]);
+                    m[qt] = grew[qt] ? ref[qt] + dlt[qt] : m[qt];
+                    l[qt] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) acc[dt][qt] *= alpha;
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt) st[kt][qt] -= dlt[qt];
+                }
+            }
+            H8 pb[2][2];
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
                 float ps = 0.f;
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float p = __builtin_amdgcn_exp2f(st[kt][qt][e] - mn);
+                        const float p = __builtin_amdgcn_exp2f(st[kt][qt][e]);
                         ps += p;
                         pb[qt][kt >> 1][4 * (kt & 1) + e] = static_cast<_Float16>(p);
                     }
-                l[qt] = l[qt] * alpha + ps;
-                if (__builtin_amdgcn_ballot_w64(grew)) {  // rescale only when a max moved
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) acc[dt][qt] *= alpha;
-                }
+                l[qt] += ps;
             }
             const _Float16* vt_base = &cur[KIMG + c * VLD + 8 * g];
 #pragma unroll
