@@ -225,18 +225,12 @@ struct AttnArgs {
     int flat;  // 1-D grid, items dealt to the XCDs in contiguous ranges
 };
 
-// max / sum over the 4 lanes c, c+16, c+32, c+48 (one query of an S^T tile)
+// max over the 4 lanes c, c+16, c+32, c+48 (one query of an S^T tile)
 __device__ __forceinline__ float qmax(float s) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
     s = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float qsum(float s) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-    s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Raw buffer loads: the descriptor's byte bound returns zeros past the valid
@@ -390,7 +384,14 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
     f32x4 acc[8][2];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[dt][0] = acc[dt][1] = zero4();
-    float m[2] = {kNegBig, kNegBig}, l[2] = {0.f, 0.f};
+    float m[2] = {kNegBig, kNegBig};
+    // row sums of P^T on the matrix cores: a product with a tile of ones gives
+    // every row of ls[qt] the sum over the block's keys of each query's fp16
+    // probabilities (the same rounded values that weight V)
+    f32x4 ls[2] = {zero4(), zero4()};
+    H8 ones;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ones[i] = static_cast<_Float16>(1.f);
 
     if (nblk > 0) {
         if (RING) {
@@ -481,7 +482,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
                     // 1 where the reference stays; 0 before the query's first key
                     const float alpha = __builtin_amdgcn_exp2f((m[qt] - ref[qt]) - dlt[qt]);
                     m[qt] = grew[qt] ? ref[qt] + dlt[qt] : m[qt];
-                    l[qt] *= alpha;
+                    ls[qt] *= alpha;
 #pragma unroll
                     for (int dt = 0; dt < 8; ++dt) acc[dt][qt] *= alpha;
 #pragma unroll
@@ -491,16 +492,12 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
             H8 pb[2][2];
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
-                float ps = 0.f;
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float p = __builtin_amdgcn_exp2f(st[kt][qt][e]);
-                        ps += p;
-                        pb[qt][kt >> 1][4 * (kt & 1) + e] = static_cast<_Float16>(p);
-                    }
-                l[qt] += ps;
+                    for (int e = 0; e < 4; ++e)
+                        pb[qt][kt >> 1][4 * (kt & 1) + e] =
+                            static_cast<_Float16>(__builtin_amdgcn_exp2f(st[kt][qt][e]));
             }
             const _Float16* vt_base = &cur[KIMG + c * VLD + 8 * g];
 #pragma unroll
@@ -511,6 +508,8 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
                     acc[dt][0] = MF::k32(va, pb[0][j2], acc[dt][0]);
                     acc[dt][1] = MF::k32(va, pb[1][j2], acc[dt][1]);
                 }
+                ls[0] = MF::k32(ones, pb[0][j2], ls[0]);
+                ls[1] = MF::k32(ones, pb[1][j2], ls[1]);
             }
         }
         if (RING) {
@@ -530,7 +529,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
             const int t = qa + 16 * qt + c;
-            const float inv = 1.0f / qsum(l[qt]);
+            const float inv = 1.0f / ls[qt][0];
             if (t < T) {
                 float* op = a.o + ((b * T + t) * a.Hq + h) * (long)SD + 4 * g;
 #pragma unroll
@@ -547,7 +546,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
             const int qi = 32 * wave + 16 * qt + c;
-            const float lt = qsum(l[qt]);
+            const float lt = ls[qt][0];
             float* op = a.part + (item * QB + qi) * (long)SD + 4 * g;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt)
