@@ -773,7 +773,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
     float* const sQ = smem + BC * LD;
     float* const sPL = smem + 2 * BC * LD;
     float* const sAS = sPL + BC * LC;
-    __shared__ float sgam[BC], sGam[BC], se[BC], sb[BC], sdg[BC], sdb[BC], sq1[BC], sk1[BC], sk2[BC];
+    __shared__ float sgam[BC], sGam[BC], se[BC], sb[BC], sdb0[BC];
+    // Partial row and column sums: per lower tile of phase 1a, per wave of phase
+    // 2.  Each partial has one writer and the final sums run in a fixed order,
+    // so dg and dbeta do not depend on the order in which the waves finish.
+    __shared__ float prg[NPAIR][16], prb[NPAIR][16], pcg[NPAIR][16];
+    __shared__ float pq1[NW][BC], pk1[NW][BC], pk2[NW][BC];
     __shared__ float red[NW];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -795,7 +800,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
         se[tid] = scp[BC + tid];
         sb[tid] = scp[2 * BC + tid];
         sgam[tid] = scp[3 * BC + tid];
-        sdg[tid] = 0.f, sdb[tid] = 0.f, sq1[tid] = 0.f, sk1[tid] = 0.f, sk2[tid] = 0.f;
     }
     // ---- phase 0: dO, Delta, dR into LDS; dv = b dR and the row dots dR.v
     constexpr int NF = BC * D / 4 / NT;  // float4 per thread per matrix
@@ -858,7 +862,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
         float x = vdp[i];
         x = group16_sum(x);
         if (D / 4 == 32) x = xor16_add(x);
-        if (lane % (D / 4) == 0) atomicAdd(&sdb[(tid + NT * i) / (D / 4)], x);
+        if (lane % (D / 4) == 0) sdb0[(tid + NT * i) / (D / 4)] = x;  // one lane per row
     }
 
     // the first H0 / G fragments of phase 1b, loaded ahead of phase 1a
@@ -909,13 +913,13 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
                 const float x = dpm * pv[p][e] + dam * sb[r] * lv[p][e];
                 cs += x;
                 const float rs = group16_sum(x), d3 = group16_sum(dam * lv[p][e]);
-                if (lc == 0) atomicAdd(&sdg[r], rs), atomicAdd(&sdb[r], d3);
+                if (lc == 0) prg[pi][4 * lg + e] = rs, prb[pi][4 * lg + e] = d3;
                 const float L = s <= r ? __expf(sgam[r] - sgam[s]) : 0.f;
                 plt[p][e] = dpm * L;
                 ast[p][e] = dam * sb[r] * L;
             }
             cs = xor32_add(xor16_add(cs));
-            if (lg == 0) atomicAdd(&sdg[s], -cs);
+            if (lg == 0) pcg[pi][lc] = -cs;
         }
     }
 
@@ -1029,7 +1033,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
             const float q1 = group16_sum(x1q[t][e] * qx);
             const float k1 = group16_sum(x1k[t][e] * kx);
             const float k2 = group16_sum(x2k[t][e] * kx);
-            if (lc == 0) atomicAdd(&sq1[r], q1), atomicAdd(&sk1[r], k1), atomicAdd(&sk2[r], k2);
+            if (lc == 0) pq1[wave][r] = q1, pk1[wave][r] = k1, pk2[wave][r] = k2;
             if (t0 + r < T) {
                 const long gi = row0 + r * HD + col;
                 a.dq[gi] = fmaf(sGam[r], x1q[t][e], x2q[t][e]);
@@ -1046,8 +1050,21 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
         float ghs = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) ghs += red[w];
-        const float k1 = sk1[r], k2 = sk2[r];
-        float dgr = sdg[r] + sGam[r] * (sq1[r] - sb[r] * k2) - se[r] * k1;
+        // the partials of row r in a fixed order: lower tiles (tr, sc) with
+        // tr = r / 16 (row sums) or sc = r / 16 (column sums), then the waves
+        float g1 = 0.f, b1 = 0.f;
+#pragma unroll
+        for (int pi = 0; pi < NPAIR; ++pi) {
+            int tr = 0;
+            while ((tr + 1) * (tr + 2) / 2 <= pi) ++tr;
+            const int sc = pi - tr * (tr + 1) / 2;
+            if (tr == r / 16) g1 += prg[pi][r % 16], b1 += prb[pi][r % 16];
+            if (sc == r / 16) g1 += pcg[pi][r % 16];
+        }
+        float q1 = 0.f, k1 = 0.f, k2 = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) q1 += pq1[w][r], k1 += pk1[w][r], k2 += pk2[w][r];
+        float dgr = g1 + sGam[r] * (q1 - sb[r] * k2) - se[r] * k1;
         float ek = se[r] * k1;
         ek = wave_sum(ek);
         if (r == BC - 1) dgr += sGam[BC - 1] * ghs + ek;
@@ -1060,7 +1077,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
         if (t0 + r < T) {
             const long gi = (b * T + t0 + r) * a.H + h;
             a.dg[gi] = dgr;
-            a.dbeta[gi] = sdb[r] - sGam[r] * k2;
+            a.dbeta[gi] = (sdb0[r] + b1) - sGam[r] * k2;
         }
     }
 }

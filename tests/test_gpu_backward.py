@@ -113,3 +113,21 @@ def test_backward_prefill8k_sampled(env):
     d_o, d_s = _upstream(B, T, H, d, seed=8192)
     got, ref, sel = _run(gdn, dev, x, d_o, d_s, heads=[(0, 2), (0, 11)])
     _check("bwd8k", got, ref, TOL["bf16"], sel)
+
+
+def test_backward_bitwise_deterministic(env):
+    """The same backward call twice gives the same bits in every gradient (the
+    cross-wave sums of the gradient kernel run in a fixed order)."""
+    gdn, dev = env
+    import torch
+    _note("case backward determinism")
+    x = gdn_inputs.random_inputs(1, 700, 4, 128, 128, dtype="bf16", seed=700, state_std=0.1)
+    d_o, d_s = _upstream(1, 700, 4, 128, seed=700)
+    t = stage(x, dev)
+    tdo, tds = to_dev(d_o, "f32", dev), to_dev(d_s, "f32", dev)
+    runs = [gdn.backward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["state0"], tdo, tds)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    for k in ("dq", "dk", "dv", "dg", "dbeta", "dstate"):
+        for r in runs[1:]:
+            assert torch.equal(runs[0][k], r[k]), k
