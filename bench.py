@@ -647,6 +647,18 @@ def time_backward(gdn, args, dev):
     kms = kernel_times(gdn, call, n, nmax=6)
     names = ["prep (bwd_prep)", "forward and reverse chains side by side (bwd_chains)",
              "gradients (bwd_grads)"]
+    # the same call with the minimal workspace (the chains one after the other)
+    least = gdn.backward_workspace_bytes(B, T, H, dk, dk, minimal=True)
+    wsm = ws[:least]
+    call_m = lambda: gdn.backward(q, k, v, g, beta, None, d_o, d_s, workspace=wsm)
+    call_m()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(n):
+        call_m()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms_min = a.elapsed_time(e) / n
     nch = B * H * ((T + 63) // 64)
     fl = BWD_FLOPS_PER_CHUNK_HEAD * nch
     tfs = fl / (ms / 1e3) / 1e12
@@ -654,6 +666,9 @@ def time_backward(gdn, args, dev):
                         "q/k/v), fp32 arithmetic",
             "value": B * T / (ms / 1e3), "unit": "tokens/s", "ms_per_call": ms,
             "kernels": [{"kernel": nm, "us": t * 1e3} for nm, t in zip(names, kms)],
+            "workspace_bytes": ws.numel(),
+            "minimal_workspace": {"workspace_bytes": least, "ms_per_call": ms_min,
+                                  "note": "the chains one after the other"},
             "roofline": {"kernel": "whole backward call", "bound": "mfma", "achieved": tfs,
                          "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": tfs / FP32_MFMA_PEAK_TFS, "flops_per_call": fl,

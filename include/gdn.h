@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 /* The enums have int as their underlying type in C++ too, so that any int a C
  * caller passes (valid or not) is a value of the type; in C they are int-sized
@@ -241,12 +241,19 @@ gdn_status gdn_gate_out(const float *o, const void *z, const float *w, void *out
  *
  * q, k, v, g, beta, state_in (or NULL = zeros): the forward's inputs.
  * d_o [B][T][H][d_v] fp32; d_state_out [B][H][d_k][d_v] fp32 or NULL (zero).
- * workspace: at least gdn_backward_workspace_bytes() bytes (it holds per-chunk
- * factors, chunk start states and chunk end gradients; contents ignored).
+ * workspace: per-chunk factors, chunk start states and chunk end gradients
+ * (contents ignored).  With at least gdn_backward_workspace_bytes() bytes the
+ * forward and reverse chunk chains run side by side; with at least
+ * gdn_backward_min_workspace_bytes() (about 3/4 of it at d = 128) they run one
+ * after the other, slower, the reverse chain's outputs reusing space of the
+ * forward chain's operands; less is GDN_ERR_WORKSPACE.  The gradients are the
+ * same bits either way.
  * Arithmetic is fp32 throughout (bf16 inputs are widened exactly).  Sizes and
- * conventions as gdn_prefill; no argument may overlap another.
+ * conventions as gdn_prefill; no argument may overlap another (the workspace
+ * range checked is the part the call uses).
  */
 size_t gdn_backward_workspace_bytes(int B, int T, int H, int dk, int dv);
+size_t gdn_backward_min_workspace_bytes(int B, int T, int H, int dk, int dv);
 gdn_status gdn_backward(const void *q, const void *k, const void *v, gdn_dtype dtype,
                  const float *g, const float *beta, const float *state_in,
                  const float *d_o, const float *d_state_out,

@@ -77,6 +77,8 @@ def _load():
     lib.gdn_gate_out.argtypes = [fp, vp, fp, vp, i, i, i, i, i, vp]
     lib.gdn_backward_workspace_bytes.restype = sz
     lib.gdn_backward_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.gdn_backward_min_workspace_bytes.restype = sz
+    lib.gdn_backward_min_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.gdn_backward.restype = i
     lib.gdn_backward.argtypes = [vp, vp, vp, i, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
                                  i, i, i, i, i, vp, sz, vp]
@@ -440,7 +442,12 @@ def swa_prefill(q, k, v, window, *, rope_base=ROPE_BASE, o=None, workspace=None,
     return o
 
 
-def backward_workspace_bytes(B, T, H, dk, dv) -> int:
+def backward_workspace_bytes(B, T, H, dk, dv, minimal=False) -> int:
+    """Workspace bytes of backward(): the size that runs the forward and
+    reverse chains side by side, or with minimal=True the smallest accepted
+    (the chains then run one after the other)."""
+    if minimal:
+        return int(_lib.gdn_backward_min_workspace_bytes(B, T, H, dk, dv))
     return int(_lib.gdn_backward_workspace_bytes(B, T, H, dk, dv))
 
 

@@ -339,7 +339,12 @@ gdn_status gdn_swa_prefill(const void* q, const void* k, const void* v, float* o
 
 size_t gdn_backward_workspace_bytes(int B, int T, int H, int dk, int dv) {
     if (check_sizes(B, T, H, dk, dv, GDN_F32) != GDN_OK) return 0;
-    return gdn::backward_workspace_bytes(B, T, H, dk);
+    return gdn::backward_workspace_bytes(B, T, H, dk, false);
+}
+
+size_t gdn_backward_min_workspace_bytes(int B, int T, int H, int dk, int dv) {
+    if (check_sizes(B, T, H, dk, dv, GDN_F32) != GDN_OK) return 0;
+    return gdn::backward_workspace_bytes(B, T, H, dk, true);
 }
 
 gdn_status gdn_backward(const void* q, const void* k, const void* v, gdn_dtype dtype, const float* g,
@@ -356,7 +361,8 @@ gdn_status gdn_backward(const void* q, const void* k, const void* v, gdn_dtype d
                           d_state_in, workspace};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return GDN_ERR_ALIGN;
-    const size_t need = gdn::backward_workspace_bytes(B, T, H, dk_);
+    const size_t full = gdn::backward_workspace_bytes(B, T, H, dk_, false);
+    const size_t need = workspace_bytes >= full ? full : gdn::backward_workspace_bytes(B, T, H, dk_, true);
     if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
     const size_t el = dtype == GDN_BF16 ? 2 : 4;
     const size_t tok = (size_t)B * T * H, sb = (size_t)B * H * dk_ * dv_ * 4;
@@ -377,7 +383,7 @@ gdn_status gdn_backward(const void* q, const void* k, const void* v, gdn_dtype d
     gdn::profile_begin(static_cast<hipStream_t>(stream));
     return launch_status(gdn::launch_backward(q, k, v, dtype == GDN_BF16, g, beta, state_in, d_o,
                                               d_state_out, dq, dk, dv, dg, dbeta, d_state_in, B,
-                                              T, H, dk_, workspace,
+                                              T, H, dk_, workspace, need,
                                               static_cast<hipStream_t>(stream)));
 }
 

@@ -703,16 +703,18 @@ __device__ __forceinline__ void bwd_chain(const BwdArgs& a, int L) {
     }
 }
 
-// The two chains in one launch of 2 nser ns workgroups: the first half runs the
-// forward chain, the second the reverse chain.  Neither reads what the other
-// writes, so at 8K (128 workgroups each) they fill the 256 CUs together
-// instead of half of them one after the other.
+// The chains: with which = 0, one launch of 2 nser ns workgroups, the first
+// half running the forward chain and the second the reverse chain.  Neither
+// reads what the other writes, so at 8K (128 workgroups each) they fill the
+// 256 CUs together instead of half of them one after the other.  With the
+// smaller workspace the reverse chain's outputs take the place of operands of
+// the forward chain, and the two run as separate launches (which = 1, then 2).
 template <typename In, int D>
-__global__ __launch_bounds__(256) void bwd_chains(const BwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_chains(const BwdArgs a, int which) {
     const int nw = a.B * a.H * (D / CW);
     const int L = blockIdx.x;
-    if (L < nw) fwd_chain<In, D>(a, L);
-    else bwd_chain<In, D>(a, L - nw);
+    if (which == 1 || (which == 0 && L < nw)) fwd_chain<In, D>(a, L);
+    else bwd_chain<In, D>(a, which == 0 ? L - nw : L);
 }
 
 // ---------------------------------------------------------------------------
@@ -1083,16 +1085,26 @@ __global__ __launch_bounds__(64 * (D / 16)) void bwd_grads(const BwdArgs a) {
 }
 
 template <typename In, int D>
-hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
-    const dim3 gc((unsigned)a.NC, (unsigned)a.H, (unsigned)a.B), gs((unsigned)(2 * a.B * a.H * (D / CW)));
+hipError_t launch_t(const BwdArgs& a, bool side_by_side, hipStream_t stream) {
+    const unsigned nw = (unsigned)(a.B * a.H * (D / CW));
+    const dim3 gc((unsigned)a.NC, (unsigned)a.H, (unsigned)a.B);
     hipLaunchKernelGGL((bwd_prep<In, D>), gc, dim3(64 * (D / 16)), 0, stream, a);
     hipError_t e = hipGetLastError();
     profile_mark(stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_chains<In, D>), gs, dim3(256), 0, stream, a);
-    e = hipGetLastError();
-    profile_mark(stream);
-    if (e != hipSuccess) return e;
+    if (side_by_side) {
+        hipLaunchKernelGGL((bwd_chains<In, D>), dim3(2 * nw), dim3(256), 0, stream, a, 0);
+        e = hipGetLastError();
+        profile_mark(stream);
+        if (e != hipSuccess) return e;
+    } else {
+        for (int which = 1; which <= 2; ++which) {
+            hipLaunchKernelGGL((bwd_chains<In, D>), dim3(nw), dim3(256), 0, stream, a, which);
+            e = hipGetLastError();
+            profile_mark(stream);
+            if (e != hipSuccess) return e;
+        }
+    }
     hipLaunchKernelGGL((bwd_grads<In, D>), gc, dim3(64 * (D / 16)), 0, stream, a);
     e = hipGetLastError();
     profile_mark(stream);
@@ -1102,13 +1114,16 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 // Per chunk: gates, the P, L o K K^T and M1 tiles, W, U, Delta, M2 and the
-// three transposed row operands (BC x D each), the start state and the end
-// gradient (D x D each), dR (BC x D).  The two chains run at the same time, so
-// the reverse chain's outputs (G, dR) cannot take the place of the forward
-// chain's operands.
-size_t backward_workspace_bytes(int B, int T, int H, int D) {
+// three transposed row operands (BC x D each), the start state (D x D) and,
+// with the full workspace, the end gradient G (D x D) and dR (BC x D) in their
+// own space, so that the two chains can run at the same time.  The minimal
+// workspace puts G over W and U (2 BC D >= D^2 for D <= 128) and dR over
+// (diag(e) K)^T, which only the forward chain reads, and runs the chains one
+// after the other.
+size_t backward_workspace_bytes(int B, int T, int H, int D, bool minimal) {
     const size_t NC = (size_t)(T + BC - 1) / BC, chunks = NC * B * H;
-    const size_t per = SCN * BC + 3 * BC * BC + 8 * (size_t)BC * D + 2 * (size_t)D * D;
+    const size_t per = SCN * BC + 3 * BC * BC + 7 * (size_t)BC * D + (size_t)D * D +
+                       (minimal ? 0 : (size_t)BC * D + (size_t)D * D);
     return chunks * per * sizeof(float);
 }
 
@@ -1116,7 +1131,8 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, int dtyp
                            const float* g, const float* beta, const float* state0,
                            const float* d_o, const float* d_state, float* dq, float* dk, float* dv,
                            float* dg, float* dbeta, float* dstate0, int B, int T, int H, int D,
-                           void* ws, hipStream_t stream) {
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+    const bool side_by_side = ws_bytes >= backward_workspace_bytes(B, T, H, D, false);
     BwdArgs a;
     a.q = q, a.k = k, a.v = v, a.g = g, a.beta = beta, a.state0 = state0, a.d_o = d_o;
     a.d_state = d_state, a.dq = dq, a.dk = dk, a.dv = dv, a.dg = dg, a.dbeta = dbeta;
@@ -1136,11 +1152,18 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, int dtyp
     a.ekt = p, p += chunks * BC * D;
     a.qgt = p, p += chunks * BC * D;
     a.kbt = p, p += chunks * BC * D;
-    a.gs = p, p += chunks * (size_t)D * D;
-    a.dr = p;
+    if (side_by_side) {
+        a.gs = p, p += chunks * (size_t)D * D;
+        a.dr = p;
+    } else {
+        a.gs = a.w;    // over W and U
+        a.dr = a.ekt;  // over (diag(e) K)^T
+    }
     if (dtype_bf16)
-        return D == 64 ? launch_t<bf16_t, 64>(a, stream) : launch_t<bf16_t, 128>(a, stream);
-    return D == 64 ? launch_t<float, 64>(a, stream) : launch_t<float, 128>(a, stream);
+        return D == 64 ? launch_t<bf16_t, 64>(a, side_by_side, stream)
+                       : launch_t<bf16_t, 128>(a, side_by_side, stream);
+    return D == 64 ? launch_t<float, 64>(a, side_by_side, stream)
+                   : launch_t<float, 128>(a, side_by_side, stream);
 }
 
 }  // namespace gdn

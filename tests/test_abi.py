@@ -287,7 +287,7 @@ def _bwd(lib, B=1, T=100, H=2, d=128, dtype=0, **over):
         [ctypes.c_int] * 5 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     return lib.gdn_backward(a["q"], a["k"], a["v"], dtype, a["g"], a["beta"], a["sin"], a["do"],
                             a["dsout"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dsin"],
-                            B, T, H, d, d, a["ws"], GB, None)
+                            B, T, H, d, d, a["ws"], a.get("ws_bytes", GB), None)
 
 
 def test_backward_errors(lib):
@@ -304,5 +304,15 @@ def test_backward_errors(lib):
     assert _bwd(lib, ws=BW["dg"]) == ALIAS
     assert _bwd(lib, ws=None) == WS
     lib.gdn_backward_workspace_bytes.restype = ctypes.c_size_t
-    assert lib.gdn_backward_workspace_bytes(1, 8192, 16, 128, 128) > 0
+    lib.gdn_backward_min_workspace_bytes.restype = ctypes.c_size_t
+    full = lib.gdn_backward_workspace_bytes(1, 8192, 16, 128, 128)
+    least = lib.gdn_backward_min_workspace_bytes(1, 8192, 16, 128, 128)
+    # per chunk x head: 4 x 64 + 3 x 64^2 + 7 x 64 x 128 + 128^2 floats, and with the
+    # chains side by side another 64 x 128 + 128^2 (their end gradients and dR)
+    per = 4 * 64 + 3 * 64 * 64 + 7 * 64 * 128 + 128 * 128
+    assert least == 2048 * per * 4
+    assert full == 2048 * (per + 64 * 128 + 128 * 128) * 4
     assert lib.gdn_backward_workspace_bytes(1, 8192, 16, 96, 96) == 0
+    assert lib.gdn_backward_min_workspace_bytes(1, 8192, 16, 96, 96) == 0
+    # between the two sizes is accepted (chains one after the other), below is not
+    assert _bwd(lib, ws_bytes=lib.gdn_backward_min_workspace_bytes(1, 100, 2, 128, 128) - 1) == WS

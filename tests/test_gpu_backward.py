@@ -131,3 +131,31 @@ def test_backward_bitwise_deterministic(env):
     for k in ("dq", "dk", "dv", "dg", "dbeta", "dstate"):
         for r in runs[1:]:
             assert torch.equal(runs[0][k], r[k]), k
+
+
+def test_backward_minimal_workspace(env):
+    """With the smallest accepted workspace the two chunk chains run one after
+    the other, the reverse chain's outputs reusing the forward chain's operand
+    space: the same bits as with the full workspace, and the oracle's values."""
+    gdn, dev = env
+    import torch
+    _note("case backward, minimal workspace")
+    B, T, H, d = 1, 300, 3, 128
+    x = gdn_inputs.random_inputs(B, T, H, d, d, dtype="bf16", seed=301, state_std=0.1)
+    d_o, d_s = _upstream(B, T, H, d, seed=301)
+    t = stage(x, dev)
+    tdo, tds = to_dev(d_o, "f32", dev), to_dev(d_s, "f32", dev)
+    least = gdn.backward_workspace_bytes(B, T, H, d, d, minimal=True)
+    full = gdn.backward_workspace_bytes(B, T, H, d, d)
+    assert 0 < least < full
+    ws_small = torch.full(((least + 3) // 4,), float("nan"), dtype=torch.float32, device=dev)
+    small = gdn.backward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["state0"], tdo, tds,
+                         workspace=ws_small.view(torch.uint8)[:least])
+    big = gdn.backward(t["q"], t["k"], t["v"], t["g"], t["beta"], t["state0"], tdo, tds)
+    torch.cuda.synchronize()
+    for k in ("dq", "dk", "dv", "dg", "dbeta", "dstate"):
+        assert torch.equal(small[k], big[k]), k
+    got = {k: v.cpu().numpy() for k, v in small.items()}
+    f = lambda a: gdn_inputs.to_f64(a, "bf16")
+    ref = obwd.backward(f(x["q"]), f(x["k"]), f(x["v"]), x["g"], x["beta"], x["state0"], d_o, d_s)
+    _check("bwd minimal workspace", got, ref, TOL["bf16"])
