@@ -622,15 +622,17 @@ __global__ __launch_bounds__(256) void swa_cache(const _Float16* wk, const _Floa
 }  // namespace
 
 // Key-range splits per query block: one while the (query block, head, batch)
-// grid already fills the chip twice, else enough to reach that, each split
-// keeping at least 4 key blocks (at most 32 splits).
+// grid already fills the chip twice (two workgroups on each of the 256 CUs),
+// else as many as still fit in that one round -- one split more would start a
+// second round for a few workgroups -- each split keeping at least 4 key
+// blocks (at most 32 splits).
 int swa_splits(int B, int T, int Hq, int window, long long pos0, bool ring) {
     const long base = (long)((T + QB - 1) / QB) * Hq * B;
     if (base >= 512) return 1;
     const long hist = ring ? std::min<long long>(window - 1, pos0) : 0;
     const long keys = std::min<long>((long)window + QB, (long)T + hist + QB);
     const long maxblk = keys / KB + 1;
-    long ns = (512 + base - 1) / base;
+    long ns = 512 / base;
     ns = std::min<long>(ns, std::max<long>(1, maxblk / 4));
     return (int)std::max<long>(1, std::min<long>(ns, 32));
 }
