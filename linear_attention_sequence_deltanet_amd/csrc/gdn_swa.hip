@@ -64,32 +64,9 @@ constexpr float kSlack = 8.f;  // log2 of the largest probability the softmax le
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Position of key kk (< 64) of a block inside each V^T row: within a 32-key
-// step, key 32 j + 16 u + 4 g + e sits at 32 j + 8 g + 4 u + e, the order in
-// which the S^T tiles hold the keys, so that a lane's 8 keys of a step are one
-// 16-byte read.
-__device__ __forceinline__ int vperm(int kk) {
-    return (kk & 32) | (((kk >> 2) & 3) << 3) | (((kk >> 4) & 1) << 2) | (kk & 3);
-}
-
-// ---------------------------------------------------------------------------
-// swa_prep: one thread per 8 features (4 rotation pairs) of one (b, t, head)
-// of q, k or v.
-// ---------------------------------------------------------------------------
-struct PrepArgs {
-    const uint16_t* q;  // bf16 [B][T][Hq][d]
-    const uint16_t* k;  // bf16 [B][T][Hkv][d]
-    const uint16_t* v;
-    _Float16* wq;       // [B][Hq][T][d]
-    _Float16* wk;       // row layout: [B][Hkv][T][d]
-    _Float16* wv;
-    _Float16* img;      // block layout: [B][Hkv][NKB][IMG], the LDS image of each key block
-    long long pos0;
-    float qscale;
-    int B, T, Hq, Hkv;
-    int blocked, NKB;   // blocked: K and V go to img (keys T .. 64 NKB - 1 as zeros)
-    double rev[SD / 2];  // base^(-2i/d) / (2 pi): rotation of pair i per position, in turns
-};
+// V^T key order: inside each V^T row, key 32 j + 16 u + 4 g + e of a block sits
+// at 32 j + 8 g + 4 u + e, the order in which the S^T tiles hold the keys, so
+// that a lane's 8 keys of a step are one 16-byte read.
 
 __device__ __forceinline__ void bf16x8_to_f32(const uint4 u, float (&f)[8]) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -100,22 +77,54 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 u, float (&f)[8]) {
     }
 }
 
+struct PrepArgs {
+    const uint16_t* q;   // bf16 [B][T][Hq][d]
+    const uint16_t* k;   // bf16 [B][T][Hkv][d]
+    const uint16_t* v;
+    const _Float16* kc;  // ring calls: the ring caches [B][Hkv][R][d] (rotated keys, values)
+    const _Float16* vc;
+    _Float16* wq;        // [B][Hq][T][d]
+    _Float16* wk;        // ring calls: the call's rotated keys and values as rows
+    _Float16* wv;        //   [B][Hkv][T][d], which the ring update copies
+    _Float16* img;       // [B][Hkv][NKB][IMG]: the LDS image of each key block
+    long long pos0;
+    float qscale;
+    int B, T, Hq, Hkv;
+    int NKB, jb0;        // image block jb holds the keys j = jb0 + 64 jb .. + 63 (jb0 <= 0)
+    int hist, R, pmod;   // keys j in [-hist, 0) come from ring slot (pmod + j) mod R
+    double rev[SD / 2];  // base^(-2i/d) / (2 pi): rotation of pair i per position, in turns
+};
+
+// Where key j (relative to the call's first token) comes from: the call's own
+// token j (0 <= j < T), the ring (-hist <= j < 0), or nowhere (zeros).
+enum KeySrc { kFromCall, kFromRing, kZero };
+__device__ __forceinline__ KeySrc key_src(const PrepArgs& a, int j) {
+    return j >= 0 ? (j < a.T ? kFromCall : kZero) : (j >= -a.hist ? kFromRing : kZero);
+}
+__device__ __forceinline__ long ring_row(const PrepArgs& a, long bh, int j) {
+    int slot = a.pmod + j;
+    slot += slot < 0 ? a.R : 0;  // j >= -hist >= -R
+    return (bh * a.R + slot) * SD;
+}
+
+// ---------------------------------------------------------------------------
+// swa_prep: the key-block image of the call's window (keys from the ring, then
+// the call's own) and the rotated, scaled queries.
+//   V^T items (first, in waves of their own, so that their longer latency
+//     overlaps the rest): item (b, h, jb, r, part) writes 16-byte chunk r < 8
+//     (the 8 keys at positions 8 r .. 8 r + 7 of the V^T key order) of the 8
+//     feature rows part 8 .. part 8 + 7 of block jb's V^T tile: 8 row loads, a
+//     transpose in registers, 8 16-byte stores.
+//   Row items (b, t, head, part): query t of the call, or key row t of the
+//     image (key j = jb0 + t), rotated at its absolute position.
+// Ring calls also write the call's rotated keys and values as rows.
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void swa_prep(const PrepArgs a) {
     long item = (long)blockIdx.x * 256 + threadIdx.x;
     constexpr int G = SD / 8;
-    // Items: with the block layout first the V^T chunks (in waves of their own,
-    // and first so that their longer latency overlaps the rest), then the rows
-    // of q and k; otherwise the rows of q, k and v.  Token rows: T, or with the
-    // block layout the whole last key block.
-    const int heads = a.Hq + (a.blocked ? 1 : 2) * a.Hkv;
-    const int TR = a.blocked ? a.NKB * KB : a.T;
-    const long nvt = a.blocked ? (long)a.B * a.Hkv * a.NKB * 8 * G : 0;
+    const int TR = a.NKB * KB;  // image rows per key-value head
+    const long nvt = (long)a.B * a.Hkv * a.NKB * 8 * G;
     if (item < nvt) {
-        // V^T of key block jb in the image: item (b, h, jb, r, part) writes
-        // 16-byte chunk r < 8 (the 8 keys at positions 8 r .. 8 r + 7 of the
-        // vperm order) of the 8 feature rows part 8 .. part 8 + 7: 8 row loads,
-        // a transpose in registers, 8 16-byte stores.  Keys past the sequence
-        // are zeros.
         long rest = item;
         const int part = (int)(rest % G);
         rest /= G;
@@ -125,21 +134,29 @@ __global__ __launch_bounds__(256) void swa_prep(const PrepArgs a) {
         rest /= a.NKB;
         const int h = (int)(rest % a.Hkv);
         const long b = rest / a.Hkv;
+        const long bh = b * a.Hkv + h;
         H8 col[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int tt = jb * KB + 32 * (r >> 2) + 16 * (i >> 2) + 4 * (r & 3) + (i & 3);
-            float x[8];
-            if (tt < a.T) {
-                bf16x8_to_f32(*reinterpret_cast<const uint4*>(a.v + ((b * a.T + tt) * a.Hkv + h) * SD + part * 8), x);
+            const int j = a.jb0 + jb * KB + 32 * (r >> 2) + 16 * (i >> 2) + 4 * (r & 3) + (i & 3);
+            const KeySrc src = key_src(a, j);
+            if (src == kFromRing) {
+                col[i] = *reinterpret_cast<const H8*>(a.vc + ring_row(a, bh, j) + part * 8);
             } else {
+                float x[8];
+                if (src == kFromCall) {
+                    bf16x8_to_f32(*reinterpret_cast<const uint4*>(a.v + ((b * a.T + j) * a.Hkv + h) * SD + part * 8), x);
+                } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = 0.f;
+                    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) col[i][e] = static_cast<_Float16>(x[e]);
+                if (src == kFromCall && a.wv)
+                    *reinterpret_cast<H8*>(a.wv + (bh * a.T + j) * SD + part * 8) = col[i];
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) col[i][e] = static_cast<_Float16>(x[e]);
         }
-        _Float16* dst = a.img + ((b * a.Hkv + h) * a.NKB + jb) * (long)IMG + KIMG + 8 * r;
+        _Float16* dst = a.img + (bh * a.NKB + jb) * (long)IMG + KIMG + 8 * r;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             H8 row;
@@ -150,62 +167,66 @@ __global__ __launch_bounds__(256) void swa_prep(const PrepArgs a) {
         return;
     }
     item -= nvt;
-    if (item >= (long)a.B * TR * heads * G) return;
+    // query items (b, t, head, part) over the call's T tokens, then key items
+    // (b, t, kv head, part) over the image's TR rows
+    const long nq = (long)a.B * a.T * a.Hq * G;
+    const bool isq = item < nq;
+    if (!isq) item -= nq;
+    const int rows = isq ? a.T : TR, nh = isq ? a.Hq : a.Hkv;
+    if (!isq && item >= (long)a.B * TR * a.Hkv * G) return;
     const int part = (int)(item % G);
     long rest = item / G;
-    const int hh = (int)(rest % heads);
-    rest /= heads;
-    const int t = (int)(rest % TR);
-    const long b = rest / TR;
-    const bool pad = t >= a.T;  // block layout only: a key row past the sequence, zeros
-    if (pad && hh < a.Hq) return;
+    const int hh = (int)(rest % nh) + (isq ? 0 : a.Hq);
+    rest /= nh;
+    const int t = (int)(rest % rows);
+    const long b = rest / rows;
 
-    const uint16_t* src;
-    _Float16* dst;
-    int kind;  // 0 q, 1 k, 2 v
-    if (hh < a.Hq) {
-        kind = 0;
-        src = a.q + ((b * a.T + t) * a.Hq + hh) * SD;
-        dst = a.wq + ((b * a.Hq + hh) * (long)a.T + t) * SD;
-    } else if (hh < a.Hq + a.Hkv) {
-        kind = 1;
-        const int h = hh - a.Hq;
-        src = a.k + ((b * a.T + t) * a.Hkv + h) * SD;
-        dst = a.blocked ? a.img + ((b * a.Hkv + h) * a.NKB + t / KB) * (long)IMG + (t % KB) * KLD
-                        : a.wk + ((b * a.Hkv + h) * (long)a.T + t) * SD;
-    } else {
-        kind = 2;  // row layout only
-        const int h = hh - a.Hq - a.Hkv;
-        src = a.v + ((b * a.T + t) * a.Hkv + h) * SD;
-        dst = a.wv + ((b * a.Hkv + h) * (long)a.T + t) * SD;
-    }
     float x[8];
-    if (pad) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    H8 out;
+    if (isq) {
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(a.q + ((b * a.T + t) * a.Hq + hh) * SD + part * 8), x);
     } else {
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(src + part * 8), x);
-    }
-    if (kind < 2 && !pad) {
-        const double p = (double)(a.pos0 + t);
+        const int h = hh - a.Hq, j = a.jb0 + t;
+        const long bh = b * a.Hkv + h;
+        _Float16* dst = a.img + (bh * a.NKB + t / KB) * (long)IMG + (t % KB) * KLD + part * 8;
+        const KeySrc src = key_src(a, j);
+        if (src != kFromCall) {
+            // ring keys are stored rotated; keys outside the window's range are zeros
+            H8 z;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const double turns = p * a.rev[part * 4 + i];
-            const float fr = (float)(turns - floor(turns));  // [0, 1)
-            const float c = __builtin_amdgcn_cosf(fr), s = __builtin_amdgcn_sinf(fr);
-            const float x0 = x[2 * i], x1 = x[2 * i + 1];
-            x[2 * i] = x0 * c - x1 * s;
-            x[2 * i + 1] = x0 * s + x1 * c;
+            for (int i = 0; i < 8; ++i) z[i] = static_cast<_Float16>(0.f);
+            *reinterpret_cast<H8*>(dst) =
+                src == kFromRing ? *reinterpret_cast<const H8*>(a.kc + ring_row(a, bh, j) + part * 8) : z;
+            return;
         }
-        if (kind == 0) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] *= a.qscale;
-        }
+        bf16x8_to_f32(*reinterpret_cast<const uint4*>(a.k + ((b * a.T + j) * a.Hkv + h) * SD + part * 8), x);
     }
-    H8 h;
+    // rotation at the absolute position of token tt of the call
+    const int tt = hh < a.Hq ? t : a.jb0 + t;
+    const double p = (double)(a.pos0 + tt);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = static_cast<_Float16>(x[i]);
-    *reinterpret_cast<H8*>(dst + part * 8) = h;
+    for (int i = 0; i < 4; ++i) {
+        const double turns = p * a.rev[part * 4 + i];
+        const float fr = (float)(turns - floor(turns));  // [0, 1)
+        const float c = __builtin_amdgcn_cosf(fr), s = __builtin_amdgcn_sinf(fr);
+        const float x0 = x[2 * i], x1 = x[2 * i + 1];
+        x[2 * i] = x0 * c - x1 * s;
+        x[2 * i + 1] = x0 * s + x1 * c;
+    }
+    if (hh < a.Hq) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] *= a.qscale;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = static_cast<_Float16>(x[i]);
+    if (hh < a.Hq) {
+        *reinterpret_cast<H8*>(a.wq + ((b * a.Hq + hh) * (long)a.T + t) * SD + part * 8) = out;
+    } else {
+        const int h = hh - a.Hq;
+        const long bh = b * a.Hkv + h;
+        *reinterpret_cast<H8*>(a.img + (bh * a.NKB + t / KB) * (long)IMG + (t % KB) * KLD + part * 8) = out;
+        if (a.wk) *reinterpret_cast<H8*>(a.wk + (bh * a.T + tt) * SD + part * 8) = out;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -213,15 +234,10 @@ __global__ __launch_bounds__(256) void swa_prep(const PrepArgs a) {
 // ---------------------------------------------------------------------------
 struct AttnArgs {
     const _Float16* q;   // [B][Hq][T][d], scaled, rotated
-    const _Float16* k;   // ring calls: [B][Hkv][T][d], rotated
-    const _Float16* v;   // ring calls: [B][Hkv][T][d]
-    const _Float16* img; // other calls: [B][Hkv][NKB][IMG], each key block's LDS image
-    const _Float16* kc;  // ring [B][Hkv][R][d] (positions < pos0), or null
-    const _Float16* vc;
+    const _Float16* img; // [B][Hkv][NKB][IMG]: block jb holds the keys jb0 + 64 jb .. + 63
     float* o;            // [B][T][Hq][d]
     float* part;         // ns > 1: partial O [B][Hq][nqb][ns][QB][d], then (m, l) [..][QB][2]
-    long long pos0;
-    int T, Hq, Hkv, W, R, hist, nqb, pmod, ns, NKB;
+    int T, Hq, Hkv, W, hist, nqb, ns, NKB, jb0;
     int flat;  // 1-D grid, items dealt to the XCDs in contiguous ranges
 };
 
@@ -233,25 +249,6 @@ __device__ __forceinline__ float qmax(float s) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Raw buffer loads: the descriptor's byte bound returns zeros past the valid
-// rows, so the staging loads need no lane tests or branches.
-using rsrc_t = __amdgpu_buffer_rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 buf_load16(rsrc_t r, unsigned off) {
-    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-    return uint4{x[0], x[1], x[2], x[3]};
-}
-constexpr unsigned kOob = 0x80000000u;  // an offset past every descriptor's bound
-
-__device__ __forceinline__ unsigned pack_h2(_Float16 a, _Float16 b) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    const h2 p = {a, b};
-    return __builtin_bit_cast(unsigned, p);
-}
-
-template <bool RING>
 __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
     // two key-block buffers, each the K tile then the V^T tile; two arrays, not
     // one indexed by parity, so that the compiler sees that the copies into one
@@ -279,11 +276,12 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
     const int T = a.T, W = a.W;
     const int t0 = qb * QB;
 
-    // key index j: j >= 0 is token j of this call, j < 0 is the ring entry of
-    // absolute position pos0 + j (available for j >= -hist).  Without a ring
-    // the key blocks are the aligned blocks of the image (the masks drop the
-    // keys before the window).
-    const int jlo_all = RING ? max(t0 - W + 1, -a.hist) : max(t0 - W + 1, 0) / KB * KB;
+    // Key index j: token j of this call for j >= 0, the ring entry of absolute
+    // position pos0 + j for -hist <= j < 0.  The key blocks are the blocks of
+    // the image, aligned to jb0; the masks drop keys outside a query's window
+    // and before -hist.
+    const int jfirst = max(t0 - W + 1, -a.hist);
+    const int jlo_all = a.jb0 + (jfirst - a.jb0) / KB * KB;
     const int jhi = min(t0 + QB - 1, T - 1);
     const int nblk_all = (jhi - jlo_all) / KB + 1;
     // this split's share of the key blocks (may be empty)
@@ -292,76 +290,15 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
     const int nblk = b_hi - b_lo;
     const int jlo = jlo_all + b_lo * KB;
 
-    const _Float16* kbase = a.k + ((b * a.Hkv + hk) * (long)T) * SD;
-    const _Float16* vbase = a.v + ((b * a.Hkv + hk) * (long)T) * SD;
-    const _Float16* kcb = RING ? a.kc + ((b * a.Hkv + hk) * (long)a.R) * SD : nullptr;
-    const _Float16* vcb = RING ? a.vc + ((b * a.Hkv + hk) * (long)a.R) * SD : nullptr;
-
-    // Row j of K or V: token j of this call for j >= 0 (rows past jhi read as
-    // zeros through the descriptor bound), ring slot (pos0 + j) mod R for j < 0
-    // (pmod = pos0 mod R).  With the ring, both loads are issued and OR'ed: the
-    // one whose rows do not hold j returns zeros.
-    const rsrc_t kd = make_rsrc(kbase, (unsigned)(jhi + 1) * SD * 2);
-    const rsrc_t vd = make_rsrc(vbase, (unsigned)(jhi + 1) * SD * 2);
-    const rsrc_t kcd = make_rsrc(RING ? kcb : kbase, RING ? (unsigned)a.R * SD * 2 : 0u);
-    const rsrc_t vcd = make_rsrc(RING ? vcb : vbase, RING ? (unsigned)a.R * SD * 2 : 0u);
-    auto offs = [&](int j, int chunk, unsigned& cur, unsigned& ring) {
-        cur = j >= 0 ? (unsigned)j * SD * 2 + chunk * 16 : kOob;
-        ring = kOob;
-        if (RING && j < 0) {
-            int slot = a.pmod + j;
-            slot += slot < 0 ? a.R : 0;  // j >= -hist >= -R
-            ring = (unsigned)slot * SD * 2 + chunk * 16;
-        }
-    };
-    auto fetch = [&](rsrc_t cd, rsrc_t rd, int j, int chunk) -> uint4 {
-        unsigned oc, orr;
-        offs(j, chunk, oc, orr);
-        uint4 x = buf_load16(cd, oc);
-        if (RING) {
-            const uint4 y = buf_load16(rd, orr);
-            x.x |= y.x, x.y |= y.y, x.z |= y.z, x.w |= y.w;
-        }
-        return x;
-    };
-    // Ring calls stage each block through registers.  K: rows 16 i + tid / 16
-    // (i < 4), chunk tid % 16 (16 bytes).  V: key pair kp = tid % 32 (keys
-    // 2 kp, 2 kp + 1), chunks tid / 32 + 8 i (i < 2), so the transposed LDS
-    // writes of a wave fill 32 consecutive dwords of one row (keys in the
-    // vperm order).
-    const int kch = tid % 16, krw = tid / 16;
-    const int kp = tid % 32, vch = tid / 32;
-    const int vpos = vperm(2 * kp);
-    uint4 pk[4], pv[4];
-    auto load_block = [&](int j0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pk[i] = fetch(kd, kcd, j0 + 16 * i + krw, kch);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pv[i] = fetch(vd, vcd, j0 + 2 * kp + (i & 1), vch + 8 * (i >> 1));
-    };
-    auto store_block = [&](_Float16* dst) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4*>(&dst[(16 * i + krw) * KLD + kch * 8]) = pk[i];
-#pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) {
-            const H8 lo = __builtin_bit_cast(H8, pv[2 * i2]), hi = __builtin_bit_cast(H8, pv[2 * i2 + 1]);
-            const int d0 = (vch + 8 * i2) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<unsigned*>(&dst[KIMG + (d0 + e) * VLD + vpos]) = pack_h2(lo[e], hi[e]);
-        }
-    };
-    // Other calls copy the block's image (written by swa_prep in the LDS
-    // layout) straight into LDS with direct-to-LDS loads: 38 pieces of 1 KB,
-    // wave w taking pieces w, w + 4, ...; lane l moves bytes 16 l .. 16 l + 15
-    // of a piece.  No registers, no VALU work, no LDS writes by the waves.
+    // A block's image (written by swa_prep in the LDS layout) goes straight
+    // into LDS with direct-to-LDS loads: 38 pieces of 1 KB, wave w taking
+    // pieces w, w + 4, ...; lane l moves bytes 16 l .. 16 l + 15 of a piece.
+    // No registers, no VALU work, no LDS writes by the waves.
     constexpr int kPieces = IMG * 2 / 1024;
     static_assert(IMG * 2 % 1024 == 0, "whole 1 KB pieces");
-    const char* img = RING ? nullptr
-                           : reinterpret_cast<const char*>(a.img + (b * a.Hkv + hk) * (long)a.NKB * IMG) + lane * 16;
+    const char* img = reinterpret_cast<const char*>(a.img + (b * a.Hkv + hk) * (long)a.NKB * IMG) + lane * 16;
     auto copy_block = [&](int j0, _Float16* dst) {
-        const char* src = img + (long)(j0 / KB) * (IMG * 2);
+        const char* src = img + (long)((j0 - a.jb0) / KB) * (IMG * 2);
 #pragma unroll
         for (int ii = 0; ii < (kPieces + 3) / 4; ++ii) {
             const int i = wave + 4 * ii;
@@ -393,14 +330,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) ones[i] = static_cast<_Float16>(1.f);
 
-    if (nblk > 0) {
-        if (RING) {
-            load_block(jlo);
-            store_block(sB0);
-        } else {
-            copy_block(jlo, sB0);
-        }
-    }
+    if (nblk > 0) copy_block(jlo, sB0);
     // Retire the query-fragment loads (and the first block's copies) here:
     // left outstanding into the loop, the in-order load counter would make
     // every block's first use of a fragment also wait for that block's
@@ -415,10 +345,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
         _Float16* const cur = BUF ? sB1 : sB0;
         _Float16* const nxt = BUF ? sB0 : sB1;
         const int j0 = jlo + bi * KB;
-        if (bi + 1 < nblk) {
-            if (RING) load_block(j0 + KB);
-            else copy_block(j0 + KB, nxt);
-        }
+        if (bi + 1 < nblk) copy_block(j0 + KB, nxt);
 
         // does any query of this wave see a key of this block?
         const bool live = qa < T && j0 <= qa + 31 && j0 + KB - 1 >= qa - W + 1;
@@ -444,12 +371,13 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
                 }
             }
             // masks: key j = j0 + 16 kt + 4 g + e, query t = qa + 16 qt + c
-            const bool full = j0 + KB - 1 <= qa && (qa + 31) - j0 < W && j0 + KB - 1 <= jhi;
+            const bool full =
+                j0 + KB - 1 <= qa && (qa + 31) - j0 < W && j0 + KB - 1 <= jhi && j0 >= -a.hist;
             if (!full) {
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) {
                     const int t = qa + 16 * qt + c;
-                    const int lo_ok = t - W + 1, hi_ok = min(t, jhi);  // keys j in [lo_ok, hi_ok]
+                    const int lo_ok = max(t - W + 1, -a.hist), hi_ok = min(t, jhi);  // keys j in [lo_ok, hi_ok]
 #pragma unroll
                     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -512,11 +440,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
                 ls[1] = MF::k32(ones, pb[1][j2], ls[1]);
             }
         }
-        if (RING) {
-            if (bi + 1 < nblk) store_block(nxt);
-        } else {
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
-        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
         __syncthreads();
     };
     for (int bi = 0; bi < nblk; bi += 2) {
@@ -546,6 +470,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
             const int qi = 32 * wave + 16 * qt + c;
+            if (t0 + qi >= T) continue;  // the combine reads queries t < T only
             const float lt = ls[qt][0];
             float* op = a.part + (item * QB + qi) * (long)SD + 4 * g;
 #pragma unroll
@@ -643,22 +568,25 @@ static size_t swa_part_bytes(int B, int T, int Hq, int ns) {
     return items * QB * (SD + 2) * sizeof(float);
 }
 
-// K and V of one call: rows [B][Hkv][T][d] each (ring calls), or the block
-// image [B][Hkv][NKB][IMG] (other calls)
-static size_t swa_kv_bytes(int B, int T, int Hkv, bool ring) {
-    if (ring) return (size_t)2 * B * Hkv * T * SD * sizeof(_Float16);
-    const size_t nkb = (size_t)(T + KB - 1) / KB;
-    return (size_t)B * Hkv * nkb * IMG * sizeof(_Float16);
+// Key blocks of a call's image: the call's own keys and, for ring calls, the
+// history before them, rounded out to whole blocks
+static int swa_img_blocks(int T, int hist) {
+    const int before = (hist + KB - 1) / KB;
+    return before + (T + KB - 1) / KB;
+}
+
+// the block image [B][Hkv][NKB][IMG], for the longest history (W - 1 keys)
+static size_t swa_img_bytes(int B, int T, int Hkv, int window) {
+    return (size_t)B * Hkv * swa_img_blocks(T, window - 1) * IMG * sizeof(_Float16);
 }
 
 size_t swa_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int window) {
     (void)D;  // 128
-    // the larger K/V layout and the largest split count any call of these
-    // sizes can use (full history)
+    // queries, the image, the call's key and value rows (ring calls), and the
+    // largest split count any call of these sizes can use (full history)
     const int ns = swa_splits(B, T, Hq, window, (long long)window, true);
-    return (size_t)B * T * Hq * SD * sizeof(_Float16) +
-           std::max(swa_kv_bytes(B, T, Hkv, true), swa_kv_bytes(B, T, Hkv, false)) +
-           swa_part_bytes(B, T, Hq, ns);
+    return (size_t)B * T * Hq * SD * sizeof(_Float16) + swa_img_bytes(B, T, Hkv, window) +
+           (size_t)2 * B * Hkv * T * SD * sizeof(_Float16) + swa_part_bytes(B, T, Hq, ns);
 }
 
 hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
@@ -667,52 +595,51 @@ hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache
     (void)D;  // 128 (checked by the caller)
     const int R = window - 1;
     const bool ring = k_cache && R > 0;
-    const int NKB = (T + KB - 1) / KB;
+    const int hist = ring ? (int)std::min<long long>(R, pos0) : 0;
+    const int NKB = swa_img_blocks(T, hist);
+    const int jb0 = -KB * ((hist + KB - 1) / KB);
     _Float16* wq = static_cast<_Float16*>(ws);
-    _Float16* wk = wq + (size_t)B * Hq * T * SD;  // ring calls: rows of K, then of V
+    _Float16* img = wq + (size_t)B * Hq * T * SD;
+    _Float16* wk = reinterpret_cast<_Float16*>(reinterpret_cast<char*>(img) + swa_img_bytes(B, T, Hkv, window));
     _Float16* wv = wk + (size_t)B * Hkv * T * SD;
-    _Float16* img = wk;                           // other calls: the block image
-    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(wk) + swa_kv_bytes(B, T, Hkv, ring));
+    float* part = reinterpret_cast<float*>(wv + (size_t)B * Hkv * T * SD);
 
     PrepArgs p;
     p.q = static_cast<const uint16_t*>(q);
     p.k = static_cast<const uint16_t*>(k);
     p.v = static_cast<const uint16_t*>(v);
-    p.wq = wq, p.wk = wk, p.wv = wv, p.img = img;
+    p.kc = ring ? static_cast<const _Float16*>(k_cache) : nullptr;
+    p.vc = ring ? static_cast<const _Float16*>(v_cache) : nullptr;
+    p.wq = wq, p.img = img;
+    p.wk = ring ? wk : nullptr;
+    p.wv = ring ? wv : nullptr;
     p.pos0 = pos0;
     p.qscale = (float)(1.4426950408889634 / 11.313708498984761);  // log2(e) / sqrt(128)
     p.B = B, p.T = T, p.Hq = Hq, p.Hkv = Hkv;
-    p.blocked = ring ? 0 : 1;
-    p.NKB = NKB;
+    p.NKB = NKB, p.jb0 = jb0;
+    p.hist = hist, p.R = R > 0 ? R : 1;
+    p.pmod = (int)(pos0 % p.R);
     for (int i = 0; i < SD / 2; ++i)
         p.rev[i] = std::pow((double)rope_base, -2.0 * i / SD) / (2.0 * 3.141592653589793);
-    const long items = ring ? (long)B * T * (Hq + 2 * Hkv) * (SD / 8)
-                            : (long)B * NKB * KB * (Hq + Hkv) * (SD / 8) + (long)B * Hkv * NKB * 8 * (SD / 8);
+    const long items =
+        (long)B * Hkv * NKB * 8 * (SD / 8) + (long)B * T * Hq * (SD / 8) + (long)B * NKB * KB * Hkv * (SD / 8);
     hipLaunchKernelGGL(swa_prep, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     profile_mark(stream);
     if (e != hipSuccess) return e;
 
     AttnArgs a;
-    a.q = wq, a.k = wk, a.v = wv, a.img = img;
-    a.NKB = NKB;
-    a.kc = ring ? static_cast<const _Float16*>(k_cache) : nullptr;
-    a.vc = ring ? static_cast<const _Float16*>(v_cache) : nullptr;
+    a.q = wq, a.img = img;
     a.o = o;
-    a.pos0 = pos0;
-    a.T = T, a.Hq = Hq, a.Hkv = Hkv, a.W = window, a.R = R > 0 ? R : 1;
-    a.hist = ring ? (int)std::min<long long>(R, pos0) : 0;
+    a.T = T, a.Hq = Hq, a.Hkv = Hkv, a.W = window;
+    a.hist = hist, a.NKB = NKB, a.jb0 = jb0;
     a.nqb = (T + QB - 1) / QB;
-    a.pmod = (int)(pos0 % a.R);
     a.ns = swa_splits(B, T, Hq, window, pos0, ring);
     a.part = part;
     const long nall = (long)a.nqb * a.ns * Hq * B;
     a.flat = nall <= 0x7fffffffL;
     const dim3 grid = a.flat ? dim3((unsigned)nall) : dim3((unsigned)(a.nqb * a.ns), (unsigned)Hq, (unsigned)B);
-    if (ring)
-        hipLaunchKernelGGL(swa_attn<true>, grid, dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL(swa_attn<false>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(swa_attn, grid, dim3(256), 0, stream, a);
     e = hipGetLastError();
     profile_mark(stream);
     if (e != hipSuccess) return e;

@@ -266,10 +266,12 @@ def test_swa_errors(lib):
     assert _swa(lib, ws=None) == WS
     lib.gdn_swa_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_swa_cache_bytes.restype = ctypes.c_size_t
-    # fp16 q rows, then k and v as 128 key blocks of (64 x 144 + 128 x 80) halves
-    # per kv head (larger than their rows, 2 x 8192 x 128 halves per kv head)
+    # fp16 q rows; k and v as key blocks of (64 x 144 + 128 x 80) halves per kv
+    # head, 128 for the call's keys and 128 for the longest history (8191 keys);
+    # then the call's k and v rows for the ring update (2 x 8192 x 128 halves
+    # per kv head)
     assert lib.gdn_swa_workspace_bytes(1, 8192, 16, 2, 128, 8192) == \
-        8192 * 16 * 128 * 2 + 2 * 128 * (64 * 144 + 128 * 80) * 2
+        8192 * 16 * 128 * 2 + 2 * 256 * (64 * 144 + 128 * 80) * 2 + 2 * 2 * 8192 * 128 * 2
     # a 272-token call against an 8K window splits its key range: partials added
     assert lib.gdn_swa_workspace_bytes(1, 272, 16, 2, 128, 8192) > 272 * 20 * 128 * 2
     assert lib.gdn_swa_cache_bytes(1, 2, 128, 8192) == 2 * 8191 * 128 * 2

@@ -218,6 +218,37 @@ def test_nan_workspace_swa(env, T, Hq, Hkv, W):
     assert e <= TOL["bf16"]
 
 
+def test_nan_workspace_swa_stream(env):
+    """Stream calls (W=100) whose workspace holds NaN before each call: the
+    image's first key block starts before the ring history (37 and 99 keys of
+    it), and its keys there must be written as zeros."""
+    gdn, dev = env
+    import torch
+    from oracle import swa as oswa
+    from parity_util import to_dev
+    B, T, Hq, Hkv, W = 1, 250, 4, 2, 100
+    cuts = (0, 37, 150, T)
+    _note("case NaN workspace swa stream W=%d cuts=%s" % (W, cuts))
+    x = gdn_inputs.swa_inputs(B, T, Hq, Hkv, 128, seed=3701)
+    t = {n: to_dev(x[n], "bf16", dev) for n in ("q", "k", "v")}
+    kc, vc = gdn.swa_new_cache(B, Hkv, 128, W, dev)
+    need = gdn.swa_workspace_bytes(B, T, Hq, Hkv, 128, W)
+    ws = torch.empty(((need + 3) // 4,), dtype=torch.float32, device=dev)
+    outs = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        ws.fill_(float("nan"))
+        piece = {n: t[n][:, a:b].contiguous() for n in ("q", "k", "v")}
+        outs.append(gdn.swa_stream_chunk(piece["q"], piece["k"], piece["v"], kc, vc, a, W,
+                                         workspace=ws.view(torch.uint8)))
+    o = torch.cat(outs, dim=1).cpu().numpy()
+    f = lambda a: gdn_inputs.to_f64(a, "bf16")
+    ref = oswa.swa(f(x["q"]), f(x["k"]), f(x["v"]), W)
+    e = rel_err(o, ref)
+    _note("NaN workspace swa stream rel err %.3e" % e)
+    assert np.isfinite(o).all()
+    assert e <= TOL["bf16"]
+
+
 def test_nan_workspace_backward(env):
     """A backward call whose workspace holds NaN before the call (ragged last
     chunk, initial state, both chains side by side)."""
