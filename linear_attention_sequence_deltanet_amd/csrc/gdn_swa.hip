@@ -486,61 +486,88 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// swa_combine: merge the ns partials of each query (base-2 log-sum-exp):
-//   M = max m_s,  o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One thread per 4 features of one (b, t, head).
+// swa_finish, after the attention:
+//   combine items (ns > 1): merge the ns partials of each query (base-2
+//     log-sum-exp), M = max m_s, o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s;
+//     one thread per 4 features of one (b, t, head).  The splits' loads are
+//     issued together (all m_s, then O_s and l_s eight splits at a time), so a
+//     thread waits for the memory a few times, not 2 ns times.
+//   cache items (ring calls): the call's last n = min(T, R) rotated keys and
+//     values into the ring (slot = absolute position mod R); one thread per 16
+//     bytes.  The ring's old entries are no longer needed: the prep has copied
+//     the history into the image.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void swa_combine(const float* part, float* o, int B, int T,
-                                                   int Hq, int nqb, int ns) {
-    const long item = (long)blockIdx.x * 256 + threadIdx.x;
-    constexpr int G = SD / 4;
-    const long total = (long)B * T * Hq * G;
-    if (item >= total) return;
-    const int part4 = (int)(item % G);
-    long rest = item / G;
-    const int h = (int)(rest % Hq);
-    rest /= Hq;
-    const int t = (int)(rest % T);
-    const long b = rest / T;
-    const int qb = t / QB, qi = t % QB;
-    const long nitems = (long)B * Hq * nqb * ns;
-    const long base = ((b * Hq + h) * nqb + qb) * ns;
-    const float* ml = part + nitems * QB * SD;
-    float M = kNegBig;
-    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, ml[((base + sp) * QB + qi) * 2]);
-    float L = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp = 0; sp < ns; ++sp) {
-        const float2 x = *reinterpret_cast<const float2*>(ml + ((base + sp) * QB + qi) * 2);
-        const float w = __builtin_amdgcn_exp2f(x.x - M);
-        L += w * x.y;
-        const float4 p = *reinterpret_cast<const float4*>(part + ((base + sp) * QB + qi) * (long)SD + 4 * part4);
-        acc.x += w * p.x, acc.y += w * p.y, acc.z += w * p.z, acc.w += w * p.w;
-    }
-    const float inv = 1.0f / L;
-    *reinterpret_cast<float4*>(o + ((b * T + t) * Hq + h) * (long)SD + 4 * part4) =
-        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-}
+constexpr int kMaxSplits = 32;
 
-// ---------------------------------------------------------------------------
-// swa_cache: the call's last min(T, R) rotated keys and values into the ring
-// (slot = absolute position mod R).  One thread per 16 bytes.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void swa_cache(const _Float16* wk, const _Float16* wv,
-                                                 _Float16* kc, _Float16* vc, long long pos0,
-                                                 int B, int T, int Hkv, int R, int n) {
-    const long item = (long)blockIdx.x * 256 + threadIdx.x;
+struct FinishArgs {
+    const float* part;  // partials as the attention writes them
+    float* o;           // [B][T][Hq][d]
+    const _Float16* wk; // the call's rotated keys and values [B][Hkv][T][d]
+    const _Float16* wv;
+    _Float16* kc;       // ring caches [B][Hkv][R][d]
+    _Float16* vc;
+    long long pos0;
+    long ncomb, ncache; // items of each kind (combine items first)
+    int B, T, Hq, Hkv, nqb, ns, R, n;
+};
+
+__global__ __launch_bounds__(256) void swa_finish(const FinishArgs a) {
+    long item = (long)blockIdx.x * 256 + threadIdx.x;
+    if (item < a.ncomb) {
+        constexpr int G = SD / 4;
+        const int part4 = (int)(item % G);
+        long rest = item / G;
+        const int h = (int)(rest % a.Hq);
+        rest /= a.Hq;
+        const int t = (int)(rest % a.T);
+        const long b = rest / a.T;
+        const int qb = t / QB, qi = t % QB, ns = a.ns;
+        const long nitems = (long)a.B * a.Hq * a.nqb * ns;
+        const long base = ((b * a.Hq + h) * a.nqb + qb) * ns;
+        const float* ml = a.part + nitems * QB * SD;
+        // split indices past ns read split ns - 1 again (in bounds) with weight 0
+        float mv[kMaxSplits];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp) mv[sp] = ml[((base + min(sp, ns - 1)) * QB + qi) * 2];
+        float M = mv[0];
+#pragma unroll
+        for (int sp = 1; sp < kMaxSplits; ++sp) M = fmaxf(M, mv[sp]);
+        float L = 0.f;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int s0 = 0; s0 < kMaxSplits; s0 += 8) {
+            if (s0 >= ns) break;
+            float lv[8];
+            float4 pv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const long sl = base + min(s0 + i, ns - 1);
+                lv[i] = ml[(sl * QB + qi) * 2 + 1];
+                pv[i] = *reinterpret_cast<const float4*>(a.part + (sl * QB + qi) * (long)SD + 4 * part4);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float w = s0 + i < ns ? __builtin_amdgcn_exp2f(mv[s0 + i] - M) : 0.f;
+                L += w * lv[i];
+                acc.x += w * pv[i].x, acc.y += w * pv[i].y, acc.z += w * pv[i].z, acc.w += w * pv[i].w;
+            }
+        }
+        const float inv = 1.0f / L;
+        *reinterpret_cast<float4*>(a.o + ((b * a.T + t) * a.Hq + h) * (long)SD + 4 * part4) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        return;
+    }
+    item -= a.ncomb;
+    if (item >= a.ncache) return;
     constexpr int G = SD / 8;
-    const long total = (long)B * Hkv * n * G * 2;
-    if (item >= total) return;
     const int part = (int)(item % G);
     long rest = item / G;
-    const int t = T - n + (int)(rest % n);
-    rest /= n;
+    const int t = a.T - a.n + (int)(rest % a.n);
+    rest /= a.n;
     const int kv = (int)(rest % 2);
     const long bh = rest / 2;  // b * Hkv + h
-    const _Float16* src = (kv ? wv : wk) + (bh * T + t) * (long)SD + part * 8;
-    _Float16* dst = (kv ? vc : kc) + (bh * R + (pos0 + t) % R) * (long)SD + part * 8;
+    const _Float16* src = (kv ? a.wv : a.wk) + (bh * a.T + t) * (long)SD + part * 8;
+    _Float16* dst = (kv ? a.vc : a.kc) + (bh * a.R + (a.pos0 + t) % a.R) * (long)SD + part * 8;
     *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
 }
 
@@ -559,7 +586,7 @@ int swa_splits(int B, int T, int Hq, int window, long long pos0, bool ring) {
     const long maxblk = keys / KB + 1;
     long ns = 512 / base;
     ns = std::min<long>(ns, std::max<long>(1, maxblk / 4));
-    return (int)std::max<long>(1, std::min<long>(ns, 32));
+    return (int)std::max<long>(1, std::min<long>(ns, kMaxSplits));
 }
 
 static size_t swa_part_bytes(int B, int T, int Hq, int ns) {
@@ -643,21 +670,20 @@ hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache
     e = hipGetLastError();
     profile_mark(stream);
     if (e != hipSuccess) return e;
-    if (a.ns > 1) {
-        const long items = (long)B * T * Hq * (SD / 4);
-        hipLaunchKernelGGL(swa_combine, dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
-                           stream, a.part, o, B, T, Hq, a.nqb, a.ns);
-        e = hipGetLastError();
-        profile_mark(stream);
-        if (e != hipSuccess) return e;
-    }
-    if (!ring) return e;
+    if (a.ns == 1 && !ring) return e;
 
-    const int n = std::min(T, R);
-    const long citems = (long)B * Hkv * n * (SD / 8) * 2;
-    hipLaunchKernelGGL(swa_cache, dim3((unsigned)((citems + 255) / 256)), dim3(256), 0, stream,
-                       wk, wv, static_cast<_Float16*>(k_cache), static_cast<_Float16*>(v_cache),
-                       pos0, B, T, Hkv, R, n);
+    FinishArgs f;
+    f.part = part, f.o = o;
+    f.wk = wk, f.wv = wv;
+    f.kc = static_cast<_Float16*>(k_cache), f.vc = static_cast<_Float16*>(v_cache);
+    f.pos0 = pos0;
+    f.B = B, f.T = T, f.Hq = Hq, f.Hkv = Hkv, f.nqb = a.nqb, f.ns = a.ns;
+    f.R = R > 0 ? R : 1;
+    f.n = ring ? std::min(T, R) : 0;
+    f.ncomb = a.ns > 1 ? (long)B * T * Hq * (SD / 4) : 0;
+    f.ncache = ring ? (long)B * Hkv * f.n * (SD / 8) * 2 : 0;
+    const long fitems = f.ncomb + f.ncache;
+    hipLaunchKernelGGL(swa_finish, dim3((unsigned)((fitems + 255) / 256)), dim3(256), 0, stream, f);
     e = hipGetLastError();
     profile_mark(stream);
     return e;
