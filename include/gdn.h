@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 /* The enums have int as their underlying type in C++ too, so that any int a C
  * caller passes (valid or not) is a value of the type; in C they are int-sized
@@ -297,8 +297,12 @@ size_t gdn_swa_workspace_bytes(int B, int T, int Hq, int Hkv, int d, int window)
 
 /*
  * Bytes of EACH of the two ring caches (k_cache, v_cache) a stream of window W
- * needs: [B][Hkv][W - 1][d] fp16 (rotated keys; values).  0 for W < 2 (no
- * history is needed) or invalid sizes.
+ * needs.  They hold the last ceil((W - 1) / 64) + 1 blocks of 64 positions
+ * (position p in block p / 64, block n in slot n mod that count), each as the
+ * fp16 tile the attention copies into on-chip memory: k_cache the rotated keys
+ * (64 rows of 144 halves per slot), v_cache the values transposed (128 rows of
+ * 80 halves).  The layout is the library's own; callers only allocate the
+ * buffers.  0 for W < 2 (no history is needed) or invalid sizes.
  */
 size_t gdn_swa_cache_bytes(int B, int Hkv, int d, int window);
 
@@ -315,10 +319,10 @@ gdn_status gdn_swa_prefill(const void *q, const void *k, const void *v, float *o
  * pos0 .. pos0 + T - 1 (InfiniteVL's streaming keeps a constant-size window
  * cache).  k_cache, v_cache (gdn_swa_cache_bytes() bytes each, or both NULL
  * when W = 1) hold the rotated keys and the values of the positions before
- * pos0, in ring slots (position mod (W - 1)); the call reads the ones inside
- * the window (positions >= max(0, pos0 - W + 1)), then writes its own last
- * min(T, W - 1) tokens into their slots.  Start a stream with pos0 = 0 (the
- * caches' contents are then ignored) and pass pos0 = the number of tokens
+ * pos0, as blocks of 64 positions in ring slots; the call reads the ones inside
+ * the window (positions >= max(0, pos0 - W + 1)), then writes the blocks of its
+ * own tokens that later calls may need into their slots.  Start a stream with
+ * pos0 = 0 (the caches' contents are then ignored) and pass pos0 = the number of tokens
  * already streamed on each following call; successive calls equal one
  * gdn_swa_prefill over the concatenated tokens, up to rounding.
  * No argument may overlap another.

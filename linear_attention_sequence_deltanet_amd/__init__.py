@@ -378,13 +378,15 @@ def swa_cache_bytes(B, Hkv, d, window) -> int:
 
 
 def swa_new_cache(B, Hkv, d, window, device):
-    """(k_cache, v_cache) fp16 ring buffers [B, Hkv, W-1, d] for a stream, or
-    (None, None) when W = 1."""
+    """(k_cache, v_cache) ring buffers of a stream, swa_cache_bytes() bytes each
+    (uint8; the library's block-image layout, written and read only by
+    swa_stream_chunk), or (None, None) when W = 1.  They need no clearing: the
+    first call of a stream (pos0 = 0) reads no history."""
     torch = _torch()
     if window < 2:
         return None, None
-    return tuple(_empty((B, Hkv, window - 1, d), torch.float16, device, None)
-                 for _ in range(2))
+    n = swa_cache_bytes(B, Hkv, d, window)
+    return tuple(_empty((n,), torch.uint8, device, None) for _ in range(2))
 
 
 def _swa_check(q, k, v, o):
@@ -406,9 +408,14 @@ def swa_stream_chunk(q, k, v, k_cache, v_cache, pos0, window, *, rope_base=ROPE_
     bf16; returns o [B, T, Hq, d] fp32."""
     torch = _torch()
     B, T, Hq, Hkv, d = _swa_check(q, k, v, o)
+    if (k_cache is None) != (v_cache is None):
+        raise ValueError("k_cache and v_cache go together")
     if k_cache is not None:
-        _check(k_cache, (B, Hkv, window - 1, d), torch.float16, "k_cache")
-        _check(v_cache, (B, Hkv, window - 1, d), torch.float16, "v_cache")
+        need_c = swa_cache_bytes(B, Hkv, d, window)
+        for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+            if t.numel() * t.element_size() < need_c or not t.is_contiguous():
+                raise ValueError("%s must be a contiguous buffer of at least %d bytes "
+                                 "(swa_new_cache)" % (name, need_c))
     if o is None:
         o = _empty((B, T, Hq, d), torch.float32, q.device, stream)
     need = swa_workspace_bytes(B, T, Hq, Hkv, d, window)

@@ -287,7 +287,7 @@ size_t gdn_swa_workspace_bytes(int B, int T, int Hq, int Hkv, int d, int window)
 
 size_t gdn_swa_cache_bytes(int B, int Hkv, int d, int window) {
     if (B < 1 || Hkv < 1 || d != 128 || window < 2) return 0;
-    return (size_t)B * Hkv * (size_t)(window - 1) * d * 2;
+    return gdn::swa_cache_bytes(B, Hkv, window);
 }
 
 gdn_status gdn_swa_stream_chunk(const void* q, const void* k, const void* v, void* k_cache,

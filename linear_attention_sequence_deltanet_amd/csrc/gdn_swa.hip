@@ -58,7 +58,8 @@ constexpr int KB = 64;         // keys per block
 constexpr int KLD = SD + 16;   // K tile row stride (halves)
 constexpr int VLD = KB + 16;   // V^T tile row stride (halves)
 constexpr int KIMG = KB * KLD;          // K tile of one key block in LDS (halves)
-constexpr int IMG = KIMG + SD * VLD;    // K and V^T tiles of one key block (halves)
+constexpr int VIMG = SD * VLD;          // V^T tile of one key block (halves)
+constexpr int IMG = KIMG + VIMG;        // K and V^T tiles of one key block (halves)
 constexpr float kNegBig = -1e30f;
 constexpr float kSlack = 8.f;  // log2 of the largest probability the softmax lets through
 
@@ -77,47 +78,48 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4 u, float (&f)[8]) {
     }
 }
 
+// Key blocks are aligned to absolute positions: block n holds the positions
+// 64 n .. 64 n + 63.  A call's image starts with the block of its first token,
+// so its first off = pos0 mod 64 rows are keys before the call (from the ring
+// cache, or zeros).  The ring cache holds the last NBR blocks of the stream as
+// images too, block n in slot n mod NBR: the K tiles in k_cache
+// [B][Hkv][NBR][KIMG], the V^T tiles in v_cache [B][Hkv][NBR][VIMG].
 struct PrepArgs {
     const uint16_t* q;   // bf16 [B][T][Hq][d]
     const uint16_t* k;   // bf16 [B][T][Hkv][d]
     const uint16_t* v;
-    const _Float16* kc;  // ring calls: the ring caches [B][Hkv][R][d] (rotated keys, values)
-    const _Float16* vc;
+    const _Float16* rk;  // ring calls: the ring's K tiles
+    const _Float16* rv;  //   and V^T tiles
     _Float16* wq;        // [B][Hq][T][d]
-    _Float16* wk;        // ring calls: the call's rotated keys and values as rows
-    _Float16* wv;        //   [B][Hkv][T][d], which the ring update copies
-    _Float16* img;       // [B][Hkv][NKB][IMG]: the LDS image of each key block
+    _Float16* img;       // [B][Hkv][NKB][IMG]: the call's key blocks
     long long pos0;
     float qscale;
     int B, T, Hq, Hkv;
-    int NKB, jb0;        // image block jb holds the keys j = jb0 + 64 jb .. + 63 (jb0 <= 0)
-    int hist, R, pmod;   // keys j in [-hist, 0) come from ring slot (pmod + j) mod R
+    int NKB, off;        // image row r of block jb is key j = 64 jb + r - off of the call
+    int hist;            // keys j in [-hist, 0) come from the ring
+    int NBR, slot0;      // ring blocks; the slot of the call's first block
     double rev[SD / 2];  // base^(-2i/d) / (2 pi): rotation of pair i per position, in turns
 };
 
 // Where key j (relative to the call's first token) comes from: the call's own
-// token j (0 <= j < T), the ring (-hist <= j < 0), or nowhere (zeros).
+// token j (0 <= j < T), the ring (-hist <= j < 0: the first block's rows before
+// the call), or nowhere (zeros).
 enum KeySrc { kFromCall, kFromRing, kZero };
 __device__ __forceinline__ KeySrc key_src(const PrepArgs& a, int j) {
     return j >= 0 ? (j < a.T ? kFromCall : kZero) : (j >= -a.hist ? kFromRing : kZero);
 }
-__device__ __forceinline__ long ring_row(const PrepArgs& a, long bh, int j) {
-    int slot = a.pmod + j;
-    slot += slot < 0 ? a.R : 0;  // j >= -hist >= -R
-    return (bh * a.R + slot) * SD;
-}
 
 // ---------------------------------------------------------------------------
-// swa_prep: the key-block image of the call's window (keys from the ring, then
-// the call's own) and the rotated, scaled queries.
+// swa_prep: the images of the call's key blocks and the rotated, scaled
+// queries.
 //   V^T items (first, in waves of their own, so that their longer latency
 //     overlaps the rest): item (b, h, jb, r, part) writes 16-byte chunk r < 8
 //     (the 8 keys at positions 8 r .. 8 r + 7 of the V^T key order) of the 8
 //     feature rows part 8 .. part 8 + 7 of block jb's V^T tile: 8 row loads, a
-//     transpose in registers, 8 16-byte stores.
-//   Row items (b, t, head, part): query t of the call, or key row t of the
-//     image (key j = jb0 + t), rotated at its absolute position.
-// Ring calls also write the call's rotated keys and values as rows.
+//     transpose in registers, 8 16-byte stores.  Keys before the call take
+//     their chunks from the ring's image of the same block.
+//   Row items (b, t, head, p): 4 parts of query t of the call, or of key row t
+//     of the image (key j = t - off), rotated at its absolute position.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void swa_prep(const PrepArgs a) {
     long item = (long)blockIdx.x * 256 + threadIdx.x;
@@ -135,14 +137,30 @@ __global__ __launch_bounds__(256) void swa_prep(const PrepArgs a) {
         const int h = (int)(rest % a.Hkv);
         const long b = rest / a.Hkv;
         const long bh = b * a.Hkv + h;
+        _Float16* dst = a.img + (bh * a.NKB + jb) * (long)IMG + KIMG + 8 * r;
+        // the item's keys: j = j8 + 16 (i >> 2) + (i & 3), i < 8
+        const int j8 = jb * KB + 32 * (r >> 2) + 4 * (r & 3) - a.off;
         H8 col[8];
+        if (j8 >= 0 && j8 + 19 < a.T) {
+            // all from the call (all items but the edges)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int j = a.jb0 + jb * KB + 32 * (r >> 2) + 16 * (i >> 2) + 4 * (r & 3) + (i & 3);
-            const KeySrc src = key_src(a, j);
-            if (src == kFromRing) {
-                col[i] = *reinterpret_cast<const H8*>(a.vc + ring_row(a, bh, j) + part * 8);
-            } else {
+            for (int i = 0; i < 8; ++i) {
+                const int j = j8 + 16 * (i >> 2) + (i & 3);
+                float x[8];
+                bf16x8_to_f32(*reinterpret_cast<const uint4*>(a.v + ((b * a.T + j) * a.Hkv + h) * SD + part * 8), x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) col[i][e] = static_cast<_Float16>(x[e]);
+            }
+        } else {
+            // keys past T are zeros; keys before the call come from the same
+            // chunk of the ring's V^T tile of this block (the first block only)
+            bool ring[8], any_ring = false;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int j = j8 + 16 * (i >> 2) + (i & 3);
+                const KeySrc src = key_src(a, j);
+                ring[i] = src == kFromRing;
+                any_ring |= ring[i];
                 float x[8];
                 if (src == kFromCall) {
                     bf16x8_to_f32(*reinterpret_cast<const uint4*>(a.v + ((b * a.T + j) * a.Hkv + h) * SD + part * 8), x);
@@ -152,11 +170,17 @@ __global__ __launch_bounds__(256) void swa_prep(const PrepArgs a) {
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) col[i][e] = static_cast<_Float16>(x[e]);
-                if (src == kFromCall && a.wv)
-                    *reinterpret_cast<H8*>(a.wv + (bh * a.T + j) * SD + part * 8) = col[i];
+            }
+            if (any_ring) {
+                const _Float16* rsrc = a.rv + (bh * a.NBR + a.slot0) * (long)VIMG + part * 8 * VLD + 8 * r;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const H8 rr = *reinterpret_cast<const H8*>(rsrc + e * VLD);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) col[i][e] = ring[i] ? rr[i] : col[i][e];
+                }
             }
         }
-        _Float16* dst = a.img + (bh * a.NKB + jb) * (long)IMG + KIMG + 8 * r;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             H8 row;
@@ -167,65 +191,79 @@ __global__ __launch_bounds__(256) void swa_prep(const PrepArgs a) {
         return;
     }
     item -= nvt;
-    // query items (b, t, head, part) over the call's T tokens, then key items
-    // (b, t, kv head, part) over the image's TR rows
-    const long nq = (long)a.B * a.T * a.Hq * G;
+    // Row items (b, t, head, p) write parts p, p + 4, p + 8, p + 12 of query t
+    // (the first B T Hq items) or of image row t of a key-value head, with the
+    // four loads in flight together.
+    constexpr int G4 = G / 4;
+    const long nq = (long)a.B * a.T * a.Hq * G4;
     const bool isq = item < nq;
     if (!isq) item -= nq;
     const int rows = isq ? a.T : TR, nh = isq ? a.Hq : a.Hkv;
-    if (!isq && item >= (long)a.B * TR * a.Hkv * G) return;
-    const int part = (int)(item % G);
-    long rest = item / G;
-    const int hh = (int)(rest % nh) + (isq ? 0 : a.Hq);
+    if (!isq && item >= (long)a.B * TR * a.Hkv * G4) return;
+    const int p4 = (int)(item % G4);
+    long rest = item / G4;
+    const int hh = (int)(rest % nh);  // query head, or key-value head
     rest /= nh;
     const int t = (int)(rest % rows);
     const long b = rest / rows;
 
-    float x[8];
-    H8 out;
+    const uint16_t* src;
+    _Float16* dst;
+    int tt;  // the row's token in the call (its position is pos0 + tt)
     if (isq) {
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(a.q + ((b * a.T + t) * a.Hq + hh) * SD + part * 8), x);
+        src = a.q + ((b * a.T + t) * a.Hq + hh) * SD;
+        dst = a.wq + ((b * a.Hq + hh) * (long)a.T + t) * SD;
+        tt = t;
     } else {
-        const int h = hh - a.Hq, j = a.jb0 + t;
-        const long bh = b * a.Hkv + h;
-        _Float16* dst = a.img + (bh * a.NKB + t / KB) * (long)IMG + (t % KB) * KLD + part * 8;
-        const KeySrc src = key_src(a, j);
-        if (src != kFromCall) {
-            // ring keys are stored rotated; keys outside the window's range are zeros
-            H8 z;
+        const int j = t - a.off;
+        const long bh = b * a.Hkv + hh;
+        dst = a.img + (bh * a.NKB + t / KB) * (long)IMG + (t % KB) * KLD;
+        const KeySrc ks = key_src(a, j);
+        if (ks != kFromCall) {
+            // ring keys (rows t < off of the first block) are stored rotated;
+            // keys outside the window's range are zeros
+            const _Float16* rs = a.rk + (bh * a.NBR + a.slot0) * (long)KIMG + t * KLD;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) z[i] = static_cast<_Float16>(0.f);
-            *reinterpret_cast<H8*>(dst) =
-                src == kFromRing ? *reinterpret_cast<const H8*>(a.kc + ring_row(a, bh, j) + part * 8) : z;
+            for (int u = 0; u < 4; ++u) {
+                const int part = p4 + 4 * u;
+                H8 val;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) val[i] = static_cast<_Float16>(0.f);
+                if (ks == kFromRing) val = *reinterpret_cast<const H8*>(rs + part * 8);
+                *reinterpret_cast<H8*>(dst + part * 8) = val;
+            }
             return;
         }
-        bf16x8_to_f32(*reinterpret_cast<const uint4*>(a.k + ((b * a.T + j) * a.Hkv + h) * SD + part * 8), x);
+        src = a.k + ((b * a.T + j) * a.Hkv + hh) * SD;
+        tt = j;
     }
-    // rotation at the absolute position of token tt of the call
-    const int tt = hh < a.Hq ? t : a.jb0 + t;
+    uint4 raw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) raw[u] = *reinterpret_cast<const uint4*>(src + (p4 + 4 * u) * 8);
+    // rotation at the row's absolute position
     const double p = (double)(a.pos0 + tt);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const double turns = p * a.rev[part * 4 + i];
-        const float fr = (float)(turns - floor(turns));  // [0, 1)
-        const float c = __builtin_amdgcn_cosf(fr), s = __builtin_amdgcn_sinf(fr);
-        const float x0 = x[2 * i], x1 = x[2 * i + 1];
-        x[2 * i] = x0 * c - x1 * s;
-        x[2 * i + 1] = x0 * s + x1 * c;
-    }
-    if (hh < a.Hq) {
+    for (int u = 0; u < 4; ++u) {
+        const int part = p4 + 4 * u;
+        float x[8];
+        bf16x8_to_f32(raw[u], x);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] *= a.qscale;
-    }
+        for (int i = 0; i < 4; ++i) {
+            const double turns = p * a.rev[part * 4 + i];
+            const float fr = (float)(turns - floor(turns));  // [0, 1)
+            const float c = __builtin_amdgcn_cosf(fr), s = __builtin_amdgcn_sinf(fr);
+            const float x0 = x[2 * i], x1 = x[2 * i + 1];
+            x[2 * i] = x0 * c - x1 * s;
+            x[2 * i + 1] = x0 * s + x1 * c;
+        }
+        if (isq) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = static_cast<_Float16>(x[i]);
-    if (hh < a.Hq) {
-        *reinterpret_cast<H8*>(a.wq + ((b * a.Hq + hh) * (long)a.T + t) * SD + part * 8) = out;
-    } else {
-        const int h = hh - a.Hq;
-        const long bh = b * a.Hkv + h;
-        *reinterpret_cast<H8*>(a.img + (bh * a.NKB + t / KB) * (long)IMG + (t % KB) * KLD + part * 8) = out;
-        if (a.wk) *reinterpret_cast<H8*>(a.wk + (bh * a.T + tt) * SD + part * 8) = out;
+            for (int i = 0; i < 8; ++i) x[i] *= a.qscale;
+        }
+        H8 out;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = static_cast<_Float16>(x[i]);
+        *reinterpret_cast<H8*>(dst + part * 8) = out;
     }
 }
 
@@ -234,10 +272,14 @@ __global__ __launch_bounds__(256) void swa_prep(const PrepArgs a) {
 // ---------------------------------------------------------------------------
 struct AttnArgs {
     const _Float16* q;   // [B][Hq][T][d], scaled, rotated
-    const _Float16* img; // [B][Hkv][NKB][IMG]: block jb holds the keys jb0 + 64 jb .. + 63
+    const _Float16* img; // [B][Hkv][NKB][IMG]: the call's key blocks
+    const _Float16* rk;  // ring calls: the ring's K tiles [B][Hkv][NBR][KIMG]
+    const _Float16* rv;  //   and V^T tiles [B][Hkv][NBR][VIMG]
     float* o;            // [B][T][Hq][d]
     float* part;         // ns > 1: partial O [B][Hq][nqb][ns][QB][d], then (m, l) [..][QB][2]
-    int T, Hq, Hkv, W, hist, nqb, ns, NKB, jb0;
+    int T, Hq, Hkv, W, hist, nqb, ns;
+    int NKB, off;        // image row r of block jb is key j = 64 jb + r - off
+    int NBR, slot0;      // ring blocks; the slot of the call's first block
     int flat;  // 1-D grid, items dealt to the XCDs in contiguous ranges
 };
 
@@ -276,12 +318,13 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
     const int T = a.T, W = a.W;
     const int t0 = qb * QB;
 
-    // Key index j: token j of this call for j >= 0, the ring entry of absolute
-    // position pos0 + j for -hist <= j < 0.  The key blocks are the blocks of
-    // the image, aligned to jb0; the masks drop keys outside a query's window
-    // and before -hist.
+    // Key index j: token j of this call for j >= 0, the key at absolute
+    // position pos0 + j for -hist <= j < 0.  Key blocks are aligned to absolute
+    // positions, so they start at the j = 64 n - off; the masks drop keys
+    // outside a query's window and before -hist.
+    static_assert(KB == 64, "block index by shift");
     const int jfirst = max(t0 - W + 1, -a.hist);
-    const int jlo_all = a.jb0 + (jfirst - a.jb0) / KB * KB;
+    const int jlo_all = ((jfirst + a.off) >> 6) * KB - a.off;  // floor, also below 0
     const int jhi = min(t0 + QB - 1, T - 1);
     const int nblk_all = (jhi - jlo_all) / KB + 1;
     // this split's share of the key blocks (may be empty)
@@ -290,24 +333,46 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
     const int nblk = b_hi - b_lo;
     const int jlo = jlo_all + b_lo * KB;
 
-    // A block's image (written by swa_prep in the LDS layout) goes straight
-    // into LDS with direct-to-LDS loads: 38 pieces of 1 KB, wave w taking
-    // pieces w, w + 4, ...; lane l moves bytes 16 l .. 16 l + 15 of a piece.
-    // No registers, no VALU work, no LDS writes by the waves.
-    constexpr int kPieces = IMG * 2 / 1024;
-    static_assert(IMG * 2 % 1024 == 0, "whole 1 KB pieces");
-    const char* img = reinterpret_cast<const char*>(a.img + (b * a.Hkv + hk) * (long)a.NKB * IMG) + lane * 16;
+    // A block's image (written in the LDS layout: the call's blocks by
+    // swa_prep, the ring's by earlier calls) goes straight into LDS with
+    // direct-to-LDS loads: 38 pieces of 1 KB (18 of the K tile, 20 of the V^T
+    // tile), wave w taking pieces w, w + 4, ... of each tile; lane l moves
+    // bytes 16 l .. 16 l + 15 of a piece.  No registers, no VALU work, no LDS writes
+    // by the waves.
+    constexpr int kPieces = IMG * 2 / 1024, kKPieces = KIMG * 2 / 1024;
+    static_assert(KIMG * 2 % 1024 == 0 && IMG * 2 % 1024 == 0, "whole 1 KB pieces");
+    const long bh = b * a.Hkv + hk;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);  // the wave index, as a scalar
     auto copy_block = [&](int j0, _Float16* dst) {
-        const char* src = img + (long)((j0 - a.jb0) / KB) * (IMG * 2);
+        const int n = (j0 + a.off) >> 6;  // block of the call's image (< 0: the ring's)
+        char* const dk = reinterpret_cast<char*>(dst);
+        if (n >= 0) {
+            // the call's image: K and V^T tiles contiguous, 38 pieces
+            const char* src = reinterpret_cast<const char*>(a.img + (bh * a.NKB + n) * (long)IMG) + lane * 16;
 #pragma unroll
-        for (int ii = 0; ii < (kPieces + 3) / 4; ++ii) {
-            const int i = wave + 4 * ii;
-            if (i < kPieces)
-                __builtin_amdgcn_global_load_lds(src + i * 1024,
-                                                 (lds_void*)(reinterpret_cast<char*>(dst) + i * 1024), 16, 0, 0);
+            for (int ii = 0; ii < (kPieces + 3) / 4; ++ii) {
+                const int i = wv + 4 * ii;
+                if (i < kPieces) __builtin_amdgcn_global_load_lds(src + i * 1024, (lds_void*)(dk + i * 1024), 16, 0, 0);
+            }
+        } else {
+            // the ring's: the K tile (18 pieces) and the V^T tile (20) apart
+            const int slot = a.slot0 + n + (a.slot0 + n < 0 ? a.NBR : 0);
+            const char* kb = reinterpret_cast<const char*>(a.rk + (bh * a.NBR + slot) * (long)KIMG) + lane * 16;
+            const char* vb = reinterpret_cast<const char*>(a.rv + (bh * a.NBR + slot) * (long)VIMG) + lane * 16;
+            char* const dv = dk + kKPieces * 1024;
+#pragma unroll
+            for (int ii = 0; ii < (kKPieces + 3) / 4; ++ii) {
+                const int i = wv + 4 * ii;
+                if (i < kKPieces) __builtin_amdgcn_global_load_lds(kb + i * 1024, (lds_void*)(dk + i * 1024), 16, 0, 0);
+            }
+#pragma unroll
+            for (int ii = 0; ii < (kPieces - kKPieces + 3) / 4; ++ii) {
+                const int i = wv + 4 * ii;
+                if (i < kPieces - kKPieces)
+                    __builtin_amdgcn_global_load_lds(vb + i * 1024, (lds_void*)(dv + i * 1024), 16, 0, 0);
+            }
         }
     };
-
     // this wave's queries: t0 + 32 wave + 16 qt + c
     const int qa = t0 + 32 * wave;
     H8 qf[2][4];
@@ -492,23 +557,23 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
 //     one thread per 4 features of one (b, t, head).  The splits' loads are
 //     issued together (all m_s, then O_s and l_s eight splits at a time), so a
 //     thread waits for the memory a few times, not 2 ns times.
-//   cache items (ring calls): the call's last n = min(T, R) rotated keys and
-//     values into the ring (slot = absolute position mod R); one thread per 16
-//     bytes.  The ring's old entries are no longer needed: the prep has copied
-//     the history into the image.
+//   cache items (ring calls): the call's last nc = min(NKB, NBR) key blocks
+//     into the ring (block n to slot n mod NBR): the K tile to the ring's K
+//     tiles, the V^T tile to its V^T tiles; one thread per 16 bytes.  These are
+//     the blocks the next calls may need; their rows past the call are zeros,
+//     which the next call's own keys replace in its image.
 // ---------------------------------------------------------------------------
 constexpr int kMaxSplits = 32;
 
 struct FinishArgs {
     const float* part;  // partials as the attention writes them
     float* o;           // [B][T][Hq][d]
-    const _Float16* wk; // the call's rotated keys and values [B][Hkv][T][d]
-    const _Float16* wv;
-    _Float16* kc;       // ring caches [B][Hkv][R][d]
-    _Float16* vc;
-    long long pos0;
-    long ncomb, ncache; // items of each kind (combine items first)
-    int B, T, Hq, Hkv, nqb, ns, R, n;
+    const _Float16* img; // the call's key blocks [B][Hkv][NKB][IMG]
+    _Float16* rk;        // ring: K tiles [B][Hkv][NBR][KIMG]
+    _Float16* rv;        //   V^T tiles [B][Hkv][NBR][VIMG]
+    long ncomb, ncache;  // items of each kind (combine items first)
+    int B, T, Hq, Hkv, nqb, ns;
+    int NKB, NBR, slot0, nc;
 };
 
 __global__ __launch_bounds__(256) void swa_finish(const FinishArgs a) {
@@ -559,15 +624,15 @@ __global__ __launch_bounds__(256) void swa_finish(const FinishArgs a) {
     }
     item -= a.ncomb;
     if (item >= a.ncache) return;
-    constexpr int G = SD / 8;
-    const int part = (int)(item % G);
+    constexpr int G = IMG / 8;  // 16-byte pieces of a block image
+    const int u = (int)(item % G);
     long rest = item / G;
-    const int t = a.T - a.n + (int)(rest % a.n);
-    rest /= a.n;
-    const int kv = (int)(rest % 2);
-    const long bh = rest / 2;  // b * Hkv + h
-    const _Float16* src = (kv ? a.wv : a.wk) + (bh * a.T + t) * (long)SD + part * 8;
-    _Float16* dst = (kv ? a.vc : a.kc) + (bh * a.R + (a.pos0 + t) % a.R) * (long)SD + part * 8;
+    const int jb = a.NKB - a.nc + (int)(rest % a.nc);
+    const long bh = rest / a.nc;  // b * Hkv + h
+    const int slot = (a.slot0 + jb) % a.NBR;
+    const _Float16* src = a.img + (bh * a.NKB + jb) * (long)IMG + u * 8;
+    _Float16* dst = u * 8 < KIMG ? a.rk + (bh * a.NBR + slot) * (long)KIMG + u * 8
+                                 : a.rv + (bh * a.NBR + slot) * (long)VIMG + (u * 8 - KIMG);
     *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
 }
 
@@ -595,25 +660,34 @@ static size_t swa_part_bytes(int B, int T, int Hq, int ns) {
     return items * QB * (SD + 2) * sizeof(float);
 }
 
-// Key blocks of a call's image: the call's own keys and, for ring calls, the
-// history before them, rounded out to whole blocks
-static int swa_img_blocks(int T, int hist) {
-    const int before = (hist + KB - 1) / KB;
-    return before + (T + KB - 1) / KB;
+// Blocks of a call's image: from the block of its first token (off = pos0 mod
+// 64 rows before it) to the block of its last
+static int swa_img_blocks(int T, int off) { return (off + T + KB - 1) / KB; }
+
+// the call's block images [B][Hkv][NKB][IMG], for the largest offset
+static size_t swa_img_bytes(int B, int T, int Hkv) {
+    return (size_t)B * Hkv * swa_img_blocks(T, KB - 1) * IMG * sizeof(_Float16);
 }
 
-// the block image [B][Hkv][NKB][IMG], for the longest history (W - 1 keys)
-static size_t swa_img_bytes(int B, int T, int Hkv, int window) {
-    return (size_t)B * Hkv * swa_img_blocks(T, window - 1) * IMG * sizeof(_Float16);
+// Ring blocks: the W - 1 keys before a call span at most ceil((W - 1) / 64) + 1
+// blocks, so with that many slots none of them is overwritten before the call
+// has read it.
+static int swa_ring_blocks(int window) { return (window - 1 + KB - 1) / KB + 1; }
+
+size_t swa_cache_bytes(int B, int Hkv, int window) {
+    // each of the two caches: the K tiles in the first KIMG halves of each slot
+    // size (the V^T tiles fill theirs)
+    static_assert(VIMG >= KIMG, "V^T tiles are the larger");
+    return (size_t)B * Hkv * swa_ring_blocks(window) * VIMG * sizeof(_Float16);
 }
 
 size_t swa_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int window) {
     (void)D;  // 128
-    // queries, the image, the call's key and value rows (ring calls), and the
-    // largest split count any call of these sizes can use (full history)
+    // queries, the call's block images, and the partials of the largest split
+    // count any call of these sizes can use (full history)
     const int ns = swa_splits(B, T, Hq, window, (long long)window, true);
-    return (size_t)B * T * Hq * SD * sizeof(_Float16) + swa_img_bytes(B, T, Hkv, window) +
-           (size_t)2 * B * Hkv * T * SD * sizeof(_Float16) + swa_part_bytes(B, T, Hq, ns);
+    return (size_t)B * T * Hq * SD * sizeof(_Float16) + swa_img_bytes(B, T, Hkv) +
+           swa_part_bytes(B, T, Hq, ns);
 }
 
 hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
@@ -623,43 +697,40 @@ hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache
     const int R = window - 1;
     const bool ring = k_cache && R > 0;
     const int hist = ring ? (int)std::min<long long>(R, pos0) : 0;
-    const int NKB = swa_img_blocks(T, hist);
-    const int jb0 = -KB * ((hist + KB - 1) / KB);
+    const int off = (int)(pos0 % KB);
+    const int NKB = swa_img_blocks(T, off);
+    const int NBR = ring ? swa_ring_blocks(window) : 1;
+    const int slot0 = (int)((pos0 / KB) % NBR);
     _Float16* wq = static_cast<_Float16*>(ws);
     _Float16* img = wq + (size_t)B * Hq * T * SD;
-    _Float16* wk = reinterpret_cast<_Float16*>(reinterpret_cast<char*>(img) + swa_img_bytes(B, T, Hkv, window));
-    _Float16* wv = wk + (size_t)B * Hkv * T * SD;
-    float* part = reinterpret_cast<float*>(wv + (size_t)B * Hkv * T * SD);
+    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(img) + swa_img_bytes(B, T, Hkv));
+    _Float16* rk = ring ? static_cast<_Float16*>(k_cache) : nullptr;
+    _Float16* rv = ring ? static_cast<_Float16*>(v_cache) : nullptr;
 
     PrepArgs p;
     p.q = static_cast<const uint16_t*>(q);
     p.k = static_cast<const uint16_t*>(k);
     p.v = static_cast<const uint16_t*>(v);
-    p.kc = ring ? static_cast<const _Float16*>(k_cache) : nullptr;
-    p.vc = ring ? static_cast<const _Float16*>(v_cache) : nullptr;
+    p.rk = rk, p.rv = rv;
     p.wq = wq, p.img = img;
-    p.wk = ring ? wk : nullptr;
-    p.wv = ring ? wv : nullptr;
     p.pos0 = pos0;
     p.qscale = (float)(1.4426950408889634 / 11.313708498984761);  // log2(e) / sqrt(128)
     p.B = B, p.T = T, p.Hq = Hq, p.Hkv = Hkv;
-    p.NKB = NKB, p.jb0 = jb0;
-    p.hist = hist, p.R = R > 0 ? R : 1;
-    p.pmod = (int)(pos0 % p.R);
+    p.NKB = NKB, p.off = off, p.hist = hist, p.NBR = NBR, p.slot0 = slot0;
     for (int i = 0; i < SD / 2; ++i)
         p.rev[i] = std::pow((double)rope_base, -2.0 * i / SD) / (2.0 * 3.141592653589793);
     const long items =
-        (long)B * Hkv * NKB * 8 * (SD / 8) + (long)B * T * Hq * (SD / 8) + (long)B * NKB * KB * Hkv * (SD / 8);
+        (long)B * Hkv * NKB * 8 * (SD / 8) + (long)B * T * Hq * (SD / 32) + (long)B * NKB * KB * Hkv * (SD / 32);
     hipLaunchKernelGGL(swa_prep, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     profile_mark(stream);
     if (e != hipSuccess) return e;
 
     AttnArgs a;
-    a.q = wq, a.img = img;
+    a.q = wq, a.img = img, a.rk = rk, a.rv = rv;
     a.o = o;
     a.T = T, a.Hq = Hq, a.Hkv = Hkv, a.W = window;
-    a.hist = hist, a.NKB = NKB, a.jb0 = jb0;
+    a.hist = hist, a.NKB = NKB, a.off = off, a.NBR = NBR, a.slot0 = slot0;
     a.nqb = (T + QB - 1) / QB;
     a.ns = swa_splits(B, T, Hq, window, pos0, ring);
     a.part = part;
@@ -674,14 +745,12 @@ hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache
 
     FinishArgs f;
     f.part = part, f.o = o;
-    f.wk = wk, f.wv = wv;
-    f.kc = static_cast<_Float16*>(k_cache), f.vc = static_cast<_Float16*>(v_cache);
-    f.pos0 = pos0;
+    f.img = img, f.rk = rk, f.rv = rv;
     f.B = B, f.T = T, f.Hq = Hq, f.Hkv = Hkv, f.nqb = a.nqb, f.ns = a.ns;
-    f.R = R > 0 ? R : 1;
-    f.n = ring ? std::min(T, R) : 0;
+    f.NKB = NKB, f.NBR = NBR, f.slot0 = slot0;
+    f.nc = ring ? std::min(NKB, NBR) : 1;
     f.ncomb = a.ns > 1 ? (long)B * T * Hq * (SD / 4) : 0;
-    f.ncache = ring ? (long)B * Hkv * f.n * (SD / 8) * 2 : 0;
+    f.ncache = ring ? (long)B * Hkv * f.nc * (IMG / 8) : 0;
     const long fitems = f.ncomb + f.ncache;
     hipLaunchKernelGGL(swa_finish, dim3((unsigned)((fitems + 255) / 256)), dim3(256), 0, stream, f);
     e = hipGetLastError();

@@ -266,15 +266,20 @@ def test_swa_errors(lib):
     assert _swa(lib, ws=None) == WS
     lib.gdn_swa_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_swa_cache_bytes.restype = ctypes.c_size_t
-    # fp16 q rows; k and v as key blocks of (64 x 144 + 128 x 80) halves per kv
-    # head, 128 for the call's keys and 128 for the longest history (8191 keys);
-    # then the call's k and v rows for the ring update (2 x 8192 x 128 halves
-    # per kv head)
+    # fp16 q rows; k and v as the images of the call's 64-position blocks,
+    # (64 x 144 + 128 x 80) halves each, 129 per kv head for 8192 tokens at any
+    # offset in a block
+    img = 64 * 144 + 128 * 80
     assert lib.gdn_swa_workspace_bytes(1, 8192, 16, 2, 128, 8192) == \
-        8192 * 16 * 128 * 2 + 2 * 256 * (64 * 144 + 128 * 80) * 2 + 2 * 2 * 8192 * 128 * 2
-    # a 272-token call against an 8K window splits its key range: partials added
-    assert lib.gdn_swa_workspace_bytes(1, 272, 16, 2, 128, 8192) > 272 * 20 * 128 * 2
-    assert lib.gdn_swa_cache_bytes(1, 2, 128, 8192) == 2 * 8191 * 128 * 2
+        8192 * 16 * 128 * 2 + 2 * 129 * img * 2
+    # a 272-token call against an 8K window splits its key range (10 splits of
+    # 3 query blocks x 16 heads): partial O and (m, l) of 128 queries each
+    assert lib.gdn_swa_workspace_bytes(1, 272, 16, 2, 128, 8192) == \
+        272 * 16 * 128 * 2 + 2 * 6 * img * 2 + 16 * 3 * 10 * 128 * (128 + 2) * 4
+    # ring: ceil(8191 / 64) + 1 = 129 blocks per kv head, each buffer sized by the
+    # larger V^T tile (128 x 80 halves)
+    assert lib.gdn_swa_cache_bytes(1, 2, 128, 8192) == 2 * 129 * 128 * 80 * 2
+    assert lib.gdn_swa_cache_bytes(1, 2, 128, 2) == 2 * 2 * 128 * 80 * 2
     assert lib.gdn_swa_cache_bytes(1, 2, 128, 1) == 0
 
 
