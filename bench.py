@@ -603,6 +603,14 @@ def time_swa(gdn, args, dev):
                      "value": 1e3 / sms, "unit": "calls/s", "us_per_call": sms * 1e3,
                      "tokens_per_s": ct * 1e3 / sms,
                      "tflops": sfl / (sms / 1e3) / 1e12}
+
+    def loop():
+        for i in range(n):
+            gdn.swa_stream_chunk(*pieces[i % len(pieces)], kc, vc, pos + i * ct, W, o=os_, workspace=wss)
+
+    gms = graph_ms(loop) / n
+    out["stream"]["graph"] = {"value": 1e3 / gms, "unit": "calls/s", "us_per_call": gms * 1e3,
+                              "note": "the %d-call loop captured once as a HIP graph and replayed" % n}
     return out
 
 

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import gdn_inputs
-from parity_util import TOL, oracle_sequence, rel_err, stage
+from parity_util import TOL, oracle_sequence, rel_err, stage, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -165,6 +165,50 @@ def test_graph_segmented_prefill(env):
     with torch.cuda.graph(g):
         call()
     _replays(torch, g, reset, (o, st), ref)
+
+
+def test_graph_swa_stream_loop(env):
+    """12 sliding-window stream calls of 37 tokens (W=100, 4/2 heads, d=128)
+    captured and replayed: the ring caches wrap several times and the calls
+    start at every offset within a 64-position block.  Each replay starts a
+    new stream at position 0, so it needs no reset of the caches."""
+    gdn, dev = env
+    import torch
+    from oracle import swa as oswa
+    _note("case graph: 12 swa stream calls x 37, W=100")
+    ct, calls, W, Hq, Hkv = 37, 12, 100, 4, 2
+    T = ct * calls
+    xs = gdn_inputs.swa_inputs(1, T, Hq, Hkv, 128, seed=3737)
+    t = {n: to_dev(xs[n], "bf16", dev) for n in ("q", "k", "v")}
+    pieces = [{n: t[n][:, c * ct:(c + 1) * ct].contiguous() for n in t} for c in range(calls)]
+    kc, vc = gdn.swa_new_cache(1, Hkv, 128, W, dev)
+    outs = [torch.zeros((1, ct, Hq, 128), dtype=torch.float32, device=dev) for _ in range(calls)]
+    ws = torch.empty(gdn.swa_workspace_bytes(1, ct, Hq, Hkv, 128, W), dtype=torch.uint8, device=dev)
+
+    def loop():
+        for c in range(calls):
+            p = pieces[c]
+            gdn.swa_stream_chunk(p["q"], p["k"], p["v"], kc, vc, c * ct, W, o=outs[c], workspace=ws)
+
+    loop()
+    torch.cuda.synchronize()
+    f = lambda a: gdn_inputs.to_f64(a, "bf16")
+    ref = oswa.swa(f(xs["q"]), f(xs["k"]), f(xs["v"]), W)
+    e = rel_err(torch.cat(outs, dim=1).cpu().numpy(), ref)
+    _note("graph swa stream eager vs oracle: %.3e" % e)
+    assert e <= TOL["bf16"]
+    expect = [y.clone() for y in outs]
+
+    def reset():
+        for y in outs:
+            y.zero_()
+
+    reset()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        loop()
+    _replays(torch, g, reset, outs, expect)
 
 
 def test_profile_hook_marks(env):
