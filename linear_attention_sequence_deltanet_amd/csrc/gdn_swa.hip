@@ -10,29 +10,30 @@
 // q and k (feature pairs (2i, 2i+1) rotated by p * base^(-2i/d)); query head h
 // reads key-value head h / (Hq / Hkv).
 //
-// Three kernels per call, all on the caller's stream:
-//   swa_prep   rotates q and k at their absolute positions and converts q
-//              (pre-scaled by log2(e) / sqrt(d)), k and v to fp16 in the
-//              workspace: q head-major ([B][H][T][d]); k and v the same for
-//              calls with a ring cache, otherwise as the image of each 64-key
-//              block in on-chip memory (the K tile and the V^T tile, padded
-//              rows, keys past T zero).  bf16 inputs convert to fp16 exactly
+// Two or three kernels per call, all on the caller's stream:
+//   swa_prep   rotates q and k at their absolute positions and converts them
+//              and v to fp16 in the workspace: q head-major ([B][H][T][d]) and
+//              pre-scaled by log2(e) / sqrt(d); k and v as the images of the
+//              call's 64-position key blocks in on-chip memory (the K tile and
+//              the V^T tile, padded rows; rows before the call from the ring
+//              cache, rows past T zero).  bf16 inputs convert to fp16 exactly
 //              at activation magnitudes; rotated values keep 3 more mantissa
 //              bits than bf16 would.
 //   swa_attn   flash-style attention: a workgroup owns 128 queries of one head
 //              (4 waves x 32) and walks 64-key blocks of their window.  A block
-//              of K (row-major) and V (transposed) sits in LDS, double-buffered:
-//              copied from its image by direct-to-LDS loads, or, with a ring
-//              cache, staged through registers (rows from the call or the
-//              ring, V transposed two keys per dword).  Each wave forms S^T = K Q^T on
-//              the matrix cores, so lane column c of every tile is one query:
-//              the online softmax (running max m, sum l, base-2 exponentials),
-//              the rescale of O^T and the final 1/l are per-lane, and P^T feeds
-//              O^T += V^T P^T directly as the B operand of 16x16x32 fp16 MFMAs
-//              (the keys of a 32-key step are taken in the order the S^T tiles
-//              hold them, for both operands).
-//   swa_cache  (streaming only) writes the call's last W-1 rotated keys and
-//              values into the caller's ring cache for the next call.
+//              of K (row-major) and V (transposed) sits in LDS, double-buffered,
+//              copied by direct-to-LDS loads from the call's image or, for
+//              blocks before the call, from the ring cache, which holds the
+//              same images.  Each wave forms S^T = K Q^T on the matrix cores,
+//              so lane column c of every tile is one query: the online softmax
+//              (running max m, sum l, base-2 exponentials), the rescale of O^T
+//              and the final 1/l are per-lane, and P^T feeds O^T += V^T P^T
+//              directly as the B operand of 16x16x32 fp16 MFMAs (the keys of a
+//              32-key step are taken in the order the S^T tiles hold them, for
+//              both operands).
+//   swa_finish (split windows or ring calls) merges the partial results of a
+//              split window, and copies the call's last key blocks into the
+//              ring cache for the next call.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -45,7 +46,6 @@ namespace gdn {
 namespace {
 
 using H8 = f16x8;
-using H4 = f16x4;
 using MF = Mfma<_Float16>;
 
 constexpr int SD = 128;        // head dimension
