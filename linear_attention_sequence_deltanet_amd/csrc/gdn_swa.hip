@@ -46,6 +46,7 @@ namespace gdn {
 namespace {
 
 using H8 = f16x8;
+using H4 = f16x4;
 using MF = Mfma<_Float16>;
 
 constexpr int SD = 128;        // head dimension
@@ -276,7 +277,7 @@ struct AttnArgs {
     const _Float16* rk;  // ring calls: the ring's K tiles [B][Hkv][NBR][KIMG]
     const _Float16* rv;  //   and V^T tiles [B][Hkv][NBR][VIMG]
     float* o;            // [B][T][Hq][d]
-    float* part;         // ns > 1: partial O [B][Hq][nqb][ns][QB][d], then (m, l) [..][QB][2]
+    float* part;         // ns > 1: O / l fp16 [B][Hq][nqb][ns][QB][d], then (m, l) fp32 [..][QB][2]
     int T, Hq, Hkv, W, hist, nqb, ns;
     int NKB, off;        // image row r of block jb is key j = 64 jb + r - off
     int NBR, slot0;      // ring blocks; the slot of the call's first block
@@ -529,21 +530,27 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
             }
         }
     } else {
-        // unnormalised partial of this split, merged by swa_combine
+        // this split's partial, merged by swa_finish: O / l in fp16 (a
+        // convex combination of value rows, so within their range), then m, l
         const long item = ((b * a.Hq + h) * a.nqb + qb) * a.ns + split;
         const long nitems = N;
+        _Float16* const po = reinterpret_cast<_Float16*>(a.part);
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
             const int qi = 32 * wave + 16 * qt + c;
-            if (t0 + qi >= T) continue;  // the combine reads queries t < T only
+            if (t0 + qi >= T) continue;  // the merge reads queries t < T only
             const float lt = ls[qt][0];
-            float* op = a.part + (item * QB + qi) * (long)SD + 4 * g;
+            const float inv = lt > 0.f ? 1.0f / lt : 0.f;  // l = 0: the split saw no key of this query
+            _Float16* op = po + (item * QB + qi) * (long)SD + 4 * g;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                *reinterpret_cast<float4*>(op + 16 * dt) =
-                    make_float4(acc[dt][qt][0], acc[dt][qt][1], acc[dt][qt][2], acc[dt][qt][3]);
+            for (int dt = 0; dt < 8; ++dt) {
+                H4 r;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e] = static_cast<_Float16>(acc[dt][qt][e] * inv);
+                *reinterpret_cast<H4*>(op + 16 * dt) = r;
+            }
             if (g == 0) {
-                float* ml = a.part + nitems * QB * SD + (item * QB + qi) * 2;
+                float* ml = a.part + nitems * QB * SD / 2 + (item * QB + qi) * 2;
                 *reinterpret_cast<float2*>(ml) = make_float2(m[qt], lt);
             }
         }
@@ -553,7 +560,8 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
 // ---------------------------------------------------------------------------
 // swa_finish, after the attention:
 //   combine items (ns > 1): merge the ns partials of each query (base-2
-//     log-sum-exp), M = max m_s, o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s;
+//     log-sum-exp): with M = max m_s and w_s = 2^(m_s - M) l_s,
+//     o = sum_s w_s (O_s / l_s) / sum_s w_s, from the stored O_s / l_s;
 //     one thread per 4 features of one (b, t, head).  The splits' loads are
 //     issued together (all m_s, then O_s and l_s eight splits at a time), so a
 //     thread waits for the memory a few times, not 2 ns times.
@@ -589,7 +597,8 @@ __global__ __launch_bounds__(256) void swa_finish(const FinishArgs a) {
         const int qb = t / QB, qi = t % QB, ns = a.ns;
         const long nitems = (long)a.B * a.Hq * a.nqb * ns;
         const long base = ((b * a.Hq + h) * a.nqb + qb) * ns;
-        const float* ml = a.part + nitems * QB * SD;
+        const _Float16* po = reinterpret_cast<const _Float16*>(a.part);
+        const float* ml = a.part + nitems * QB * SD / 2;
         // split indices past ns read split ns - 1 again (in bounds) with weight 0
         float mv[kMaxSplits];
 #pragma unroll
@@ -603,18 +612,19 @@ __global__ __launch_bounds__(256) void swa_finish(const FinishArgs a) {
         for (int s0 = 0; s0 < kMaxSplits; s0 += 8) {
             if (s0 >= ns) break;
             float lv[8];
-            float4 pv[8];
+            H4 pv[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const long sl = base + min(s0 + i, ns - 1);
                 lv[i] = ml[(sl * QB + qi) * 2 + 1];
-                pv[i] = *reinterpret_cast<const float4*>(a.part + (sl * QB + qi) * (long)SD + 4 * part4);
+                pv[i] = *reinterpret_cast<const H4*>(po + (sl * QB + qi) * (long)SD + 4 * part4);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float w = s0 + i < ns ? __builtin_amdgcn_exp2f(mv[s0 + i] - M) : 0.f;
-                L += w * lv[i];
-                acc.x += w * pv[i].x, acc.y += w * pv[i].y, acc.z += w * pv[i].z, acc.w += w * pv[i].w;
+                const float w = s0 + i < ns ? __builtin_amdgcn_exp2f(mv[s0 + i] - M) * lv[i] : 0.f;
+                L += w;
+                acc.x += w * static_cast<float>(pv[i][0]), acc.y += w * static_cast<float>(pv[i][1]);
+                acc.z += w * static_cast<float>(pv[i][2]), acc.w += w * static_cast<float>(pv[i][3]);
             }
         }
         const float inv = 1.0f / L;
@@ -657,7 +667,7 @@ int swa_splits(int B, int T, int Hq, int window, long long pos0, bool ring) {
 static size_t swa_part_bytes(int B, int T, int Hq, int ns) {
     if (ns <= 1) return 0;
     const size_t items = (size_t)B * Hq * ((T + QB - 1) / QB) * ns;
-    return items * QB * (SD + 2) * sizeof(float);
+    return items * QB * (SD * sizeof(_Float16) + 2 * sizeof(float));  // O / l fp16, then m, l
 }
 
 // Blocks of a call's image: from the block of its first token (off = pos0 mod
