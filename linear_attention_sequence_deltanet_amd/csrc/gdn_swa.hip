@@ -282,6 +282,8 @@ struct AttnArgs {
     int NKB, off;        // image row r of block jb is key j = 64 jb + r - off
     int NBR, slot0;      // ring blocks; the slot of the call's first block
     int flat;  // 1-D grid, items dealt to the XCDs in contiguous ranges
+    int B;
+    int P, hpw;  // last query block: P queries of each of hpw heads per workgroup (hpw = 1: 128 of one)
 };
 
 // max over the 4 lanes c, c+16, c+32, c+48 (one query of an S^T tile)
@@ -292,32 +294,26 @@ __device__ __forceinline__ float qmax(float s) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-__global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
-    // two key-block buffers, each the K tile then the V^T tile; two arrays, not
-    // one indexed by parity, so that the compiler sees that the copies into one
-    // do not alias the reads of the other and does not wait for them
-    __shared__ __attribute__((aligned(16))) _Float16 sB0[IMG];
-    __shared__ __attribute__((aligned(16))) _Float16 sB1[IMG];
-
-    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+// The attention of one workgroup item (batch b, heads h .. h + nh - 1, query
+// block qb, key-range split); Pq queries per head (kPacked false: 128 of one
+// head).
+template <bool kPacked>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, _Float16* sB0, _Float16* sB1, long b, int h,
+                                          int nh, int qb, int split, int Pq) {
+    const int P = kPacked ? Pq : QB;
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform: scalar branches on it
     const int g = lane / 16, c = lane % 16;
-    // Workgroups are dealt to the 8 XCDs in turn (XCD = id mod 8), so item
-    // (id mod 8) N / 8 + id / 8 gives each XCD a contiguous range of items:
-    // ordered by (batch, head, query block, split), its workgroups share one or
-    // two heads and their key-value head in the XCD's L2.  Within a range the
-    // longest windows come first.
-    // (With more items than a 1-D grid holds, the grid is (query block x
-    // split, head, batch) in the hardware's order.)
-    const long N = (long)gridDim.x * gridDim.y * gridDim.z;
-    const long L = blockIdx.x + (long)gridDim.x * (blockIdx.y + (long)gridDim.y * blockIdx.z);
-    const long I = a.flat && N % 8 == 0 ? (L % 8) * (N / 8) + L / 8 : L;
-    const int split = (int)(I % a.ns);
-    const int qb = a.nqb - 1 - (int)((I / a.ns) % a.nqb);  // longest windows first
-    const int h = (int)((I / ((long)a.ns * a.nqb)) % a.Hq);
-    const long b = I / ((long)a.ns * a.nqb * a.Hq);
-    const int hk = h / (a.Hq / a.Hkv);
+    const int G = a.Hq / a.Hkv;  // query heads per key-value head
+    const int hk = h / G;
     const int T = a.T, W = a.W;
     const int t0 = qb * QB;
+    // Query slot qi = 32 wave + 16 qt + c (lane column c of tile qt) holds
+    // query t0 + qi mod P of head h + qi / P; heads past nh are idle slots.
+    // This wave's queries are tw .. tw + nw - 1.
+    const int tw = t0 + (32 * wave) % P, nw = min(P, 32);
+    const bool wave_on = !kPacked || (32 * wave) / P < nh;
+    const bool wave_all_on = !kPacked || (32 * wave + 31) / P < nh;  // every slot of the wave
 
     // Key index j: token j of this call for j >= 0, the key at absolute
     // position pos0 + j for -hist <= j < 0.  Key blocks are aligned to absolute
@@ -375,12 +371,20 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
         }
     };
     // this wave's queries: t0 + 32 wave + 16 qt + c
-    const int qa = t0 + 32 * wave;
+    int tq[2], hq[2];
+    bool on[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        const int qi = 32 * wave + 16 * qt + c;
+        tq[qt] = t0 + qi % P;
+        hq[qt] = h + qi / P;
+        on[qt] = !kPacked || qi / P < nh;
+    }
     H8 qf[2][4];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-        const int t = qa + 16 * qt + c;
-        const _Float16* qp = a.q + ((b * a.Hq + h) * (long)T + min(t, T - 1)) * SD;
+        const int hh = on[qt] ? hq[qt] : h;  // idle slots load a valid row
+        const _Float16* qp = a.q + ((b * a.Hq + hh) * (long)T + min(tq[qt], T - 1)) * SD;
 #pragma unroll
         for (int s = 0; s < 4; ++s) qf[qt][s] = *reinterpret_cast<const H8*>(qp + 32 * s + 8 * g);
     }
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
         if (bi + 1 < nblk) copy_block(j0 + KB, nxt);
 
         // does any query of this wave see a key of this block?
-        const bool live = qa < T && j0 <= qa + 31 && j0 + KB - 1 >= qa - W + 1;
+        const bool live = wave_on && tw < T && j0 <= tw + nw - 1 && j0 + KB - 1 >= tw - W + 1;
         if (live) {
             const _Float16* kt_base = &cur[c * KLD + 8 * g];
             // Scores relative to the reference max, S - ref: the first product of
@@ -436,14 +440,15 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
                     st[kt][1] = MF::k32(ka, qf[1][s], s == 0 ? nref[1] : st[kt][1]);
                 }
             }
-            // masks: key j = j0 + 16 kt + 4 g + e, query t = qa + 16 qt + c
-            const bool full =
-                j0 + KB - 1 <= qa && (qa + 31) - j0 < W && j0 + KB - 1 <= jhi && j0 >= -a.hist;
+            // masks: key j = j0 + 16 kt + 4 g + e, query t = tq[qt] (lane column c)
+            const bool full = j0 + KB - 1 <= tw && (tw + nw - 1) - j0 < W && j0 + KB - 1 <= jhi &&
+                              j0 >= -a.hist && wave_all_on;
             if (!full) {
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) {
-                    const int t = qa + 16 * qt + c;
-                    const int lo_ok = max(t - W + 1, -a.hist), hi_ok = min(t, jhi);  // keys j in [lo_ok, hi_ok]
+                    const int t = tq[qt];
+                    const int lo_ok = max(t - W + 1, -a.hist);
+                    const int hi_ok = (!kPacked || on[qt]) ? min(t, jhi) : -(1 << 30);  // keys j in [lo_ok, hi_ok]
 #pragma unroll
                     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -518,10 +523,10 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
         // o[t][16 dt + 4 g + e] = acc / l
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-            const int t = qa + 16 * qt + c;
+            const int t = tq[qt];
             const float inv = 1.0f / ls[qt][0];
-            if (t < T) {
-                float* op = a.o + ((b * T + t) * a.Hq + h) * (long)SD + 4 * g;
+            if (on[qt] && t < T) {
+                float* op = a.o + ((b * T + t) * a.Hq + hq[qt]) * (long)SD + 4 * g;
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt) {
                     const f32x4 r = acc[dt][qt] * inv;
@@ -531,14 +536,16 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
         }
     } else {
         // this split's partial, merged by swa_finish: O / l in fp16 (a
-        // convex combination of value rows, so within their range), then m, l
-        const long item = ((b * a.Hq + h) * a.nqb + qb) * a.ns + split;
-        const long nitems = N;
+        // convex combination of value rows, so within their range), then m, l;
+        // row t - t0 of item (b, head, query block, split), whatever the
+        // packing of the workgroup
+        const long nitems = (long)a.B * a.Hq * a.nqb * a.ns;
         _Float16* const po = reinterpret_cast<_Float16*>(a.part);
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-            const int qi = 32 * wave + 16 * qt + c;
-            if (t0 + qi >= T) continue;  // the merge reads queries t < T only
+            const int qi = tq[qt] - t0;
+            if (!on[qt] || tq[qt] >= T) continue;  // the merge reads queries t < T only
+            const long item = ((b * a.Hq + hq[qt]) * a.nqb + qb) * a.ns + split;
             const float lt = ls[qt][0];
             const float inv = lt > 0.f ? 1.0f / lt : 0.f;  // l = 0: the split saw no key of this query
             _Float16* op = po + (item * QB + qi) * (long)SD + 4 * g;
@@ -555,6 +562,62 @@ __global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
             }
         }
     }
+}
+
+// kPacked: the grid's last query blocks are packed (AttnArgs P, hpw); the
+// launch without packing runs the code for 128 queries of one head only.
+template <bool kPacked>
+__global__ __launch_bounds__(256, 2) void swa_attn(const AttnArgs a) {
+    // two key-block buffers, each the K tile then the V^T tile; two arrays, not
+    // one indexed by parity, so that the compiler sees that the copies into one
+    // do not alias the reads of the other and does not wait for them
+    __shared__ __attribute__((aligned(16))) _Float16 sB0[IMG];
+    __shared__ __attribute__((aligned(16))) _Float16 sB1[IMG];
+
+    // Workgroups are dealt to the 8 XCDs in turn (XCD = id mod 8), so item
+    // (id mod 8) N / 8 + id / 8 gives each XCD a contiguous range of items:
+    // ordered by (batch, head, query block, split), its workgroups share one or
+    // two heads and their key-value head in the XCD's L2.  Within a range the
+    // longest windows come first.
+    // (With more items than a 1-D grid holds, the grid is (query block x
+    // split, head, batch) in the hardware's order.)
+    const long N = (long)gridDim.x * gridDim.y * gridDim.z;
+    const long L = blockIdx.x + (long)gridDim.x * (blockIdx.y + (long)gridDim.y * blockIdx.z);
+    const long I = a.flat && N % 8 == 0 ? (L % 8) * (N / 8) + L / 8 : L;
+    const int G = a.Hq / a.Hkv;  // query heads per key-value head
+    int split, qb, h, P = QB, nh = 1;
+    long b;
+    if (!kPacked) {
+        split = (int)(I % a.ns);
+        qb = a.nqb - 1 - (int)((I / a.ns) % a.nqb);  // longest windows first
+        h = (int)((I / ((long)a.ns * a.nqb)) % a.Hq);
+        b = I / ((long)a.ns * a.nqb * a.Hq);
+    } else {
+        // The last query block holds few queries: its workgroups serve hpw
+        // heads of one key-value group each (P queries per head).  Per (batch,
+        // key-value head): those items first (the longest windows), then the
+        // other query blocks of each head.
+        const int npk = (G + a.hpw - 1) / a.hpw;
+        const long per_kh = ((long)npk + (long)G * (a.nqb - 1)) * a.ns;
+        b = I / (per_kh * a.Hkv);
+        long r = I % (per_kh * a.Hkv);
+        const int kh = (int)(r / per_kh);
+        r %= per_kh;
+        split = (int)(r % a.ns);
+        if (r < (long)npk * a.ns) {
+            const int pk = (int)(r / a.ns);
+            qb = a.nqb - 1;
+            h = kh * G + pk * a.hpw;
+            P = a.P;
+            nh = min(a.hpw, G - pk * a.hpw);
+        } else {
+            r -= (long)npk * a.ns;
+            const long perh = (long)(a.nqb - 1) * a.ns;
+            h = kh * G + (int)(r / perh);
+            qb = a.nqb - 2 - (int)((r % perh) / a.ns);
+        }
+    }
+    attn_body<kPacked>(a, sB0, sB1, b, h, nh, qb, split, P);
 }
 
 // ---------------------------------------------------------------------------
@@ -648,13 +711,34 @@ __global__ __launch_bounds__(256) void swa_finish(const FinishArgs a) {
 
 }  // namespace
 
-// Key-range splits per query block: one while the (query block, head, batch)
-// grid already fills the chip twice (two workgroups on each of the 256 CUs),
-// else as many as still fit in that one round -- one split more would start a
-// second round for a few workgroups -- each split keeping at least 4 key
-// blocks (at most 32 splits).
-int swa_splits(int B, int T, int Hq, int window, long long pos0, bool ring) {
-    const long base = (long)((T + QB - 1) / QB) * Hq * B;
+// Packing of the last query block: when it holds few queries (nlast), one
+// workgroup serves hpw heads of a key-value group, P >= nlast queries of each
+// (P in 16, 32, 64; hpw = 1 and P = 128 when no packing helps).
+struct QPack {
+    int P, hpw;
+};
+static QPack swa_pack(int T, int Hq, int Hkv) {
+    const int nqb = (T + QB - 1) / QB;
+    const int nlast = T - (nqb - 1) * QB;
+    int P = 16;
+    while (P < nlast) P *= 2;
+    const int hpw = std::min(Hq / Hkv, QB / P);
+    return hpw > 1 ? QPack{P, hpw} : QPack{QB, 1};
+}
+
+// (query block, head) workgroup items of a call, before any key-range split
+static long swa_base_items(int B, int T, int Hq, int Hkv, const QPack& pk) {
+    const int nqb = (T + QB - 1) / QB;
+    const int G = Hq / Hkv;
+    const long last = pk.hpw > 1 ? (long)Hkv * ((G + pk.hpw - 1) / pk.hpw) : Hq;
+    return (long)B * ((long)Hq * (nqb - 1) + last);
+}
+
+// Key-range splits per item: one while the items already fill the chip twice
+// (two workgroups on each of the 256 CUs), else as many as still fit in that
+// one round -- one split more would start a second round for a few
+// workgroups -- each split keeping at least 4 key blocks (at most 32 splits).
+static int swa_splits(long base, int T, int window, long long pos0, bool ring) {
     if (base >= 512) return 1;
     const long hist = ring ? std::min<long long>(window - 1, pos0) : 0;
     const long keys = std::min<long>((long)window + QB, (long)T + hist + QB);
@@ -662,6 +746,28 @@ int swa_splits(int B, int T, int Hq, int window, long long pos0, bool ring) {
     long ns = 512 / base;
     ns = std::min<long>(ns, std::max<long>(1, maxblk / 4));
     return (int)std::max<long>(1, std::min<long>(ns, kMaxSplits));
+}
+
+// A call's workgroup plan.  Packing only pays where it buys more key-range
+// splits (a workgroup's time is its block count, whatever it packs); without
+// splits the plain items run the code for one head.  Fewer items never give
+// fewer splits, so the packed plan's count bounds every call's.
+struct SwaPlan {
+    QPack pk;
+    int ns;
+    long items;
+};
+static SwaPlan swa_plan(int B, int T, int Hq, int Hkv, int window, long long pos0, bool ring) {
+    const QPack pk = swa_pack(T, Hq, Hkv);
+    if (pk.hpw > 1) {
+        const long base = swa_base_items(B, T, Hq, Hkv, pk);
+        const int ns = swa_splits(base, T, window, pos0, ring);
+        if (ns > 1) return {pk, ns, base * ns};
+    }
+    const QPack none{QB, 1};
+    const long base = swa_base_items(B, T, Hq, Hkv, none);
+    const int ns = swa_splits(base, T, window, pos0, ring);
+    return {none, ns, base * ns};
 }
 
 static size_t swa_part_bytes(int B, int T, int Hq, int ns) {
@@ -695,7 +801,7 @@ size_t swa_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int window) {
     (void)D;  // 128
     // queries, the call's block images, and the partials of the largest split
     // count any call of these sizes can use (full history)
-    const int ns = swa_splits(B, T, Hq, window, (long long)window, true);
+    const int ns = swa_plan(B, T, Hq, Hkv, window, (long long)window, true).ns;
     return (size_t)B * T * Hq * SD * sizeof(_Float16) + swa_img_bytes(B, T, Hkv) +
            swa_part_bytes(B, T, Hq, ns);
 }
@@ -742,12 +848,19 @@ hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache
     a.T = T, a.Hq = Hq, a.Hkv = Hkv, a.W = window;
     a.hist = hist, a.NKB = NKB, a.off = off, a.NBR = NBR, a.slot0 = slot0;
     a.nqb = (T + QB - 1) / QB;
-    a.ns = swa_splits(B, T, Hq, window, pos0, ring);
+    const SwaPlan plan = swa_plan(B, T, Hq, Hkv, window, pos0, ring);
+    a.ns = plan.ns;
     a.part = part;
-    const long nall = (long)a.nqb * a.ns * Hq * B;
+    a.B = B;
+    a.P = plan.pk.P, a.hpw = plan.pk.hpw;
+    const long nall = plan.items;
+    // (a packed plan has splits, so a grid of at most 32 x 512 workgroups)
     a.flat = nall <= 0x7fffffffL;
     const dim3 grid = a.flat ? dim3((unsigned)nall) : dim3((unsigned)(a.nqb * a.ns), (unsigned)Hq, (unsigned)B);
-    hipLaunchKernelGGL(swa_attn, grid, dim3(256), 0, stream, a);
+    if (a.hpw > 1)
+        hipLaunchKernelGGL(swa_attn<true>, grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(swa_attn<false>, grid, dim3(256), 0, stream, a);
     e = hipGetLastError();
     profile_mark(stream);
     if (e != hipSuccess) return e;

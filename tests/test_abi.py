@@ -272,11 +272,12 @@ def test_swa_errors(lib):
     img = 64 * 144 + 128 * 80
     assert lib.gdn_swa_workspace_bytes(1, 8192, 16, 2, 128, 8192) == \
         8192 * 16 * 128 * 2 + 2 * 129 * img * 2
-    # a 272-token call against an 8K window splits its key range (10 splits of
-    # 3 query blocks x 16 heads): partial O / l (fp16) and (m, l) (fp32) of 128
-    # queries each
+    # a 272-token call against an 8K window splits its key range: 2 full query
+    # blocks x 16 heads, and the last block's 16 queries of 8 heads per
+    # workgroup (2 workgroups) make 34 items, 15 splits each; partial O / l
+    # (fp16) and (m, l) (fp32) of 128 query rows per (head, query block, split)
     assert lib.gdn_swa_workspace_bytes(1, 272, 16, 2, 128, 8192) == \
-        272 * 16 * 128 * 2 + 2 * 6 * img * 2 + 16 * 3 * 10 * 128 * (128 * 2 + 2 * 4)
+        272 * 16 * 128 * 2 + 2 * 6 * img * 2 + 16 * 3 * 15 * 128 * (128 * 2 + 2 * 4)
     # ring: ceil(8191 / 64) + 1 = 129 blocks per kv head, each buffer sized by the
     # larger V^T tile (128 x 80 halves)
     assert lib.gdn_swa_cache_bytes(1, 2, 128, 8192) == 2 * 129 * 128 * 80 * 2
