@@ -20,7 +20,9 @@
 //              at activation magnitudes; rotated values keep 3 more mantissa
 //              bits than bf16 would.
 //   swa_attn   flash-style attention: a workgroup owns 128 queries of one head
-//              (4 waves x 32) and walks 64-key blocks of their window.  A block
+//              (4 waves x 32; a ragged last query block of a split call may
+//              take fewer queries of several heads of one key-value group) and
+//              walks 64-key blocks of their window.  A block
 //              of K (row-major) and V (transposed) sits in LDS, double-buffered,
 //              copied by direct-to-LDS loads from the call's image or, for
 //              blocks before the call, from the ring cache, which holds the
