@@ -1121,7 +1121,7 @@ hipError_t launch_t(const BwdArgs& a, bool side_by_side, hipStream_t stream) {
 // (diag(e) K)^T, which only the forward chain reads, and runs the chains one
 // after the other.
 size_t backward_workspace_bytes(int B, int T, int H, int D, bool minimal) {
-    const size_t NC = (size_t)(T + BC - 1) / BC, chunks = NC * B * H;
+    const size_t NC = ((size_t)T + BC - 1) / BC, chunks = NC * B * H;
     const size_t per = SCN * BC + 3 * BC * BC + 7 * (size_t)BC * D + (size_t)D * D +
                        (minimal ? 0 : (size_t)BC * D + (size_t)D * D);
     return chunks * per * sizeof(float);
@@ -1137,7 +1137,7 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, int dtyp
     a.q = q, a.k = k, a.v = v, a.g = g, a.beta = beta, a.state0 = state0, a.d_o = d_o;
     a.d_state = d_state, a.dq = dq, a.dk = dk, a.dv = dv, a.dg = dg, a.dbeta = dbeta;
     a.dstate0 = dstate0;
-    a.B = B, a.T = T, a.H = H, a.NC = (T + BC - 1) / BC;
+    a.B = B, a.T = T, a.H = H, a.NC = (int)(((long)T + BC - 1) / BC);
     const size_t chunks = (size_t)a.NC * B * H;
     float* p = static_cast<float*>(ws);
     a.sc = p, p += chunks * SCN * BC;

@@ -908,7 +908,7 @@ struct Plan {
 
 static Plan make_plan(int B, int T, int H, int D) {
     Plan p;
-    p.NC = (T + CH - 1) / CH;
+    p.NC = (int)(((long)T + CH - 1) / CH);
     const long BH = (long)B * H;
     // One segment when the heads alone give enough workgroups or the sequence
     // is short; otherwise segments of about sqrt(NC / 2) chunks, balancing the

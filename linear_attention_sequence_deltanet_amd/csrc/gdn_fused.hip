@@ -848,7 +848,7 @@ FPlan fused_plan(int B, int T, int H, int D) {
     constexpr long kCUs = 256;
     constexpr double kOut = 6.5, kSum = 5.7, kComb = 1.2, kLaunch = 5.0, kMap = 7.0, kStep = 0.8;
     FPlan p;
-    p.NC = (T + FC - 1) / FC;
+    p.NC = (int)(((long)T + FC - 1) / FC);
     const long BH = (long)B * H;
     auto rounds = [](long wgs) { return (double)((wgs + kCUs - 1) / kCUs); };
     p.S = 1;

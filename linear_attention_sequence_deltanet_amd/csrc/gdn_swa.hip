@@ -720,7 +720,7 @@ struct QPack {
     int P, hpw;
 };
 static QPack swa_pack(int T, int Hq, int Hkv) {
-    const int nqb = (T + QB - 1) / QB;
+    const int nqb = (int)(((long)T + QB - 1) / QB);
     const int nlast = T - (nqb - 1) * QB;
     int P = 16;
     while (P < nlast) P *= 2;
@@ -730,7 +730,7 @@ static QPack swa_pack(int T, int Hq, int Hkv) {
 
 // (query block, head) workgroup items of a call, before any key-range split
 static long swa_base_items(int B, int T, int Hq, int Hkv, const QPack& pk) {
-    const int nqb = (T + QB - 1) / QB;
+    const int nqb = (int)(((long)T + QB - 1) / QB);
     const int G = Hq / Hkv;
     const long last = pk.hpw > 1 ? (long)Hkv * ((G + pk.hpw - 1) / pk.hpw) : Hq;
     return (long)B * ((long)Hq * (nqb - 1) + last);
@@ -774,13 +774,13 @@ static SwaPlan swa_plan(int B, int T, int Hq, int Hkv, int window, long long pos
 
 static size_t swa_part_bytes(int B, int T, int Hq, int ns) {
     if (ns <= 1) return 0;
-    const size_t items = (size_t)B * Hq * ((T + QB - 1) / QB) * ns;
+    const size_t items = (size_t)B * Hq * (((size_t)T + QB - 1) / QB) * ns;
     return items * QB * (SD * sizeof(_Float16) + 2 * sizeof(float));  // O / l fp16, then m, l
 }
 
 // Blocks of a call's image: from the block of its first token (off = pos0 mod
 // 64 rows before it) to the block of its last
-static int swa_img_blocks(int T, int off) { return (off + T + KB - 1) / KB; }
+static int swa_img_blocks(int T, int off) { return (int)(((long)off + T + KB - 1) / KB); }
 
 // the call's block images [B][Hkv][NKB][IMG], for the largest offset
 static size_t swa_img_bytes(int B, int T, int Hkv) {
@@ -790,7 +790,7 @@ static size_t swa_img_bytes(int B, int T, int Hkv) {
 // Ring blocks: the W - 1 keys before a call span at most ceil((W - 1) / 64) + 1
 // blocks, so with that many slots none of them is overwritten before the call
 // has read it.
-static int swa_ring_blocks(int window) { return (window - 1 + KB - 1) / KB + 1; }
+static int swa_ring_blocks(int window) { return (int)(((long)window - 1 + KB - 1) / KB) + 1; }
 
 size_t swa_cache_bytes(int B, int Hkv, int window) {
     // each of the two caches: the K tiles in the first KIMG halves of each slot
@@ -849,7 +849,7 @@ hipError_t launch_swa(const void* q, const void* k, const void* v, void* k_cache
     a.o = o;
     a.T = T, a.Hq = Hq, a.Hkv = Hkv, a.W = window;
     a.hist = hist, a.NKB = NKB, a.off = off, a.NBR = NBR, a.slot0 = slot0;
-    a.nqb = (T + QB - 1) / QB;
+    a.nqb = (int)(((long)T + QB - 1) / QB);
     const SwaPlan plan = swa_plan(B, T, Hq, Hkv, window, pos0, ring);
     a.ns = plan.ns;
     a.part = part;
