@@ -25,8 +25,13 @@
  *     (dtype GDN_BF16, raw bfloat16 bits) or fp32 (GDN_F32); g, beta, state
  *     and o are always fp32.  g is the log of the decay a (g <= 0), beta the
  *     write strength (0 <= beta <= 1).  Values outside that domain are not
- *     rejected; the result is then unspecified (bf16-input paths hold operands
- *     in fp16 inside the matrix cores and assume unit-norm-scale keys).
+ *     rejected; the result is then unspecified.  bf16-input prefill and
+ *     stream calls hold the state, Delta and q in fp16 inside the matrix cores,
+ *     so keys should be unit-norm scale (as L2-normalised keys are) and the
+ *     entries of the state and of v must stay inside fp16's normal range
+ *     (about 6e-5 to 65504 in magnitude); v and the state scaled by 1e-2 to
+ *     1e3 against unit-scale values are tested.  Decode and fp32 inputs
+ *     compute in fp32.
  *   - Supported sizes: d_k == d_v in {64, 128}; B, H >= 1; T >= 1 (any T).
  *   - Every pointer must be 16-byte aligned.
  *   - Outputs must not overlap any input or each other; the only allowed

@@ -276,3 +276,30 @@ def test_nan_workspace_backward(env):
         _note("NaN workspace backward %s rel err %.3e" % (gk, e))
         assert np.isfinite(x_).all(), gk
         assert e <= TOL["f32"], (gk, e)
+
+
+@pytest.mark.parametrize("scale", [1e-2, 1e2, 1e3])
+@pytest.mark.parametrize("T,H,g_shift", [(3000, 4, 2.0), (5000, 2, -9.0)])
+def test_value_scale(env, scale, T, H, g_shift):
+    """bf16 prefill with v scaled by 1e-2 .. 1e3 (the header's domain: the
+    state and Delta enter the matrix cores as fp16, so state entries must stay
+    inside fp16's normal range), through the chunk-map plan (T=3000, H=4) and
+    the segmented plan (T=5000, H=2, gates near one: the longest memory, so
+    the largest state).  The error metric is relative to max |ref|, so it
+    does not depend on the scale while nothing leaves that range."""
+    gdn, dev = env
+    _note("case value scale %.0e T=%d H=%d g_shift=%g" % (scale, T, H, g_shift))
+    d = gdn_inputs.random_inputs(1, T, H, 128, 128, dtype="bf16", seed=int(T + H),
+                                 g_shift=g_shift, state_std=0.2)
+    v = gdn_inputs.bf16_to_f32(d["v"]) * np.float32(scale)
+    d["v"] = gdn_inputs.bf16_bits(v)
+    d["state0"] = (d["state0"] * scale).astype(np.float32)
+    x = stage(d, dev)
+    st = x["state0"].clone()
+    o, _ = gdn.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"], st, state_out=st)
+    import torch
+    torch.cuda.synchronize()
+    ro, rs = oracle_sequence(d)
+    on, sn = o.cpu().numpy(), st.cpu().numpy()
+    assert np.isfinite(on).all() and np.isfinite(sn).all()
+    _check("value scale %.0e T=%d" % (scale, T), on, sn, ro, rs, TOL["bf16"])
