@@ -189,6 +189,28 @@ def test_prefill256k_sampled(env):
     assert np.isfinite(o).all() and np.isfinite(st).all()
 
 
+def test_prefill1m_sampled(env):
+    """B=1, H=16, T=2^20+37 (ragged): q, k, v take 4.3 GB each and o 8.6 GB, so
+    every tensor spans more than 2^31 bytes.  Full GPU run; oracle on 2 sampled
+    heads, every token, and their final states."""
+    gdn, dev = env
+    import torch
+    T = (1 << 20) + 37
+    _note("case prefill 1M+37 (sampled heads 0, 9)")
+    d = gdn_inputs.sequence_inputs("prefill256k", T=T)
+    x = stage(d, dev)
+    o, st = gdn.prefill(x["q"], x["k"], x["v"], x["g"], x["beta"])
+    heads = [(0, 0), (0, 9)]
+    oh = torch.stack([o[b, :, h] for b, h in heads]).cpu().numpy()
+    sh = torch.stack([st[b, h] for b, h in heads]).cpu().numpy()
+    del x, o, st
+    torch.cuda.empty_cache()
+    ro, rs = oracle_heads(d, heads)
+    for n, (b, h) in enumerate(heads):
+        _check("prefill 1M head %d" % h, oh[n], sh[n], ro[n], rs[n], TOL["bf16"])
+    assert np.isfinite(oh).all() and np.isfinite(sh).all()
+
+
 def test_decode64_1000_steps(env):
     """B=64 sequences, H=16, 1000 consecutive steps from a random state, in place.
     All heads checked on every step's output and on the final state."""
