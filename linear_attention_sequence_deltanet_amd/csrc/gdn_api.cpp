@@ -115,9 +115,11 @@ gdn_status run_prefill(const void* q, const void* k, const void* v, gdn_dtype dt
 
 namespace gdn {
 
+// With the hook off nothing here writes, so calls from several threads share
+// no written state.
 void profile_begin(hipStream_t stream) {
-    g_marks = 0;
-    if (g_nevents > 0 && hipEventRecord(g_events[0], stream) == hipSuccess) g_marks = 1;
+    if (g_nevents <= 0) return;
+    g_marks = hipEventRecord(g_events[0], stream) == hipSuccess ? 1 : 0;
 }
 
 void profile_mark(hipStream_t stream) {
