@@ -259,7 +259,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void gdn_fused(
     // (tile w of M) of the augmented state together; OUT only the value tile.
     const int BH = B * H;
     // MAP: blocks [0, BH NC) the value halves, [BH NC, 2 BH NC) the identity halves
-    const int blk_x = MAP ? (int)blockIdx.x % (BH * S) : (int)blockIdx.x;
+    int blk_x = MAP ? (int)blockIdx.x % (BH * S) : (int)blockIdx.x;
+    if (!MAP && (BH * S) % 8 == 0) {
+        // Workgroups are dealt to the eight XCDs in turn (XCD = id mod 8).  XCD x
+        // takes the contiguous range x N/8 .. of the (segment, head) order, so it
+        // reads whole token rows (every head of its segments) rather than two
+        // heads' pieces of every row: 80.1 against 80.8 µs per prefill8k call.
+        const int N = BH * S, L = blk_x;
+        blk_x = (L % 8) * (N / 8) + L / 8;
+    }
     const bool idc = MAP && (int)blockIdx.x >= BH * S;  // identity half (workgroup-uniform)
     const int bh = blk_x % BH, seg = blk_x / BH;
     const int b = bh / H, h = bh % H;
