@@ -98,7 +98,13 @@ __global__ __launch_bounds__(256) void conv_qkv_kernel(const ConvArgs a) {
     const bool norm = a.l2norm && m < 2;
 
     const int G = a.C / 8;
-    const long item = (long)blockIdx.x * 256 + threadIdx.x;
+    // Blocks are dealt to the eight XCDs in turn (XCD = id mod 8); XCD x takes a
+    // contiguous range of token blocks, so the three rows before a block, which
+    // the previous block also read, are mostly still in that XCD's L2
+    // (35.4 against 36.1 us at the 8K prefill shape).
+    long blk = blockIdx.x;
+    if (gridDim.x % 8 == 0) blk = (blk % 8) * (gridDim.x / 8) + blk / 8;
+    const long item = blk * 256 + threadIdx.x;
     const int cg = (int)(item % G);
     const long rest = item / G;
     const int tb = (int)(rest % a.ntb);
